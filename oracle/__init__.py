@@ -1,0 +1,200 @@
+"""Plain CPU oracle for the shared-INT4 speculative-decoding hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(the HIP library and its Python binding) never touches it, and it shares no code
+with them.
+
+The arithmetic lives in ``qspec_oracle.c`` (scalar loops, fp64/int64); this
+module only marshals numpy arrays into it.  ``build()`` compiles the C file with
+gcc; ``_lib()`` builds it on first use when no built copy exists.
+
+Every function follows a definition on the QSPEC study-notes page ("QSPEC 논문
+요점 정리", notes on "QSPEC: Speculative Decoding with Complementary Quantization
+Schemes"); the C source cites the section for each.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+GROUP = 128
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qspec_oracle.c")
+_SO = os.path.join(_HERE, "libqspec_oracle.so")
+_LIB = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-fexcess-precision=standard", "-Wall", "-Wextra",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_SO):
+            build(force=False)
+        lib = ctypes.CDLL(_SO)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.orc_fp16_to_double.argtypes = [ctypes.c_uint16]
+        lib.orc_fp16_to_double.restype = ctypes.c_double
+        lib.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.orc_bf16_to_double.restype = ctypes.c_double
+        lib.orc_double_to_bf16.argtypes = [ctypes.c_double]
+        lib.orc_double_to_bf16.restype = ctypes.c_uint16
+        lib.orc_dequant_one.argtypes = [ctypes.c_uint16, ctypes.c_int, ctypes.c_int]
+        lib.orc_dequant_one.restype = ctypes.c_uint16
+        lib.orc_dequant.argtypes = [P, P, P, I, I, P]
+        lib.orc_gemm_w4a16.argtypes = [P, I, P, P, P, I, I, P]
+        lib.orc_quantize_act.argtypes = [P, I, I, P, P]
+        lib.orc_gemm_w4a4.argtypes = [P, P, I, P, P, P, I, I, P, P]
+        lib.orc_verify_greedy.argtypes = [P, P, I, I, I, P, P]
+        lib.orc_verify_sample.argtypes = [P, P, P, P, P, I, I, I, P, P, P]
+        lib.orc_kv_overwrite.argtypes = [P, P, P, P, I, I, I, I, I, I]
+        for name in ("orc_dequant", "orc_gemm_w4a16", "orc_quantize_act", "orc_gemm_w4a4",
+                     "orc_verify_greedy", "orc_verify_sample", "orc_kv_overwrite"):
+            getattr(lib, name).restype = None
+        _LIB = lib
+    return _LIB
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+# ---- scalar format helpers (exposed so the tests can pin them) -------------
+
+def fp16_to_double(bits: int) -> float:
+    return _lib().orc_fp16_to_double(int(bits))
+
+
+def bf16_to_double(bits: int) -> float:
+    return _lib().orc_bf16_to_double(int(bits))
+
+
+def double_to_bf16(v: float) -> int:
+    return int(_lib().orc_double_to_bf16(float(v)))
+
+
+def dequant_one(scale_bits: int, w: int, z: int) -> int:
+    return int(_lib().orc_dequant_one(int(scale_bits), int(w), int(z)))
+
+
+# ---- the hot-path operations --------------------------------------------------
+
+def dequant(codes, scales, zeros):
+    """W_hat = bf16(s * (w - z)) for every (n, k); returns u16 [N][K]."""
+    codes = _c(codes, np.uint8)
+    N, K2 = codes.shape
+    K = 2 * K2
+    scales = _c(scales, np.uint16)
+    zeros = _c(zeros, np.uint8)
+    assert scales.shape == (N, K // GROUP) and zeros.shape == (N, K // GROUP)
+    out = np.empty((N, K), np.uint16)
+    _lib().orc_dequant(_p(codes), _p(scales), _p(zeros), K, N, _p(out))
+    return out
+
+
+def gemm_w4a16(x, codes, scales, zeros):
+    """y = X W_hat in fp64; x u16 bf16 [M][K]; returns f64 [M][N]."""
+    x = _c(x, np.uint16)
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint16)
+    zeros = _c(zeros, np.uint8)
+    M, K = x.shape
+    N = codes.shape[0]
+    assert codes.shape == (N, K // 2)
+    assert scales.shape == (N, K // GROUP) and zeros.shape == (N, K // GROUP)
+    y = np.empty((M, N), np.float64)
+    _lib().orc_gemm_w4a16(_p(x), M, _p(codes), _p(scales), _p(zeros), K, N, _p(y))
+    return y
+
+
+def quantize_act(x):
+    """Per-(token, group) symmetric INT4; returns (codes u8 [M][K/2], scales f32 [M][K/128])."""
+    x = _c(x, np.uint16)
+    M, K = x.shape
+    assert K % GROUP == 0
+    codes = np.zeros((M, K // 2), np.uint8)
+    scales = np.empty((M, K // GROUP), np.float32)
+    _lib().orc_quantize_act(_p(x), M, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def gemm_w4a4(a_codes, a_scales, codes, scales, zeros, want_dots: bool = True):
+    """Returns (y f64 [M][N], D i64 [K/128][M][N] or None)."""
+    a_codes = _c(a_codes, np.uint8)
+    a_scales = _c(a_scales, np.float32)
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint16)
+    zeros = _c(zeros, np.uint8)
+    M, K2 = a_codes.shape
+    K = 2 * K2
+    N = codes.shape[0]
+    assert codes.shape == (N, K2) and a_scales.shape == (M, K // GROUP)
+    y = np.empty((M, N), np.float64)
+    D = np.empty((K // GROUP, M, N), np.int64) if want_dots else None
+    _lib().orc_gemm_w4a4(_p(a_codes), _p(a_scales), M, _p(codes), _p(scales), _p(zeros), K, N,
+                         _p(D), _p(y))
+    return y, D
+
+
+def verify_greedy(target, draft_tokens):
+    """target f32 [B][g+1][V], draft_tokens i32 [B][g] -> (accept i32 [B], out i32 [B][g+1])."""
+    target = _c(target, np.float32)
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    d = _c(draft_tokens, np.int32).reshape(B, gamma)
+    acc = np.empty(B, np.int32)
+    out = np.empty((B, g1), np.int32)
+    _lib().orc_verify_greedy(_p(target), _p(d), B, gamma, V, _p(acc), _p(out))
+    return acc, out
+
+
+def verify_sample(target, draft, draft_tokens, u, v, with_diag: bool = True):
+    """Speculative-sampling verification.  Returns (accept, out, diag)."""
+    target = _c(target, np.float32)
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    draft = _c(draft, np.float32).reshape(B, gamma, V)
+    d = _c(draft_tokens, np.int32).reshape(B, gamma)
+    u = _c(u, np.float32).reshape(B, gamma)
+    v = _c(v, np.float32).reshape(B)
+    acc = np.empty(B, np.int32)
+    out = np.empty((B, g1), np.int32)
+    diag = np.empty((B, g1), np.float64) if with_diag else None
+    _lib().orc_verify_sample(_p(target), _p(draft), _p(d), _p(u), _p(v), B, gamma, V,
+                             _p(acc), _p(out), _p(diag))
+    return acc, out, diag
+
+
+def kv_overwrite(cache, verify_kv, start_pos, accept):
+    """In place on ``cache`` (u16 [L][B][2][H][T][D]); verify_kv u16 [L][B][2][H][g+1][D]."""
+    assert cache.dtype == np.uint16 and cache.flags["C_CONTIGUOUS"]
+    L, B, two, H, T, D = cache.shape
+    assert two == 2
+    verify_kv = _c(verify_kv, np.uint16)
+    gamma = verify_kv.shape[4] - 1
+    assert verify_kv.shape == (L, B, 2, H, gamma + 1, D)
+    start_pos = _c(start_pos, np.int32).reshape(B)
+    accept = _c(accept, np.int32).reshape(B)
+    _lib().orc_kv_overwrite(_p(cache), _p(verify_kv), _p(start_pos), _p(accept), L, B, H, T, D,
+                            gamma)
+    return cache

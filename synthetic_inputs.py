@@ -1,0 +1,122 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module only draws random numbers and lays them out in the storage formats;
+it holds none of the method's arithmetic (no quantizer, no dequantization, no
+product, no softmax).  Both the oracle side and the HIP side read what it makes.
+
+Storage formats (fixed by this project):
+  weight codes  u8  [N][K/2]   two unsigned 4-bit codes per byte, even k in the low nibble
+  weight scales u16 [N][K/128] IEEE binary16 bit patterns
+  weight zeros  u8  [N][K/128] 0..15
+  activations   u16 [M][K]     bfloat16 bit patterns
+  logits        f32
+
+Distributions (one PCG64 stream per tensor, seeded by a fixed table):
+  * weight codes uniform 0..15 (so each packed byte is uniform 0..255);
+  * weight scales uniform [1e-3, 1e-2], rounded to binary16; zero points uniform 0..15;
+  * activations N(0, 1) with round(1% of K) channels (same for every token) scaled
+    by 20, then rounded to bfloat16 (nearest-even, by torch's conversion);
+  * target logits N(0, sigma=3); draft logits = target + N(0, 0.5);
+  * uniforms in [0, 1) as float32;
+  * KV: a position-dependent canary pattern in the cache, N(0, 1) bfloat16 staging rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128
+
+# seed table: one base per tensor kind; a config index or layer index is added.
+SEED_WEIGHTS = 100
+SEED_ACT = 200
+SEED_OUTLIER = 300
+SEED_LOGITS = 400
+SEED_NOISE = 500
+SEED_UNIFORM = 600
+SEED_START = 700
+SEED_KV = 800
+SEED_GUMBEL = 900
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(int(seed)))
+
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round float32 values to bfloat16 (torch's nearest-even conversion); u16 patterns."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def weights(K: int, N: int, seed: int) -> dict:
+    """Shared INT4 weights: codes [N][K/2], fp16 scales [N][K/128], zeros [N][K/128]."""
+    assert K % GROUP == 0
+    G = K // GROUP
+    r = rng(SEED_WEIGHTS + seed)
+    codes = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = r.uniform(1e-3, 1e-2, size=(N, G)).astype(np.float16).view(np.uint16)
+    zeros = r.integers(0, 16, size=(N, G), dtype=np.uint8)
+    return {"codes": codes, "scales": scales, "zeros": zeros, "K": K, "N": N}
+
+
+def outlier_channels(K: int, seed: int) -> np.ndarray:
+    n_out = int(round(0.01 * K))
+    return rng(SEED_OUTLIER + seed).choice(K, size=n_out, replace=False)
+
+
+def activations(M: int, K: int, seed: int, outlier_seed: int | None = None) -> np.ndarray:
+    """bfloat16 [M][K] with 1% outlier channels x20."""
+    x = rng(SEED_ACT + seed).standard_normal((M, K)).astype(np.float32)
+    cols = outlier_channels(K, seed if outlier_seed is None else outlier_seed)
+    x[:, cols] *= 20.0
+    return f32_to_bf16_bits(x)
+
+
+def logits(B: int, gamma: int, V: int, seed: int, sigma: float = 3.0, noise: float = 0.5):
+    """target f32 [B][gamma+1][V] ~ N(0, sigma); draft f32 [B][gamma][V] = target rows + N(0, noise)."""
+    t = (rng(SEED_LOGITS + seed).standard_normal((B, gamma + 1, V)) * sigma).astype(np.float32)
+    e = (rng(SEED_NOISE + seed).standard_normal((B, gamma, V)) * noise).astype(np.float32)
+    d = (t[:, :gamma, :] + e).astype(np.float32)
+    return t, d
+
+
+def draft_tokens_greedy(draft: np.ndarray) -> np.ndarray:
+    """The draft's own greedy choices (argmax of each draft row), i32 [B][gamma]."""
+    return np.argmax(draft, axis=-1).astype(np.int32)
+
+
+def draft_tokens_sampled(draft: np.ndarray, seed: int) -> np.ndarray:
+    """Draft tokens drawn from softmax(draft row) with the Gumbel-max rule."""
+    g = rng(SEED_GUMBEL + seed).gumbel(size=draft.shape)
+    return np.argmax(draft.astype(np.float64) + g, axis=-1).astype(np.int32)
+
+
+def uniforms(shape, seed: int) -> np.ndarray:
+    return rng(SEED_UNIFORM + seed).random(size=shape, dtype=np.float32)
+
+
+def kv_canary(L: int, B: int, H: int, T: int, D: int) -> np.ndarray:
+    """A cache filled with a pattern that encodes (l, b, kv, h, t, e); u16 [L][B][2][H][T][D]."""
+    idx = np.arange(L * B * 2 * H * T * D, dtype=np.uint64)
+    return ((idx * np.uint64(2654435761)) >> np.uint64(7)).astype(np.uint16)
+
+
+def kv_staging(L: int, B: int, H: int, gamma: int, D: int, seed: int) -> np.ndarray:
+    x = rng(SEED_KV + seed).standard_normal((L, B, 2, H, gamma + 1, D)).astype(np.float32)
+    return f32_to_bf16_bits(x)
+
+
+def start_positions(B: int, T: int, gamma: int, seed: int) -> np.ndarray:
+    return rng(SEED_START + seed).integers(0, T - gamma - 1 + 1, size=B).astype(np.int32)
+
+
+# ---- named workloads (shapes only; see the design doc for the recipe) -------------
+
+LLAMA3_8B_PROJ = {"qkv": (4096, 6144), "o": (4096, 4096), "gate_up": (4096, 2 * 14336),
+                  "down": (14336, 4096)}
+QWEN25_7B_PROJ = {"qkv": (3584, 4608), "o": (3584, 3584), "gate_up": (3584, 2 * 18944),
+                  "down": (18944, 3584), "lm_head": (3584, 152064)}
+LLAMA3_70B_FFN = {"gate_up": (8192, 2 * 28672), "down": (28672, 8192)}
+SMALL_LAYER = {"proj": (512, 512)}

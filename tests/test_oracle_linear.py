@@ -1,0 +1,211 @@
+"""Pins for the oracle's quantizer, W4A16 and W4A4 linear layers.
+
+QSPEC notes, background terms: W4A16 keeps 4-bit weights and 16-bit activations
+and multiplies by the dequantized W_hat = s (W_INT4 - z); W4A4 quantizes the
+activations to 4 bits too, accumulates the integer products in INT32 and applies
+the scales afterwards.  The pins below use library routines (numpy matmul and
+einsum in float64 / int64), closed forms and invariants -- never the oracle's
+own loops.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic_inputs as si
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")))
+
+
+def bf16_to_f64(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def unpack_unsigned(codes):
+    """[R][K/2] bytes -> [R][K] nibbles, even k from the low nibble (the storage format)."""
+    lo = codes & 0x0F
+    hi = codes >> 4
+    out = np.empty((codes.shape[0], codes.shape[1] * 2), np.int64)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def unpack_signed(codes):
+    u = unpack_unsigned(codes)
+    return np.where(u >= 8, u - 16, u)
+
+
+# ---------------------------------------------------------------- quantizer
+
+def test_quantizer_golden_ties():
+    g = GOLDEN["quantizer_ties"]
+    head = np.array(g["group_head"], np.float32)
+    x = np.zeros((1, 256), np.float32)
+    x[0, :len(head)] = head
+    xb = si.f32_to_bf16_bits(x)
+    assert np.array_equal(bf16_to_f64(xb)[0, :len(head)], head)   # all exactly representable
+    codes, scales = oracle.quantize_act(xb)
+    q = unpack_signed(codes)[0]
+    assert scales[0, 0] == g["scale"]
+    assert list(q[:len(head)]) == g["codes_head"]
+    assert np.all(q[len(head):128] == 0)
+    assert scales[0, 1] == 0.0 and np.all(q[128:] == 0)
+
+
+@pytest.fixture(scope="module")
+def act():
+    return si.activations(7, 1024, seed=11)
+
+
+def test_quantizer_range_and_absmax_code(act):
+    codes, scales = oracle.quantize_act(act)
+    q = unpack_signed(codes).reshape(7, 8, 128)
+    x = bf16_to_f64(act).reshape(7, 8, 128)
+    assert q.min() >= -7 and q.max() <= 7          # divisor 7: nothing reaches -8
+    amax = np.abs(x).max(axis=2)
+    # s_a * 7 reproduces the group's absmax to within one float32 rounding
+    assert np.allclose(scales.astype(np.float64) * 7.0, amax, rtol=2 ** -23, atol=0)
+    # the absmax element(s) quantize to +-7 exactly
+    at_max = np.abs(x) == amax[..., None]
+    assert np.all(np.abs(q[at_max]) == 7)
+
+
+def test_quantizer_error_bound(act):
+    codes, scales = oracle.quantize_act(act)
+    q = unpack_signed(codes).reshape(7, 8, 128).astype(np.float64)
+    x = bf16_to_f64(act).reshape(7, 8, 128)
+    s = scales.astype(np.float64)[..., None]
+    assert np.all(np.abs(x - q * s) <= s / 2 * (1 + 2 ** -20))
+
+
+def test_quantizer_sign_symmetry_and_scaling(act):
+    codes, scales = oracle.quantize_act(act)
+    neg = act ^ np.uint16(0x8000)
+    codes_n, scales_n = oracle.quantize_act(neg)
+    assert np.array_equal(unpack_signed(codes_n), -unpack_signed(codes))
+    assert np.array_equal(scales_n, scales)
+    # doubling x (exact in bfloat16) doubles the scale and keeps the codes
+    dbl = si.f32_to_bf16_bits(bf16_to_f64(act).astype(np.float32) * 2)
+    codes_d, scales_d = oracle.quantize_act(dbl)
+    assert np.array_equal(codes_d, codes)
+    assert np.array_equal(scales_d, scales * 2)
+
+
+def test_quantizer_groups_are_independent(act):
+    codes, scales = oracle.quantize_act(act)
+    mod = act.copy()
+    mod[3, 300] = si.f32_to_bf16_bits(np.array([50.0], np.float32))[0]   # group 2 of row 3
+    codes_m, scales_m = oracle.quantize_act(mod)
+    qa, qb = unpack_signed(codes), unpack_signed(codes_m)
+    changed = np.argwhere(qa != qb)
+    assert len(changed) > 0
+    assert np.all(changed[:, 0] == 3) and np.all((changed[:, 1] >= 256) & (changed[:, 1] < 384))
+    diff_s = np.argwhere(scales != scales_m)
+    assert diff_s.tolist() == [[3, 2]]
+
+
+def test_quantizer_zero_group_and_packing():
+    x = np.zeros((2, 256), np.float32)
+    x[1, 129] = -3.0    # odd k in group 1 -> high nibble of byte 64
+    codes, scales = oracle.quantize_act(si.f32_to_bf16_bits(x))
+    assert np.all(codes[0] == 0) and np.all(scales[0] == 0)
+    assert scales[1, 0] == 0 and scales[1, 1] == np.float32(3.0) / np.float32(7.0)
+    assert codes[1, 64] == ((-7) & 15) << 4
+    assert np.count_nonzero(codes[1]) == 1
+
+
+# ---------------------------------------------------------------- W4A16
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (5, 384, 40), (3, 512, 7)])
+def test_w4a16_unit_scale_reduces_to_plain_matmul(M, K, N):
+    w = si.weights(K, N, seed=M)
+    w["scales"][:] = np.float16(1.0).view(np.uint16)
+    w["zeros"][:] = 0
+    x = si.activations(M, K, seed=N)
+    y = oracle.gemm_w4a16(x, w["codes"], w["scales"], w["zeros"])
+    ref = bf16_to_f64(x) @ unpack_unsigned(w["codes"]).astype(np.float64).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("M,K,N", [(2, 256, 24), (5, 640, 33)])
+def test_w4a16_matches_matmul_with_dequantized_weights(M, K, N):
+    w = si.weights(K, N, seed=7 + M)
+    x = si.activations(M, K, seed=3)
+    y = oracle.gemm_w4a16(x, w["codes"], w["scales"], w["zeros"])
+    what = bf16_to_f64(oracle.dequant(w["codes"], w["scales"], w["zeros"]))   # [N][K]
+    ref = bf16_to_f64(x) @ what.T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    # zero points shift every output by -z*s*sum(x) per group: recomputed by hand
+    w2 = dict(w)
+    w2["zeros"] = np.zeros_like(w["zeros"])
+    w2["scales"] = np.full_like(w["scales"], np.float16(2.0 ** -6).view(np.uint16))
+    y2 = oracle.gemm_w4a16(x, w["codes"], w2["scales"], w2["zeros"])
+    ref2 = bf16_to_f64(x) @ (unpack_unsigned(w["codes"]).astype(np.float64).T * 2.0 ** -6)
+    assert np.allclose(y2, ref2, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- W4A4
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (4, 512, 24), (3, 384, 5)])
+def test_w4a4_group_dots_exact(M, K, N):
+    w = si.weights(K, N, seed=20 + M)
+    x = si.activations(M, K, seed=21)
+    ac, asc = oracle.quantize_act(x)
+    y, D = oracle.gemm_w4a4(ac, asc, w["codes"], w["scales"], w["zeros"])
+    qa = unpack_signed(ac).reshape(M, K // 128, 128)
+    wu = unpack_unsigned(w["codes"]).reshape(N, K // 128, 128) - w["zeros"][..., None].astype(np.int64)
+    ref = np.einsum("mgk,ngk->gmn", qa, wu)
+    assert np.array_equal(D, ref)
+    assert np.abs(D).max() <= 7 * 15 * 128
+    # y is the scale-weighted sum of the exact group dots
+    s = np.array([oracle.fp16_to_double(b) for b in w["scales"].ravel()]).reshape(N, K // 128)
+    yref = np.einsum("mg,ng,gmn->mn", asc.astype(np.float64), s, D.astype(np.float64))
+    assert np.allclose(y, yref, rtol=1e-12, atol=1e-15)
+
+
+def test_w4a4_zero_point_equal_to_code_gives_zero():
+    K, N, M = 256, 8, 2
+    w = si.weights(K, N, seed=5)
+    w["codes"][:] = 0x77       # every code 7
+    w["zeros"][:] = 7
+    ac, asc = oracle.quantize_act(si.activations(M, K, seed=5))
+    y, D = oracle.gemm_w4a4(ac, asc, w["codes"], w["scales"], w["zeros"])
+    assert np.all(D == 0) and np.all(y == 0)
+
+
+def test_w4a4_on_grid_activations_match_exact_dequant_product():
+    """When x already lies on its own quantization grid, W4A4 equals X (s (W - z))
+    computed with the exact (unrounded) dequantized weights."""
+    M, K, N = 3, 384, 12
+    r = np.random.default_rng(9)
+    q = r.integers(-7, 8, size=(M, K)).astype(np.float32)
+    q[:, ::128] = 7                                           # absmax 7 in every group
+    step = (2.0 ** r.integers(-4, 3, size=(M, K // 128))).astype(np.float32)
+    x = q * np.repeat(step, 128, axis=1)                      # exact in bfloat16
+    xb = si.f32_to_bf16_bits(x)
+    ac, asc = oracle.quantize_act(xb)
+    assert np.array_equal(asc, step)                          # s_a = 7*step/7 exactly
+    w = si.weights(K, N, seed=9)
+    y, _ = oracle.gemm_w4a4(ac, asc, w["codes"], w["scales"], w["zeros"])
+    s = np.array([oracle.fp16_to_double(b) for b in w["scales"].ravel()]).reshape(N, K // 128)
+    wexact = (unpack_unsigned(w["codes"]) - np.repeat(w["zeros"].astype(np.int64), 128, axis=1)) \
+        * np.repeat(s, 128, axis=1)
+    ref = x.astype(np.float64) @ wexact.T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_w4a4_dots_are_linear_in_activation_codes():
+    K, N = 256, 6
+    w = si.weights(K, N, seed=31)
+    e = np.zeros((1, K), np.float32)
+    e[0, 130] = 7.0                      # one-hot activation: code 7 at k = 130, scale 1
+    ac, asc = oracle.quantize_act(si.f32_to_bf16_bits(e))
+    _, D = oracle.gemm_w4a4(ac, asc, w["codes"], w["scales"], w["zeros"])
+    col = unpack_unsigned(w["codes"])[:, 130] - w["zeros"][:, 1].astype(np.int64)
+    assert np.array_equal(D[1, 0], 7 * col)
+    assert np.all(D[0] == 0)
