@@ -1,0 +1,198 @@
+/*
+ * qspec.h -- C ABI of the shared-INT4 speculative-decoding hot path (gfx950).
+ *
+ * One set of 4-bit weight codes with a per-group scale s and zero point z is
+ * read by two linear-layer kernels: a W4A4 draft layer (activations quantized to
+ * 4 bits, exact integer group dot products, then rescaling) and a W4A16 verify
+ * layer (W_hat = s (W - z) dequantized on the fly, bfloat16 activations).  They
+ * are followed by the verification step and by the replacement of draft KV
+ * with verify KV for the accepted positions.
+ *
+ * Source: the study-notes page "QSPEC 논문 요점 정리" on "QSPEC: Speculative
+ * Decoding with Complementary Quantization Schemes" (Zhao, Lu, Wang, Kong, Wu).
+ * Its sections are cited by content: "background terms" (weight-only vs
+ * weight-activation quantization, INT32 accumulation then scaling, the
+ * dequantization example), "speculative-decoding background" (acceptance rule,
+ * greedy acceptance, first-reject cutoff, L = A + 1), "QSPEC structure" (draft
+ * with W4A4, verify with W4A16 over gamma+1 positions, shared 4-bit weights,
+ * KV replacement).
+ *
+ * Conventions for every call
+ *   - Every pointer argument is DEVICE memory (hipMalloc'd or a torch CUDA
+ *     tensor), allocated, owned and freed by the caller.  The library never
+ *     allocates or frees memory and keeps no state between calls.
+ *   - Calls are asynchronous: they validate their arguments on the host, enqueue
+ *     kernels on `stream` (a hipStream_t; NULL = the legacy default stream) and
+ *     return without synchronizing.  Results are visible after the caller
+ *     synchronizes the stream or orders later work on it.
+ *   - Argument errors (NULL pointers, non-positive or inconsistent sizes,
+ *     unsupported shapes or dtypes, a too-small workspace) are detected before
+ *     any launch and return a negative status with no side effects.
+ *     QSPEC_ERR_HIP reports a launch failure.  Device-resident values (logits,
+ *     token ids, positions, accept counts) are not inspected on the host;
+ *     out-of-range values there never cause out-of-bounds accesses (see each
+ *     call) but give unspecified results.
+ *   - Outputs must not alias inputs.
+ *   - Alignment: x / activation codes / weight codes 16 bytes (they are read with 16-byte
+ *     loads; row starts stay aligned because K is a multiple of 128); fp32 / int32 arrays
+ *     4 bytes; fp16 / bf16 arrays 2 bytes; the verify workspace 16 bytes.  Torch allocations
+ *     satisfy all of these.  A violation returns QSPEC_ERR_ALIGN.
+ *
+ * Storage formats (the pages fix none of these; this library's choices)
+ *   weight codes   u8  [N][K/2]     w(k,n) = (codes[n][k/2] >> 4*(k&1)) & 15, unsigned 0..15
+ *   weight scales  u16 [N][K/128]   IEEE binary16 bit patterns (finite)
+ *   weight zeros   u8  [N][K/128]   zero points 0..15
+ *   activations    u16 [M][K]       bfloat16 bit patterns, row-major
+ *   act. codes     u8  [M][K/2]     4-bit two's complement, even k in the low nibble
+ *   act. scales    f32 [M][K/128]
+ *   K must be a positive multiple of QSPEC_GROUP (128); N >= 1; M >= 1.
+ */
+#ifndef QSPEC_H
+#define QSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *qspec_stream_t; /* hipStream_t */
+
+#define QSPEC_GROUP 128
+
+enum qspec_status {
+    QSPEC_OK = 0,
+    QSPEC_ERR_NULL = -1,        /* a required pointer is NULL */
+    QSPEC_ERR_SHAPE = -2,       /* a size is non-positive, too large or inconsistent */
+    QSPEC_ERR_UNSUPPORTED = -3, /* unknown dtype or mode */
+    QSPEC_ERR_HIP = -4,         /* a kernel launch failed */
+    QSPEC_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than qspec_verify_workspace_bytes() */
+    QSPEC_ERR_ALIGN = -6        /* a pointer is not aligned as its call requires */
+};
+
+enum qspec_out_dtype { QSPEC_OUT_BF16 = 0, QSPEC_OUT_F32 = 1 };
+enum qspec_verify_mode { QSPEC_GREEDY = 0, QSPEC_SAMPLE = 1 };
+
+/* Human-readable name of a status code (static string). */
+const char *qspec_status_string(int status);
+
+/*
+ * qspec_quantize_act -- per-token, per-group symmetric INT4 activation codes.
+ * [QSPEC notes, background terms: weight-activation (W4A4) quantization puts the
+ * activations in 4 bits as well.]  The page fixes no quantizer; this one is, for
+ * every row m and 128-wide group g:
+ *     a = max |x|,  s_a = a / 7 (binary32 division, nearest-even),
+ *     q = clamp(nearest_even(x / s_a), -8, 7)   (binary32 division), q = 0 when a = 0.
+ * x        [in]  u16 [M][K] bfloat16 (finite values)
+ * codes    [out] u8  [M][K/2]   (format above)
+ * scales   [out] f32 [M][K/128] (s_a)
+ * Errors: NULL pointer; M < 1; K < 128 or K % 128 != 0.
+ */
+int qspec_quantize_act(const uint16_t *x, int32_t M, int32_t K, uint8_t *codes, float *scales,
+                       qspec_stream_t stream);
+
+/*
+ * qspec_gemm_w4a4 -- W4A4 draft linear layer over the shared 4-bit weights.
+ * [QSPEC notes, background terms: the 4-bit MACs accumulate in INT32 and the
+ * scale is applied afterwards; QSPEC structure: the draft runs W4A4 on the same
+ * 4-bit weights as the verifier.]  With per-group scales:
+ *     D[g][m][n] = sum_{k in g} q_a[m][k] * (w[k][n] - z[n][g])   (exact, int32)
+ *     y[m][n]    = sum_g s_a[m][g] * s[n][g] * D[g][m][n]          (fp32 accumulation)
+ * a_codes     [in]  u8  [M][K/2], a_scales [in] f32 [M][K/128]  (from qspec_quantize_act)
+ * w_codes, w_scales, w_zeros [in] shared weights, formats above
+ * y           [out] [M][N], bfloat16 (y_dtype = QSPEC_OUT_BF16, nearest-even) or f32
+ * group_dots  [out, optional] i32 [K/128][M][N] -- the exact D; NULL to skip
+ *             (diagnostic: slower).
+ * Row m of y does not depend on the other rows or on M (fixed reduction order).
+ * Errors: NULL pointer; M < 1; N < 1; K < 128 or K % 128 != 0; bad y_dtype.
+ */
+int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int32_t M,
+                    const uint8_t *w_codes, const uint16_t *w_scales, const uint8_t *w_zeros,
+                    int32_t K, int32_t N, void *y, int32_t y_dtype, int32_t *group_dots,
+                    qspec_stream_t stream);
+
+/*
+ * qspec_gemm_w4a16 -- W4A16 verify linear layer over the shared 4-bit weights.
+ * [QSPEC notes, background terms: dequantization example, Y = X W_hat with
+ * W_hat = s (W_INT4 - z) in 16 bits; QSPEC structure: the verifier scores the
+ * gamma+1 positions in one pass.]  W_hat[k][n] = bfloat16_nearest_even(s[n][g] *
+ * (w[k][n] - z[n][g])) (the product is exact before that rounding);
+ * y[m][n] = sum_k x[m][k] * W_hat[k][n] accumulated in fp32.
+ * x   [in]  u16 [M][K] bfloat16
+ * y   [out] [M][N], bfloat16 (nearest-even) or f32 per y_dtype
+ * For M <= 80 row m of y does not depend on the other rows or on M (a fixed
+ * reduction order chosen from K and N only), so verifying gamma+1 positions
+ * reproduces one-position decoding bit for bit.
+ * Errors: NULL pointer; M < 1; N < 1; K < 128 or K % 128 != 0; bad y_dtype.
+ */
+int qspec_gemm_w4a16(const uint16_t *x, int32_t M, const uint8_t *w_codes,
+                     const uint16_t *w_scales, const uint8_t *w_zeros, int32_t K, int32_t N,
+                     void *y, int32_t y_dtype, qspec_stream_t stream);
+
+/*
+ * qspec_verify_workspace_bytes -- device workspace qspec_verify_accept needs
+ * for (mode, B, gamma, V); 0 on invalid sizes.
+ */
+size_t qspec_verify_workspace_bytes(int32_t mode, int32_t B, int32_t gamma, int32_t V);
+
+/*
+ * qspec_verify_accept -- verification of gamma draft tokens per sequence.
+ * [QSPEC notes, speculative-decoding background: greedy acceptance when the
+ * target's most probable token equals the draft; otherwise acceptance with
+ * probability min(1, p(x|h)/q(x|h)); the first rejection discards the rest; a
+ * correction token follows a rejection and an extra target token follows full
+ * acceptance, so L = A + 1 tokens are committed.  QSPEC structure: the verifier
+ * outputs gamma+1 distributions p_{i+1..i+gamma+1}.]
+ * GREEDY: t_j = argmax target[b][j] (ties -> lowest index); A = number of
+ *   leading j with draft_tokens[b][j] == t_j; out = d_0..d_{A-1}, t_A.
+ * SAMPLE: p_j = softmax(target[b][j]), q_j = softmax(draft[b][j]) (temperature 1);
+ *   candidate j is accepted iff u_accept[b][j] < p_j(d_j) / q_j(d_j); A = index of
+ *   the first rejection (gamma if none); the last token is drawn from the
+ *   residual max(0, p_A - q_A) (or from p_A if that has no mass) when A < gamma,
+ *   and from p_gamma when A == gamma, by inverse CDF at u_resample[b] times the
+ *   total mass (first x whose running sum exceeds it).  Softmax normalizers,
+ *   ratios and running sums are in fp64.
+ * target_logits [in]  f32 [B][gamma+1][V]
+ * draft_logits  [in]  f32 [B][gamma][V]  (SAMPLE only; may be NULL for GREEDY or gamma = 0)
+ * draft_tokens  [in]  i32 [B][gamma]     (may be NULL when gamma = 0)
+ * u_accept      [in]  f32 [B][gamma] in [0,1)  (SAMPLE only; may be NULL otherwise)
+ * u_resample    [in]  f32 [B] in [0,1)         (SAMPLE only; may be NULL otherwise)
+ * accept_count  [out] i32 [B]            A per sequence
+ * out_tokens    [out] i32 [B][gamma+1]   committed tokens, -1 after position A
+ * workspace     [in]  device scratch of at least qspec_verify_workspace_bytes(mode, B, gamma, V)
+ *               bytes; contents on entry are ignored.
+ * A draft token outside [0, V) counts as a mismatch / rejection.  Logits must be
+ * finite.
+ * Errors: NULL pointer; bad mode; B < 1; gamma < 0; V < 1; too many rows;
+ * workspace too small.
+ */
+int qspec_verify_accept(int32_t mode, const float *target_logits, const float *draft_logits,
+                        const int32_t *draft_tokens, const float *u_accept,
+                        const float *u_resample, int32_t B, int32_t gamma, int32_t V,
+                        int32_t *accept_count, int32_t *out_tokens, void *workspace,
+                        size_t workspace_bytes, qspec_stream_t stream);
+
+/*
+ * qspec_kv_overwrite -- replace draft KV with verify KV for committed positions.
+ * [QSPEC notes, QSPEC structure: for accepted tokens the low-precision KV written
+ * by the W4A4 draft is replaced with the KV computed by the W4A16 verifier.]
+ * The verifier scores gamma+1 positions starting at start_pos[b] (the previous
+ * round's last token, then the gamma drafts), so rows r = 0..A_b of verify_kv go
+ * to positions start_pos[b] + r; nothing else in the cache changes.
+ * cache        [in/out] u16 [L][B][2][H][T][D] bfloat16 (2 = key, value)
+ * verify_kv    [in]     u16 [L][B][2][H][gamma+1][D]
+ * start_pos    [in]     i32 [B]
+ * accept_count [in]     i32 [B] (device; e.g. straight from qspec_verify_accept),
+ *                       clamped to [0, gamma]; positions outside [0, T) are skipped.
+ * Errors: NULL pointer; any size < 1 (gamma < 0); gamma + 1 > T.
+ */
+int qspec_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const int32_t *start_pos,
+                       const int32_t *accept_count, int32_t L, int32_t B, int32_t H, int32_t T,
+                       int32_t D, int32_t gamma, qspec_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSPEC_H */

@@ -1,0 +1,210 @@
+"""Python binding of libqspec (include/qspec.h): argument marshalling only.
+
+Each function takes torch CUDA tensors, checks dtype / shape / device /
+contiguity, and passes raw device pointers, sizes and the current HIP stream to
+the C entry point of the same name.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback.  A missing or unloadable library
+raises at first use.
+
+Tensor conventions (row-major, contiguous):
+  activations / KV   torch.bfloat16
+  weight codes       torch.uint8 [N][K/2]    (even k in the low nibble, unsigned 0..15)
+  weight scales      torch.float16 [N][K/128]
+  weight zeros       torch.uint8 [N][K/128]
+  activation codes   torch.uint8 [M][K/2]    (4-bit two's complement)
+  activation scales  torch.float32 [M][K/128]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+GROUP = 128
+QSPEC_GREEDY = 0
+QSPEC_SAMPLE = 1
+QSPEC_OUT_BF16 = 0
+QSPEC_OUT_F32 = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqspec.so")
+
+_lib = None
+
+
+class QspecError(RuntimeError):
+    """A negative status returned by the C ABI."""
+
+    def __init__(self, fn: str, status: int):
+        msg = _lib.qspec_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqspec.so (building it once if no built copy exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build(force=False)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.qspec_status_string.argtypes = [ctypes.c_int]
+        L.qspec_status_string.restype = ctypes.c_char_p
+        L.qspec_quantize_act.argtypes = [P, I, I, P, P, P]
+        L.qspec_gemm_w4a4.argtypes = [P, P, I, P, P, P, I, I, P, I, P, P]
+        L.qspec_gemm_w4a16.argtypes = [P, I, P, P, P, I, I, P, I, P]
+        L.qspec_verify_workspace_bytes.argtypes = [I, I, I, I]
+        L.qspec_verify_workspace_bytes.restype = S
+        L.qspec_verify_accept.argtypes = [I, P, P, P, P, P, I, I, I, P, P, P, S, P]
+        L.qspec_kv_overwrite.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
+        for fn in ("qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16",
+                   "qspec_verify_accept", "qspec_kv_overwrite"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise QspecError(fn, status)
+
+
+def _stream(stream, ref: torch.Tensor):
+    if stream is None:
+        stream = torch.cuda.current_stream(ref.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _req(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _weights(w_codes, w_scales, w_zeros):
+    if w_codes.dim() != 2:
+        raise ValueError("w_codes must be [N][K/2]")
+    N, K2 = w_codes.shape
+    K = 2 * K2
+    _req(w_codes, "w_codes", torch.uint8)
+    _req(w_scales, "w_scales", torch.float16, (N, K // GROUP))
+    _req(w_zeros, "w_zeros", torch.uint8, (N, K // GROUP))
+    return K, N
+
+
+def _out_dtype(y: torch.Tensor) -> int:
+    if y.dtype == torch.bfloat16:
+        return QSPEC_OUT_BF16
+    if y.dtype == torch.float32:
+        return QSPEC_OUT_F32
+    raise TypeError("y must be bfloat16 or float32")
+
+
+def qspec_quantize_act(x, codes, scales, stream=None) -> None:
+    """x bf16 [M][K] -> codes u8 [M][K/2], scales f32 [M][K/128]."""
+    _req(x, "x", torch.bfloat16)
+    M, K = x.shape
+    _req(codes, "codes", torch.uint8, (M, K // 2))
+    _req(scales, "scales", torch.float32, (M, K // GROUP))
+    _check("qspec_quantize_act",
+           lib().qspec_quantize_act(_ptr(x), M, K, _ptr(codes), _ptr(scales), _stream(stream, x)))
+
+
+def qspec_gemm_w4a4(a_codes, a_scales, w_codes, w_scales, w_zeros, y, group_dots=None,
+                    stream=None) -> None:
+    """W4A4 draft layer: y [M][N] (bf16 or f32); optional exact group dots i32 [K/128][M][N]."""
+    K, N = _weights(w_codes, w_scales, w_zeros)
+    _req(a_codes, "a_codes", torch.uint8)
+    M = a_codes.shape[0]
+    _req(a_codes, "a_codes", torch.uint8, (M, K // 2))
+    _req(a_scales, "a_scales", torch.float32, (M, K // GROUP))
+    dt = _out_dtype(y)
+    _req(y, "y", y.dtype, (M, N))
+    if group_dots is not None:
+        _req(group_dots, "group_dots", torch.int32, (K // GROUP, M, N))
+    _check("qspec_gemm_w4a4",
+           lib().qspec_gemm_w4a4(_ptr(a_codes), _ptr(a_scales), M, _ptr(w_codes), _ptr(w_scales),
+                                 _ptr(w_zeros), K, N, _ptr(y), dt, _ptr(group_dots),
+                                 _stream(stream, y)))
+
+
+def qspec_gemm_w4a16(x, w_codes, w_scales, w_zeros, y, stream=None) -> None:
+    """W4A16 verify layer: y [M][N] = x W_hat (bf16 or f32 out)."""
+    K, N = _weights(w_codes, w_scales, w_zeros)
+    _req(x, "x", torch.bfloat16)
+    M = x.shape[0]
+    _req(x, "x", torch.bfloat16, (M, K))
+    dt = _out_dtype(y)
+    _req(y, "y", y.dtype, (M, N))
+    _check("qspec_gemm_w4a16",
+           lib().qspec_gemm_w4a16(_ptr(x), M, _ptr(w_codes), _ptr(w_scales), _ptr(w_zeros), K, N,
+                                  _ptr(y), dt, _stream(stream, y)))
+
+
+def qspec_verify_workspace_bytes(mode: int, B: int, gamma: int, V: int) -> int:
+    return int(lib().qspec_verify_workspace_bytes(mode, B, gamma, V))
+
+
+def qspec_verify_accept(mode, target_logits, draft_logits, draft_tokens, u_accept, u_resample,
+                        accept_count, out_tokens, workspace, stream=None) -> None:
+    """Greedy (mode 0) or sampling (mode 1) verification; see include/qspec.h."""
+    _req(target_logits, "target_logits", torch.float32)
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    if gamma > 0 or draft_tokens is not None:
+        _req(draft_tokens, "draft_tokens", torch.int32, (B, gamma))
+    if mode == QSPEC_SAMPLE:
+        if gamma > 0 or draft_logits is not None:
+            _req(draft_logits, "draft_logits", torch.float32, (B, gamma, V))
+        if gamma > 0 or u_accept is not None:
+            _req(u_accept, "u_accept", torch.float32, (B, gamma))
+        _req(u_resample, "u_resample", torch.float32, (B,))
+    _req(accept_count, "accept_count", torch.int32, (B,))
+    _req(out_tokens, "out_tokens", torch.int32, (B, g1))
+    _req(workspace, "workspace", torch.uint8)
+    _check("qspec_verify_accept",
+           lib().qspec_verify_accept(mode, _ptr(target_logits),
+                                     _ptr(draft_logits) if mode == QSPEC_SAMPLE else None,
+                                     _ptr(draft_tokens), _ptr(u_accept) if mode == QSPEC_SAMPLE else None,
+                                     _ptr(u_resample) if mode == QSPEC_SAMPLE else None, B, gamma, V,
+                                     _ptr(accept_count), _ptr(out_tokens), _ptr(workspace),
+                                     workspace.numel(), _stream(stream, target_logits)))
+
+
+def qspec_kv_overwrite(cache, verify_kv, start_pos, accept_count, stream=None) -> None:
+    """cache bf16 [L][B][2][H][T][D] <- verify_kv bf16 [L][B][2][H][gamma+1][D] for rows 0..A_b."""
+    _req(cache, "cache", torch.bfloat16)
+    if cache.dim() != 6 or cache.shape[2] != 2:
+        raise ValueError("cache must be [L][B][2][H][T][D]")
+    L, B, _, H, T, D = cache.shape
+    _req(verify_kv, "verify_kv", torch.bfloat16)
+    if verify_kv.dim() != 6:
+        raise ValueError("verify_kv must be [L][B][2][H][gamma+1][D]")
+    gamma = verify_kv.shape[4] - 1
+    _req(verify_kv, "verify_kv", torch.bfloat16, (L, B, 2, H, gamma + 1, D))
+    _req(start_pos, "start_pos", torch.int32, (B,))
+    _req(accept_count, "accept_count", torch.int32, (B,))
+    _check("qspec_kv_overwrite",
+           lib().qspec_kv_overwrite(_ptr(cache), _ptr(verify_kv), _ptr(start_pos), _ptr(accept_count),
+                                    L, B, H, T, D, gamma, _stream(stream, cache)))
+
+
+__all__ = [
+    "GROUP", "QSPEC_GREEDY", "QSPEC_SAMPLE", "QSPEC_OUT_BF16", "QSPEC_OUT_F32", "QspecError", "lib",
+    "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_verify_workspace_bytes",
+    "qspec_verify_accept", "qspec_kv_overwrite",
+]

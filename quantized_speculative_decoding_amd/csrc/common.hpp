@@ -1,0 +1,79 @@
+// Device-side helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qspec {
+
+constexpr int kGroup = 128;   // quantization group along K (weights and activations)
+constexpr int kWave = 64;     // CDNA wavefront width
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+// 16-byte load marked non-temporal (streamed once: weights, logits).
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+__device__ __forceinline__ float fp16_bits_to_float(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Nearest-even conversion of two floats into a packed bfloat16 pair (lo = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float a) {
+    return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+
+// Wave-wide reductions (64 lanes) through cross-lane shuffles.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+}  // namespace qspec
+
+namespace qspec {
+
+// (a & m) | o in one VALU op; m and o are loop-invariant constants the compiler keeps in VGPRs
+// (gfx9 VOP3 encodings take no literals, so the fused form is not selected on its own).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+    return r;
+}
+
+// Column-count per workgroup split of K among waves: depends on (K, N) only, so that every
+// batch size reduces each output in the same order.
+__host__ __device__ inline int skinny_waves_for_shape(int K, int N) {
+    const int G = K / kGroup;
+    const int tiles = (N + 15) / 16;
+    int kw = 1;
+    while (kw < 8 && tiles * kw * 2 <= 4096) kw *= 2;
+    while (kw > G) kw >>= 1;
+    return kw < 1 ? 1 : kw;
+}
+
+}  // namespace qspec

@@ -1,0 +1,34 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the public
+// interface is include/qspec.h).  Each returns the status of its last launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qspec {
+
+hipError_t launch_quantize_act(const uint16_t *x, int M, int K, uint8_t *codes, float *scales,
+                               hipStream_t st);
+
+hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, const uint16_t *scales,
+                             const uint8_t *zeros, int K, int N, void *y, int y_f32, hipStream_t st);
+
+hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M,
+                            const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                            int K, int N, void *y, int y_f32, int32_t *group_dots, hipStream_t st);
+
+size_t verify_workspace_bytes(int mode, int B, int gamma, int V);
+
+hipError_t launch_verify_accept(int mode, const float *target, const float *draft,
+                                const int32_t *draft_tokens, const float *u_accept,
+                                const float *u_resample, int B, int gamma, int V,
+                                int32_t *accept_count, int32_t *out_tokens, void *workspace,
+                                hipStream_t st);
+
+hipError_t launch_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const int32_t *start_pos,
+                               const int32_t *accept_count, int L, int B, int H, int T, int D,
+                               int gamma, hipStream_t st);
+
+
+}  // namespace qspec

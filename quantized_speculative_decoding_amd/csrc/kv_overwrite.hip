@@ -1,0 +1,52 @@
+// Replacement of draft KV by verify KV for the committed positions, on gfx950.
+// (QSPEC notes, QSPEC structure: for accepted tokens the W4A4 draft's KV is replaced with the
+//  W4A16 verifier's KV.)  Rows r = 0..A_b of the verifier's gamma+1 rows land at positions
+// start_pos[b] + r; nothing else is written.  One thread per 16-byte vector of a candidate row;
+// the accept count is read on the device, so no host round trip separates this from verify.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qspec {
+
+template <typename VecT>
+__global__ void __launch_bounds__(256)
+k_kv_overwrite(uint16_t *__restrict__ cache, const uint16_t *__restrict__ vkv,
+               const int32_t *__restrict__ start_pos, const int32_t *__restrict__ accept,
+               int B, int H, int T, int D, int gamma, long long total) {
+    constexpr int EPV = sizeof(VecT) / sizeof(uint16_t);   // elements per vector
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    const int DV = D / EPV;
+    const int v = (int)(idx % DV);
+    const long long rest = idx / DV;
+    const int r = (int)(rest % (gamma + 1));
+    const long long head = rest / (gamma + 1);             // ((l * B + b) * 2 + kv) * H + h
+    const int b = (int)((head / (2LL * H)) % B);
+    int A = accept[b];
+    A = A < 0 ? 0 : (A > gamma ? gamma : A);
+    if (r > A) return;
+    const long long t = (long long)start_pos[b] + r;
+    if (t < 0 || t >= T) return;
+    VecT *dst = (VecT *)(cache + ((size_t)head * T + (size_t)t) * D) + v;
+    const VecT *src = (const VecT *)(vkv + ((size_t)head * (gamma + 1) + r) * D) + v;
+    *dst = *src;
+}
+
+hipError_t launch_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const int32_t *start_pos,
+                               const int32_t *accept_count, int L, int B, int H, int T, int D,
+                               int gamma, hipStream_t st) {
+    const long long heads = (long long)L * B * 2 * H;
+    const bool vec = (D % 8 == 0) && (((uintptr_t)cache | (uintptr_t)verify_kv) % 16 == 0);
+    const int epv = vec ? 8 : 1;
+    const long long total = heads * (gamma + 1) * (D / epv);
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (vec)
+        hipLaunchKernelGGL(k_kv_overwrite<uint4>, dim3(blocks), dim3(256), 0, st, cache, verify_kv,
+                           start_pos, accept_count, B, H, T, D, gamma, total);
+    else
+        hipLaunchKernelGGL(k_kv_overwrite<uint16_t>, dim3(blocks), dim3(256), 0, st, cache, verify_kv,
+                           start_pos, accept_count, B, H, T, D, gamma, total);
+    return hipGetLastError();
+}
+
+}  // namespace qspec

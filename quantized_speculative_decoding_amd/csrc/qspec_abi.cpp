@@ -1,0 +1,126 @@
+// The C ABI (include/qspec.h): host-side argument validation, then kernel launches on the
+// caller's stream.  No allocation, no synchronization, no state.
+#include "qspec.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+#define QSPEC_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+inline int status_of(hipError_t e) { return e == hipSuccess ? QSPEC_OK : QSPEC_ERR_HIP; }
+
+inline bool bad_k(int32_t K) { return K < QSPEC_GROUP || K % QSPEC_GROUP != 0; }
+
+inline hipStream_t as_stream(qspec_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Largest M * N (or row count) whose flat indices stay far inside the int64 range and whose
+// grids fit the launch limits; sizes are int32 on the interface.
+constexpr long long kMaxElems = 1LL << 40;
+
+}  // namespace
+
+QSPEC_EXPORT const char *qspec_status_string(int status) {
+    switch (status) {
+    case QSPEC_OK: return "ok";
+    case QSPEC_ERR_NULL: return "null pointer argument";
+    case QSPEC_ERR_SHAPE: return "invalid or inconsistent size";
+    case QSPEC_ERR_UNSUPPORTED: return "unsupported dtype or mode";
+    case QSPEC_ERR_HIP: return "HIP launch failure";
+    case QSPEC_ERR_WORKSPACE: return "workspace missing or too small";
+    case QSPEC_ERR_ALIGN: return "misaligned pointer";
+    default: return "unknown status";
+    }
+}
+
+QSPEC_EXPORT int qspec_quantize_act(const uint16_t *x, int32_t M, int32_t K, uint8_t *codes,
+                                    float *scales, qspec_stream_t stream) {
+    if (!x || !codes || !scales) return QSPEC_ERR_NULL;
+    if (M < 1 || bad_k(K)) return QSPEC_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(scales, 4)) return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_quantize_act(x, M, K, codes, scales, as_stream(stream)));
+}
+
+QSPEC_EXPORT int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int32_t M,
+                                 const uint8_t *w_codes, const uint16_t *w_scales,
+                                 const uint8_t *w_zeros, int32_t K, int32_t N, void *y,
+                                 int32_t y_dtype, int32_t *group_dots, qspec_stream_t stream) {
+    if (!a_codes || !a_scales || !w_codes || !w_scales || !w_zeros || !y) return QSPEC_ERR_NULL;
+    if (M < 1 || N < 1 || bad_k(K)) return QSPEC_ERR_SHAPE;
+    if ((long long)M * N > kMaxElems) return QSPEC_ERR_SHAPE;
+    if (y_dtype != QSPEC_OUT_BF16 && y_dtype != QSPEC_OUT_F32) return QSPEC_ERR_UNSUPPORTED;
+    if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 4) || !aligned(w_scales, 2) ||
+        !aligned(y, y_dtype == QSPEC_OUT_F32 ? 4 : 2) || !aligned(group_dots, 4))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_gemm_w4a4(a_codes, a_scales, M, w_codes, w_scales, w_zeros, K, N,
+                                             y, y_dtype == QSPEC_OUT_F32, group_dots,
+                                             as_stream(stream)));
+}
+
+QSPEC_EXPORT int qspec_gemm_w4a16(const uint16_t *x, int32_t M, const uint8_t *w_codes,
+                                  const uint16_t *w_scales, const uint8_t *w_zeros, int32_t K,
+                                  int32_t N, void *y, int32_t y_dtype, qspec_stream_t stream) {
+    if (!x || !w_codes || !w_scales || !w_zeros || !y) return QSPEC_ERR_NULL;
+    if (M < 1 || N < 1 || bad_k(K)) return QSPEC_ERR_SHAPE;
+    if ((long long)M * N > kMaxElems) return QSPEC_ERR_SHAPE;
+    if (y_dtype != QSPEC_OUT_BF16 && y_dtype != QSPEC_OUT_F32) return QSPEC_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 2) ||
+        !aligned(y, y_dtype == QSPEC_OUT_F32 ? 4 : 2))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_gemm_w4a16(x, M, w_codes, w_scales, w_zeros, K, N, y,
+                                              y_dtype == QSPEC_OUT_F32, as_stream(stream)));
+}
+
+static bool verify_sizes_ok(int32_t B, int32_t gamma, int32_t V) {
+    if (B < 1 || gamma < 0 || V < 1) return false;
+    // row-chunk grids are 1-D with at most 2^31 - 1 workgroups
+    const long long rows = (long long)B * (2LL * gamma + 1);
+    const long long chunks = (V + 8191) / 8192;
+    return rows * chunks < (1LL << 31) && (long long)B * (gamma + 1) * V <= kMaxElems;
+}
+
+QSPEC_EXPORT size_t qspec_verify_workspace_bytes(int32_t mode, int32_t B, int32_t gamma, int32_t V) {
+    if ((mode != QSPEC_GREEDY && mode != QSPEC_SAMPLE) || !verify_sizes_ok(B, gamma, V)) return 0;
+    return qspec::verify_workspace_bytes(mode, B, gamma, V);
+}
+
+QSPEC_EXPORT int qspec_verify_accept(int32_t mode, const float *target_logits,
+                                     const float *draft_logits, const int32_t *draft_tokens,
+                                     const float *u_accept, const float *u_resample, int32_t B,
+                                     int32_t gamma, int32_t V, int32_t *accept_count,
+                                     int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                                     qspec_stream_t stream) {
+    if (mode != QSPEC_GREEDY && mode != QSPEC_SAMPLE) return QSPEC_ERR_UNSUPPORTED;
+    if (!target_logits || !accept_count || !out_tokens) return QSPEC_ERR_NULL;
+    if (gamma > 0 && !draft_tokens) return QSPEC_ERR_NULL;
+    if (mode == QSPEC_SAMPLE && (!u_resample || (gamma > 0 && (!draft_logits || !u_accept))))
+        return QSPEC_ERR_NULL;
+    if (!verify_sizes_ok(B, gamma, V)) return QSPEC_ERR_SHAPE;
+    if (!workspace || workspace_bytes < qspec::verify_workspace_bytes(mode, B, gamma, V))
+        return QSPEC_ERR_WORKSPACE;
+    if (!aligned(target_logits, 4) || !aligned(draft_logits, 4) || !aligned(draft_tokens, 4) ||
+        !aligned(u_accept, 4) || !aligned(u_resample, 4) || !aligned(accept_count, 4) ||
+        !aligned(out_tokens, 4) || !aligned(workspace, 16))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_verify_accept(mode, target_logits, draft_logits, draft_tokens,
+                                                 u_accept, u_resample, B, gamma, V, accept_count,
+                                                 out_tokens, workspace, as_stream(stream)));
+}
+
+QSPEC_EXPORT int qspec_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv,
+                                    const int32_t *start_pos, const int32_t *accept_count,
+                                    int32_t L, int32_t B, int32_t H, int32_t T, int32_t D,
+                                    int32_t gamma, qspec_stream_t stream) {
+    if (!cache || !verify_kv || !start_pos || !accept_count) return QSPEC_ERR_NULL;
+    if (L < 1 || B < 1 || H < 1 || T < 1 || D < 1 || gamma < 0 || gamma + 1 > T)
+        return QSPEC_ERR_SHAPE;
+    if ((long long)L * B * 2 * H * (gamma + 1) * D > kMaxElems) return QSPEC_ERR_SHAPE;
+    if (!aligned(cache, 2) || !aligned(verify_kv, 2) || !aligned(start_pos, 4) || !aligned(accept_count, 4))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_kv_overwrite(cache, verify_kv, start_pos, accept_count, L, B, H, T,
+                                                D, gamma, as_stream(stream)));
+}

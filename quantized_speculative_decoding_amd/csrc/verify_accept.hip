@@ -1,0 +1,426 @@
+// Verification of gamma draft tokens per sequence on gfx950.
+// (QSPEC notes, speculative-decoding background: greedy acceptance when the target's top-1 equals
+//  the draft; otherwise acceptance with probability min(1, p/q); the first rejection discards the
+//  rest; a correction token follows a rejection and an extra target token follows full
+//  acceptance.  QSPEC structure: the verifier produces gamma+1 distributions.)
+//
+// Logit rows are far larger than one workgroup's LDS (a 128256-wide fp32 row is 501 KB), so every
+// row is cut into chunks of VCHUNK logits and reduced in two deterministic stages:
+//   greedy:   k_argmax_partial (one workgroup per row chunk: max and its lowest index)
+//             -> k_greedy_accept (one thread per sequence: combine chunks in order, prefix match)
+//   sampling: k_softmax_partial (per row chunk: chunk max and sum of exp(l - max) in fp64)
+//             -> k_sample_accept (per sequence: row max / normalizer, u < p(d)/q(d) scan in fp64)
+//             -> k_residual_partial (per chunk of the last row: mass of max(0, p - q), or of p)
+//             -> k_residual_pick (per sequence: locate the chunk, scan it in fp64, pick the token)
+// Softmax normalizers, ratios and running sums are fp64; the exponentials are fp64 as well.
+#include <float.h>
+#include <limits.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qspec {
+
+constexpr int VCHUNK = 8192;     // logits per workgroup chunk
+constexpr int VT = 256;          // threads per workgroup
+constexpr int VSEG = VCHUNK / VT;
+
+static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct VerifyLayout {
+    int C;            // chunks per row
+    size_t gval, gidx;                                   // greedy partials
+    size_t pmax, psum, rowM, rowS, accA, resid, pmass;   // sampling partials
+    size_t total;
+};
+
+static VerifyLayout verify_layout(int mode, int B, int gamma, int V) {
+    VerifyLayout L = {};
+    L.C = (V + VCHUNK - 1) / VCHUNK;
+    const size_t Rt = (size_t)B * (gamma + 1);
+    size_t off = 0;
+    if (mode == 0) {
+        L.gval = off; off = align256(off + Rt * L.C * sizeof(float));
+        L.gidx = off; off = align256(off + Rt * L.C * sizeof(int));
+    } else {
+        const size_t R = Rt + (size_t)B * gamma;
+        L.pmax = off; off = align256(off + R * L.C * sizeof(float));
+        L.psum = off; off = align256(off + R * L.C * sizeof(double));
+        L.rowM = off; off = align256(off + R * sizeof(float));
+        L.rowS = off; off = align256(off + R * sizeof(double));
+        L.accA = off; off = align256(off + (size_t)B * sizeof(int));
+        L.resid = off; off = align256(off + (size_t)B * L.C * sizeof(double));
+        L.pmass = off; off = align256(off + (size_t)B * L.C * sizeof(double));
+    }
+    L.total = off;
+    return L;
+}
+
+size_t verify_workspace_bytes(int mode, int B, int gamma, int V) {
+    return verify_layout(mode, B, gamma, V).total;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Block reductions (4 waves).  Shuffle trees at a fixed lane give a run-to-run fixed order.
+
+struct ArgMax {
+    float v;
+    int i;
+};
+
+__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
+    return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+}
+
+__device__ ArgMax block_argmax(ArgMax a) {
+    __shared__ float sv[VT / kWave];
+    __shared__ int si[VT / kWave];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        ArgMax o = {__shfl_xor(a.v, off, kWave), __shfl_xor(a.i, off, kWave)};
+        a = better(a, o);
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { sv[w] = a.v; si[w] = a.i; }
+    __syncthreads();
+    ArgMax r = {sv[0], si[0]};
+    for (int k = 1; k < VT / kWave; ++k) r = better(r, ArgMax{sv[k], si[k]});
+    return r;
+}
+
+__device__ float block_max(float v) {
+    __shared__ float s[VT / kWave];
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = s[0];
+    for (int k = 1; k < VT / kWave; ++k) r = fmaxf(r, s[k]);
+    __syncthreads();
+    return r;
+}
+
+__device__ double block_sum(double v) {
+    __shared__ double s[VT / kWave];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_down(v, off, kWave);
+    if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double r = s[0];
+    for (int k = 1; k < VT / kWave; ++k) r += s[k];
+    __syncthreads();
+    return r;
+}
+
+// Visit the logits of [lo, hi) of one row, 16-byte vectors when the row allows it.
+template <typename F>
+__device__ __forceinline__ void for_chunk(const float *row, int lo, int hi, bool vec, F &&f) {
+    if (vec) {
+        for (int x = lo + 4 * (int)threadIdx.x; x < hi; x += 4 * VT) {
+            const uint4 q = load_stream16(row + x);
+            f(x, __uint_as_float(q.x));
+            f(x + 1, __uint_as_float(q.y));
+            f(x + 2, __uint_as_float(q.z));
+            f(x + 3, __uint_as_float(q.w));
+        }
+    } else {
+        for (int x = lo + (int)threadIdx.x; x < hi; x += VT) f(x, row[x]);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Greedy.
+
+__global__ void __launch_bounds__(VT)
+k_argmax_partial(const float *__restrict__ target, int V, int C, bool vec, float *__restrict__ gval,
+                 int *__restrict__ gidx) {
+    const int row = blockIdx.x / C, c = blockIdx.x % C;
+    const float *p = target + (size_t)row * V;
+    const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
+    ArgMax a = {-INFINITY, INT_MAX};
+    // each thread visits increasing x, so keeping strict improvements keeps the lowest index
+    for_chunk(p, lo, hi, vec, [&](int x, float v) {
+        if (a.i == INT_MAX || v > a.v) { a.v = v; a.i = x; }
+    });
+    a = block_argmax(a);
+    if (threadIdx.x == 0) {
+        gval[blockIdx.x] = a.v;
+        gidx[blockIdx.x] = a.i;
+    }
+}
+
+__global__ void k_greedy_accept(const float *__restrict__ gval, const int *__restrict__ gidx, int C,
+                                const int32_t *__restrict__ tokens, int B, int gamma, int V,
+                                int32_t *__restrict__ accept, int32_t *__restrict__ out) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    int A = 0;
+    int top = 0;
+    for (int j = 0; j <= gamma; ++j) {
+        const size_t base = ((size_t)b * (gamma + 1) + j) * C;
+        ArgMax r = {gval[base], gidx[base]};
+        for (int c = 1; c < C; ++c) r = better(r, ArgMax{gval[base + c], gidx[base + c]});
+        top = r.i;
+        if (j == gamma) break;
+        const int d = tokens[(size_t)b * gamma + j];
+        if (d < 0 || d >= V || d != top) break;
+        ++A;
+    }
+    accept[b] = A;
+    for (int j = 0; j <= gamma; ++j) {
+        int t = -1;
+        if (j < A) t = tokens[(size_t)b * gamma + j];
+        else if (j == A) t = top;
+        out[(size_t)b * (gamma + 1) + j] = t;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Speculative sampling.
+
+__device__ __forceinline__ const float *logit_row(const float *target, const float *draft, int B,
+                                                  int gamma, int V, long long row) {
+    const long long Rt = (long long)B * (gamma + 1);
+    return row < Rt ? target + (size_t)row * V : draft + (size_t)(row - Rt) * V;
+}
+
+__global__ void __launch_bounds__(VT)
+k_softmax_partial(const float *__restrict__ target, const float *__restrict__ draft, int B, int gamma,
+                  int V, int C, bool vec, float *__restrict__ pmax, double *__restrict__ psum) {
+    const long long row = blockIdx.x / C;
+    const int c = blockIdx.x % C;
+    const float *p = logit_row(target, draft, B, gamma, V, row);
+    const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
+    float m = -INFINITY;
+    for_chunk(p, lo, hi, vec, [&](int, float v) { m = fmaxf(m, v); });
+    m = block_max(m);
+    double s = 0.0;
+    const double md = (double)m;
+    for_chunk(p, lo, hi, vec, [&](int, float v) { s += exp((double)v - md); });
+    s = block_sum(s);
+    if (threadIdx.x == 0) {
+        pmax[blockIdx.x] = m;
+        psum[blockIdx.x] = s;
+    }
+}
+
+__global__ void k_sample_accept(const float *__restrict__ target, const float *__restrict__ draft,
+                                const int32_t *__restrict__ tokens, const float *__restrict__ u,
+                                int B, int gamma, int V, int C, const float *__restrict__ pmax,
+                                const double *__restrict__ psum, float *__restrict__ rowM,
+                                double *__restrict__ rowS, int *__restrict__ accA,
+                                int32_t *__restrict__ accept, int32_t *__restrict__ out) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const long long Rt = (long long)B * (gamma + 1);
+    // combine the chunk statistics of this sequence's rows, in chunk order
+    for (int side = 0; side < 2; ++side) {
+        const int nrows = side == 0 ? gamma + 1 : gamma;
+        for (int j = 0; j < nrows; ++j) {
+            const long long row = side == 0 ? (long long)b * (gamma + 1) + j : Rt + (long long)b * gamma + j;
+            const size_t base = (size_t)row * C;
+            float M = pmax[base];
+            for (int c = 1; c < C; ++c) M = fmaxf(M, pmax[base + c]);
+            double S = 0.0;
+            for (int c = 0; c < C; ++c) S += psum[base + c] * exp((double)pmax[base + c] - (double)M);
+            rowM[row] = M;
+            rowS[row] = S;
+        }
+    }
+    int A = 0;
+    while (A < gamma) {
+        const int d = tokens[(size_t)b * gamma + A];
+        if (d < 0 || d >= V) break;
+        const long long rt = (long long)b * (gamma + 1) + A;
+        const long long rd = Rt + (long long)b * gamma + A;
+        const double p = exp((double)target[(size_t)rt * V + d] - (double)rowM[rt]) / rowS[rt];
+        const double q = exp((double)draft[(size_t)(rd - Rt) * V + d] - (double)rowM[rd]) / rowS[rd];
+        if (!((double)u[(size_t)b * gamma + A] < p / q)) break;
+        ++A;
+    }
+    accA[b] = A;
+    accept[b] = A;
+    for (int j = 0; j <= gamma; ++j)
+        if (j != A) out[(size_t)b * (gamma + 1) + j] = j < A ? tokens[(size_t)b * gamma + j] : -1;
+}
+
+// Residual (or target) mass at one logit of the last committed row.
+struct ResidRow {
+    const float *t;  // target row A
+    const float *d;  // draft row A, or nullptr for the extra token (A == gamma)
+    double Mt, St, Md, Sd;
+    __device__ __forceinline__ double p(int x) const { return exp((double)t[x] - Mt) / St; }
+    __device__ __forceinline__ double r(int x) const {
+        const double pv = p(x);
+        if (!d) return pv;
+        const double dv = pv - exp((double)d[x] - Md) / Sd;
+        return dv > 0.0 ? dv : 0.0;
+    }
+};
+
+__device__ __forceinline__ ResidRow resid_row(const float *target, const float *draft, int B, int gamma,
+                                              int V, int b, int A, const float *rowM, const double *rowS) {
+    const long long Rt = (long long)B * (gamma + 1);
+    const long long rt = (long long)b * (gamma + 1) + A;
+    ResidRow R;
+    R.t = target + (size_t)rt * V;
+    R.Mt = rowM[rt];
+    R.St = rowS[rt];
+    if (A < gamma) {
+        const long long rd = Rt + (long long)b * gamma + A;
+        R.d = draft + (size_t)(rd - Rt) * V;
+        R.Md = rowM[rd];
+        R.Sd = rowS[rd];
+    } else {
+        R.d = nullptr;
+        R.Md = 0.0;
+        R.Sd = 1.0;
+    }
+    return R;
+}
+
+__global__ void __launch_bounds__(VT)
+k_residual_partial(const float *__restrict__ target, const float *__restrict__ draft, int B, int gamma,
+                   int V, int C, const float *__restrict__ rowM, const double *__restrict__ rowS,
+                   const int *__restrict__ accA, double *__restrict__ resid, double *__restrict__ pmass) {
+    const int b = blockIdx.x / C, c = blockIdx.x % C;
+    const ResidRow R = resid_row(target, draft, B, gamma, V, b, accA[b], rowM, rowS);
+    const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
+    double sr = 0.0, sp = 0.0;
+    for (int x = lo + (int)threadIdx.x; x < hi; x += VT) {
+        sr += R.r(x);
+        sp += R.p(x);
+    }
+    sr = block_sum(sr);
+    sp = block_sum(sp);
+    if (threadIdx.x == 0) {
+        resid[blockIdx.x] = sr;
+        pmass[blockIdx.x] = sp;
+    }
+}
+
+__global__ void __launch_bounds__(VT)
+k_residual_pick(const float *__restrict__ target, const float *__restrict__ draft,
+                const float *__restrict__ v, int B, int gamma, int V, int C,
+                const float *__restrict__ rowM, const double *__restrict__ rowS,
+                const int *__restrict__ accA, const double *__restrict__ resid,
+                const double *__restrict__ pmass, int32_t *__restrict__ out) {
+    __shared__ double seg[VT];
+    __shared__ int s_chunk, s_fallback, s_usep, s_tok;
+    __shared__ double s_thr;
+    const int b = blockIdx.x;
+    const int A = accA[b];
+    ResidRow R = resid_row(target, draft, B, gamma, V, b, A, rowM, rowS);
+    if (threadIdx.x == 0) {
+        const double *part = resid + (size_t)b * C;
+        double tot = 0.0;
+        for (int c = 0; c < C; ++c) tot += part[c];
+        int usep = 0;
+        if (!(tot > 0.0)) {
+            usep = 1;
+            part = pmass + (size_t)b * C;
+            tot = 0.0;
+            for (int c = 0; c < C; ++c) tot += part[c];
+        }
+        const double thr = (double)v[b] * tot;
+        double run = 0.0;
+        int chunk = -1;
+        double before = 0.0;
+        for (int c = 0; c < C; ++c) {
+            before = run;
+            run += part[c];
+            if (run > thr) { chunk = c; break; }
+        }
+        int fallback = 0;
+        if (chunk < 0) {
+            fallback = 1;
+            for (int c = C - 1; c >= 0; --c)
+                if (part[c] > 0.0) { chunk = c; break; }
+            if (chunk < 0) chunk = C - 1;
+        }
+        s_chunk = chunk;
+        s_fallback = fallback;
+        s_usep = usep;
+        s_thr = thr - before;
+        s_tok = -1;
+    }
+    __syncthreads();
+    if (s_usep) R.d = nullptr;
+    const int lo = s_chunk * VCHUNK, hi = min(V, lo + VCHUNK);
+    const int x0 = lo + (int)threadIdx.x * VSEG, x1 = min(hi, x0 + VSEG);
+    double mine = 0.0;
+    for (int x = x0; x < x1; ++x) mine += R.r(x);
+    seg[threadIdx.x] = mine;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        // the segment holding the threshold, then a sequential scan inside it
+        int tok = -1;
+        if (!s_fallback) {
+            double run = 0.0;
+            for (int t = 0; t < VT && tok < 0; ++t) {
+                if (run + seg[t] > s_thr) {
+                    const int a = lo + t * VSEG, e = min(hi, a + VSEG);
+                    double rr = run;
+                    for (int x = a; x < e; ++x) {
+                        rr += R.r(x);
+                        if (rr > s_thr) { tok = x; break; }
+                    }
+                    if (tok < 0)   // rounding left the threshold at the segment's end
+                        for (int x = e - 1; x >= a; --x)
+                            if (R.r(x) > 0.0) { tok = x; break; }
+                    if (tok < 0) tok = min(a, hi - 1);
+                }
+                run += seg[t];
+            }
+        }
+        if (tok < 0) {             // no crossing: the last logit of positive mass in the chunk
+            for (int x = hi - 1; x >= lo; --x)
+                if (R.r(x) > 0.0) { tok = x; break; }
+            if (tok < 0) tok = hi - 1;
+        }
+        s_tok = tok;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) out[(size_t)b * (gamma + 1) + A] = s_tok;
+}
+
+// ---------------------------------------------------------------------------------------------
+
+hipError_t launch_verify_accept(int mode, const float *target, const float *draft,
+                                const int32_t *tokens, const float *u_accept, const float *u_resample,
+                                int B, int gamma, int V, int32_t *accept, int32_t *out, void *ws,
+                                hipStream_t st) {
+    const VerifyLayout L = verify_layout(mode, B, gamma, V);
+    char *w = (char *)ws;
+    const int C = L.C;
+    const bool vec_t = (V % 4 == 0) && ((uintptr_t)target % 16 == 0);
+    const long long Rt = (long long)B * (gamma + 1);
+    if (mode == 0) {
+        float *gval = (float *)(w + L.gval);
+        int *gidx = (int *)(w + L.gidx);
+        hipLaunchKernelGGL(k_argmax_partial, dim3((unsigned)(Rt * C)), dim3(VT), 0, st, target, V, C,
+                           vec_t, gval, gidx);
+        hipLaunchKernelGGL(k_greedy_accept, dim3((B + 63) / 64), dim3(64), 0, st, gval, gidx, C, tokens,
+                           B, gamma, V, accept, out);
+        return hipGetLastError();
+    }
+    const bool vec = vec_t && (gamma == 0 || (uintptr_t)draft % 16 == 0);
+    const long long R = Rt + (long long)B * gamma;
+    float *pmax = (float *)(w + L.pmax);
+    double *psum = (double *)(w + L.psum);
+    float *rowM = (float *)(w + L.rowM);
+    double *rowS = (double *)(w + L.rowS);
+    int *accA = (int *)(w + L.accA);
+    double *resid = (double *)(w + L.resid);
+    double *pmass = (double *)(w + L.pmass);
+    hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)(R * C)), dim3(VT), 0, st, target, draft, B,
+                       gamma, V, C, vec, pmax, psum);
+    hipLaunchKernelGGL(k_sample_accept, dim3((B + 63) / 64), dim3(64), 0, st, target, draft, tokens,
+                       u_accept, B, gamma, V, C, pmax, psum, rowM, rowS, accA, accept, out);
+    hipLaunchKernelGGL(k_residual_partial, dim3((unsigned)((long long)B * C)), dim3(VT), 0, st, target,
+                       draft, B, gamma, V, C, rowM, rowS, accA, resid, pmass);
+    hipLaunchKernelGGL(k_residual_pick, dim3(B), dim3(VT), 0, st, target, draft, u_resample, B, gamma, V,
+                       C, rowM, rowS, accA, resid, pmass, out);
+    return hipGetLastError();
+}
+
+}  // namespace qspec

@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports exactly the
+entry points include/qspec.h declares, and rejects invalid arguments with the documented
+status before launching anything.  The binding rejects host tensors."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import quantized_speculative_decoding_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qspec.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP, ERR_WS, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int|size_t)\s*(qspec_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "qspec_status_string", "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16",
+        "qspec_verify_workspace_bytes", "qspec_verify_accept", "qspec_kv_overwrite"])
+
+
+def test_library_exports_every_declared_symbol_and_nothing_else():
+    L = q.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r"\bT (qspec_\w+)", out)))
+    assert exported == declared_functions()
+
+
+def test_status_strings():
+    L = q.lib()
+    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP, ERR_WS, ERR_ALIGN):
+        assert L.qspec_status_string(s)
+    assert L.qspec_status_string(-99) == b"unknown status"
+
+
+def test_quantize_act_validation():
+    L = q.lib()
+    assert L.qspec_quantize_act(None, 1, 128, FAKE, FAKE, None) == ERR_NULL
+    assert L.qspec_quantize_act(FAKE, 0, 128, FAKE, FAKE, None) == ERR_SHAPE
+    assert L.qspec_quantize_act(FAKE, 1, 100, FAKE, FAKE, None) == ERR_SHAPE
+    assert L.qspec_quantize_act(FAKE, 1, 0, FAKE, FAKE, None) == ERR_SHAPE
+
+
+def test_gemm_validation():
+    L = q.lib()
+    args = [FAKE, FAKE, 4, FAKE, FAKE, FAKE, 256, 64, FAKE, 0, None, None]
+    for i in (0, 1, 3, 4, 5, 8):
+        bad = list(args)
+        bad[i] = None
+        assert L.qspec_gemm_w4a4(*bad) == ERR_NULL, i
+    for (M, K, N) in [(0, 256, 64), (4, 200, 64), (4, 256, 0), (-1, 256, 64), (4, 64, 64)]:
+        assert L.qspec_gemm_w4a4(FAKE, FAKE, M, FAKE, FAKE, FAKE, K, N, FAKE, 0, None, None) == ERR_SHAPE
+    assert L.qspec_gemm_w4a4(FAKE, FAKE, 4, FAKE, FAKE, FAKE, 256, 64, FAKE, 7, None, None) == ERR_UNSUPPORTED
+    assert L.qspec_gemm_w4a16(None, 4, FAKE, FAKE, FAKE, 256, 64, FAKE, 0, None) == ERR_NULL
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, FAKE, 129, 64, FAKE, 0, None) == ERR_SHAPE
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, FAKE, 256, 64, FAKE, 2, None) == ERR_UNSUPPORTED
+
+
+def test_verify_validation_and_workspace_sizes():
+    L = q.lib()
+    ws = L.qspec_verify_workspace_bytes(0, 32, 4, 128256)
+    assert ws > 0 and L.qspec_verify_workspace_bytes(1, 32, 4, 128256) > ws
+    assert L.qspec_verify_workspace_bytes(2, 1, 1, 10) == 0
+    assert L.qspec_verify_workspace_bytes(0, 0, 1, 10) == 0
+    assert L.qspec_verify_workspace_bytes(0, 1, -1, 10) == 0
+    # greedy needs target, tokens (gamma > 0), outputs
+    assert L.qspec_verify_accept(0, None, None, FAKE, None, None, 1, 4, 100, FAKE, FAKE, FAKE, 1 << 20, None) == ERR_NULL
+    assert L.qspec_verify_accept(0, FAKE, None, None, None, None, 1, 4, 100, FAKE, FAKE, FAKE, 1 << 20, None) == ERR_NULL
+    # sampling additionally needs draft logits, u_accept and u_resample
+    assert L.qspec_verify_accept(1, FAKE, None, FAKE, FAKE, FAKE, 1, 4, 100, FAKE, FAKE, FAKE, 1 << 20, None) == ERR_NULL
+    assert L.qspec_verify_accept(1, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 100, FAKE, FAKE, FAKE, 1 << 20, None) == ERR_NULL
+    assert L.qspec_verify_accept(3, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 100, FAKE, FAKE, FAKE, 1 << 20, None) == ERR_UNSUPPORTED
+    assert L.qspec_verify_accept(0, FAKE, None, FAKE, None, None, 0, 4, 100, FAKE, FAKE, FAKE, 1 << 20, None) == ERR_SHAPE
+    assert L.qspec_verify_accept(0, FAKE, None, FAKE, None, None, 1, 4, 0, FAKE, FAKE, FAKE, 1 << 20, None) == ERR_SHAPE
+    need = L.qspec_verify_workspace_bytes(0, 2, 3, 5000)
+    assert L.qspec_verify_accept(0, FAKE, None, FAKE, None, None, 2, 3, 5000, FAKE, FAKE, FAKE, need - 1, None) == ERR_WS
+    assert L.qspec_verify_accept(0, FAKE, None, FAKE, None, None, 2, 3, 5000, FAKE, FAKE, None, need, None) == ERR_WS
+
+
+def test_kv_overwrite_validation():
+    L = q.lib()
+    assert L.qspec_kv_overwrite(None, FAKE, FAKE, FAKE, 1, 1, 1, 8, 8, 2, None) == ERR_NULL
+    assert L.qspec_kv_overwrite(FAKE, FAKE, FAKE, None, 1, 1, 1, 8, 8, 2, None) == ERR_NULL
+    for (Lx, B, H, T, D, g) in [(0, 1, 1, 8, 8, 2), (1, 1, 1, 8, 0, 2), (1, 1, 1, 2, 8, 2), (1, 1, 1, 8, 8, -1)]:
+        assert L.qspec_kv_overwrite(FAKE, FAKE, FAKE, FAKE, Lx, B, H, T, D, g, None) == ERR_SHAPE
+
+
+def test_binding_rejects_host_tensors():
+    x = torch.zeros((2, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        q.qspec_quantize_act(x, torch.zeros((2, 128), dtype=torch.uint8), torch.zeros((2, 2)))
+
+
+def test_alignment_validation():
+    L = q.lib()
+    odd = ctypes.c_void_p(0x1001)
+    assert L.qspec_quantize_act(odd, 1, 128, FAKE, FAKE, None) == ERR_ALIGN
+    assert L.qspec_gemm_w4a16(FAKE, 4, ctypes.c_void_p(0x1008), FAKE, FAKE, 256, 64, FAKE, 0, None) == ERR_ALIGN
+    assert L.qspec_gemm_w4a4(FAKE, odd, 4, FAKE, FAKE, FAKE, 256, 64, FAKE, 1, None, None) == ERR_ALIGN
+    need = L.qspec_verify_workspace_bytes(0, 2, 3, 5000)
+    assert L.qspec_verify_accept(0, FAKE, None, FAKE, None, None, 2, 3, 5000, FAKE, FAKE,
+                                 ctypes.c_void_p(0x1004), need, None) == ERR_ALIGN
+    assert L.qspec_kv_overwrite(odd, FAKE, FAKE, FAKE, 1, 1, 1, 8, 8, 2, None) == ERR_ALIGN

@@ -1,0 +1,203 @@
+"""GPU parity of the activation quantizer, the W4A16 verify layer and the W4A4 draft layer
+against the CPU oracle, called through the C ABI.
+
+Bit-exact: activation codes and scales, the W4A4 group dot products, W_hat (through one-hot
+activations).  Tolerance: final outputs (bf16: abs 1e-3 + rel 1e-2; f32 ten times tighter).
+Small shapes span several tiles with ragged tails; the full workload shapes are checked on
+sampled columns computed by the oracle one by one."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_speculative_decoding_amd as q
+import synthetic_inputs as si
+from gpu_helpers import DEV, assert_close, bf16_dev, cu, host_bits16, host_f64, note, weights_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_quant(x_bits):
+    M, K = x_bits.shape
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((M, K // 128), dtype=torch.float32, device=DEV)
+    q.qspec_quantize_act(bf16_dev(x_bits), codes, scales)
+    return codes, scales
+
+
+def run_w4a16(x_bits, w, out=torch.bfloat16, wdev=None):
+    M = x_bits.shape[0]
+    wc, ws, wz = wdev if wdev is not None else weights_dev(w)
+    y = torch.empty((M, w["N"]), dtype=out, device=DEV)
+    q.qspec_gemm_w4a16(bf16_dev(x_bits), wc, ws, wz, y)
+    return y
+
+
+# ---------------------------------------------------------------- quantizer
+
+@pytest.mark.parametrize("M,K", [(1, 128), (5, 384), (16, 4096), (7, 14336), (3, 28672), (256, 8192)])
+def test_quantize_act_bit_exact(M, K):
+    note(f"quantize_act M={M} K={K}")
+    x = si.activations(M, K, seed=M + K)
+    codes, scales = run_quant(x)
+    oc, osc = oracle.quantize_act(x)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+
+
+def test_quantize_act_edge_values():
+    note("quantize_act edge values")
+    K = 512
+    x = np.zeros((4, K), np.float32)
+    x[1, :128] = np.linspace(-7, 7, 128)                      # ties and exact steps (s_a = 1)
+    x[1, 128:256] = [0.5, 1.5, 2.5, -2.5, 7.0] + [0.0] * 123
+    x[2, :] = si.rng(5).standard_normal(K) * 1e-30           # tiny but normal in fp32
+    x[3, :] = si.rng(6).standard_normal(K) * 1e30
+    xb = si.f32_to_bf16_bits(x)
+    codes, scales = run_quant(xb)
+    oc, osc = oracle.quantize_act(xb)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    assert np.all(codes.cpu().numpy()[0] == 0) and np.all(scales.cpu().numpy()[0] == 0)
+
+
+# ---------------------------------------------------------------- W4A16
+
+SMALL_W4A16 = [(1, 128, 16), (5, 512, 512), (3, 384, 40), (17, 640, 100), (20, 256, 72),
+               (33, 384, 52), (48, 256, 36), (64, 128, 16), (80, 512, 144), (81, 256, 130),
+               (200, 384, 260), (130, 640, 7)]
+
+
+@pytest.mark.parametrize("M,K,N", SMALL_W4A16)
+@pytest.mark.parametrize("out", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_w4a16_small(M, K, N, out):
+    note(f"gemm_w4a16 M={M} K={K} N={N} out={out}")
+    w = si.weights(K, N, seed=M * 7 + N)
+    x = si.activations(M, K, seed=M + 1000)
+    y = run_w4a16(x, w, out)
+    ref = oracle.gemm_w4a16(x, w["codes"], w["scales"], w["zeros"])
+    assert_close(host_f64(y), ref, out == torch.bfloat16, f"w4a16 {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M", [16, 96])
+def test_w4a16_one_hot_rows_reproduce_dequantized_weights_exactly(M):
+    """x = e_k gives y = W_hat[k] with a single exact product: checks the dequantization bits."""
+    K, N = 512, 100
+    note(f"gemm_w4a16 one-hot M={M}")
+    w = si.weights(K, N, seed=3)
+    ks = si.rng(M).choice(K, size=M, replace=False)
+    x = np.zeros((M, K), np.float32)
+    x[np.arange(M), ks] = 1.0
+    y = run_w4a16(si.f32_to_bf16_bits(x), w, torch.float32)
+    what = oracle.dequant(w["codes"], w["scales"], w["zeros"])            # u16 [N][K]
+    ref = np.vectorize(oracle.bf16_to_double)(what[:, ks].T)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+def test_w4a16_rows_do_not_depend_on_batch():
+    """Every M in the skinny range reduces a row in the same order: bitwise-equal rows."""
+    K, N = 1024, 200
+    note("gemm_w4a16 batch invariance")
+    w = si.weights(K, N, seed=4)
+    wdev = weights_dev(w)
+    x = si.activations(80, K, seed=4)
+    full = {M: run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy() for M in (1, 5, 17, 20, 33, 80)}
+    for M, y in full.items():
+        assert np.array_equal(y, full[80][:M]), M
+
+
+FULL_W4A16 = [
+    # Llama-3-8B-shaped projections, verify at M = 5B for B in 1, 4, 16
+    ("llama8b.qkv", 4096, 6144, 80), ("llama8b.o", 4096, 4096, 20), ("llama8b.gate_up", 4096, 28672, 5),
+    ("llama8b.down", 14336, 4096, 80),
+    # Qwen2.5-7B-shaped layer at gamma + 1 in 3, 5, 9, 17; fp32 logits for the head
+    ("qwen7b.qkv", 3584, 4608, 3), ("qwen7b.gate_up", 3584, 37888, 9), ("qwen7b.down", 18944, 3584, 17),
+    ("qwen7b.lm_head", 3584, 152064, 5),
+    # 70B-shaped FFN, compute-bound verify at 256 x 5 tokens
+    ("llama70b.gate_up", 8192, 57344, 1280), ("llama70b.down", 28672, 8192, 1280),
+]
+
+
+@pytest.mark.parametrize("name,K,N,M", FULL_W4A16, ids=[c[0] + f".M{c[3]}" for c in FULL_W4A16])
+def test_w4a16_full_shapes_sampled_columns(name, K, N, M):
+    note(f"gemm_w4a16 full {name} M={M} K={K} N={N}")
+    w = si.weights(K, N, seed=zlib.crc32(name.encode()) % 1000)
+    x = si.activations(M, K, seed=M)
+    out = torch.float32 if name.endswith("lm_head") else torch.bfloat16
+    y = run_w4a16(x, w, out)
+    cols = np.sort(si.rng(N).choice(N, size=24, replace=False))
+    rows = np.arange(M) if M <= 80 else np.sort(si.rng(M).choice(M, size=64, replace=False))
+    ref = oracle.gemm_w4a16(x[rows], w["codes"][cols], w["scales"][cols], w["zeros"][cols])
+    got = host_f64(y)[np.ix_(rows, cols)]
+    assert_close(got, ref, out == torch.bfloat16, name)
+
+
+# ---------------------------------------------------------------- W4A4
+
+SMALL_W4A4 = [(1, 128, 16), (1, 512, 512), (4, 384, 40), (16, 640, 100), (5, 256, 7),
+              (17, 384, 52), (33, 256, 36), (64, 128, 48), (65, 256, 130), (256, 512, 260), (100, 384, 16)]
+
+
+@pytest.mark.parametrize("M,K,N", SMALL_W4A4)
+def test_w4a4_small_exact_dots_and_outputs(M, K, N):
+    note(f"gemm_w4a4 M={M} K={K} N={N}")
+    w = si.weights(K, N, seed=M * 3 + N)
+    x = si.activations(M, K, seed=M + 2000)
+    codes, scales = run_quant(x)
+    oc, osc = oracle.quantize_act(x)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    wc, ws, wz = weights_dev(w)
+    dots = torch.full((K // 128, M, N), -(2 ** 31), dtype=torch.int32, device=DEV)
+    for out in (torch.bfloat16, torch.float32):
+        y = torch.empty((M, N), dtype=out, device=DEV)
+        q.qspec_gemm_w4a4(codes, scales, wc, ws, wz, y, group_dots=dots)
+        ref, D = oracle.gemm_w4a4(oc, osc, w["codes"], w["scales"], w["zeros"])
+        assert np.array_equal(dots.cpu().numpy().astype(np.int64), D)
+        assert_close(host_f64(y), ref, out == torch.bfloat16, f"w4a4 {M}x{K}x{N}")
+        # the diagnostic output does not change y
+        y2 = torch.empty_like(y)
+        q.qspec_gemm_w4a4(codes, scales, wc, ws, wz, y2)
+        assert torch.equal(y, y2)
+
+
+def test_w4a4_rows_do_not_depend_on_batch():
+    K, N = 1024, 96
+    note("gemm_w4a4 batch invariance")
+    w = si.weights(K, N, seed=8)
+    wc, ws, wz = weights_dev(w)
+    codes, scales = run_quant(si.activations(64, K, seed=8))
+    ys = {}
+    for M in (1, 4, 16, 33, 64):
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        q.qspec_gemm_w4a4(codes[:M].contiguous(), scales[:M].contiguous(), wc, ws, wz, y)
+        ys[M] = y.cpu().numpy()
+    for M in (1, 4, 16):
+        assert np.array_equal(ys[M], ys[16][:M])
+    for M in (33,):
+        assert np.array_equal(ys[M], ys[64][:M])
+
+
+FULL_W4A4 = [
+    ("llama8b.qkv", 4096, 6144, 16), ("llama8b.o", 4096, 4096, 4), ("llama8b.gate_up", 4096, 28672, 1),
+    ("llama8b.down", 14336, 4096, 16), ("qwen7b.gate_up", 3584, 37888, 1), ("qwen7b.lm_head", 3584, 152064, 1),
+    ("llama70b.gate_up", 8192, 57344, 256), ("llama70b.down", 28672, 8192, 256),
+]
+
+
+@pytest.mark.parametrize("name,K,N,M", FULL_W4A4, ids=[c[0] + f".M{c[3]}" for c in FULL_W4A4])
+def test_w4a4_full_shapes_sampled_columns(name, K, N, M):
+    note(f"gemm_w4a4 full {name} M={M} K={K} N={N}")
+    w = si.weights(K, N, seed=zlib.crc32(name.encode()) % 1000 + 1)
+    x = si.activations(M, K, seed=M + 7)
+    codes, scales = run_quant(x)
+    oc, osc = oracle.quantize_act(x)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    out = torch.float32 if name.endswith("lm_head") else torch.bfloat16
+    wc, ws, wz = weights_dev(w)
+    y = torch.empty((M, N), dtype=out, device=DEV)
+    q.qspec_gemm_w4a4(codes, scales, wc, ws, wz, y)
+    cols = np.sort(si.rng(N + 1).choice(N, size=24, replace=False))
+    ref, _ = oracle.gemm_w4a4(oc, osc, w["codes"][cols], w["scales"][cols], w["zeros"][cols], want_dots=False)
+    assert_close(host_f64(y)[:, cols], ref, out == torch.bfloat16, name)
