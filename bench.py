@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the shared-INT4 speculative-decoding hot path on one MI355X.
+
+One step = one QSPEC round over the projections of a Llama-3-8B-shaped model (32 layers of
+qkv 4096->6144, o 4096->4096, gate+up 4096->2x14336, down 14336->4096, each layer with its
+own shared INT4 group-128 weights: 3.65 GB, far beyond the 256 MB last-level cache), batch B
+(default 16) and gamma = 4:
+  draft   gamma x (per layer and projection: qspec_quantize_act + qspec_gemm_w4a4 at M = B)
+  verify  per layer and projection: qspec_gemm_w4a16 at M = B (gamma + 1)
+  accept  qspec_verify_accept (speculative sampling) over a 128256-word vocabulary
+  commit  qspec_kv_overwrite of the accepted rows in a 32-layer x 8-head x 4096 x 128 bf16 cache
+Attention, norms, activations and the vocabulary projection are not on this path; every
+projection reads fixed synthetic activations, so the launches of one phase are independent.
+
+Each phase is captured once as a HIP graph and replayed; HIP events between phase replays
+time each phase, so the per-launch average of the dominant kernel includes only the graph's
+own inter-kernel gaps.  The value is verify tokens/s: B (gamma + 1) positions per round over
+the measured round time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "shared-INT4 GEMM HBM TB/s (% of peak) at M=1..16; verify tokens/s at gamma=4"
+HBM_PEAK_GBS = 8000.0
+GROUP = 128
+VOCAB = 128256
+KV_HEADS, HEAD_DIM, CONTEXT = 8, 128, 4096
+
+
+def w4_bytes(K, N):
+    """Shared weight store: 4-bit codes + one 4-byte meta word (fp16 scale, zero) per 128-group."""
+    return K * N // 2 + 4 * N * (K // GROUP)
+
+
+def w4a4_alg_bytes(M, K, N):
+    return w4_bytes(K, N) + M * K // 2 + 4 * M * (K // GROUP) + 2 * M * N
+
+
+def w4a16_alg_bytes(M, K, N):
+    return w4_bytes(K, N) + 2 * M * K + 2 * M * N
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--gamma", type=int, default=4)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this size (for counter scaling)")
+    return ap.parse_args()
+
+
+class Round:
+    """Device buffers and per-phase launch closures of one QSPEC round."""
+
+    def __init__(self, args, dev):
+        import torch
+
+        import quantized_speculative_decoding_amd as q
+        import synthetic_inputs as si
+
+        self.q, self.torch = q, torch
+        B, g, L = args.batch, args.gamma, args.layers
+        self.B, self.gamma, self.L = B, g, L
+        self.projs = list(si.LLAMA3_8B_PROJ.items())
+        self.weights = [[si.weights_device(K, N, seed=l * 8 + i, device=dev) for i, (_, (K, N)) in
+                         enumerate(self.projs)] for l in range(L)]
+        self.x_draft = [si.activations_device(B, K, seed=10 + i, device=dev) for i, (_, (K, N)) in enumerate(self.projs)]
+        self.x_verify = [si.activations_device(B * (g + 1), K, seed=20 + i, device=dev)
+                         for i, (_, (K, N)) in enumerate(self.projs)]
+        # activation codes / scales and outputs per (layer, projection): distinct buffers
+        self.codes = [[torch.empty((B, K // 2), dtype=torch.uint8, device=dev) for _, (K, N) in self.projs]
+                      for _ in range(L)]
+        self.ascales = [[torch.empty((B, K // GROUP), dtype=torch.float32, device=dev) for _, (K, N) in self.projs]
+                        for _ in range(L)]
+        self.y_draft = [torch.empty((B, N), dtype=torch.bfloat16, device=dev) for _, (K, N) in self.projs]
+        self.y_verify = [torch.empty((B * (g + 1), N), dtype=torch.bfloat16, device=dev) for _, (K, N) in self.projs]
+        # verification: 4 rotating logit sets (4 x 74 MB at B = 16) so no replay reads a cached set
+        self.n_logit_sets = 4
+        self.logits = []
+        for s in range(self.n_logit_sets):
+            t, d = si.logits_device(B, g, VOCAB, seed=s, device=dev)
+            toks = si.draft_tokens_sampled_device(d, seed=s)
+            self.logits.append((t, d, toks, si.uniforms_device((B, g), seed=s, device=dev),
+                                si.uniforms_device((B,), seed=100 + s, device=dev)))
+        self.accept = torch.zeros((B,), dtype=torch.int32, device=dev)
+        self.out_tokens = torch.zeros((B, g + 1), dtype=torch.int32, device=dev)
+        self.ws = torch.empty((q.qspec_verify_workspace_bytes(q.QSPEC_SAMPLE, B, g, VOCAB),), dtype=torch.uint8,
+                              device=dev)
+        # KV cache and the verifier's staging rows
+        self.cache = torch.zeros((L, B, 2, KV_HEADS, CONTEXT, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.stage = torch.randn((L, B, 2, KV_HEADS, g + 1, HEAD_DIM), device=dev).to(torch.bfloat16)
+        self.start = torch.from_numpy(si.start_positions(B, CONTEXT, g, seed=0)).to(dev)
+
+    # ---- phases
+    def quant(self):
+        for l in range(self.L):
+            for i in range(len(self.projs)):
+                self.q.qspec_quantize_act(self.x_draft[i], self.codes[l][i], self.ascales[l][i])
+
+    def draft_gemm(self):
+        for l in range(self.L):
+            for i in range(len(self.projs)):
+                wc, wm = self.weights[l][i]
+                self.q.qspec_gemm_w4a4(self.codes[l][i], self.ascales[l][i], wc, wm, self.y_draft[i])
+
+    def verify_gemm(self):
+        for l in range(self.L):
+            for i in range(len(self.projs)):
+                wc, wm = self.weights[l][i]
+                self.q.qspec_gemm_w4a16(self.x_verify[i], wc, wm, self.y_verify[i])
+
+    def accept_phase(self, s):
+        t, d, toks, u, v = self.logits[s]
+        self.q.qspec_verify_accept(self.q.QSPEC_SAMPLE, t, d, toks, u, v, self.accept, self.out_tokens, self.ws)
+
+    def commit(self):
+        self.q.qspec_kv_overwrite(self.cache, self.stage, self.start, self.accept)
+
+    # ---- algorithmic work per phase
+    def draft_gemm_bytes(self):
+        return self.L * sum(w4a4_alg_bytes(self.B, K, N) for _, (K, N) in self.projs)
+
+    def verify_gemm_bytes(self):
+        return self.L * sum(w4a16_alg_bytes(self.B * (self.gamma + 1), K, N) for _, (K, N) in self.projs)
+
+    def launches_per_gemm_phase(self):
+        return self.L * len(self.projs)
+
+
+def capture(fn, torch):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def gpu_leg(args):
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    R = Round(args, dev)
+    torch.cuda.synchronize()
+
+    # eager reference outputs, then the captured phases
+    R.quant(); R.draft_gemm(); R.verify_gemm(); R.accept_phase(0); R.commit()
+    torch.cuda.synchronize()
+    ref = (R.y_draft[2].clone(), R.y_verify[3].clone(), R.accept.clone(), R.out_tokens.clone())
+    g_quant = capture(R.quant, torch)
+    g_draft = capture(R.draft_gemm, torch)
+    g_verify = capture(R.verify_gemm, torch)
+    g_accept = [capture(lambda s=s: R.accept_phase(s), torch) for s in range(R.n_logit_sets)]
+    g_commit = capture(R.commit, torch)
+
+    phases = ["quantize_act", "gemm_w4a4", "gemm_w4a16", "verify_accept", "kv_overwrite"]
+    n_ev = R.gamma * 2 + 4
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+
+    def step(i, ev):
+        k = 0
+        if ev: ev[k].record(); k += 1
+        for _ in range(R.gamma):
+            g_quant.replay()
+            if ev: ev[k].record(); k += 1
+            g_draft.replay()
+            if ev: ev[k].record(); k += 1
+        g_verify.replay()
+        if ev: ev[k].record(); k += 1
+        g_accept[i % R.n_logit_sets].replay()
+        if ev: ev[k].record(); k += 1
+        g_commit.replay()
+        if ev: ev[k].record(); k += 1
+
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    # replays reproduce the eager outputs (logit set 0 is replayed at i = 0 below)
+    g_accept[0].replay()
+    torch.cuda.synchronize()
+    same = (torch.equal(R.y_draft[2], ref[0]) and torch.equal(R.y_verify[3], ref[1])
+            and torch.equal(R.accept, ref[2]) and torch.equal(R.out_tokens, ref[3]))
+    if not same:
+        raise SystemExit("graph replay differs from the eager run")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-phase times from the events (ms)
+    ph = {p: 0.0 for p in phases}
+    for ev in evs:
+        k = 0
+        for _ in range(R.gamma):
+            ph["quantize_act"] += ev[k].elapsed_time(ev[k + 1]); k += 1
+            ph["gemm_w4a4"] += ev[k].elapsed_time(ev[k + 1]); k += 1
+        ph["gemm_w4a16"] += ev[k].elapsed_time(ev[k + 1]); k += 1
+        ph["verify_accept"] += ev[k].elapsed_time(ev[k + 1]); k += 1
+        ph["kv_overwrite"] += ev[k].elapsed_time(ev[k + 1]); k += 1
+    ph = {p: v / args.steps for p, v in ph.items()}
+    event_ms = sum(ph.values())
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+    return R, ph, wall, event_ms
+
+
+def cpu_leg(args):
+    """The oracle, as written, on a bounded sample of one round, scaled to a whole round."""
+    import numpy as np
+
+    import oracle
+    import synthetic_inputs as si
+
+    B, g, L = args.batch, args.gamma, args.layers
+    frac = 16           # every projection is sampled on 1/frac of its output columns
+    est = 0.0
+    t_start = time.perf_counter()
+    parts = {}
+    for i, (name, (K, N)) in enumerate(si.LLAMA3_8B_PROJ.items()):
+        Ns = N // frac
+        w = si.weights(K, Ns, seed=i)
+        xd = si.activations(B, K, seed=10 + i)
+        xv = si.activations(B * (g + 1), K, seed=20 + i)
+        t0 = time.perf_counter()
+        c, s = oracle.quantize_act(xd)
+        t1 = time.perf_counter()
+        oracle.gemm_w4a4(c, s, w["codes"], w["meta"], want_dots=False)
+        t2 = time.perf_counter()
+        oracle.gemm_w4a16(xv, w["codes"], w["meta"])
+        t3 = time.perf_counter()
+        parts[name] = (t1 - t0, t2 - t1, t3 - t2)
+        est += L * (g * ((t1 - t0) + frac * (t2 - t1)) + frac * (t3 - t2))
+    t, d = si.logits(B, g, VOCAB, seed=0)
+    toks = si.draft_tokens_sampled(d, seed=0)
+    u, v = si.uniforms((B, g), 0), si.uniforms((B,), 1)
+    t0 = time.perf_counter()
+    acc, _, _ = oracle.verify_sample(t, d, toks, u, v, with_diag=False)
+    est += time.perf_counter() - t0
+    # KV: one layer of the cache at a short context (the copy cost does not depend on T)
+    cache = si.kv_canary(1, B, KV_HEADS, 64, HEAD_DIM).reshape(1, B, 2, KV_HEADS, 64, HEAD_DIM)
+    stage = si.kv_staging(1, B, KV_HEADS, g, HEAD_DIM, seed=0)
+    start = si.start_positions(B, 64, g, seed=0)
+    t0 = time.perf_counter()
+    oracle.kv_overwrite(cache, stage, start, acc)
+    est += L * (time.perf_counter() - t0)
+    spent = time.perf_counter() - t_start
+    return {
+        "value": B * (g + 1) / est,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"one layer of each projection on 1/{frac} of its columns (draft quantize + W4A4 at M={B}, "
+                   f"verify W4A16 at M={B * (g + 1)}), full verify_accept (sampling, B={B}, V={VOCAB}), "
+                   f"one KV layer; scaled x{L} layers, x{g} draft steps, x{frac} columns; "
+                   f"estimated round {est:.1f} s from {spent:.1f} s of single-threaded CPU work"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: every box here has one MI355X and this build has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    R, ph, wall, event_ms = gpu_leg(args)
+    B, g = args.batch, args.gamma
+    ms_per_step = wall * 1e3 / args.steps
+    value = B * (g + 1) / (ms_per_step / 1e3)
+    nl = R.launches_per_gemm_phase()
+    draft_ms = ph["gemm_w4a4"]                     # gamma draft passes per round
+    verify_ms = ph["gemm_w4a16"]
+    dom = "gemm_w4a4" if draft_ms >= verify_ms else "gemm_w4a16"
+    if dom == "gemm_w4a4":
+        bytes_per_launch = R.draft_gemm_bytes() / nl
+        launch_ms = draft_ms / (g * nl)
+    else:
+        bytes_per_launch = R.verify_gemm_bytes() / nl
+        launch_ms = verify_ms / nl
+    achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+bf16",
+        "data": "synthetic",
+        "config": {"workload": f"llama3-8b-projections-{args.layers}L-qspec-round-B{B}-gamma{g}",
+                   "batch": B, "gamma": g, "layers": args.layers, "draft_M": B, "verify_M": B * (g + 1),
+                   "vocab": VOCAB, "kv_cache": f"{args.layers}x{B}x2x{KV_HEADS}x{CONTEXT}x{HEAD_DIM} bf16",
+                   "verify_mode": "sample"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(bytes_per_launch), "us_per_launch": round(launch_ms * 1e3, 3)},
+        "phases_ms_per_round": {k: round(v, 4) for k, v in ph.items()},
+        "event_ms_per_round": round(event_ms, 4),
+        "gemm_hbm_tbs": {"gemm_w4a4_M%d" % B: round(R.draft_gemm_bytes() * g / (draft_ms / 1e3) / 1e12, 3),
+                         "gemm_w4a16_M%d" % (B * (g + 1)): round(R.verify_gemm_bytes() / (verify_ms / 1e3) / 1e12, 3)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_leg(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -34,18 +34,25 @@
  *     call) but give unspecified results.
  *   - Outputs must not alias inputs.
  *   - Alignment: x / activation codes / weight codes 16 bytes (they are read with 16-byte
- *     loads; row starts stay aligned because K is a multiple of 128); fp32 / int32 arrays
- *     4 bytes; fp16 / bf16 arrays 2 bytes; the verify workspace 16 bytes.  Torch allocations
+ *     loads; row starts stay aligned because K is a multiple of 128); fp32 / int32 / meta
+ *     arrays 4 bytes; bf16 arrays 2 bytes; the verify workspace 16 bytes.  Torch allocations
  *     satisfy all of these.  A violation returns QSPEC_ERR_ALIGN.
  *
  * Storage formats (the pages fix none of these; this library's choices)
- *   weight codes   u8  [N][K/2]     w(k,n) = (codes[n][k/2] >> 4*(k&1)) & 15, unsigned 0..15
- *   weight scales  u16 [N][K/128]   IEEE binary16 bit patterns (finite)
- *   weight zeros   u8  [N][K/128]   zero points 0..15
+ *   weight codes   u8  [N/16][K/128][1024]  the shared 4-bit store, tile-major.  Block (t, g)
+ *                  holds columns n = 16t..16t+15 and k = 128g..128g+127 as
+ *                  [quarter q = (k%128)/32][column c = n%16][16 bytes for k%32 = 0..31], two
+ *                  unsigned codes (0..15) per byte, even k in the low nibble.  A wave reading a
+ *                  block with lane l taking bytes 16l..16l+15 reads one contiguous kilobyte and
+ *                  receives exactly its MFMA B fragments (lane l = column l%16, quarter l/16).
+ *   weight meta    u32 [N/16][K/128][16]    per (column, group): binary16 scale s in bits
+ *                  0..15, zero point z (0..15) in bits 16..23, bits 24..31 zero; entry (t, g, c)
+ *                  belongs to column 16t + c.
  *   activations    u16 [M][K]       bfloat16 bit patterns, row-major
  *   act. codes     u8  [M][K/2]     4-bit two's complement, even k in the low nibble
  *   act. scales    f32 [M][K/128]
- *   K must be a positive multiple of QSPEC_GROUP (128); N >= 1; M >= 1.
+ *   K must be a positive multiple of QSPEC_GROUP (128); N a positive multiple of 16; M >= 1.
+ *   Weight bytes per element: 0.5 (code) + 4/128 (meta) = 0.53125.
  */
 #ifndef QSPEC_H
 #define QSPEC_H
@@ -100,17 +107,18 @@ int qspec_quantize_act(const uint16_t *x, int32_t M, int32_t K, uint8_t *codes, 
  *     D[g][m][n] = sum_{k in g} q_a[m][k] * (w[k][n] - z[n][g])   (exact, int32)
  *     y[m][n]    = sum_g s_a[m][g] * s[n][g] * D[g][m][n]          (fp32 accumulation)
  * a_codes     [in]  u8  [M][K/2], a_scales [in] f32 [M][K/128]  (from qspec_quantize_act)
- * w_codes, w_scales, w_zeros [in] shared weights, formats above
+ * w_codes, w_meta [in] the shared weight store, formats above
  * y           [out] [M][N], bfloat16 (y_dtype = QSPEC_OUT_BF16, nearest-even) or f32
  * group_dots  [out, optional] i32 [K/128][M][N] -- the exact D; NULL to skip
  *             (diagnostic: slower).
- * Row m of y does not depend on the other rows or on M (fixed reduction order).
- * Errors: NULL pointer; M < 1; N < 1; K < 128 or K % 128 != 0; bad y_dtype.
+ * Batch invariance: the reduction order of an output depends only on (K, N) and on the batch
+ * tier of M -- [1, 16], (16, 64] or above 64 -- so row m of y is bit-identical for every M in
+ * the same tier.
+ * Errors: NULL pointer; M < 1; N < 1 or N % 16 != 0; K < 128 or K % 128 != 0; bad y_dtype.
  */
 int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int32_t M,
-                    const uint8_t *w_codes, const uint16_t *w_scales, const uint8_t *w_zeros,
-                    int32_t K, int32_t N, void *y, int32_t y_dtype, int32_t *group_dots,
-                    qspec_stream_t stream);
+                    const uint8_t *w_codes, const uint32_t *w_meta, int32_t K, int32_t N, void *y,
+                    int32_t y_dtype, int32_t *group_dots, qspec_stream_t stream);
 
 /*
  * qspec_gemm_w4a16 -- W4A16 verify linear layer over the shared 4-bit weights.
@@ -120,15 +128,16 @@ int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int32_t M,
  * (w[k][n] - z[n][g])) (the product is exact before that rounding);
  * y[m][n] = sum_k x[m][k] * W_hat[k][n] accumulated in fp32.
  * x   [in]  u16 [M][K] bfloat16
+ * w_codes, w_meta [in] the shared weight store (the same arrays the W4A4 layer reads)
  * y   [out] [M][N], bfloat16 (nearest-even) or f32 per y_dtype
- * For M <= 80 row m of y does not depend on the other rows or on M (a fixed
- * reduction order chosen from K and N only), so verifying gamma+1 positions
- * reproduces one-position decoding bit for bit.
- * Errors: NULL pointer; M < 1; N < 1; K < 128 or K % 128 != 0; bad y_dtype.
+ * Batch invariance: the reduction order of an output depends only on (K, N) and on the
+ * batch tier of M -- [1, 16], (16, 80] or above 80 -- so row m of y is bit-identical for every
+ * M in the same tier; verifying gamma+1 <= 16 positions therefore reproduces one-position
+ * decoding bit for bit.
+ * Errors: NULL pointer; M < 1; N < 1 or N % 16 != 0; K < 128 or K % 128 != 0; bad y_dtype.
  */
-int qspec_gemm_w4a16(const uint16_t *x, int32_t M, const uint8_t *w_codes,
-                     const uint16_t *w_scales, const uint8_t *w_zeros, int32_t K, int32_t N,
-                     void *y, int32_t y_dtype, qspec_stream_t stream);
+int qspec_gemm_w4a16(const uint16_t *x, int32_t M, const uint8_t *w_codes, const uint32_t *w_meta,
+                     int32_t K, int32_t N, void *y, int32_t y_dtype, qspec_stream_t stream);
 
 /*
  * qspec_verify_workspace_bytes -- device workspace qspec_verify_accept needs

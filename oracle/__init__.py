@@ -56,10 +56,10 @@ def _lib():
         lib.orc_double_to_bf16.restype = ctypes.c_uint16
         lib.orc_dequant_one.argtypes = [ctypes.c_uint16, ctypes.c_int, ctypes.c_int]
         lib.orc_dequant_one.restype = ctypes.c_uint16
-        lib.orc_dequant.argtypes = [P, P, P, I, I, P]
-        lib.orc_gemm_w4a16.argtypes = [P, I, P, P, P, I, I, P]
+        lib.orc_dequant.argtypes = [P, P, I, I, P]
+        lib.orc_gemm_w4a16.argtypes = [P, I, P, P, I, I, P]
         lib.orc_quantize_act.argtypes = [P, I, I, P, P]
-        lib.orc_gemm_w4a4.argtypes = [P, P, I, P, P, P, I, I, P, P]
+        lib.orc_gemm_w4a4.argtypes = [P, P, I, P, P, I, I, P, P]
         lib.orc_verify_greedy.argtypes = [P, P, I, I, I, P, P]
         lib.orc_verify_sample.argtypes = [P, P, P, P, P, I, I, I, P, P, P]
         lib.orc_kv_overwrite.argtypes = [P, P, P, P, I, I, I, I, I, I]
@@ -99,31 +99,31 @@ def dequant_one(scale_bits: int, w: int, z: int) -> int:
 
 # ---- the hot-path operations --------------------------------------------------
 
-def dequant(codes, scales, zeros):
-    """W_hat = bf16(s * (w - z)) for every (n, k); returns u16 [N][K]."""
+def _weights(codes, meta):
+    """Shared weight store: codes u8 [N/16][K/128][1024], meta u32 [N/16][K/128][16]."""
     codes = _c(codes, np.uint8)
-    N, K2 = codes.shape
-    K = 2 * K2
-    scales = _c(scales, np.uint16)
-    zeros = _c(zeros, np.uint8)
-    assert scales.shape == (N, K // GROUP) and zeros.shape == (N, K // GROUP)
+    meta = _c(meta, np.uint32)
+    T, G, blk = codes.shape
+    assert blk == 1024 and meta.shape == (T, G, 16)
+    return codes, meta, G * GROUP, 16 * T
+
+
+def dequant(codes, meta):
+    """W_hat = bf16(s * (w - z)) for every (n, k); returns u16 [N][K]."""
+    codes, meta, K, N = _weights(codes, meta)
     out = np.empty((N, K), np.uint16)
-    _lib().orc_dequant(_p(codes), _p(scales), _p(zeros), K, N, _p(out))
+    _lib().orc_dequant(_p(codes), _p(meta), K, N, _p(out))
     return out
 
 
-def gemm_w4a16(x, codes, scales, zeros):
+def gemm_w4a16(x, codes, meta):
     """y = X W_hat in fp64; x u16 bf16 [M][K]; returns f64 [M][N]."""
+    codes, meta, K, N = _weights(codes, meta)
     x = _c(x, np.uint16)
-    codes = _c(codes, np.uint8)
-    scales = _c(scales, np.uint16)
-    zeros = _c(zeros, np.uint8)
-    M, K = x.shape
-    N = codes.shape[0]
-    assert codes.shape == (N, K // 2)
-    assert scales.shape == (N, K // GROUP) and zeros.shape == (N, K // GROUP)
+    M = x.shape[0]
+    assert x.shape == (M, K)
     y = np.empty((M, N), np.float64)
-    _lib().orc_gemm_w4a16(_p(x), M, _p(codes), _p(scales), _p(zeros), K, N, _p(y))
+    _lib().orc_gemm_w4a16(_p(x), M, _p(codes), _p(meta), K, N, _p(y))
     return y
 
 
@@ -138,21 +138,16 @@ def quantize_act(x):
     return codes, scales
 
 
-def gemm_w4a4(a_codes, a_scales, codes, scales, zeros, want_dots: bool = True):
+def gemm_w4a4(a_codes, a_scales, codes, meta, want_dots: bool = True):
     """Returns (y f64 [M][N], D i64 [K/128][M][N] or None)."""
+    codes, meta, K, N = _weights(codes, meta)
     a_codes = _c(a_codes, np.uint8)
     a_scales = _c(a_scales, np.float32)
-    codes = _c(codes, np.uint8)
-    scales = _c(scales, np.uint16)
-    zeros = _c(zeros, np.uint8)
-    M, K2 = a_codes.shape
-    K = 2 * K2
-    N = codes.shape[0]
-    assert codes.shape == (N, K2) and a_scales.shape == (M, K // GROUP)
+    M = a_codes.shape[0]
+    assert a_codes.shape == (M, K // 2) and a_scales.shape == (M, K // GROUP)
     y = np.empty((M, N), np.float64)
     D = np.empty((K // GROUP, M, N), np.int64) if want_dots else None
-    _lib().orc_gemm_w4a4(_p(a_codes), _p(a_scales), M, _p(codes), _p(scales), _p(zeros), K, N,
-                         _p(D), _p(y))
+    _lib().orc_gemm_w4a4(_p(a_codes), _p(a_scales), M, _p(codes), _p(meta), K, N, _p(D), _p(y))
     return y, D
 
 

@@ -21,9 +21,12 @@
  *   KV replacement).
  *
  * Data formats (the pages fix none of them; these are this project's choices):
- *   weight codes  u8  [N][K/2]   w(k,n) = (codes[n][k/2] >> 4*(k&1)) & 15, unsigned 0..15
- *   weight scales u16 [N][K/128] IEEE binary16 bit patterns
- *   weight zeros  u8  [N][K/128] 0..15
+ *   weight codes  u8  [N/16][K/128][4][16][16]   tile-major: for column tile t = n/16 and group
+ *                 g = k/128 one 1024-byte block; inside it quarter q = (k%128)/32, column
+ *                 c = n%16, then 16 bytes holding k%32 = 0..31, even k in the low nibble.
+ *                 Codes are unsigned 0..15.  N is a multiple of 16.
+ *   weight meta   u32 [N/16][K/128][16]   bits 0..15 binary16 scale s, bits 16..23 zero
+ *                 point z (0..15), bits 24..31 zero; entry (t, g, c) is column 16t + c.
  *   activations   u16 [M][K]     bfloat16 bit patterns
  *   act. codes    u8  [M][K/2]   4-bit two's complement, low nibble = even k
  *   act. scales   f32 [M][K/128]
@@ -107,11 +110,25 @@ uint16_t orc_double_to_bf16(double v)
  * (the activations are bfloat16); the product s*(w-z) is exact in double, so the
  * only rounding is the one to bfloat16.
  */
+/* The weight store, read one element at a time through the layout definition above. */
 static int weight_code(const uint8_t *codes, int64_t K, int64_t n, int64_t k)
 {
-    uint8_t byte = codes[n * (K / 2) + k / 2];
+    int64_t G = K / ORC_GROUP;
+    int64_t block = (n / 16) * G + k / ORC_GROUP;
+    int64_t q = (k % ORC_GROUP) / 32;
+    int64_t byte_index = block * 1024 + q * 256 + (n % 16) * 16 + (k % 32) / 2;
+    uint8_t byte = codes[byte_index];
     return (k & 1) ? (byte >> 4) & 15 : byte & 15;
 }
+
+static uint32_t meta_word(const uint32_t *meta, int64_t K, int64_t n, int64_t g)
+{
+    int64_t G = K / ORC_GROUP;
+    return meta[((n / 16) * G + g) * 16 + n % 16];
+}
+
+static uint16_t meta_scale(uint32_t word) { return (uint16_t)(word & 0xFFFFu); }
+static int meta_zero(uint32_t word) { return (int)((word >> 16) & 0xFFu); }
 
 uint16_t orc_dequant_one(uint16_t scale_fp16, int w, int z)
 {
@@ -120,15 +137,12 @@ uint16_t orc_dequant_one(uint16_t scale_fp16, int w, int z)
 }
 
 /* w_hat: u16 [N][K] bfloat16 patterns. */
-void orc_dequant(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
-                 int64_t K, int64_t N, uint16_t *w_hat)
+void orc_dequant(const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N, uint16_t *w_hat)
 {
-    int64_t G = K / ORC_GROUP;
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) {
-            int64_t g = k / ORC_GROUP;
-            w_hat[n * K + k] = orc_dequant_one(scales[n * G + g], weight_code(codes, K, n, k),
-                                               zeros[n * G + g]);
+            uint32_t word = meta_word(meta, K, n, k / ORC_GROUP);
+            w_hat[n * K + k] = orc_dequant_one(meta_scale(word), weight_code(codes, K, n, k), meta_zero(word));
         }
 }
 
@@ -138,16 +152,15 @@ void orc_dequant(const uint8_t *codes, const uint16_t *scales, const uint8_t *ze
  * double (every product of two bfloat16 values is exact in double).
  * y: f64 [M][N].
  */
-void orc_gemm_w4a16(const uint16_t *x, int64_t M, const uint8_t *codes, const uint16_t *scales,
-                    const uint8_t *zeros, int64_t K, int64_t N, double *y)
+void orc_gemm_w4a16(const uint16_t *x, int64_t M, const uint8_t *codes, const uint32_t *meta,
+                    int64_t K, int64_t N, double *y)
 {
     double *col = (double *)malloc(sizeof(double) * (size_t)K);
-    int64_t G = K / ORC_GROUP;
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t k = 0; k < K; ++k) {
-            int64_t g = k / ORC_GROUP;
+            uint32_t word = meta_word(meta, K, n, k / ORC_GROUP);
             col[k] = orc_bf16_to_double(
-                orc_dequant_one(scales[n * G + g], weight_code(codes, K, n, k), zeros[n * G + g]));
+                orc_dequant_one(meta_scale(word), weight_code(codes, K, n, k), meta_zero(word)));
         }
         for (int64_t m = 0; m < M; ++m) {
             double acc = 0.0;
@@ -218,20 +231,21 @@ static int act_code(const uint8_t *codes, int64_t K, int64_t m, int64_t k)
  * D: i64 [K/128][M][N] (may be NULL), y: f64 [M][N].
  */
 void orc_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int64_t M,
-                   const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
-                   int64_t K, int64_t N, int64_t *D, double *y)
+                   const uint8_t *codes, const uint32_t *meta, int64_t K, int64_t N, int64_t *D,
+                   double *y)
 {
     int64_t G = K / ORC_GROUP;
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0;
             for (int64_t g = 0; g < G; ++g) {
-                int z = zeros[n * G + g];
+                uint32_t word = meta_word(meta, K, n, g);
+                int z = meta_zero(word);
                 int64_t dot = 0;
                 for (int64_t k = g * ORC_GROUP; k < (g + 1) * ORC_GROUP; ++k)
                     dot += (int64_t)act_code(a_codes, K, m, k) * (int64_t)(weight_code(codes, K, n, k) - z);
                 if (D) D[(g * M + m) * N + n] = dot;
-                acc += (double)a_scales[m * G + g] * orc_fp16_to_double(scales[n * G + g]) * (double)dot;
+                acc += (double)a_scales[m * G + g] * orc_fp16_to_double(meta_scale(word)) * (double)dot;
             }
             y[m * N + n] = acc;
         }

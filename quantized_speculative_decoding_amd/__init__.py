@@ -6,12 +6,11 @@ the C entry point of the same name.  Every step of the computation runs in the
 library's HIP kernels; there is no fallback.  A missing or unloadable library
 raises at first use.
 
-Tensor conventions (row-major, contiguous):
-  activations / KV   torch.bfloat16
-  weight codes       torch.uint8 [N][K/2]    (even k in the low nibble, unsigned 0..15)
-  weight scales      torch.float16 [N][K/128]
-  weight zeros       torch.uint8 [N][K/128]
-  activation codes   torch.uint8 [M][K/2]    (4-bit two's complement)
+Tensor conventions (contiguous):
+  activations / KV   torch.bfloat16, row-major
+  weight codes       torch.uint8 [N/16][K/128][1024]   the tile-major shared store
+  weight meta        torch.int32 (or uint32) [N/16][K/128][16]: fp16 scale bits 0..15, zero 16..23
+  activation codes   torch.uint8 [M][K/2]    (4-bit two's complement, even k in the low nibble)
   activation scales  torch.float32 [M][K/128]
 """
 from __future__ import annotations
@@ -54,8 +53,8 @@ def lib() -> ctypes.CDLL:
         L.qspec_status_string.argtypes = [ctypes.c_int]
         L.qspec_status_string.restype = ctypes.c_char_p
         L.qspec_quantize_act.argtypes = [P, I, I, P, P, P]
-        L.qspec_gemm_w4a4.argtypes = [P, P, I, P, P, P, I, I, P, I, P, P]
-        L.qspec_gemm_w4a16.argtypes = [P, I, P, P, P, I, I, P, I, P]
+        L.qspec_gemm_w4a4.argtypes = [P, P, I, P, P, I, I, P, I, P, P]
+        L.qspec_gemm_w4a16.argtypes = [P, I, P, P, I, I, P, I, P]
         L.qspec_verify_workspace_bytes.argtypes = [I, I, I, I]
         L.qspec_verify_workspace_bytes.restype = S
         L.qspec_verify_accept.argtypes = [I, P, P, P, P, P, I, I, I, P, P, P, S, P]
@@ -95,15 +94,15 @@ def _req(t: torch.Tensor, name: str, dtype, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def _weights(w_codes, w_scales, w_zeros):
-    if w_codes.dim() != 2:
-        raise ValueError("w_codes must be [N][K/2]")
-    N, K2 = w_codes.shape
-    K = 2 * K2
+def _weights(w_codes, w_meta):
+    if w_codes.dim() != 3 or w_codes.shape[2] != 1024:
+        raise ValueError("w_codes must be [N/16][K/128][1024]")
+    T, G, _ = w_codes.shape
     _req(w_codes, "w_codes", torch.uint8)
-    _req(w_scales, "w_scales", torch.float16, (N, K // GROUP))
-    _req(w_zeros, "w_zeros", torch.uint8, (N, K // GROUP))
-    return K, N
+    if w_meta.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("w_meta must be int32 or uint32")
+    _req(w_meta, "w_meta", w_meta.dtype, (T, G, 16))
+    return G * GROUP, 16 * T
 
 
 def _out_dtype(y: torch.Tensor) -> int:
@@ -124,10 +123,9 @@ def qspec_quantize_act(x, codes, scales, stream=None) -> None:
            lib().qspec_quantize_act(_ptr(x), M, K, _ptr(codes), _ptr(scales), _stream(stream, x)))
 
 
-def qspec_gemm_w4a4(a_codes, a_scales, w_codes, w_scales, w_zeros, y, group_dots=None,
-                    stream=None) -> None:
+def qspec_gemm_w4a4(a_codes, a_scales, w_codes, w_meta, y, group_dots=None, stream=None) -> None:
     """W4A4 draft layer: y [M][N] (bf16 or f32); optional exact group dots i32 [K/128][M][N]."""
-    K, N = _weights(w_codes, w_scales, w_zeros)
+    K, N = _weights(w_codes, w_meta)
     _req(a_codes, "a_codes", torch.uint8)
     M = a_codes.shape[0]
     _req(a_codes, "a_codes", torch.uint8, (M, K // 2))
@@ -137,22 +135,21 @@ def qspec_gemm_w4a4(a_codes, a_scales, w_codes, w_scales, w_zeros, y, group_dots
     if group_dots is not None:
         _req(group_dots, "group_dots", torch.int32, (K // GROUP, M, N))
     _check("qspec_gemm_w4a4",
-           lib().qspec_gemm_w4a4(_ptr(a_codes), _ptr(a_scales), M, _ptr(w_codes), _ptr(w_scales),
-                                 _ptr(w_zeros), K, N, _ptr(y), dt, _ptr(group_dots),
-                                 _stream(stream, y)))
+           lib().qspec_gemm_w4a4(_ptr(a_codes), _ptr(a_scales), M, _ptr(w_codes), _ptr(w_meta), K, N,
+                                 _ptr(y), dt, _ptr(group_dots), _stream(stream, y)))
 
 
-def qspec_gemm_w4a16(x, w_codes, w_scales, w_zeros, y, stream=None) -> None:
+def qspec_gemm_w4a16(x, w_codes, w_meta, y, stream=None) -> None:
     """W4A16 verify layer: y [M][N] = x W_hat (bf16 or f32 out)."""
-    K, N = _weights(w_codes, w_scales, w_zeros)
+    K, N = _weights(w_codes, w_meta)
     _req(x, "x", torch.bfloat16)
     M = x.shape[0]
     _req(x, "x", torch.bfloat16, (M, K))
     dt = _out_dtype(y)
     _req(y, "y", y.dtype, (M, N))
     _check("qspec_gemm_w4a16",
-           lib().qspec_gemm_w4a16(_ptr(x), M, _ptr(w_codes), _ptr(w_scales), _ptr(w_zeros), K, N,
-                                  _ptr(y), dt, _stream(stream, y)))
+           lib().qspec_gemm_w4a16(_ptr(x), M, _ptr(w_codes), _ptr(w_meta), K, N, _ptr(y), dt,
+                                  _stream(stream, y)))
 
 
 def qspec_verify_workspace_bytes(mode: int, B: int, gamma: int, V: int) -> int:

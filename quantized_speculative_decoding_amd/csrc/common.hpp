@@ -65,13 +65,16 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
     return r;
 }
 
-// Column-count per workgroup split of K among waves: depends on (K, N) only, so that every
-// batch size reduces each output in the same order.
+// Number of waves per workgroup that split the K groups of one column tile between them.  It
+// depends on (K, N) only, so every batch size reduces each output in the same order.  Small-N
+// layers get more waves per tile so the chip still holds thousands of waves in flight.
+constexpr int kMaxSplitWaves = 16;
+
 __host__ __device__ inline int skinny_waves_for_shape(int K, int N) {
     const int G = K / kGroup;
     const int tiles = (N + 15) / 16;
     int kw = 1;
-    while (kw < 8 && tiles * kw * 2 <= 4096) kw *= 2;
+    while (kw < kMaxSplitWaves && tiles * kw * 2 <= 8192) kw *= 2;
     while (kw > G) kw >>= 1;
     return kw < 1 ? 1 : kw;
 }

@@ -49,16 +49,27 @@ __device__ __forceinline__ void store_out4(void *y, int y_f32, size_t idx, float
 
 // ---------------------------------------------------------------------------------------------
 // Skinny kernel.  Lane l: col = l % 16, kq = l / 16.  A group's 128 codes split into 4 lane
-// quarters of 32; MFMA j (0, 1) takes the lane's codes 16 j .. 16 j + 15 of its quarter, in the
-// order [even k of dword 2j, odd k of dword 2j, even k of dword 2j+1, odd k of dword 2j+1] for
-// both operands.  Output of v_mfma_i32_16x16x64_i8: lane l, element r holds D[4 (l/16) + r][l%16].
-template <int MT, int NT, int U>
-__global__ void __launch_bounds__(512)
+// quarters of 32 (the tile-major block gives lane l exactly bytes 16 l .. 16 l + 15); MFMA j
+// (0, 1) takes the lane's codes 16 j .. 16 j + 15 of its quarter, in the order [even k of dword
+// 2j, odd k of dword 2j, even k of dword 2j+1, odd k of dword 2j+1] for both operands.  Output of
+// v_mfma_i32_16x16x64_i8: lane l, element r holds D[4 (l/16) + r][l%16].
+// The memory pipeline is the one of the W4A16 skinny kernel: a stage holds one group's codes and
+// meta of NT column tiles plus the activation codes and scales of MT row tiles; U stages stay in
+// flight; rows past M read row M - 1 and are discarded.
+template <int MT, int NT>
+struct W4Stage {
+    uint4 w[NT];
+    uint32_t meta[NT];
+    uint4 a[MT];
+    float as[MT][4];
+};
+
+template <int MT, int NT, int U, int MAXW, bool DOTS>
+__global__ void __launch_bounds__(64 * MAXW)
 k_w4a4_skinny(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, int M,
-              const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-              const uint8_t *__restrict__ zeros, int K, int N, void *__restrict__ y, int y_f32,
-              int32_t *__restrict__ dots, int kw) {
-    __shared__ float red[8 * 4 * 64];   // [kw <= 8][4][64]
+              const uint8_t *__restrict__ codes, const uint32_t *__restrict__ meta, int K, int N,
+              void *__restrict__ y, int y_f32, int32_t *__restrict__ dots, int kw) {
+    __shared__ float red[kMaxSplitWaves * 4 * 64];   // [kw][4][64]
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int col = lane & 15;
@@ -66,10 +77,43 @@ k_w4a4_skinny(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
     const int G = K / kGroup;
     const int g0 = (wave * G) / kw;
     const int ng = ((wave + 1) * G) / kw - g0;
-    const int nbase = blockIdx.x * 16 * NT;
+    const int T = N / 16;
+    const int tbase = blockIdx.x * NT;
     const size_t row_bytes = (size_t)K / 2;
     const i32x4_t ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
     const i32x4_t izero = {0, 0, 0, 0};
+
+    const uint8_t *wblk[NT];
+    const uint32_t *mblk[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int t = min(tbase + nt, T - 1);
+        wblk[nt] = codes + ((size_t)t * G + g0) * 1024 + lane * 16;
+        mblk[nt] = meta + ((size_t)t * G + g0) * 16 + col;
+    }
+    // A operand row of this lane, and the output rows whose activation scales it needs.
+    const uint8_t *arow[MT];
+    const float *asrow[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        arow[mt] = a_codes + (size_t)min(16 * mt + col, M - 1) * row_bytes + (size_t)g0 * 64 + kq * 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) asrow[mt][r] = a_scales + (size_t)min(16 * mt + 4 * kq + r, M - 1) * G + g0;
+    }
+
+    auto load = [&](W4Stage<MT, NT> &st, int i) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            st.w[nt] = load_stream16(wblk[nt] + (size_t)i * 1024);
+            st.meta[nt] = mblk[nt][(size_t)i * 16];
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            st.a[mt] = *(const uint4 *)(arow[mt] + (size_t)i * 64);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.as[mt][r] = asrow[mt][r][i];
+        }
+    };
 
     f32x4_t acc[MT][NT];
 #pragma unroll
@@ -77,111 +121,60 @@ k_w4a4_skinny(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const uint8_t *wrow[NT];
-    const uint16_t *srow[NT];
-    const uint8_t *zrow[NT];
+    auto compute = [&](const W4Stage<MT, NT> &cur, int i) {
+        i32x4_t A0[MT], A1[MT], sa[MT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        int n = nbase + 16 * nt + col;
-        n = n < N ? n : N - 1;
-        wrow[nt] = codes + (size_t)n * row_bytes + (size_t)g0 * 64 + kq * 16;
-        srow[nt] = scales + (size_t)n * G + g0;
-        zrow[nt] = zeros + (size_t)n * G + g0;
-    }
-    // A operand rows (one per lane) and the output rows whose activation scales this lane needs.
-    const uint8_t *arow[MT];
-    bool avalid[MT];
-    const float *asrow[MT][4];
-    bool ovalid[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + col;
-        avalid[mt] = m < M;
-        arow[mt] = a_codes + (size_t)(avalid[mt] ? m : 0) * row_bytes + (size_t)g0 * 64 + kq * 16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int mo = 16 * mt + 4 * kq + r;
-            ovalid[mt][r] = mo < M;
-            asrow[mt][r] = a_scales + (size_t)(ovalid[mt][r] ? mo : 0) * G + g0;
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint4 e = cur.a[mt];
+            A0[mt] = as_i32x4(snib_lo(e.x), snib_hi(e.x), snib_lo(e.y), snib_hi(e.y));
+            A1[mt] = as_i32x4(snib_lo(e.z), snib_hi(e.z), snib_lo(e.w), snib_hi(e.w));
+            sa[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0[mt], ones, izero, 0, 0, 0);
+            sa[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1[mt], ones, sa[mt], 0, 0, 0);
         }
-    }
-
-    uint4 wbuf[U][NT];
-    uint16_t sbuf[U][NT];
-    uint8_t zbuf[U][NT];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-        if (u < ng)
+        for (int nt = 0; nt < NT; ++nt) {
+            const uint4 d = cur.w[nt];
+            const float sw = fp16_bits_to_float((uint16_t)(cur.meta[nt] & 0xFFFFu));
+            const int zw = (int)((cur.meta[nt] >> 16) & 0xFFu);
+            const i32x4_t B0 = as_i32x4(nib_lo(d.x), nib_hi(d.x), nib_lo(d.y), nib_hi(d.y));
+            const i32x4_t B1 = as_i32x4(nib_lo(d.z), nib_hi(d.z), nib_lo(d.w), nib_hi(d.w));
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                wbuf[u][nt] = load_stream16(wrow[nt] + u * 64);
-                sbuf[u][nt] = srow[nt][u];
-                zbuf[u][nt] = zrow[nt][u];
+            for (int mt = 0; mt < MT; ++mt) {
+                i32x4_t ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0[mt], B0, izero, 0, 0, 0);
+                ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1[mt], B1, ia, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int Dv = ia[r] - zw * sa[mt][r];
+                    acc[mt][nt][r] = __builtin_fmaf(cur.as[mt][r] * sw, (float)Dv, acc[mt][nt][r]);
+                    if (DOTS) {
+                        const int mo = 16 * mt + 4 * kq + r;
+                        const int n = 16 * (tbase + nt) + col;
+                        if (mo < M && n < N) dots[((size_t)(g0 + i) * M + mo) * N + n] = Dv;
+                    }
+                }
             }
+        }
+    };
 
-    for (int base = 0; base < ng; base += U) {
+    W4Stage<MT, NT> st[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        load(st[u], min(u, ng - 1));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const int nfull = ng - ng % U;
+    for (int base = 0; base < nfull; base += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int i = base + u;
-            if (i < ng) {
-                i32x4_t A0[MT], A1[MT], sa[MT];
-                float as[MT][4];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    // rows past M read as code 0, so they add nothing to any sum
-                    const uint4 e = avalid[mt] ? *(const uint4 *)(arow[mt] + (size_t)i * 64)
-                                               : make_uint4(0, 0, 0, 0);
-                    A0[mt] = as_i32x4(snib_lo(e.x), snib_hi(e.x), snib_lo(e.y), snib_hi(e.y));
-                    A1[mt] = as_i32x4(snib_lo(e.z), snib_hi(e.z), snib_lo(e.w), snib_hi(e.w));
-                    sa[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0[mt], ones, izero, 0, 0, 0);
-                    sa[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1[mt], ones, sa[mt], 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) as[mt][r] = ovalid[mt][r] ? asrow[mt][r][i] : 0.f;
-                }
-                uint4 cur[NT];
-                float sw[NT];
-                int zw[NT];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    cur[nt] = wbuf[u][nt];
-                    sw[nt] = fp16_bits_to_float(sbuf[u][nt]);
-                    zw[nt] = zbuf[u][nt];
-                }
-                if (i + U < ng) {
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        wbuf[u][nt] = load_stream16(wrow[nt] + (size_t)(i + U) * 64);
-                        sbuf[u][nt] = srow[nt][i + U];
-                        zbuf[u][nt] = zrow[nt][i + U];
-                    }
-                }
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const uint4 d = cur[nt];
-                    const i32x4_t B0 = as_i32x4(nib_lo(d.x), nib_hi(d.x), nib_lo(d.y), nib_hi(d.y));
-                    const i32x4_t B1 = as_i32x4(nib_lo(d.z), nib_hi(d.z), nib_lo(d.w), nib_hi(d.w));
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        i32x4_t ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0[mt], B0, izero, 0, 0, 0);
-                        ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1[mt], B1, ia, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int Dv = ia[r] - zw[nt] * sa[mt][r];
-                            acc[mt][nt][r] = __builtin_fmaf(as[mt][r] * sw[nt], (float)Dv, acc[mt][nt][r]);
-                            if (dots) {
-                                const int mo = 16 * mt + 4 * kq + r;
-                                const int n = nbase + 16 * nt + col;
-                                if (mo < M && n < N)
-                                    dots[((size_t)(g0 + i) * M + mo) * N + n] = Dv;
-                            }
-                        }
-                    }
-                }
-            }
+            compute(st[u], base + u);
+            load(st[u], min(base + u + U, ng - 1));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u)
+        if (nfull + u < ng) compute(st[u], nfull + u);
 
-    // Fixed-order reduction of the kw wave partials, one 16x16 output tile at a time.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -191,11 +184,11 @@ k_w4a4_skinny(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
             __syncthreads();
             for (int e = threadIdx.x; e < 256; e += blockDim.x) {
                 const int r = e >> 6, l = e & 63;
-                float s = 0.f;
-                for (int w = 0; w < kw; ++w) s += red[(w * 4 + r) * 64 + l];
+                float sum = 0.f;
+                for (int w = 0; w < kw; ++w) sum += red[(w * 4 + r) * 64 + l];
                 const int m = 16 * mt + 4 * (l >> 4) + r;
-                const int n = nbase + 16 * nt + (l & 15);
-                if (m < M && n < N) store_out4(y, y_f32, (size_t)m * N + n, s);
+                const int n = 16 * (tbase + nt) + (l & 15);
+                if (m < M && n < N) store_out4(y, y_f32, (size_t)m * N + n, sum);
             }
             __syncthreads();
         }
@@ -208,9 +201,8 @@ constexpr int QLDS = kGroup + 16;   // padded row pitch in bytes
 
 __global__ void __launch_bounds__(256)
 k_w4a4_tiled(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, int M,
-             const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-             const uint8_t *__restrict__ zeros, int K, int N, void *__restrict__ y, int y_f32,
-             int32_t *__restrict__ dots) {
+             const uint8_t *__restrict__ codes, const uint32_t *__restrict__ meta, int K, int N,
+             void *__restrict__ y, int y_f32, int32_t *__restrict__ dots) {
     __shared__ __attribute__((aligned(16))) uint8_t As[QBM * QLDS];
     __shared__ __attribute__((aligned(16))) uint8_t Bs[QBN * QLDS];
     __shared__ float sA[QBM], sB[QBN];
@@ -219,6 +211,7 @@ k_w4a4_tiled(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_sc
     const int wm = wave >> 1, wn = wave & 1;
     const int col = lane & 15, kq = lane >> 4;
     const int G = K / kGroup;
+    const int T = N / 16;
     const size_t row_bytes = (size_t)K / 2;
     const int m0 = blockIdx.y * QBM, n0 = blockIdx.x * QBN;
     const i32x4_t izero = {0, 0, 0, 0};
@@ -230,35 +223,38 @@ k_w4a4_tiled(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_sc
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     for (int g = 0; g < G; ++g) {
-        // 128 rows x 64 bytes of codes per operand = 512 uint4 each, 2 + 2 per thread.
+        // 128 rows x 64 bytes of codes per operand = 512 uint4 each, 2 + 2 per thread.  Both are
+        // widened in the same byte order, so k slots line up.
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int idx = tid + it * 256;
-            const int r = idx >> 2, c = idx & 3;
-            const int m = m0 + r;
-            uint4 e = make_uint4(0, 0, 0, 0);
-            if (m < M) e = *(const uint4 *)(a_codes + (size_t)m * row_bytes + (size_t)g * 64 + c * 16);
-            uint4 *dst = (uint4 *)(As + r * QLDS + c * 32);   // rows past M stay code 0
-            dst[0] = make_uint4(snib_lo(e.x), snib_hi(e.x), snib_lo(e.y), snib_hi(e.y));
-            dst[1] = make_uint4(snib_lo(e.z), snib_hi(e.z), snib_lo(e.w), snib_hi(e.w));
-
-            int n = n0 + r;
-            n = n < N ? n : N - 1;
-            const uint4 d = load_stream16(codes + (size_t)n * row_bytes + (size_t)g * 64 + c * 16);
-            const uint32_t zz = (uint32_t)zeros[(size_t)n * G + g] * 0x01010101u;
-            uint4 *bd = (uint4 *)(Bs + r * QLDS + c * 32);
-            bd[0] = make_uint4(wz_bytes(nib_lo(d.x), zz), wz_bytes(nib_hi(d.x), zz),
-                               wz_bytes(nib_lo(d.y), zz), wz_bytes(nib_hi(d.y), zz));
-            bd[1] = make_uint4(wz_bytes(nib_lo(d.z), zz), wz_bytes(nib_hi(d.z), zz),
-                               wz_bytes(nib_lo(d.w), zz), wz_bytes(nib_hi(d.w), zz));
+            {   // activations: row r, 16-byte chunk c (k = 32 c .. 32 c + 31)
+                const int r = idx >> 2, c = idx & 3;
+                const int m = min(m0 + r, M - 1);
+                const uint4 e = *(const uint4 *)(a_codes + (size_t)m * row_bytes + (size_t)g * 64 + c * 16);
+                uint4 *dst = (uint4 *)(As + r * QLDS + c * 32);
+                dst[0] = make_uint4(snib_lo(e.x), snib_hi(e.x), snib_lo(e.y), snib_hi(e.y));
+                dst[1] = make_uint4(snib_lo(e.z), snib_hi(e.z), snib_lo(e.w), snib_hi(e.w));
+            }
+            {   // weights: tile tj, chunk b = column b % 16, k = 32 (b / 16) .. + 31
+                const int tj = idx >> 6, b = idx & 63;
+                const int t = min(n0 / 16 + tj, T - 1);
+                const uint4 d = load_stream16(codes + ((size_t)t * G + g) * 1024 + b * 16);
+                const uint32_t mw = meta[((size_t)t * G + g) * 16 + (b & 15)];
+                const uint32_t zz = ((mw >> 16) & 0xFFu) * 0x01010101u;
+                uint4 *bd = (uint4 *)(Bs + (tj * 16 + (b & 15)) * QLDS + (b >> 4) * 32);
+                bd[0] = make_uint4(wz_bytes(nib_lo(d.x), zz), wz_bytes(nib_hi(d.x), zz),
+                                   wz_bytes(nib_lo(d.y), zz), wz_bytes(nib_hi(d.y), zz));
+                bd[1] = make_uint4(wz_bytes(nib_lo(d.z), zz), wz_bytes(nib_hi(d.z), zz),
+                                   wz_bytes(nib_lo(d.w), zz), wz_bytes(nib_hi(d.w), zz));
+            }
         }
         if (tid < QBM) {
-            const int m = m0 + tid;
-            sA[tid] = m < M ? a_scales[(size_t)m * G + g] : 0.f;
+            sA[tid] = a_scales[(size_t)min(m0 + tid, M - 1) * G + g];
         } else {
-            int n = n0 + tid - QBM;
-            n = n < N ? n : N - 1;
-            sB[tid - QBM] = fp16_bits_to_float(scales[(size_t)n * G + g]);
+            const int c = tid - QBM;
+            const int t = min(n0 / 16 + c / 16, T - 1);
+            sB[c] = fp16_bits_to_float((uint16_t)(meta[((size_t)t * G + g) * 16 + (c & 15)] & 0xFFFFu));
         }
         __syncthreads();
         i32x4_t ia[4][4];
@@ -316,32 +312,37 @@ k_w4a4_tiled(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_sc
 
 // ---------------------------------------------------------------------------------------------
 
-template <int MT, int NT>
+template <int MT, int NT, int U, int MAXW>
 static hipError_t launch_skinny4(const uint8_t *a_codes, const float *a_scales, int M,
-                                 const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
-                                 int K, int N, void *y, int y_f32, int32_t *dots, hipStream_t st) {
-    constexpr int U = 4;
-    const int kw = skinny_waves_for_shape(K, N);
-    const int cols = 16 * NT;
-    dim3 grid((N + cols - 1) / cols);
+                                 const uint8_t *codes, const uint32_t *meta, int K, int N, void *y,
+                                 int y_f32, int32_t *dots, hipStream_t st) {
+    const int kw = min(skinny_waves_for_shape(K, N), MAXW);
+    const int T = N / 16;
+    dim3 grid((T + NT - 1) / NT);
     dim3 block(64 * kw);
-    hipLaunchKernelGGL((k_w4a4_skinny<MT, NT, U>), grid, block, 0, st, a_codes, a_scales, M, codes,
-                       scales, zeros, K, N, y, y_f32, dots, kw);
+    if (dots)
+        hipLaunchKernelGGL((k_w4a4_skinny<MT, NT, U, MAXW, true>), grid, block, 0, st, a_codes, a_scales, M,
+                           codes, meta, K, N, y, y_f32, dots, kw);
+    else
+        hipLaunchKernelGGL((k_w4a4_skinny<MT, NT, U, MAXW, false>), grid, block, 0, st, a_codes, a_scales, M,
+                           codes, meta, K, N, y, y_f32, dots, kw);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M,
-                            const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
-                            int K, int N, void *y, int y_f32, int32_t *group_dots, hipStream_t st) {
+hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M, const uint8_t *codes,
+                            const uint32_t *meta, int K, int N, void *y, int y_f32, int32_t *group_dots,
+                            hipStream_t st) {
+    // Batch tiers with one reduction order each: M <= 16 and 16 < M <= 64.
     if (M <= 16)
-        return launch_skinny4<1, 1>(a_codes, a_scales, M, codes, scales, zeros, K, N, y, y_f32, group_dots, st);
+        return launch_skinny4<1, 1, 4, kMaxSplitWaves>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32,
+                                                       group_dots, st);
     if (M <= 32)
-        return launch_skinny4<2, 1>(a_codes, a_scales, M, codes, scales, zeros, K, N, y, y_f32, group_dots, st);
+        return launch_skinny4<2, 1, 3, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, st);
     if (M <= 64)
-        return launch_skinny4<4, 1>(a_codes, a_scales, M, codes, scales, zeros, K, N, y, y_f32, group_dots, st);
+        return launch_skinny4<4, 1, 2, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, st);
     dim3 grid((N + QBN - 1) / QBN, (M + QBM - 1) / QBM);
-    hipLaunchKernelGGL(k_w4a4_tiled, grid, dim3(256), 0, st, a_codes, a_scales, M, codes, scales, zeros,
-                       K, N, y, y_f32, group_dots);
+    hipLaunchKernelGGL(k_w4a4_tiled, grid, dim3(256), 0, st, a_codes, a_scales, M, codes, meta, K, N, y, y_f32,
+                       group_dots);
     return hipGetLastError();
 }
 

@@ -11,12 +11,12 @@ namespace qspec {
 hipError_t launch_quantize_act(const uint16_t *x, int M, int K, uint8_t *codes, float *scales,
                                hipStream_t st);
 
-hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, const uint16_t *scales,
-                             const uint8_t *zeros, int K, int N, void *y, int y_f32, hipStream_t st);
+hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K,
+                             int N, void *y, int y_f32, hipStream_t st);
 
-hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M,
-                            const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
-                            int K, int N, void *y, int y_f32, int32_t *group_dots, hipStream_t st);
+hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M, const uint8_t *codes,
+                            const uint32_t *meta, int K, int N, void *y, int y_f32, int32_t *group_dots,
+                            hipStream_t st);
 
 size_t verify_workspace_bytes(int mode, int B, int gamma, int V);
 

@@ -14,6 +14,8 @@ inline int status_of(hipError_t e) { return e == hipSuccess ? QSPEC_OK : QSPEC_E
 
 inline bool bad_k(int32_t K) { return K < QSPEC_GROUP || K % QSPEC_GROUP != 0; }
 
+inline bool bad_n(int32_t N) { return N < 16 || N % 16 != 0; }
+
 inline hipStream_t as_stream(qspec_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -46,33 +48,31 @@ QSPEC_EXPORT int qspec_quantize_act(const uint16_t *x, int32_t M, int32_t K, uin
 }
 
 QSPEC_EXPORT int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int32_t M,
-                                 const uint8_t *w_codes, const uint16_t *w_scales,
-                                 const uint8_t *w_zeros, int32_t K, int32_t N, void *y,
-                                 int32_t y_dtype, int32_t *group_dots, qspec_stream_t stream) {
-    if (!a_codes || !a_scales || !w_codes || !w_scales || !w_zeros || !y) return QSPEC_ERR_NULL;
-    if (M < 1 || N < 1 || bad_k(K)) return QSPEC_ERR_SHAPE;
+                                 const uint8_t *w_codes, const uint32_t *w_meta, int32_t K, int32_t N,
+                                 void *y, int32_t y_dtype, int32_t *group_dots, qspec_stream_t stream) {
+    if (!a_codes || !a_scales || !w_codes || !w_meta || !y) return QSPEC_ERR_NULL;
+    if (M < 1 || bad_n(N) || bad_k(K)) return QSPEC_ERR_SHAPE;
     if ((long long)M * N > kMaxElems) return QSPEC_ERR_SHAPE;
     if (y_dtype != QSPEC_OUT_BF16 && y_dtype != QSPEC_OUT_F32) return QSPEC_ERR_UNSUPPORTED;
-    if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 4) || !aligned(w_scales, 2) ||
+    if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 4) || !aligned(w_meta, 4) ||
         !aligned(y, y_dtype == QSPEC_OUT_F32 ? 4 : 2) || !aligned(group_dots, 4))
         return QSPEC_ERR_ALIGN;
-    return status_of(qspec::launch_gemm_w4a4(a_codes, a_scales, M, w_codes, w_scales, w_zeros, K, N,
-                                             y, y_dtype == QSPEC_OUT_F32, group_dots,
-                                             as_stream(stream)));
+    return status_of(qspec::launch_gemm_w4a4(a_codes, a_scales, M, w_codes, w_meta, K, N, y,
+                                             y_dtype == QSPEC_OUT_F32, group_dots, as_stream(stream)));
 }
 
 QSPEC_EXPORT int qspec_gemm_w4a16(const uint16_t *x, int32_t M, const uint8_t *w_codes,
-                                  const uint16_t *w_scales, const uint8_t *w_zeros, int32_t K,
-                                  int32_t N, void *y, int32_t y_dtype, qspec_stream_t stream) {
-    if (!x || !w_codes || !w_scales || !w_zeros || !y) return QSPEC_ERR_NULL;
-    if (M < 1 || N < 1 || bad_k(K)) return QSPEC_ERR_SHAPE;
+                                  const uint32_t *w_meta, int32_t K, int32_t N, void *y, int32_t y_dtype,
+                                  qspec_stream_t stream) {
+    if (!x || !w_codes || !w_meta || !y) return QSPEC_ERR_NULL;
+    if (M < 1 || bad_n(N) || bad_k(K)) return QSPEC_ERR_SHAPE;
     if ((long long)M * N > kMaxElems) return QSPEC_ERR_SHAPE;
     if (y_dtype != QSPEC_OUT_BF16 && y_dtype != QSPEC_OUT_F32) return QSPEC_ERR_UNSUPPORTED;
-    if (!aligned(x, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 2) ||
+    if (!aligned(x, 16) || !aligned(w_codes, 16) || !aligned(w_meta, 4) ||
         !aligned(y, y_dtype == QSPEC_OUT_F32 ? 4 : 2))
         return QSPEC_ERR_ALIGN;
-    return status_of(qspec::launch_gemm_w4a16(x, M, w_codes, w_scales, w_zeros, K, N, y,
-                                              y_dtype == QSPEC_OUT_F32, as_stream(stream)));
+    return status_of(qspec::launch_gemm_w4a16(x, M, w_codes, w_meta, K, N, y, y_dtype == QSPEC_OUT_F32,
+                                              as_stream(stream)));
 }
 
 static bool verify_sizes_ok(int32_t B, int32_t gamma, int32_t V) {

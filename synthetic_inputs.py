@@ -5,9 +5,10 @@ it holds none of the method's arithmetic (no quantizer, no dequantization, no
 product, no softmax).  Both the oracle side and the HIP side read what it makes.
 
 Storage formats (fixed by this project):
-  weight codes  u8  [N][K/2]   two unsigned 4-bit codes per byte, even k in the low nibble
-  weight scales u16 [N][K/128] IEEE binary16 bit patterns
-  weight zeros  u8  [N][K/128] 0..15
+  weight codes  u8  [N/16][K/128][1024]  tile-major: block (t, g) holds columns 16t..16t+15 and
+                k = 128g..128g+127 as [quarter q = (k%128)/32][column c][16 bytes of k%32],
+                two unsigned 4-bit codes per byte, even k in the low nibble
+  weight meta   u32 [N/16][K/128][16]    binary16 scale in bits 0..15, zero point in bits 16..23
   activations   u16 [M][K]     bfloat16 bit patterns
   logits        f32
 
@@ -50,15 +51,47 @@ def f32_to_bf16_bits(a) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def pack_weights(codes_rm, scales_bits, zeros):
+    """Row-major weights -> the tile-major store.  codes_rm u8 [N][K/2] (even k low nibble),
+    scales_bits u16 [N][K/128] (binary16), zeros u8 [N][K/128] -> (codes u8 [N/16][G][1024],
+    meta u32 [N/16][G][16]).  Pure layout: no arithmetic on the values."""
+    codes_rm = np.ascontiguousarray(codes_rm, np.uint8)
+    N, K2 = codes_rm.shape
+    assert N % 16 == 0 and (2 * K2) % GROUP == 0
+    G = 2 * K2 // GROUP
+    # [N][K/2] -> [t][c][g][q][16] -> [t][g][q][c][16]
+    blocks = codes_rm.reshape(N // 16, 16, G, 4, 16).transpose(0, 2, 3, 1, 4)
+    codes = np.ascontiguousarray(blocks).reshape(N // 16, G, 1024)
+    meta = (np.asarray(scales_bits, np.uint32) | (np.asarray(zeros, np.uint32) << np.uint32(16)))
+    meta = np.ascontiguousarray(meta.reshape(N // 16, 16, G).transpose(0, 2, 1))
+    return codes, meta
+
+
+def unpack_weights(codes, meta):
+    """Inverse of pack_weights: (codes_rm u8 [N][K/2], scales_bits u16 [N][G], zeros u8 [N][G])."""
+    T, G, _ = codes.shape
+    rm = np.ascontiguousarray(codes.reshape(T, G, 4, 16, 16).transpose(0, 3, 1, 2, 4)).reshape(16 * T, G * 64)
+    m = np.ascontiguousarray(meta.transpose(0, 2, 1)).reshape(16 * T, G)
+    return rm, (m & np.uint32(0xFFFF)).astype(np.uint16), ((m >> np.uint32(16)) & np.uint32(0xFF)).astype(np.uint8)
+
+
+def slice_tiles(w: dict, tiles) -> dict:
+    """The sub-store of the given 16-column tiles (columns 16t..16t+15 of each tile t)."""
+    tiles = np.asarray(tiles)
+    return {"codes": np.ascontiguousarray(w["codes"][tiles]), "meta": np.ascontiguousarray(w["meta"][tiles]),
+            "K": w["K"], "N": 16 * len(tiles)}
+
+
 def weights(K: int, N: int, seed: int) -> dict:
-    """Shared INT4 weights: codes [N][K/2], fp16 scales [N][K/128], zeros [N][K/128]."""
-    assert K % GROUP == 0
+    """Shared INT4 weights in the tile-major store (see pack_weights)."""
+    assert K % GROUP == 0 and N % 16 == 0
     G = K // GROUP
     r = rng(SEED_WEIGHTS + seed)
-    codes = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    codes_rm = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     scales = r.uniform(1e-3, 1e-2, size=(N, G)).astype(np.float16).view(np.uint16)
     zeros = r.integers(0, 16, size=(N, G), dtype=np.uint8)
-    return {"codes": codes, "scales": scales, "zeros": zeros, "K": K, "N": N}
+    codes, meta = pack_weights(codes_rm, scales, zeros)
+    return {"codes": codes, "meta": meta, "K": K, "N": N}
 
 
 def outlier_channels(K: int, seed: int) -> np.ndarray:
@@ -120,3 +153,60 @@ QWEN25_7B_PROJ = {"qkv": (3584, 4608), "o": (3584, 3584), "gate_up": (3584, 2 * 
                   "down": (18944, 3584), "lm_head": (3584, 152064)}
 LLAMA3_70B_FFN = {"gate_up": (8192, 2 * 28672), "down": (28672, 8192)}
 SMALL_LAYER = {"proj": (512, 512)}
+
+
+# ---- device-side generators for large benchmark inputs (same distributions) -----------------
+# torch.Generator streams seeded from the same table; used where host generation and copies of
+# gigabytes of weights would dominate start-up.
+
+def _gen(device, base: int, seed: int):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(base * 1_000_003 + seed)
+    return g
+
+
+def weights_device(K: int, N: int, seed: int, device):
+    """(codes u8 [N/16][G][1024], meta i32 [N/16][G][16]) drawn directly in the tile-major store."""
+    import torch
+
+    G = K // GROUP
+    g = _gen(device, SEED_WEIGHTS, seed)
+    codes = torch.randint(0, 256, (N // 16, G, 1024), dtype=torch.uint8, device=device, generator=g)
+    scales = (torch.rand((N // 16, G, 16), device=device, generator=g) * 9e-3 + 1e-3).to(torch.float16)
+    zeros = torch.randint(0, 16, (N // 16, G, 16), dtype=torch.int32, device=device, generator=g)
+    meta = (scales.view(torch.int16).to(torch.int32) & 0xFFFF) | (zeros << 16)
+    return codes, meta
+
+
+def activations_device(M: int, K: int, seed: int, device):
+    import torch
+
+    x = torch.randn((M, K), device=device, generator=_gen(device, SEED_ACT, seed))
+    cols = torch.from_numpy(outlier_channels(K, seed)).to(device)
+    x[:, cols] *= 20.0
+    return x.to(torch.bfloat16)
+
+
+def logits_device(B: int, gamma: int, V: int, seed: int, device, sigma: float = 3.0, noise: float = 0.5):
+    import torch
+
+    t = torch.randn((B, gamma + 1, V), device=device, generator=_gen(device, SEED_LOGITS, seed)) * sigma
+    e = torch.randn((B, gamma, V), device=device, generator=_gen(device, SEED_NOISE, seed)) * noise
+    return t, (t[:, :gamma, :] + e).contiguous()
+
+
+def draft_tokens_sampled_device(draft, seed: int):
+    """Gumbel-max draws from softmax(draft row), on the device."""
+    import torch
+
+    u = torch.rand(draft.shape, device=draft.device, generator=_gen(draft.device, SEED_GUMBEL, seed))
+    gumbel = -torch.log(-torch.log(u.clamp_min(1e-20)))
+    return torch.argmax(draft + gumbel, dim=-1).to(torch.int32)
+
+
+def uniforms_device(shape, seed: int, device):
+    import torch
+
+    return torch.rand(shape, device=device, generator=_gen(device, SEED_UNIFORM, seed))

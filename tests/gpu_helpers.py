@@ -30,7 +30,8 @@ def bf16_dev(bits):
 
 
 def weights_dev(w):
-    return cu(w["codes"]), cu(w["scales"].view(np.float16)), cu(w["zeros"])
+    """(codes u8 [N/16][G][1024], meta i32 [N/16][G][16]) on the device."""
+    return cu(w["codes"]), cu(np.ascontiguousarray(w["meta"]).view(np.int32))
 
 
 def host_f64(t: torch.Tensor) -> np.ndarray:

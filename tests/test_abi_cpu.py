@@ -55,17 +55,19 @@ def test_quantize_act_validation():
 
 def test_gemm_validation():
     L = q.lib()
-    args = [FAKE, FAKE, 4, FAKE, FAKE, FAKE, 256, 64, FAKE, 0, None, None]
-    for i in (0, 1, 3, 4, 5, 8):
+    args = [FAKE, FAKE, 4, FAKE, FAKE, 256, 64, FAKE, 0, None, None]
+    for i in (0, 1, 3, 4, 7):
         bad = list(args)
         bad[i] = None
         assert L.qspec_gemm_w4a4(*bad) == ERR_NULL, i
-    for (M, K, N) in [(0, 256, 64), (4, 200, 64), (4, 256, 0), (-1, 256, 64), (4, 64, 64)]:
-        assert L.qspec_gemm_w4a4(FAKE, FAKE, M, FAKE, FAKE, FAKE, K, N, FAKE, 0, None, None) == ERR_SHAPE
-    assert L.qspec_gemm_w4a4(FAKE, FAKE, 4, FAKE, FAKE, FAKE, 256, 64, FAKE, 7, None, None) == ERR_UNSUPPORTED
-    assert L.qspec_gemm_w4a16(None, 4, FAKE, FAKE, FAKE, 256, 64, FAKE, 0, None) == ERR_NULL
-    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, FAKE, 129, 64, FAKE, 0, None) == ERR_SHAPE
-    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, FAKE, 256, 64, FAKE, 2, None) == ERR_UNSUPPORTED
+    for (M, K, N) in [(0, 256, 64), (4, 200, 64), (4, 256, 0), (-1, 256, 64), (4, 64, 64), (4, 256, 40)]:
+        assert L.qspec_gemm_w4a4(FAKE, FAKE, M, FAKE, FAKE, K, N, FAKE, 0, None, None) == ERR_SHAPE
+    assert L.qspec_gemm_w4a4(FAKE, FAKE, 4, FAKE, FAKE, 256, 64, FAKE, 7, None, None) == ERR_UNSUPPORTED
+    assert L.qspec_gemm_w4a16(None, 4, FAKE, FAKE, 256, 64, FAKE, 0, None) == ERR_NULL
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, None, 256, 64, FAKE, 0, None) == ERR_NULL
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 129, 64, FAKE, 0, None) == ERR_SHAPE
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 256, 72, FAKE, 0, None) == ERR_SHAPE
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 256, 64, FAKE, 2, None) == ERR_UNSUPPORTED
 
 
 def test_verify_validation_and_workspace_sizes():
@@ -107,8 +109,8 @@ def test_alignment_validation():
     L = q.lib()
     odd = ctypes.c_void_p(0x1001)
     assert L.qspec_quantize_act(odd, 1, 128, FAKE, FAKE, None) == ERR_ALIGN
-    assert L.qspec_gemm_w4a16(FAKE, 4, ctypes.c_void_p(0x1008), FAKE, FAKE, 256, 64, FAKE, 0, None) == ERR_ALIGN
-    assert L.qspec_gemm_w4a4(FAKE, odd, 4, FAKE, FAKE, FAKE, 256, 64, FAKE, 1, None, None) == ERR_ALIGN
+    assert L.qspec_gemm_w4a16(FAKE, 4, ctypes.c_void_p(0x1008), FAKE, 256, 64, FAKE, 0, None) == ERR_ALIGN
+    assert L.qspec_gemm_w4a4(FAKE, odd, 4, FAKE, FAKE, 256, 64, FAKE, 1, None, None) == ERR_ALIGN
     need = L.qspec_verify_workspace_bytes(0, 2, 3, 5000)
     assert L.qspec_verify_accept(0, FAKE, None, FAKE, None, None, 2, 3, 5000, FAKE, FAKE,
                                  ctypes.c_void_p(0x1004), need, None) == ERR_ALIGN

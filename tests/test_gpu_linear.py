@@ -29,10 +29,14 @@ def run_quant(x_bits):
 
 def run_w4a16(x_bits, w, out=torch.bfloat16, wdev=None):
     M = x_bits.shape[0]
-    wc, ws, wz = wdev if wdev is not None else weights_dev(w)
+    wc, wm = wdev if wdev is not None else weights_dev(w)
     y = torch.empty((M, w["N"]), dtype=out, device=DEV)
-    q.qspec_gemm_w4a16(bf16_dev(x_bits), wc, ws, wz, y)
+    q.qspec_gemm_w4a16(bf16_dev(x_bits), wc, wm, y)
     return y
+
+
+def tile_columns(tiles):
+    return (16 * np.asarray(tiles)[:, None] + np.arange(16)[None, :]).ravel()
 
 
 # ---------------------------------------------------------------- quantizer
@@ -65,9 +69,11 @@ def test_quantize_act_edge_values():
 
 # ---------------------------------------------------------------- W4A16
 
-SMALL_W4A16 = [(1, 128, 16), (5, 512, 512), (3, 384, 40), (17, 640, 100), (20, 256, 72),
-               (33, 384, 52), (48, 256, 36), (64, 128, 16), (80, 512, 144), (81, 256, 130),
-               (200, 384, 260), (130, 640, 7)]
+# N is a multiple of the 16-column storage tile but ragged against the 32-column skinny tiles and
+# the 128-column tiled-kernel tiles; K spans several groups; M is ragged against the 16-row tiles.
+SMALL_W4A16 = [(1, 128, 16), (5, 512, 512), (3, 384, 48), (17, 640, 112), (20, 256, 80),
+               (33, 384, 48), (48, 256, 32), (64, 128, 16), (80, 512, 144), (81, 256, 144),
+               (200, 384, 272), (130, 640, 16)]
 
 
 @pytest.mark.parametrize("M,K,N", SMALL_W4A16)
@@ -77,35 +83,37 @@ def test_w4a16_small(M, K, N, out):
     w = si.weights(K, N, seed=M * 7 + N)
     x = si.activations(M, K, seed=M + 1000)
     y = run_w4a16(x, w, out)
-    ref = oracle.gemm_w4a16(x, w["codes"], w["scales"], w["zeros"])
+    ref = oracle.gemm_w4a16(x, w["codes"], w["meta"])
     assert_close(host_f64(y), ref, out == torch.bfloat16, f"w4a16 {M}x{K}x{N}")
 
 
 @pytest.mark.parametrize("M", [16, 96])
 def test_w4a16_one_hot_rows_reproduce_dequantized_weights_exactly(M):
     """x = e_k gives y = W_hat[k] with a single exact product: checks the dequantization bits."""
-    K, N = 512, 100
+    K, N = 512, 112
     note(f"gemm_w4a16 one-hot M={M}")
     w = si.weights(K, N, seed=3)
     ks = si.rng(M).choice(K, size=M, replace=False)
     x = np.zeros((M, K), np.float32)
     x[np.arange(M), ks] = 1.0
     y = run_w4a16(si.f32_to_bf16_bits(x), w, torch.float32)
-    what = oracle.dequant(w["codes"], w["scales"], w["zeros"])            # u16 [N][K]
+    what = oracle.dequant(w["codes"], w["meta"])                          # u16 [N][K]
     ref = np.vectorize(oracle.bf16_to_double)(what[:, ks].T)
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
 def test_w4a16_rows_do_not_depend_on_batch():
-    """Every M in the skinny range reduces a row in the same order: bitwise-equal rows."""
-    K, N = 1024, 200
+    """Every M in one batch tier reduces a row in the same order: bitwise-equal rows."""
+    K, N = 1024, 208
     note("gemm_w4a16 batch invariance")
     w = si.weights(K, N, seed=4)
     wdev = weights_dev(w)
     x = si.activations(80, K, seed=4)
-    full = {M: run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy() for M in (1, 5, 17, 20, 33, 80)}
-    for M, y in full.items():
-        assert np.array_equal(y, full[80][:M]), M
+    full = {M: run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy() for M in (1, 5, 16, 17, 20, 33, 80)}
+    for M in (1, 5):                     # tier M <= 16
+        assert np.array_equal(full[M], full[16][:M]), M
+    for M in (17, 20, 33):               # tier 16 < M <= 80
+        assert np.array_equal(full[M], full[80][:M]), M
 
 
 FULL_W4A16 = [
@@ -127,17 +135,19 @@ def test_w4a16_full_shapes_sampled_columns(name, K, N, M):
     x = si.activations(M, K, seed=M)
     out = torch.float32 if name.endswith("lm_head") else torch.bfloat16
     y = run_w4a16(x, w, out)
-    cols = np.sort(si.rng(N).choice(N, size=24, replace=False))
+    tiles = np.sort(si.rng(N).choice(N // 16, size=2, replace=False))
+    cols = tile_columns(tiles)
     rows = np.arange(M) if M <= 80 else np.sort(si.rng(M).choice(M, size=64, replace=False))
-    ref = oracle.gemm_w4a16(x[rows], w["codes"][cols], w["scales"][cols], w["zeros"][cols])
+    sub = si.slice_tiles(w, tiles)
+    ref = oracle.gemm_w4a16(x[rows], sub["codes"], sub["meta"])
     got = host_f64(y)[np.ix_(rows, cols)]
     assert_close(got, ref, out == torch.bfloat16, name)
 
 
 # ---------------------------------------------------------------- W4A4
 
-SMALL_W4A4 = [(1, 128, 16), (1, 512, 512), (4, 384, 40), (16, 640, 100), (5, 256, 7),
-              (17, 384, 52), (33, 256, 36), (64, 128, 48), (65, 256, 130), (256, 512, 260), (100, 384, 16)]
+SMALL_W4A4 = [(1, 128, 16), (1, 512, 512), (4, 384, 48), (16, 640, 112), (5, 256, 16),
+              (17, 384, 48), (33, 256, 32), (64, 128, 48), (65, 256, 144), (256, 512, 272), (100, 384, 16)]
 
 
 @pytest.mark.parametrize("M,K,N", SMALL_W4A4)
@@ -148,17 +158,17 @@ def test_w4a4_small_exact_dots_and_outputs(M, K, N):
     codes, scales = run_quant(x)
     oc, osc = oracle.quantize_act(x)
     assert np.array_equal(codes.cpu().numpy(), oc)
-    wc, ws, wz = weights_dev(w)
+    wc, wm = weights_dev(w)
     dots = torch.full((K // 128, M, N), -(2 ** 31), dtype=torch.int32, device=DEV)
     for out in (torch.bfloat16, torch.float32):
         y = torch.empty((M, N), dtype=out, device=DEV)
-        q.qspec_gemm_w4a4(codes, scales, wc, ws, wz, y, group_dots=dots)
-        ref, D = oracle.gemm_w4a4(oc, osc, w["codes"], w["scales"], w["zeros"])
+        q.qspec_gemm_w4a4(codes, scales, wc, wm, y, group_dots=dots)
+        ref, D = oracle.gemm_w4a4(oc, osc, w["codes"], w["meta"])
         assert np.array_equal(dots.cpu().numpy().astype(np.int64), D)
         assert_close(host_f64(y), ref, out == torch.bfloat16, f"w4a4 {M}x{K}x{N}")
         # the diagnostic output does not change y
         y2 = torch.empty_like(y)
-        q.qspec_gemm_w4a4(codes, scales, wc, ws, wz, y2)
+        q.qspec_gemm_w4a4(codes, scales, wc, wm, y2)
         assert torch.equal(y, y2)
 
 
@@ -166,12 +176,12 @@ def test_w4a4_rows_do_not_depend_on_batch():
     K, N = 1024, 96
     note("gemm_w4a4 batch invariance")
     w = si.weights(K, N, seed=8)
-    wc, ws, wz = weights_dev(w)
+    wc, wm = weights_dev(w)
     codes, scales = run_quant(si.activations(64, K, seed=8))
     ys = {}
     for M in (1, 4, 16, 33, 64):
         y = torch.empty((M, N), dtype=torch.float32, device=DEV)
-        q.qspec_gemm_w4a4(codes[:M].contiguous(), scales[:M].contiguous(), wc, ws, wz, y)
+        q.qspec_gemm_w4a4(codes[:M].contiguous(), scales[:M].contiguous(), wc, wm, y)
         ys[M] = y.cpu().numpy()
     for M in (1, 4, 16):
         assert np.array_equal(ys[M], ys[16][:M])
@@ -195,9 +205,10 @@ def test_w4a4_full_shapes_sampled_columns(name, K, N, M):
     oc, osc = oracle.quantize_act(x)
     assert np.array_equal(codes.cpu().numpy(), oc)
     out = torch.float32 if name.endswith("lm_head") else torch.bfloat16
-    wc, ws, wz = weights_dev(w)
+    wc, wm = weights_dev(w)
     y = torch.empty((M, N), dtype=out, device=DEV)
-    q.qspec_gemm_w4a4(codes, scales, wc, ws, wz, y)
-    cols = np.sort(si.rng(N + 1).choice(N, size=24, replace=False))
-    ref, _ = oracle.gemm_w4a4(oc, osc, w["codes"][cols], w["scales"][cols], w["zeros"][cols], want_dots=False)
-    assert_close(host_f64(y)[:, cols], ref, out == torch.bfloat16, name)
+    q.qspec_gemm_w4a4(codes, scales, wc, wm, y)
+    tiles = np.sort(si.rng(N + 1).choice(N // 16, size=2, replace=False))
+    sub = si.slice_tiles(w, tiles)
+    ref, _ = oracle.gemm_w4a4(oc, osc, sub["codes"], sub["meta"], want_dots=False)
+    assert_close(host_f64(y)[:, tile_columns(tiles)], ref, out == torch.bfloat16, name)

@@ -116,18 +116,29 @@ def test_dequant_w_equal_z_is_zero():
 
 
 def test_dequant_layout_nibble_and_group_placement():
-    K, N = 384, 3
+    """Single planted codes land where the tile-major layout definition puts them."""
+    import synthetic_inputs as si
+    K, N = 384, 48
     codes = np.zeros((N, K // 2), np.uint8)
     one = np.float16(1.0).view(np.uint16)
     scales = np.full((N, K // 128), one, np.uint16)
     zeros = np.zeros((N, K // 128), np.uint8)
-    codes[1, 70] = 0x5A          # k = 140 -> low nibble 0xA, k = 141 -> high nibble 0x5
-    scales[1, 1] = np.float16(0.5).view(np.uint16)   # group 1 covers k = 128..255
+    codes[17, 70] = 0x5A          # column 17, k = 140 -> low nibble 0xA, k = 141 -> high nibble 0x5
+    codes[33, 191] = 0x0C         # column 33, k = 382 (last group, last quarter)
+    scales[17, 1] = np.float16(0.5).view(np.uint16)   # group 1 covers k = 128..255
     zeros[2, 2] = 3
-    w = np.vectorize(oracle.bf16_to_double)(oracle.dequant(codes, scales, zeros))
+    tc, meta = si.pack_weights(codes, scales, zeros)
+    assert tc.shape == (3, 3, 1024) and meta.shape == (3, 3, 16)
+    # byte of (n=17, k=140): tile 1, group 1, quarter 0, column 1, byte 6
+    assert tc[1, 1, 0 * 256 + 1 * 16 + 6] == 0x5A
+    assert tc[2, 2, 3 * 256 + 1 * 16 + 15] == 0x0C
+    assert meta[1, 1, 1] == (np.uint32(np.float16(0.5).view(np.uint16)))
+    assert meta[0, 2, 2] == (np.uint32(one) | np.uint32(3 << 16))
+    w = np.vectorize(oracle.bf16_to_double)(oracle.dequant(tc, meta))
     expect = np.zeros((N, K))
-    expect[1, 140] = 10 * 0.5
-    expect[1, 141] = 5 * 0.5
+    expect[17, 140] = 10 * 0.5
+    expect[17, 141] = 5 * 0.5
+    expect[33, 382] = 12.0
     expect[2, 256:384] = -3.0
     assert np.array_equal(w, expect)
 

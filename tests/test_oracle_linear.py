@@ -121,67 +121,79 @@ def test_quantizer_zero_group_and_packing():
 
 # ---------------------------------------------------------------- W4A16
 
-@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (5, 384, 40), (3, 512, 7)])
+def rowmajor(w):
+    """(codes [N][K], scales f64 [N][G], zeros i64 [N][G]) of a tile-major store, via numpy layout ops."""
+    rm, sb, z = si.unpack_weights(w["codes"], w["meta"])
+    return unpack_unsigned(rm), sb.view(np.float16).astype(np.float64), z.astype(np.int64)
+
+
+def with_params(w, scales_bits=None, zeros=None):
+    rm, sb, z = si.unpack_weights(w["codes"], w["meta"])
+    sb = sb if scales_bits is None else np.broadcast_to(np.asarray(scales_bits, np.uint16), sb.shape)
+    z = z if zeros is None else np.broadcast_to(np.asarray(zeros, np.uint8), z.shape)
+    c, m = si.pack_weights(rm, sb, z)
+    return {"codes": c, "meta": m, "K": w["K"], "N": w["N"]}
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (5, 384, 48), (3, 512, 16)])
 def test_w4a16_unit_scale_reduces_to_plain_matmul(M, K, N):
-    w = si.weights(K, N, seed=M)
-    w["scales"][:] = np.float16(1.0).view(np.uint16)
-    w["zeros"][:] = 0
+    w = with_params(si.weights(K, N, seed=M), scales_bits=np.float16(1.0).view(np.uint16), zeros=0)
     x = si.activations(M, K, seed=N)
-    y = oracle.gemm_w4a16(x, w["codes"], w["scales"], w["zeros"])
-    ref = bf16_to_f64(x) @ unpack_unsigned(w["codes"]).astype(np.float64).T
+    y = oracle.gemm_w4a16(x, w["codes"], w["meta"])
+    W, _, _ = rowmajor(w)
+    ref = bf16_to_f64(x) @ W.astype(np.float64).T
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("M,K,N", [(2, 256, 24), (5, 640, 33)])
+@pytest.mark.parametrize("M,K,N", [(2, 256, 32), (5, 640, 48)])
 def test_w4a16_matches_matmul_with_dequantized_weights(M, K, N):
     w = si.weights(K, N, seed=7 + M)
     x = si.activations(M, K, seed=3)
-    y = oracle.gemm_w4a16(x, w["codes"], w["scales"], w["zeros"])
-    what = bf16_to_f64(oracle.dequant(w["codes"], w["scales"], w["zeros"]))   # [N][K]
+    y = oracle.gemm_w4a16(x, w["codes"], w["meta"])
+    what = bf16_to_f64(oracle.dequant(w["codes"], w["meta"]))   # [N][K]
     ref = bf16_to_f64(x) @ what.T
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
-    # zero points shift every output by -z*s*sum(x) per group: recomputed by hand
-    w2 = dict(w)
-    w2["zeros"] = np.zeros_like(w["zeros"])
-    w2["scales"] = np.full_like(w["scales"], np.float16(2.0 ** -6).view(np.uint16))
-    y2 = oracle.gemm_w4a16(x, w["codes"], w2["scales"], w2["zeros"])
-    ref2 = bf16_to_f64(x) @ (unpack_unsigned(w["codes"]).astype(np.float64).T * 2.0 ** -6)
+    # power-of-two scale and zero point 0: W_hat = w * 2^-6 exactly, recomputed by hand
+    w2 = with_params(w, scales_bits=np.float16(2.0 ** -6).view(np.uint16), zeros=0)
+    y2 = oracle.gemm_w4a16(x, w2["codes"], w2["meta"])
+    W, _, _ = rowmajor(w2)
+    ref2 = bf16_to_f64(x) @ (W.astype(np.float64).T * 2.0 ** -6)
     assert np.allclose(y2, ref2, rtol=1e-12, atol=1e-12)
 
 
 # ---------------------------------------------------------------- W4A4
 
-@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (4, 512, 24), (3, 384, 5)])
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (4, 512, 32), (3, 384, 16)])
 def test_w4a4_group_dots_exact(M, K, N):
     w = si.weights(K, N, seed=20 + M)
     x = si.activations(M, K, seed=21)
     ac, asc = oracle.quantize_act(x)
-    y, D = oracle.gemm_w4a4(ac, asc, w["codes"], w["scales"], w["zeros"])
+    y, D = oracle.gemm_w4a4(ac, asc, w["codes"], w["meta"])
+    W, s, z = rowmajor(w)
     qa = unpack_signed(ac).reshape(M, K // 128, 128)
-    wu = unpack_unsigned(w["codes"]).reshape(N, K // 128, 128) - w["zeros"][..., None].astype(np.int64)
+    wu = W.reshape(N, K // 128, 128) - z[..., None]
     ref = np.einsum("mgk,ngk->gmn", qa, wu)
     assert np.array_equal(D, ref)
     assert np.abs(D).max() <= 7 * 15 * 128
     # y is the scale-weighted sum of the exact group dots
-    s = np.array([oracle.fp16_to_double(b) for b in w["scales"].ravel()]).reshape(N, K // 128)
     yref = np.einsum("mg,ng,gmn->mn", asc.astype(np.float64), s, D.astype(np.float64))
     assert np.allclose(y, yref, rtol=1e-12, atol=1e-15)
 
 
 def test_w4a4_zero_point_equal_to_code_gives_zero():
-    K, N, M = 256, 8, 2
-    w = si.weights(K, N, seed=5)
-    w["codes"][:] = 0x77       # every code 7
-    w["zeros"][:] = 7
+    K, N, M = 256, 16, 2
+    rm, sb, _ = si.unpack_weights(*[si.weights(K, N, seed=5)[k] for k in ("codes", "meta")])
+    rm[:] = 0x77       # every code 7
+    c, m = si.pack_weights(rm, sb, np.full(sb.shape, 7, np.uint8))
     ac, asc = oracle.quantize_act(si.activations(M, K, seed=5))
-    y, D = oracle.gemm_w4a4(ac, asc, w["codes"], w["scales"], w["zeros"])
+    y, D = oracle.gemm_w4a4(ac, asc, c, m)
     assert np.all(D == 0) and np.all(y == 0)
 
 
 def test_w4a4_on_grid_activations_match_exact_dequant_product():
     """When x already lies on its own quantization grid, W4A4 equals X (s (W - z))
     computed with the exact (unrounded) dequantized weights."""
-    M, K, N = 3, 384, 12
+    M, K, N = 3, 384, 16
     r = np.random.default_rng(9)
     q = r.integers(-7, 8, size=(M, K)).astype(np.float32)
     q[:, ::128] = 7                                           # absmax 7 in every group
@@ -191,21 +203,21 @@ def test_w4a4_on_grid_activations_match_exact_dequant_product():
     ac, asc = oracle.quantize_act(xb)
     assert np.array_equal(asc, step)                          # s_a = 7*step/7 exactly
     w = si.weights(K, N, seed=9)
-    y, _ = oracle.gemm_w4a4(ac, asc, w["codes"], w["scales"], w["zeros"])
-    s = np.array([oracle.fp16_to_double(b) for b in w["scales"].ravel()]).reshape(N, K // 128)
-    wexact = (unpack_unsigned(w["codes"]) - np.repeat(w["zeros"].astype(np.int64), 128, axis=1)) \
-        * np.repeat(s, 128, axis=1)
+    y, _ = oracle.gemm_w4a4(ac, asc, w["codes"], w["meta"])
+    W, s, z = rowmajor(w)
+    wexact = (W - np.repeat(z, 128, axis=1)) * np.repeat(s, 128, axis=1)
     ref = x.astype(np.float64) @ wexact.T
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-14)
 
 
 def test_w4a4_dots_are_linear_in_activation_codes():
-    K, N = 256, 6
+    K, N = 256, 16
     w = si.weights(K, N, seed=31)
     e = np.zeros((1, K), np.float32)
     e[0, 130] = 7.0                      # one-hot activation: code 7 at k = 130, scale 1
     ac, asc = oracle.quantize_act(si.f32_to_bf16_bits(e))
-    _, D = oracle.gemm_w4a4(ac, asc, w["codes"], w["scales"], w["zeros"])
-    col = unpack_unsigned(w["codes"])[:, 130] - w["zeros"][:, 1].astype(np.int64)
+    _, D = oracle.gemm_w4a4(ac, asc, w["codes"], w["meta"])
+    W, _, z = rowmajor(w)
+    col = W[:, 130] - z[:, 1]
     assert np.array_equal(D[1, 0], 7 * col)
     assert np.all(D[0] == 0)
