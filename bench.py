@@ -49,6 +49,103 @@ def w4a16_alg_bytes(M, K, N):
     return w4_bytes(K, N) + 2 * M * K + 2 * M * N
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_JSON = os.path.join(PROFILES, "pmc_traffic.json")
+COPY_MIB = 256
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; counter figures are only reused while it is unchanged."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_speculative_decoding_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def summarize(args):
+    """rocprofv3 CSVs -> profiles/*.md and profiles/pmc_traffic.json."""
+    import collections
+    import csv
+    import glob
+
+    def find(d, suffix):
+        hits = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+        if not hits:
+            raise SystemExit(f"no *{suffix} under {d}")
+        return hits[0]
+
+    trace_dir, fetch_dir, write_dir = args.summarize
+    stats = list(csv.DictReader(open(find(trace_dir, "kernel_stats.csv"))))
+    os.makedirs(PROFILES, exist_ok=True)
+    lines = ["# rocprofv3 kernel statistics: one QSPEC round, Llama-3-8B-shaped projections (32 layers, B=16, gamma=4)",
+             "", "Command (run from /tmp with TMPDIR=/tmp):", "", "```", args.summary_command or "(not recorded)", "```",
+             "", "| kernel | calls | avg us | total % |", "|---|---:|---:|---:|"]
+    for r in stats[:16]:
+        name = r["Name"].split("(")[0]
+        lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    open(os.path.join(PROFILES, "kernel_trace_llama3_8b_round_B16_g4.md"), "w").write("\n".join(lines) + "\n")
+
+    def per_dispatch(d):
+        rows = list(csv.DictReader(open(find(d, "counter_collection.csv"))))
+        agg = collections.defaultdict(list)
+        calib = None
+        for r in rows:
+            key = r["Kernel_Name"].split("(")[0]
+            agg[(key, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+            if "copyBuffer" in r["Kernel_Name"]:
+                calib = float(r["Counter_Value"])      # the last copy is the calibration copy
+        return agg, calib
+
+    fetch, fcal = per_dispatch(fetch_dir)
+    write, wcal = per_dispatch(write_dir)
+    known_kib = COPY_MIB * 1024.0
+    ffac = known_kib / fcal if fcal else None
+    wfac = known_kib / wcal if wcal else None
+    out = {"src_hash": kernel_source_hash(), "copy_mib": COPY_MIB, "fetch_factor": ffac, "write_factor": wfac,
+           "kernels": {}}
+    md = ["# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE; separate runs)", "",
+          f"Copy calibration: a {COPY_MIB} MiB device-to-device copy reads {fcal} KiB on FETCH_SIZE and writes "
+          f"{wcal} KiB on WRITE_SIZE, so FETCH_SIZE is scaled by {ffac:.4f} and WRITE_SIZE by {wfac:.4f}.", "",
+          "Command:", "", "```", args.summary_command or "(not recorded)", "```", "",
+          "| kernel | grid | dispatches | fetch MB (scaled) | write MB (scaled) |", "|---|---:|---:|---:|---:|"]
+    for (k, grid), v in sorted(fetch.items(), key=lambda kv: -sum(kv[1])):
+        if not k.startswith("void qspec::") and not k.startswith("qspec::"):
+            continue
+        f = sum(v) / len(v) * 1024 * ffac
+        w = write.get((k, grid))
+        wb = (sum(w) / len(w) * 1024 * wfac) if w else 0.0
+        md.append(f"| `{k}` | {grid} | {len(v)} | {f / 1e6:.3f} | {wb / 1e6:.3f} |")
+        ent = out["kernels"].setdefault(k, {"fetch_bytes": 0.0, "write_bytes": 0.0, "dispatches": 0})
+        ent["fetch_bytes"] += f * len(v)
+        ent["write_bytes"] += wb * len(v)
+        ent["dispatches"] += len(v)
+    for k, e in out["kernels"].items():
+        e["bytes_per_dispatch"] = (e["fetch_bytes"] + e["write_bytes"]) / e["dispatches"]
+    open(os.path.join(PROFILES, "pmc_traffic_llama3_8b_round.md"), "w").write("\n".join(md) + "\n")
+    json.dump(out, open(TRAFFIC_JSON, "w"), indent=1)
+    print(f"wrote profiles/ (src_hash {out['src_hash']})")
+
+
+def traffic_for(kernel_prefix: str):
+    """Counter-measured HBM bytes per dispatch of a kernel, if taken on the current sources."""
+    try:
+        d = json.load(open(TRAFFIC_JSON))
+    except (OSError, ValueError):
+        return None
+    if d.get("src_hash") != kernel_source_hash():
+        return None
+    hits = [e for k, e in d["kernels"].items() if kernel_prefix in k]
+    if not hits:
+        return None
+    disp = sum(e["dispatches"] for e in hits)
+    return (sum(e["fetch_bytes"] + e["write_bytes"] for e in hits)) / disp
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,6 +157,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this size (for counter scaling)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 CSV output and exit (no GPU needed)")
+    ap.add_argument("--summary-command", default="", help="the command that produced the profiles (recorded)")
     return ap.parse_args()
 
 
@@ -285,6 +385,9 @@ def cpu_leg(args):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: every box here has one MI355X and this build has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -304,6 +407,8 @@ def main():
         bytes_per_launch = R.verify_gemm_bytes() / nl
         launch_ms = verify_ms / nl
     achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
+    tb = traffic_for("k_w4a4_skinny" if dom == "gemm_w4a4" else "k_w4a16_skinny")
+    traffic = None if tb is None else round(tb)
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -322,7 +427,7 @@ def main():
                    "vocab": VOCAB, "kv_cache": f"{args.layers}x{B}x2x{KV_HEADS}x{CONTEXT}x{HEAD_DIM} bf16",
                    "verify_mode": "sample"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": int(bytes_per_launch), "us_per_launch": round(launch_ms * 1e3, 3)},
         "phases_ms_per_round": {k: round(v, 4) for k, v in ph.items()},
         "event_ms_per_round": round(event_ms, 4),
