@@ -188,6 +188,7 @@ class Round:
                         for _ in range(L)]
         self.y_draft = [torch.empty((B, N), dtype=torch.bfloat16, device=dev) for _, (K, N) in self.projs]
         self.y_verify = [torch.empty((B * (g + 1), N), dtype=torch.bfloat16, device=dev) for _, (K, N) in self.projs]
+        self.ws_verify = [q.gemm_w4a16_workspace(B * (g + 1), K, N, dev) for _, (K, N) in self.projs]
         # verification: 4 rotating logit sets (4 x 74 MB at B = 16) so no replay reads a cached set
         self.n_logit_sets = 4
         self.logits = []
@@ -221,7 +222,7 @@ class Round:
         for l in range(self.L):
             for i in range(len(self.projs)):
                 wc, wm = self.weights[l][i]
-                self.q.qspec_gemm_w4a16(self.x_verify[i], wc, wm, self.y_verify[i])
+                self.q.qspec_gemm_w4a16(self.x_verify[i], wc, wm, self.y_verify[i], self.ws_verify[i])
 
     def accept_phase(self, s):
         t, d, toks, u, v = self.logits[s]

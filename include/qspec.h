@@ -20,7 +20,8 @@
  * Conventions for every call
  *   - Every pointer argument is DEVICE memory (hipMalloc'd or a torch CUDA
  *     tensor), allocated, owned and freed by the caller.  The library never
- *     allocates or frees memory and keeps no state between calls.
+ *     allocates or frees memory and keeps no state between calls (workspaces
+ *     are the caller's).
  *   - Calls are asynchronous: they validate their arguments on the host, enqueue
  *     kernels on `stream` (a hipStream_t; NULL = the legacy default stream) and
  *     return without synchronizing.  Results are visible after the caller
@@ -121,6 +122,12 @@ int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int32_t M,
                     int32_t y_dtype, int32_t *group_dots, qspec_stream_t stream);
 
 /*
+ * qspec_gemm_w4a16_workspace_bytes -- device workspace qspec_gemm_w4a16 needs for (M, K, N); 0
+ * when the shape needs none (M <= 16, M > 80, or a shape whose K is not split) or on invalid sizes.
+ */
+size_t qspec_gemm_w4a16_workspace_bytes(int32_t M, int32_t K, int32_t N);
+
+/*
  * qspec_gemm_w4a16 -- W4A16 verify linear layer over the shared 4-bit weights.
  * [QSPEC notes, background terms: dequantization example, Y = X W_hat with
  * W_hat = s (W_INT4 - z) in 16 bits; QSPEC structure: the verifier scores the
@@ -130,14 +137,20 @@ int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int32_t M,
  * x   [in]  u16 [M][K] bfloat16
  * w_codes, w_meta [in] the shared weight store (the same arrays the W4A4 layer reads)
  * y   [out] [M][N], bfloat16 (nearest-even) or f32 per y_dtype
+ * workspace [in/out] at least qspec_gemm_w4a16_workspace_bytes(M, K, N) bytes, 256-byte aligned
+ *           (NULL allowed when that is 0).  It receives the fp32 partial sums of the K splits,
+ *           [S][M][N], which a second kernel on the same stream adds in split order; its contents
+ *           need no initialization.  Calls sharing a workspace must be ordered on one stream.
  * Batch invariance: the reduction order of an output depends only on (K, N) and on the
  * batch tier of M -- [1, 16], (16, 80] or above 80 -- so row m of y is bit-identical for every
  * M in the same tier; verifying gamma+1 <= 16 positions therefore reproduces one-position
  * decoding bit for bit.
- * Errors: NULL pointer; M < 1; N < 1 or N % 16 != 0; K < 128 or K % 128 != 0; bad y_dtype.
+ * Errors: NULL pointer; M < 1; N < 1 or N % 16 != 0; K < 128 or K % 128 != 0; bad y_dtype;
+ * workspace missing or too small.
  */
 int qspec_gemm_w4a16(const uint16_t *x, int32_t M, const uint8_t *w_codes, const uint32_t *w_meta,
-                     int32_t K, int32_t N, void *y, int32_t y_dtype, qspec_stream_t stream);
+                     int32_t K, int32_t N, void *y, int32_t y_dtype, void *workspace,
+                     size_t workspace_bytes, qspec_stream_t stream);
 
 /*
  * qspec_verify_workspace_bytes -- device workspace qspec_verify_accept needs

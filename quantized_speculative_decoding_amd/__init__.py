@@ -54,7 +54,9 @@ def lib() -> ctypes.CDLL:
         L.qspec_status_string.restype = ctypes.c_char_p
         L.qspec_quantize_act.argtypes = [P, I, I, P, P, P]
         L.qspec_gemm_w4a4.argtypes = [P, P, I, P, P, I, I, P, I, P, P]
-        L.qspec_gemm_w4a16.argtypes = [P, I, P, P, I, I, P, I, P]
+        L.qspec_gemm_w4a16.argtypes = [P, I, P, P, I, I, P, I, P, S, P]
+        L.qspec_gemm_w4a16_workspace_bytes.argtypes = [I, I, I]
+        L.qspec_gemm_w4a16_workspace_bytes.restype = S
         L.qspec_verify_workspace_bytes.argtypes = [I, I, I, I]
         L.qspec_verify_workspace_bytes.restype = S
         L.qspec_verify_accept.argtypes = [I, P, P, P, P, P, I, I, I, P, P, P, S, P]
@@ -139,16 +141,29 @@ def qspec_gemm_w4a4(a_codes, a_scales, w_codes, w_meta, y, group_dots=None, stre
                                  _ptr(y), dt, _ptr(group_dots), _stream(stream, y)))
 
 
-def qspec_gemm_w4a16(x, w_codes, w_meta, y, stream=None) -> None:
-    """W4A16 verify layer: y [M][N] = x W_hat (bf16 or f32 out)."""
+def qspec_gemm_w4a16_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(lib().qspec_gemm_w4a16_workspace_bytes(M, K, N))
+
+
+def gemm_w4a16_workspace(M: int, K: int, N: int, device) -> torch.Tensor:
+    """A workspace of the size qspec_gemm_w4a16 needs (at least one byte; no initialization needed)."""
+    return torch.empty(max(1, qspec_gemm_w4a16_workspace_bytes(M, K, N)), dtype=torch.uint8, device=device)
+
+
+def qspec_gemm_w4a16(x, w_codes, w_meta, y, workspace=None, stream=None) -> None:
+    """W4A16 verify layer: y [M][N] = x W_hat (bf16 or f32 out).  ``workspace``: a uint8
+    device tensor of qspec_gemm_w4a16_workspace_bytes(M, K, N) bytes (None if that is 0)."""
     K, N = _weights(w_codes, w_meta)
     _req(x, "x", torch.bfloat16)
     M = x.shape[0]
     _req(x, "x", torch.bfloat16, (M, K))
     dt = _out_dtype(y)
     _req(y, "y", y.dtype, (M, N))
+    if workspace is not None:
+        _req(workspace, "workspace", torch.uint8)
     _check("qspec_gemm_w4a16",
            lib().qspec_gemm_w4a16(_ptr(x), M, _ptr(w_codes), _ptr(w_meta), K, N, _ptr(y), dt,
+                                  _ptr(workspace), workspace.numel() if workspace is not None else 0,
                                   _stream(stream, y)))
 
 
@@ -202,6 +217,7 @@ def qspec_kv_overwrite(cache, verify_kv, start_pos, accept_count, stream=None) -
 
 __all__ = [
     "GROUP", "QSPEC_GREEDY", "QSPEC_SAMPLE", "QSPEC_OUT_BF16", "QSPEC_OUT_F32", "QspecError", "lib",
-    "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_verify_workspace_bytes",
+    "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_gemm_w4a16_workspace_bytes",
+    "gemm_w4a16_workspace", "qspec_verify_workspace_bytes",
     "qspec_verify_accept", "qspec_kv_overwrite",
 ]

@@ -21,6 +21,24 @@ __device__ __forceinline__ uint4 load_stream16(const void *p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Buffer loads: a wave-uniform resource (base address and size in SGPRs), a 32-bit per-lane
+// offset and a wave-uniform offset.  Reads past `bytes` return zero instead of faulting.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufCachePolicyNT = 2;   // non-temporal: streamed once
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint4 buf_load16_stream(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kBufCachePolicyNT));
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
     return __uint_as_float(b << 16);
 }

@@ -205,6 +205,273 @@ k_w4a16_skinny(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
+// Mid kernel (16 < M <= 80): verify shapes near the MFMA ridge, where the activation tile of a
+// group (M x 128 bf16, 20 KB at M = 80) is as large as 20 weight blocks and has to be shared.
+//
+// A workgroup = 8 waves = 2 K halves x 4 column waves; each wave owns MID_NT = 2 column tiles, so
+// the workgroup covers 8 tiles (128 columns) of one K split, with two waves per SIMD (a single
+// wave per SIMD issues MFMA and VALU work at about half the rate two waves reach).  Per group, the
+// four waves of a K half stage the half's activation tile into LDS in fragment-major order
+// (fragment f = (row tile, 32-k step), lane l's 16 bytes at f * 1 KB + 16 l: conflict-free
+// 128-bit reads and writes), and every wave reads all fragments from there, each fragment
+// feeding MID_NT MFMAs.  Activations and weights travel through one U-deep register ring in group
+// order (the in-order vmcnt wait for a stage never covers a younger one); a stage's activations
+// are written to LDS one step before they are consumed, its weights are dequantized in registers
+// when consumed.  One barrier per step.  The two K halves are added in LDS (half 0 + half 1).
+// With S > 1 K splits (a function of (K, N) only), each workgroup writes an fp32 partial tile and
+// k_w4a16_splitk_reduce adds the S partials in split order, so every output has one fixed
+// reduction order per (K, N).
+constexpr int MID_NT = 2;                // column tiles per wave
+constexpr int MID_CW = 4;                // column waves per K half
+constexpr int MID_TILES = MID_CW * MID_NT;   // column tiles per workgroup
+constexpr int MID_THREADS = 2 * MID_CW * 64;
+
+template <int MT, int U>
+__global__ void __launch_bounds__(MID_THREADS)
+k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
+            const uint32_t *__restrict__ meta, int K, int N, void *__restrict__ y, int y_f32, int S,
+            float *__restrict__ partials) {
+    constexpr int NF = MT * 4;        // activation fragments per group
+    constexpr int NFW = NF / MID_CW;  // staged by each wave of a K half
+    __shared__ uint4 abuf[2][2][NF * 64];   // [K half][buffer][fragment][lane]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    const int kh = wave / MID_CW, cw = wave % MID_CW;
+    const int col = lane & 15, kq = lane >> 4;
+    const int G = K / kGroup;
+    const int T = N / 16;
+    const int split = blockIdx.y;
+    const int gs0 = (split * G) / S;
+    const int n = ((split + 1) * G) / S - gs0;
+    const int hstart = gs0 + (kh ? n / 2 : 0);
+    const int nh = kh ? n - n / 2 : n / 2;   // groups of this half (half 0 may have one less)
+    const int nsteps = n - n / 2;            // both halves step together
+    const int hlast = max(nh, 1) - 1;
+    const int tile0 = blockIdx.x * MID_TILES + cw * MID_NT;
+
+    // Buffer resources per column tile (SGPRs) plus one 32-bit lane offset per stream; the
+    // group index enters as the wave-uniform offset.
+    rsrc_t wr[MID_NT], mr[MID_NT];
+#pragma unroll
+    for (int nt = 0; nt < MID_NT; ++nt) {
+        const int t = min(tile0 + nt, T - 1);              // ragged tile tail: clamp the loads
+        wr[nt] = make_rsrc(codes + (size_t)t * G * 1024, (uint32_t)G * 1024);
+        mr[nt] = make_rsrc(meta + (size_t)t * G * 16, (uint32_t)G * 64);
+    }
+    const rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
+    // Activation staging: load q = cw * NFW + u of a K half reads rows 4 q .. 4 q + 3 of the
+    // group, 16 lanes per row (row-contiguous: 8 cache lines per load).  The 16 bytes of (row, 8-k
+    // chunk c) are element (row % 16, k = 8 c) of fragment f = 4 (row / 16) + c % 4, i.e. lane
+    // l = row % 16 + 16 (c / 4) of it; they are stored at slot l ^ c of the fragment's 1 KB block.
+    // The swizzle keeps the 16 lanes of a row on distinct banks, and a reader lane l of fragment
+    // (row tile, 32-k step j) finds its data at slot l ^ (4 (l / 16) + j).
+    uint32_t xoff[NFW], xslot[NFW];
+#pragma unroll
+    for (int u = 0; u < NFW; ++u) {
+        const int row = 4 * (cw * NFW + u) + (lane >> 4);
+        const int c = lane & 15;
+        xoff[u] = (uint32_t)(min(row, M - 1) * K + c * 8) * 2;
+        xslot[u] = (uint32_t)((4 * (row >> 4) + (c & 3)) * 64 + (((row & 15) + 16 * (c >> 2)) ^ c));
+    }
+    const int rslot = lane ^ (4 * kq);   // reader slot, before the 32-k step j
+
+    struct Stage {
+        uint4 w[MID_NT];
+        uint32_t m[MID_NT];
+        uint4 a[NFW];
+    };
+    // Group i of the half; a refill past the end re-reads the first group (long since arrived)
+    // rather than a group whose load may still be in flight.
+    auto load = [&](Stage &st, int i) {
+        const uint32_t g = (uint32_t)(hstart + (i <= hlast ? i : 0));
+#pragma unroll
+        for (int nt = 0; nt < MID_NT; ++nt) {
+            st.w[nt] = buf_load16_stream(wr[nt], lane * 16, g * 1024);
+            st.m[nt] = buf_load4(mr[nt], col * 4, g * 64);
+        }
+#pragma unroll
+        for (int u = 0; u < NFW; ++u) st.a[u] = buf_load16(xr, xoff[u], g * 256);
+    };
+    auto stage_act = [&](const Stage &st, int buf) {
+#pragma unroll
+        for (int u = 0; u < NFW; ++u) abuf[kh][buf][xslot[u]] = st.a[u];
+    };
+
+    f32x4_t acc[MT][MID_NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < MID_NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const Stage &st, int buf) {
+        DqConst dq[MID_NT];
+#pragma unroll
+        for (int nt = 0; nt < MID_NT; ++nt) dq[nt] = make_dq(st.m[nt]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x8_t av[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                av[mt] = __builtin_bit_cast(bf16x8_t, abuf[kh][buf][(mt * 4 + j) * 64 + (rslot ^ j)]);
+#pragma unroll
+            for (int nt = 0; nt < MID_NT; ++nt) {
+                const uint32_t word = j == 0 ? st.w[nt].x : j == 1 ? st.w[nt].y : j == 2 ? st.w[nt].z : st.w[nt].w;
+                uint32_t b[4];
+                dequant8(word, dq[nt], b);
+                const bf16x8_t bv = as_bf16x8(b[0], b[1], b[2], b[3]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, acc[mt][nt], 0, 0, 0);
+            }
+        }
+    };
+
+    // Ring slot s % U holds group s.  Step i first refills slot (i + U - 1) % U (it held group
+    // i - 1: weights consumed at step i - 1, activations staged at step i - 2) with group
+    // i + U - 1, then consumes the weights of slot i % U and writes the activations of slot
+    // (i + 1) % U to LDS for step i + 1.  The refill loads are spread through the MFMA / VALU
+    // stream.  The steady loop never runs the last step and loads unconditionally (indices past
+    // the end re-read the first group), so no load is predicated there.
+    Stage st[U];
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u) {
+        load(st[u], u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    stage_act(st[0], 0);
+    __syncthreads();
+    constexpr int NMFMA = MT * MID_NT * 4;   // per step
+    auto interleave = [&]() {
+#pragma unroll
+        for (int k = 0; k < NMFMA; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);       // four VALU
+            if (k % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one load
+        }
+    };
+    const int nfull = ((nsteps - 1) / U) * U;
+    for (int base = 0; base < nfull; base += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u;
+            load(st[(u + U - 1) % U], i + U - 1);
+            compute(st[u], i & 1);
+            interleave();
+            __builtin_amdgcn_sched_barrier(0);
+            stage_act(st[(u + 1) % U], (i + 1) & 1);
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = nfull + u;
+        if (i < nsteps) {                        // uniform over the workgroup
+            if (i + U - 1 < nsteps) load(st[(u + U - 1) % U], i + U - 1);
+            if (i < nh) compute(st[u], i & 1);   // half 0 may have one group less
+            if (i + 1 < nsteps) {
+                stage_act(st[(u + 1) % U], (i + 1) & 1);
+                __syncthreads();
+            }
+        }
+    }
+    __syncthreads();   // every wave is done reading the staging buffers
+
+    // Epilogue.  (1) Half 1 hands its accumulators to half 0 through LDS (the staging buffers
+    // are free); (2) half 0 adds them (half 0 + half 1) and (3) writes the sums row-major into
+    // LDS; (4) all four waves store the M x 128 block in 16-byte pieces: bfloat16 / f32 output,
+    // or the fp32 partial of this split.
+    constexpr int NACC = MT * MID_NT * 4;
+    constexpr int OPITCH = 128 + 4;             // floats per output row in LDS
+    float *red = (float *)&abuf[0][0][0];
+    static_assert(MID_CW * NACC * 64 <= 2 * 2 * NF * 64 * 4, "hand-over buffer");
+    static_assert(MT * 16 * OPITCH <= 2 * 2 * NF * 64 * 4, "output buffer");
+    if (kh == 1) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < MID_NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[(cw * NACC + (mt * MID_NT + nt) * 4 + r) * 64 + lane] = acc[mt][nt][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < MID_NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[mt][nt][r] += red[(cw * NACC + (mt * MID_NT + nt) * 4 + r) * 64 + lane];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < MID_NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    red[(16 * mt + 4 * kq + r) * OPITCH + cw * (MID_NT * 16) + 16 * nt + col] = acc[mt][nt][r];
+    }
+    __syncthreads();
+    const int n0 = blockIdx.x * MID_TILES * 16;
+    const int ncols = min(MID_TILES * 16, N - n0);   // a multiple of 16
+    if (S > 1 || y_f32) {
+        float *dst = S > 1 ? partials + (size_t)split * M * N : (float *)y;
+        for (int e = tid; e < M * 32; e += MID_THREADS) {     // 4 floats per thread
+            const int m = e >> 5, c = (e & 31) * 4;
+            if (c < ncols) *(float4 *)(dst + (size_t)m * N + n0 + c) = *(const float4 *)(red + m * OPITCH + c);
+        }
+    } else {
+        uint16_t *dst = (uint16_t *)y;
+        for (int e = tid; e < M * 16; e += MID_THREADS) {     // 8 outputs per thread
+            const int m = e >> 4, c = (e & 15) * 8;
+            if (c < ncols) {
+                const float4 lo = *(const float4 *)(red + m * OPITCH + c);
+                const float4 hi = *(const float4 *)(red + m * OPITCH + c + 4);
+                uint4 o;
+                o.x = pack_bf16x2(lo.x, lo.y);
+                o.y = pack_bf16x2(lo.z, lo.w);
+                o.z = pack_bf16x2(hi.x, hi.y);
+                o.w = pack_bf16x2(hi.z, hi.w);
+                *(uint4 *)(dst + (size_t)m * N + n0 + c) = o;
+            }
+        }
+    }
+}
+
+// y = sum of the S <= kMaxSplits fp32 partials in split order (4 outputs per thread; M * N is a
+// multiple of 16).  All S loads are issued before the first add.
+constexpr int kMaxSplits = 16;
+
+__global__ void __launch_bounds__(256)
+k_w4a16_splitk_reduce(const float *__restrict__ partials, int S, size_t MN, void *__restrict__ y, int y_f32) {
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= MN) return;
+    float4 v[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+        if (s < S) v[s] = *(const float4 *)(partials + (size_t)s * MN + i);
+    float4 a = v[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSplits; ++s)
+        if (s < S) {
+            a.x += v[s].x;
+            a.y += v[s].y;
+            a.z += v[s].z;
+            a.w += v[s].w;
+        }
+    if (y_f32) {
+        *(float4 *)((float *)y + i) = a;
+    } else {
+        uint2 o;
+        o.x = pack_bf16x2(a.x, a.y);
+        o.y = pack_bf16x2(a.z, a.w);
+        *(uint2 *)((uint16_t *)y + i) = o;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Tiled kernel for large M.  256 threads = 4 waves in a 2x2 arrangement over a 128x128 tile.
 constexpr int TBM = 128, TBN = 128, TBK = kGroup;
 constexpr int TLDS = TBK + 8;   // padded row pitch (bf16 elements) against bank conflicts
@@ -304,15 +571,48 @@ static hipError_t launch_skinny(const uint16_t *x, int M, const uint8_t *codes, 
     return hipGetLastError();
 }
 
+// K splits of the mid kernel: a function of (K, N) only.  Column blocks alone fill the chip when
+// there are at least 192 of them; otherwise split K until about 256 workgroups exist, keeping at
+// least 4 groups (2 per K half) per split and at most kMaxSplits splits.
+static int mid_splits(int K, int N) {
+    const int G = K / kGroup;
+    const int cbs = (N / 16 + MID_TILES - 1) / MID_TILES;
+    if (cbs >= 192) return 1;
+    const int want = (256 + cbs - 1) / cbs;
+    return max(1, min(min(want, kMaxSplits), G / 4));
+}
+
+size_t gemm_w4a16_workspace_bytes(int M, int K, int N) {
+    if (M <= 16 || M > 80) return 0;
+    const int S = mid_splits(K, N);
+    return S == 1 ? 0 : (size_t)S * M * N * sizeof(float);
+}
+
+template <int MT, int U>
+static hipError_t launch_mid(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K, int N,
+                             void *y, int y_f32, void *ws, hipStream_t st) {
+    const int S = mid_splits(K, N);
+    const int cbs = (N / 16 + MID_TILES - 1) / MID_TILES;
+    float *partials = S > 1 ? (float *)ws : nullptr;
+    hipLaunchKernelGGL((k_w4a16_mid<MT, U>), dim3(cbs, S), dim3(MID_THREADS), 0, st, x, M, codes, meta, K, N, y, y_f32, S,
+                       partials);
+    if (S > 1) {
+        const size_t MN = (size_t)M * N;
+        const unsigned blocks = (unsigned)((MN / 4 + 255) / 256);
+        hipLaunchKernelGGL(k_w4a16_splitk_reduce, dim3(blocks), dim3(256), 0, st, partials, S, MN, y, y_f32);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K,
-                             int N, void *y, int y_f32, hipStream_t st) {
-    // Two batch tiers, each with one reduction order for all its M: M <= 16 and 16 < M <= 80
-    // (the latter at most 4 waves per tile, so its larger activation stages fit in registers).
+                             int N, void *y, int y_f32, void *ws, hipStream_t st) {
+    // Batch tiers, each with one reduction order for all its M: M <= 16 (skinny), 16 < M <= 80
+    // (mid, split-K), M > 80 (tiled).
     if (M <= 16) return launch_skinny<1, 1, 4, kMaxSplitWaves>(x, M, codes, meta, K, N, y, y_f32, st);
-    if (M <= 32) return launch_skinny<2, 2, 2, 4>(x, M, codes, meta, K, N, y, y_f32, st);
-    if (M <= 48) return launch_skinny<3, 2, 2, 4>(x, M, codes, meta, K, N, y, y_f32, st);
-    if (M <= 64) return launch_skinny<4, 2, 2, 4>(x, M, codes, meta, K, N, y, y_f32, st);
-    if (M <= 80) return launch_skinny<5, 2, 2, 4>(x, M, codes, meta, K, N, y, y_f32, st);
+    if (M <= 32) return launch_mid<2, 6>(x, M, codes, meta, K, N, y, y_f32, ws, st);
+    if (M <= 48) return launch_mid<3, 5>(x, M, codes, meta, K, N, y, y_f32, ws, st);
+    if (M <= 64) return launch_mid<4, 4>(x, M, codes, meta, K, N, y, y_f32, ws, st);
+    if (M <= 80) return launch_mid<5, 4>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     dim3 grid((N + TBN - 1) / TBN, (M + TBM - 1) / TBM);
     hipLaunchKernelGGL(k_w4a16_tiled, grid, dim3(256), 0, st, x, M, codes, meta, K, N, y, y_f32);
     return hipGetLastError();

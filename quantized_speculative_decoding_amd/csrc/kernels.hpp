@@ -12,7 +12,9 @@ hipError_t launch_quantize_act(const uint16_t *x, int M, int K, uint8_t *codes, 
                                hipStream_t st);
 
 hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K,
-                             int N, void *y, int y_f32, hipStream_t st);
+                             int N, void *y, int y_f32, void *workspace, hipStream_t st);
+
+size_t gemm_w4a16_workspace_bytes(int M, int K, int N);
 
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M, const uint8_t *codes,
                             const uint32_t *meta, int K, int N, void *y, int y_f32, int32_t *group_dots,

@@ -61,18 +61,25 @@ QSPEC_EXPORT int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, 
                                              y_dtype == QSPEC_OUT_F32, group_dots, as_stream(stream)));
 }
 
+QSPEC_EXPORT size_t qspec_gemm_w4a16_workspace_bytes(int32_t M, int32_t K, int32_t N) {
+    if (M < 1 || bad_n(N) || bad_k(K) || (long long)M * N > kMaxElems) return 0;
+    return qspec::gemm_w4a16_workspace_bytes(M, K, N);
+}
+
 QSPEC_EXPORT int qspec_gemm_w4a16(const uint16_t *x, int32_t M, const uint8_t *w_codes,
                                   const uint32_t *w_meta, int32_t K, int32_t N, void *y, int32_t y_dtype,
-                                  qspec_stream_t stream) {
+                                  void *workspace, size_t workspace_bytes, qspec_stream_t stream) {
     if (!x || !w_codes || !w_meta || !y) return QSPEC_ERR_NULL;
     if (M < 1 || bad_n(N) || bad_k(K)) return QSPEC_ERR_SHAPE;
     if ((long long)M * N > kMaxElems) return QSPEC_ERR_SHAPE;
     if (y_dtype != QSPEC_OUT_BF16 && y_dtype != QSPEC_OUT_F32) return QSPEC_ERR_UNSUPPORTED;
+    const size_t need = qspec::gemm_w4a16_workspace_bytes(M, K, N);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return QSPEC_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(w_codes, 16) || !aligned(w_meta, 4) ||
-        !aligned(y, y_dtype == QSPEC_OUT_F32 ? 4 : 2))
+        !aligned(y, y_dtype == QSPEC_OUT_F32 ? 4 : 2) || !aligned(workspace, 256))
         return QSPEC_ERR_ALIGN;
     return status_of(qspec::launch_gemm_w4a16(x, M, w_codes, w_meta, K, N, y, y_dtype == QSPEC_OUT_F32,
-                                              as_stream(stream)));
+                                              workspace, as_stream(stream)));
 }
 
 static bool verify_sizes_ok(int32_t B, int32_t gamma, int32_t V) {

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "qspec_status_string", "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16",
-        "qspec_verify_workspace_bytes", "qspec_verify_accept", "qspec_kv_overwrite"])
+        "qspec_gemm_w4a16_workspace_bytes", "qspec_verify_workspace_bytes", "qspec_verify_accept",
+        "qspec_kv_overwrite"])
 
 
 def test_library_exports_every_declared_symbol_and_nothing_else():
@@ -63,11 +64,18 @@ def test_gemm_validation():
     for (M, K, N) in [(0, 256, 64), (4, 200, 64), (4, 256, 0), (-1, 256, 64), (4, 64, 64), (4, 256, 40)]:
         assert L.qspec_gemm_w4a4(FAKE, FAKE, M, FAKE, FAKE, K, N, FAKE, 0, None, None) == ERR_SHAPE
     assert L.qspec_gemm_w4a4(FAKE, FAKE, 4, FAKE, FAKE, 256, 64, FAKE, 7, None, None) == ERR_UNSUPPORTED
-    assert L.qspec_gemm_w4a16(None, 4, FAKE, FAKE, 256, 64, FAKE, 0, None) == ERR_NULL
-    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, None, 256, 64, FAKE, 0, None) == ERR_NULL
-    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 129, 64, FAKE, 0, None) == ERR_SHAPE
-    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 256, 72, FAKE, 0, None) == ERR_SHAPE
-    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 256, 64, FAKE, 2, None) == ERR_UNSUPPORTED
+    assert L.qspec_gemm_w4a16(None, 4, FAKE, FAKE, 256, 64, FAKE, 0, None, 0, None) == ERR_NULL
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, None, 256, 64, FAKE, 0, None, 0, None) == ERR_NULL
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 129, 64, FAKE, 0, None, 0, None) == ERR_SHAPE
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 256, 72, FAKE, 0, None, 0, None) == ERR_SHAPE
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 256, 64, FAKE, 2, None, 0, None) == ERR_UNSUPPORTED
+    # split-K verify shapes need a workspace; decode shapes need none
+    assert L.qspec_gemm_w4a16_workspace_bytes(4, 4096, 4096) == 0
+    need = L.qspec_gemm_w4a16_workspace_bytes(80, 4096, 4096)
+    assert need >= 80 * 4096 * 4 * 2
+    assert L.qspec_gemm_w4a16(FAKE, 80, FAKE, FAKE, 4096, 4096, FAKE, 0, None, 0, None) == ERR_WS
+    assert L.qspec_gemm_w4a16(FAKE, 80, FAKE, FAKE, 4096, 4096, FAKE, 0, FAKE, need - 1, None) == ERR_WS
+    assert L.qspec_gemm_w4a16_workspace_bytes(80, 4096, 70) == 0
 
 
 def test_verify_validation_and_workspace_sizes():
@@ -109,7 +117,7 @@ def test_alignment_validation():
     L = q.lib()
     odd = ctypes.c_void_p(0x1001)
     assert L.qspec_quantize_act(odd, 1, 128, FAKE, FAKE, None) == ERR_ALIGN
-    assert L.qspec_gemm_w4a16(FAKE, 4, ctypes.c_void_p(0x1008), FAKE, 256, 64, FAKE, 0, None) == ERR_ALIGN
+    assert L.qspec_gemm_w4a16(FAKE, 4, ctypes.c_void_p(0x1008), FAKE, 256, 64, FAKE, 0, None, 0, None) == ERR_ALIGN
     assert L.qspec_gemm_w4a4(FAKE, odd, 4, FAKE, FAKE, 256, 64, FAKE, 1, None, None) == ERR_ALIGN
     need = L.qspec_verify_workspace_bytes(0, 2, 3, 5000)
     assert L.qspec_verify_accept(0, FAKE, None, FAKE, None, None, 2, 3, 5000, FAKE, FAKE,

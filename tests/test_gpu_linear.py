@@ -27,11 +27,13 @@ def run_quant(x_bits):
     return codes, scales
 
 
-def run_w4a16(x_bits, w, out=torch.bfloat16, wdev=None):
+def run_w4a16(x_bits, w, out=torch.bfloat16, wdev=None, ws=None):
     M = x_bits.shape[0]
     wc, wm = wdev if wdev is not None else weights_dev(w)
     y = torch.empty((M, w["N"]), dtype=out, device=DEV)
-    q.qspec_gemm_w4a16(bf16_dev(x_bits), wc, wm, y)
+    if ws is None:
+        ws = q.gemm_w4a16_workspace(M, w["K"], w["N"], DEV)
+    q.qspec_gemm_w4a16(bf16_dev(x_bits), wc, wm, y, ws)
     return y
 
 
@@ -114,6 +116,28 @@ def test_w4a16_rows_do_not_depend_on_batch():
         assert np.array_equal(full[M], full[16][:M]), M
     for M in (17, 20, 33):               # tier 16 < M <= 80
         assert np.array_equal(full[M], full[80][:M]), M
+
+
+@pytest.mark.parametrize("M,K,N", [(80, 4096, 4096), (20, 14336, 512), (33, 2048, 784)])
+def test_w4a16_split_k_workspace_reuse(M, K, N):
+    """Split-K verify shapes: the workspace needs no initialization (it starts as NaN bytes here)
+    and repeated calls on it give identical results."""
+    note(f"gemm_w4a16 split-K reuse M={M} K={K} N={N}")
+    w = si.weights(K, N, seed=K + N)
+    wdev = weights_dev(w)
+    x = si.activations(M, K, seed=5)
+    need = q.qspec_gemm_w4a16_workspace_bytes(M, K, N)
+    assert need > 0 and need % (4 * M * N) == 0
+    ws = q.gemm_w4a16_workspace(M, K, N, DEV)
+    ws.fill_(0xFF)
+    outs = [run_w4a16(x, w, torch.float32, wdev, ws).cpu().numpy() for _ in range(3)]
+    assert all(np.array_equal(o, outs[0]) for o in outs)
+    assert np.isfinite(outs[0]).all()
+    tiles = np.array([0, 7, 8, N // 16 - 1])
+    cols = tile_columns(tiles)
+    sub = si.slice_tiles(w, tiles)
+    assert_close(outs[0][:, cols].astype(np.float64), oracle.gemm_w4a16(x, sub["codes"], sub["meta"]), False,
+                 "split-K")
 
 
 FULL_W4A16 = [
