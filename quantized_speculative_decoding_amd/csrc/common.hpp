@@ -97,4 +97,30 @@ __host__ __device__ inline int skinny_waves_for_shape(int K, int N) {
     return kw < 1 ? 1 : kw;
 }
 
+// Decode kernels (M <= 16): column tiles per workgroup (nt) and K-splitting waves (kw), a
+// function of (K, N) only, so the reduction order is too.  Chosen from measured sweeps over the
+// Llama-3-8B / Qwen2.5-7B projection shapes: about 500 - 2000 waves in flight, wider workgroups
+// rather than more K splits, two groups per wave at least.
+constexpr int kMaxDecodeWaves = 8;
+
+struct DecodeShape {
+    int nt, kw;
+};
+
+__host__ __device__ inline DecodeShape decode_shape(int K, int N, bool w4a4) {
+    const int T = N / 16, G = K / kGroup;
+    DecodeShape d;
+    if (T >= 4096) {
+        d = {4, 1};
+    } else if (T >= 1024) {
+        d = {2, 1};
+    } else if (T >= 384) {
+        d = {2, 4};
+    } else {
+        d = {1, w4a4 ? 4 : 2};
+    }
+    while (d.kw > 1 && 2 * d.kw > G) d.kw >>= 1;
+    return d;
+}
+
 }  // namespace qspec

@@ -9,15 +9,13 @@
 // exactly the 32 codes its v_mfma_f32_16x16x32_bf16 B fragments need.  Every wave-wide weight
 // load is one contiguous kilobyte.
 //
-// Two kernels share the dequantization routine:
-//  * k_w4a16_skinny (M <= 80): HBM-bound decode/verify shapes.  A workgroup owns NT column tiles
-//    and KW waves split the K groups between them; every wave keeps U groups of loads in flight,
-//    dequantizes in registers and feeds the MFMA with the activations as the A operand (rows =
-//    tokens, padded to 16) and W_hat as the B operand.  Wave partials are summed through LDS in
-//    a fixed order, so the reduction order depends on (K, N) and the batch tier only.
-//  * k_w4a16_tiled (M > 80): MFMA-bound shapes.  128x128 output tiles, one K group per step; the
-//    activation tile and the dequantized weight tile are staged in LDS and each of the 4 waves
-//    computes a 64x64 sub-tile with 16 MFMAs per 32-wide k step.
+// Three kernels share the dequantization routine, one per batch tier:
+//  * k_w4a16_decode (M <= 16): HBM-bound decode / short-verify shapes; NT column tiles per
+//    workgroup, K groups split between its waves, activations in registers.
+//  * k_w4a16_mid (16 < M <= 80): verify shapes near the MFMA ridge; 8 waves share each group's
+//    activation tile through LDS, optional K split across workgroups with an ordered reduction.
+//  * k_w4a16_tiled (M > 80): MFMA-bound shapes; 128x128 output tiles with the activation tile and
+//    the dequantized weight tile staged in LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -81,29 +79,32 @@ __device__ __forceinline__ void store_out(void *y, int y_f32, size_t idx, float 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Skinny kernel.  Lane l: col = l % 16 (B column / A row), kq = l / 16 (k quarter of a group).
-// In MFMA j (0..3) of a group, k slot (kq, i) holds k = 128 g + 32 kq + 8 j + i for both operands.
-// Output of v_mfma_f32_16x16x32_bf16: lane l, element r holds D[4 (l / 16) + r][l % 16].
+// Decode kernel (M <= 16): HBM-bound decode / short-verify shapes.  Lane l: col = l % 16 (B
+// column / A row), kq = l / 16 (k quarter of a group).  In MFMA j (0..3) of a group, k slot
+// (kq, i) holds k = 128 g + 32 kq + 8 j + i for both operands.  Output of
+// v_mfma_f32_16x16x32_bf16: lane l, element r holds D[4 (l / 16) + r][l % 16].
 //
-// Memory pipeline: one stage holds everything a group needs (codes and meta of NT column tiles,
-// and the lane's 64 bytes of activations for MT row tiles).  U stages are in flight; each stage
-// is consumed in place and refilled with group i + U, and a scheduling barrier keeps the stages'
-// loads in group order, so the in-order vmcnt wait for a stage never covers a younger one.  Rows
-// past M read row M - 1 (their MFMA rows are discarded), so no load is predicated.
-template <int MT, int NT>
-struct W16Stage {
+// A workgroup owns NT column tiles and KW waves split the K groups; every wave loads the group's
+// activations once (64 bytes per lane) and feeds them to the 4 NT MFMAs of its tiles.  Loads are
+// buffer loads from wave-uniform bases through a U-deep register ring: each stage is consumed in
+// place and refilled with group i + U, and a scheduling barrier keeps the stages' loads in group
+// order, so the in-order vmcnt wait for a stage never covers a younger one.  Rows past M read row
+// M - 1 (their MFMA rows are discarded).  Wave partials are summed through LDS in wave order, so
+// the reduction order depends on (K, N) only.
+template <int NT>
+struct W16DStage {
     uint4 w[NT];
     uint32_t meta[NT];
-    uint4 a[MT][4];
+    uint4 a[4];
 };
 
-template <int MT, int NT, int U, int MAXW>
-__global__ void __launch_bounds__(64 * MAXW)
-k_w4a16_skinny(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
+template <int NT, int U>
+__global__ void __launch_bounds__(64 * kMaxDecodeWaves)
+k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
                const uint32_t *__restrict__ meta, int K, int N, void *__restrict__ y, int y_f32, int kw) {
-    __shared__ float red[kMaxSplitWaves * 4 * 64];   // [kw][4][64]
+    __shared__ float red[kMaxDecodeWaves * 4 * 64];   // [kw][4][64]
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int G = K / kGroup;
@@ -112,40 +113,33 @@ k_w4a16_skinny(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
     const int T = N / 16;
     const int tbase = blockIdx.x * NT;
 
-    const uint8_t *wblk[NT];
-    const uint32_t *mblk[NT];
+    rsrc_t wr[NT], mr[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int t = min(tbase + nt, T - 1);                 // ragged tile tail: clamp the loads
-        wblk[nt] = codes + ((size_t)t * G + g0) * 1024 + lane * 16;
-        mblk[nt] = meta + ((size_t)t * G + g0) * 16 + col;
+        wr[nt] = make_rsrc(codes + ((size_t)t * G + g0) * 1024, (uint32_t)ng * 1024);
+        mr[nt] = make_rsrc(meta + ((size_t)t * G + g0) * 16, (uint32_t)ng * 64);
     }
-    const uint16_t *xrow[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        xrow[mt] = x + (size_t)min(16 * mt + col, M - 1) * K + (size_t)g0 * kGroup + kq * 32;
+    const rsrc_t xr = make_rsrc(x + (size_t)g0 * kGroup, (uint32_t)(((size_t)M * K - (size_t)g0 * kGroup) * 2));
+    const uint32_t xoff = (uint32_t)(min(col, M - 1) * K + kq * 32) * 2;
 
-    auto load = [&](W16Stage<MT, NT> &st, int i) {
+    // Group i of this wave; refills past the end re-read the first group (long since arrived).
+    auto load = [&](W16DStage<NT> &st, int i) {
+        const uint32_t g = (uint32_t)(i < ng ? i : 0);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            st.w[nt] = load_stream16(wblk[nt] + (size_t)i * 1024);
-            st.meta[nt] = mblk[nt][(size_t)i * 16];
+            st.w[nt] = buf_load16_stream(wr[nt], lane * 16, g * 1024);
+            st.meta[nt] = buf_load4(mr[nt], col * 4, g * 64);
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const uint4 *xp = (const uint4 *)(xrow[mt] + (size_t)i * kGroup);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) st.a[mt][j] = xp[j];
-        }
+        for (int j = 0; j < 4; ++j) st.a[j] = buf_load16(xr, xoff + 16 * j, g * 256);
     };
 
-    f32x4_t acc[MT][NT];
+    f32x4_t acc[NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const W16Stage<MT, NT> &cur) {
+    auto compute = [&](const W16DStage<NT> &cur) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const DqConst dq = make_dq(cur.meta[nt]);
@@ -154,21 +148,16 @@ k_w4a16_skinny(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
             for (int j = 0; j < 4; ++j) {
                 uint32_t b[4];
                 dequant8(words[j], dq, b);
-                const bf16x8_t bv = as_bf16x8(b[0], b[1], b[2], b[3]);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, cur.a[mt][j]), bv, acc[mt][nt], 0, 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.a[j]),
+                                                                  as_bf16x8(b[0], b[1], b[2], b[3]), acc[nt], 0, 0, 0);
             }
         }
     };
 
-    // Steady state: full blocks of U groups, every stage refilled unconditionally (indices past
-    // the end re-read the last group); the remaining ng % U groups are in registers afterwards.
-    W16Stage<MT, NT> st[U];
+    W16DStage<NT> st[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        load(st[u], min(u, ng - 1));
+        load(st[u], u);
         __builtin_amdgcn_sched_barrier(0);
     }
     const int nfull = ng - ng % U;
@@ -176,7 +165,7 @@ k_w4a16_skinny(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             compute(st[u]);
-            load(st[u], min(base + u + U, ng - 1));
+            load(st[u], base + u + U);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -184,24 +173,22 @@ k_w4a16_skinny(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
     for (int u = 0; u < U - 1; ++u)
         if (nfull + u < ng) compute(st[u]);
 
-    // Fixed-order reduction of the kw wave partials, one 16x16 output tile at a time.
+    // Fixed-order reduction of the kw wave partials, one 16 x 16 output tile at a time.
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[mt][nt][r];
-            __syncthreads();
-            for (int e = threadIdx.x; e < 256; e += blockDim.x) {
-                const int r = e >> 6, l = e & 63;
-                float sum = 0.f;
-                for (int w = 0; w < kw; ++w) sum += red[(w * 4 + r) * 64 + l];
-                const int m = 16 * mt + 4 * (l >> 4) + r;
-                const int n = 16 * (tbase + nt) + (l & 15);
-                if (m < M && n < N) store_out(y, y_f32, (size_t)m * N + n, sum);
-            }
-            __syncthreads();
+        for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[nt][r];
+        __syncthreads();
+        for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+            const int r = e >> 6, l = e & 63;
+            float sum = 0.f;
+            for (int w = 0; w < kw; ++w) sum += red[(w * 4 + r) * 64 + l];
+            const int m = 4 * (l >> 4) + r;
+            const int n = 16 * (tbase + nt) + (l & 15);
+            if (m < M && n < N) store_out(y, y_f32, (size_t)m * N + n, sum);
         }
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -559,15 +546,12 @@ k_w4a16_tiled(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__
 // ---------------------------------------------------------------------------------------------
 // Host launchers.
 
-template <int MT, int NT, int U, int MAXW>
-static hipError_t launch_skinny(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta,
-                                int K, int N, void *y, int y_f32, hipStream_t st) {
-    const int kw = min(skinny_waves_for_shape(K, N), MAXW);
-    const int T = N / 16;
-    dim3 grid((T + NT - 1) / NT);
-    dim3 block(64 * kw);
-    hipLaunchKernelGGL((k_w4a16_skinny<MT, NT, U, MAXW>), grid, block, 0, st, x, M, codes, meta, K, N, y,
-                       y_f32, kw);
+template <int NT, int U>
+static hipError_t launch_decode(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K, int N,
+                                void *y, int y_f32, hipStream_t st) {
+    const int kw = decode_shape(K, N, false).kw;
+    hipLaunchKernelGGL((k_w4a16_decode<NT, U>), dim3((N / 16 + NT - 1) / NT), dim3(64 * kw), 0, st, x, M, codes,
+                       meta, K, N, y, y_f32, kw);
     return hipGetLastError();
 }
 
@@ -606,9 +590,14 @@ static hipError_t launch_mid(const uint16_t *x, int M, const uint8_t *codes, con
 
 hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K,
                              int N, void *y, int y_f32, void *ws, hipStream_t st) {
-    // Batch tiers, each with one reduction order for all its M: M <= 16 (skinny), 16 < M <= 80
+    // Batch tiers, each with one reduction order for all its M: M <= 16 (decode), 16 < M <= 80
     // (mid, split-K), M > 80 (tiled).
-    if (M <= 16) return launch_skinny<1, 1, 4, kMaxSplitWaves>(x, M, codes, meta, K, N, y, y_f32, st);
+    if (M <= 16) {
+        const int nt = decode_shape(K, N, false).nt;
+        if (nt == 4) return launch_decode<4, 4>(x, M, codes, meta, K, N, y, y_f32, st);
+        if (nt == 2) return launch_decode<2, 4>(x, M, codes, meta, K, N, y, y_f32, st);
+        return launch_decode<1, 4>(x, M, codes, meta, K, N, y, y_f32, st);
+    }
     if (M <= 32) return launch_mid<2, 6>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     if (M <= 48) return launch_mid<3, 5>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     if (M <= 64) return launch_mid<4, 4>(x, M, codes, meta, K, N, y, y_f32, ws, st);

@@ -7,12 +7,12 @@
 //
 // CDNA4 has no 4-bit integer MFMA, so both operands are widened to int8 in registers (two SWAR
 // ops per 4 codes) and fed to v_mfma_i32_16x16x64_i8, whose int32 sums are exact.
-//  * k_w4a4_skinny (M <= 64): HBM-bound draft shapes.  Same work split as the W4A16 skinny
-//    kernel: 16*NT columns per workgroup, KW waves splitting the K groups, U groups of weight
-//    loads in flight, fixed-order LDS reduction of the wave partials.  Weights stay unsigned
-//    (0..15) and the zero point is applied after the MFMA as D = sum(q_a w) - z sum(q_a); the
-//    per-(token, group) code sums come from one extra MFMA against a matrix of ones, which lands
-//    them in the accumulator layout.
+//  * k_w4a4_decode (M <= 16) and k_w4a4_skinny (16 < M <= 64): HBM-bound draft shapes.  A
+//    workgroup owns 16 NT columns, KW waves split the K groups, U groups of weight loads stay in
+//    flight, and the wave partials are reduced through LDS in a fixed order.  Weights stay
+//    unsigned (0..15) and the zero point is applied after the MFMA as
+//    D = sum(q_a w) - z sum(q_a); the per-(token, group) code sums come from one extra MFMA
+//    against a matrix of ones, which lands them in the accumulator layout.
 //  * k_w4a4_tiled (M > 64): 128x128 tiles per workgroup; the codes of one K group are widened
 //    into LDS once (weights as signed w - z), 4 waves each own a 64x64 sub-tile.
 #include "common.hpp"
@@ -195,6 +195,135 @@ k_w4a4_skinny(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
 }
 
 // ---------------------------------------------------------------------------------------------
+// Decode kernel (M <= 16): one row tile, NT column tiles per wave.  A workgroup owns NT tiles and
+// KW waves split the K groups; each wave widens the group's activation codes once and feeds them
+// to the 2 NT MFMAs of its tiles (plus the two against ones for the code sums).  Loads are buffer
+// loads from wave-uniform bases; U groups stay in flight in a register ring; wave partials are
+// summed through LDS in wave order (the reduction order depends on (K, N) only).
+template <int NT>
+struct W4DStage {
+    uint4 w[NT];
+    uint32_t meta[NT];
+    uint4 a;
+    float as[4];
+};
+
+template <int NT, int U, bool DOTS>
+__global__ void __launch_bounds__(64 * kMaxDecodeWaves)
+k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, int M,
+              const uint8_t *__restrict__ codes, const uint32_t *__restrict__ meta, int K, int N,
+              void *__restrict__ y, int y_f32, int32_t *__restrict__ dots, int kw) {
+    __shared__ float red[kMaxDecodeWaves * 4 * 64];   // [kw][4][64]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int G = K / kGroup;
+    const int g0 = (wave * G) / kw;
+    const int ng = ((wave + 1) * G) / kw - g0;
+    const int T = N / 16;
+    const int tbase = blockIdx.x * NT;
+    const i32x4_t ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    const i32x4_t izero = {0, 0, 0, 0};
+
+    rsrc_t wr[NT], mr[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int t = min(tbase + nt, T - 1);                 // ragged tile tail: clamp the loads
+        wr[nt] = make_rsrc(codes + ((size_t)t * G + g0) * 1024, (uint32_t)ng * 1024);
+        mr[nt] = make_rsrc(meta + ((size_t)t * G + g0) * 16, (uint32_t)ng * 64);
+    }
+    const rsrc_t ar = make_rsrc(a_codes + (size_t)g0 * 64, (uint32_t)((size_t)M * K / 2 - (size_t)g0 * 64));
+    const rsrc_t sr = make_rsrc(a_scales + g0, (uint32_t)(((size_t)M * G - g0) * 4));
+    // lane offsets: A row = the lane's MFMA row, scales of the 4 output rows the lane holds
+    const uint32_t aoff = (uint32_t)(min(col, M - 1) * (K / 2) + kq * 16);
+    uint32_t soff[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) soff[r] = (uint32_t)(min(4 * kq + r, M - 1) * G) * 4;
+
+    // Group i of this wave; refills past the end re-read the first group (long since arrived).
+    auto load = [&](W4DStage<NT> &st, int i) {
+        const uint32_t g = (uint32_t)(i < ng ? i : 0);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            st.w[nt] = buf_load16_stream(wr[nt], lane * 16, g * 1024);
+            st.meta[nt] = buf_load4(mr[nt], col * 4, g * 64);
+        }
+        st.a = buf_load16(ar, aoff, g * 64);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.as[r] = __uint_as_float(buf_load4(sr, soff[r], g * 4));
+    };
+
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const W4DStage<NT> &cur, int i) {
+        const uint4 e = cur.a;
+        const i32x4_t A0 = as_i32x4(snib_lo(e.x), snib_hi(e.x), snib_lo(e.y), snib_hi(e.y));
+        const i32x4_t A1 = as_i32x4(snib_lo(e.z), snib_hi(e.z), snib_lo(e.w), snib_hi(e.w));
+        i32x4_t sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, ones, izero, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, ones, sa, 0, 0, 0);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const uint4 d = cur.w[nt];
+            const float sw = fp16_bits_to_float((uint16_t)(cur.meta[nt] & 0xFFFFu));
+            const int zw = (int)((cur.meta[nt] >> 16) & 0xFFu);
+            const i32x4_t B0 = as_i32x4(nib_lo(d.x), nib_hi(d.x), nib_lo(d.y), nib_hi(d.y));
+            const i32x4_t B1 = as_i32x4(nib_lo(d.z), nib_hi(d.z), nib_lo(d.w), nib_hi(d.w));
+            i32x4_t ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, izero, 0, 0, 0);
+            ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, ia, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int Dv = ia[r] - zw * sa[r];
+                acc[nt][r] = __builtin_fmaf(cur.as[r] * sw, (float)Dv, acc[nt][r]);
+                if (DOTS) {
+                    const int mo = 4 * kq + r;
+                    const int n = 16 * (tbase + nt) + col;
+                    if (mo < M && n < N) dots[((size_t)(g0 + i) * M + mo) * N + n] = Dv;
+                }
+            }
+        }
+    };
+
+    W4DStage<NT> st[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        load(st[u], u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const int nfull = ng - ng % U;
+    for (int base = 0; base < nfull; base += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            compute(st[u], base + u);
+            load(st[u], base + u + U);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u)
+        if (nfull + u < ng) compute(st[u], nfull + u);
+
+    // Fixed-order reduction of the kw wave partials, one 16 x 16 output tile at a time.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[nt][r];
+        __syncthreads();
+        for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+            const int r = e >> 6, l = e & 63;
+            float sum = 0.f;
+            for (int w = 0; w < kw; ++w) sum += red[(w * 4 + r) * 64 + l];
+            const int m = 4 * (l >> 4) + r;
+            const int n = 16 * (tbase + nt) + (l & 15);
+            if (m < M && n < N) store_out4(y, y_f32, (size_t)m * N + n, sum);
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Tiled kernel for large M.  256 threads = 4 waves (2x2) over a 128x128 output tile.
 constexpr int QBM = 128, QBN = 128;
 constexpr int QLDS = kGroup + 16;   // padded row pitch in bytes
@@ -329,13 +458,32 @@ static hipError_t launch_skinny4(const uint8_t *a_codes, const float *a_scales, 
     return hipGetLastError();
 }
 
+template <int NT, int U>
+static hipError_t launch_decode4(const uint8_t *a_codes, const float *a_scales, int M, const uint8_t *codes,
+                                 const uint32_t *meta, int K, int N, void *y, int y_f32, int32_t *dots, int kw,
+                                 hipStream_t st) {
+    dim3 grid((N / 16 + NT - 1) / NT), block(64 * kw);
+    if (dots)
+        hipLaunchKernelGGL((k_w4a4_decode<NT, U, true>), grid, block, 0, st, a_codes, a_scales, M, codes, meta, K,
+                           N, y, y_f32, dots, kw);
+    else
+        hipLaunchKernelGGL((k_w4a4_decode<NT, U, false>), grid, block, 0, st, a_codes, a_scales, M, codes, meta, K,
+                           N, y, y_f32, dots, kw);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M, const uint8_t *codes,
                             const uint32_t *meta, int K, int N, void *y, int y_f32, int32_t *group_dots,
                             hipStream_t st) {
     // Batch tiers with one reduction order each: M <= 16 and 16 < M <= 64.
-    if (M <= 16)
-        return launch_skinny4<1, 1, 4, kMaxSplitWaves>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32,
-                                                       group_dots, st);
+    if (M <= 16) {
+        const DecodeShape d = decode_shape(K, N, true);
+        if (d.nt == 4)
+            return launch_decode4<4, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, d.kw, st);
+        if (d.nt == 2)
+            return launch_decode4<2, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, d.kw, st);
+        return launch_decode4<1, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, d.kw, st);
+    }
     if (M <= 32)
         return launch_skinny4<2, 1, 3, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, st);
     if (M <= 64)
