@@ -211,7 +211,8 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
 constexpr int MID_NT = 2;                // column tiles per wave
 constexpr int MID_CW = 4;                // column waves per K half
 constexpr int MID_TILES = MID_CW * MID_NT;   // column tiles per workgroup
-constexpr int MID_THREADS = 2 * MID_CW * 64;
+constexpr int MID_KP = 2;                // K parts per workgroup
+constexpr int MID_THREADS = MID_KP * MID_CW * 64;
 
 template <int MT, int U>
 __global__ void __launch_bounds__(MID_THREADS)
@@ -220,7 +221,7 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
             float *__restrict__ partials) {
     constexpr int NF = MT * 4;        // activation fragments per group
     constexpr int NFW = NF / MID_CW;  // staged by each wave of a K half
-    __shared__ uint4 abuf[2][2][NF * 64];   // [K half][buffer][fragment][lane]
+    __shared__ uint4 abuf[MID_KP][2][NF * 64];   // [K part][buffer][fragment][lane]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
@@ -231,9 +232,9 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     const int split = blockIdx.y;
     const int gs0 = (split * G) / S;
     const int n = ((split + 1) * G) / S - gs0;
-    const int hstart = gs0 + (kh ? n / 2 : 0);
-    const int nh = kh ? n - n / 2 : n / 2;   // groups of this half (half 0 may have one less)
-    const int nsteps = n - n / 2;            // both halves step together
+    const int hstart = gs0 + (kh * n) / MID_KP;
+    const int nh = ((kh + 1) * n) / MID_KP - (kh * n) / MID_KP;   // groups of this part
+    const int nsteps = (n + MID_KP - 1) / MID_KP;                 // all parts step together
     const int hlast = max(nh, 1) - 1;
     const int tile0 = blockIdx.x * MID_TILES + cw * MID_NT;
 
@@ -355,7 +356,7 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         const int i = nfull + u;
         if (i < nsteps) {                        // uniform over the workgroup
             if (i + U - 1 < nsteps) load(st[(u + U - 1) % U], i + U - 1);
-            if (i < nh) compute(st[u], i & 1);   // half 0 may have one group less
+            if (i < nh) compute(st[u], i & 1);   // a part may have one group less
             if (i + 1 < nsteps) {
                 stage_act(st[(u + 1) % U], (i + 1) & 1);
                 __syncthreads();
@@ -364,33 +365,37 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     }
     __syncthreads();   // every wave is done reading the staging buffers
 
-    // Epilogue.  (1) Half 1 hands its accumulators to half 0 through LDS (the staging buffers
-    // are free); (2) half 0 adds them (half 0 + half 1) and (3) writes the sums row-major into
-    // LDS; (4) all four waves store the M x 128 block in 16-byte pieces: bfloat16 / f32 output,
-    // or the fp32 partial of this split.
+    // Epilogue.  (1) Parts 1 .. MID_KP - 1 in turn hand their accumulators to part 0 through
+    // LDS (the staging buffers are free), which adds them in part order; (2) part 0 writes the
+    // sums row-major into LDS; (3) all waves store the M x 128 block in 16-byte pieces: bfloat16
+    // / f32 output, or the fp32 partial of this split.
     constexpr int NACC = MT * MID_NT * 4;
     constexpr int OPITCH = 128 + 4;             // floats per output row in LDS
     float *red = (float *)&abuf[0][0][0];
-    static_assert(MID_CW * NACC * 64 <= 2 * 2 * NF * 64 * 4, "hand-over buffer");
-    static_assert(MT * 16 * OPITCH <= 2 * 2 * NF * 64 * 4, "output buffer");
-    if (kh == 1) {
+    static_assert(MID_CW * NACC * 64 <= MID_KP * 2 * NF * 64 * 4, "hand-over buffer");
+    static_assert(MT * 16 * OPITCH <= MID_KP * 2 * NF * 64 * 4, "output buffer");
+    for (int p = 1; p < MID_KP; ++p) {       // part 0 + part 1 + ... in part order
+        if (kh == p) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < MID_NT; ++nt)
+                for (int nt = 0; nt < MID_NT; ++nt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) red[(cw * NACC + (mt * MID_NT + nt) * 4 + r) * 64 + lane] = acc[mt][nt][r];
+                    for (int r = 0; r < 4; ++r)
+                        red[(cw * NACC + (mt * MID_NT + nt) * 4 + r) * 64 + lane] = acc[mt][nt][r];
+        }
+        __syncthreads();
+        if (kh == 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < MID_NT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[mt][nt][r] += red[(cw * NACC + (mt * MID_NT + nt) * 4 + r) * 64 + lane];
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    if (kh == 0) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < MID_NT; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mt][nt][r] += red[(cw * NACC + (mt * MID_NT + nt) * 4 + r) * 64 + lane];
-    }
-    __syncthreads();
     if (kh == 0) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -428,7 +433,9 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
 }
 
 // y = sum of the S <= kMaxSplits fp32 partials in split order (4 outputs per thread; M * N is a
-// multiple of 16).  All S loads are issued before the first add.
+// multiple of 16).  All S loads are issued before the first add.  A second kernel rather than a
+// last-arriving workgroup: the device-scope fence that hand-off needs writes back the XCD's L2,
+// which measured 35 - 50 us slower per call than this launch on the verify shapes.
 constexpr int kMaxSplits = 16;
 
 __global__ void __launch_bounds__(256)
@@ -556,14 +563,14 @@ static hipError_t launch_decode(const uint16_t *x, int M, const uint8_t *codes, 
 }
 
 // K splits of the mid kernel: a function of (K, N) only.  Column blocks alone fill the chip when
-// there are at least 192 of them; otherwise split K until about 256 workgroups exist, keeping at
-// least 4 groups (2 per K half) per split and at most kMaxSplits splits.
+// there are at least 192 of them; otherwise split K as far as the grid still fits one workgroup
+// per CU (256), keeping at least 4 groups (2 per K part) per split and at most kMaxSplits splits.
 static int mid_splits(int K, int N) {
     const int G = K / kGroup;
     const int cbs = (N / 16 + MID_TILES - 1) / MID_TILES;
     if (cbs >= 192) return 1;
-    const int want = (256 + cbs - 1) / cbs;
-    return max(1, min(min(want, kMaxSplits), G / 4));
+    const int fit = 256 / cbs;
+    return max(1, min(min(fit, kMaxSplits), G / 4));
 }
 
 size_t gemm_w4a16_workspace_bytes(int M, int K, int N) {
