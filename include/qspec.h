@@ -35,9 +35,11 @@
  *     call) but give unspecified results.
  *   - Outputs must not alias inputs.
  *   - Alignment: x / activation codes / weight codes 16 bytes (they are read with 16-byte
- *     loads; row starts stay aligned because K is a multiple of 128); fp32 / int32 / meta
- *     arrays 4 bytes; bf16 arrays 2 bytes; the verify workspace 16 bytes.  Torch allocations
- *     satisfy all of these.  A violation returns QSPEC_ERR_ALIGN.
+ *     loads; row starts stay aligned because K is a multiple of 128); the GEMM outputs y
+ *     16 bytes (written with 16-byte stores; rows stay aligned because N is a multiple of 16);
+ *     other fp32 / int32 / meta arrays 4 bytes; other bf16 arrays 2 bytes; the verify
+ *     workspace 16 bytes and the W4A16 workspace 256 bytes.  Torch allocations satisfy all of
+ *     these.  A violation returns QSPEC_ERR_ALIGN.
  *
  * Storage formats (the pages fix none of these; this library's choices)
  *   weight codes   u8  [N/16][K/128][1024]  the shared 4-bit store, tile-major.  Block (t, g)

@@ -102,7 +102,7 @@ template <int NT, int U>
 __global__ void __launch_bounds__(64 * kMaxDecodeWaves)
 k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
                const uint32_t *__restrict__ meta, int K, int N, void *__restrict__ y, int y_f32, int kw) {
-    __shared__ float red[kMaxDecodeWaves * 4 * 64];   // [kw][4][64]
+    extern __shared__ __attribute__((aligned(16))) float red[];   // [kw][NT][4][64], sized at launch
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;
@@ -173,21 +173,39 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
     for (int u = 0; u < U - 1; ++u)
         if (nfull + u < ng) compute(st[u]);
 
-    // Fixed-order reduction of the kw wave partials, one 16 x 16 output tile at a time.
+    // Fixed-order reduction of the kw wave partials: every wave parks its NT tiles in LDS (lane
+    // layout of the MFMA output), one barrier, then each thread sums 8 consecutive columns of one
+    // row over the waves in wave order and writes them with one 16-byte (bf16) or two 16-byte
+    // (f32) stores.
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[nt][r];
-        __syncthreads();
-        for (int e = threadIdx.x; e < 256; e += blockDim.x) {
-            const int r = e >> 6, l = e & 63;
-            float sum = 0.f;
-            for (int w = 0; w < kw; ++w) sum += red[(w * 4 + r) * 64 + l];
-            const int m = 4 * (l >> 4) + r;
-            const int n = 16 * (tbase + nt) + (l & 15);
-            if (m < M && n < N) store_out(y, y_f32, (size_t)m * N + n, sum);
+        for (int r = 0; r < 4; ++r) red[((wave * NT + nt) * 4 + r) * 64 + lane] = acc[nt][r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < NT * 32; e += blockDim.x) {
+        const int nt = e >> 5, m = (e >> 1) & 15, c0 = (e & 1) * 8;
+        const int t = tbase + nt;
+        if (m >= M || t >= T) continue;
+        const int base = (nt * 4 + (m & 3)) * 64 + 16 * (m >> 2) + c0;
+        float4 lo = *(const float4 *)&red[base], hi = *(const float4 *)&red[base + 4];
+        for (int w = 1; w < kw; ++w) {
+            const float4 a = *(const float4 *)&red[w * NT * 256 + base];
+            const float4 b = *(const float4 *)&red[w * NT * 256 + base + 4];
+            lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+            hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
         }
-        __syncthreads();
+        const size_t idx = (size_t)m * N + 16 * t + c0;
+        if (y_f32) {
+            *(float4 *)((float *)y + idx) = lo;
+            *(float4 *)((float *)y + idx + 4) = hi;
+        } else {
+            uint4 o;
+            o.x = pack_bf16x2(lo.x, lo.y);
+            o.y = pack_bf16x2(lo.z, lo.w);
+            o.z = pack_bf16x2(hi.x, hi.y);
+            o.w = pack_bf16x2(hi.z, hi.w);
+            *(uint4 *)((uint16_t *)y + idx) = o;
+        }
     }
 }
 
@@ -557,7 +575,8 @@ template <int NT, int U>
 static hipError_t launch_decode(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K, int N,
                                 void *y, int y_f32, hipStream_t st) {
     const int kw = decode_shape(K, N, false).kw;
-    hipLaunchKernelGGL((k_w4a16_decode<NT, U>), dim3((N / 16 + NT - 1) / NT), dim3(64 * kw), 0, st, x, M, codes,
+    const size_t lds = (size_t)kw * NT * 256 * sizeof(float);
+    hipLaunchKernelGGL((k_w4a16_decode<NT, U>), dim3((N / 16 + NT - 1) / NT), dim3(64 * kw), lds, st, x, M, codes,
                        meta, K, N, y, y_f32, kw);
     return hipGetLastError();
 }

@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(64 * kMaxDecodeWaves)
 k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, int M,
               const uint8_t *__restrict__ codes, const uint32_t *__restrict__ meta, int K, int N,
               void *__restrict__ y, int y_f32, int32_t *__restrict__ dots, int kw) {
-    __shared__ float red[kMaxDecodeWaves * 4 * 64];   // [kw][4][64]
+    extern __shared__ __attribute__((aligned(16))) float red[];   // [kw][NT][4][64], sized at launch
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;
@@ -305,21 +305,39 @@ k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
     for (int u = 0; u < U - 1; ++u)
         if (nfull + u < ng) compute(st[u], nfull + u);
 
-    // Fixed-order reduction of the kw wave partials, one 16 x 16 output tile at a time.
+    // Fixed-order reduction of the kw wave partials: every wave parks its NT tiles in LDS (lane
+    // layout of the MFMA output), one barrier, then each thread sums 8 consecutive columns of one
+    // row over the waves in wave order and writes them with one 16-byte (bf16) or two 16-byte
+    // (f32) stores.
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[nt][r];
-        __syncthreads();
-        for (int e = threadIdx.x; e < 256; e += blockDim.x) {
-            const int r = e >> 6, l = e & 63;
-            float sum = 0.f;
-            for (int w = 0; w < kw; ++w) sum += red[(w * 4 + r) * 64 + l];
-            const int m = 4 * (l >> 4) + r;
-            const int n = 16 * (tbase + nt) + (l & 15);
-            if (m < M && n < N) store_out4(y, y_f32, (size_t)m * N + n, sum);
+        for (int r = 0; r < 4; ++r) red[((wave * NT + nt) * 4 + r) * 64 + lane] = acc[nt][r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < NT * 32; e += blockDim.x) {
+        const int nt = e >> 5, m = (e >> 1) & 15, c0 = (e & 1) * 8;
+        const int t = tbase + nt;
+        if (m >= M || t >= T) continue;
+        const int base = (nt * 4 + (m & 3)) * 64 + 16 * (m >> 2) + c0;
+        float4 lo = *(const float4 *)&red[base], hi = *(const float4 *)&red[base + 4];
+        for (int w = 1; w < kw; ++w) {
+            const float4 a = *(const float4 *)&red[w * NT * 256 + base];
+            const float4 b = *(const float4 *)&red[w * NT * 256 + base + 4];
+            lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+            hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
         }
-        __syncthreads();
+        const size_t idx = (size_t)m * N + 16 * t + c0;
+        if (y_f32) {
+            *(float4 *)((float *)y + idx) = lo;
+            *(float4 *)((float *)y + idx + 4) = hi;
+        } else {
+            uint4 o;
+            o.x = pack_bf16x2(lo.x, lo.y);
+            o.y = pack_bf16x2(lo.z, lo.w);
+            o.z = pack_bf16x2(hi.x, hi.y);
+            o.w = pack_bf16x2(hi.z, hi.w);
+            *(uint4 *)((uint16_t *)y + idx) = o;
+        }
     }
 }
 
@@ -463,11 +481,12 @@ static hipError_t launch_decode4(const uint8_t *a_codes, const float *a_scales, 
                                  const uint32_t *meta, int K, int N, void *y, int y_f32, int32_t *dots, int kw,
                                  hipStream_t st) {
     dim3 grid((N / 16 + NT - 1) / NT), block(64 * kw);
+    const size_t lds = (size_t)kw * NT * 256 * sizeof(float);
     if (dots)
-        hipLaunchKernelGGL((k_w4a4_decode<NT, U, true>), grid, block, 0, st, a_codes, a_scales, M, codes, meta, K,
+        hipLaunchKernelGGL((k_w4a4_decode<NT, U, true>), grid, block, lds, st, a_codes, a_scales, M, codes, meta, K,
                            N, y, y_f32, dots, kw);
     else
-        hipLaunchKernelGGL((k_w4a4_decode<NT, U, false>), grid, block, 0, st, a_codes, a_scales, M, codes, meta, K,
+        hipLaunchKernelGGL((k_w4a4_decode<NT, U, false>), grid, block, lds, st, a_codes, a_scales, M, codes, meta, K,
                            N, y, y_f32, dots, kw);
     return hipGetLastError();
 }

@@ -55,7 +55,7 @@ QSPEC_EXPORT int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, 
     if ((long long)M * N > kMaxElems) return QSPEC_ERR_SHAPE;
     if (y_dtype != QSPEC_OUT_BF16 && y_dtype != QSPEC_OUT_F32) return QSPEC_ERR_UNSUPPORTED;
     if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 4) || !aligned(w_meta, 4) ||
-        !aligned(y, y_dtype == QSPEC_OUT_F32 ? 4 : 2) || !aligned(group_dots, 4))
+        !aligned(y, 16) || !aligned(group_dots, 4))
         return QSPEC_ERR_ALIGN;
     return status_of(qspec::launch_gemm_w4a4(a_codes, a_scales, M, w_codes, w_meta, K, N, y,
                                              y_dtype == QSPEC_OUT_F32, group_dots, as_stream(stream)));
@@ -76,7 +76,7 @@ QSPEC_EXPORT int qspec_gemm_w4a16(const uint16_t *x, int32_t M, const uint8_t *w
     const size_t need = qspec::gemm_w4a16_workspace_bytes(M, K, N);
     if (need > 0 && (!workspace || workspace_bytes < need)) return QSPEC_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(w_codes, 16) || !aligned(w_meta, 4) ||
-        !aligned(y, y_dtype == QSPEC_OUT_F32 ? 4 : 2) || !aligned(workspace, 256))
+        !aligned(y, 16) || !aligned(workspace, 256))
         return QSPEC_ERR_ALIGN;
     return status_of(qspec::launch_gemm_w4a16(x, M, w_codes, w_meta, K, N, y, y_dtype == QSPEC_OUT_F32,
                                               workspace, as_stream(stream)));

@@ -119,6 +119,9 @@ def test_alignment_validation():
     assert L.qspec_quantize_act(odd, 1, 128, FAKE, FAKE, None) == ERR_ALIGN
     assert L.qspec_gemm_w4a16(FAKE, 4, ctypes.c_void_p(0x1008), FAKE, 256, 64, FAKE, 0, None, 0, None) == ERR_ALIGN
     assert L.qspec_gemm_w4a4(FAKE, odd, 4, FAKE, FAKE, 256, 64, FAKE, 1, None, None) == ERR_ALIGN
+    # GEMM outputs are written with 16-byte stores
+    assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 256, 64, ctypes.c_void_p(0x1008), 0, None, 0, None) == ERR_ALIGN
+    assert L.qspec_gemm_w4a4(FAKE, FAKE, 4, FAKE, FAKE, 256, 64, ctypes.c_void_p(0x1004), 1, None, None) == ERR_ALIGN
     need = L.qspec_verify_workspace_bytes(0, 2, 3, 5000)
     assert L.qspec_verify_accept(0, FAKE, None, FAKE, None, None, 2, 3, 5000, FAKE, FAKE,
                                  ctypes.c_void_p(0x1004), need, None) == ERR_ALIGN
