@@ -196,6 +196,30 @@ def test_w4a4_small_exact_dots_and_outputs(M, K, N):
         assert torch.equal(y, y2)
 
 
+# Decode-tier workgroup shapes (M <= 16): 2 column tiles per workgroup from 1024 tiles on, 4 from
+# 4096 on, with a ragged last workgroup (odd tile counts), and 1 tile with several K-splitting
+# waves; every output element is compared.
+DECODE_TILINGS = [(16, 256, 16 * 1025), (3, 128, 16 * 4097), (9, 1024, 16 * 385), (1, 512, 16 * 257)]
+
+
+@pytest.mark.parametrize("M,K,N", DECODE_TILINGS)
+def test_decode_tilings_w4a4_and_w4a16(M, K, N):
+    note(f"decode tilings M={M} K={K} N={N}")
+    w = si.weights(K, N, seed=N % 997)
+    x = si.activations(M, K, seed=M + 3000)
+    wc, wm = weights_dev(w)
+    y16 = run_w4a16(x, w, torch.bfloat16, (wc, wm))
+    assert_close(host_f64(y16), oracle.gemm_w4a16(x, w["codes"], w["meta"]), True, f"w4a16 {M}x{K}x{N}")
+    codes, scales = run_quant(x)
+    oc, osc = oracle.quantize_act(x)
+    dots = torch.full((K // 128, M, N), -(2 ** 31), dtype=torch.int32, device=DEV)
+    y4 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    q.qspec_gemm_w4a4(codes, scales, wc, wm, y4, group_dots=dots)
+    ref, D = oracle.gemm_w4a4(oc, osc, w["codes"], w["meta"])
+    assert np.array_equal(dots.cpu().numpy().astype(np.int64), D)
+    assert_close(host_f64(y4), ref, False, f"w4a4 {M}x{K}x{N}")
+
+
 def test_w4a4_rows_do_not_depend_on_batch():
     K, N = 1024, 96
     note("gemm_w4a4 batch invariance")
