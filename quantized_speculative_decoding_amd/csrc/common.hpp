@@ -97,6 +97,19 @@ __host__ __device__ inline int skinny_waves_for_shape(int K, int N) {
     return kw < 1 ? 1 : kw;
 }
 
+// The dispatcher deals workgroup i to XCD i % 8.  xcd_remap(i, n) is a bijection of [0, n) that
+// gives each XCD one contiguous range of logical tiles, walked in order, so neighbouring logical
+// tiles (which share operands) meet in the same L2.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+    const int per = (n + kXcds - 1) / kXcds;          // tiles of the larger XCD ranges
+    int tall = n % kXcds;                             // XCDs holding `per` tiles
+    if (tall == 0) tall = kXcds;
+    const int xcd = i % kXcds, local = i / kXcds;
+    return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
 // Decode kernels (M <= 16): column tiles per workgroup (nt) and K-splitting waves (kw), a
 // function of (K, N) only, so the reduction order is too.  Chosen from measured sweeps over the
 // Llama-3-8B / Qwen2.5-7B projection shapes: about 500 - 2000 waves in flight, wider workgroups

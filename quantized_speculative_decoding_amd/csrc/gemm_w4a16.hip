@@ -9,13 +9,12 @@
 // exactly the 32 codes its v_mfma_f32_16x16x32_bf16 B fragments need.  Every wave-wide weight
 // load is one contiguous kilobyte.
 //
-// Three kernels share the dequantization routine, one per batch tier:
+// Two kernels share the dequantization routine:
 //  * k_w4a16_decode (M <= 16): HBM-bound decode / short-verify shapes; NT column tiles per
 //    workgroup, K groups split between its waves, activations in registers.
-//  * k_w4a16_mid (16 < M <= 80): verify shapes near the MFMA ridge; 8 waves share each group's
-//    activation tile through LDS, optional K split across workgroups with an ordered reduction.
-//  * k_w4a16_tiled (M > 80): MFMA-bound shapes; 128x128 output tiles with the activation tile and
-//    the dequantized weight tile staged in LDS.
+//  * k_w4a16_lds (16 < M <= 80 and M > 80): the activation tile of each group is staged once in
+//    LDS and shared by the workgroup's waves; the verify tier splits K between two wave groups
+//    (and across workgroups with an ordered reduction), the large tier covers 128-row blocks.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -210,89 +209,109 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
-// Mid kernel (16 < M <= 80): verify shapes near the MFMA ridge, where the activation tile of a
-// group (M x 128 bf16, 20 KB at M = 80) is as large as 20 weight blocks and has to be shared.
+// Shared-activation kernel k_w4a16_lds: the verify tier (16 < M <= 80) and the large-batch tier
+// (M > 80).  At these M a group's activation tile (M x 128 bf16: 20 KB at M = 80, 32 KB for a
+// 128-row block) is as large as 20 - 32 weight blocks, so it is staged once in LDS and shared by
+// the workgroup's waves, while every weight block is dequantized exactly once, in registers, by
+// the wave whose MFMA B operand it is.
 //
-// A workgroup = 8 waves = 2 K halves x 4 column waves; each wave owns MID_NT = 2 column tiles, so
-// the workgroup covers 8 tiles (128 columns) of one K split, with two waves per SIMD (a single
-// wave per SIMD issues MFMA and VALU work at about half the rate two waves reach).  Per group, the
-// four waves of a K half stage the half's activation tile into LDS in fragment-major order
-// (fragment f = (row tile, 32-k step), lane l's 16 bytes at f * 1 KB + 16 l: conflict-free
-// 128-bit reads and writes), and every wave reads all fragments from there, each fragment
-// feeding MID_NT MFMAs.  Activations and weights travel through one U-deep register ring in group
+// A workgroup = KP K parts x CW column waves; each wave owns LDS_NT = 2 column tiles, so the
+// workgroup covers 16 * 2 * CW columns of one K split and one block of up to 16 MT rows.
+//  * verify tier: KP = 2, CW = 4 (8 waves, 128 columns, all M rows), two waves per SIMD (a single
+//    wave per SIMD issues MFMA and VALU work at about half the rate two waves reach);
+//  * large tier: KP = 1, CW = 8 (8 waves, 256 columns, 128-row blocks).
+// Per group, the CW waves of a K part stage the part's activation tile into LDS in fragment-major
+// order (fragment f = (row tile, 32-k step), lane l's 16 bytes in f's 1 KB block, XOR-swizzled:
+// conflict-free 128-bit writes and reads) and every wave reads all fragments from there, each
+// feeding LDS_NT MFMAs.  Activations and weights travel through one U-deep register ring in group
 // order (the in-order vmcnt wait for a stage never covers a younger one); a stage's activations
 // are written to LDS one step before they are consumed, its weights are dequantized in registers
-// when consumed.  One barrier per step.  The two K halves are added in LDS (half 0 + half 1).
-// With S > 1 K splits (a function of (K, N) only), each workgroup writes an fp32 partial tile and
+// when consumed.  One barrier per step.  The K parts are added in LDS in part order.  With S > 1 K
+// splits (a function of (K, N) only), each workgroup writes an fp32 partial tile and
 // k_w4a16_splitk_reduce adds the S partials in split order, so every output has one fixed
-// reduction order per (K, N).
-constexpr int MID_NT = 2;                // column tiles per wave
-constexpr int MID_CW = 4;                // column waves per K half
-constexpr int MID_TILES = MID_CW * MID_NT;   // column tiles per workgroup
-constexpr int MID_KP = 2;                // K parts per workgroup
-constexpr int MID_THREADS = MID_KP * MID_CW * 64;
+// reduction order per (K, N) in each tier.
+constexpr int LDS_NT = 2;                    // column tiles per wave
+constexpr int MID_KP = 2, MID_CW = 4;        // verify tier
+constexpr int MID_TILES = MID_CW * LDS_NT;   // column tiles per verify-tier workgroup
+constexpr int BIG_MT = 8, BIG_CW = 8;        // large tier: 128-row blocks, 256 columns
+constexpr int BIG_TILES = BIG_CW * LDS_NT;
 
-template <int MT, int U>
-__global__ void __launch_bounds__(MID_THREADS)
-k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
+template <int MT, int U, int KP, int CW>
+__global__ void __launch_bounds__(KP * CW * 64)
+k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
             const uint32_t *__restrict__ meta, int K, int N, void *__restrict__ y, int y_f32, int S,
-            float *__restrict__ partials) {
-    constexpr int NF = MT * 4;        // activation fragments per group
-    constexpr int NFW = NF / MID_CW;  // staged by each wave of a K half
-    __shared__ uint4 abuf[MID_KP][2][NF * 64];   // [K part][buffer][fragment][lane]
+            float *__restrict__ partials, int row_blocks) {
+    constexpr int NT = LDS_NT;
+    constexpr int THREADS = KP * CW * 64;
+    constexpr int TILES = CW * NT;          // column tiles per workgroup
+    constexpr int NF = MT * 4;              // activation fragments per group
+    constexpr int NFW = NF / CW;            // staged by each wave of a K part
+    static_assert(NF % CW == 0, "activation fragments per wave");
+    __shared__ uint4 abuf[KP][2][NF * 64];  // [K part][buffer][fragment][lane]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-    const int kh = wave / MID_CW, cw = wave % MID_CW;
+    const int kh = wave / CW, cw = wave % CW;
     const int col = lane & 15, kq = lane >> 4;
     const int G = K / kGroup;
     const int T = N / 16;
-    const int split = blockIdx.y;
+    // Workgroup -> (column block, split, row block).  A 1-D grid (gridDim.y == 1, the large tier)
+    // walks row blocks fastest inside each XCD's contiguous range of tiles, so the workgroups that
+    // share a column block's weights run together on one XCD and its L2.
+    int cblk = blockIdx.x, split = blockIdx.y, rblk = 0;
+    if (gridDim.y == 1 && row_blocks > 1) {
+        const int t = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+        rblk = t % row_blocks;
+        cblk = t / row_blocks;
+    }
+    const int m0 = rblk * MT * 16;           // this workgroup's row block
+    const int Mb = min(MT * 16, M - m0);
     const int gs0 = (split * G) / S;
     const int n = ((split + 1) * G) / S - gs0;
-    const int hstart = gs0 + (kh * n) / MID_KP;
-    const int nh = ((kh + 1) * n) / MID_KP - (kh * n) / MID_KP;   // groups of this part
-    const int nsteps = (n + MID_KP - 1) / MID_KP;                 // all parts step together
+    const int hstart = gs0 + (kh * n) / KP;
+    const int nh = ((kh + 1) * n) / KP - (kh * n) / KP;   // groups of this part
+    const int nsteps = (n + KP - 1) / KP;                 // all parts step together
     const int hlast = max(nh, 1) - 1;
-    const int tile0 = blockIdx.x * MID_TILES + cw * MID_NT;
+    const int tile0 = cblk * TILES + cw * NT;
 
     // Buffer resources per column tile (SGPRs) plus one 32-bit lane offset per stream; the
     // group index enters as the wave-uniform offset.
-    rsrc_t wr[MID_NT], mr[MID_NT];
+    rsrc_t wr[NT], mr[NT];
 #pragma unroll
-    for (int nt = 0; nt < MID_NT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
         const int t = min(tile0 + nt, T - 1);              // ragged tile tail: clamp the loads
         wr[nt] = make_rsrc(codes + (size_t)t * G * 1024, (uint32_t)G * 1024);
         mr[nt] = make_rsrc(meta + (size_t)t * G * 16, (uint32_t)G * 64);
     }
-    const rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
-    // Activation staging: load q = cw * NFW + u of a K half reads rows 4 q .. 4 q + 3 of the
+    const rsrc_t xr = make_rsrc(x + (size_t)m0 * K, (uint32_t)Mb * K * 2);
+    // Activation staging: load q = cw * NFW + u of a K part reads rows 4 q .. 4 q + 3 of the
     // group, 16 lanes per row (row-contiguous: 8 cache lines per load).  The 16 bytes of (row, 8-k
     // chunk c) are element (row % 16, k = 8 c) of fragment f = 4 (row / 16) + c % 4, i.e. lane
     // l = row % 16 + 16 (c / 4) of it; they are stored at slot l ^ c of the fragment's 1 KB block.
     // The swizzle keeps the 16 lanes of a row on distinct banks, and a reader lane l of fragment
-    // (row tile, 32-k step j) finds its data at slot l ^ (4 (l / 16) + j).
+    // (row tile, 32-k step j) finds its data at slot l ^ (4 (l / 16) + j).  Rows past the block
+    // read its last row (their MFMA rows are discarded).
     uint32_t xoff[NFW], xslot[NFW];
 #pragma unroll
     for (int u = 0; u < NFW; ++u) {
         const int row = 4 * (cw * NFW + u) + (lane >> 4);
         const int c = lane & 15;
-        xoff[u] = (uint32_t)(min(row, M - 1) * K + c * 8) * 2;
+        xoff[u] = (uint32_t)(min(row, Mb - 1) * K + c * 8) * 2;
         xslot[u] = (uint32_t)((4 * (row >> 4) + (c & 3)) * 64 + (((row & 15) + 16 * (c >> 2)) ^ c));
     }
     const int rslot = lane ^ (4 * kq);   // reader slot, before the 32-k step j
 
     struct Stage {
-        uint4 w[MID_NT];
-        uint32_t m[MID_NT];
+        uint4 w[NT];
+        uint32_t m[NT];
         uint4 a[NFW];
     };
-    // Group i of the half; a refill past the end re-reads the first group (long since arrived)
+    // Group i of the part; a refill past the end re-reads the first group (long since arrived)
     // rather than a group whose load may still be in flight.
     auto load = [&](Stage &st, int i) {
         const uint32_t g = (uint32_t)(hstart + (i <= hlast ? i : 0));
 #pragma unroll
-        for (int nt = 0; nt < MID_NT; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
             st.w[nt] = buf_load16_stream(wr[nt], lane * 16, g * 1024);
             st.m[nt] = buf_load4(mr[nt], col * 4, g * 64);
         }
@@ -304,16 +323,16 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         for (int u = 0; u < NFW; ++u) abuf[kh][buf][xslot[u]] = st.a[u];
     };
 
-    f32x4_t acc[MT][MID_NT];
+    f32x4_t acc[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < MID_NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](const Stage &st, int buf) {
-        DqConst dq[MID_NT];
+        DqConst dq[NT];
 #pragma unroll
-        for (int nt = 0; nt < MID_NT; ++nt) dq[nt] = make_dq(st.m[nt]);
+        for (int nt = 0; nt < NT; ++nt) dq[nt] = make_dq(st.m[nt]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             bf16x8_t av[MT];
@@ -321,7 +340,7 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
             for (int mt = 0; mt < MT; ++mt)
                 av[mt] = __builtin_bit_cast(bf16x8_t, abuf[kh][buf][(mt * 4 + j) * 64 + (rslot ^ j)]);
 #pragma unroll
-            for (int nt = 0; nt < MID_NT; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
                 const uint32_t word = j == 0 ? st.w[nt].x : j == 1 ? st.w[nt].y : j == 2 ? st.w[nt].z : st.w[nt].w;
                 uint32_t b[4];
                 dequant8(word, dq[nt], b);
@@ -336,8 +355,8 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     // Ring slot s % U holds group s.  Step i first refills slot (i + U - 1) % U (it held group
     // i - 1: weights consumed at step i - 1, activations staged at step i - 2) with group
     // i + U - 1, then consumes the weights of slot i % U and writes the activations of slot
-    // (i + 1) % U to LDS for step i + 1.  The refill loads are spread through the MFMA / VALU
-    // stream.  The steady loop never runs the last step and loads unconditionally (indices past
+    // (i + 1) % U to LDS for step i + 1; the compiler spreads the refill loads through the MFMA /
+    // VALU stream.  The steady loop never runs the last step and loads unconditionally (indices past
     // the end re-read the first group), so no load is predicated there.
     Stage st[U];
 #pragma unroll
@@ -347,15 +366,6 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     }
     stage_act(st[0], 0);
     __syncthreads();
-    constexpr int NMFMA = MT * MID_NT * 4;   // per step
-    auto interleave = [&]() {
-#pragma unroll
-        for (int k = 0; k < NMFMA; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);       // four VALU
-            if (k % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one load
-        }
-    };
     const int nfull = ((nsteps - 1) / U) * U;
     for (int base = 0; base < nfull; base += U) {
 #pragma unroll
@@ -363,7 +373,6 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
             const int i = base + u;
             load(st[(u + U - 1) % U], i + U - 1);
             compute(st[u], i & 1);
-            interleave();
             __builtin_amdgcn_sched_barrier(0);
             stage_act(st[(u + 1) % U], (i + 1) & 1);
             __syncthreads();
@@ -383,70 +392,77 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     }
     __syncthreads();   // every wave is done reading the staging buffers
 
-    // Epilogue.  (1) Parts 1 .. MID_KP - 1 in turn hand their accumulators to part 0 through
-    // LDS (the staging buffers are free), which adds them in part order; (2) part 0 writes the
-    // sums row-major into LDS; (3) all waves store the M x 128 block in 16-byte pieces: bfloat16
-    // / f32 output, or the fp32 partial of this split.
-    constexpr int NACC = MT * MID_NT * 4;
-    constexpr int OPITCH = 128 + 4;             // floats per output row in LDS
+    // Epilogue.  (1) Parts 1 .. KP - 1 in turn hand their accumulators to part 0 through LDS (the
+    // staging buffers are free), which adds them in part order.  (2) In rounds of 64 columns (two
+    // column waves), part 0 writes its sums row-major into LDS and all waves store them in
+    // 16-byte pieces: bfloat16 / f32 output, or the fp32 partial of this split.
+    constexpr int NACC = MT * NT * 4;
+    constexpr int CHUNK = 64;                       // output columns per round
+    constexpr int CHUNK_WAVES = CHUNK / (NT * 16);
+    constexpr int OPITCH = CHUNK + 4;               // floats per output row in LDS
     float *red = (float *)&abuf[0][0][0];
-    static_assert(MID_CW * NACC * 64 <= MID_KP * 2 * NF * 64 * 4, "hand-over buffer");
-    static_assert(MT * 16 * OPITCH <= MID_KP * 2 * NF * 64 * 4, "output buffer");
-    for (int p = 1; p < MID_KP; ++p) {       // part 0 + part 1 + ... in part order
+    static_assert(KP == 1 || CW * NACC * 64 <= KP * 2 * NF * 64 * 4, "hand-over buffer");
+    static_assert(MT * 16 * OPITCH <= KP * 2 * NF * 64 * 4, "output buffer");
+    static_assert(CW % CHUNK_WAVES == 0, "column rounds");
+    for (int p = 1; p < KP; ++p) {
         if (kh == p) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < MID_NT; ++nt)
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        red[(cw * NACC + (mt * MID_NT + nt) * 4 + r) * 64 + lane] = acc[mt][nt][r];
+                        red[(cw * NACC + (mt * NT + nt) * 4 + r) * 64 + lane] = acc[mt][nt][r];
         }
         __syncthreads();
         if (kh == 0) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < MID_NT; ++nt)
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        acc[mt][nt][r] += red[(cw * NACC + (mt * MID_NT + nt) * 4 + r) * 64 + lane];
+                        acc[mt][nt][r] += red[(cw * NACC + (mt * NT + nt) * 4 + r) * 64 + lane];
         }
         __syncthreads();
     }
-    if (kh == 0) {
+    float *dstf = S > 1 ? partials + (size_t)split * M * N + (size_t)m0 * N : (float *)y + (size_t)m0 * N;
+    uint16_t *dsth = (uint16_t *)y + (size_t)m0 * N;
+    for (int rnd = 0; rnd < CW / CHUNK_WAVES; ++rnd) {
+        if (kh == 0 && cw / CHUNK_WAVES == rnd) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < MID_NT; ++nt)
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    red[(16 * mt + 4 * kq + r) * OPITCH + cw * (MID_NT * 16) + 16 * nt + col] = acc[mt][nt][r];
-    }
-    __syncthreads();
-    const int n0 = blockIdx.x * MID_TILES * 16;
-    const int ncols = min(MID_TILES * 16, N - n0);   // a multiple of 16
-    if (S > 1 || y_f32) {
-        float *dst = S > 1 ? partials + (size_t)split * M * N : (float *)y;
-        for (int e = tid; e < M * 32; e += MID_THREADS) {     // 4 floats per thread
-            const int m = e >> 5, c = (e & 31) * 4;
-            if (c < ncols) *(float4 *)(dst + (size_t)m * N + n0 + c) = *(const float4 *)(red + m * OPITCH + c);
+                    for (int r = 0; r < 4; ++r)
+                        red[(16 * mt + 4 * kq + r) * OPITCH + (cw % CHUNK_WAVES) * (NT * 16) + 16 * nt + col] =
+                            acc[mt][nt][r];
         }
-    } else {
-        uint16_t *dst = (uint16_t *)y;
-        for (int e = tid; e < M * 16; e += MID_THREADS) {     // 8 outputs per thread
-            const int m = e >> 4, c = (e & 15) * 8;
-            if (c < ncols) {
-                const float4 lo = *(const float4 *)(red + m * OPITCH + c);
-                const float4 hi = *(const float4 *)(red + m * OPITCH + c + 4);
-                uint4 o;
-                o.x = pack_bf16x2(lo.x, lo.y);
-                o.y = pack_bf16x2(lo.z, lo.w);
-                o.z = pack_bf16x2(hi.x, hi.y);
-                o.w = pack_bf16x2(hi.z, hi.w);
-                *(uint4 *)(dst + (size_t)m * N + n0 + c) = o;
+        __syncthreads();
+        const int n0 = (cblk * TILES) * 16 + rnd * CHUNK;
+        const int ncols = min(CHUNK, N - n0);   // a multiple of 16 (possibly <= 0)
+        if (S > 1 || y_f32) {
+            for (int e = tid; e < Mb * (CHUNK / 4); e += THREADS) {     // 4 floats per thread
+                const int m = e / (CHUNK / 4), c = (e % (CHUNK / 4)) * 4;
+                if (c < ncols) *(float4 *)(dstf + (size_t)m * N + n0 + c) = *(const float4 *)(red + m * OPITCH + c);
+            }
+        } else {
+            for (int e = tid; e < Mb * (CHUNK / 8); e += THREADS) {     // 8 outputs per thread
+                const int m = e / (CHUNK / 8), c = (e % (CHUNK / 8)) * 8;
+                if (c < ncols) {
+                    const float4 lo = *(const float4 *)(red + m * OPITCH + c);
+                    const float4 hi = *(const float4 *)(red + m * OPITCH + c + 4);
+                    uint4 o;
+                    o.x = pack_bf16x2(lo.x, lo.y);
+                    o.y = pack_bf16x2(lo.z, lo.w);
+                    o.z = pack_bf16x2(hi.x, hi.y);
+                    o.w = pack_bf16x2(hi.z, hi.w);
+                    *(uint4 *)(dsth + (size_t)m * N + n0 + c) = o;
+                }
             }
         }
+        __syncthreads();
     }
 }
 
@@ -481,91 +497,6 @@ k_w4a16_splitk_reduce(const float *__restrict__ partials, int S, size_t MN, void
         o.y = pack_bf16x2(a.z, a.w);
         *(uint2 *)((uint16_t *)y + i) = o;
     }
-}
-
-// ---------------------------------------------------------------------------------------------
-// Tiled kernel for large M.  256 threads = 4 waves in a 2x2 arrangement over a 128x128 tile.
-constexpr int TBM = 128, TBN = 128, TBK = kGroup;
-constexpr int TLDS = TBK + 8;   // padded row pitch (bf16 elements) against bank conflicts
-
-__global__ void __launch_bounds__(256)
-k_w4a16_tiled(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
-              const uint32_t *__restrict__ meta, int K, int N, void *__restrict__ y, int y_f32) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[TBM * TLDS];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[TBN * TLDS];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int col = lane & 15, kq = lane >> 4;
-    const int G = K / kGroup;
-    const int T = N / 16;
-    const int m0 = blockIdx.y * TBM, n0 = blockIdx.x * TBN;
-
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int g = 0; g < G; ++g) {
-        // activations: 128 rows x 128 k bf16 = 2048 uint4, 8 per thread
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int idx = tid + it * 256;
-            const int r = idx >> 4, c = idx & 15;
-            const int m = min(m0 + r, M - 1);
-            *(uint4 *)(As + r * TLDS + c * 8) = *(const uint4 *)(x + (size_t)m * K + (size_t)g * kGroup + c * 8);
-        }
-        // weights: 8 column tiles x 1 KB = 512 uint4, 2 per thread; dequantized into LDS.  Chunk b
-        // of a tile block holds column b % 16, k = 32 (b / 16) .. + 31 of the group.
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int idx = tid + it * 256;
-            const int tj = idx >> 6, b = idx & 63;
-            const int t = min(n0 / 16 + tj, T - 1);
-            const uint4 w = load_stream16(codes + ((size_t)t * G + g) * 1024 + b * 16);
-            const DqConst dq = make_dq(meta[((size_t)t * G + g) * 16 + (b & 15)]);
-            const int r = tj * 16 + (b & 15), kc = (b >> 4) * 32;
-            const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t bb[4];
-                dequant8(words[j], dq, bb);
-                *(uint4 *)(Bs + r * TLDS + kc + j * 8) = make_uint4(bb[0], bb[1], bb[2], bb[3]);
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < TBK / 32; ++ks) {
-            bf16x8_t af[4], bfr[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wm * 64 + i * 16 + col;
-                af[i] = __builtin_bit_cast(bf16x8_t, *(const uint4 *)(As + r * TLDS + ks * 32 + kq * 8));
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = wn * 64 + j * 16 + col;
-                bfr[j] = __builtin_bit_cast(bf16x8_t, *(const uint4 *)(Bs + r * TLDS + ks * 32 + kq * 8));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 64 + i * 16 + 4 * kq + r;
-                const int n = n0 + wn * 64 + j * 16 + col;
-                if (m < M && n < N) store_out(y, y_f32, (size_t)m * N + n, acc[i][j][r]);
-            }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -604,8 +535,8 @@ static hipError_t launch_mid(const uint16_t *x, int M, const uint8_t *codes, con
     const int S = mid_splits(K, N);
     const int cbs = (N / 16 + MID_TILES - 1) / MID_TILES;
     float *partials = S > 1 ? (float *)ws : nullptr;
-    hipLaunchKernelGGL((k_w4a16_mid<MT, U>), dim3(cbs, S), dim3(MID_THREADS), 0, st, x, M, codes, meta, K, N, y, y_f32, S,
-                       partials);
+    hipLaunchKernelGGL((k_w4a16_lds<MT, U, MID_KP, MID_CW>), dim3(cbs, S), dim3(MID_KP * MID_CW * 64), 0, st, x,
+                       M, codes, meta, K, N, y, y_f32, S, partials, 1);
     if (S > 1) {
         const size_t MN = (size_t)M * N;
         const unsigned blocks = (unsigned)((MN / 4 + 255) / 256);
@@ -617,7 +548,7 @@ static hipError_t launch_mid(const uint16_t *x, int M, const uint8_t *codes, con
 hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K,
                              int N, void *y, int y_f32, void *ws, hipStream_t st) {
     // Batch tiers, each with one reduction order for all its M: M <= 16 (decode), 16 < M <= 80
-    // (mid, split-K), M > 80 (tiled).
+    // (shared activations, K parts, optional split-K), M > 80 (shared activations, row blocks).
     if (M <= 16) {
         const int nt = decode_shape(K, N, false).nt;
         if (nt == 4) return launch_decode<4, 4>(x, M, codes, meta, K, N, y, y_f32, st);
@@ -628,8 +559,11 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, con
     if (M <= 48) return launch_mid<3, 5>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     if (M <= 64) return launch_mid<4, 4>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     if (M <= 80) return launch_mid<5, 4>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    dim3 grid((N + TBN - 1) / TBN, (M + TBM - 1) / TBM);
-    hipLaunchKernelGGL(k_w4a16_tiled, grid, dim3(256), 0, st, x, M, codes, meta, K, N, y, y_f32);
+    // M > 80: 128-row blocks x 256 columns, no K split, one XCD-remapped 1-D grid
+    const int rbs = (M + BIG_MT * 16 - 1) / (BIG_MT * 16);
+    const int cbs = (N / 16 + BIG_TILES - 1) / BIG_TILES;
+    hipLaunchKernelGGL((k_w4a16_lds<BIG_MT, 4, 1, BIG_CW>), dim3(cbs * rbs), dim3(BIG_CW * 64), 0, st, x, M, codes, meta,
+                       K, N, y, y_f32, 1, (float *)nullptr, rbs);
     return hipGetLastError();
 }
 
