@@ -342,6 +342,218 @@ k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
 }
 
 // ---------------------------------------------------------------------------------------------
+// Shared-activation kernel (M > 64): 64-row blocks x 128 columns per workgroup, 4 waves, each
+// wave 2 column tiles x all rows of the block (128-row blocks spill registers: the per-group
+// int32 products and their rescale need more than 256 VGPRs next to 64 accumulators).  Per group, the waves widen the block's activation
+// codes once into LDS as int8 MFMA fragments (fragment (row tile, MFMA j), lane l's 16 bytes at
+// slot l: conflict-free) next to the rows' activation scales; every wave widens its own weight
+// blocks in registers as signed bytes w - z, so D = sum q_a (w - z) comes straight out of
+// v_mfma_i32_16x16x64_i8 and is rescaled in registers: y += s_a s D.  Codes, meta and scales
+// travel through a U-deep register ring in group order; one barrier per step.  A 1-D grid walks
+// row blocks fastest inside each XCD's range of tiles.
+constexpr int Q_NT = 2, Q_CW = 4, Q_MT = 4;
+constexpr int Q_TILES = Q_NT * Q_CW;
+
+template <int U, bool DOTS>
+__global__ void __launch_bounds__(Q_CW * 64)
+k_w4a4_lds(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, int M,
+           const uint8_t *__restrict__ codes, const uint32_t *__restrict__ meta, int K, int N,
+           void *__restrict__ y, int y_f32, int32_t *__restrict__ dots, int row_blocks) {
+    constexpr int NT = Q_NT, MT = Q_MT, CW = Q_CW;
+    constexpr int THREADS = CW * 64;
+    constexpr int NFW = MT / CW;            // activation row tiles staged per wave
+    static_assert(MT % CW == 0, "row tiles per wave");
+    constexpr int AB = MT * 2 * 64;         // uint4 per staging buffer: [row tile][MFMA j][lane]
+    constexpr int CHUNK = 64, CHUNK_WAVES = CHUNK / (NT * 16), OPITCH = CHUNK + 4;   // epilogue
+    constexpr int LDS_U4 = (2 * AB > (MT * 16 * OPITCH + 3) / 4) ? 2 * AB : (MT * 16 * OPITCH + 3) / 4;
+    __shared__ uint4 lds[LDS_U4];           // staging buffers, reused by the epilogue
+    __shared__ float sbuf[2][MT * 16];      // [buffer][row] activation scales
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int cw = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, kq = lane >> 4;
+    const int G = K / kGroup;
+    const int T = N / 16;
+    const int t_log = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int rblk = t_log % row_blocks, cblk = t_log / row_blocks;
+    const int m0 = rblk * MT * 16;
+    const int Mb = min(MT * 16, M - m0);
+    const int tile0 = cblk * Q_TILES + cw * NT;
+    const i32x4_t izero = {0, 0, 0, 0};
+
+    rsrc_t wr[NT], mr[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int t = min(tile0 + nt, T - 1);              // ragged tile tail: clamp the loads
+        wr[nt] = make_rsrc(codes + (size_t)t * G * 1024, (uint32_t)G * 1024);
+        mr[nt] = make_rsrc(meta + (size_t)t * G * 16, (uint32_t)G * 64);
+    }
+    const rsrc_t ar = make_rsrc(a_codes + (size_t)m0 * (K / 2), (uint32_t)Mb * (K / 2));
+    const rsrc_t sr = make_rsrc(a_scales + (size_t)m0 * G, (uint32_t)Mb * G * 4);
+    // staged row tile q = cw * NFW + u: lane l loads the 16 code bytes of row 16 q + l % 16,
+    // k-quarter l / 16 (its own MFMA A fragment), and that row's scale; rows past the block read
+    // its last row (their MFMA rows are discarded)
+    uint32_t aoff[NFW], soff[NFW];
+#pragma unroll
+    for (int u = 0; u < NFW; ++u) {
+        const int row = min(16 * (cw * NFW + u) + col, Mb - 1);
+        aoff[u] = (uint32_t)(row * (K / 2) + kq * 16);
+        soff[u] = (uint32_t)(row * G) * 4;
+    }
+
+    struct Stage {
+        uint4 w[NT];
+        uint32_t m[NT];
+        uint4 a[NFW];
+        uint32_t s[NFW];
+    };
+    auto load = [&](Stage &st, int i) {
+        const uint32_t g = (uint32_t)(i < G ? i : 0);  // past the end: re-read the first group
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            st.w[nt] = buf_load16_stream(wr[nt], lane * 16, g * 1024);
+            st.m[nt] = buf_load4(mr[nt], col * 4, g * 64);
+        }
+#pragma unroll
+        for (int u = 0; u < NFW; ++u) {
+            st.a[u] = buf_load16(ar, aoff[u], g * 64);
+            st.s[u] = buf_load4(sr, soff[u], g * 4);
+        }
+    };
+    auto stage_act = [&](const Stage &st, int buf) {
+#pragma unroll
+        for (int u = 0; u < NFW; ++u) {
+            const int q = cw * NFW + u;
+            const uint4 e = st.a[u];
+            lds[buf * AB + (q * 2 + 0) * 64 + lane] = make_uint4(snib_lo(e.x), snib_hi(e.x), snib_lo(e.y), snib_hi(e.y));
+            lds[buf * AB + (q * 2 + 1) * 64 + lane] = make_uint4(snib_lo(e.z), snib_hi(e.z), snib_lo(e.w), snib_hi(e.w));
+            if (kq == 0) sbuf[buf][q * 16 + col] = __uint_as_float(st.s[u]);
+        }
+    };
+
+    f32x4_t acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const Stage &st, int buf, int g) {
+        i32x4_t B0[NT], B1[NT];
+        float sw[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const uint4 d = st.w[nt];
+            const uint32_t zz = ((st.m[nt] >> 16) & 0xFFu) * 0x01010101u;
+            sw[nt] = fp16_bits_to_float((uint16_t)(st.m[nt] & 0xFFFFu));
+            B0[nt] = as_i32x4(wz_bytes(nib_lo(d.x), zz), wz_bytes(nib_hi(d.x), zz), wz_bytes(nib_lo(d.y), zz),
+                              wz_bytes(nib_hi(d.y), zz));
+            B1[nt] = as_i32x4(wz_bytes(nib_lo(d.z), zz), wz_bytes(nib_hi(d.z), zz), wz_bytes(nib_lo(d.w), zz),
+                              wz_bytes(nib_hi(d.w), zz));
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint4 a0 = lds[buf * AB + (mt * 2 + 0) * 64 + lane];
+            const uint4 a1 = lds[buf * AB + (mt * 2 + 1) * 64 + lane];
+            const float4 sa = *(const float4 *)&sbuf[buf][mt * 16 + 4 * kq];
+            const float sar[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                i32x4_t ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(a0.x, a0.y, a0.z, a0.w), B0[nt], izero, 0, 0, 0);
+                ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(a1.x, a1.y, a1.z, a1.w), B1[nt], ia, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc[mt][nt][r] = __builtin_fmaf(sar[r] * sw[nt], (float)ia[r], acc[mt][nt][r]);
+                    if (DOTS) {
+                        const int m = 16 * mt + 4 * kq + r;
+                        const int n = 16 * (tile0 + nt) + col;
+                        if (m < Mb && n < N) dots[((size_t)g * M + m0 + m) * N + n] = ia[r];
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);   // one row tile at a time: bounded register use
+        }
+    };
+
+    // Ring: step i refills slot (i + U - 1) % U with group i + U - 1, consumes slot i % U and
+    // stages slot (i + 1) % U into the other LDS buffer; as in the W4A16 shared-activation kernel.
+    Stage st[U];
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u) {
+        load(st[u], u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    stage_act(st[0], 0);
+    __syncthreads();
+    const int nfull = ((G - 1) / U) * U;
+    for (int base = 0; base < nfull; base += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u;
+            load(st[(u + U - 1) % U], i + U - 1);
+            compute(st[u], i & 1, i);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_act(st[(u + 1) % U], (i + 1) & 1);
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = nfull + u;
+        if (i < G) {
+            if (i + U - 1 < G) load(st[(u + U - 1) % U], i + U - 1);
+            compute(st[u], i & 1, i);
+            if (i + 1 < G) {
+                stage_act(st[(u + 1) % U], (i + 1) & 1);
+                __syncthreads();
+            }
+        }
+    }
+    __syncthreads();
+
+    // Epilogue: in rounds of 64 columns (two waves), the sums go row-major through LDS and out
+    // in 16-byte pieces (bfloat16 or f32).
+    float *red = (float *)&lds[0];
+    for (int rnd = 0; rnd < CW / CHUNK_WAVES; ++rnd) {
+        if (cw / CHUNK_WAVES == rnd) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        red[(16 * mt + 4 * kq + r) * OPITCH + (cw % CHUNK_WAVES) * (NT * 16) + 16 * nt + col] =
+                            acc[mt][nt][r];
+        }
+        __syncthreads();
+        const int n0 = cblk * Q_TILES * 16 + rnd * CHUNK;
+        const int ncols = min(CHUNK, N - n0);
+        if (y_f32) {
+            float *dst = (float *)y + (size_t)m0 * N;
+            for (int e = tid; e < Mb * (CHUNK / 4); e += THREADS) {
+                const int m = e / (CHUNK / 4), c = (e % (CHUNK / 4)) * 4;
+                if (c < ncols) *(float4 *)(dst + (size_t)m * N + n0 + c) = *(const float4 *)(red + m * OPITCH + c);
+            }
+        } else {
+            uint16_t *dst = (uint16_t *)y + (size_t)m0 * N;
+            for (int e = tid; e < Mb * (CHUNK / 8); e += THREADS) {
+                const int m = e / (CHUNK / 8), c = (e % (CHUNK / 8)) * 8;
+                if (c < ncols) {
+                    const float4 lo = *(const float4 *)(red + m * OPITCH + c);
+                    const float4 hi = *(const float4 *)(red + m * OPITCH + c + 4);
+                    uint4 o;
+                    o.x = pack_bf16x2(lo.x, lo.y);
+                    o.y = pack_bf16x2(lo.z, lo.w);
+                    o.z = pack_bf16x2(hi.x, hi.y);
+                    o.w = pack_bf16x2(hi.z, hi.w);
+                    *(uint4 *)(dst + (size_t)m * N + n0 + c) = o;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Tiled kernel for large M.  256 threads = 4 waves (2x2) over a 128x128 output tile.
 constexpr int QBM = 128, QBN = 128;
 constexpr int QLDS = kGroup + 16;   // padded row pitch in bytes
@@ -507,9 +719,15 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M
         return launch_skinny4<2, 1, 3, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, st);
     if (M <= 64)
         return launch_skinny4<4, 1, 2, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, st);
-    dim3 grid((N + QBN - 1) / QBN, (M + QBM - 1) / QBM);
-    hipLaunchKernelGGL(k_w4a4_tiled, grid, dim3(256), 0, st, a_codes, a_scales, M, codes, meta, K, N, y, y_f32,
-                       group_dots);
+    // M > 64: 64-row blocks x 128 columns, one XCD-remapped 1-D grid
+    const int rbs = (M + Q_MT * 16 - 1) / (Q_MT * 16);
+    const int cbs = (N / 16 + Q_TILES - 1) / Q_TILES;
+    if (group_dots)
+        hipLaunchKernelGGL((k_w4a4_lds<4, true>), dim3(cbs * rbs), dim3(Q_CW * 64), 0, st, a_codes, a_scales, M, codes,
+                           meta, K, N, y, y_f32, group_dots, rbs);
+    else
+        hipLaunchKernelGGL((k_w4a4_lds<4, false>), dim3(cbs * rbs), dim3(Q_CW * 64), 0, st, a_codes, a_scales, M, codes,
+                           meta, K, N, y, y_f32, group_dots, rbs);
     return hipGetLastError();
 }
 
