@@ -13,8 +13,9 @@
 //    unsigned (0..15) and the zero point is applied after the MFMA as
 //    D = sum(q_a w) - z sum(q_a); the per-(token, group) code sums come from one extra MFMA
 //    against a matrix of ones, which lands them in the accumulator layout.
-//  * k_w4a4_tiled (M > 64): 128x128 tiles per workgroup; the codes of one K group are widened
-//    into LDS once (weights as signed w - z), 4 waves each own a 64x64 sub-tile.
+//  * k_w4a4_lds (M > 64): 64-row blocks; the block's activation codes are widened once per group
+//    into LDS and shared by the workgroup's waves, weights are widened as signed w - z in the
+//    registers of the wave that feeds them to the MFMA.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -551,122 +552,6 @@ k_w4a4_lds(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scal
         }
         __syncthreads();
     }
-}
-
-// ---------------------------------------------------------------------------------------------
-// Tiled kernel for large M.  256 threads = 4 waves (2x2) over a 128x128 output tile.
-constexpr int QBM = 128, QBN = 128;
-constexpr int QLDS = kGroup + 16;   // padded row pitch in bytes
-
-__global__ void __launch_bounds__(256)
-k_w4a4_tiled(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, int M,
-             const uint8_t *__restrict__ codes, const uint32_t *__restrict__ meta, int K, int N,
-             void *__restrict__ y, int y_f32, int32_t *__restrict__ dots) {
-    __shared__ __attribute__((aligned(16))) uint8_t As[QBM * QLDS];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[QBN * QLDS];
-    __shared__ float sA[QBM], sB[QBN];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int col = lane & 15, kq = lane >> 4;
-    const int G = K / kGroup;
-    const int T = N / 16;
-    const size_t row_bytes = (size_t)K / 2;
-    const int m0 = blockIdx.y * QBM, n0 = blockIdx.x * QBN;
-    const i32x4_t izero = {0, 0, 0, 0};
-
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int g = 0; g < G; ++g) {
-        // 128 rows x 64 bytes of codes per operand = 512 uint4 each, 2 + 2 per thread.  Both are
-        // widened in the same byte order, so k slots line up.
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int idx = tid + it * 256;
-            {   // activations: row r, 16-byte chunk c (k = 32 c .. 32 c + 31)
-                const int r = idx >> 2, c = idx & 3;
-                const int m = min(m0 + r, M - 1);
-                const uint4 e = *(const uint4 *)(a_codes + (size_t)m * row_bytes + (size_t)g * 64 + c * 16);
-                uint4 *dst = (uint4 *)(As + r * QLDS + c * 32);
-                dst[0] = make_uint4(snib_lo(e.x), snib_hi(e.x), snib_lo(e.y), snib_hi(e.y));
-                dst[1] = make_uint4(snib_lo(e.z), snib_hi(e.z), snib_lo(e.w), snib_hi(e.w));
-            }
-            {   // weights: tile tj, chunk b = column b % 16, k = 32 (b / 16) .. + 31
-                const int tj = idx >> 6, b = idx & 63;
-                const int t = min(n0 / 16 + tj, T - 1);
-                const uint4 d = load_stream16(codes + ((size_t)t * G + g) * 1024 + b * 16);
-                const uint32_t mw = meta[((size_t)t * G + g) * 16 + (b & 15)];
-                const uint32_t zz = ((mw >> 16) & 0xFFu) * 0x01010101u;
-                uint4 *bd = (uint4 *)(Bs + (tj * 16 + (b & 15)) * QLDS + (b >> 4) * 32);
-                bd[0] = make_uint4(wz_bytes(nib_lo(d.x), zz), wz_bytes(nib_hi(d.x), zz),
-                                   wz_bytes(nib_lo(d.y), zz), wz_bytes(nib_hi(d.y), zz));
-                bd[1] = make_uint4(wz_bytes(nib_lo(d.z), zz), wz_bytes(nib_hi(d.z), zz),
-                                   wz_bytes(nib_lo(d.w), zz), wz_bytes(nib_hi(d.w), zz));
-            }
-        }
-        if (tid < QBM) {
-            sA[tid] = a_scales[(size_t)min(m0 + tid, M - 1) * G + g];
-        } else {
-            const int c = tid - QBM;
-            const int t = min(n0 / 16 + c / 16, T - 1);
-            sB[c] = fp16_bits_to_float((uint16_t)(meta[((size_t)t * G + g) * 16 + (c & 15)] & 0xFFFFu));
-        }
-        __syncthreads();
-        i32x4_t ia[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ia[i][j] = izero;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            i32x4_t af[4], bfr[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 v = *(const uint4 *)(As + (wm * 64 + i * 16 + col) * QLDS + ks * 64 + kq * 16);
-                af[i] = as_i32x4(v.x, v.y, v.z, v.w);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint4 v = *(const uint4 *)(Bs + (wn * 64 + j * 16 + col) * QLDS + ks * 64 + kq * 16);
-                bfr[j] = as_i32x4(v.x, v.y, v.z, v.w);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    ia[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bfr[j], ia[i][j], 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float sbj = sB[wn * 64 + j * 16 + col];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int ml = wm * 64 + i * 16 + 4 * kq + r;
-                    acc[i][j][r] = __builtin_fmaf(sA[ml] * sbj, (float)ia[i][j][r], acc[i][j][r]);
-                    if (dots) {
-                        const int m = m0 + ml, n = n0 + wn * 64 + j * 16 + col;
-                        if (m < M && n < N) dots[((size_t)g * M + m) * N + n] = ia[i][j][r];
-                    }
-                }
-            }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 64 + i * 16 + 4 * kq + r;
-                const int n = n0 + wn * 64 + j * 16 + col;
-                if (m < M && n < N) store_out4(y, y_f32, (size_t)m * N + n, acc[i][j][r]);
-            }
 }
 
 // ---------------------------------------------------------------------------------------------
