@@ -201,25 +201,44 @@ k_w4a4_skinny(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
 // to the 2 NT MFMAs of its tiles (plus the two against ones for the code sums).  Loads are buffer
 // loads from wave-uniform bases; U groups stay in flight in a register ring; wave partials are
 // summed through LDS in wave order (the reduction order depends on (K, N) only).
+// Activation scales: a wave reads those of up to kScaleChunk of its groups at once, 16 groups of
+// one row per lane and 16-byte load, and parks them in its own LDS region as [group][row]; a
+// group then costs one ds_read_b128 (the four rows a lane's outputs hold) instead of four 4-byte
+// loads that touch 16 lines.  The region is private to the wave, so no barrier guards it: a
+// wave's LDS accesses execute in program order.
+constexpr int kScaleChunk = 64;
+
 template <int NT>
 struct W4DStage {
     uint4 w[NT];
     uint32_t meta[NT];
     uint4 a;
-    float as[4];
 };
+
+// Groups per wave-private scale chunk, and the decode kernel's dynamic LDS bytes.
+__host__ __device__ inline int decode_scale_chunk(int G, int kw) {
+    const int per_wave = (G + kw - 1) / kw;
+    return per_wave < kScaleChunk ? per_wave : kScaleChunk;
+}
+
+__host__ inline size_t decode4_lds_bytes(int G, int kw, int NT) {
+    return ((size_t)kw * NT * 256 + (size_t)kw * decode_scale_chunk(G, kw) * 16) * sizeof(float);
+}
 
 template <int NT, int U, bool DOTS>
 __global__ void __launch_bounds__(64 * kMaxDecodeWaves)
 k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, int M,
               const uint8_t *__restrict__ codes, const uint32_t *__restrict__ meta, int K, int N,
               void *__restrict__ y, int y_f32, int32_t *__restrict__ dots, int kw) {
-    extern __shared__ __attribute__((aligned(16))) float red[];   // [kw][NT][4][64], sized at launch
+    // dynamic LDS: red [kw][NT][4][64] floats, then per wave a scale chunk [sch][16] floats
+    extern __shared__ __attribute__((aligned(16))) float red[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int G = K / kGroup;
+    const int sch = decode_scale_chunk(G, kw);
+    float *const sl = red + kw * NT * 256 + wave * sch * 16;
     const int g0 = (wave * G) / kw;
     const int ng = ((wave + 1) * G) / kw - g0;
     const int T = N / 16;
@@ -236,75 +255,92 @@ k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
     }
     const rsrc_t ar = make_rsrc(a_codes + (size_t)g0 * 64, (uint32_t)((size_t)M * K / 2 - (size_t)g0 * 64));
     const rsrc_t sr = make_rsrc(a_scales + g0, (uint32_t)(((size_t)M * G - g0) * 4));
-    // lane offsets: A row = the lane's MFMA row, scales of the 4 output rows the lane holds
+    // lane offsets: A row = the lane's MFMA row; the scale row this lane parks.  Rows past M read
+    // row M - 1 (their outputs are discarded).
     const uint32_t aoff = (uint32_t)(min(col, M - 1) * (K / 2) + kq * 16);
-    uint32_t soff[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) soff[r] = (uint32_t)(min(4 * kq + r, M - 1) * G) * 4;
-
-    // Group i of this wave; refills past the end re-read the first group (long since arrived).
-    auto load = [&](W4DStage<NT> &st, int i) {
-        const uint32_t g = (uint32_t)(i < ng ? i : 0);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            st.w[nt] = buf_load16_stream(wr[nt], lane * 16, g * 1024);
-            st.meta[nt] = buf_load4(mr[nt], col * 4, g * 64);
-        }
-        st.a = buf_load16(ar, aoff, g * 64);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st.as[r] = __uint_as_float(buf_load4(sr, soff[r], g * 4));
-    };
+    const uint32_t srow = (uint32_t)min(col, M - 1) * G;
 
     f32x4_t acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const W4DStage<NT> &cur, int i) {
-        const uint4 e = cur.a;
-        const i32x4_t A0 = as_i32x4(snib_lo(e.x), snib_hi(e.x), snib_lo(e.y), snib_hi(e.y));
-        const i32x4_t A1 = as_i32x4(snib_lo(e.z), snib_hi(e.z), snib_lo(e.w), snib_hi(e.w));
-        i32x4_t sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, ones, izero, 0, 0, 0);
-        sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, ones, sa, 0, 0, 0);
+    for (int c0 = 0; c0 < ng; c0 += sch) {
+        const int cn = min(sch, ng - c0);
+        // Group c0 + i of this wave; refills past the chunk re-read its first group (long since
+        // arrived).
+        auto load = [&](W4DStage<NT> &st, int i) {
+            const uint32_t g = (uint32_t)(c0 + (i < cn ? i : 0));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const uint4 d = cur.w[nt];
-            const float sw = fp16_bits_to_float((uint16_t)(cur.meta[nt] & 0xFFFFu));
-            const int zw = (int)((cur.meta[nt] >> 16) & 0xFFu);
-            const i32x4_t B0 = as_i32x4(nib_lo(d.x), nib_hi(d.x), nib_lo(d.y), nib_hi(d.y));
-            const i32x4_t B1 = as_i32x4(nib_lo(d.z), nib_hi(d.z), nib_lo(d.w), nib_hi(d.w));
-            i32x4_t ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, izero, 0, 0, 0);
-            ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, ia, 0, 0, 0);
+            for (int nt = 0; nt < NT; ++nt) {
+                st.w[nt] = buf_load16_stream(wr[nt], lane * 16, g * 1024);
+                st.meta[nt] = buf_load4(mr[nt], col * 4, g * 64);
+            }
+            st.a = buf_load16(ar, aoff, g * 64);
+        };
+
+        auto compute = [&](const W4DStage<NT> &cur, int i) {
+            const uint4 e = cur.a;
+            const float4 s4 = *(const float4 *)&sl[i * 16 + 4 * kq];   // rows 4 kq .. 4 kq + 3
+            const float as[4] = {s4.x, s4.y, s4.z, s4.w};
+            const i32x4_t A0 = as_i32x4(snib_lo(e.x), snib_hi(e.x), snib_lo(e.y), snib_hi(e.y));
+            const i32x4_t A1 = as_i32x4(snib_lo(e.z), snib_hi(e.z), snib_lo(e.w), snib_hi(e.w));
+            i32x4_t sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, ones, izero, 0, 0, 0);
+            sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, ones, sa, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int Dv = ia[r] - zw * sa[r];
-                acc[nt][r] = __builtin_fmaf(cur.as[r] * sw, (float)Dv, acc[nt][r]);
-                if (DOTS) {
-                    const int mo = 4 * kq + r;
-                    const int n = 16 * (tbase + nt) + col;
-                    if (mo < M && n < N) dots[((size_t)(g0 + i) * M + mo) * N + n] = Dv;
+            for (int nt = 0; nt < NT; ++nt) {
+                const uint4 d = cur.w[nt];
+                const float sw = fp16_bits_to_float((uint16_t)(cur.meta[nt] & 0xFFFFu));
+                const int zw = (int)((cur.meta[nt] >> 16) & 0xFFu);
+                const i32x4_t B0 = as_i32x4(nib_lo(d.x), nib_hi(d.x), nib_lo(d.y), nib_hi(d.y));
+                const i32x4_t B1 = as_i32x4(nib_lo(d.z), nib_hi(d.z), nib_lo(d.w), nib_hi(d.w));
+                i32x4_t ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, izero, 0, 0, 0);
+                ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, ia, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int Dv = ia[r] - zw * sa[r];
+                    acc[nt][r] = __builtin_fmaf(as[r] * sw, (float)Dv, acc[nt][r]);
+                    if (DOTS) {
+                        const int mo = 4 * kq + r;
+                        const int n = 16 * (tbase + nt) + col;
+                        if (mo < M && n < N) dots[((size_t)(g0 + c0 + i) * M + mo) * N + n] = Dv;
+                    }
                 }
             }
-        }
-    };
+        };
 
-    W4DStage<NT> st[U];
+        W4DStage<NT> st[U];
+        // The chunk's scales first (they come from L2; the ring's first group waits on HBM): lane
+        // l reads row l % 16, groups c0 + c + 4 (l / 16) .. + 3, and parks those inside the chunk
+        // at [group][row].  Reads past the array return 0.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // previous chunk's reads first
+        for (int c = 0; c < cn; c += 16) {
+            const int gl = c + 4 * kq;
+            const uint4 v = buf_load16(sr, (srow + (uint32_t)(c0 + gl)) * 4, 0);
+            const float vv[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                 __uint_as_float(v.w)};
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        load(st[u], u);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    const int nfull = ng - ng % U;
-    for (int base = 0; base < nfull; base += U) {
+            for (int e = 0; e < 4; ++e)
+                if (gl + e < cn) sl[(gl + e) * 16 + col] = vv[e];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            compute(st[u], base + u);
-            load(st[u], base + u + U);
+            load(st[u], u);
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
+        const int nfull = cn - cn % U;
+        for (int base = 0; base < nfull; base += U) {
 #pragma unroll
-    for (int u = 0; u < U - 1; ++u)
-        if (nfull + u < ng) compute(st[u], nfull + u);
+            for (int u = 0; u < U; ++u) {
+                compute(st[u], base + u);
+                load(st[u], base + u + U);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U - 1; ++u)
+            if (nfull + u < cn) compute(st[u], nfull + u);
+    }
 
     // Fixed-order reduction of the kw wave partials: every wave parks its NT tiles in LDS (lane
     // layout of the MFMA output), one barrier, then each thread sums 8 consecutive columns of one
@@ -578,7 +614,7 @@ static hipError_t launch_decode4(const uint8_t *a_codes, const float *a_scales, 
                                  const uint32_t *meta, int K, int N, void *y, int y_f32, int32_t *dots, int kw,
                                  hipStream_t st) {
     dim3 grid((N / 16 + NT - 1) / NT), block(64 * kw);
-    const size_t lds = (size_t)kw * NT * 256 * sizeof(float);
+    const size_t lds = decode4_lds_bytes(K / kGroup, kw, NT);
     if (dots)
         hipLaunchKernelGGL((k_w4a4_decode<NT, U, true>), grid, block, lds, st, a_codes, a_scales, M, codes, meta, K,
                            N, y, y_f32, dots, kw);

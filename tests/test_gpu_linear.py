@@ -220,6 +220,27 @@ def test_decode_tilings_w4a4_and_w4a16(M, K, N):
     assert_close(host_f64(y4), ref, False, f"w4a4 {M}x{K}x{N}")
 
 
+# The decode kernel parks activation scales per wave in chunks of 64 groups: K split over 4 waves
+# into 75 groups each (two chunks, a ragged ring tail), and one wave over 70 groups.
+SCALE_CHUNKS = [(16, 128 * 300, 128), (5, 128 * 300, 128), (2, 128 * 70, 16 * 1024)]
+
+
+@pytest.mark.parametrize("M,K,N", SCALE_CHUNKS)
+def test_w4a4_decode_scale_chunks(M, K, N):
+    note(f"w4a4 decode scale chunks M={M} K={K} N={N}")
+    w = si.weights(K, N, seed=K % 991)
+    x = si.activations(M, K, seed=M + 4000)
+    wc, wm = weights_dev(w)
+    codes, scales = run_quant(x)
+    oc, osc = oracle.quantize_act(x)
+    dots = torch.full((K // 128, M, N), -(2 ** 31), dtype=torch.int32, device=DEV)
+    y4 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    q.qspec_gemm_w4a4(codes, scales, wc, wm, y4, group_dots=dots)
+    ref, D = oracle.gemm_w4a4(oc, osc, w["codes"], w["meta"])
+    assert np.array_equal(dots.cpu().numpy().astype(np.int64), D)
+    assert_close(host_f64(y4), ref, False, f"w4a4 {M}x{K}x{N}")
+
+
 def test_w4a4_rows_do_not_depend_on_batch():
     K, N = 1024, 96
     note("gemm_w4a4 batch invariance")
