@@ -247,7 +247,13 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     constexpr int NF = MT * 4;              // activation fragments per group
     constexpr int NFW = NF / CW;            // staged by each wave of a K part
     static_assert(NF % CW == 0, "activation fragments per wave");
-    __shared__ uint4 abuf[KP][2][NF * 64];  // [K part][buffer][fragment][lane]
+    // LDS: the staging buffers [K part][buffer][fragment][lane]; the epilogue reuses them (and,
+    // with K parts, needs a little more: every part's sums, row-major with a padded pitch).
+    constexpr int STAGE_U4 = KP * 2 * NF * 64;
+    constexpr int EPITCH = TILES * 16 + 4;          // floats per output row, K-part epilogue
+    constexpr int EPI_U4 = KP > 1 ? (KP * MT * 16 * EPITCH + 3) / 4 : 0;
+    __shared__ uint4 lds[STAGE_U4 > EPI_U4 ? STAGE_U4 : EPI_U4];
+    auto abuf = [&](int part, int buf) -> uint4 * { return lds + (part * 2 + buf) * NF * 64; };
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
@@ -320,7 +326,7 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     };
     auto stage_act = [&](const Stage &st, int buf) {
 #pragma unroll
-        for (int u = 0; u < NFW; ++u) abuf[kh][buf][xslot[u]] = st.a[u];
+        for (int u = 0; u < NFW; ++u) abuf(kh, buf)[xslot[u]] = st.a[u];
     };
 
     f32x4_t acc[MT][NT];
@@ -329,26 +335,74 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Stage &st, int buf) {
-        DqConst dq[NT];
+    // Verify tier (PIPE): dequantization runs one 32-k step ahead of the MFMAs that consume it, so
+    // a wave's VALU and MFMA work are independent and overlap: while the MFMAs of step j run, the
+    // VALU dequantizes step j + 1, and during the group's last step it dequantizes step 0 of the
+    // next group (whose weights have arrived by then: that stage's activations are staged at the
+    // end of this step).  bq / dc carry the next step's operand and the next group's constants
+    // between calls.  The large tier, with 8 row tiles of accumulators, has no registers for the
+    // carried operands and dequantizes each step right before its MFMAs.
+    constexpr bool PIPE = KP > 1;
+    auto dq_step = [&](const Stage &st, const DqConst (&dq)[NT], int j, bf16x8_t (&bq)[NT]) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const uint32_t word = j == 0 ? st.w[nt].x : j == 1 ? st.w[nt].y : j == 2 ? st.w[nt].z : st.w[nt].w;
+            uint32_t b[4];
+            dequant8(word, dq[nt], b);
+            bq[nt] = as_bf16x8(b[0], b[1], b[2], b[3]);
+        }
+    };
+    auto make_dqs = [&](const Stage &st, DqConst (&dq)[NT]) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) dq[nt] = make_dq(st.m[nt]);
+    };
+    bf16x8_t bq[NT];
+    DqConst dc[NT];
+    auto compute = [&](const Stage &st, const Stage &next, int buf) {
+        if constexpr (!PIPE) {
+            DqConst dq[NT];
+            make_dqs(st, dq);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bf16x8_t av[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                av[mt] = __builtin_bit_cast(bf16x8_t, abuf[kh][buf][(mt * 4 + j) * 64 + (rslot ^ j)]);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const uint32_t word = j == 0 ? st.w[nt].x : j == 1 ? st.w[nt].y : j == 2 ? st.w[nt].z : st.w[nt].w;
-                uint32_t b[4];
-                dequant8(word, dq[nt], b);
-                const bf16x8_t bv = as_bf16x8(b[0], b[1], b[2], b[3]);
+            for (int j = 0; j < 4; ++j) {
+                bf16x8_t av[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, acc[mt][nt], 0, 0, 0);
+                    av[mt] = __builtin_bit_cast(bf16x8_t, abuf(kh, buf)[(mt * 4 + j) * 64 + (rslot ^ j)]);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const uint32_t word = j == 0 ? st.w[nt].x : j == 1 ? st.w[nt].y : j == 2 ? st.w[nt].z : st.w[nt].w;
+                    uint32_t b[4];
+                    dequant8(word, dq[nt], b);
+                    const bf16x8_t bv = as_bf16x8(b[0], b[1], b[2], b[3]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, acc[mt][nt], 0, 0, 0);
+                }
             }
+            return;
+        }
+        DqConst dq[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) dq[nt] = dc[nt];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x8_t av[MT], bv[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) bv[nt] = bq[nt];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                av[mt] = __builtin_bit_cast(bf16x8_t, abuf(kh, buf)[(mt * 4 + j) * 64 + (rslot ^ j)]);
+            if (j < 3) {
+                dq_step(st, dq, j + 1, bq);
+            } else {
+                make_dqs(next, dc);
+                dq_step(next, dc, 0, bq);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
         }
     };
 
@@ -365,6 +419,10 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         __builtin_amdgcn_sched_barrier(0);
     }
     stage_act(st[0], 0);
+    if constexpr (PIPE) {
+        make_dqs(st[0], dc);
+        dq_step(st[0], dc, 0, bq);
+    }
     __syncthreads();
     const int nfull = ((nsteps - 1) / U) * U;
     for (int base = 0; base < nfull; base += U) {
@@ -372,7 +430,7 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         for (int u = 0; u < U; ++u) {
             const int i = base + u;
             load(st[(u + U - 1) % U], i + U - 1);
-            compute(st[u], i & 1);
+            compute(st[u], st[(u + 1) % U], i & 1);
             __builtin_amdgcn_sched_barrier(0);
             stage_act(st[(u + 1) % U], (i + 1) & 1);
             __syncthreads();
@@ -383,7 +441,7 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         const int i = nfull + u;
         if (i < nsteps) {                        // uniform over the workgroup
             if (i + U - 1 < nsteps) load(st[(u + U - 1) % U], i + U - 1);
-            if (i < nh) compute(st[u], i & 1);   // a part may have one group less
+            if (i < nh) compute(st[u], st[(u + 1) % U], i & 1);   // a part may have one group less
             if (i + 1 < nsteps) {
                 stage_act(st[(u + 1) % U], (i + 1) & 1);
                 __syncthreads();
@@ -392,44 +450,64 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     }
     __syncthreads();   // every wave is done reading the staging buffers
 
-    // Epilogue.  (1) Parts 1 .. KP - 1 in turn hand their accumulators to part 0 through LDS (the
-    // staging buffers are free), which adds them in part order.  (2) In rounds of 64 columns (two
-    // column waves), part 0 writes its sums row-major into LDS and all waves store them in
-    // 16-byte pieces: bfloat16 / f32 output, or the fp32 partial of this split.
-    constexpr int NACC = MT * NT * 4;
+    // Epilogue.  With K parts, every wave writes its sums row-major into its part's LDS region,
+    // one barrier, and all waves add the parts in part order and store 16-byte pieces: bfloat16 /
+    // f32 output, or the fp32 partial of this split.  Without K parts (the large tier, whose 128 x
+    // 256 block of sums exceeds the staging buffers), part 0 writes rounds of 64 columns (two
+    // column waves) and all waves store them.
+    float *dstf = S > 1 ? partials + (size_t)split * M * N + (size_t)m0 * N : (float *)y + (size_t)m0 * N;
+    uint16_t *dsth = (uint16_t *)y + (size_t)m0 * N;
+    float *red = (float *)lds;
+    if constexpr (KP > 1) {
+        constexpr int WCOLS = TILES * 16;            // columns of this workgroup
+        constexpr int PART = MT * 16 * EPITCH;       // floats per part region
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    red[kh * PART + (16 * mt + 4 * kq + r) * EPITCH + cw * NT * 16 + 16 * nt + col] = acc[mt][nt][r];
+        __syncthreads();
+        const int n0 = cblk * TILES * 16;
+        const int ncols = min(WCOLS, N - n0);       // a multiple of 16
+        auto part_sum4 = [&](int m, int c) {
+            float4 v = *(const float4 *)(red + m * EPITCH + c);
+#pragma unroll
+            for (int p = 1; p < KP; ++p) {
+                const float4 w = *(const float4 *)(red + p * PART + m * EPITCH + c);
+                v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+            }
+            return v;
+        };
+        if (S > 1 || y_f32) {
+            for (int e = tid; e < Mb * (WCOLS / 4); e += THREADS) {     // 4 floats per thread
+                const int m = e / (WCOLS / 4), c = (e % (WCOLS / 4)) * 4;
+                if (c < ncols) *(float4 *)(dstf + (size_t)m * N + n0 + c) = part_sum4(m, c);
+            }
+        } else {
+            for (int e = tid; e < Mb * (WCOLS / 8); e += THREADS) {     // 8 outputs per thread
+                const int m = e / (WCOLS / 8), c = (e % (WCOLS / 8)) * 8;
+                if (c < ncols) {
+                    const float4 lo = part_sum4(m, c), hi = part_sum4(m, c + 4);
+                    uint4 o;
+                    o.x = pack_bf16x2(lo.x, lo.y);
+                    o.y = pack_bf16x2(lo.z, lo.w);
+                    o.z = pack_bf16x2(hi.x, hi.y);
+                    o.w = pack_bf16x2(hi.z, hi.w);
+                    *(uint4 *)(dsth + (size_t)m * N + n0 + c) = o;
+                }
+            }
+        }
+        return;
+    }
     constexpr int CHUNK = 64;                       // output columns per round
     constexpr int CHUNK_WAVES = CHUNK / (NT * 16);
     constexpr int OPITCH = CHUNK + 4;               // floats per output row in LDS
-    float *red = (float *)&abuf[0][0][0];
-    static_assert(KP == 1 || CW * NACC * 64 <= KP * 2 * NF * 64 * 4, "hand-over buffer");
-    static_assert(MT * 16 * OPITCH <= KP * 2 * NF * 64 * 4, "output buffer");
+    static_assert(MT * 16 * OPITCH <= STAGE_U4 * 4, "output buffer");
     static_assert(CW % CHUNK_WAVES == 0, "column rounds");
-    for (int p = 1; p < KP; ++p) {
-        if (kh == p) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        red[(cw * NACC + (mt * NT + nt) * 4 + r) * 64 + lane] = acc[mt][nt][r];
-        }
-        __syncthreads();
-        if (kh == 0) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[mt][nt][r] += red[(cw * NACC + (mt * NT + nt) * 4 + r) * 64 + lane];
-        }
-        __syncthreads();
-    }
-    float *dstf = S > 1 ? partials + (size_t)split * M * N + (size_t)m0 * N : (float *)y + (size_t)m0 * N;
-    uint16_t *dsth = (uint16_t *)y + (size_t)m0 * N;
     for (int rnd = 0; rnd < CW / CHUNK_WAVES; ++rnd) {
-        if (kh == 0 && cw / CHUNK_WAVES == rnd) {
+        if (cw / CHUNK_WAVES == rnd) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
