@@ -9,9 +9,11 @@
 //   greedy:   k_argmax_partial (one workgroup per row chunk: max and its lowest index)
 //             -> k_greedy_accept (one thread per sequence: combine chunks in order, prefix match)
 //   sampling: k_softmax_partial (per row chunk: chunk max and sum of exp(l - max) in fp64)
-//             -> k_sample_accept (per sequence: row max / normalizer, u < p(d)/q(d) scan in fp64)
+//             -> k_sample_accept (one wave per sequence: lanes combine the rows' chunk statistics
+//                and test the candidates u < p(d)/q(d) in fp64; a ballot finds the first rejection)
 //             -> k_residual_partial (per chunk of the last row: mass of max(0, p - q), or of p)
-//             -> k_residual_pick (per sequence: locate the chunk, scan it in fp64, pick the token)
+//             -> k_residual_pick (per sequence: locate the chunk, its segment and the token; the
+//                residual masses are evaluated in parallel, the running sums stay sequential)
 // Softmax normalizers, ratios and running sums are fp64; the exponentials are fp64 as well.
 #include <float.h>
 #include <limits.h>
@@ -203,43 +205,55 @@ k_softmax_partial(const float *__restrict__ target, const float *__restrict__ dr
     }
 }
 
-__global__ void k_sample_accept(const float *__restrict__ target, const float *__restrict__ draft,
-                                const int32_t *__restrict__ tokens, const float *__restrict__ u,
-                                int B, int gamma, int V, int C, const float *__restrict__ pmax,
-                                const double *__restrict__ psum, float *__restrict__ rowM,
-                                double *__restrict__ rowS, int *__restrict__ accA,
-                                int32_t *__restrict__ accept, int32_t *__restrict__ out) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= B) return;
+// One wave per sequence.  Lane j combines the chunk statistics of row j of the sequence (target
+// rows 0..gamma, then draft rows) in chunk order; then lane j tests candidate j, and the first
+// rejection (an invalid token, or not u < p/q) among the candidates in order ends acceptance.
+__global__ void __launch_bounds__(kWave)
+k_sample_accept(const float *__restrict__ target, const float *__restrict__ draft,
+                const int32_t *__restrict__ tokens, const float *__restrict__ u,
+                int B, int gamma, int V, int C, const float *__restrict__ pmax,
+                const double *__restrict__ psum, float *__restrict__ rowM,
+                double *__restrict__ rowS, int *__restrict__ accA,
+                int32_t *__restrict__ accept, int32_t *__restrict__ out) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
     const long long Rt = (long long)B * (gamma + 1);
-    // combine the chunk statistics of this sequence's rows, in chunk order
-    for (int side = 0; side < 2; ++side) {
-        const int nrows = side == 0 ? gamma + 1 : gamma;
-        for (int j = 0; j < nrows; ++j) {
-            const long long row = side == 0 ? (long long)b * (gamma + 1) + j : Rt + (long long)b * gamma + j;
-            const size_t base = (size_t)row * C;
-            float M = pmax[base];
-            for (int c = 1; c < C; ++c) M = fmaxf(M, pmax[base + c]);
-            double S = 0.0;
-            for (int c = 0; c < C; ++c) S += psum[base + c] * exp((double)pmax[base + c] - (double)M);
-            rowM[row] = M;
-            rowS[row] = S;
+    for (int j = lane; j < 2 * gamma + 1; j += kWave) {
+        const long long row = j <= gamma ? (long long)b * (gamma + 1) + j : Rt + (long long)b * gamma + (j - gamma - 1);
+        const size_t base = (size_t)row * C;
+        float M = pmax[base];
+        for (int c = 1; c < C; ++c) M = fmaxf(M, pmax[base + c]);
+        double S = 0.0;
+        for (int c = 0; c < C; ++c) S += psum[base + c] * exp((double)pmax[base + c] - (double)M);
+        rowM[row] = M;
+        rowS[row] = S;
+    }
+    __syncthreads();   // the rows' statistics, written above by other lanes
+    int A = gamma;
+    for (int j0 = 0; j0 < gamma; j0 += kWave) {
+        const int j = j0 + lane;
+        bool ok = false;
+        if (j < gamma) {
+            const int d = tokens[(size_t)b * gamma + j];
+            if (d >= 0 && d < V) {
+                const long long rt = (long long)b * (gamma + 1) + j;
+                const long long rd = Rt + (long long)b * gamma + j;
+                const double p = exp((double)target[(size_t)rt * V + d] - (double)rowM[rt]) / rowS[rt];
+                const double q = exp((double)draft[(size_t)(rd - Rt) * V + d] - (double)rowM[rd]) / rowS[rd];
+                ok = (double)u[(size_t)b * gamma + j] < p / q;
+            }
+        }
+        const unsigned long long rej = __ballot(j < gamma && !ok);
+        if (rej != 0ull) {
+            A = j0 + __ffsll((long long)rej) - 1;
+            break;
         }
     }
-    int A = 0;
-    while (A < gamma) {
-        const int d = tokens[(size_t)b * gamma + A];
-        if (d < 0 || d >= V) break;
-        const long long rt = (long long)b * (gamma + 1) + A;
-        const long long rd = Rt + (long long)b * gamma + A;
-        const double p = exp((double)target[(size_t)rt * V + d] - (double)rowM[rt]) / rowS[rt];
-        const double q = exp((double)draft[(size_t)(rd - Rt) * V + d] - (double)rowM[rd]) / rowS[rd];
-        if (!((double)u[(size_t)b * gamma + A] < p / q)) break;
-        ++A;
+    if (lane == 0) {
+        accA[b] = A;
+        accept[b] = A;
     }
-    accA[b] = A;
-    accept[b] = A;
-    for (int j = 0; j <= gamma; ++j)
+    for (int j = lane; j <= gamma; j += kWave)
         if (j != A) out[(size_t)b * (gamma + 1) + j] = j < A ? tokens[(size_t)b * gamma + j] : -1;
 }
 
@@ -249,12 +263,12 @@ struct ResidRow {
     const float *d;  // draft row A, or nullptr for the extra token (A == gamma)
     double Mt, St, Md, Sd;
     __device__ __forceinline__ double p(int x) const { return exp((double)t[x] - Mt) / St; }
-    __device__ __forceinline__ double r(int x) const {
-        const double pv = p(x);
+    __device__ __forceinline__ double r_of(int x, double pv) const {
         if (!d) return pv;
         const double dv = pv - exp((double)d[x] - Md) / Sd;
         return dv > 0.0 ? dv : 0.0;
     }
+    __device__ __forceinline__ double r(int x) const { return r_of(x, p(x)); }
 };
 
 __device__ __forceinline__ ResidRow resid_row(const float *target, const float *draft, int B, int gamma,
@@ -287,8 +301,9 @@ k_residual_partial(const float *__restrict__ target, const float *__restrict__ d
     const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
     double sr = 0.0, sp = 0.0;
     for (int x = lo + (int)threadIdx.x; x < hi; x += VT) {
-        sr += R.r(x);
-        sp += R.p(x);
+        const double pv = R.p(x);
+        sr += R.r_of(x, pv);
+        sp += pv;
     }
     sr = block_sum(sr);
     sp = block_sum(sp);
@@ -305,8 +320,8 @@ k_residual_pick(const float *__restrict__ target, const float *__restrict__ draf
                 const int *__restrict__ accA, const double *__restrict__ resid,
                 const double *__restrict__ pmass, int32_t *__restrict__ out) {
     __shared__ double seg[VT];
-    __shared__ int s_chunk, s_fallback, s_usep, s_tok;
-    __shared__ double s_thr;
+    __shared__ int s_chunk, s_fallback, s_usep, s_seg;
+    __shared__ double s_thr, s_run;
     const int b = blockIdx.x;
     const int A = accA[b];
     ResidRow R = resid_row(target, draft, B, gamma, V, b, A, rowM, rowS);
@@ -341,7 +356,6 @@ k_residual_pick(const float *__restrict__ target, const float *__restrict__ draf
         s_fallback = fallback;
         s_usep = usep;
         s_thr = thr - before;
-        s_tok = -1;
     }
     __syncthreads();
     if (s_usep) R.d = nullptr;
@@ -351,36 +365,63 @@ k_residual_pick(const float *__restrict__ target, const float *__restrict__ draf
     for (int x = x0; x < x1; ++x) mine += R.r(x);
     seg[threadIdx.x] = mine;
     __syncthreads();
+    // The segment holding the threshold: a sequential running sum over the segment masses in
+    // order (read 8 at a time).
     if (threadIdx.x == 0) {
-        // the segment holding the threshold, then a sequential scan inside it
-        int tok = -1;
+        int tsel = -1;
+        double run = 0.0;
         if (!s_fallback) {
-            double run = 0.0;
-            for (int t = 0; t < VT && tok < 0; ++t) {
-                if (run + seg[t] > s_thr) {
-                    const int a = lo + t * VSEG, e = min(hi, a + VSEG);
-                    double rr = run;
-                    for (int x = a; x < e; ++x) {
-                        rr += R.r(x);
-                        if (rr > s_thr) { tok = x; break; }
+            for (int t0 = 0; t0 < VT && tsel < 0; t0 += 8) {
+                double sv[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) sv[k] = seg[t0 + k];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (tsel < 0) {
+                        if (run + sv[k] > s_thr) tsel = t0 + k;
+                        else run += sv[k];
                     }
-                    if (tok < 0)   // rounding left the threshold at the segment's end
-                        for (int x = e - 1; x >= a; --x)
-                            if (R.r(x) > 0.0) { tok = x; break; }
-                    if (tok < 0) tok = min(a, hi - 1);
-                }
-                run += seg[t];
             }
         }
-        if (tok < 0) {             // no crossing: the last logit of positive mass in the chunk
-            for (int x = hi - 1; x >= lo; --x)
-                if (R.r(x) > 0.0) { tok = x; break; }
-            if (tok < 0) tok = hi - 1;
-        }
-        s_tok = tok;
+        s_seg = tsel;
+        s_run = run;
     }
     __syncthreads();
-    if (threadIdx.x == 0) out[(size_t)b * (gamma + 1) + A] = s_tok;
+    const int tsel = s_seg;
+    if (tsel >= 0) {
+        // the segment's masses in parallel, then the running sum through them in order
+        const int a = lo + tsel * VSEG, e = min(hi, a + VSEG);
+        if ((int)threadIdx.x < e - a) seg[threadIdx.x] = R.r(a + (int)threadIdx.x);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int tok = -1;
+            double rr = s_run;
+            for (int x = a; x < e; ++x) {
+                rr += seg[x - a];
+                if (rr > s_thr) { tok = x; break; }
+            }
+            if (tok < 0)   // rounding left the threshold at the segment's end
+                for (int x = e - 1; x >= a; --x)
+                    if (seg[x - a] > 0.0) { tok = x; break; }
+            if (tok < 0) tok = min(a, hi - 1);
+            out[(size_t)b * (gamma + 1) + A] = tok;
+        }
+        return;
+    }
+    // No crossing: the last logit of positive mass in the chunk (each thread finds the last one in
+    // its segment; the highest wins), else the chunk's last logit.
+    int last = -1;
+    for (int x = x1 - 1; x >= x0; --x)
+        if (R.r(x) > 0.0) { last = x; break; }
+    __shared__ int s_last[VT];
+    s_last[threadIdx.x] = last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int tok = -1;
+        for (int t = VT - 1; t >= 0 && tok < 0; --t) tok = s_last[t];
+        if (tok < 0) tok = hi - 1;
+        out[(size_t)b * (gamma + 1) + A] = tok;
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -414,7 +455,7 @@ hipError_t launch_verify_accept(int mode, const float *target, const float *draf
     double *pmass = (double *)(w + L.pmass);
     hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)(R * C)), dim3(VT), 0, st, target, draft, B,
                        gamma, V, C, vec, pmax, psum);
-    hipLaunchKernelGGL(k_sample_accept, dim3((B + 63) / 64), dim3(64), 0, st, target, draft, tokens,
+    hipLaunchKernelGGL(k_sample_accept, dim3(B), dim3(kWave), 0, st, target, draft, tokens,
                        u_accept, B, gamma, V, C, pmax, psum, rowM, rowS, accA, accept, out);
     hipLaunchKernelGGL(k_residual_partial, dim3((unsigned)((long long)B * C)), dim3(VT), 0, st, target,
                        draft, B, gamma, V, C, rowM, rowS, accA, resid, pmass);
