@@ -454,6 +454,10 @@ def main():
         "event_ms_per_round": round(event_ms, 4),
         "gemm_hbm_tbs": {"gemm_w4a4_M%d" % B: round(R.draft_gemm_bytes() * g / (draft_ms / 1e3) / 1e12, 3),
                          "gemm_w4a16_M%d" % (B * (g + 1)): round(R.verify_gemm_bytes() / (verify_ms / 1e3) / 1e12, 3)},
+        # verify tokens/s at this gamma as the verify GEMMs alone bound it: B (gamma + 1) tokens per
+        # pass over the layers' four projections (W4A16 at M = B (gamma + 1)), whole stack and per layer
+        "verify_gemm_tokens_per_s": {"layers_%d" % args.layers: round(B * (g + 1) / (verify_ms / 1e3), 1),
+                                     "per_layer": round(B * (g + 1) / (verify_ms / 1e3 / args.layers), 1)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_leg(args)
