@@ -262,13 +262,14 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     const int G = K / kGroup;
     const int T = N / 16;
     // Workgroup -> (column block, split, row block).  A 1-D grid (gridDim.y == 1, the large tier)
-    // walks row blocks fastest inside each XCD's contiguous range of tiles, so the workgroups that
-    // share a column block's weights run together on one XCD and its L2.
+    // walks row blocks fastest, then splits, inside each XCD's contiguous range of tiles, so the
+    // workgroups that share a column block's weights run together on one XCD and its L2.
     int cblk = blockIdx.x, split = blockIdx.y, rblk = 0;
     if (gridDim.y == 1 && row_blocks > 1) {
         const int t = xcd_remap((int)blockIdx.x, (int)gridDim.x);
         rblk = t % row_blocks;
-        cblk = t / row_blocks;
+        split = (t / row_blocks) % S;
+        cblk = t / row_blocks / S;
     }
     const int m0 = rblk * MT * 16;           // this workgroup's row block
     const int Mb = min(MT * 16, M - m0);
@@ -603,10 +604,29 @@ static int mid_splits(int K, int N) {
     return max(1, min(min(fit, kMaxSplits), G / 8));
 }
 
+// K splits of the large tier: a function of (K, N) only.  Its 128-row x 256-column blocks run one
+// workgroup per CU, so a shape with few column blocks leaves a last, mostly empty generation of
+// workgroups (Llama-70B down, 32 column blocks x 10 row blocks at M = 1280: 320 workgroups, 1.25
+// generations); splitting K multiplies the workgroups by S (a power of two up to 128 / column
+// blocks) while every split keeps at least 32 groups.
+static int big_splits(int K, int N) {
+    const int G = K / kGroup;
+    const int cbs = (N / 16 + BIG_TILES - 1) / BIG_TILES;
+    int S = 1;
+    while (S < 8 && 2 * S * cbs <= 128 && G / (2 * S) >= 32) S *= 2;
+    return S;
+}
+
 size_t gemm_w4a16_workspace_bytes(int M, int K, int N) {
-    if (M <= 16 || M > 80) return 0;
-    const int S = mid_splits(K, N);
+    if (M <= 16) return 0;
+    const int S = M <= 80 ? mid_splits(K, N) : big_splits(K, N);
     return S == 1 ? 0 : (size_t)S * M * N * sizeof(float);
+}
+
+static void launch_splitk_reduce(const float *partials, int S, int M, int N, void *y, int y_f32, hipStream_t st) {
+    const size_t MN = (size_t)M * N;
+    const unsigned blocks = (unsigned)((MN / 4 + 255) / 256);
+    hipLaunchKernelGGL(k_w4a16_splitk_reduce, dim3(blocks), dim3(256), 0, st, partials, S, MN, y, y_f32);
 }
 
 template <int MT, int U>
@@ -617,11 +637,7 @@ static hipError_t launch_mid(const uint16_t *x, int M, const uint8_t *codes, con
     float *partials = S > 1 ? (float *)ws : nullptr;
     hipLaunchKernelGGL((k_w4a16_lds<MT, U, MID_KP, MID_CW>), dim3(cbs, S), dim3(MID_KP * MID_CW * 64), 0, st, x,
                        M, codes, meta, K, N, y, y_f32, S, partials, 1);
-    if (S > 1) {
-        const size_t MN = (size_t)M * N;
-        const unsigned blocks = (unsigned)((MN / 4 + 255) / 256);
-        hipLaunchKernelGGL(k_w4a16_splitk_reduce, dim3(blocks), dim3(256), 0, st, partials, S, MN, y, y_f32);
-    }
+    if (S > 1) launch_splitk_reduce(partials, S, M, N, y, y_f32, st);
     return hipGetLastError();
 }
 
@@ -639,11 +655,16 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, con
     if (M <= 48) return launch_mid<3, 5>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     if (M <= 64) return launch_mid<4, 4>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     if (M <= 80) return launch_mid<5, 4>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    // M > 80: 128-row blocks x 256 columns, no K split, one XCD-remapped 1-D grid
+    // M > 80: 128-row blocks x 256 columns, K splits for shapes with few column blocks, one
+    // XCD-remapped 1-D grid (a 2-D (column block, split) grid for a single row block)
     const int rbs = (M + BIG_MT * 16 - 1) / (BIG_MT * 16);
     const int cbs = (N / 16 + BIG_TILES - 1) / BIG_TILES;
-    hipLaunchKernelGGL((k_w4a16_lds<BIG_MT, 4, 1, BIG_CW>), dim3(cbs * rbs), dim3(BIG_CW * 64), 0, st, x, M, codes, meta,
-                       K, N, y, y_f32, 1, (float *)nullptr, rbs);
+    const int S = big_splits(K, N);
+    float *partials = S > 1 ? (float *)ws : nullptr;
+    const dim3 grid = rbs > 1 ? dim3(cbs * S * rbs) : dim3(cbs, S);
+    hipLaunchKernelGGL((k_w4a16_lds<BIG_MT, 4, 1, BIG_CW>), grid, dim3(BIG_CW * 64), 0, st, x, M, codes, meta,
+                       K, N, y, y_f32, S, partials, rbs);
+    if (S > 1) launch_splitk_reduce(partials, S, M, N, y, y_f32, st);
     return hipGetLastError();
 }
 

@@ -76,6 +76,11 @@ def test_gemm_validation():
     assert L.qspec_gemm_w4a16(FAKE, 80, FAKE, FAKE, 4096, 4096, FAKE, 0, None, 0, None) == ERR_WS
     assert L.qspec_gemm_w4a16(FAKE, 80, FAKE, FAKE, 4096, 4096, FAKE, 0, FAKE, need - 1, None) == ERR_WS
     assert L.qspec_gemm_w4a16_workspace_bytes(80, 4096, 70) == 0
+    # large tier: K is split only for few 256-column blocks and long K
+    assert L.qspec_gemm_w4a16_workspace_bytes(1280, 8192, 57344) == 0
+    assert L.qspec_gemm_w4a16_workspace_bytes(1280, 28672, 8192) == 4 * 1280 * 8192 * 4
+    assert L.qspec_gemm_w4a16_workspace_bytes(96, 32768, 512) == 8 * 96 * 512 * 4
+    assert L.qspec_gemm_w4a16(FAKE, 1280, FAKE, FAKE, 28672, 8192, FAKE, 0, None, 0, None) == ERR_WS
 
 
 def test_verify_validation_and_workspace_sizes():

@@ -140,6 +140,29 @@ def test_w4a16_split_k_workspace_reuse(M, K, N):
                  "split-K")
 
 
+# Large tier (M > 80) with K splits: few 256-column blocks and long K.  8192 x 256 splits K in two
+# (one row block: a 2-D grid; two row blocks, the second ragged: the 1-D remapped grid),
+# 32768 x 512 in eight.
+LARGE_SPLIT = [(100, 8192, 256), (200, 8192, 256), (96, 32768, 512)]
+
+
+@pytest.mark.parametrize("M,K,N", LARGE_SPLIT)
+def test_w4a16_large_tier_split_k(M, K, N):
+    note(f"gemm_w4a16 large-tier split-K M={M} K={K} N={N}")
+    assert q.qspec_gemm_w4a16_workspace_bytes(M, K, N) >= 2 * 4 * M * N
+    w = si.weights(K, N, seed=K // 128 + N)
+    wdev = weights_dev(w)
+    x = si.activations(M, K, seed=M + 77)
+    y = run_w4a16(x, w, torch.float32, wdev).cpu().numpy()
+    tiles = np.array([0, N // 16 - 1])
+    sub = si.slice_tiles(w, tiles)
+    assert_close(y[:, tile_columns(tiles)].astype(np.float64), oracle.gemm_w4a16(x, sub["codes"], sub["meta"]),
+                 False, "large split-K")
+    if M > 100:                          # same tier, same (K, N): bitwise-equal rows
+        y100 = run_w4a16(x[:100], w, torch.float32, wdev).cpu().numpy()
+        assert np.array_equal(y100, y[:100])
+
+
 FULL_W4A16 = [
     # Llama-3-8B-shaped projections, verify at M = 5B for B in 1, 4, 16
     ("llama8b.qkv", 4096, 6144, 80), ("llama8b.o", 4096, 4096, 20), ("llama8b.gate_up", 4096, 28672, 5),

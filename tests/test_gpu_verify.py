@@ -33,8 +33,9 @@ def run_verify(mode, t, d, toks, u, v):
     return acc.cpu().numpy(), out.cpu().numpy()
 
 
+# gamma = 0 is the draft-side sampling head: one token per row from softmax(row) (or its argmax).
 SHAPES = [(1, 4, 1024), (3, 2, 100), (5, 0, 77), (4, 8, 50001), (2, 16, 8191), (7, 3, 8193),
-          (32, 4, 128256)]
+          (32, 4, 128256), (16, 0, 128256)]
 
 
 @pytest.mark.parametrize("B,gamma,V", SHAPES)
