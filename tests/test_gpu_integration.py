@@ -1,0 +1,137 @@
+"""Integration identity: a toy decoder built only from the C ABI plus host glue.  QSPEC greedy
+decoding (gamma W4A4 draft steps writing low-precision KV, one W4A16 verify pass over gamma + 1
+positions, greedy acceptance, KV overwrite of the committed positions) must emit exactly the
+token stream of plain W4A16 greedy decoding.  (QSPEC notes, QSPEC structure: the W4A4 draft and
+the W4A16 verifier share one set of 4-bit weights, verification keeps the output W4A16-equivalent
+and the verifier's KV replaces the draft's for accepted tokens; speculative-decoding background:
+greedy acceptance and the first-reject cutoff.)
+
+The toy model: an embedding table E [V][H]; a one-projection "KV" row kv(t) = W_kv E[token_t]
+cached per position; next-token logits = lm_head(E[token_t] + mean of the cached rows 0..t).
+The identity holds because row results of qspec_gemm_w4a16 do not depend on M within a batch
+tier (M = 1 in plain decoding, gamma + 1 in verification), so the verifier reproduces plain
+decoding's KV rows and logits bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_speculative_decoding_amd as q
+import synthetic_inputs as si
+from gpu_helpers import DEV, bf16_dev, cu, note, weights_dev
+
+pytestmark = pytest.mark.gpu
+
+V, H, HEADS, D, CTX = 1024, 256, 2, 128, 96
+
+
+class Toy:
+    def __init__(self, seed: int, unrelated_draft_head: bool = False):
+        self.E = si.activations(V, H, seed=seed)                  # bf16 bits [V][H]
+        self.Ef = self.E.astype(np.uint32) << 16
+        self.Ef = self.Ef.view(np.float32)
+        self.w_kv = weights_dev(si.weights(H, H, seed=seed + 1))
+        self.w_lm = weights_dev(si.weights(H, V, seed=seed + 2))
+        # a draft head unrelated to the target's: most drafts are rejected, which exercises the
+        # correction token and the overwrite of rejected draft KV on every round
+        self.w_lm_draft = weights_dev(si.weights(H, V, seed=seed + 3)) if unrelated_draft_head else self.w_lm
+
+    # ---- glue (host): h = bf16(E[token] + mean of the KV rows), the same arithmetic everywhere
+    def hidden(self, tok: int, rows: np.ndarray) -> np.ndarray:
+        kv = (rows.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        mean = kv.sum(axis=0) / kv.shape[0]
+        return si.f32_to_bf16_bits((self.Ef[tok].astype(np.float64) + mean).astype(np.float32))
+
+    # ---- W4A16 (verify precision)
+    def kv16(self, toks) -> np.ndarray:
+        x = bf16_dev(self.E[np.asarray(toks)])
+        y = torch.empty((len(toks), H), dtype=torch.bfloat16, device=DEV)
+        q.qspec_gemm_w4a16(x, *self.w_kv, y)
+        return y.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def logits16(self, hs: np.ndarray) -> torch.Tensor:
+        y = torch.empty((hs.shape[0], V), dtype=torch.float32, device=DEV)
+        q.qspec_gemm_w4a16(bf16_dev(hs), *self.w_lm, y)
+        return y
+
+    # ---- W4A4 (draft precision): quantize, then the draft layer
+    def _w4a4(self, x_bits: np.ndarray, w, N: int, out) -> torch.Tensor:
+        M = x_bits.shape[0]
+        codes = torch.empty((M, H // 2), dtype=torch.uint8, device=DEV)
+        scales = torch.empty((M, H // 128), dtype=torch.float32, device=DEV)
+        q.qspec_quantize_act(bf16_dev(x_bits), codes, scales)
+        y = torch.empty((M, N), dtype=out, device=DEV)
+        q.qspec_gemm_w4a4(codes, scales, *w, y)
+        return y
+
+    def kv4(self, tok: int) -> np.ndarray:
+        y = self._w4a4(self.E[[tok]], self.w_kv, H, torch.bfloat16)
+        return y.view(torch.int16).cpu().numpy().view(np.uint16)[0]
+
+    def logits4(self, h: np.ndarray) -> np.ndarray:
+        return self._w4a4(h[None], self.w_lm_draft, V, torch.float32).cpu().numpy()[0]
+
+
+def plain_greedy(m: Toy, first: int, n: int) -> list:
+    toks, rows = [first], []
+    while len(toks) < n + 1:
+        t = len(toks) - 1
+        rows.append(m.kv16([toks[t]])[0])
+        h = m.hidden(toks[t], np.stack(rows))
+        toks.append(int(np.argmax(m.logits16(h[None]).cpu().numpy()[0])))
+    return toks
+
+
+def qspec_greedy(m: Toy, first: int, n: int, gamma: int):
+    cache = torch.zeros((1, 1, 2, HEADS, CTX, D), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty((q.qspec_verify_workspace_bytes(q.QSPEC_GREEDY, 1, gamma, V),), dtype=torch.uint8, device=DEV)
+    acc = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    out = torch.zeros((1, gamma + 1), dtype=torch.int32, device=DEV)
+
+    def rows(lo, hi):   # cached KV rows lo..hi-1 (slot 0), [n][H] bf16 bits
+        r = cache[0, 0, 0, :, lo:hi, :].permute(1, 0, 2).reshape(hi - lo, H)
+        return r.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    toks, p, accepts = [first], 0, []
+    while len(toks) < n + 1:
+        # draft: gamma W4A4 steps, each writing its low-precision KV row at its position
+        d, tok = [], toks[p]
+        for j in range(gamma):
+            kvd = torch.from_numpy(m.kv4(tok).view(np.int16)).view(torch.bfloat16).to(DEV)
+            cache[0, 0, 0, :, p + j, :] = kvd.view(HEADS, D)
+            h = m.hidden(tok, rows(0, p + j + 1))
+            tok = int(np.argmax(m.logits4(h)))
+            d.append(tok)
+        # verify: one W4A16 pass over positions p .. p + gamma
+        vt = [toks[p]] + d                                         # tokens at p .. p + gamma
+        vkv = m.kv16(vt)                                           # [gamma + 1][H]
+        base = rows(0, p)
+        hs = np.stack([m.hidden(vt[j], np.concatenate([base, vkv[: j + 1]])) for j in range(gamma + 1)])
+        target = m.logits16(hs).view(1, gamma + 1, V)
+        q.qspec_verify_accept(q.QSPEC_GREEDY, target, None, cu(np.array([d], np.int32)), None, None, acc, out, ws)
+        stage = torch.zeros((1, 1, 2, HEADS, gamma + 1, D), dtype=torch.bfloat16, device=DEV)
+        stage[0, 0, 0] = torch.from_numpy(vkv.view(np.int16)).view(torch.bfloat16).to(DEV).view(
+            gamma + 1, HEADS, D).permute(1, 0, 2)
+        q.qspec_kv_overwrite(cache, stage, cu(np.array([p], np.int32)), acc)
+        A = int(acc.cpu()[0])
+        committed = out.cpu().numpy()[0, : A + 1].tolist()
+        assert committed[:A] == d[:A]
+        accepts.append(A)
+        toks.extend(committed)
+        p += A + 1
+    return toks[: n + 1], accepts
+
+
+@pytest.mark.parametrize("seed,gamma,unrelated", [(11, 4, False), (23, 2, False), (37, 7, False), (5, 4, True)])
+def test_qspec_greedy_loop_equals_plain_w4a16_greedy(seed, gamma, unrelated):
+    note(f"toy decoder identity seed={seed} gamma={gamma} unrelated draft head={unrelated}")
+    m = Toy(seed, unrelated)
+    n = 40
+    ref = plain_greedy(m, first=seed % V, n=n)
+    got, accepts = qspec_greedy(m, first=seed % V, n=n, gamma=gamma)
+    note(f"accept counts per round: {accepts}")
+    assert got == ref
+    assert len(accepts) > 1
+    if unrelated:
+        assert accepts.count(0) > len(accepts) // 2       # mostly first-position rejections
+    else:
+        assert sum(accepts) > 0                           # the drafts were used
