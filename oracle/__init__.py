@@ -63,8 +63,9 @@ def _lib():
         lib.orc_verify_greedy.argtypes = [P, P, I, I, I, P, P]
         lib.orc_verify_sample.argtypes = [P, P, P, P, P, I, I, I, P, P, P]
         lib.orc_kv_overwrite.argtypes = [P, P, P, P, I, I, I, I, I, I]
+        lib.orc_speckv_gamma.argtypes = [P, I, I, ctypes.c_float, P, P, P, P, I, P, P, P]
         for name in ("orc_dequant", "orc_gemm_w4a16", "orc_quantize_act", "orc_gemm_w4a4",
-                     "orc_verify_greedy", "orc_verify_sample", "orc_kv_overwrite"):
+                     "orc_verify_greedy", "orc_verify_sample", "orc_kv_overwrite", "orc_speckv_gamma"):
             getattr(lib, name).restype = None
         _LIB = lib
     return _LIB
@@ -178,6 +179,24 @@ def verify_sample(target, draft, draft_tokens, u, v, with_diag: bool = True):
     _lib().orc_verify_sample(_p(target), _p(draft), _p(d), _p(u), _p(v), B, gamma, V,
                              _p(acc), _p(out), _p(diag))
     return acc, out, diag
+
+
+def speckv_gamma(logits, quant_feature, w1, b1, w2, b2):
+    """Draft statistics and the adaptive-gamma controller (SpecKV notes).
+    logits f32 [R][V]; w1 [64][3], b1 [64], w2 [G1][64], b2 [G1] (f32).
+    Returns (gamma i32 [R], features f64 [R][2] = (confidence, entropy), mlp f64 [R][G1])."""
+    logits = _c(logits, np.float32)
+    R, V = logits.shape
+    w1, b1 = _c(w1, np.float32).reshape(64, 3), _c(b1, np.float32).reshape(64)
+    w2 = _c(w2, np.float32)
+    G1 = w2.shape[0]
+    w2, b2 = w2.reshape(G1, 64), _c(b2, np.float32).reshape(G1)
+    gamma = np.empty(R, np.int32)
+    feats = np.empty((R, 2), np.float64)
+    mlp = np.empty((R, G1), np.float64)
+    _lib().orc_speckv_gamma(_p(logits), R, V, float(quant_feature), _p(w1), _p(b1), _p(w2), _p(b2), G1 - 1,
+                            _p(feats), _p(gamma), _p(mlp))
+    return gamma, feats, mlp
 
 
 def kv_overwrite(cache, verify_kv, start_pos, accept):

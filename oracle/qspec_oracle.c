@@ -387,6 +387,64 @@ void orc_verify_sample(const float *target, const float *draft, const int32_t *d
     free(r);
 }
 
+/* ---- O8: draft statistics and the adaptive-gamma controller ----------------
+ * [SpecKV notes, architecture and mechanism: the draft's confidence is its
+ * largest softmax probability and its uncertainty is the entropy of the
+ * softmax; together with the compression level they feed a small MLP that
+ * picks gamma.  Implementation guide (the controller listing): the entropy
+ * adds 1e-9 inside the logarithm, the MLP is Linear(3 -> 64), ReLU,
+ * Linear(64 -> max_gamma + 1), and gamma is the index of the largest output.]
+ * Readings: softmax at temperature 1 in fp64 as in O6; confidence = max_x p(x);
+ * entropy = -sum_x p(x) log(p(x) + 1e-9), summed in x order; the third input is
+ * one caller-supplied number for all rows (the page feeds one column of the
+ * compression-level one-hot); the MLP runs in fp64 on fp32 weights, every dot
+ * product summed in input order after the bias; ties in the argmax take the
+ * lowest index.
+ * logits: f32 [R][V]; w1: f32 [64][3]; b1: f32 [64]; w2: f32 [G1][64]; b2: f32 [G1]
+ * with G1 = max_gamma + 1.  features (may be NULL): f64 [R][2] = (confidence,
+ * entropy); gamma: i32 [R]; logits_out (may be NULL): f64 [R][G1].
+ */
+void orc_speckv_gamma(const float *logits, int64_t R, int64_t V, float quant_feature,
+                      const float *w1, const float *b1, const float *w2, const float *b2,
+                      int64_t max_gamma, double *features, int32_t *gamma, double *logits_out)
+{
+    double *p = (double *)malloc(sizeof(double) * (size_t)V);
+    const int64_t G1 = max_gamma + 1;
+    for (int64_t r = 0; r < R; ++r) {
+        softmax_row(logits + r * V, V, p);
+        double conf = 0.0, ent = 0.0;
+        for (int64_t x = 0; x < V; ++x) {
+            if (p[x] > conf) conf = p[x];
+            ent += p[x] * log(p[x] + 1e-9);
+        }
+        ent = -ent;
+        if (features) {
+            features[2 * r] = conf;
+            features[2 * r + 1] = ent;
+        }
+        const double in[3] = {conf, ent, (double)quant_feature};
+        double h[64];
+        for (int i = 0; i < 64; ++i) {
+            double t = (double)b1[i];
+            for (int k = 0; k < 3; ++k) t += (double)w1[i * 3 + k] * in[k];
+            h[i] = t > 0.0 ? t : 0.0;
+        }
+        int32_t best = 0;
+        double best_v = 0.0;
+        for (int64_t j = 0; j < G1; ++j) {
+            double t = (double)b2[j];
+            for (int i = 0; i < 64; ++i) t += (double)w2[j * 64 + i] * h[i];
+            if (logits_out) logits_out[r * G1 + j] = t;
+            if (j == 0 || t > best_v) {
+                best_v = t;
+                best = (int32_t)j;
+            }
+        }
+        gamma[r] = best;
+    }
+    free(p);
+}
+
 /* ---- O7: KV replacement for accepted positions ------------------------------
  * [QSPEC notes, QSPEC structure: for accepted tokens the low-precision KV the
  * W4A4 draft wrote is replaced by the KV the W4A16 verifier computed.]
