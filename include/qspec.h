@@ -84,6 +84,9 @@ enum qspec_status {
 enum qspec_out_dtype { QSPEC_OUT_BF16 = 0, QSPEC_OUT_F32 = 1 };
 enum qspec_verify_mode { QSPEC_GREEDY = 0, QSPEC_SAMPLE = 1 };
 
+/* Largest gamma the adaptive-gamma controller may choose (its outputs are 0..max_gamma). */
+#define QSPEC_SPECKV_MAX_GAMMA 63
+
 /* Human-readable name of a status code (static string). */
 const char *qspec_status_string(int status);
 
@@ -217,6 +220,43 @@ int qspec_verify_accept(int32_t mode, const float *target_logits, const float *d
 int qspec_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const int32_t *start_pos,
                        const int32_t *accept_count, int32_t L, int32_t B, int32_t H, int32_t T,
                        int32_t D, int32_t gamma, qspec_stream_t stream);
+
+/*
+ * qspec_speckv_workspace_bytes -- device workspace qspec_speckv_gamma needs for R rows of V
+ * logits; 0 on invalid sizes.
+ */
+size_t qspec_speckv_workspace_bytes(int32_t R, int32_t V);
+
+/*
+ * qspec_speckv_gamma -- draft statistics and the adaptive-gamma controller.
+ * [SpecKV notes, architecture and mechanism: how sure the draft is (its largest
+ * softmax probability) and how spread its distribution is (its entropy), with
+ * the compression level, feed a small MLP that picks gamma for the next step;
+ * implementation guide: the controller is Linear(3 -> 64), ReLU,
+ * Linear(64 -> max_gamma + 1), and gamma is the index of the largest output;
+ * the entropy adds 1e-9 inside the logarithm.]  Per row r, in fp64:
+ *     p = softmax(draft_logits[r])                          (temperature 1)
+ *     confidence = max p,  entropy = -sum_x p(x) log(p(x) + 1e-9)
+ *     h = relu(w1 [confidence, entropy, quant_feature] + b1)       (64 units)
+ *     gamma_out[r] = argmax_j (w2 h + b2)_j   (lowest index among equal outputs)
+ * Every dot product is summed in input order after its bias.
+ * draft_logits  [in]  f32 [R][V] (finite values)
+ * quant_feature [in]  the controller's third input, shared by all rows (the page feeds one column
+ *                     of the compression-level one-hot)
+ * w1 [in] f32 [64][3], b1 [in] f32 [64], w2 [in] f32 [max_gamma + 1][64], b2 [in] f32
+ *                     [max_gamma + 1]: device copies of the controller's weights
+ * max_gamma     [in]  0 .. QSPEC_SPECKV_MAX_GAMMA
+ * features      [out] f64 [R][2] = (confidence, entropy), or NULL
+ * gamma_out     [out] i32 [R]
+ * workspace     [in/out] at least qspec_speckv_workspace_bytes(R, V) bytes (chunk partials; no
+ *                     initialization needed)
+ * Errors: NULL pointer (features may be NULL); R < 1; V < 1; max_gamma outside
+ * [0, QSPEC_SPECKV_MAX_GAMMA]; workspace missing or too small.
+ */
+int qspec_speckv_gamma(const float *draft_logits, int32_t R, int32_t V, float quant_feature,
+                       const float *w1, const float *b1, const float *w2, const float *b2,
+                       int32_t max_gamma, double *features, int32_t *gamma_out, void *workspace,
+                       size_t workspace_bytes, qspec_stream_t stream);
 
 #ifdef __cplusplus
 }

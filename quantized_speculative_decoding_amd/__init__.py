@@ -61,8 +61,11 @@ def lib() -> ctypes.CDLL:
         L.qspec_verify_workspace_bytes.restype = S
         L.qspec_verify_accept.argtypes = [I, P, P, P, P, P, I, I, I, P, P, P, S, P]
         L.qspec_kv_overwrite.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
+        L.qspec_speckv_workspace_bytes.argtypes = [I, I]
+        L.qspec_speckv_workspace_bytes.restype = S
+        L.qspec_speckv_gamma.argtypes = [P, I, I, ctypes.c_float, P, P, P, P, I, P, P, P, S, P]
         for fn in ("qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16",
-                   "qspec_verify_accept", "qspec_kv_overwrite"):
+                   "qspec_verify_accept", "qspec_kv_overwrite", "qspec_speckv_gamma"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -215,9 +218,36 @@ def qspec_kv_overwrite(cache, verify_kv, start_pos, accept_count, stream=None) -
                                     L, B, H, T, D, gamma, _stream(stream, cache)))
 
 
+def qspec_speckv_workspace_bytes(R: int, V: int) -> int:
+    return int(lib().qspec_speckv_workspace_bytes(R, V))
+
+
+def qspec_speckv_gamma(draft_logits, quant_feature, w1, b1, w2, b2, gamma_out, features=None, workspace=None,
+                       stream=None) -> None:
+    """Draft statistics and the adaptive-gamma controller; see include/qspec.h.
+    draft_logits f32 [R][V]; w1 f32 [64][3], b1 [64], w2 [G1][64], b2 [G1]; gamma_out i32 [R];
+    features f64 [R][2] or None; workspace u8 (qspec_speckv_workspace_bytes(R, V) bytes)."""
+    _req(draft_logits, "draft_logits", torch.float32)
+    R, V = draft_logits.shape
+    _req(w1, "w1", torch.float32, (64, 3))
+    _req(b1, "b1", torch.float32, (64,))
+    _req(w2, "w2", torch.float32)
+    G1 = w2.shape[0]
+    _req(w2, "w2", torch.float32, (G1, 64))
+    _req(b2, "b2", torch.float32, (G1,))
+    _req(gamma_out, "gamma_out", torch.int32, (R,))
+    if features is not None:
+        _req(features, "features", torch.float64, (R, 2))
+    _req(workspace, "workspace", torch.uint8)
+    _check("qspec_speckv_gamma",
+           lib().qspec_speckv_gamma(_ptr(draft_logits), R, V, float(quant_feature), _ptr(w1), _ptr(b1), _ptr(w2),
+                                    _ptr(b2), G1 - 1, _ptr(features), _ptr(gamma_out), _ptr(workspace),
+                                    workspace.numel(), _stream(stream, draft_logits)))
+
+
 __all__ = [
     "GROUP", "QSPEC_GREEDY", "QSPEC_SAMPLE", "QSPEC_OUT_BF16", "QSPEC_OUT_F32", "QspecError", "lib",
     "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_gemm_w4a16_workspace_bytes",
     "gemm_w4a16_workspace", "qspec_verify_workspace_bytes",
-    "qspec_verify_accept", "qspec_kv_overwrite",
+    "qspec_verify_accept", "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma",
 ]

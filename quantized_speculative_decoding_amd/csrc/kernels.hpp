@@ -28,6 +28,12 @@ hipError_t launch_verify_accept(int mode, const float *target, const float *draf
                                 int32_t *accept_count, int32_t *out_tokens, void *workspace,
                                 hipStream_t st);
 
+size_t speckv_workspace_bytes(int R, int V);
+
+hipError_t launch_speckv_gamma(const float *logits, int R, int V, float quant_feature, const float *w1,
+                               const float *b1, const float *w2, const float *b2, int max_gamma,
+                               double *features, int32_t *gamma_out, void *workspace, hipStream_t st);
+
 hipError_t launch_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const int32_t *start_pos,
                                const int32_t *accept_count, int L, int B, int H, int T, int D,
                                int gamma, hipStream_t st);

@@ -118,6 +118,30 @@ QSPEC_EXPORT int qspec_verify_accept(int32_t mode, const float *target_logits,
                                                  out_tokens, workspace, as_stream(stream)));
 }
 
+static bool speckv_sizes_ok(int32_t R, int32_t V, int32_t max_gamma) {
+    if (R < 1 || V < 1 || max_gamma < 0 || max_gamma > QSPEC_SPECKV_MAX_GAMMA) return false;
+    return (long long)R * ((V + 8191) / 8192) < (1LL << 31) && (long long)R * V <= kMaxElems;
+}
+
+QSPEC_EXPORT size_t qspec_speckv_workspace_bytes(int32_t R, int32_t V) {
+    if (!speckv_sizes_ok(R, V, 0)) return 0;
+    return qspec::speckv_workspace_bytes(R, V);
+}
+
+QSPEC_EXPORT int qspec_speckv_gamma(const float *draft_logits, int32_t R, int32_t V, float quant_feature,
+                                    const float *w1, const float *b1, const float *w2, const float *b2,
+                                    int32_t max_gamma, double *features, int32_t *gamma_out, void *workspace,
+                                    size_t workspace_bytes, qspec_stream_t stream) {
+    if (!draft_logits || !w1 || !b1 || !w2 || !b2 || !gamma_out) return QSPEC_ERR_NULL;
+    if (!speckv_sizes_ok(R, V, max_gamma)) return QSPEC_ERR_SHAPE;
+    if (!workspace || workspace_bytes < qspec::speckv_workspace_bytes(R, V)) return QSPEC_ERR_WORKSPACE;
+    if (!aligned(draft_logits, 4) || !aligned(w1, 4) || !aligned(b1, 4) || !aligned(w2, 4) || !aligned(b2, 4) ||
+        !aligned(features, 8) || !aligned(gamma_out, 4) || !aligned(workspace, 16))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_speckv_gamma(draft_logits, R, V, quant_feature, w1, b1, w2, b2, max_gamma,
+                                                features, gamma_out, workspace, as_stream(stream)));
+}
+
 QSPEC_EXPORT int qspec_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv,
                                     const int32_t *start_pos, const int32_t *accept_count,
                                     int32_t L, int32_t B, int32_t H, int32_t T, int32_t D,

@@ -425,6 +425,136 @@ k_residual_pick(const float *__restrict__ target, const float *__restrict__ draf
 }
 
 // ---------------------------------------------------------------------------------------------
+// Draft statistics and the adaptive-gamma controller (SpecKV notes, architecture and mechanism;
+// the implementation guide's controller): per draft row, confidence = max p and entropy =
+// -sum p log(p + 1e-9) of softmax(row) in fp64, then Linear(3 -> 64), ReLU, Linear(64 -> G1) and
+// the index of the largest output (lowest on ties).  Stages: k_softmax_partial (chunk max and
+// sum of exp), k_entropy_partial (per chunk: sum of p log(p + 1e-9) with the row's max and
+// normalizer), k_speckv_head (one wave per row: combine in chunk order, run the MLP).
+constexpr int kSpeckvHidden = 64;
+
+struct SpeckvLayout {
+    int C;
+    size_t pmax, psum, pent, total;
+};
+
+static SpeckvLayout speckv_layout(int R, int V) {
+    SpeckvLayout L = {};
+    L.C = (V + VCHUNK - 1) / VCHUNK;
+    size_t off = 0;
+    L.pmax = off; off = align256(off + (size_t)R * L.C * sizeof(float));
+    L.psum = off; off = align256(off + (size_t)R * L.C * sizeof(double));
+    L.pent = off; off = align256(off + (size_t)R * L.C * sizeof(double));
+    L.total = off;
+    return L;
+}
+
+size_t speckv_workspace_bytes(int R, int V) { return speckv_layout(R, V).total; }
+
+// The row's max and softmax normalizer from its chunk statistics, in chunk order.
+__device__ __forceinline__ void row_stats(const float *pmax, const double *psum, int C, float &M, double &S) {
+    M = pmax[0];
+    for (int c = 1; c < C; ++c) M = fmaxf(M, pmax[c]);
+    S = 0.0;
+    for (int c = 0; c < C; ++c) S += psum[c] * exp((double)pmax[c] - (double)M);
+}
+
+__global__ void __launch_bounds__(VT)
+k_entropy_partial(const float *__restrict__ logits, int V, int C, const float *__restrict__ pmax,
+                  const double *__restrict__ psum, double *__restrict__ pent) {
+    __shared__ float sM;
+    __shared__ double sS;
+    const int row = blockIdx.x / C, c = blockIdx.x % C;
+    if (threadIdx.x == 0) {
+        float M;
+        double S;
+        row_stats(pmax + (size_t)row * C, psum + (size_t)row * C, C, M, S);
+        sM = M;
+        sS = S;
+    }
+    __syncthreads();
+    const double M = (double)sM, S = sS;
+    const float *p = logits + (size_t)row * V;
+    const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
+    double t = 0.0;
+    for (int x = lo + (int)threadIdx.x; x < hi; x += VT) {
+        const double pv = exp((double)p[x] - M) / S;
+        t += pv * log(pv + 1e-9);
+    }
+    t = block_sum(t);
+    if (threadIdx.x == 0) pent[blockIdx.x] = t;
+}
+
+__global__ void __launch_bounds__(kWave)
+k_speckv_head(int C, const float *__restrict__ pmax, const double *__restrict__ psum,
+              const double *__restrict__ pent, float quant_feature, const float *__restrict__ w1,
+              const float *__restrict__ b1, const float *__restrict__ w2, const float *__restrict__ b2, int G1,
+              double *__restrict__ features, int32_t *__restrict__ gamma_out) {
+#pragma clang fp contract(off)
+    __shared__ double h[kSpeckvHidden];
+    const int row = blockIdx.x;
+    const int lane = threadIdx.x;
+    float M;
+    double S;
+    row_stats(pmax + (size_t)row * C, psum + (size_t)row * C, C, M, S);
+    double ent = 0.0;
+    for (int c = 0; c < C; ++c) ent += pent[(size_t)row * C + c];
+    ent = -ent;
+    const double conf = 1.0 / S;       // the largest probability: exp(M - M) / S
+    const double in[3] = {conf, ent, (double)quant_feature};
+    {
+        double t = (double)b1[lane];
+        for (int k = 0; k < 3; ++k) t += (double)w1[lane * 3 + k] * in[k];
+        h[lane] = t > 0.0 ? t : 0.0;
+    }
+    __syncthreads();
+    double o = -INFINITY;
+    if (lane < G1) {
+        o = (double)b2[lane];
+        for (int i = 0; i < kSpeckvHidden; ++i) o += (double)w2[lane * kSpeckvHidden + i] * h[i];
+    }
+    // argmax over the lanes, lowest index on ties (lanes past G1 hold -inf and lose)
+    int best = lane < G1 ? lane : INT_MAX;
+    double bv = o;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double ov = __shfl_xor(bv, off, kWave);
+        const int oi = __shfl_xor(best, off, kWave);
+        if (ov > bv || (ov == bv && oi < best)) {
+            bv = ov;
+            best = oi;
+        }
+    }
+    if (lane == 0) {
+        gamma_out[row] = best;
+        if (features) {
+            features[2 * (size_t)row] = conf;
+            features[2 * (size_t)row + 1] = ent;
+        }
+    }
+}
+
+hipError_t launch_speckv_gamma(const float *logits, int R, int V, float quant_feature, const float *w1,
+                               const float *b1, const float *w2, const float *b2, int max_gamma,
+                               double *features, int32_t *gamma_out, void *ws, hipStream_t st) {
+    const SpeckvLayout L = speckv_layout(R, V);
+    char *w = (char *)ws;
+    const int C = L.C;
+    float *pmax = (float *)(w + L.pmax);
+    double *psum = (double *)(w + L.psum);
+    double *pent = (double *)(w + L.pent);
+    const bool vec = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0);
+    // R rows of "target" logits and no draft rows: the verification's chunk pass with gamma = 0
+    hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)((long long)R * C)), dim3(VT), 0, st, logits,
+                       (const float *)nullptr, R, 0, V, C, vec, pmax, psum);
+    hipLaunchKernelGGL(k_entropy_partial, dim3((unsigned)((long long)R * C)), dim3(VT), 0, st, logits, V, C, pmax,
+                       psum, pent);
+    hipLaunchKernelGGL(k_speckv_head, dim3(R), dim3(kWave), 0, st, C, pmax, psum, pent, quant_feature, w1, b1, w2, b2,
+                       max_gamma + 1, features, gamma_out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
 
 hipError_t launch_verify_accept(int mode, const float *target, const float *draft,
                                 const int32_t *tokens, const float *u_accept, const float *u_resample,

@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "qspec_status_string", "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16",
         "qspec_gemm_w4a16_workspace_bytes", "qspec_verify_workspace_bytes", "qspec_verify_accept",
-        "qspec_kv_overwrite"])
+        "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma"])
 
 
 def test_library_exports_every_declared_symbol_and_nothing_else():
@@ -131,3 +131,26 @@ def test_alignment_validation():
     assert L.qspec_verify_accept(0, FAKE, None, FAKE, None, None, 2, 3, 5000, FAKE, FAKE,
                                  ctypes.c_void_p(0x1004), need, None) == ERR_ALIGN
     assert L.qspec_kv_overwrite(odd, FAKE, FAKE, FAKE, 1, 1, 1, 8, 8, 2, None) == ERR_ALIGN
+
+
+def test_speckv_validation():
+    L = q.lib()
+    L.qspec_speckv_gamma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float] + \
+        [ctypes.c_void_p] * 4 + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p]
+    L.qspec_speckv_workspace_bytes.restype = ctypes.c_size_t
+    need = L.qspec_speckv_workspace_bytes(16, 128256)
+    assert need > 0 and L.qspec_speckv_workspace_bytes(0, 10) == 0 and L.qspec_speckv_workspace_bytes(1, 0) == 0
+
+    def call(**kw):
+        a = dict(logits=FAKE, R=16, V=128256, qf=0.0, w1=FAKE, b1=FAKE, w2=FAKE, b2=FAKE, g=8, feat=None,
+                 out=FAKE, ws=FAKE, nbytes=need)
+        a.update(kw)
+        return L.qspec_speckv_gamma(a["logits"], a["R"], a["V"], a["qf"], a["w1"], a["b1"], a["w2"], a["b2"],
+                                    a["g"], a["feat"], a["out"], a["ws"], a["nbytes"], None)
+    for k in ("logits", "w1", "b1", "w2", "b2", "out"):
+        assert call(**{k: None}) == ERR_NULL, k
+    assert call(R=0) == ERR_SHAPE and call(V=0) == ERR_SHAPE
+    assert call(g=-1) == ERR_SHAPE and call(g=64) == ERR_SHAPE
+    assert call(ws=None) == ERR_WS and call(nbytes=need - 1) == ERR_WS
+    assert call(feat=ctypes.c_void_p(0x1004)) == ERR_ALIGN
