@@ -341,7 +341,32 @@ def gpu_leg(args):
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
+    R.speckv_us = speckv_controller_us(R, torch)
     return R, ph, wall, event_ms
+
+
+def speckv_controller_us(R, torch):
+    """Outside the timed round: the adaptive-gamma controller (draft confidence and entropy over
+    one draft row per sequence, then its MLP) on the round's draft logits, graph-replayed over the
+    4 logit sets; random controller weights (the trained ones are not published)."""
+    q, B, V = R.q, R.B, VOCAB
+    dev = R.accept.device
+    rows = [d[:, -1, :].contiguous() for (_, d, _, _, _) in R.logits]       # the last draft step
+    gen = torch.Generator(device=dev).manual_seed(900)
+    w1, b1 = torch.randn((64, 3), device=dev, generator=gen), torch.randn((64,), device=dev, generator=gen)
+    w2, b2 = torch.randn((9, 64), device=dev, generator=gen), torch.randn((9,), device=dev, generator=gen)
+    g = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = torch.empty((q.qspec_speckv_workspace_bytes(B, V),), dtype=torch.uint8, device=dev)
+    graph = capture(lambda: [q.qspec_speckv_gamma(r, 0.0, w1, b1, w2, b2, g, None, ws) for r in rows], torch)
+    graph.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (5 * len(rows))
 
 
 def cpu_leg(args):
@@ -456,6 +481,8 @@ def main():
                          "gemm_w4a16_M%d" % (B * (g + 1)): round(R.verify_gemm_bytes() / (verify_ms / 1e3) / 1e12, 3)},
         # verify tokens/s at this gamma as the verify GEMMs alone bound it: B (gamma + 1) tokens per
         # pass over the layers' four projections (W4A16 at M = B (gamma + 1)), whole stack and per layer
+        # outside the timed round: the adaptive-gamma controller on one draft row per sequence
+        "speckv_controller_us": round(R.speckv_us, 1),
         "verify_gemm_tokens_per_s": {"layers_%d" % args.layers: round(B * (g + 1) / (verify_ms / 1e3), 1),
                                      "per_layer": round(B * (g + 1) / (verify_ms / 1e3 / args.layers), 1)},
     }
