@@ -55,6 +55,10 @@ TRAFFIC_JSON = os.path.join(PROFILES, "pmc_traffic.json")
 COPY_MIB = 256
 
 
+# How the summaries under profiles/ are made (OUT = an output folder, REPO = this repository).
+PROFILE_COMMAND = ('cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o bench -- python3 REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline ; rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/prof_fetch -o bench -- python3 REPO/bench.py --steps 1 --warmup 0 --layers 8 --no-cpu-baseline --copy-calibration-mib 256 ; (the same with --pmc WRITE_SIZE -d OUT/prof_write) ; python3 REPO/bench.py --summarize OUT/prof_trace OUT/prof_fetch OUT/prof_write')
+
+
 def kernel_source_hash() -> str:
     """Hash of the HIP sources; counter figures are only reused while it is unchanged."""
     import glob
@@ -171,7 +175,8 @@ def parse():
                     help="after the timed region, run one plain device copy of this size (for counter scaling)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output and exit (no GPU needed)")
-    ap.add_argument("--summary-command", default="", help="the command that produced the profiles (recorded)")
+    ap.add_argument("--summary-command", default=PROFILE_COMMAND,
+                    help="the command that produced the profiles (recorded in the summaries)")
     return ap.parse_args()
 
 
