@@ -64,8 +64,10 @@ def _lib():
         lib.orc_verify_sample.argtypes = [P, P, P, P, P, I, I, I, P, P, P]
         lib.orc_kv_overwrite.argtypes = [P, P, P, P, I, I, I, I, I, I]
         lib.orc_speckv_gamma.argtypes = [P, I, I, ctypes.c_float, P, P, P, P, I, P, P, P]
+        lib.orc_attention.argtypes = [P, P, P, I, I, I, I, I, I, ctypes.c_float, P]
         for name in ("orc_dequant", "orc_gemm_w4a16", "orc_quantize_act", "orc_gemm_w4a4",
-                     "orc_verify_greedy", "orc_verify_sample", "orc_kv_overwrite", "orc_speckv_gamma"):
+                     "orc_verify_greedy", "orc_verify_sample", "orc_kv_overwrite", "orc_speckv_gamma",
+                     "orc_attention"):
             getattr(lib, name).restype = None
         _LIB = lib
     return _LIB
@@ -197,6 +199,22 @@ def speckv_gamma(logits, quant_feature, w1, b1, w2, b2):
     _lib().orc_speckv_gamma(_p(logits), R, V, float(quant_feature), _p(w1), _p(b1), _p(w2), _p(b2), G1 - 1,
                             _p(feats), _p(gamma), _p(mlp))
     return gamma, feats, mlp
+
+
+def attention(q, cache, pos, scale):
+    """Causal attention of Q query tokens per sequence over one layer of the KV cache.
+    q u16 [B][Q][Hq][D] (bf16 bits); cache u16 [B][2][Hkv][T][D]; pos i32 [B]; returns u16
+    [B][Q][Hq][D].  Query j of sequence b attends to positions 0 .. min(pos[b] + j, T - 1)."""
+    q = _c(q, np.uint16)
+    B, Q, Hq, D = q.shape
+    cache = _c(cache, np.uint16)
+    assert cache.shape[:2] == (B, 2) and cache.shape[4] == D
+    Hkv, T = cache.shape[2], cache.shape[3]
+    assert Hq % Hkv == 0
+    pos = _c(pos, np.int32).reshape(B)
+    out = np.empty_like(q)
+    _lib().orc_attention(_p(q), _p(cache), _p(pos), B, Q, Hq, Hkv, T, D, float(scale), _p(out))
+    return out
 
 
 def kv_overwrite(cache, verify_kv, start_pos, accept):

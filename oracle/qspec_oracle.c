@@ -445,6 +445,56 @@ void orc_speckv_gamma(const float *logits, int64_t R, int64_t V, float quant_fea
     free(p);
 }
 
+/* ---- O9: attention over the shared KV cache ---------------------------------
+ * [QSPEC notes, QSPEC structure: the draft and the verifier attend over one KV
+ * cache, in which the verifier's KV replaces the draft's for accepted tokens.]
+ * The pages fix no attention arithmetic; the plainest reading is scaled
+ * dot-product attention: query token j of sequence b sits at position
+ * pos[b] + j and attends to the cached positions 0 .. min(pos[b] + j, T - 1)
+ * (causal); query head h reads KV head h / (Hq / Hkv); scores s_t = scale *
+ * q . k_t, weights softmax(s) (fp64, max subtracted), output sum_t p_t v_t
+ * rounded to bfloat16 (nearest-even).
+ * q: u16 [B][Q][Hq][D] bf16; cache: u16 [B][2][Hkv][T][D] bf16 (one layer; 0 = key,
+ * 1 = value); pos: i32 [B]; out: u16 [B][Q][Hq][D] bf16.
+ */
+void orc_attention(const uint16_t *q, const uint16_t *cache, const int32_t *pos, int64_t B, int64_t Q,
+                   int64_t Hq, int64_t Hkv, int64_t T, int64_t D, float scale, uint16_t *out)
+{
+    double *s = (double *)malloc(sizeof(double) * (size_t)T);
+    double *o = (double *)malloc(sizeof(double) * (size_t)D);
+    const int64_t G = Hq / Hkv;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < Q; ++j)
+            for (int64_t h = 0; h < Hq; ++h) {
+                const int64_t hk = h / G;
+                const uint16_t *qv = q + ((b * Q + j) * Hq + h) * D;
+                const uint16_t *kb = cache + ((b * 2 + 0) * Hkv + hk) * T * D;
+                const uint16_t *vb = cache + ((b * 2 + 1) * Hkv + hk) * T * D;
+                int64_t last = (int64_t)pos[b] + j;
+                if (last > T - 1) last = T - 1;
+                double mx = -INFINITY;
+                for (int64_t t = 0; t <= last; ++t) {
+                    double d = 0.0;
+                    for (int64_t e = 0; e < D; ++e)
+                        d += (double)bf16_to_float(qv[e]) * (double)bf16_to_float(kb[t * D + e]);
+                    s[t] = (double)scale * d;
+                    if (s[t] > mx) mx = s[t];
+                }
+                double sum = 0.0;
+                for (int64_t t = 0; t <= last; ++t) {
+                    s[t] = exp(s[t] - mx);
+                    sum += s[t];
+                }
+                for (int64_t e = 0; e < D; ++e) o[e] = 0.0;
+                for (int64_t t = 0; t <= last; ++t)
+                    for (int64_t e = 0; e < D; ++e) o[e] += s[t] / sum * (double)bf16_to_float(vb[t * D + e]);
+                uint16_t *ov = out + ((b * Q + j) * Hq + h) * D;
+                for (int64_t e = 0; e < D; ++e) ov[e] = orc_double_to_bf16(o[e]);
+            }
+    free(s);
+    free(o);
+}
+
 /* ---- O7: KV replacement for accepted positions ------------------------------
  * [QSPEC notes, QSPEC structure: for accepted tokens the low-precision KV the
  * W4A4 draft wrote is replaced by the KV the W4A16 verifier computed.]
