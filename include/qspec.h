@@ -87,6 +87,10 @@ enum qspec_verify_mode { QSPEC_GREEDY = 0, QSPEC_SAMPLE = 1 };
 /* Largest gamma the adaptive-gamma controller may choose (its outputs are 0..max_gamma). */
 #define QSPEC_SPECKV_MAX_GAMMA 63
 
+/* qspec_attention: the head dimension it supports and the most query tokens per sequence. */
+#define QSPEC_ATTN_HEAD_DIM 128
+#define QSPEC_ATTN_MAX_QUERIES 64
+
 /* Human-readable name of a status code (static string). */
 const char *qspec_status_string(int status);
 
@@ -257,6 +261,42 @@ int qspec_speckv_gamma(const float *draft_logits, int32_t R, int32_t V, float qu
                        const float *w1, const float *b1, const float *w2, const float *b2,
                        int32_t max_gamma, double *features, int32_t *gamma_out, void *workspace,
                        size_t workspace_bytes, qspec_stream_t stream);
+
+/*
+ * qspec_attention_workspace_bytes -- device workspace qspec_attention needs; 0 on invalid sizes
+ * (the head dimension is QSPEC_ATTN_HEAD_DIM).
+ */
+size_t qspec_attention_workspace_bytes(int32_t B, int32_t Q, int32_t Hq, int32_t Hkv, int32_t T);
+
+/*
+ * qspec_attention -- one layer's attention over the shared KV cache.
+ * [QSPEC notes, QSPEC structure: the W4A4 draft and the W4A16 verifier read and write one KV
+ * cache, and the verifier's KV replaces the draft's for accepted tokens (qspec_kv_overwrite).]
+ * The pages fix no attention arithmetic; this call is causal scaled dot-product attention with
+ * grouped KV heads.  Query token j of sequence b sits at position pos[b] + j (a draft step has
+ * Q = 1, a verify pass Q = gamma + 1) and attends to cached positions t = 0 .. min(pos[b] + j,
+ * T - 1); query head h reads KV head h / (Hq / Hkv):
+ *     out[b][j][h] = sum_t softmax_t(scale * q[b][j][h] . key[b][h'][t]) value[b][h'][t]
+ * Scores, exponentials and sums are fp32; the output is rounded once to bfloat16.  The cache
+ * entries of the query positions themselves are expected to be written before the call.
+ * q          [in]  u16 [B][Q][Hq][D] bfloat16
+ * cache      [in]  u16 [B][2][Hkv][T][D] bfloat16 (2 = key, value): one layer of the
+ *                  [L][B][2][H][T][D] cache qspec_kv_overwrite updates, i.e. its base plus
+ *                  layer * B * 2 * H * T * D elements
+ * pos        [in]  i32 [B] (device); negative entries read as 0
+ * D          QSPEC_ATTN_HEAD_DIM
+ * scale      the score scale, typically 1 / sqrt(D)
+ * out        [out] u16 [B][Q][Hq][D] bfloat16
+ * workspace  [in/out] at least qspec_attention_workspace_bytes(B, Q, Hq, Hkv, T) bytes (chunk
+ *            partials; no initialization needed)
+ * Alignment: q, cache and workspace 16 bytes.
+ * Errors: NULL pointer; B, Q, Hq, Hkv or T < 1; D other than QSPEC_ATTN_HEAD_DIM; Q above
+ * QSPEC_ATTN_MAX_QUERIES; Hq not a multiple of Hkv; B * Hkv above 65535; workspace missing or
+ * too small.
+ */
+int qspec_attention(const uint16_t *q, const uint16_t *cache, const int32_t *pos, int32_t B, int32_t Q,
+                    int32_t Hq, int32_t Hkv, int32_t T, int32_t D, float scale, uint16_t *out,
+                    void *workspace, size_t workspace_bytes, qspec_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -64,8 +64,11 @@ def lib() -> ctypes.CDLL:
         L.qspec_speckv_workspace_bytes.argtypes = [I, I]
         L.qspec_speckv_workspace_bytes.restype = S
         L.qspec_speckv_gamma.argtypes = [P, I, I, ctypes.c_float, P, P, P, P, I, P, P, P, S, P]
+        L.qspec_attention_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.qspec_attention_workspace_bytes.restype = S
+        L.qspec_attention.argtypes = [P, P, P, I, I, I, I, I, I, ctypes.c_float, P, P, S, P]
         for fn in ("qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16",
-                   "qspec_verify_accept", "qspec_kv_overwrite", "qspec_speckv_gamma"):
+                   "qspec_verify_accept", "qspec_kv_overwrite", "qspec_speckv_gamma", "qspec_attention"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -245,9 +248,34 @@ def qspec_speckv_gamma(draft_logits, quant_feature, w1, b1, w2, b2, gamma_out, f
                                     workspace.numel(), _stream(stream, draft_logits)))
 
 
+def qspec_attention_workspace_bytes(B: int, Q: int, Hq: int, Hkv: int, T: int) -> int:
+    return int(lib().qspec_attention_workspace_bytes(B, Q, Hq, Hkv, T))
+
+
+def qspec_attention(q, cache, pos, scale, out, workspace, stream=None) -> None:
+    """Causal attention over one layer of the shared KV cache; see include/qspec.h.
+    q bf16 [B][Q][Hq][D]; cache bf16 [B][2][Hkv][T][D]; pos i32 [B]; out bf16 [B][Q][Hq][D];
+    workspace u8 (qspec_attention_workspace_bytes(B, Q, Hq, Hkv, T) bytes)."""
+    _req(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B][Q][Hq][D]")
+    B, Q, Hq, D = q.shape
+    _req(cache, "cache", torch.bfloat16)
+    if cache.dim() != 5 or cache.shape[0] != B or cache.shape[1] != 2 or cache.shape[4] != D:
+        raise ValueError("cache must be [B][2][Hkv][T][D]")
+    Hkv, T = cache.shape[2], cache.shape[3]
+    _req(pos, "pos", torch.int32, (B,))
+    _req(out, "out", torch.bfloat16, (B, Q, Hq, D))
+    _req(workspace, "workspace", torch.uint8)
+    _check("qspec_attention",
+           lib().qspec_attention(_ptr(q), _ptr(cache), _ptr(pos), B, Q, Hq, Hkv, T, D, float(scale), _ptr(out),
+                                 _ptr(workspace), workspace.numel(), _stream(stream, q)))
+
+
 __all__ = [
     "GROUP", "QSPEC_GREEDY", "QSPEC_SAMPLE", "QSPEC_OUT_BF16", "QSPEC_OUT_F32", "QspecError", "lib",
     "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_gemm_w4a16_workspace_bytes",
     "gemm_w4a16_workspace", "qspec_verify_workspace_bytes",
     "qspec_verify_accept", "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma",
+    "qspec_attention_workspace_bytes", "qspec_attention",
 ]

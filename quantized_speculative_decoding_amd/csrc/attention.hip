@@ -1,0 +1,294 @@
+// Attention over the shared KV cache on gfx950 (QSPEC notes, QSPEC structure: the draft and the
+// verifier attend over one KV cache in which the verifier's KV replaces the draft's for accepted
+// tokens).  The pages fix no attention arithmetic; this is causal scaled dot-product attention:
+// query token j of sequence b sits at position pos[b] + j and sees the cached positions
+// 0 .. min(pos[b] + j, T - 1); query head h reads KV head h / (Hq / Hkv).
+//
+// All Q * G query rows that read one KV head (G = Hq / Hkv) are handled by one workgroup, so
+// every cached key and value is read from HBM once per pass of up to 16 * RT rows.  Both
+// contractions are bf16 MFMAs (v_mfma_f32_16x16x32_bf16; lane l = c + 16 kq):
+//   scores  S^T = K Q^T: A = keys (row = position 16 tt + c), B = queries (col = row r = c), the
+//           contraction over d in slots d = 32 j + 8 kq + i; lane l receives S[16 tt + 4 kq + e][c].
+//   outputs O^T = V^T P^T: A = values transposed in registers (row c <-> d = 8 c + m for MFMA m),
+//           B = probabilities (col = row r = c) in the 8 position slots {4 kq + e, 16 + 4 kq + e}
+//           where the scores left them; lane l receives O[c][8 (4 kq + e) + m].
+// So a row's scores, running max, running sum and outputs all sit on the 4 lanes c + 16 kq, and
+// the online softmax needs only two cross-lane steps per reduction.  Probabilities enter the MFMA
+// as a bf16 pair hi + lo (p - hi is exact in fp32), which keeps them to about 2^-17 relative.
+//
+// A wave streams 128 positions (4 steps of 32) through a 2-deep register ring; the 4 waves of a
+// workgroup cover a chunk of 512 positions and merge their (max, sum, outputs) through LDS in
+// wave order; k_attn_combine merges the chunks of each query row in chunk order.  Loads past the
+// last visible position of the group read that position instead (probability 0).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qspec {
+
+constexpr int kAttnD = 128;                      // head dimension
+constexpr int kAttnWaves = 4;
+constexpr int kAttnStep = 32;                    // positions per MFMA step
+constexpr int kAttnSteps = 4;                    // steps per wave
+constexpr int kAttnChunk = kAttnWaves * kAttnSteps * kAttnStep;   // 512 positions per workgroup
+constexpr int kAttnOPitch = kAttnD + 4;          // floats per LDS output row
+
+typedef __attribute__((ext_vector_type(8))) __bf16 attn_bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float attn_f32x4_t;
+
+struct AttnLayout {
+    int NC;                                      // chunks per sequence
+    size_t m, l, o, total;
+};
+
+static AttnLayout attn_layout(int B, int Q, int Hq, int T) {
+    AttnLayout L = {};
+    L.NC = (T + kAttnChunk - 1) / kAttnChunk;
+    const size_t rows = (size_t)B * Q * Hq * L.NC;
+    size_t off = 0;
+    L.m = off; off = (off + rows * sizeof(float) + 255) & ~(size_t)255;
+    L.l = off; off = (off + rows * sizeof(float) + 255) & ~(size_t)255;
+    L.o = off; off = (off + rows * kAttnD * sizeof(float) + 255) & ~(size_t)255;
+    L.total = off;
+    return L;
+}
+
+size_t attention_workspace_bytes(int B, int Q, int Hq, int T) { return attn_layout(B, Q, Hq, T).total; }
+
+// Last position visible to query token j of a sequence whose first query sits at p (p < 0 reads as 0).
+__device__ __forceinline__ int attn_last(int p, int j, int T) {
+    const long long v = (long long)max(p, 0) + j;
+    return v < T ? (int)v : T - 1;
+}
+
+__device__ __forceinline__ attn_bf16x8_t attn_as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint4 u = {a, b, c, d};
+    return __builtin_bit_cast(attn_bf16x8_t, u);
+}
+
+template <int RT>
+struct AttnStage {
+    uint4 k[2][4];                               // [position tile][d step]
+    uint4 v[8];                                  // [position slot]
+};
+
+template <int RT>
+__global__ void __launch_bounds__(kAttnWaves * kWave)
+k_attn_partial(const uint16_t *__restrict__ q, const uint16_t *__restrict__ cache, const int32_t *__restrict__ pos,
+               int Q, int Hq, int Hkv, int T, float scale, int NC, float *__restrict__ wm, float *__restrict__ wl,
+               float *__restrict__ wo) {
+    constexpr int ROWS = 16 * RT;
+    __shared__ float sm[kAttnWaves][ROWS], sl[kAttnWaves][ROWS];
+    __shared__ __attribute__((aligned(16))) float so[kAttnWaves][ROWS][kAttnOPitch];
+
+    const int chunk = blockIdx.x;
+    const int b = blockIdx.y / Hkv, hk = blockIdx.y % Hkv;
+    const int G = Hq / Hkv, R = Q * G;
+    const int p0 = pos[b];
+    const int lastmax = attn_last(p0, Q - 1, T);
+    const int cbase = chunk * kAttnChunk;
+    if (cbase > lastmax) return;                                  // uniform: nothing visible
+
+    const int lane = threadIdx.x & 63, c = lane & 15, kq = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wbase = cbase + w * kAttnSteps * kAttnStep;
+    const int ns = wbase > lastmax ? 0 : min(kAttnSteps, (lastmax - wbase) / kAttnStep + 1);
+    const uint16_t *kplane = cache + ((size_t)(b * 2 + 0) * Hkv + hk) * T * kAttnD;
+    const uint16_t *vplane = cache + ((size_t)(b * 2 + 1) * Hkv + hk) * T * kAttnD;
+
+    auto load = [&](int s, AttnStage<RT> &st) {
+        const int tb = wbase + s * kAttnStep;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const size_t row = (size_t)min(tb + 16 * tt + c, lastmax) * kAttnD;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st.k[tt][j] = *(const uint4 *)(kplane + row + 32 * j + 8 * kq);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = tb + (i < 4 ? 4 * kq + i : 16 + 4 * kq + i - 4);
+            st.v[i] = *(const uint4 *)(vplane + (size_t)min(t, lastmax) * kAttnD + 8 * c);
+        }
+    };
+
+    for (int rp = 0; rp < R; rp += ROWS) {
+        uint4 qb[RT][4];
+        int last[RT];
+        float m[RT], l[RT];
+        attn_f32x4_t o[RT][8];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int r = min(rp + rt * 16 + c, R - 1);
+            const int jq = r / G, g = r % G;
+            last[rt] = attn_last(p0, jq, T);
+            const uint16_t *qr = q + (((size_t)b * Q + jq) * Hq + hk * G + g) * kAttnD;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qb[rt][j] = *(const uint4 *)(qr + 32 * j + 8 * kq);
+            m[rt] = -INFINITY;
+            l[rt] = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) o[rt][mm] = attn_f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+
+        AttnStage<RT> cur, nxt;
+        if (ns > 0) load(0, cur);
+        for (int s = 0; s < ns; ++s) {
+            if (s + 1 < ns) load(s + 1, nxt);
+            const int tb = wbase + s * kAttnStep;
+            // values transposed: vt[mm] holds V[slot i][8 c + mm] for the 8 position slots
+            attn_bf16x8_t vt[8];
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) {
+                uint32_t d4[4];
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) {
+                    const uint32_t *lo = (const uint32_t *)&cur.v[2 * k2], *hi = (const uint32_t *)&cur.v[2 * k2 + 1];
+                    const uint32_t x = lo[mm >> 1], y = hi[mm >> 1];
+                    d4[k2] = (mm & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+                }
+                vt[mm] = attn_as_bf16x8(d4[0], d4[1], d4[2], d4[3]);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float sc[8];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    attn_f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(attn_bf16x8_t, cur.k[tt][j]),
+                                                                      __builtin_bit_cast(attn_bf16x8_t, qb[rt][j]), acc,
+                                                                      0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = tb + 16 * tt + 4 * kq + e;
+                        sc[tt * 4 + e] = t <= last[rt] ? acc[e] * scale : -INFINITY;
+                    }
+                }
+                float mk = sc[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) mk = fmaxf(mk, sc[i]);
+                mk = fmaxf(mk, __shfl_xor(mk, 16, kWave));
+                mk = fmaxf(mk, __shfl_xor(mk, 32, kWave));
+                const float mn = fmaxf(m[rt], mk);
+                float alpha = 1.f, p[8];
+                if (mn == -INFINITY) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) p[i] = 0.f;
+                } else {
+                    alpha = __expf(m[rt] - mn);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) p[i] = __expf(sc[i] - mn);
+                }
+                m[rt] = mn;
+                float ps = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ps += p[i];
+                l[rt] = __builtin_fmaf(l[rt], alpha, ps);
+                uint32_t ph[4], pl[4];
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) {
+                    ph[k2] = pack_bf16x2(p[2 * k2], p[2 * k2 + 1]);
+                    const float h0 = __uint_as_float(ph[k2] << 16), h1 = __uint_as_float(ph[k2] & 0xFFFF0000u);
+                    pl[k2] = pack_bf16x2(p[2 * k2] - h0, p[2 * k2 + 1] - h1);
+                }
+                const attn_bf16x8_t phi = attn_as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
+                const attn_bf16x8_t plo = attn_as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+#pragma unroll
+                for (int mm = 0; mm < 8; ++mm) {
+                    attn_f32x4_t acc = o[rt][mm] * alpha;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[mm], phi, acc, 0, 0, 0);
+                    o[rt][mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[mm], plo, acc, 0, 0, 0);
+                }
+            }
+            if (s + 1 < ns) cur = nxt;
+        }
+
+        // wave results into LDS: row r = rt * 16 + c on lanes c + 16 kq
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float lt = l[rt];
+            lt += __shfl_xor(lt, 16, kWave);
+            lt += __shfl_xor(lt, 32, kWave);
+            const int r = rt * 16 + c;
+            if (kq == 0) {
+                sm[w][r] = m[rt];
+                sl[w][r] = lt;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float *dst = &so[w][r][32 * kq + 8 * e];
+                *(float4 *)dst = float4{o[rt][0][e], o[rt][1][e], o[rt][2][e], o[rt][3][e]};
+                *(float4 *)(dst + 4) = float4{o[rt][4][e], o[rt][5][e], o[rt][6][e], o[rt][7][e]};
+            }
+        }
+        __syncthreads();
+        // merge the waves in wave order; one (row, 4 dimensions) item per thread and round
+        for (int it = threadIdx.x; it < ROWS * (kAttnD / 4); it += kAttnWaves * kWave) {
+            const int r = it / (kAttnD / 4), d = (it % (kAttnD / 4)) * 4;
+            const int rg = rp + r;
+            if (rg >= R) continue;
+            float M = sm[0][r];
+            for (int v = 1; v < kAttnWaves; ++v) M = fmaxf(M, sm[v][r]);
+            float L = 0.f;
+            float4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (M != -INFINITY) {
+                for (int v = 0; v < kAttnWaves; ++v) {
+                    const float wt = __expf(sm[v][r] - M);
+                    const float4 x = *(const float4 *)&so[v][r][d];
+                    L = __builtin_fmaf(sl[v][r], wt, L);
+                    acc.x = __builtin_fmaf(x.x, wt, acc.x);
+                    acc.y = __builtin_fmaf(x.y, wt, acc.y);
+                    acc.z = __builtin_fmaf(x.z, wt, acc.z);
+                    acc.w = __builtin_fmaf(x.w, wt, acc.w);
+                }
+            }
+            const int jq = rg / G, g = rg % G;
+            const size_t prow = (((size_t)b * Q + jq) * Hq + hk * G + g) * NC + chunk;
+            *(float4 *)(wo + prow * kAttnD + d) = acc;
+            if (d == 0) {
+                wm[prow] = M;
+                wl[prow] = L;
+            }
+        }
+        __syncthreads();                                          // LDS reused by the next pass
+    }
+}
+
+// One workgroup per query row (b, j, h), one thread per dimension: the chunks up to the row's
+// causal limit, merged in chunk order with weights exp(m_c - M).
+__global__ void __launch_bounds__(kAttnD)
+k_attn_combine(const int32_t *__restrict__ pos, int Q, int Hq, int T, int NC, const float *__restrict__ wm,
+               const float *__restrict__ wl, const float *__restrict__ wo, uint16_t *__restrict__ out) {
+    const int row = blockIdx.x;
+    const int j = (row / Hq) % Q, b = row / (Hq * Q);
+    const int d = threadIdx.x;
+    const int nc = attn_last(pos[b], j, T) / kAttnChunk + 1;
+    const size_t base = (size_t)row * NC;
+    float M = wm[base];
+    for (int c = 1; c < nc; ++c) M = fmaxf(M, wm[base + c]);
+    float L = 0.f, acc = 0.f;
+    for (int c = 0; c < nc; ++c) {
+        const float wt = __expf(wm[base + c] - M);
+        L = __builtin_fmaf(wl[base + c], wt, L);
+        acc = __builtin_fmaf(wo[(base + c) * kAttnD + d], wt, acc);
+    }
+    out[(size_t)row * kAttnD + d] = to_bf16_bits(acc / L);
+}
+
+hipError_t launch_attention(const uint16_t *q, const uint16_t *cache, const int32_t *pos, int B, int Q, int Hq,
+                            int Hkv, int T, float scale, uint16_t *out, void *ws, hipStream_t st) {
+    const AttnLayout L = attn_layout(B, Q, Hq, T);
+    char *w = (char *)ws;
+    float *wm = (float *)(w + L.m), *wl = (float *)(w + L.l), *wo = (float *)(w + L.o);
+    const dim3 grid(L.NC, B * Hkv);
+    if (Q * (Hq / Hkv) <= 16)
+        hipLaunchKernelGGL(k_attn_partial<1>, grid, dim3(kAttnWaves * kWave), 0, st, q, cache, pos, Q, Hq, Hkv, T,
+                           scale, L.NC, wm, wl, wo);
+    else
+        hipLaunchKernelGGL(k_attn_partial<2>, grid, dim3(kAttnWaves * kWave), 0, st, q, cache, pos, Q, Hq, Hkv, T,
+                           scale, L.NC, wm, wl, wo);
+    hipLaunchKernelGGL(k_attn_combine, dim3(B * Q * Hq), dim3(kAttnD), 0, st, pos, Q, Hq, T, L.NC, wm, wl, wo, out);
+    return hipGetLastError();
+}
+
+}  // namespace qspec

@@ -34,6 +34,11 @@ hipError_t launch_speckv_gamma(const float *logits, int R, int V, float quant_fe
                                const float *b1, const float *w2, const float *b2, int max_gamma,
                                double *features, int32_t *gamma_out, void *workspace, hipStream_t st);
 
+size_t attention_workspace_bytes(int B, int Q, int Hq, int T);
+
+hipError_t launch_attention(const uint16_t *q, const uint16_t *cache, const int32_t *pos, int B, int Q, int Hq,
+                            int Hkv, int T, float scale, uint16_t *out, void *workspace, hipStream_t st);
+
 hipError_t launch_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const int32_t *start_pos,
                                const int32_t *accept_count, int L, int B, int H, int T, int D,
                                int gamma, hipStream_t st);

@@ -155,3 +155,27 @@ QSPEC_EXPORT int qspec_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv,
     return status_of(qspec::launch_kv_overwrite(cache, verify_kv, start_pos, accept_count, L, B, H, T,
                                                 D, gamma, as_stream(stream)));
 }
+
+static bool attention_sizes_ok(int32_t B, int32_t Q, int32_t Hq, int32_t Hkv, int32_t T, int32_t D) {
+    if (B < 1 || Q < 1 || Hq < 1 || Hkv < 1 || T < 1 || D != QSPEC_ATTN_HEAD_DIM) return false;
+    if (Q > QSPEC_ATTN_MAX_QUERIES || Hq % Hkv != 0) return false;
+    if ((long long)B * Hkv > 65535 || (long long)B * Q * Hq >= (1LL << 31)) return false;
+    return (long long)B * 2 * Hkv * T * D <= kMaxElems && (long long)B * Q * Hq * T <= kMaxElems;
+}
+
+QSPEC_EXPORT size_t qspec_attention_workspace_bytes(int32_t B, int32_t Q, int32_t Hq, int32_t Hkv, int32_t T) {
+    if (!attention_sizes_ok(B, Q, Hq, Hkv, T, QSPEC_ATTN_HEAD_DIM)) return 0;
+    return qspec::attention_workspace_bytes(B, Q, Hq, T);
+}
+
+QSPEC_EXPORT int qspec_attention(const uint16_t *q, const uint16_t *cache, const int32_t *pos, int32_t B, int32_t Q,
+                                 int32_t Hq, int32_t Hkv, int32_t T, int32_t D, float scale, uint16_t *out,
+                                 void *workspace, size_t workspace_bytes, qspec_stream_t stream) {
+    if (!q || !cache || !pos || !out) return QSPEC_ERR_NULL;
+    if (!attention_sizes_ok(B, Q, Hq, Hkv, T, D)) return QSPEC_ERR_SHAPE;
+    if (!workspace || workspace_bytes < qspec::attention_workspace_bytes(B, Q, Hq, T)) return QSPEC_ERR_WORKSPACE;
+    if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(pos, 4) || !aligned(out, 2) || !aligned(workspace, 16))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_attention(q, cache, pos, B, Q, Hq, Hkv, T, scale, out, workspace,
+                                             as_stream(stream)));
+}

@@ -19,7 +19,9 @@ Distributions (one PCG64 stream per tensor, seeded by a fixed table):
     by 20, then rounded to bfloat16 (nearest-even, by torch's conversion);
   * target logits N(0, sigma=3); draft logits = target + N(0, 0.5);
   * uniforms in [0, 1) as float32;
-  * KV: a position-dependent canary pattern in the cache, N(0, 1) bfloat16 staging rows.
+  * KV: a position-dependent canary pattern in the cache, N(0, 1) bfloat16 staging rows;
+  * attention: queries N(0, 2^2) (scores of standard deviation 2 at scale 1/sqrt(D)), cached
+    keys and values N(0, 1), all bfloat16.
 """
 from __future__ import annotations
 
@@ -37,6 +39,7 @@ SEED_UNIFORM = 600
 SEED_START = 700
 SEED_KV = 800
 SEED_GUMBEL = 900
+SEED_ATTN = 1000
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -145,6 +148,14 @@ def start_positions(B: int, T: int, gamma: int, seed: int) -> np.ndarray:
     return rng(SEED_START + seed).integers(0, T - gamma - 1 + 1, size=B).astype(np.int32)
 
 
+def attention_inputs(B: int, Q: int, Hq: int, Hkv: int, T: int, D: int, seed: int, q_sigma: float = 2.0):
+    """(q u16 [B][Q][Hq][D], cache u16 [B][2][Hkv][T][D]) as bfloat16 bits."""
+    r = rng(SEED_ATTN + seed)
+    q = f32_to_bf16_bits((r.standard_normal((B, Q, Hq, D)) * q_sigma).astype(np.float32))
+    cache = f32_to_bf16_bits(r.standard_normal((B, 2, Hkv, T, D), dtype=np.float32))
+    return q, cache
+
+
 # ---- named workloads (shapes only; see DESIGN.md for the recipe) -------------
 
 LLAMA3_8B_PROJ = {"qkv": (4096, 6144), "o": (4096, 4096), "gate_up": (4096, 2 * 14336),
@@ -204,6 +215,17 @@ def draft_tokens_sampled_device(draft, seed: int):
     u = torch.rand(draft.shape, device=draft.device, generator=_gen(draft.device, SEED_GUMBEL, seed))
     gumbel = -torch.log(-torch.log(u.clamp_min(1e-20)))
     return torch.argmax(draft + gumbel, dim=-1).to(torch.int32)
+
+
+def attention_inputs_device(B: int, Q: int, Hq: int, Hkv: int, T: int, D: int, seed: int, device,
+                            q_sigma: float = 2.0):
+    """(q bf16 [B][Q][Hq][D], cache bf16 [B][2][Hkv][T][D]) drawn on the device."""
+    import torch
+
+    g = _gen(device, SEED_ATTN, seed)
+    q = (torch.randn((B, Q, Hq, D), device=device, generator=g) * q_sigma).to(torch.bfloat16)
+    cache = torch.randn((B, 2, Hkv, T, D), device=device, generator=g).to(torch.bfloat16)
+    return q, cache
 
 
 def uniforms_device(shape, seed: int, device):

@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "qspec_status_string", "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16",
         "qspec_gemm_w4a16_workspace_bytes", "qspec_verify_workspace_bytes", "qspec_verify_accept",
-        "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma"])
+        "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma",
+        "qspec_attention_workspace_bytes", "qspec_attention"])
 
 
 def test_library_exports_every_declared_symbol_and_nothing_else():
@@ -154,3 +155,28 @@ def test_speckv_validation():
     assert call(g=-1) == ERR_SHAPE and call(g=64) == ERR_SHAPE
     assert call(ws=None) == ERR_WS and call(nbytes=need - 1) == ERR_WS
     assert call(feat=ctypes.c_void_p(0x1004)) == ERR_ALIGN
+
+
+def test_attention_validation():
+    L = q.lib()
+    need = q.qspec_attention_workspace_bytes(16, 5, 32, 8, 4096)
+    # chunk partials of 512 positions: (max, sum, 128 outputs) fp32 per (query row, chunk)
+    assert need >= 16 * 5 * 32 * 8 * (2 + 128) * 4
+    assert q.qspec_attention_workspace_bytes(0, 1, 1, 1, 8) == 0
+    assert q.qspec_attention_workspace_bytes(1, 65, 1, 1, 8) == 0          # Q above the limit
+    assert q.qspec_attention_workspace_bytes(1, 1, 6, 4, 8) == 0           # Hq not a multiple of Hkv
+    assert q.qspec_attention_workspace_bytes(65536, 1, 1, 1, 8) == 0       # B * Hkv above 65535
+
+    def call(**kw):
+        a = dict(q=FAKE, cache=FAKE, pos=FAKE, B=16, Q=5, Hq=32, Hkv=8, T=4096, D=128, scale=0.088, out=FAKE,
+                 ws=FAKE, nbytes=need)
+        a.update(kw)
+        return L.qspec_attention(a["q"], a["cache"], a["pos"], a["B"], a["Q"], a["Hq"], a["Hkv"], a["T"], a["D"],
+                                 a["scale"], a["out"], a["ws"], a["nbytes"], None)
+    for k in ("q", "cache", "pos", "out"):
+        assert call(**{k: None}) == ERR_NULL, k
+    for kw in (dict(B=0), dict(Q=0), dict(Hq=0), dict(Hkv=0), dict(T=0), dict(D=64), dict(Q=65), dict(Hkv=6)):
+        assert call(**kw) == ERR_SHAPE, kw
+    assert call(ws=None) == ERR_WS and call(nbytes=need - 1) == ERR_WS
+    assert call(q=ctypes.c_void_p(0x1008)) == ERR_ALIGN and call(cache=ctypes.c_void_p(0x1002)) == ERR_ALIGN
+    assert call(ws=ctypes.c_void_p(0x1004)) == ERR_ALIGN
