@@ -347,6 +347,7 @@ def gpu_leg(args):
         b.copy_(a)
         torch.cuda.synchronize()
     R.speckv_us = speckv_controller_us(R, torch)
+    R.attention = attention_us(R, torch)
     return R, ph, wall, event_ms
 
 
@@ -372,6 +373,38 @@ def speckv_controller_us(R, torch):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / (5 * len(rows))
+
+
+def attention_us(R, torch):
+    """Outside the timed round: one layer's attention over a full 4096-position cache (B
+    sequences, 32 query heads, 8 KV heads, d 128) for a draft step (Q = 1) and a verify pass
+    (Q = gamma + 1), graph-replayed; returns {Q: microseconds per call}."""
+    import math
+
+    import synthetic_inputs as si
+
+    q, B, dev = R.q, R.B, R.accept.device
+    Hq = 32
+    res = {}
+    for Q in (1, R.gamma + 1):
+        qd, cache = si.attention_inputs_device(B, Q, Hq, KV_HEADS, CONTEXT, HEAD_DIM, 1, dev)
+        pos = torch.full((B,), CONTEXT - Q, dtype=torch.int32, device=dev)
+        out = torch.empty((B, Q, Hq, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((q.qspec_attention_workspace_bytes(B, Q, Hq, KV_HEADS, CONTEXT),), dtype=torch.uint8,
+                         device=dev)
+        graph = capture(lambda: [q.qspec_attention(qd, cache, pos, 1.0 / math.sqrt(HEAD_DIM), out, ws)
+                                 for _ in range(10)], torch)
+        graph.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(3):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res[Q] = a.elapsed_time(b) * 1e3 / 30
+        del qd, cache
+    return res
 
 
 def cpu_leg(args):
@@ -484,10 +517,16 @@ def main():
         "event_ms_per_round": round(event_ms, 4),
         "gemm_hbm_tbs": {"gemm_w4a4_M%d" % B: round(R.draft_gemm_bytes() * g / (draft_ms / 1e3) / 1e12, 3),
                          "gemm_w4a16_M%d" % (B * (g + 1)): round(R.verify_gemm_bytes() / (verify_ms / 1e3) / 1e12, 3)},
-        # verify tokens/s at this gamma as the verify GEMMs alone bound it: B (gamma + 1) tokens per
-        # pass over the layers' four projections (W4A16 at M = B (gamma + 1)), whole stack and per layer
         # outside the timed round: the adaptive-gamma controller on one draft row per sequence
         "speckv_controller_us": round(R.speckv_us, 1),
+        # outside the timed round: one layer's attention over the full cache; every key and value
+        # (B x 8 heads x 4096 positions x 2 x 256 bytes) is read once per call
+        "attention": {"workload": f"B{B}-Hq32-Hkv{KV_HEADS}-d{HEAD_DIM}-T{CONTEXT}-one-layer",
+                      **{f"us_Q{Qa}": round(u, 1) for Qa, u in R.attention.items()},
+                      **{f"hbm_frac_Q{Qa}": round(B * KV_HEADS * CONTEXT * 2 * HEAD_DIM * 2 / (u * 1e-6) / 1e9
+                                                  / HBM_PEAK_GBS, 4) for Qa, u in R.attention.items()}},
+        # verify tokens/s at this gamma as the verify GEMMs alone bound it: B (gamma + 1) tokens per
+        # pass over the layers' four projections (W4A16 at M = B (gamma + 1)), whole stack and per layer
         "verify_gemm_tokens_per_s": {"layers_%d" % args.layers: round(B * (g + 1) / (verify_ms / 1e3), 1),
                                      "per_layer": round(B * (g + 1) / (verify_ms / 1e3 / args.layers), 1)},
     }

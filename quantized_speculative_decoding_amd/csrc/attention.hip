@@ -18,8 +18,9 @@
 //
 // A wave streams 128 positions (4 steps of 32) through a 2-deep register ring; the 4 waves of a
 // workgroup cover a chunk of 512 positions and merge their (max, sum, outputs) through LDS in
-// wave order; k_attn_combine merges the chunks of each query row in chunk order.  Loads past the
-// last visible position of the group read that position instead (probability 0).
+// wave order; k_attn_combine merges the chunks of each query row in chunk order.  Keys and values
+// are buffer loads whose range ends after the group's last visible position, so later rows of
+// the cache are never read.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,6 +32,7 @@ constexpr int kAttnStep = 32;                    // positions per MFMA step
 constexpr int kAttnSteps = 4;                    // steps per wave
 constexpr int kAttnChunk = kAttnWaves * kAttnSteps * kAttnStep;   // 512 positions per workgroup
 constexpr int kAttnOPitch = kAttnD + 4;          // floats per LDS output row
+constexpr int kAttnQPitch = kAttnD + 8;          // bf16 per LDS query row
 
 typedef __attribute__((ext_vector_type(8))) __bf16 attn_bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float attn_f32x4_t;
@@ -66,19 +68,14 @@ __device__ __forceinline__ attn_bf16x8_t attn_as_bf16x8(uint32_t a, uint32_t b, 
 }
 
 template <int RT>
-struct AttnStage {
-    uint4 k[2][4];                               // [position tile][d step]
-    uint4 v[8];                                  // [position slot]
-};
-
-template <int RT>
-__global__ void __launch_bounds__(kAttnWaves * kWave)
+__global__ void __launch_bounds__(kAttnWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_attn_partial(const uint16_t *__restrict__ q, const uint16_t *__restrict__ cache, const int32_t *__restrict__ pos,
                int Q, int Hq, int Hkv, int T, float scale, int NC, float *__restrict__ wm, float *__restrict__ wl,
                float *__restrict__ wo) {
     constexpr int ROWS = 16 * RT;
     __shared__ float sm[kAttnWaves][ROWS], sl[kAttnWaves][ROWS];
     __shared__ __attribute__((aligned(16))) float so[kAttnWaves][ROWS][kAttnOPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t qs[ROWS][kAttnQPitch];
 
     const int chunk = blockIdx.x;
     const int b = blockIdx.y / Hkv, hk = blockIdx.y % Hkv;
@@ -92,115 +89,137 @@ k_attn_partial(const uint16_t *__restrict__ q, const uint16_t *__restrict__ cach
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wbase = cbase + w * kAttnSteps * kAttnStep;
     const int ns = wbase > lastmax ? 0 : min(kAttnSteps, (lastmax - wbase) / kAttnStep + 1);
-    const uint16_t *kplane = cache + ((size_t)(b * 2 + 0) * Hkv + hk) * T * kAttnD;
-    const uint16_t *vplane = cache + ((size_t)(b * 2 + 1) * Hkv + hk) * T * kAttnD;
+    // Wave-uniform buffer resources over the group's key and value planes, ending after the last
+    // visible position: rows past it read as zero (their probabilities are zero).
+    const size_t plane = (size_t)T * kAttnD;
+    const rsrc_t kr = make_rsrc(cache + ((size_t)(b * 2 + 0) * Hkv + hk) * plane, (uint32_t)(lastmax + 1) * 256u);
+    const rsrc_t vr = make_rsrc(cache + ((size_t)(b * 2 + 1) * Hkv + hk) * plane, (uint32_t)(lastmax + 1) * 256u);
+    const uint32_t kvo = (uint32_t)c * 256u + 16u * kq;          // key row c of a tile, d = 8 kq ..
+    const uint32_t vvo = (uint32_t)kq * 1024u + 16u * c;         // value rows 4 kq + i, d = 8 c ..
 
-    auto load = [&](int s, AttnStage<RT> &st) {
-        const int tb = wbase + s * kAttnStep;
+    // K of step s: [position tile tt][d step j]; V of step s: [position slot i]
+    auto load_k = [&](int s, uint4 (&kb)[2][4]) {
+        const uint32_t so = (uint32_t)(wbase + s * kAttnStep) * 256u;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const size_t row = (size_t)min(tb + 16 * tt + c, lastmax) * kAttnD;
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) st.k[tt][j] = *(const uint4 *)(kplane + row + 32 * j + 8 * kq);
-        }
+            for (int j = 0; j < 4; ++j) kb[tt][j] = buf_load16(kr, kvo + tt * 4096u + 64u * j, so);
+    };
+    auto load_v = [&](int s, uint4 (&vb)[8]) {
+        const uint32_t so = (uint32_t)(wbase + s * kAttnStep) * 256u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = tb + (i < 4 ? 4 * kq + i : 16 + 4 * kq + i - 4);
-            st.v[i] = *(const uint4 *)(vplane + (size_t)min(t, lastmax) * kAttnD + 8 * c);
-        }
+        for (int i = 0; i < 8; ++i) vb[i] = buf_load16(vr, vvo + (i < 4 ? i : 12 + i) * 256u, so);
     };
 
     for (int rp = 0; rp < R; rp += ROWS) {
-        uint4 qb[RT][4];
+        // the pass's query rows into LDS (rows past R repeat row R - 1; their results are dropped)
+        for (int e = threadIdx.x; e < ROWS * (kAttnD / 8); e += kAttnWaves * kWave) {
+            const int rr = e / (kAttnD / 8), d8 = (e % (kAttnD / 8)) * 8;
+            const int r = min(rp + rr, R - 1);
+            const int jq = r / G, g = r % G;
+            *(uint4 *)&qs[rr][d8] = *(const uint4 *)(q + (((size_t)b * Q + jq) * Hq + hk * G + g) * kAttnD + d8);
+        }
         int last[RT];
         float m[RT], l[RT];
         attn_f32x4_t o[RT][8];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const int r = min(rp + rt * 16 + c, R - 1);
-            const int jq = r / G, g = r % G;
-            last[rt] = attn_last(p0, jq, T);
-            const uint16_t *qr = q + (((size_t)b * Q + jq) * Hq + hk * G + g) * kAttnD;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) qb[rt][j] = *(const uint4 *)(qr + 32 * j + 8 * kq);
+            last[rt] = attn_last(p0, min(rp + rt * 16 + c, R - 1) / G, T);
             m[rt] = -INFINITY;
             l[rt] = 0.f;
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm) o[rt][mm] = attn_f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+        __syncthreads();
 
-        AttnStage<RT> cur, nxt;
-        if (ns > 0) load(0, cur);
-        for (int s = 0; s < ns; ++s) {
-            if (s + 1 < ns) load(s + 1, nxt);
-            const int tb = wbase + s * kAttnStep;
-            // values transposed: vt[mm] holds V[slot i][8 c + mm] for the 8 position slots
-            attn_bf16x8_t vt[8];
+        // K: two-deep ring, step s + 1 issued before step s's scores.  V: with one row tile, a
+        // two-deep ring (step s + 1 issued after step s's scores); with two, step s is issued
+        // before its own scores (registers for two row tiles of outputs leave no room for more).
+        constexpr bool VRING = RT == 1;
+        uint4 kb[2][2][4], vb[VRING ? 2 : 1][8];
+        if (ns > 0) {
+            load_k(0, kb[0]);
+            if (VRING) load_v(0, vb[0]);
+        }
 #pragma unroll
-            for (int mm = 0; mm < 8; ++mm) {
-                uint32_t d4[4];
+        for (int s = 0; s < kAttnSteps; ++s) {
+            if (s < ns) {
+                const int cb = s & 1;
+                if (s + 1 < ns) load_k(s + 1, kb[cb ^ 1]);
+                if (!VRING) load_v(s, vb[0]);
+                const int tb = wbase + s * kAttnStep;
+                attn_bf16x8_t phi[RT], plo[RT];
+                float alpha[RT];
 #pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) {
-                    const uint32_t *lo = (const uint32_t *)&cur.v[2 * k2], *hi = (const uint32_t *)&cur.v[2 * k2 + 1];
-                    const uint32_t x = lo[mm >> 1], y = hi[mm >> 1];
-                    d4[k2] = (mm & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-                }
-                vt[mm] = attn_as_bf16x8(d4[0], d4[1], d4[2], d4[3]);
-            }
+                for (int rt = 0; rt < RT; ++rt) {
+                    float sc[8];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                float sc[8];
+                    for (int tt = 0; tt < 2; ++tt) {
+                        attn_f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    attn_f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                        for (int j = 0; j < 4; ++j)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(attn_bf16x8_t, kb[cb][tt][j]),
+                                __builtin_bit_cast(attn_bf16x8_t, *(const uint4 *)&qs[rt * 16 + c][32 * j + 8 * kq]),
+                                acc, 0, 0, 0);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(attn_bf16x8_t, cur.k[tt][j]),
-                                                                      __builtin_bit_cast(attn_bf16x8_t, qb[rt][j]), acc,
-                                                                      0, 0, 0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = tb + 16 * tt + 4 * kq + e;
-                        sc[tt * 4 + e] = t <= last[rt] ? acc[e] * scale : -INFINITY;
+                        for (int e = 0; e < 4; ++e) {
+                            const int t = tb + 16 * tt + 4 * kq + e;
+                            sc[tt * 4 + e] = t <= last[rt] ? acc[e] * scale : -INFINITY;
+                        }
                     }
+                    float mk = sc[0];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) mk = fmaxf(mk, sc[i]);
+                    mk = fmaxf(mk, __shfl_xor(mk, 16, kWave));
+                    mk = fmaxf(mk, __shfl_xor(mk, 32, kWave));
+                    const float mn = fmaxf(m[rt], mk);
+                    float p[8];
+                    alpha[rt] = 1.f;
+                    if (mn == -INFINITY) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) p[i] = 0.f;
+                    } else {
+                        alpha[rt] = __expf(m[rt] - mn);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) p[i] = __expf(sc[i] - mn);
+                    }
+                    m[rt] = mn;
+                    float ps = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) ps += p[i];
+                    l[rt] = __builtin_fmaf(l[rt], alpha[rt], ps);
+                    uint32_t ph[4], pl[4];
+#pragma unroll
+                    for (int k2 = 0; k2 < 4; ++k2) {
+                        ph[k2] = pack_bf16x2(p[2 * k2], p[2 * k2 + 1]);
+                        const float h0 = __uint_as_float(ph[k2] << 16), h1 = __uint_as_float(ph[k2] & 0xFFFF0000u);
+                        pl[k2] = pack_bf16x2(p[2 * k2] - h0, p[2 * k2 + 1] - h1);
+                    }
+                    phi[rt] = attn_as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
+                    plo[rt] = attn_as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
                 }
-                float mk = sc[0];
-#pragma unroll
-                for (int i = 1; i < 8; ++i) mk = fmaxf(mk, sc[i]);
-                mk = fmaxf(mk, __shfl_xor(mk, 16, kWave));
-                mk = fmaxf(mk, __shfl_xor(mk, 32, kWave));
-                const float mn = fmaxf(m[rt], mk);
-                float alpha = 1.f, p[8];
-                if (mn == -INFINITY) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) p[i] = 0.f;
-                } else {
-                    alpha = __expf(m[rt] - mn);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) p[i] = __expf(sc[i] - mn);
-                }
-                m[rt] = mn;
-                float ps = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) ps += p[i];
-                l[rt] = __builtin_fmaf(l[rt], alpha, ps);
-                uint32_t ph[4], pl[4];
-#pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) {
-                    ph[k2] = pack_bf16x2(p[2 * k2], p[2 * k2 + 1]);
-                    const float h0 = __uint_as_float(ph[k2] << 16), h1 = __uint_as_float(ph[k2] & 0xFFFF0000u);
-                    pl[k2] = pack_bf16x2(p[2 * k2] - h0, p[2 * k2 + 1] - h1);
-                }
-                const attn_bf16x8_t phi = attn_as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
-                const attn_bf16x8_t plo = attn_as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+                if (VRING && s + 1 < ns) load_v(s + 1, vb[(cb ^ 1) % (VRING ? 2 : 1)]);
+                const int vc = VRING ? cb : 0;
 #pragma unroll
                 for (int mm = 0; mm < 8; ++mm) {
-                    attn_f32x4_t acc = o[rt][mm] * alpha;
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[mm], phi, acc, 0, 0, 0);
-                    o[rt][mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[mm], plo, acc, 0, 0, 0);
+                    // V[slot i][8 c + mm] for the 8 position slots, transposed in registers
+                    uint32_t d4[4];
+#pragma unroll
+                    for (int k2 = 0; k2 < 4; ++k2) {
+                        const uint32_t x = ((const uint32_t *)&vb[vc][2 * k2])[mm >> 1];
+                        const uint32_t y = ((const uint32_t *)&vb[vc][2 * k2 + 1])[mm >> 1];
+                        d4[k2] = (mm & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+                    }
+                    const attn_bf16x8_t vt = attn_as_bf16x8(d4[0], d4[1], d4[2], d4[3]);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        attn_f32x4_t acc = o[rt][mm] * alpha[rt];
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[rt], acc, 0, 0, 0);
+                        o[rt][mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo[rt], acc, 0, 0, 0);
+                    }
                 }
             }
-            if (s + 1 < ns) cur = nxt;
         }
 
         // wave results into LDS: row r = rt * 16 + c on lanes c + 16 kq
@@ -255,7 +274,10 @@ k_attn_partial(const uint16_t *__restrict__ q, const uint16_t *__restrict__ cach
 }
 
 // One workgroup per query row (b, j, h), one thread per dimension: the chunks up to the row's
-// causal limit, merged in chunk order with weights exp(m_c - M).
+// causal limit, merged in chunk order with weights exp(m_c - M).  Chunks are taken 8 at a time
+// with all their loads issued together; a later block with a larger maximum rescales the sums.
+constexpr int kAttnMergeBlock = 8;
+
 __global__ void __launch_bounds__(kAttnD)
 k_attn_combine(const int32_t *__restrict__ pos, int Q, int Hq, int T, int NC, const float *__restrict__ wm,
                const float *__restrict__ wl, const float *__restrict__ wo, uint16_t *__restrict__ out) {
@@ -264,13 +286,31 @@ k_attn_combine(const int32_t *__restrict__ pos, int Q, int Hq, int T, int NC, co
     const int d = threadIdx.x;
     const int nc = attn_last(pos[b], j, T) / kAttnChunk + 1;
     const size_t base = (size_t)row * NC;
-    float M = wm[base];
-    for (int c = 1; c < nc; ++c) M = fmaxf(M, wm[base + c]);
-    float L = 0.f, acc = 0.f;
-    for (int c = 0; c < nc; ++c) {
-        const float wt = __expf(wm[base + c] - M);
-        L = __builtin_fmaf(wl[base + c], wt, L);
-        acc = __builtin_fmaf(wo[(base + c) * kAttnD + d], wt, acc);
+    float M = -INFINITY, L = 0.f, acc = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += kAttnMergeBlock) {
+        float mv[kAttnMergeBlock], lv[kAttnMergeBlock], ov[kAttnMergeBlock];
+#pragma unroll
+        for (int i = 0; i < kAttnMergeBlock; ++i) {
+            const int c = min(c0 + i, nc - 1);
+            mv[i] = wm[base + c];
+            lv[i] = wl[base + c];
+            ov[i] = wo[(base + c) * kAttnD + d];
+        }
+        float Mb = M;
+#pragma unroll
+        for (int i = 0; i < kAttnMergeBlock; ++i)
+            if (c0 + i < nc) Mb = fmaxf(Mb, mv[i]);
+        const float r = __expf(M - Mb);                           // 0 on the first block
+        L *= r;
+        acc *= r;
+#pragma unroll
+        for (int i = 0; i < kAttnMergeBlock; ++i)
+            if (c0 + i < nc) {
+                const float wt = __expf(mv[i] - Mb);
+                L = __builtin_fmaf(lv[i], wt, L);
+                acc = __builtin_fmaf(ov[i], wt, acc);
+            }
+        M = Mb;
     }
     out[(size_t)row * kAttnD + d] = to_bf16_bits(acc / L);
 }

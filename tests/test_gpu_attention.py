@@ -39,9 +39,11 @@ def check(qb, cache, pos, scale, what, seqs=None):
 
 
 # (B, Q, Hq, Hkv, T): contexts shorter than one 32-position step, ragged chunk tails, one and two
-# 16-row tiles per pass and several passes (Q * Hq / Hkv = 4, 20, 32, 40, 64, 68), G = 1 and 8
+# 16-row tiles per pass and several passes (Q * Hq / Hkv = 4, 20, 32, 40, 64, 68), G = 1 and 8,
+# and contexts of more than 8 chunks of 512 (the merge takes chunks 8 at a time)
 CASES = [(2, 1, 4, 1, 7, ), (3, 1, 32, 8, 70), (2, 5, 32, 8, 600), (2, 4, 8, 1, 1100), (1, 8, 32, 8, 513),
-         (2, 5, 64, 8, 300), (1, 16, 32, 8, 200), (2, 17, 8, 2, 260), (2, 2, 8, 8, 1500)]
+         (2, 5, 64, 8, 300), (1, 16, 32, 8, 200), (2, 17, 8, 2, 260), (2, 2, 8, 8, 1500), (2, 3, 8, 2, 5000),
+         (1, 1, 32, 8, 32768)]
 
 
 @pytest.mark.parametrize("B,Q,Hq,Hkv,T", CASES)
