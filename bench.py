@@ -104,6 +104,13 @@ def summarize(args):
               "| kernel | calls | avg us |", "|---|---:|---:|"]
     for k, (c, t) in sorted(fam.items(), key=lambda kv: -kv[1][1]):
         lines.append(f"| `{k}` | {c} | {t / c / 1e3:.2f} |")
+    lines += ["", "Attention over one layer of the cache, outside the timed round (B=16, 32 query heads, 8 KV "
+              "heads, d 128, T=4096; k_attn_partial<1> serves the draft step Q=1, <2> the verify pass Q=5):", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for r in stats:
+        if "k_attn" in r["Name"]:
+            lines.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     open(os.path.join(PROFILES, "kernel_trace_llama3_8b_round_B16_g4.md"), "w").write("\n".join(lines) + "\n")
 
     def per_dispatch(d):
