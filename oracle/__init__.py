@@ -65,6 +65,13 @@ def _lib():
         lib.orc_kv_overwrite.argtypes = [P, P, P, P, I, I, I, I, I, I]
         lib.orc_speckv_gamma.argtypes = [P, I, I, ctypes.c_float, P, P, P, P, I, P, P, P]
         lib.orc_attention.argtypes = [P, P, P, I, I, I, I, I, I, ctypes.c_float, P]
+        lib.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        lib.orc_e4m3_to_double.restype = ctypes.c_double
+        lib.orc_double_to_e4m3.argtypes = [ctypes.c_double]
+        lib.orc_double_to_e4m3.restype = ctypes.c_uint8
+        lib.orc_quantize_act_fp8.argtypes = [P, I, I, P, P]
+        lib.orc_quantize_weights_fp8.argtypes = [P, I, I, P, P]
+        lib.orc_gemm_w8a8.argtypes = [P, P, I, P, P, I, I, P]
         for name in ("orc_dequant", "orc_gemm_w4a16", "orc_quantize_act", "orc_gemm_w4a4",
                      "orc_verify_greedy", "orc_verify_sample", "orc_kv_overwrite", "orc_speckv_gamma",
                      "orc_attention"):
@@ -215,6 +222,50 @@ def attention(q, cache, pos, scale):
     out = np.empty_like(q)
     _lib().orc_attention(_p(q), _p(cache), _p(pos), B, Q, Hq, Hkv, T, D, float(scale), _p(out))
     return out
+
+
+def e4m3_to_double(code: int) -> float:
+    return _lib().orc_e4m3_to_double(int(code))
+
+
+def double_to_e4m3(v: float) -> int:
+    return int(_lib().orc_double_to_e4m3(float(v)))
+
+
+def quantize_act_fp8(x):
+    """Per-token FP8 (E4M3) activation codes: x u16 bf16 [M][K] -> (codes u8 [M][K], scales f32 [M])."""
+    x = _c(x, np.uint16)
+    M, K = x.shape
+    codes = np.empty((M, K), np.uint8)
+    scales = np.empty(M, np.float32)
+    _lib().orc_quantize_act_fp8(_p(x), M, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def quantize_weights_fp8(w):
+    """Per-column FP8 post-training quantization: w u16 bf16 [K][N] -> (codes u8 [N][K], scales f32 [N])."""
+    w = _c(w, np.uint16)
+    K, N = w.shape
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty(N, np.float32)
+    _lib().orc_quantize_weights_fp8(_p(w), K, N, _p(codes), _p(scales))
+    return codes, scales
+
+
+def gemm_w8a8(a_codes, a_scales, w_store, w_scales):
+    """y f64 [M][N] = s_a s_w sum_k dec(a) dec(w); a_codes u8 [M][K], a_scales f32 [M], w_store u8
+    [N/16][K/128][2048], w_scales f32 [N]."""
+    a_codes = _c(a_codes, np.uint8)
+    M, K = a_codes.shape
+    a_scales = _c(a_scales, np.float32).reshape(M)
+    w_store = _c(w_store, np.uint8)
+    T, G, blk = w_store.shape
+    assert blk == 2048 and G * 128 == K
+    N = 16 * T
+    w_scales = _c(w_scales, np.float32).reshape(N)
+    y = np.empty((M, N), np.float64)
+    _lib().orc_gemm_w8a8(_p(a_codes), _p(a_scales), M, _p(w_store), _p(w_scales), K, N, _p(y))
+    return y
 
 
 def kv_overwrite(cache, verify_kv, start_pos, accept):

@@ -14,6 +14,9 @@
  * Sources (page titles as published):
  *   [QSPEC notes]  "QSPEC 논문 요점 정리" -- study notes on "QSPEC: Speculative
  *                  Decoding with Complementary Quantization Schemes" (Zhao et al.)
+ *   [SpecQuant notes] "SpecQuant: Speculative Decoding with Multi-Parent Quantization
+ *                  for Adaptive LLM Inference" -- a summary page (sections: one-line
+ *                  summary, key contributions, approach, limitations)
  *   Sections of that page are named by content: background terms (weight-only
  *   vs weight-activation quantization, the dequantization example),
  *   speculative-decoding background (acceptance rule, first-reject cutoff,
@@ -525,4 +528,108 @@ void orc_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const int32_t 
                         for (int64_t e = 0; e < D; ++e) dst[e] = src[e];
                     }
         }
+}
+
+/* ---- O10: the FP8 parent variant ---------------------------------------------
+ * [SpecQuant notes, one-line summary, key contributions and approach: INT4, FP8
+ * and FP16 variants of one FP16 model are made by post-training quantization
+ * with shared base weights; a low-precision draft proposes and a parent variant
+ * verifies.  Limitations: the quantization recipe itself is not given.]
+ * Reading used here (the page fixes none of it):
+ *   - FP8 is OCP E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits, no
+ *     infinities, 0x7F / 0xFF are NaN, largest finite value 448;
+ *   - weights: one scale per output column, s_w = max_k |W[k][n]| / 448;
+ *   - activations: one scale per token (row), s_a = max_k |x[m][k]| / 448, taken
+ *     at run time (no calibration data is described);
+ *   - codes: the nearest finite E4M3 value to (value / scale), ties to the even
+ *     code, saturating at +-448; the quotient is one binary32 division;
+ *   - y[m][n] = s_a[m] s_w[n] sum_k dec(a[m][k]) dec(w[k][n]).
+ * Weight store u8 [N/16][K/128][2][64][16]: block (t, g) holds columns 16t..16t+15
+ * and k = 128g..128g+127; byte (h, l, b) with l = c + 16 q is column 16t + c at
+ * k = 128g + 32q + 16h + b.  Activation codes u8 [M][K] row-major.
+ */
+double orc_e4m3_to_double(uint8_t c)
+{
+    int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    /* subnormal: m/8 * 2^-6; normal: (1 + m/8) * 2^(e-7) */
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return (c & 0x80) ? -v : v;
+}
+
+uint8_t orc_double_to_e4m3(double v)
+{
+    double a = fabs(v);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {        /* finite non-negative codes, increasing values */
+        double d = fabs(orc_e4m3_to_double((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best_d = d;
+            best = c;
+        }
+    }
+    return (uint8_t)((signbit(v) ? 0x80 : 0x00) | best);
+}
+
+void orc_quantize_act_fp8(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, float *scales)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * K;
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf(bf16_to_float(xr[k]));
+            if (v > a) a = v;
+        }
+        float s = a / 448.0f;
+        scales[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            float r = (a != 0.0f) ? bf16_to_float(xr[k]) / s : 0.0f;
+            codes[m * K + k] = (a != 0.0f) ? orc_double_to_e4m3((double)r) : 0;
+        }
+    }
+}
+
+/* Post-training quantization of a bfloat16 weight matrix w [K][N] into codes [N][K]
+ * (column n's codes contiguous) and per-column scales [N]. */
+void orc_quantize_weights_fp8(const uint16_t *w, int64_t K, int64_t N, uint8_t *codes_nk, float *scales)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf(bf16_to_float(w[k * N + n]));
+            if (v > a) a = v;
+        }
+        float s = a / 448.0f;
+        scales[n] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            float r = (a != 0.0f) ? bf16_to_float(w[k * N + n]) / s : 0.0f;
+            codes_nk[n * K + k] = (a != 0.0f) ? orc_double_to_e4m3((double)r) : 0;
+        }
+    }
+}
+
+static uint8_t fp8_weight_code(const uint8_t *store, int64_t K, int64_t n, int64_t k)
+{
+    int64_t G = K / ORC_GROUP;
+    int64_t kk = k % ORC_GROUP;
+    int64_t block = (n / 16) * G + k / ORC_GROUP;
+    int64_t lane = (n % 16) + 16 * (kk / 32);
+    return store[block * 2048 + ((kk % 32) / 16) * 1024 + lane * 16 + kk % 16];
+}
+
+/* y f64 [M][N]: the exact products summed in double, then both scales. */
+void orc_gemm_w8a8(const uint8_t *a_codes, const float *a_scales, int64_t M, const uint8_t *w_store,
+                   const float *w_scales, int64_t K, int64_t N, double *y)
+{
+    double *col = (double *)malloc(sizeof(double) * (size_t)K);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) col[k] = orc_e4m3_to_double(fp8_weight_code(w_store, K, n, k));
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += orc_e4m3_to_double(a_codes[m * K + k]) * col[k];
+            y[m * N + n] = (double)a_scales[m] * (double)w_scales[n] * acc;
+        }
+    }
+    free(col);
 }

@@ -20,6 +20,8 @@ Distributions (one PCG64 stream per tensor, seeded by a fixed table):
   * target logits N(0, sigma=3); draft logits = target + N(0, 0.5);
   * uniforms in [0, 1) as float32;
   * KV: a position-dependent canary pattern in the cache, N(0, 1) bfloat16 staging rows;
+  * FP8 stores: E4M3 codes drawn uniformly from the 254 finite codes, column scales uniform
+    [1e-4, 1e-3] (benchmark); the tests also quantize N(0, 0.02^2) bfloat16 weights with the oracle;
   * attention: queries N(0, 2^2) (scores of standard deviation 2 at scale 1/sqrt(D)), cached
     keys and values N(0, 1), all bfloat16.
 """
@@ -40,6 +42,7 @@ SEED_START = 700
 SEED_KV = 800
 SEED_GUMBEL = 900
 SEED_ATTN = 1000
+SEED_FP8 = 1100
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -76,6 +79,31 @@ def unpack_weights(codes, meta):
     rm = np.ascontiguousarray(codes.reshape(T, G, 4, 16, 16).transpose(0, 3, 1, 2, 4)).reshape(16 * T, G * 64)
     m = np.ascontiguousarray(meta.transpose(0, 2, 1)).reshape(16 * T, G)
     return rm, (m & np.uint32(0xFFFF)).astype(np.uint16), ((m >> np.uint32(16)) & np.uint32(0xFF)).astype(np.uint8)
+
+
+def pack_fp8_weights(codes_nk):
+    """FP8 codes u8 [N][K] (column n's codes contiguous) -> the tile-major FP8 store u8
+    [N/16][K/128][2048]: byte (h, l, b), l = c + 16 q, is column 16t + c at k = 128g + 32q + 16h + b.
+    Pure layout."""
+    codes_nk = np.ascontiguousarray(codes_nk, np.uint8)
+    N, K = codes_nk.shape
+    assert N % 16 == 0 and K % GROUP == 0
+    G = K // GROUP
+    # [t][c][g][q][h][b] -> [t][g][h][q][c][b]
+    blocks = codes_nk.reshape(N // 16, 16, G, 4, 2, 16).transpose(0, 2, 4, 3, 1, 5)
+    return np.ascontiguousarray(blocks).reshape(N // 16, G, 2048)
+
+
+def unpack_fp8_weights(store):
+    """Inverse of pack_fp8_weights: codes u8 [N][K]."""
+    T, G, _ = store.shape
+    return np.ascontiguousarray(store.reshape(T, G, 2, 4, 16, 16).transpose(0, 4, 1, 3, 2, 5)).reshape(16 * T, G * GROUP)
+
+
+def fp8_codes(shape, seed: int) -> np.ndarray:
+    """Uniformly drawn finite E4M3 codes (every byte except 0x7F and 0xFF)."""
+    c = rng(SEED_FP8 + seed).integers(0, 254, size=shape).astype(np.uint8)
+    return c + (c >= 0x7F).astype(np.uint8)
 
 
 def slice_tiles(w: dict, tiles) -> dict:
@@ -226,6 +254,18 @@ def attention_inputs_device(B: int, Q: int, Hq: int, Hkv: int, T: int, D: int, s
     q = (torch.randn((B, Q, Hq, D), device=device, generator=g) * q_sigma).to(torch.bfloat16)
     cache = torch.randn((B, 2, Hkv, T, D), device=device, generator=g).to(torch.bfloat16)
     return q, cache
+
+
+def fp8_weights_device(K: int, N: int, seed: int, device):
+    """(FP8 store u8 [N/16][K/128][2048] of uniformly drawn finite E4M3 codes, column scales f32 [N]
+    uniform [1e-4, 1e-3]) drawn on the device."""
+    import torch
+
+    g = _gen(device, SEED_FP8, seed)
+    c = torch.randint(0, 254, (N // 16, K // GROUP, 2048), dtype=torch.uint8, device=device, generator=g)
+    c = c + (c >= 0x7F).to(torch.uint8)
+    s = torch.rand((N,), device=device, generator=g) * 9e-4 + 1e-4
+    return c, s
 
 
 def uniforms_device(shape, seed: int, device):
