@@ -298,6 +298,63 @@ int qspec_attention(const uint16_t *q, const uint16_t *cache, const int32_t *pos
                     int32_t Hq, int32_t Hkv, int32_t T, int32_t D, float scale, uint16_t *out,
                     void *workspace, size_t workspace_bytes, qspec_stream_t stream);
 
+/*
+ * The FP8 parent variant.
+ * [SpecQuant notes, one-line summary, key contributions and approach: INT4, FP8 and FP16
+ * variants of one model are made by post-training quantization with shared base weights; a
+ * low-precision draft proposes and a parent variant verifies.  The recipe is not given.]
+ * FP8 here is OCP E4M3 (1 sign, 4 exponent bits with bias 7, 3 fraction bits, no infinities,
+ * 0x7F / 0xFF NaN, largest finite 448).  Codes are the nearest finite E4M3 value to the scaled
+ * input (ties to the even code, saturating at +-448; the sign bit is the input's).
+ *   FP8 weight store  u8 [N/16][K/128][2048]: block (t, g) holds columns 16t..16t+15 and
+ *                     k = 128g..128g+127; byte h * 1024 + l * 16 + b, with lane l = c + 16 q, is
+ *                     column 16t + c at k = 128g + 32q + 16h + b.  A wave reading a block half
+ *                     with lane l taking 16 bytes at 16 l reads one contiguous kilobyte.
+ *   weight scales     f32 [N], one per output column (absmax over K / 448 for a post-training
+ *                     quantized FP16 weight; any positive values are accepted)
+ *   FP8 act. codes    u8 [M][K] row-major;  act. scales f32 [M]
+ * K must be a positive multiple of 128, N of 16; M * K and K * N must stay below 2^32.
+ */
+
+/*
+ * qspec_quantize_act_fp8 -- per-token FP8 activation codes.
+ * a = max_k |x[m][k]|, scales[m] = a / 448 (one binary32 division), codes[m][k] =
+ * E4M3(x[m][k] / scales[m]) with the quotient a binary32 division; a row with a == 0 gets
+ * scale 0 and all codes 0.
+ * x [in] u16 [M][K] bfloat16 (finite values); codes [out] u8 [M][K]; scales [out] f32 [M]
+ * Alignment: x and codes 16 bytes.
+ * Errors: NULL pointer; M < 1; K < 128 or K % 128 != 0.
+ */
+int qspec_quantize_act_fp8(const uint16_t *x, int32_t M, int32_t K, uint8_t *codes, float *scales,
+                           qspec_stream_t stream);
+
+/*
+ * qspec_gemm_w8a8_workspace_bytes -- device workspace qspec_gemm_w8a8 needs for (M, K, N); 0 when
+ * K is not split or on invalid sizes.  The split count depends on (K, N) only; the size is
+ * S * M * N * 4 bytes.
+ */
+size_t qspec_gemm_w8a8_workspace_bytes(int32_t M, int32_t K, int32_t N);
+
+/*
+ * qspec_gemm_w8a8 -- the FP8 parent's linear layer.
+ * y[m][n] = a_scales[m] * w_scales[n] * sum_k E4M3(a_codes[m][k]) * E4M3(w[k][n]): every product
+ * is exact, the sum is fp32 (FP8 MFMA), the scales are applied to the fp32 sum of each K split
+ * and the splits are added in split order.
+ * a_codes, a_scales [in] from qspec_quantize_act_fp8
+ * w_store, w_scales [in] the FP8 weight store and its column scales
+ * y   [out] [M][N], bfloat16 (nearest-even) or f32 per y_dtype
+ * workspace [in/out] at least qspec_gemm_w8a8_workspace_bytes(M, K, N) bytes, 256-byte aligned
+ *           (NULL allowed when that is 0); contents need no initialization; calls sharing a
+ *           workspace must be ordered on one stream.
+ * Batch invariance: the reduction order of an output depends only on (K, N), so row m of y is
+ * bit-identical for every M.
+ * Errors: NULL pointer; M < 1; N < 16 or N % 16 != 0; K < 128 or K % 128 != 0; M * K or K * N
+ * of 2^32 or more; bad y_dtype; workspace missing or too small.
+ */
+int qspec_gemm_w8a8(const uint8_t *a_codes, const float *a_scales, int32_t M, const uint8_t *w_store,
+                    const float *w_scales, int32_t K, int32_t N, void *y, int32_t y_dtype, void *workspace,
+                    size_t workspace_bytes, qspec_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

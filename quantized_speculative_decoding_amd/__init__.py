@@ -67,8 +67,13 @@ def lib() -> ctypes.CDLL:
         L.qspec_attention_workspace_bytes.argtypes = [I, I, I, I, I]
         L.qspec_attention_workspace_bytes.restype = S
         L.qspec_attention.argtypes = [P, P, P, I, I, I, I, I, I, ctypes.c_float, P, P, S, P]
-        for fn in ("qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16",
-                   "qspec_verify_accept", "qspec_kv_overwrite", "qspec_speckv_gamma", "qspec_attention"):
+        L.qspec_quantize_act_fp8.argtypes = [P, I, I, P, P, P]
+        L.qspec_gemm_w8a8_workspace_bytes.argtypes = [I, I, I]
+        L.qspec_gemm_w8a8_workspace_bytes.restype = S
+        L.qspec_gemm_w8a8.argtypes = [P, P, I, P, P, I, I, P, I, P, S, P]
+        for fn in ("qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_verify_accept",
+                   "qspec_kv_overwrite", "qspec_speckv_gamma", "qspec_attention", "qspec_quantize_act_fp8",
+                   "qspec_gemm_w8a8"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -272,10 +277,47 @@ def qspec_attention(q, cache, pos, scale, out, workspace, stream=None) -> None:
                                  _ptr(workspace), workspace.numel(), _stream(stream, q)))
 
 
+def qspec_quantize_act_fp8(x, codes, scales, stream=None) -> None:
+    """x bf16 [M][K] -> per-token FP8 (E4M3) codes u8 [M][K] and scales f32 [M]."""
+    _req(x, "x", torch.bfloat16)
+    M, K = x.shape
+    _req(codes, "codes", torch.uint8, (M, K))
+    _req(scales, "scales", torch.float32, (M,))
+    _check("qspec_quantize_act_fp8",
+           lib().qspec_quantize_act_fp8(_ptr(x), M, K, _ptr(codes), _ptr(scales), _stream(stream, x)))
+
+
+def qspec_gemm_w8a8_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(lib().qspec_gemm_w8a8_workspace_bytes(M, K, N))
+
+
+def qspec_gemm_w8a8(a_codes, a_scales, w_store, w_scales, y, workspace=None, stream=None) -> None:
+    """FP8 parent layer: y [M][N] (bf16 or f32) = s_a s_w sum E4M3(a) E4M3(w).  w_store u8
+    [N/16][K/128][2048], w_scales f32 [N]; workspace u8 of qspec_gemm_w8a8_workspace_bytes bytes."""
+    _req(w_store, "w_store", torch.uint8)
+    if w_store.dim() != 3 or w_store.shape[2] != 2048:
+        raise ValueError("w_store must be [N/16][K/128][2048]")
+    K, N = w_store.shape[1] * GROUP, w_store.shape[0] * 16
+    _req(w_scales, "w_scales", torch.float32, (N,))
+    _req(a_codes, "a_codes", torch.uint8)
+    M = a_codes.shape[0]
+    _req(a_codes, "a_codes", torch.uint8, (M, K))
+    _req(a_scales, "a_scales", torch.float32, (M,))
+    dt = _out_dtype(y)
+    _req(y, "y", y.dtype, (M, N))
+    if workspace is not None:
+        _req(workspace, "workspace", torch.uint8)
+    _check("qspec_gemm_w8a8",
+           lib().qspec_gemm_w8a8(_ptr(a_codes), _ptr(a_scales), M, _ptr(w_store), _ptr(w_scales), K, N, _ptr(y), dt,
+                                 _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                 _stream(stream, y)))
+
+
 __all__ = [
     "GROUP", "QSPEC_GREEDY", "QSPEC_SAMPLE", "QSPEC_OUT_BF16", "QSPEC_OUT_F32", "QspecError", "lib",
     "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_gemm_w4a16_workspace_bytes",
     "gemm_w4a16_workspace", "qspec_verify_workspace_bytes",
     "qspec_verify_accept", "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma",
-    "qspec_attention_workspace_bytes", "qspec_attention",
+    "qspec_attention_workspace_bytes", "qspec_attention", "qspec_quantize_act_fp8",
+    "qspec_gemm_w8a8_workspace_bytes", "qspec_gemm_w8a8",
 ]

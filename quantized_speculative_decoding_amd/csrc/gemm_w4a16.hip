@@ -623,7 +623,7 @@ size_t gemm_w4a16_workspace_bytes(int M, int K, int N) {
     return S == 1 ? 0 : (size_t)S * M * N * sizeof(float);
 }
 
-static void launch_splitk_reduce(const float *partials, int S, int M, int N, void *y, int y_f32, hipStream_t st) {
+void launch_splitk_reduce(const float *partials, int S, int M, int N, void *y, int y_f32, hipStream_t st) {
     const size_t MN = (size_t)M * N;
     const unsigned blocks = (unsigned)((MN / 4 + 255) / 256);
     hipLaunchKernelGGL(k_w4a16_splitk_reduce, dim3(blocks), dim3(256), 0, st, partials, S, MN, y, y_f32);

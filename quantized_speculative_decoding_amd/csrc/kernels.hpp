@@ -34,6 +34,17 @@ hipError_t launch_speckv_gamma(const float *logits, int R, int V, float quant_fe
                                const float *b1, const float *w2, const float *b2, int max_gamma,
                                double *features, int32_t *gamma_out, void *workspace, hipStream_t st);
 
+// y (bf16 or fp32) = the sum of S <= 16 fp32 partials [S][M][N], added in split order.
+void launch_splitk_reduce(const float *partials, int S, int M, int N, void *y, int y_f32, hipStream_t st);
+
+hipError_t launch_quantize_act_fp8(const uint16_t *x, int M, int K, uint8_t *codes, float *scales, hipStream_t st);
+
+size_t gemm_w8a8_workspace_bytes(int M, int K, int N);
+
+hipError_t launch_gemm_w8a8(const uint8_t *a_codes, const float *a_scales, int M, const uint8_t *w_store,
+                            const float *w_scales, int K, int N, void *y, int y_f32, void *workspace,
+                            hipStream_t st);
+
 size_t attention_workspace_bytes(int B, int Q, int Hq, int T);
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *cache, const int32_t *pos, int B, int Q, int Hq,

@@ -179,3 +179,38 @@ QSPEC_EXPORT int qspec_attention(const uint16_t *q, const uint16_t *cache, const
     return status_of(qspec::launch_attention(q, cache, pos, B, Q, Hq, Hkv, T, scale, out, workspace,
                                              as_stream(stream)));
 }
+
+// The W8A8 kernels address a_codes (M * K bytes) and the FP8 store (K * N bytes) through 32-bit
+// buffer offsets.
+static bool w8a8_sizes_ok(int32_t M, int32_t K, int32_t N) {
+    if (M < 1 || bad_n(N) || bad_k(K) || (long long)M * N > kMaxElems) return false;
+    return (long long)M * K < (1LL << 32) && (long long)K * N < (1LL << 32) && M < (1 << 30);
+}
+
+QSPEC_EXPORT int qspec_quantize_act_fp8(const uint16_t *x, int32_t M, int32_t K, uint8_t *codes, float *scales,
+                                        qspec_stream_t stream) {
+    if (!x || !codes || !scales) return QSPEC_ERR_NULL;
+    if (M < 1 || bad_k(K)) return QSPEC_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_quantize_act_fp8(x, M, K, codes, scales, as_stream(stream)));
+}
+
+QSPEC_EXPORT size_t qspec_gemm_w8a8_workspace_bytes(int32_t M, int32_t K, int32_t N) {
+    if (!w8a8_sizes_ok(M, K, N)) return 0;
+    return qspec::gemm_w8a8_workspace_bytes(M, K, N);
+}
+
+QSPEC_EXPORT int qspec_gemm_w8a8(const uint8_t *a_codes, const float *a_scales, int32_t M, const uint8_t *w_store,
+                                 const float *w_scales, int32_t K, int32_t N, void *y, int32_t y_dtype,
+                                 void *workspace, size_t workspace_bytes, qspec_stream_t stream) {
+    if (!a_codes || !a_scales || !w_store || !w_scales || !y) return QSPEC_ERR_NULL;
+    if (!w8a8_sizes_ok(M, K, N)) return QSPEC_ERR_SHAPE;
+    if (y_dtype != QSPEC_OUT_BF16 && y_dtype != QSPEC_OUT_F32) return QSPEC_ERR_UNSUPPORTED;
+    const size_t need = qspec::gemm_w8a8_workspace_bytes(M, K, N);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return QSPEC_ERR_WORKSPACE;
+    if (!aligned(a_codes, 16) || !aligned(w_store, 16) || !aligned(a_scales, 4) || !aligned(w_scales, 4) ||
+        !aligned(y, 16) || !aligned(workspace, 256))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_gemm_w8a8(a_codes, a_scales, M, w_store, w_scales, K, N, y,
+                                             y_dtype == QSPEC_OUT_F32, workspace, as_stream(stream)));
+}

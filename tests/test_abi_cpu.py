@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
         "qspec_status_string", "qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16",
         "qspec_gemm_w4a16_workspace_bytes", "qspec_verify_workspace_bytes", "qspec_verify_accept",
         "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma",
-        "qspec_attention_workspace_bytes", "qspec_attention"])
+        "qspec_attention_workspace_bytes", "qspec_attention", "qspec_quantize_act_fp8",
+        "qspec_gemm_w8a8_workspace_bytes", "qspec_gemm_w8a8"])
 
 
 def test_library_exports_every_declared_symbol_and_nothing_else():
@@ -180,3 +181,31 @@ def test_attention_validation():
     assert call(ws=None) == ERR_WS and call(nbytes=need - 1) == ERR_WS
     assert call(q=ctypes.c_void_p(0x1008)) == ERR_ALIGN and call(cache=ctypes.c_void_p(0x1002)) == ERR_ALIGN
     assert call(ws=ctypes.c_void_p(0x1004)) == ERR_ALIGN
+
+
+def test_fp8_validation():
+    L = q.lib()
+    assert L.qspec_quantize_act_fp8(None, 4, 256, FAKE, FAKE, None) == ERR_NULL
+    assert L.qspec_quantize_act_fp8(FAKE, 0, 256, FAKE, FAKE, None) == ERR_SHAPE
+    assert L.qspec_quantize_act_fp8(FAKE, 4, 200, FAKE, FAKE, None) == ERR_SHAPE
+    assert L.qspec_quantize_act_fp8(FAKE, 4, 256, ctypes.c_void_p(0x1008), FAKE, None) == ERR_ALIGN
+    # splits depend on (K, N) only: none for a wide N, some for narrow N with long K
+    assert q.qspec_gemm_w8a8_workspace_bytes(5, 3584, 152064) == 0
+    need = q.qspec_gemm_w8a8_workspace_bytes(5, 18944, 3584)
+    assert need > 0 and need % (5 * 3584 * 4) == 0 and need // (5 * 3584 * 4) <= 16
+    assert q.qspec_gemm_w8a8_workspace_bytes(80, 18944, 3584) == need // 5 * 80
+    assert q.qspec_gemm_w8a8_workspace_bytes(0, 256, 64) == 0
+    assert q.qspec_gemm_w8a8_workspace_bytes(1, 65536, 65536) == 0          # K * N = 2^32
+
+    def call(**kw):
+        a = dict(a=FAKE, sa=FAKE, M=5, w=FAKE, sw=FAKE, K=18944, N=3584, y=FAKE, dt=0, ws=FAKE, nbytes=need)
+        a.update(kw)
+        return L.qspec_gemm_w8a8(a["a"], a["sa"], a["M"], a["w"], a["sw"], a["K"], a["N"], a["y"], a["dt"], a["ws"],
+                                 a["nbytes"], None)
+    for k in ("a", "sa", "w", "sw", "y"):
+        assert call(**{k: None}) == ERR_NULL, k
+    for kw in (dict(M=0), dict(K=200), dict(N=40), dict(K=65536, N=65536)):
+        assert call(**kw) == ERR_SHAPE, kw
+    assert call(dt=5) == ERR_UNSUPPORTED
+    assert call(ws=None) == ERR_WS and call(nbytes=need - 1) == ERR_WS
+    assert call(w=ctypes.c_void_p(0x1008)) == ERR_ALIGN and call(ws=ctypes.c_void_p(0x1010)) == ERR_ALIGN
