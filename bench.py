@@ -355,6 +355,7 @@ def gpu_leg(args):
         torch.cuda.synchronize()
     R.speckv_us = speckv_controller_us(R, torch)
     R.attention = attention_us(R, torch)
+    R.fp8 = fp8_parent_us(R, torch)
     return R, ph, wall, event_ms
 
 
@@ -411,6 +412,45 @@ def attention_us(R, torch):
         torch.cuda.synchronize()
         res[Q] = a.elapsed_time(b) * 1e3 / 30
         del qd, cache
+    return res
+
+
+QWEN25_7B = {"qkv": (3584, 4608), "o": (3584, 3584), "gate_up": (3584, 2 * 18944), "down": (18944, 3584),
+             "lm_head": (3584, 152064)}
+
+
+def fp8_parent_us(R, torch, gamma=4):
+    """Outside the timed round: the FP8 parent (per-token E4M3 activations, E4M3 weights with column
+    scales) verifying gamma = 4 drafts of one sequence (M = 5) on Qwen2.5-7B's shapes: per projection,
+    qspec_quantize_act_fp8 + qspec_gemm_w8a8, graph-replayed over 4 weight copies of the layer (beyond
+    the last-level cache); returns {projection: (layer us, quantize us, weight+scale bytes)}."""
+    import synthetic_inputs as si
+
+    q, dev, M = R.q, R.accept.device, gamma + 1
+    res = {}
+    for name, (K, N) in QWEN25_7B.items():
+        copies = 1 if name == "lm_head" else 4
+        W = [si.fp8_weights_device(K, N, seed=c, device=dev) for c in range(copies)]
+        x = si.activations_device(M, K, seed=1, device=dev)
+        codes = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sa = torch.empty((M,), dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((max(1, q.qspec_gemm_w8a8_workspace_bytes(M, K, N)),), dtype=torch.uint8, device=dev)
+        times = []
+        for fn in (lambda: [q.qspec_gemm_w8a8(codes, sa, *W[c], y, ws) for c in range(copies)],
+                   lambda: [q.qspec_quantize_act_fp8(x, codes, sa) for c in range(copies)]):
+            graph = capture(lambda: [fn() for _ in range(8 // copies if copies < 8 else 1)], torch)
+            graph.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(4):
+                graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3 / (4 * 8))
+        res[name] = (times[0], times[1], K * N + 4 * N)
+        del W
     return res
 
 
@@ -532,6 +572,13 @@ def main():
                       **{f"us_Q{Qa}": round(u, 1) for Qa, u in R.attention.items()},
                       **{f"hbm_frac_Q{Qa}": round(B * KV_HEADS * CONTEXT * 2 * HEAD_DIM * 2 / (u * 1e-6) / 1e9
                                                   / HBM_PEAK_GBS, 4) for Qa, u in R.attention.items()}},
+        # outside the timed round: the FP8 parent (W8A8, E4M3) verifying gamma = 4 drafts of one
+        # sequence (M = 5) on Qwen2.5-7B's projections; HBM fraction of the weight bytes alone
+        "fp8_parent_qwen25_7b_M5": {
+            **{f"{k}_us": round(v[0], 2) for k, v in R.fp8.items()},
+            **{f"{k}_hbm_frac": round(v[2] / (v[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 3) for k, v in R.fp8.items()},
+            "quantize_act_fp8_us": {k: round(v[1], 2) for k, v in R.fp8.items()},
+            "layer_projections_us": round(sum(v[0] + v[1] for k, v in R.fp8.items() if k != "lm_head"), 1)},
         # verify tokens/s at this gamma as the verify GEMMs alone bound it: B (gamma + 1) tokens per
         # pass over the layers' four projections (W4A16 at M = B (gamma + 1)), whole stack and per layer
         "verify_gemm_tokens_per_s": {"layers_%d" % args.layers: round(B * (g + 1) / (verify_ms / 1e3), 1),

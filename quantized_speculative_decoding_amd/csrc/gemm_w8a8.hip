@@ -5,7 +5,8 @@
 // per token, both absmax / 448; y = s_a[m] s_w[n] sum_k dec(a[m][k]) dec(w[k][n]).
 //
 //   k_quantize_act_fp8  one workgroup per token: the row's absmax, s = absmax / 448 (one binary32
-//                       division), codes = E4M3(x / s) rounded to nearest even, saturating.
+//                       division), codes = E4M3(x / s) rounded to nearest even, saturating; the row
+//                       stays in registers between the two passes.
 //   k_w8a8              v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E4M3 and unit
 //                       scales: products of E4M3 values are exact, sums fp32.  Lane l = c + 16 q
 //                       holds 32 consecutive k (128 g + 32 q + 0..31) of its A row and of its B
@@ -20,6 +21,8 @@ constexpr int kW8Waves = 4;              // waves per workgroup
 constexpr int kW8NT = 2;                 // 16-column tiles per wave
 constexpr int kW8MaxMT = 5;              // 16-row tiles per workgroup (M <= 80 in one pass)
 constexpr int kW8MaxSplits = 16;         // the split-K reduce adds at most 16 partials
+constexpr int kW8Ring = 4;               // register ring depth (groups in flight per wave), MT <= 2
+constexpr int kW8TargetWaves = 2048;     // K splits aim at this many waves
 
 typedef __attribute__((ext_vector_type(8))) int w8_i32x8_t;
 
@@ -43,27 +46,43 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
     return sign | code;
 }
 
-__global__ void __launch_bounds__(256)
+// One workgroup of kQThreads per token.  Rows of up to kQThreads * 8 * kQCache elements are read
+// once and kept in registers for the second pass; longer rows are read again.
+constexpr int kQThreads = 1024;
+constexpr int kQCache = 4;
+
+__global__ void __launch_bounds__(kQThreads)
 k_quantize_act_fp8(const uint16_t *__restrict__ x, int K, uint8_t *__restrict__ codes, float *__restrict__ scales) {
-    __shared__ float red[256 / kWave];
+    __shared__ float red[kQThreads / kWave];
     const int m = blockIdx.x;
     const uint16_t *xr = x + (size_t)m * K;
+    constexpr int STEP = kQThreads * 8;
+    uint4 keep[kQCache];
     float a = 0.f;
-    for (int k = threadIdx.x * 8; k < K; k += 256 * 8) {
-        const uint4 u = *(const uint4 *)(xr + k);
+    auto absmax8 = [](uint4 u, float acc) {
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            a = fmaxf(a, fmaxf(fabsf(bf16_bits_to_float(w[i] & 0xFFFFu)), fabsf(bf16_bits_to_float(w[i] >> 16))));
+            acc = fmaxf(acc, fmaxf(fabsf(bf16_bits_to_float(w[i] & 0xFFFFu)), fabsf(bf16_bits_to_float(w[i] >> 16))));
+        return acc;
+    };
+#pragma unroll
+    for (int it = 0; it < kQCache; ++it) {
+        const int k = it * STEP + threadIdx.x * 8;
+        keep[it] = k < K ? *(const uint4 *)(xr + k) : make_uint4(0u, 0u, 0u, 0u);
     }
+#pragma unroll
+    for (int it = 0; it < kQCache; ++it) a = absmax8(keep[it], a);
+    for (int k = kQCache * STEP + threadIdx.x * 8; k < K; k += STEP) a = absmax8(*(const uint4 *)(xr + k), a);
     a = wave_max(a);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
     __syncthreads();
-    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    a = red[0];
+#pragma unroll
+    for (int i = 1; i < kQThreads / kWave; ++i) a = fmaxf(a, red[i]);
     const float s = a / 448.0f;
     if (threadIdx.x == 0) scales[m] = s;
-    for (int k = threadIdx.x * 8; k < K; k += 256 * 8) {
-        const uint4 u = *(const uint4 *)(xr + k);
+    auto encode8 = [&](uint4 u, int k) {
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
         uint32_t out[2] = {0u, 0u};
         if (a != 0.f) {
@@ -75,15 +94,21 @@ k_quantize_act_fp8(const uint16_t *__restrict__ x, int K, uint8_t *__restrict__ 
             }
         }
         *(uint2 *)(codes + (size_t)m * K + k) = make_uint2(out[0], out[1]);
+    };
+#pragma unroll
+    for (int it = 0; it < kQCache; ++it) {
+        const int k = it * STEP + threadIdx.x * 8;
+        if (k < K) encode8(keep[it], k);
     }
+    for (int k = kQCache * STEP + threadIdx.x * 8; k < K; k += STEP) encode8(*(const uint4 *)(xr + k), k);
 }
 
 // K splits: a function of (K, N) only (so a row's sum order does not depend on M).  Enough
-// splits for about 2048 waves, at least 4 groups per split, at most 16.
+// splits for about kW8TargetWaves waves, at least 4 groups per split, at most 16.
 static int w8a8_splits(int K, int N) {
     const int G = K / kGroup;
     const int wave_cols = (N / 16 + kW8NT - 1) / kW8NT;
-    int S = min(min((2048 + wave_cols - 1) / wave_cols, kW8MaxSplits), max(1, G / 4));
+    int S = min(min((kW8TargetWaves + wave_cols - 1) / wave_cols, kW8MaxSplits), max(1, G / 4));
     S = max(S, 1);
     const int gps = (G + S - 1) / S;
     return (G + gps - 1) / gps;                                  // no empty split
@@ -141,25 +166,37 @@ k_w8a8(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, 
 #pragma unroll
         for (int nt = 0; nt < kW8NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    Stage cur, nxt;
-    if (g0 < g1) load(g0, cur);
-    for (int g = g0; g < g1; ++g) {
-        if (g + 1 < g1) load(g + 1, nxt);
+    // U-deep register ring: group g's loads are issued U - 1 groups ahead of its MFMAs (two deep
+    // for three or more row tiles, whose stages are larger)
+    constexpr int U = MT <= 2 ? kW8Ring : 2;
+    Stage st[U];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const w8_i32x8_t av = {(int)cur.a[mt][0].x, (int)cur.a[mt][0].y, (int)cur.a[mt][0].z, (int)cur.a[mt][0].w,
-                                   (int)cur.a[mt][1].x, (int)cur.a[mt][1].y, (int)cur.a[mt][1].z, (int)cur.a[mt][1].w};
+    for (int u = 0; u + 1 < U; ++u)
+        if (g0 + u < g1) load(g0 + u, st[u]);
+    for (int gb = g0; gb < g1; gb += U) {
 #pragma unroll
-            for (int nt = 0; nt < kW8NT; ++nt) {
-                const w8_i32x8_t bv = {(int)cur.b[nt][0].x, (int)cur.b[nt][0].y, (int)cur.b[nt][0].z,
-                                       (int)cur.b[nt][0].w, (int)cur.b[nt][1].x, (int)cur.b[nt][1].y,
-                                       (int)cur.b[nt][1].z, (int)cur.b[nt][1].w};
-                // formats 0, 0: both operands E4M3; E8M0 scales 127 = 2^0
-                acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt][nt], 0, 0, 0, 127, 0,
-                                                                                127);
+        for (int u = 0; u < U; ++u) {
+            const int g = gb + u;
+            if (g < g1) {
+                if (g + U - 1 < g1) load(g + U - 1, st[(u + U - 1) % U]);
+                const Stage &cur = st[u];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const w8_i32x8_t av = {(int)cur.a[mt][0].x, (int)cur.a[mt][0].y, (int)cur.a[mt][0].z,
+                                           (int)cur.a[mt][0].w, (int)cur.a[mt][1].x, (int)cur.a[mt][1].y,
+                                           (int)cur.a[mt][1].z, (int)cur.a[mt][1].w};
+#pragma unroll
+                    for (int nt = 0; nt < kW8NT; ++nt) {
+                        const w8_i32x8_t bv = {(int)cur.b[nt][0].x, (int)cur.b[nt][0].y, (int)cur.b[nt][0].z,
+                                               (int)cur.b[nt][0].w, (int)cur.b[nt][1].x, (int)cur.b[nt][1].y,
+                                               (int)cur.b[nt][1].z, (int)cur.b[nt][1].w};
+                        // formats 0, 0: both operands E4M3; E8M0 scales 127 = 2^0
+                        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt][nt], 0, 0, 0,
+                                                                                        127, 0, 127);
+                    }
+                }
             }
         }
-        if (g + 1 < g1) cur = nxt;
     }
 
     // lane l, element e holds D[4 kq + e][c]: row row0 + 16 mt + 4 kq + e, column 16 tile + c
@@ -189,7 +226,7 @@ k_w8a8(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, 
 }
 
 hipError_t launch_quantize_act_fp8(const uint16_t *x, int M, int K, uint8_t *codes, float *scales, hipStream_t st) {
-    hipLaunchKernelGGL(k_quantize_act_fp8, dim3(M), dim3(256), 0, st, x, K, codes, scales);
+    hipLaunchKernelGGL(k_quantize_act_fp8, dim3(M), dim3(kQThreads), 0, st, x, K, codes, scales);
     return hipGetLastError();
 }
 
