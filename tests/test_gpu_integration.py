@@ -10,7 +10,11 @@ The toy model: an embedding table E [V][H]; a one-projection "KV" row kv(t) = W_
 cached per position; next-token logits = lm_head(E[token_t] + mean of the cached rows 0..t).
 The identity holds because row results of qspec_gemm_w4a16 do not depend on M within a batch
 tier (M = 1 in plain decoding, gamma + 1 in verification), so the verifier reproduces plain
-decoding's KV rows and logits bit for bit."""
+decoding's KV rows and logits bit for bit.
+
+A second toy replaces the mean with qspec_attention over the shared cache (queries E[token],
+keys = values = the cached rows); there the identity also needs every query row of an attention
+call to be bit-identical whether it is computed alone (Q = 1) or with gamma others (Q = gamma + 1)."""
 import numpy as np
 import pytest
 import torch
@@ -135,3 +139,87 @@ def test_qspec_greedy_loop_equals_plain_w4a16_greedy(seed, gamma, unrelated):
         assert accepts.count(0) > len(accepts) // 2       # mostly first-position rejections
     else:
         assert sum(accepts) > 0                           # the drafts were used
+
+
+# ---- the same identity with attention over the shared cache -------------------------------------
+# hidden(t) = bf16(E[token_t] + attention(q = E[token_t], keys = values = the cached KV rows 0..t)),
+# through qspec_attention: Q = 1 per plain step and per draft step (over a cache holding the
+# draft's W4A4 rows for the current round), Q = gamma + 1 for the verify pass (over the committed
+# rows plus the verifier's gamma + 1 staged rows); qspec_kv_overwrite then commits A + 1 rows.
+
+class AttnToy(Toy):
+    def attend(self, cache, toks, pos):
+        """toks: the Q query tokens at positions pos .. pos + Q - 1; returns hidden bf16 bits [Q][H]."""
+        Qn = len(toks)
+        qd = bf16_dev(self.E[np.asarray(toks)]).view(1, Qn, HEADS, D)
+        out = torch.empty((1, Qn, HEADS, D), dtype=torch.bfloat16, device=DEV)
+        ws = torch.empty((q.qspec_attention_workspace_bytes(1, Qn, HEADS, HEADS, CTX),), dtype=torch.uint8, device=DEV)
+        q.qspec_attention(qd, cache[0], cu(np.array([pos], np.int32)), D ** -0.5, out, ws)
+        o = (out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(Qn, H).astype(np.uint32) << 16).view(np.float32)
+        return si.f32_to_bf16_bits(self.Ef[np.asarray(toks)] + o)
+
+
+def write_row(cache, t, bits):
+    row = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV).view(HEADS, D)
+    cache[0, 0, 0, :, t, :] = row                  # key
+    cache[0, 0, 1, :, t, :] = row                  # value
+
+
+def plain_greedy_attn(m: AttnToy, first: int, n: int) -> list:
+    cache = torch.zeros((1, 1, 2, HEADS, CTX, D), dtype=torch.bfloat16, device=DEV)
+    toks = [first]
+    while len(toks) < n + 1:
+        t = len(toks) - 1
+        write_row(cache, t, m.kv16([toks[t]])[0])
+        h = m.attend(cache, [toks[t]], t)
+        toks.append(int(np.argmax(m.logits16(h).cpu().numpy()[0])))
+    return toks
+
+
+def qspec_greedy_attn(m: AttnToy, first: int, n: int, gamma: int):
+    cache = torch.zeros((1, 1, 2, HEADS, CTX, D), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty((q.qspec_verify_workspace_bytes(q.QSPEC_GREEDY, 1, gamma, V),), dtype=torch.uint8, device=DEV)
+    acc = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    out = torch.zeros((1, gamma + 1), dtype=torch.int32, device=DEV)
+    toks, p, accepts = [first], 0, []
+    while len(toks) < n + 1:
+        d, tok = [], toks[p]
+        for j in range(gamma):                                     # draft: W4A4 KV row, Q = 1 attention
+            write_row(cache, p + j, m.kv4(tok))
+            tok = int(np.argmax(m.logits4(m.attend(cache, [tok], p + j)[0])))
+            d.append(tok)
+        vt = [toks[p]] + d
+        vkv = m.kv16(vt)                                           # the verifier's rows for p .. p + gamma
+        vcache = cache.clone()
+        for j in range(gamma + 1):
+            write_row(vcache, p + j, vkv[j])
+        target = m.logits16(m.attend(vcache, vt, p)).view(1, gamma + 1, V)
+        q.qspec_verify_accept(q.QSPEC_GREEDY, target, None, cu(np.array([d], np.int32)), None, None, acc, out, ws)
+        stage = torch.zeros((1, 1, 2, HEADS, gamma + 1, D), dtype=torch.bfloat16, device=DEV)
+        rows = torch.from_numpy(vkv.view(np.int16)).view(torch.bfloat16).to(DEV).view(gamma + 1, HEADS, D)
+        stage[0, 0, 0] = rows.permute(1, 0, 2)
+        stage[0, 0, 1] = rows.permute(1, 0, 2)
+        q.qspec_kv_overwrite(cache, stage, cu(np.array([p], np.int32)), acc)
+        A = int(acc.cpu()[0])
+        committed = out.cpu().numpy()[0, : A + 1].tolist()
+        assert committed[:A] == d[:A]
+        # the committed positions now hold exactly the verifier's rows
+        assert torch.equal(cache[0, 0, :, :, p:p + A + 1, :], vcache[0, 0, :, :, p:p + A + 1, :])
+        accepts.append(A)
+        toks.extend(committed)
+        p += A + 1
+    return toks[: n + 1], accepts
+
+
+@pytest.mark.parametrize("seed,gamma,unrelated", [(11, 4, False), (29, 3, False), (5, 4, True)])
+def test_qspec_greedy_with_attention_over_the_shared_cache_equals_plain_greedy(seed, gamma, unrelated):
+    note(f"toy decoder with attention seed={seed} gamma={gamma} unrelated draft head={unrelated}")
+    m = AttnToy(seed, unrelated)
+    n = 40
+    ref = plain_greedy_attn(m, first=seed % V, n=n)
+    got, accepts = qspec_greedy_attn(m, first=seed % V, n=n, gamma=gamma)
+    note(f"accept counts per round: {accepts}")
+    assert got == ref
+    assert len(accepts) > 1
+    if not unrelated:
+        assert sum(accepts) > 0
