@@ -111,6 +111,13 @@ def summarize(args):
         if "k_attn" in r["Name"]:
             lines.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "FP8 parent, outside the timed round (Qwen2.5-7B qkv, o, gate+up, down, lm_head at M=5; "
+              "the split-K reduce it shares with W4A16 is in the table above):", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for r in stats:
+        if "w8a8" in r["Name"] or "fp8" in r["Name"]:
+            lines.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     open(os.path.join(PROFILES, "kernel_trace_llama3_8b_round_B16_g4.md"), "w").write("\n".join(lines) + "\n")
 
     def per_dispatch(d):
@@ -121,7 +128,8 @@ def summarize(args):
             key = r["Kernel_Name"].split("(")[0]
             agg[(key, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
             if "copyBuffer" in r["Kernel_Name"]:
-                calib = float(r["Counter_Value"])      # the last copy is the calibration copy
+                # the calibration copy is by far the largest copy of the run
+                calib = max(calib or 0.0, float(r["Counter_Value"]))
         return agg, calib
 
     fetch, fcal = per_dispatch(fetch_dir)
