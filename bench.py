@@ -256,6 +256,13 @@ class Round:
                 wc, wm = self.weights[l][i]
                 self.q.qspec_gemm_w4a16(self.x_verify[i], wc, wm, self.y_verify[i], self.ws_verify[i])
 
+    def plain_gemm(self):
+        """One plain W4A16 decoding step (M = B) over the same layers: the round model's T_target."""
+        for l in range(self.L):
+            for i in range(len(self.projs)):
+                wc, wm = self.weights[l][i]
+                self.q.qspec_gemm_w4a16(self.x_draft[i], wc, wm, self.y_draft[i])
+
     def accept_phase(self, s):
         t, d, toks, u, v = self.logits[s]
         self.q.qspec_verify_accept(self.q.QSPEC_SAMPLE, t, d, toks, u, v, self.accept, self.out_tokens, self.ws)
@@ -361,10 +368,43 @@ def gpu_leg(args):
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
+    R.model = round_model(R, ph, torch)
     R.speckv_us = speckv_controller_us(R, torch)
     R.attention = attention_us(R, torch)
     R.fp8 = fp8_parent_us(R, torch)
     return R, ph, wall, event_ms
+
+
+def round_model(R, ph, torch):
+    """Outside the timed round: the speedup model S = E[L] T_target / (T_draft + T_verify +
+    T_overhead) with every time measured here (T_target = one plain W4A16 decoding step at M = B
+    over the same layers, graph-replayed) and E[L] both as the round's accept counts give it (mean
+    A + 1 over the 4 logit sets) and as (1 - a^(gamma+1)) / (1 - a) at a few acceptance rates a."""
+    graph = capture(R.plain_gemm, torch)
+    graph.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    t_target = a.elapsed_time(b) / 5
+    counts = []
+    for s_ in range(R.n_logit_sets):
+        R.accept_phase(s_)
+        counts.append(R.accept.cpu().clone())
+    e_l = float(torch.cat(counts).double().mean()) + 1.0
+    t_draft = ph["quantize_act"] + ph["gemm_w4a4"]
+    t_verify = ph["gemm_w4a16"]
+    t_over = ph["verify_accept"] + ph["kv_overwrite"]
+    t_round = t_draft + t_verify + t_over
+    g = R.gamma
+    at = {al: (1 - al ** (g + 1)) / (1 - al) * t_target / t_round for al in (0.6, 0.8, 0.9)}
+    return {"T_target_ms": round(t_target, 4), "T_draft_ms": round(t_draft, 4), "T_verify_ms": round(t_verify, 4),
+            "T_overhead_ms": round(t_over, 4), "E_L_measured": round(e_l, 4),
+            "S_measured_E_L": round(e_l * t_target / t_round, 3),
+            "S_at_alpha": {str(k): round(v, 3) for k, v in at.items()}}
 
 
 def speckv_controller_us(R, torch):
@@ -572,6 +612,9 @@ def main():
         "event_ms_per_round": round(event_ms, 4),
         "gemm_hbm_tbs": {"gemm_w4a4_M%d" % B: round(R.draft_gemm_bytes() * g / (draft_ms / 1e3) / 1e12, 3),
                          "gemm_w4a16_M%d" % (B * (g + 1)): round(R.verify_gemm_bytes() / (verify_ms / 1e3) / 1e12, 3)},
+        # outside the timed round: the round-time and speedup model from these measurements
+        # (projections only: attention, norms and the vocabulary projection are not in T_target)
+        "round_model": R.model,
         # outside the timed round: the adaptive-gamma controller on one draft row per sequence
         "speckv_controller_us": round(R.speckv_us, 1),
         # outside the timed round: one layer's attention over the full cache; every key and value
