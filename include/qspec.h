@@ -208,6 +208,35 @@ int qspec_verify_accept(int32_t mode, const float *target_logits, const float *d
                         size_t workspace_bytes, qspec_stream_t stream);
 
 /*
+ * qspec_draft_sample_workspace_bytes -- device workspace qspec_draft_sample needs; 0 on invalid
+ * arguments.
+ */
+size_t qspec_draft_sample_workspace_bytes(int32_t mode, int32_t B, int32_t V);
+
+/*
+ * qspec_draft_sample -- the draft-side head of one draft step: one token per sequence from that
+ * step's draft logits.
+ * [QSPEC notes, QSPEC structure: the W4A4 draft proposes gamma tokens one step at a time; the
+ * speculative-decoding background: a draft token x is drawn from the draft distribution q, which
+ * verification later compares with p.]  GREEDY: tokens[b] = argmax logits[b] (lowest index on
+ * ties).  SAMPLE: tokens[b] = the first x whose running sum of softmax(logits[b]) (temperature 1,
+ * fp64) exceeds u[b] times the total mass -- exactly qspec_verify_accept's draw for gamma = 0.
+ * The rows may be strided so that step j of a [B][gamma][V] draft-logit buffer (row_stride =
+ * gamma * V) is read in place and its tokens land in column j of the [B][gamma] draft-token
+ * buffer (token_stride = gamma) that qspec_verify_accept then reads.
+ * logits     [in]  f32, row b at logits + b * row_stride, V values each (finite)
+ * row_stride       elements between rows, >= V
+ * u          [in]  f32 [B] uniforms in [0, 1) (SAMPLE; ignored and may be NULL for GREEDY)
+ * tokens     [out] i32, token b at tokens + b * token_stride
+ * workspace  [in/out] at least qspec_draft_sample_workspace_bytes(mode, B, V) bytes
+ * Errors: bad mode; NULL pointer; B < 1; V < 1; row_stride < V; token_stride < 1; workspace missing
+ * or too small.
+ */
+int qspec_draft_sample(int32_t mode, const float *logits, int32_t B, int32_t V, int64_t row_stride,
+                       const float *u, int32_t *tokens, int32_t token_stride, void *workspace,
+                       size_t workspace_bytes, qspec_stream_t stream);
+
+/*
  * qspec_kv_overwrite -- replace draft KV with verify KV for committed positions.
  * [QSPEC notes, QSPEC structure: for accepted tokens the low-precision KV written
  * by the W4A4 draft is replaced with the KV computed by the W4A16 verifier.]

@@ -71,9 +71,12 @@ def lib() -> ctypes.CDLL:
         L.qspec_gemm_w8a8_workspace_bytes.argtypes = [I, I, I]
         L.qspec_gemm_w8a8_workspace_bytes.restype = S
         L.qspec_gemm_w8a8.argtypes = [P, P, I, P, P, I, I, P, I, P, S, P]
+        L.qspec_draft_sample_workspace_bytes.argtypes = [I, I, I]
+        L.qspec_draft_sample_workspace_bytes.restype = S
+        L.qspec_draft_sample.argtypes = [I, P, I, I, ctypes.c_int64, P, P, I, P, S, P]
         for fn in ("qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_verify_accept",
                    "qspec_kv_overwrite", "qspec_speckv_gamma", "qspec_attention", "qspec_quantize_act_fp8",
-                   "qspec_gemm_w8a8"):
+                   "qspec_gemm_w8a8", "qspec_draft_sample"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -208,6 +211,32 @@ def qspec_verify_accept(mode, target_logits, draft_logits, draft_tokens, u_accep
                                      workspace.numel(), _stream(stream, target_logits)))
 
 
+def qspec_draft_sample_workspace_bytes(mode: int, B: int, V: int) -> int:
+    return int(lib().qspec_draft_sample_workspace_bytes(mode, B, V))
+
+
+def qspec_draft_sample(mode, logits, tokens, u, workspace, stream=None) -> None:
+    """The draft-side head of one step: logits f32 [B][V] with unit stride along V (rows may be
+    strided, e.g. draft_logits[:, j, :]); tokens i32 [B] (may be strided, e.g. draft_tokens[:, j]);
+    u f32 [B] (SAMPLE) or None (GREEDY); workspace u8 of qspec_draft_sample_workspace_bytes bytes."""
+    for t, name, dt in ((logits, "logits", torch.float32), (tokens, "tokens", torch.int32)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA (HIP) device tensor")
+        if t.dtype != dt:
+            raise TypeError(f"{name} must have dtype {dt}")
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [B][V] with unit stride along V")
+    B, V = logits.shape
+    if tokens.dim() != 1 or tokens.shape[0] != B:
+        raise ValueError("tokens must be [B]")
+    if u is not None:
+        _req(u, "u", torch.float32, (B,))
+    _req(workspace, "workspace", torch.uint8)
+    _check("qspec_draft_sample",
+           lib().qspec_draft_sample(mode, _ptr(logits), B, V, logits.stride(0), _ptr(u), _ptr(tokens),
+                                    tokens.stride(0), _ptr(workspace), workspace.numel(), _stream(stream, logits)))
+
+
 def qspec_kv_overwrite(cache, verify_kv, start_pos, accept_count, stream=None) -> None:
     """cache bf16 [L][B][2][H][T][D] <- verify_kv bf16 [L][B][2][H][gamma+1][D] for rows 0..A_b."""
     _req(cache, "cache", torch.bfloat16)
@@ -319,5 +348,6 @@ __all__ = [
     "gemm_w4a16_workspace", "qspec_verify_workspace_bytes",
     "qspec_verify_accept", "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma",
     "qspec_attention_workspace_bytes", "qspec_attention", "qspec_quantize_act_fp8",
-    "qspec_gemm_w8a8_workspace_bytes", "qspec_gemm_w8a8",
+    "qspec_gemm_w8a8_workspace_bytes", "qspec_gemm_w8a8", "qspec_draft_sample_workspace_bytes",
+    "qspec_draft_sample",
 ]

@@ -28,6 +28,11 @@ hipError_t launch_verify_accept(int mode, const float *target, const float *draf
                                 int32_t *accept_count, int32_t *out_tokens, void *workspace,
                                 hipStream_t st);
 
+size_t draft_sample_workspace_bytes(int mode, int B, int V);
+
+hipError_t launch_draft_sample(int mode, const float *logits, size_t ldt, const float *u, int B, int V,
+                               int32_t *tokens, int ldo, void *workspace, hipStream_t st);
+
 size_t speckv_workspace_bytes(int R, int V);
 
 hipError_t launch_speckv_gamma(const float *logits, int R, int V, float quant_feature, const float *w1,

@@ -214,3 +214,22 @@ QSPEC_EXPORT int qspec_gemm_w8a8(const uint8_t *a_codes, const float *a_scales, 
     return status_of(qspec::launch_gemm_w8a8(a_codes, a_scales, M, w_store, w_scales, K, N, y,
                                              y_dtype == QSPEC_OUT_F32, workspace, as_stream(stream)));
 }
+
+QSPEC_EXPORT size_t qspec_draft_sample_workspace_bytes(int32_t mode, int32_t B, int32_t V) {
+    if ((mode != QSPEC_GREEDY && mode != QSPEC_SAMPLE) || !verify_sizes_ok(B, 0, V)) return 0;
+    return qspec::draft_sample_workspace_bytes(mode, B, V);
+}
+
+QSPEC_EXPORT int qspec_draft_sample(int32_t mode, const float *logits, int32_t B, int32_t V, int64_t row_stride,
+                                    const float *u, int32_t *tokens, int32_t token_stride, void *workspace,
+                                    size_t workspace_bytes, qspec_stream_t stream) {
+    if (mode != QSPEC_GREEDY && mode != QSPEC_SAMPLE) return QSPEC_ERR_UNSUPPORTED;
+    if (!logits || !tokens || (mode == QSPEC_SAMPLE && !u)) return QSPEC_ERR_NULL;
+    if (!verify_sizes_ok(B, 0, V) || row_stride < V || token_stride < 1) return QSPEC_ERR_SHAPE;
+    if ((long long)(B - 1) * row_stride + V > kMaxElems) return QSPEC_ERR_SHAPE;
+    if (!workspace || workspace_bytes < qspec::draft_sample_workspace_bytes(mode, B, V)) return QSPEC_ERR_WORKSPACE;
+    if (!aligned(logits, 4) || !aligned(u, 4) || !aligned(tokens, 4) || !aligned(workspace, 16))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_draft_sample(mode, logits, (size_t)row_stride, u, B, V, tokens, token_stride,
+                                                workspace, as_stream(stream)));
+}

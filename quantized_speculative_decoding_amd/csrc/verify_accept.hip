@@ -133,10 +133,10 @@ __device__ __forceinline__ void for_chunk(const float *row, int lo, int hi, bool
 // Greedy.
 
 __global__ void __launch_bounds__(VT)
-k_argmax_partial(const float *__restrict__ target, int V, int C, bool vec, float *__restrict__ gval,
+k_argmax_partial(const float *__restrict__ target, size_t ldt, int V, int C, bool vec, float *__restrict__ gval,
                  int *__restrict__ gidx) {
     const int row = blockIdx.x / C, c = blockIdx.x % C;
-    const float *p = target + (size_t)row * V;
+    const float *p = target + (size_t)row * ldt;
     const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
     ArgMax a = {-INFINITY, INT_MAX};
     // each thread visits increasing x, so keeping strict improvements keeps the lowest index
@@ -152,7 +152,7 @@ k_argmax_partial(const float *__restrict__ target, int V, int C, bool vec, float
 
 __global__ void k_greedy_accept(const float *__restrict__ gval, const int *__restrict__ gidx, int C,
                                 const int32_t *__restrict__ tokens, int B, int gamma, int V,
-                                int32_t *__restrict__ accept, int32_t *__restrict__ out) {
+                                int32_t *__restrict__ accept, int32_t *__restrict__ out, int ldo) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
     int A = 0;
@@ -172,25 +172,25 @@ __global__ void k_greedy_accept(const float *__restrict__ gval, const int *__res
         int t = -1;
         if (j < A) t = tokens[(size_t)b * gamma + j];
         else if (j == A) t = top;
-        out[(size_t)b * (gamma + 1) + j] = t;
+        out[(size_t)b * ldo + j] = t;
     }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Speculative sampling.
 
-__device__ __forceinline__ const float *logit_row(const float *target, const float *draft, int B,
+__device__ __forceinline__ const float *logit_row(const float *target, size_t ldt, const float *draft, int B,
                                                   int gamma, int V, long long row) {
     const long long Rt = (long long)B * (gamma + 1);
-    return row < Rt ? target + (size_t)row * V : draft + (size_t)(row - Rt) * V;
+    return row < Rt ? target + (size_t)row * ldt : draft + (size_t)(row - Rt) * V;
 }
 
 __global__ void __launch_bounds__(VT)
-k_softmax_partial(const float *__restrict__ target, const float *__restrict__ draft, int B, int gamma,
+k_softmax_partial(const float *__restrict__ target, size_t ldt, const float *__restrict__ draft, int B, int gamma,
                   int V, int C, bool vec, float *__restrict__ pmax, double *__restrict__ psum) {
     const long long row = blockIdx.x / C;
     const int c = blockIdx.x % C;
-    const float *p = logit_row(target, draft, B, gamma, V, row);
+    const float *p = logit_row(target, ldt, draft, B, gamma, V, row);
     const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
     float m = -INFINITY;
     for_chunk(p, lo, hi, vec, [&](int, float v) { m = fmaxf(m, v); });
@@ -209,12 +209,12 @@ k_softmax_partial(const float *__restrict__ target, const float *__restrict__ dr
 // rows 0..gamma, then draft rows) in chunk order; then lane j tests candidate j, and the first
 // rejection (an invalid token, or not u < p/q) among the candidates in order ends acceptance.
 __global__ void __launch_bounds__(kWave)
-k_sample_accept(const float *__restrict__ target, const float *__restrict__ draft,
+k_sample_accept(const float *__restrict__ target, size_t ldt, const float *__restrict__ draft,
                 const int32_t *__restrict__ tokens, const float *__restrict__ u,
                 int B, int gamma, int V, int C, const float *__restrict__ pmax,
                 const double *__restrict__ psum, float *__restrict__ rowM,
                 double *__restrict__ rowS, int *__restrict__ accA,
-                int32_t *__restrict__ accept, int32_t *__restrict__ out) {
+                int32_t *__restrict__ accept, int32_t *__restrict__ out, int ldo) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     const long long Rt = (long long)B * (gamma + 1);
@@ -238,7 +238,7 @@ k_sample_accept(const float *__restrict__ target, const float *__restrict__ draf
             if (d >= 0 && d < V) {
                 const long long rt = (long long)b * (gamma + 1) + j;
                 const long long rd = Rt + (long long)b * gamma + j;
-                const double p = exp((double)target[(size_t)rt * V + d] - (double)rowM[rt]) / rowS[rt];
+                const double p = exp((double)target[(size_t)rt * ldt + d] - (double)rowM[rt]) / rowS[rt];
                 const double q = exp((double)draft[(size_t)(rd - Rt) * V + d] - (double)rowM[rd]) / rowS[rd];
                 ok = (double)u[(size_t)b * gamma + j] < p / q;
             }
@@ -254,7 +254,7 @@ k_sample_accept(const float *__restrict__ target, const float *__restrict__ draf
         accept[b] = A;
     }
     for (int j = lane; j <= gamma; j += kWave)
-        if (j != A) out[(size_t)b * (gamma + 1) + j] = j < A ? tokens[(size_t)b * gamma + j] : -1;
+        if (j != A) out[(size_t)b * ldo + j] = j < A ? tokens[(size_t)b * gamma + j] : -1;
 }
 
 // Residual (or target) mass at one logit of the last committed row.
@@ -271,12 +271,13 @@ struct ResidRow {
     __device__ __forceinline__ double r(int x) const { return r_of(x, p(x)); }
 };
 
-__device__ __forceinline__ ResidRow resid_row(const float *target, const float *draft, int B, int gamma,
-                                              int V, int b, int A, const float *rowM, const double *rowS) {
+__device__ __forceinline__ ResidRow resid_row(const float *target, size_t ldt, const float *draft, int B,
+                                              int gamma, int V, int b, int A, const float *rowM,
+                                              const double *rowS) {
     const long long Rt = (long long)B * (gamma + 1);
     const long long rt = (long long)b * (gamma + 1) + A;
     ResidRow R;
-    R.t = target + (size_t)rt * V;
+    R.t = target + (size_t)rt * ldt;
     R.Mt = rowM[rt];
     R.St = rowS[rt];
     if (A < gamma) {
@@ -293,11 +294,11 @@ __device__ __forceinline__ ResidRow resid_row(const float *target, const float *
 }
 
 __global__ void __launch_bounds__(VT)
-k_residual_partial(const float *__restrict__ target, const float *__restrict__ draft, int B, int gamma,
-                   int V, int C, const float *__restrict__ rowM, const double *__restrict__ rowS,
+k_residual_partial(const float *__restrict__ target, size_t ldt, const float *__restrict__ draft, int B,
+                   int gamma, int V, int C, const float *__restrict__ rowM, const double *__restrict__ rowS,
                    const int *__restrict__ accA, double *__restrict__ resid, double *__restrict__ pmass) {
     const int b = blockIdx.x / C, c = blockIdx.x % C;
-    const ResidRow R = resid_row(target, draft, B, gamma, V, b, accA[b], rowM, rowS);
+    const ResidRow R = resid_row(target, ldt, draft, B, gamma, V, b, accA[b], rowM, rowS);
     const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
     double sr = 0.0, sp = 0.0;
     for (int x = lo + (int)threadIdx.x; x < hi; x += VT) {
@@ -314,17 +315,17 @@ k_residual_partial(const float *__restrict__ target, const float *__restrict__ d
 }
 
 __global__ void __launch_bounds__(VT)
-k_residual_pick(const float *__restrict__ target, const float *__restrict__ draft,
+k_residual_pick(const float *__restrict__ target, size_t ldt, const float *__restrict__ draft,
                 const float *__restrict__ v, int B, int gamma, int V, int C,
                 const float *__restrict__ rowM, const double *__restrict__ rowS,
                 const int *__restrict__ accA, const double *__restrict__ resid,
-                const double *__restrict__ pmass, int32_t *__restrict__ out) {
+                const double *__restrict__ pmass, int32_t *__restrict__ out, int ldo) {
     __shared__ double seg[VT];
     __shared__ int s_chunk, s_fallback, s_usep, s_seg;
     __shared__ double s_thr, s_run;
     const int b = blockIdx.x;
     const int A = accA[b];
-    ResidRow R = resid_row(target, draft, B, gamma, V, b, A, rowM, rowS);
+    ResidRow R = resid_row(target, ldt, draft, B, gamma, V, b, A, rowM, rowS);
     if (threadIdx.x == 0) {
         const double *part = resid + (size_t)b * C;
         double tot = 0.0;
@@ -404,7 +405,7 @@ k_residual_pick(const float *__restrict__ target, const float *__restrict__ draf
                 for (int x = e - 1; x >= a; --x)
                     if (seg[x - a] > 0.0) { tok = x; break; }
             if (tok < 0) tok = min(a, hi - 1);
-            out[(size_t)b * (gamma + 1) + A] = tok;
+            out[(size_t)b * ldo + A] = tok;
         }
         return;
     }
@@ -420,7 +421,7 @@ k_residual_pick(const float *__restrict__ target, const float *__restrict__ draf
         int tok = -1;
         for (int t = VT - 1; t >= 0 && tok < 0; --t) tok = s_last[t];
         if (tok < 0) tok = hi - 1;
-        out[(size_t)b * (gamma + 1) + A] = tok;
+        out[(size_t)b * ldo + A] = tok;
     }
 }
 
@@ -545,7 +546,7 @@ hipError_t launch_speckv_gamma(const float *logits, int R, int V, float quant_fe
     double *pent = (double *)(w + L.pent);
     const bool vec = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0);
     // R rows of "target" logits and no draft rows: the verification's chunk pass with gamma = 0
-    hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)((long long)R * C)), dim3(VT), 0, st, logits,
+    hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)((long long)R * C)), dim3(VT), 0, st, logits, (size_t)V,
                        (const float *)nullptr, R, 0, V, C, vec, pmax, psum);
     hipLaunchKernelGGL(k_entropy_partial, dim3((unsigned)((long long)R * C)), dim3(VT), 0, st, logits, V, C, pmax,
                        psum, pent);
@@ -556,22 +557,24 @@ hipError_t launch_speckv_gamma(const float *logits, int R, int V, float quant_fe
 
 // ---------------------------------------------------------------------------------------------
 
-hipError_t launch_verify_accept(int mode, const float *target, const float *draft,
+// Target row r starts at target + r * ldt; out row b at out + b * ldo (verification: ldt = V,
+// ldo = gamma + 1; the draft-side head reads one step's rows of a [B][gamma][V] buffer).
+static hipError_t launch_verify(int mode, const float *target, size_t ldt, const float *draft,
                                 const int32_t *tokens, const float *u_accept, const float *u_resample,
-                                int B, int gamma, int V, int32_t *accept, int32_t *out, void *ws,
+                                int B, int gamma, int V, int32_t *accept, int32_t *out, int ldo, void *ws,
                                 hipStream_t st) {
     const VerifyLayout L = verify_layout(mode, B, gamma, V);
     char *w = (char *)ws;
     const int C = L.C;
-    const bool vec_t = (V % 4 == 0) && ((uintptr_t)target % 16 == 0);
+    const bool vec_t = (V % 4 == 0) && (ldt % 4 == 0) && ((uintptr_t)target % 16 == 0);
     const long long Rt = (long long)B * (gamma + 1);
     if (mode == 0) {
         float *gval = (float *)(w + L.gval);
         int *gidx = (int *)(w + L.gidx);
-        hipLaunchKernelGGL(k_argmax_partial, dim3((unsigned)(Rt * C)), dim3(VT), 0, st, target, V, C,
+        hipLaunchKernelGGL(k_argmax_partial, dim3((unsigned)(Rt * C)), dim3(VT), 0, st, target, ldt, V, C,
                            vec_t, gval, gidx);
         hipLaunchKernelGGL(k_greedy_accept, dim3((B + 63) / 64), dim3(64), 0, st, gval, gidx, C, tokens,
-                           B, gamma, V, accept, out);
+                           B, gamma, V, accept, out, ldo);
         return hipGetLastError();
     }
     const bool vec = vec_t && (gamma == 0 || (uintptr_t)draft % 16 == 0);
@@ -583,15 +586,37 @@ hipError_t launch_verify_accept(int mode, const float *target, const float *draf
     int *accA = (int *)(w + L.accA);
     double *resid = (double *)(w + L.resid);
     double *pmass = (double *)(w + L.pmass);
-    hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)(R * C)), dim3(VT), 0, st, target, draft, B,
+    hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)(R * C)), dim3(VT), 0, st, target, ldt, draft, B,
                        gamma, V, C, vec, pmax, psum);
-    hipLaunchKernelGGL(k_sample_accept, dim3(B), dim3(kWave), 0, st, target, draft, tokens,
-                       u_accept, B, gamma, V, C, pmax, psum, rowM, rowS, accA, accept, out);
-    hipLaunchKernelGGL(k_residual_partial, dim3((unsigned)((long long)B * C)), dim3(VT), 0, st, target,
+    hipLaunchKernelGGL(k_sample_accept, dim3(B), dim3(kWave), 0, st, target, ldt, draft, tokens,
+                       u_accept, B, gamma, V, C, pmax, psum, rowM, rowS, accA, accept, out, ldo);
+    hipLaunchKernelGGL(k_residual_partial, dim3((unsigned)((long long)B * C)), dim3(VT), 0, st, target, ldt,
                        draft, B, gamma, V, C, rowM, rowS, accA, resid, pmass);
-    hipLaunchKernelGGL(k_residual_pick, dim3(B), dim3(VT), 0, st, target, draft, u_resample, B, gamma, V,
-                       C, rowM, rowS, accA, resid, pmass, out);
+    hipLaunchKernelGGL(k_residual_pick, dim3(B), dim3(VT), 0, st, target, ldt, draft, u_resample, B, gamma, V,
+                       C, rowM, rowS, accA, resid, pmass, out, ldo);
     return hipGetLastError();
+}
+
+hipError_t launch_verify_accept(int mode, const float *target, const float *draft,
+                                const int32_t *tokens, const float *u_accept, const float *u_resample,
+                                int B, int gamma, int V, int32_t *accept, int32_t *out, void *ws,
+                                hipStream_t st) {
+    return launch_verify(mode, target, (size_t)V, draft, tokens, u_accept, u_resample, B, gamma, V, accept, out,
+                         gamma + 1, ws, st);
+}
+
+// The draft-side head: one token per row of a draft step's logits (row b at logits + b * ldt),
+// written to tokens[b * ldo]; the verification with gamma = 0 (greedy: the argmax; sampling: the
+// inverse-CDF draw from softmax(row) at u[b]).  Its accept counts (always 0) go to the workspace
+// after the verification's own layout.
+size_t draft_sample_workspace_bytes(int mode, int B, int V) {
+    return align256(verify_layout(mode, B, 0, V).total) + align256((size_t)B * sizeof(int32_t));
+}
+
+hipError_t launch_draft_sample(int mode, const float *logits, size_t ldt, const float *u, int B, int V,
+                               int32_t *tokens, int ldo, void *ws, hipStream_t st) {
+    int32_t *acc = (int32_t *)((char *)ws + align256(verify_layout(mode, B, 0, V).total));
+    return launch_verify(mode, logits, ldt, nullptr, nullptr, nullptr, u, B, 0, V, acc, tokens, ldo, ws, st);
 }
 
 }  // namespace qspec

@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
         "qspec_gemm_w4a16_workspace_bytes", "qspec_verify_workspace_bytes", "qspec_verify_accept",
         "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma",
         "qspec_attention_workspace_bytes", "qspec_attention", "qspec_quantize_act_fp8",
-        "qspec_gemm_w8a8_workspace_bytes", "qspec_gemm_w8a8"])
+        "qspec_gemm_w8a8_workspace_bytes", "qspec_gemm_w8a8", "qspec_draft_sample_workspace_bytes",
+        "qspec_draft_sample"])
 
 
 def test_library_exports_every_declared_symbol_and_nothing_else():
@@ -209,3 +210,23 @@ def test_fp8_validation():
     assert call(dt=5) == ERR_UNSUPPORTED
     assert call(ws=None) == ERR_WS and call(nbytes=need - 1) == ERR_WS
     assert call(w=ctypes.c_void_p(0x1008)) == ERR_ALIGN and call(ws=ctypes.c_void_p(0x1010)) == ERR_ALIGN
+
+
+def test_draft_sample_validation():
+    L = q.lib()
+    need = q.qspec_draft_sample_workspace_bytes(1, 16, 128256)
+    assert need >= q.qspec_verify_workspace_bytes(1, 16, 0, 128256) + 16 * 4
+    assert q.qspec_draft_sample_workspace_bytes(2, 16, 100) == 0 and q.qspec_draft_sample_workspace_bytes(0, 0, 9) == 0
+
+    def call(**kw):
+        a = dict(mode=1, logits=FAKE, B=16, V=128256, ld=4 * 128256, u=FAKE, tok=FAKE, lt=4, ws=FAKE, nbytes=need)
+        a.update(kw)
+        return L.qspec_draft_sample(a["mode"], a["logits"], a["B"], a["V"], a["ld"], a["u"], a["tok"], a["lt"],
+                                    a["ws"], a["nbytes"], None)
+    assert call(mode=3) == ERR_UNSUPPORTED
+    for k in ("logits", "u", "tok"):
+        assert call(**{k: None}) == ERR_NULL, k
+    for kw in (dict(B=0), dict(V=0), dict(ld=128255), dict(lt=0)):
+        assert call(**kw) == ERR_SHAPE, kw
+    assert call(ws=None) == ERR_WS and call(nbytes=need - 1) == ERR_WS
+    assert call(tok=ctypes.c_void_p(0x1002)) == ERR_ALIGN
