@@ -5,7 +5,9 @@ One step = one QSPEC round over the projections of a Llama-3-8B-shaped model (32
 qkv 4096->6144, o 4096->4096, gate+up 4096->2x14336, down 14336->4096, each layer with its
 own shared INT4 group-128 weights: 3.65 GB, far beyond the 256 MB last-level cache), batch B
 (default 16) and gamma = 4:
-  draft   gamma x (per layer and projection: qspec_quantize_act + qspec_gemm_w4a4 at M = B)
+  draft   gamma x (per layer and projection: qspec_quantize_act + qspec_gemm_w4a4 at M = B; then
+          qspec_draft_sample drawing each sequence's draft token from that step's rows of the
+          [B][gamma][V] draft logits, into the draft-token buffer the verification reads)
   verify  per layer and projection: qspec_gemm_w4a16 at M = B (gamma + 1)
   accept  qspec_verify_accept (speculative sampling) over a 128256-word vocabulary
   commit  qspec_kv_overwrite of the accepted rows in a 32-layer x 8-head x 4096 x 128 bf16 cache
@@ -229,6 +231,10 @@ class Round:
             toks = si.draft_tokens_sampled_device(d, seed=s)
             self.logits.append((t, d, toks, si.uniforms_device((B, g), seed=s, device=dev),
                                 si.uniforms_device((B,), seed=100 + s, device=dev)))
+        # the draft-side head's uniforms, [gamma][B] per logit set (one contiguous row per step)
+        self.head_u = [si.uniforms_device((g, B), seed=200 + s, device=dev) for s in range(self.n_logit_sets)]
+        self.ws_head = torch.empty((q.qspec_draft_sample_workspace_bytes(q.QSPEC_SAMPLE, B, VOCAB),),
+                                   dtype=torch.uint8, device=dev)
         self.accept = torch.zeros((B,), dtype=torch.int32, device=dev)
         self.out_tokens = torch.zeros((B, g + 1), dtype=torch.int32, device=dev)
         self.ws = torch.empty((q.qspec_verify_workspace_bytes(q.QSPEC_SAMPLE, B, g, VOCAB),), dtype=torch.uint8,
@@ -262,6 +268,10 @@ class Round:
             for i in range(len(self.projs)):
                 wc, wm = self.weights[l][i]
                 self.q.qspec_gemm_w4a16(self.x_draft[i], wc, wm, self.y_draft[i])
+
+    def draft_head(self, s, j):
+        t, d, toks, u, v = self.logits[s]
+        self.q.qspec_draft_sample(self.q.QSPEC_SAMPLE, d[:, j, :], toks[:, j], self.head_u[s][j], self.ws_head)
 
     def accept_phase(self, s):
         t, d, toks, u, v = self.logits[s]
@@ -303,26 +313,33 @@ def gpu_leg(args):
     torch.cuda.synchronize()
 
     # eager reference outputs, then the captured phases
-    R.quant(); R.draft_gemm(); R.verify_gemm(); R.accept_phase(0); R.commit()
+    R.quant(); R.draft_gemm()
+    for j in range(R.gamma):
+        R.draft_head(0, j)
+    R.verify_gemm(); R.accept_phase(0); R.commit()
     torch.cuda.synchronize()
     ref = (R.y_draft[2].clone(), R.y_verify[3].clone(), R.accept.clone(), R.out_tokens.clone())
     g_quant = capture(R.quant, torch)
     g_draft = capture(R.draft_gemm, torch)
     g_verify = capture(R.verify_gemm, torch)
+    g_head = [[capture(lambda s=s, j=j: R.draft_head(s, j), torch) for j in range(R.gamma)]
+              for s in range(R.n_logit_sets)]
     g_accept = [capture(lambda s=s: R.accept_phase(s), torch) for s in range(R.n_logit_sets)]
     g_commit = capture(R.commit, torch)
 
-    phases = ["quantize_act", "gemm_w4a4", "gemm_w4a16", "verify_accept", "kv_overwrite"]
-    n_ev = R.gamma * 2 + 4
+    phases = ["quantize_act", "gemm_w4a4", "draft_head", "gemm_w4a16", "verify_accept", "kv_overwrite"]
+    n_ev = R.gamma * 3 + 4
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
 
     def step(i, ev):
         k = 0
         if ev: ev[k].record(); k += 1
-        for _ in range(R.gamma):
+        for j in range(R.gamma):
             g_quant.replay()
             if ev: ev[k].record(); k += 1
             g_draft.replay()
+            if ev: ev[k].record(); k += 1
+            g_head[i % R.n_logit_sets][j].replay()
             if ev: ev[k].record(); k += 1
         g_verify.replay()
         if ev: ev[k].record(); k += 1
@@ -356,6 +373,7 @@ def gpu_leg(args):
         for _ in range(R.gamma):
             ph["quantize_act"] += ev[k].elapsed_time(ev[k + 1]); k += 1
             ph["gemm_w4a4"] += ev[k].elapsed_time(ev[k + 1]); k += 1
+            ph["draft_head"] += ev[k].elapsed_time(ev[k + 1]); k += 1
         ph["gemm_w4a16"] += ev[k].elapsed_time(ev[k + 1]); k += 1
         ph["verify_accept"] += ev[k].elapsed_time(ev[k + 1]); k += 1
         ph["kv_overwrite"] += ev[k].elapsed_time(ev[k + 1]); k += 1
@@ -395,7 +413,7 @@ def round_model(R, ph, torch):
         R.accept_phase(s_)
         counts.append(R.accept.cpu().clone())
     e_l = float(torch.cat(counts).double().mean()) + 1.0
-    t_draft = ph["quantize_act"] + ph["gemm_w4a4"]
+    t_draft = ph["quantize_act"] + ph["gemm_w4a4"] + ph["draft_head"]
     t_verify = ph["gemm_w4a16"]
     t_over = ph["verify_accept"] + ph["kv_overwrite"]
     t_round = t_draft + t_verify + t_over
@@ -529,9 +547,15 @@ def cpu_leg(args):
         parts[name] = (t1 - t0, t2 - t1, t3 - t2)
         est += L * (g * ((t1 - t0) + frac * (t2 - t1)) + frac * (t3 - t2))
     t, d = si.logits(B, g, VOCAB, seed=0)
-    toks = si.draft_tokens_sampled(d, seed=0)
-    u, v = si.uniforms((B, g), 0), si.uniforms((B,), 1)
+    hu = si.uniforms((g, B), 2)
+    toks = np.empty((B, g), np.int32)
     t0 = time.perf_counter()
+    for j in range(g):              # the draft-side head: verification with gamma = 0 on step j's rows
+        _, o, _ = oracle.verify_sample(d[:, j:j + 1, :], np.zeros((B, 0, VOCAB), np.float32),
+                                       np.zeros((B, 0), np.int32), np.zeros((B, 0), np.float32), hu[j],
+                                       with_diag=False)
+        toks[:, j] = o[:, 0]
+    u, v = si.uniforms((B, g), 0), si.uniforms((B,), 1)
     acc, _, _ = oracle.verify_sample(t, d, toks, u, v, with_diag=False)
     est += time.perf_counter() - t0
     # KV: one layer of the cache at a short context (the copy cost does not depend on T)
@@ -548,7 +572,8 @@ def cpu_leg(args):
         "cores": 1,
         "kind": "oracle",
         "sample": (f"one layer of each projection on 1/{frac} of its columns (draft quantize + W4A4 at M={B}, "
-                   f"verify W4A16 at M={B * (g + 1)}), full verify_accept (sampling, B={B}, V={VOCAB}), "
+                   f"verify W4A16 at M={B * (g + 1)}), {g} full draft heads and the full verify_accept (sampling, "
+                   f"B={B}, V={VOCAB}), "
                    f"one KV layer; scaled x{L} layers, x{g} draft steps, x{frac} columns; "
                    f"estimated round {est:.1f} s from {spent:.1f} s of single-threaded CPU work"),
     }
