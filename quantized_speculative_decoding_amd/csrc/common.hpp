@@ -110,17 +110,18 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
     return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
 }
 
-// Decode kernels (M <= 16): column tiles per workgroup (nt) and K-splitting waves (kw), a
-// function of (K, N) only, so the reduction order is too.  Chosen from measured sweeps over the
-// Llama-3-8B / Qwen2.5-7B projection shapes: about 500 - 2000 waves in flight, wider workgroups
-// rather than more K splits, two groups per wave at least.
+// Decode kernels (M <= 16), W4A4 and W4A16 alike: column tiles per workgroup (nt) and K-splitting
+// waves (kw), a function of (K, N) only, so the reduction order is too.  Chosen from measured
+// sweeps of every (nt, kw) over the Llama-3-8B / Qwen2.5-7B projection shapes at M = 1, 5, 16:
+// about 500 - 2000 waves in flight, wider workgroups rather than more K splits, two groups per
+// wave at least.
 constexpr int kMaxDecodeWaves = 8;
 
 struct DecodeShape {
     int nt, kw;
 };
 
-__host__ __device__ inline DecodeShape decode_shape(int K, int N, bool w4a4) {
+__host__ __device__ inline DecodeShape decode_shape(int K, int N) {
     const int T = N / 16, G = K / kGroup;
     DecodeShape d;
     if (T >= 4096) {
@@ -130,7 +131,7 @@ __host__ __device__ inline DecodeShape decode_shape(int K, int N, bool w4a4) {
     } else if (T >= 384) {
         d = {2, 4};
     } else {
-        d = {1, w4a4 ? 4 : 2};
+        d = {1, 4};
     }
     while (d.kw > 1 && 2 * d.kw > G) d.kw >>= 1;
     return d;

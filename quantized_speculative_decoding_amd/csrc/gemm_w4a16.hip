@@ -584,7 +584,7 @@ k_w4a16_splitk_reduce(const float *__restrict__ partials, int S, size_t MN, void
 template <int NT, int U>
 static hipError_t launch_decode(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K, int N,
                                 void *y, int y_f32, hipStream_t st) {
-    const int kw = decode_shape(K, N, false).kw;
+    const int kw = decode_shape(K, N).kw;
     const size_t lds = (size_t)kw * NT * 256 * sizeof(float);
     hipLaunchKernelGGL((k_w4a16_decode<NT, U>), dim3((N / 16 + NT - 1) / NT), dim3(64 * kw), lds, st, x, M, codes,
                        meta, K, N, y, y_f32, kw);
@@ -646,7 +646,7 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, con
     // Batch tiers, each with one reduction order for all its M: M <= 16 (decode), 16 < M <= 80
     // (shared activations, K parts, optional split-K), M > 80 (shared activations, row blocks).
     if (M <= 16) {
-        const int nt = decode_shape(K, N, false).nt;
+        const int nt = decode_shape(K, N).nt;
         if (nt == 4) return launch_decode<4, 4>(x, M, codes, meta, K, N, y, y_f32, st);
         if (nt == 2) return launch_decode<2, 4>(x, M, codes, meta, K, N, y, y_f32, st);
         return launch_decode<1, 4>(x, M, codes, meta, K, N, y, y_f32, st);

@@ -629,7 +629,7 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M
                             hipStream_t st) {
     // Batch tiers with one reduction order each: M <= 16 and 16 < M <= 64.
     if (M <= 16) {
-        const DecodeShape d = decode_shape(K, N, true);
+        const DecodeShape d = decode_shape(K, N);
         if (d.nt == 4)
             return launch_decode4<4, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, d.kw, st);
         if (d.nt == 2)

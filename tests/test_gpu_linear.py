@@ -221,8 +221,9 @@ def test_w4a4_small_exact_dots_and_outputs(M, K, N):
 
 # Decode-tier workgroup shapes (M <= 16): 2 column tiles per workgroup from 1024 tiles on, 4 from
 # 4096 on, with a ragged last workgroup (odd tile counts), and 1 tile with several K-splitting
-# waves; every output element is compared.
-DECODE_TILINGS = [(16, 256, 16 * 1025), (3, 128, 16 * 4097), (9, 1024, 16 * 385), (1, 512, 16 * 257)]
+# waves (2 at K = 512, 4 from K = 1024 on); every output element is compared.
+DECODE_TILINGS = [(16, 256, 16 * 1025), (3, 128, 16 * 4097), (9, 1024, 16 * 385), (1, 512, 16 * 257),
+                  (5, 1024, 16 * 257)]
 
 
 @pytest.mark.parametrize("M,K,N", DECODE_TILINGS)
