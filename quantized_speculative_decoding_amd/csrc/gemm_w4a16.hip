@@ -122,7 +122,7 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
     const rsrc_t xr = make_rsrc(x + (size_t)g0 * kGroup, (uint32_t)(((size_t)M * K - (size_t)g0 * kGroup) * 2));
     const uint32_t xoff = (uint32_t)(min(col, M - 1) * K + kq * 32) * 2;
 
-    // Group i of this wave; refills past the end re-read the first group (long since arrived).
+    // Group i of this wave; prologue loads past a range shorter than the ring re-read its first group.
     auto load = [&](W16DStage<NT> &st, int i) {
         const uint32_t g = (uint32_t)(i < ng ? i : 0);
 #pragma unroll
@@ -159,8 +159,10 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
         load(st[u], u);
         __builtin_amdgcn_sched_barrier(0);
     }
-    const int nfull = ng - ng % U;
-    for (int base = 0; base < nfull; base += U) {
+    // Steady passes refill every slot with a group of this wave (no branch around a load); the
+    // last pass refills only the slots whose group exists, and the drain consumes them.
+    int base = 0;
+    for (; base + 2 * U <= ng; base += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             compute(st[u]);
@@ -169,8 +171,14 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
         }
     }
 #pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (base + u < ng) compute(st[u]);
+        if (base + u + U < ng) load(st[u], base + u + U);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
     for (int u = 0; u < U - 1; ++u)
-        if (nfull + u < ng) compute(st[u]);
+        if (base + U + u < ng) compute(st[u]);
 
     // Fixed-order reduction of the kw wave partials: every wave parks its NT tiles in LDS (lane
     // layout of the MFMA output), one barrier, then each thread sums 8 consecutive columns of one

@@ -163,18 +163,26 @@ k_w4a4_skinny(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
         load(st[u], min(u, ng - 1));
         __builtin_amdgcn_sched_barrier(0);
     }
-    const int nfull = ng - ng % U;
-    for (int base = 0; base < nfull; base += U) {
+    // Steady passes refill every slot with a real group; the last pass refills only the slots
+    // whose group exists, and the drain consumes them.
+    int base = 0;
+    for (; base + 2 * U <= ng; base += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             compute(st[u], base + u);
-            load(st[u], min(base + u + U, ng - 1));
+            load(st[u], base + u + U);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (base + u < ng) compute(st[u], base + u);
+        if (base + u + U < ng) load(st[u], base + u + U);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
     for (int u = 0; u < U - 1; ++u)
-        if (nfull + u < ng) compute(st[u], nfull + u);
+        if (base + U + u < ng) compute(st[u], base + U + u);
 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -266,8 +274,8 @@ k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
 
     for (int c0 = 0; c0 < ng; c0 += sch) {
         const int cn = min(sch, ng - c0);
-        // Group c0 + i of this wave; refills past the chunk re-read its first group (long since
-        // arrived).
+        // Group c0 + i of this wave; prologue loads past a chunk shorter than the ring re-read its
+        // first group.
         auto load = [&](W4DStage<NT> &st, int i) {
             const uint32_t g = (uint32_t)(c0 + (i < cn ? i : 0));
 #pragma unroll
@@ -328,8 +336,11 @@ k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
             load(st[u], u);
             __builtin_amdgcn_sched_barrier(0);
         }
-        const int nfull = cn - cn % U;
-        for (int base = 0; base < nfull; base += U) {
+        // Steady passes refill every slot with a group of the chunk (no branch around a load); the
+        // last pass refills only the slots whose group exists, and the drain consumes them, so no
+        // wave waits at its end on loads of groups it never uses.
+        int base = 0;
+        for (; base + 2 * U <= cn; base += U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 compute(st[u], base + u);
@@ -338,8 +349,14 @@ k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
             }
         }
 #pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (base + u < cn) compute(st[u], base + u);
+            if (base + u + U < cn) load(st[u], base + u + U);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
         for (int u = 0; u < U - 1; ++u)
-            if (nfull + u < cn) compute(st[u], nfull + u);
+            if (base + U + u < cn) compute(st[u], base + U + u);
     }
 
     // Fixed-order reduction of the kw wave partials: every wave parks its NT tiles in LDS (lane

@@ -193,8 +193,11 @@ def test_w4a16_full_shapes_sampled_columns(name, K, N, M):
 
 # ---------------------------------------------------------------- W4A4
 
+# (24, 5120, 64) and (40, 2944, 48): 10 and 5 - 6 groups per wave in the 16 < M <= 64 kernel, so its
+# ring runs steady passes and a last pass with only some slots refilled.
 SMALL_W4A4 = [(1, 128, 16), (1, 512, 512), (4, 384, 48), (16, 640, 112), (5, 256, 16),
-              (17, 384, 48), (33, 256, 32), (64, 128, 48), (65, 256, 144), (256, 512, 272), (100, 384, 16)]
+              (17, 384, 48), (33, 256, 32), (64, 128, 48), (65, 256, 144), (256, 512, 272), (100, 384, 16),
+              (24, 5120, 64), (40, 2944, 48)]
 
 
 @pytest.mark.parametrize("M,K,N", SMALL_W4A4)
@@ -221,9 +224,10 @@ def test_w4a4_small_exact_dots_and_outputs(M, K, N):
 
 # Decode-tier workgroup shapes (M <= 16): 2 column tiles per workgroup from 1024 tiles on, 4 from
 # 4096 on, with a ragged last workgroup (odd tile counts), and 1 tile with several K-splitting
-# waves (2 at K = 512, 4 from K = 1024 on); every output element is compared.
+# waves (2 at K = 512, 4 from K = 1024 on); every output element is compared.  K = 3840 gives the
+# 4 waves 7 or 8 groups: a full ring pass, and a last pass that refills only 3 of its 4 slots.
 DECODE_TILINGS = [(16, 256, 16 * 1025), (3, 128, 16 * 4097), (9, 1024, 16 * 385), (1, 512, 16 * 257),
-                  (5, 1024, 16 * 257)]
+                  (5, 1024, 16 * 257), (7, 3840, 16 * 257)]
 
 
 @pytest.mark.parametrize("M,K,N", DECODE_TILINGS)
