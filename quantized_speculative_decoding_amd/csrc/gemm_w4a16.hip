@@ -302,19 +302,24 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     // Activation staging: load q = cw * NFW + u of a K part reads rows 4 q .. 4 q + 3 of the
     // group, 16 lanes per row (row-contiguous: 8 cache lines per load).  The 16 bytes of (row, 8-k
     // chunk c) are element (row % 16, k = 8 c) of fragment f = 4 (row / 16) + c % 4, i.e. lane
-    // l = row % 16 + 16 (c / 4) of it; they are stored at slot l ^ c of the fragment's 1 KB block.
-    // The swizzle keeps the 16 lanes of a row on distinct banks, and a reader lane l of fragment
-    // (row tile, 32-k step j) finds its data at slot l ^ (4 (l / 16) + j).  Rows past the block
-    // read its last row (their MFMA rows are discarded).
+    // l = row % 16 + 16 (c / 4) of it; they are stored at slot l ^ (c / 4) ^ 4 (c % 4) of the
+    // fragment's 1 KB block, so a reader lane l of fragment (row tile, 32-k step j) finds its data
+    // at slot l ^ (l / 16) ^ 4 j.  Lane p of a row loads chunk c = 4 (p % 4) + p / 4, which makes
+    // the low four slot bits of a staging write p ^ row.  Measured on gfx950 with 16-byte LDS
+    // accesses: reads whose lane-dependent XOR reaches slot bit 3 (such as l ^ 4 (l / 16)) and
+    // writes whose low slot bits are not the lane XOR a uniform value run 15 - 18% slower; this
+    // layout has neither.  Rows past the block read its last row (their MFMA rows are discarded).
     uint32_t xoff[NFW], xslot[NFW];
 #pragma unroll
     for (int u = 0; u < NFW; ++u) {
         const int row = 4 * (cw * NFW + u) + (lane >> 4);
-        const int c = lane & 15;
+        const int p = lane & 15;
+        const int c = ((p & 3) << 2) | (p >> 2);
         xoff[u] = (uint32_t)(min(row, Mb - 1) * K + c * 8) * 2;
-        xslot[u] = (uint32_t)((4 * (row >> 4) + (c & 3)) * 64 + (((row & 15) + 16 * (c >> 2)) ^ c));
+        xslot[u] = (uint32_t)((4 * (row >> 4) + (c & 3)) * 64 +
+                              (((row & 15) + 16 * (c >> 2)) ^ (c >> 2) ^ (4 * (c & 3))));
     }
-    const int rslot = lane ^ (4 * kq);   // reader slot, before the 32-k step j
+    const int rslot = lane ^ kq;   // reader slot, before the 32-k step j
 
     struct Stage {
         uint4 w[NT];
@@ -376,7 +381,7 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
                 bf16x8_t av[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
-                    av[mt] = __builtin_bit_cast(bf16x8_t, abuf(kh, buf)[(mt * 4 + j) * 64 + (rslot ^ j)]);
+                    av[mt] = __builtin_bit_cast(bf16x8_t, abuf(kh, buf)[(mt * 4 + j) * 64 + (rslot ^ (4 * j))]);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     const uint32_t word = j == 0 ? st.w[nt].x : j == 1 ? st.w[nt].y : j == 2 ? st.w[nt].z : st.w[nt].w;
@@ -400,7 +405,7 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
             for (int nt = 0; nt < NT; ++nt) bv[nt] = bq[nt];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                av[mt] = __builtin_bit_cast(bf16x8_t, abuf(kh, buf)[(mt * 4 + j) * 64 + (rslot ^ j)]);
+                av[mt] = __builtin_bit_cast(bf16x8_t, abuf(kh, buf)[(mt * 4 + j) * 64 + (rslot ^ (4 * j))]);
             if (j < 3) {
                 dq_step(st, dq, j + 1, bq);
             } else {
