@@ -11,10 +11,13 @@
 //   sampling: k_softmax_partial (per row chunk: chunk max and sum of exp(l - max) in fp64)
 //             -> k_sample_accept (one wave per sequence: lanes combine the rows' chunk statistics
 //                and test the candidates u < p(d)/q(d) in fp64; a ballot finds the first rejection)
-//             -> k_residual_partial (per chunk of the last row: mass of max(0, p - q), or of p)
+//             -> k_residual_partial (per RCHUNK-logit chunk of the last row: mass of max(0, p - q),
+//                or of p)
 //             -> k_residual_pick (per sequence: locate the chunk, its segment and the token; the
 //                residual masses are evaluated in parallel, the running sums stay sequential)
-// Softmax normalizers, ratios and running sums are fp64; the exponentials are fp64 as well.
+// Softmax normalizers, ratios and running sums are fp64; the exponentials are fp64 as well.  The
+// residual stages use shorter chunks than the softmax statistics: they touch two rows per
+// sequence instead of 2 gamma + 1, so 8192-logit chunks left most of the chip idle.
 #include <float.h>
 #include <limits.h>
 
@@ -23,14 +26,16 @@
 
 namespace qspec {
 
-constexpr int VCHUNK = 8192;     // logits per workgroup chunk
+constexpr int VCHUNK = 8192;     // logits per workgroup chunk (argmax and softmax statistics)
+constexpr int RCHUNK = 2048;     // logits per workgroup chunk of the residual stages
 constexpr int VT = 256;          // threads per workgroup
-constexpr int VSEG = VCHUNK / VT;
+constexpr int RSEG = RCHUNK / VT;
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct VerifyLayout {
     int C;            // chunks per row
+    int CR;           // residual chunks per row
     size_t gval, gidx;                                   // greedy partials
     size_t pmax, psum, rowM, rowS, accA, resid, pmass;   // sampling partials
     size_t total;
@@ -39,6 +44,7 @@ struct VerifyLayout {
 static VerifyLayout verify_layout(int mode, int B, int gamma, int V) {
     VerifyLayout L = {};
     L.C = (V + VCHUNK - 1) / VCHUNK;
+    L.CR = (V + RCHUNK - 1) / RCHUNK;
     const size_t Rt = (size_t)B * (gamma + 1);
     size_t off = 0;
     if (mode == 0) {
@@ -51,8 +57,8 @@ static VerifyLayout verify_layout(int mode, int B, int gamma, int V) {
         L.rowM = off; off = align256(off + R * sizeof(float));
         L.rowS = off; off = align256(off + R * sizeof(double));
         L.accA = off; off = align256(off + (size_t)B * sizeof(int));
-        L.resid = off; off = align256(off + (size_t)B * L.C * sizeof(double));
-        L.pmass = off; off = align256(off + (size_t)B * L.C * sizeof(double));
+        L.resid = off; off = align256(off + (size_t)B * L.CR * sizeof(double));
+        L.pmass = off; off = align256(off + (size_t)B * L.CR * sizeof(double));
     }
     L.total = off;
     return L;
@@ -257,15 +263,24 @@ k_sample_accept(const float *__restrict__ target, size_t ldt, const float *__res
         if (j != A) out[(size_t)b * ldo + j] = j < A ? tokens[(size_t)b * gamma + j] : -1;
 }
 
-// Residual (or target) mass at one logit of the last committed row.
+// Residual (or target) mass at one logit of the last committed row.  The probabilities multiply
+// by the reciprocals of the row normalizers (one rounding more than a division, about 1e-16
+// relative, far inside the draw's near-tie band).  Contraction is off: fusing the draft product
+// into the subtraction would leave the rounding error of p where p == q must give exactly 0
+// (equal rows have zero residual mass and fall back to p).
 struct ResidRow {
     const float *t;  // target row A
     const float *d;  // draft row A, or nullptr for the extra token (A == gamma)
-    double Mt, St, Md, Sd;
-    __device__ __forceinline__ double p(int x) const { return exp((double)t[x] - Mt) / St; }
+    double Mt, iSt, Md, iSd;
+    __device__ __forceinline__ double p(int x) const {
+#pragma clang fp contract(off)
+        return exp((double)t[x] - Mt) * iSt;
+    }
     __device__ __forceinline__ double r_of(int x, double pv) const {
+#pragma clang fp contract(off)
         if (!d) return pv;
-        const double dv = pv - exp((double)d[x] - Md) / Sd;
+        const double qv = exp((double)d[x] - Md) * iSd;
+        const double dv = pv - qv;
         return dv > 0.0 ? dv : 0.0;
     }
     __device__ __forceinline__ double r(int x) const { return r_of(x, p(x)); }
@@ -279,16 +294,16 @@ __device__ __forceinline__ ResidRow resid_row(const float *target, size_t ldt, c
     ResidRow R;
     R.t = target + (size_t)rt * ldt;
     R.Mt = rowM[rt];
-    R.St = rowS[rt];
+    R.iSt = 1.0 / rowS[rt];
     if (A < gamma) {
         const long long rd = Rt + (long long)b * gamma + A;
         R.d = draft + (size_t)(rd - Rt) * V;
         R.Md = rowM[rd];
-        R.Sd = rowS[rd];
+        R.iSd = 1.0 / rowS[rd];
     } else {
         R.d = nullptr;
         R.Md = 0.0;
-        R.Sd = 1.0;
+        R.iSd = 1.0;
     }
     return R;
 }
@@ -297,9 +312,9 @@ __global__ void __launch_bounds__(VT)
 k_residual_partial(const float *__restrict__ target, size_t ldt, const float *__restrict__ draft, int B,
                    int gamma, int V, int C, const float *__restrict__ rowM, const double *__restrict__ rowS,
                    const int *__restrict__ accA, double *__restrict__ resid, double *__restrict__ pmass) {
-    const int b = blockIdx.x / C, c = blockIdx.x % C;
+    const int b = blockIdx.x / C, c = blockIdx.x % C;   // C: residual chunks per row
     const ResidRow R = resid_row(target, ldt, draft, B, gamma, V, b, accA[b], rowM, rowS);
-    const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
+    const int lo = c * RCHUNK, hi = min(V, lo + RCHUNK);
     double sr = 0.0, sp = 0.0;
     for (int x = lo + (int)threadIdx.x; x < hi; x += VT) {
         const double pv = R.p(x);
@@ -360,8 +375,8 @@ k_residual_pick(const float *__restrict__ target, size_t ldt, const float *__res
     }
     __syncthreads();
     if (s_usep) R.d = nullptr;
-    const int lo = s_chunk * VCHUNK, hi = min(V, lo + VCHUNK);
-    const int x0 = lo + (int)threadIdx.x * VSEG, x1 = min(hi, x0 + VSEG);
+    const int lo = s_chunk * RCHUNK, hi = min(V, lo + RCHUNK);
+    const int x0 = lo + (int)threadIdx.x * RSEG, x1 = min(hi, x0 + RSEG);
     double mine = 0.0;
     for (int x = x0; x < x1; ++x) mine += R.r(x);
     seg[threadIdx.x] = mine;
@@ -391,7 +406,7 @@ k_residual_pick(const float *__restrict__ target, size_t ldt, const float *__res
     const int tsel = s_seg;
     if (tsel >= 0) {
         // the segment's masses in parallel, then the running sum through them in order
-        const int a = lo + tsel * VSEG, e = min(hi, a + VSEG);
+        const int a = lo + tsel * RSEG, e = min(hi, a + RSEG);
         if ((int)threadIdx.x < e - a) seg[threadIdx.x] = R.r(a + (int)threadIdx.x);
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -590,10 +605,10 @@ static hipError_t launch_verify(int mode, const float *target, size_t ldt, const
                        gamma, V, C, vec, pmax, psum);
     hipLaunchKernelGGL(k_sample_accept, dim3(B), dim3(kWave), 0, st, target, ldt, draft, tokens,
                        u_accept, B, gamma, V, C, pmax, psum, rowM, rowS, accA, accept, out, ldo);
-    hipLaunchKernelGGL(k_residual_partial, dim3((unsigned)((long long)B * C)), dim3(VT), 0, st, target, ldt,
-                       draft, B, gamma, V, C, rowM, rowS, accA, resid, pmass);
+    hipLaunchKernelGGL(k_residual_partial, dim3((unsigned)((long long)B * L.CR)), dim3(VT), 0, st, target, ldt,
+                       draft, B, gamma, V, L.CR, rowM, rowS, accA, resid, pmass);
     hipLaunchKernelGGL(k_residual_pick, dim3(B), dim3(VT), 0, st, target, ldt, draft, u_resample, B, gamma, V,
-                       C, rowM, rowS, accA, resid, pmass, out, ldo);
+                       L.CR, rowM, rowS, accA, resid, pmass, out, ldo);
     return hipGetLastError();
 }
 
