@@ -390,6 +390,7 @@ def gpu_leg(args):
     R.speckv_us = speckv_controller_us(R, torch)
     R.attention = attention_us(R, torch)
     R.fp8 = fp8_parent_us(R, torch)
+    R.verify_commit = verify_commit_us(R, torch)
     return R, ph, wall, event_ms
 
 
@@ -478,6 +479,62 @@ def attention_us(R, torch):
         torch.cuda.synchronize()
         res[Q] = a.elapsed_time(b) * 1e3 / 30
         del qd, cache
+    return res
+
+
+def verify_commit_us(R, torch, B=32, gamma=4, sets=4):
+    """Outside the timed round: the verify-and-commit stage at B = 32, gamma = 4 over a
+    128256-word vocabulary (target logits N(0, 3), draft = target + N(0, 0.5)), in greedy mode
+    (argmax-match drafts) and sampling mode (drafts sampled from softmax(draft)): qspec_verify_accept
+    and then qspec_kv_overwrite of the accepted rows into a 32-layer x 32-sequence x 8-head x 4096 x
+    128 bf16 cache, graph-replayed over `sets` logit sets (beyond the last-level cache).  Returns
+    {mode: (accept us, kv us, mean committed rows per sequence)}."""
+    import synthetic_inputs as si
+
+    q, dev, V = R.q, R.accept.device, VOCAB
+    cache = torch.empty((R.L, B, 2, KV_HEADS, CONTEXT, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    stage = torch.randn((R.L, B, 2, KV_HEADS, gamma + 1, HEAD_DIM), device=dev).to(torch.bfloat16)
+    start = torch.from_numpy(si.start_positions(B, CONTEXT, gamma, seed=1)).to(dev)
+    acc = torch.zeros((B,), dtype=torch.int32, device=dev)
+    out = torch.zeros((B, gamma + 1), dtype=torch.int32, device=dev)
+    res = {}
+    for mode, name in ((q.QSPEC_GREEDY, "greedy"), (q.QSPEC_SAMPLE, "sample")):
+        inputs = []
+        for s_ in range(sets):
+            t, d = si.logits_device(B, gamma, V, seed=50 + s_, device=dev)
+            toks = (d.argmax(dim=-1).to(torch.int32) if mode == q.QSPEC_GREEDY
+                    else si.draft_tokens_sampled_device(d, seed=50 + s_))
+            inputs.append((t, d if mode == q.QSPEC_SAMPLE else None, toks,
+                           si.uniforms_device((B, gamma), seed=60 + s_, device=dev),
+                           si.uniforms_device((B,), seed=70 + s_, device=dev)))
+        ws = torch.empty((q.qspec_verify_workspace_bytes(mode, B, gamma, V),), dtype=torch.uint8, device=dev)
+
+        def accept(i):
+            t, d, toks, u, v = inputs[i]
+            q.qspec_verify_accept(mode, t, d, toks, u if d is not None else None, v if d is not None else None,
+                                  acc, out, ws)
+
+        rows = 0.0
+        for i in range(sets):
+            accept(i)
+            rows += float((acc.double() + 1).mean())
+        times = []
+        for fn in (lambda: [accept(i) for i in range(sets)],
+                   lambda: [q.qspec_kv_overwrite(cache, stage, start, acc) for _ in range(sets)]):
+            graph = capture(fn, torch)
+            graph.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(5):
+                graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3 / (5 * sets))
+        res[name] = (times[0], times[1], rows / sets)
+        del inputs, ws
+    del cache, stage
+    torch.cuda.empty_cache()
     return res
 
 
@@ -655,6 +712,18 @@ def main():
             **{f"{k}_hbm_frac": round(v[2] / (v[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 3) for k, v in R.fp8.items()},
             "quantize_act_fp8_us": {k: round(v[1], 2) for k, v in R.fp8.items()},
             "layer_projections_us": round(sum(v[0] + v[1] for k, v in R.fp8.items() if k != "lm_head"), 1)},
+        # outside the timed round: the verify-and-commit stage at B = 32, gamma = 4, V = 128256:
+        # tokens/s = B (gamma + 1) / (T_accept + T_kv); HBM fractions of the algorithmic bytes
+        # (greedy: the B (gamma + 1) target rows; sampling: those and the B gamma draft rows; KV:
+        # each committed row read from the staging rows and written to the cache, all layers)
+        "verify_commit_B32_g4": {
+            name: {"accept_us": round(ta, 2), "kv_us": round(tk, 2), "committed_rows_per_seq": round(rows, 3),
+                   "tokens_per_s": round(32 * 5 / ((ta + tk) * 1e-6), 1),
+                   "accept_hbm_frac": round(4 * 32 * (5 if name == "greedy" else 9) * VOCAB / (ta * 1e-6) / 1e9
+                                            / HBM_PEAK_GBS, 4),
+                   "kv_hbm_frac": round(2 * rows * 32 * args.layers * 2 * KV_HEADS * HEAD_DIM * 2 / (tk * 1e-6) / 1e9
+                                        / HBM_PEAK_GBS, 4)}
+            for name, (ta, tk, rows) in R.verify_commit.items()},
         # verify tokens/s at this gamma as the verify GEMMs alone bound it: B (gamma + 1) tokens per
         # pass over the layers' four projections (W4A16 at M = B (gamma + 1)), whole stack and per layer
         "verify_gemm_tokens_per_s": {"layers_%d" % args.layers: round(B * (g + 1) / (verify_ms / 1e3), 1),

@@ -135,6 +135,23 @@ __device__ __forceinline__ void for_chunk(const float *row, int lo, int hi, bool
     }
 }
 
+// The 32 logits of a full, 16-byte-aligned chunk held by this thread: slot 4 k + e is logit
+// lo + 4 VT k + 4 threadIdx.x + e, the order for_chunk visits them in.  All eight loads are issued
+// before the first is used, so a wave waits on one memory latency instead of eight.
+constexpr int VPT = VCHUNK / VT;
+__device__ __forceinline__ void load_full_chunk(const float *row, int lo, float (&v)[VPT]) {
+    uint4 q[VPT / 4];
+#pragma unroll
+    for (int k = 0; k < VPT / 4; ++k) q[k] = load_stream16(row + lo + 4 * VT * k + 4 * (int)threadIdx.x);
+#pragma unroll
+    for (int k = 0; k < VPT / 4; ++k) {
+        v[4 * k] = __uint_as_float(q[k].x);
+        v[4 * k + 1] = __uint_as_float(q[k].y);
+        v[4 * k + 2] = __uint_as_float(q[k].z);
+        v[4 * k + 3] = __uint_as_float(q[k].w);
+    }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Greedy.
 
@@ -146,9 +163,17 @@ k_argmax_partial(const float *__restrict__ target, size_t ldt, int V, int C, boo
     const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
     ArgMax a = {-INFINITY, INT_MAX};
     // each thread visits increasing x, so keeping strict improvements keeps the lowest index
-    for_chunk(p, lo, hi, vec, [&](int x, float v) {
+    auto visit = [&](int x, float v) {
         if (a.i == INT_MAX || v > a.v) { a.v = v; a.i = x; }
-    });
+    };
+    if (vec && hi - lo == VCHUNK) {
+        float v[VPT];
+        load_full_chunk(p, lo, v);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) visit(lo + 4 * VT * (k / 4) + 4 * (int)threadIdx.x + k % 4, v[k]);
+    } else {
+        for_chunk(p, lo, hi, vec, visit);
+    }
     a = block_argmax(a);
     if (threadIdx.x == 0) {
         gval[blockIdx.x] = a.v;
@@ -199,11 +224,22 @@ k_softmax_partial(const float *__restrict__ target, size_t ldt, const float *__r
     const float *p = logit_row(target, ldt, draft, B, gamma, V, row);
     const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
     float m = -INFINITY;
-    for_chunk(p, lo, hi, vec, [&](int, float v) { m = fmaxf(m, v); });
-    m = block_max(m);
     double s = 0.0;
-    const double md = (double)m;
-    for_chunk(p, lo, hi, vec, [&](int, float v) { s += exp((double)v - md); });
+    if (vec && hi - lo == VCHUNK) {   // one read of the chunk, kept in registers for both passes
+        float v[VPT];
+        load_full_chunk(p, lo, v);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) m = fmaxf(m, v[k]);
+        m = block_max(m);
+        const double md = (double)m;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) s += exp((double)v[k] - md);
+    } else {
+        for_chunk(p, lo, hi, vec, [&](int, float v) { m = fmaxf(m, v); });
+        m = block_max(m);
+        const double md = (double)m;
+        for_chunk(p, lo, hi, vec, [&](int, float v) { s += exp((double)v - md); });
+    }
     s = block_sum(s);
     if (threadIdx.x == 0) {
         pmax[blockIdx.x] = m;
