@@ -248,7 +248,8 @@ int qspec_draft_sample(int32_t mode, const float *logits, int32_t B, int32_t V, 
  * start_pos    [in]     i32 [B]
  * accept_count [in]     i32 [B] (device; e.g. straight from qspec_verify_accept),
  *                       clamped to [0, gamma]; positions outside [0, T) are skipped.
- * Errors: NULL pointer; any size < 1 (gamma < 0); gamma + 1 > T.
+ * Errors: NULL pointer; any size < 1 (gamma < 0); gamma + 1 > T; verify_kv of 2^32
+ * elements or more (QSPEC_ERR_SHAPE).
  */
 int qspec_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const int32_t *start_pos,
                        const int32_t *accept_count, int32_t L, int32_t B, int32_t H, int32_t T,

@@ -1,8 +1,10 @@
 // Replacement of draft KV by verify KV for the committed positions, on gfx950.
 // (QSPEC notes, QSPEC structure: for accepted tokens the W4A4 draft's KV is replaced with the
 //  W4A16 verifier's KV.)  Rows r = 0..A_b of the verifier's gamma+1 rows land at positions
-// start_pos[b] + r; nothing else is written.  One thread per 16-byte vector of a candidate row;
-// the accept count is read on the device, so no host round trip separates this from verify.
+// start_pos[b] + r; nothing else is written.  One thread per 16-byte vector of a candidate row,
+// with 32-bit index arithmetic (the staging rows hold fewer than 2^32 elements, checked at the
+// boundary); the accept count is read on the device, so no host round trip separates this from
+// the verification.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -14,14 +16,14 @@ k_kv_overwrite(uint16_t *__restrict__ cache, const uint16_t *__restrict__ vkv,
                const int32_t *__restrict__ start_pos, const int32_t *__restrict__ accept,
                int B, int H, int T, int D, int gamma, long long total) {
     constexpr int EPV = sizeof(VecT) / sizeof(uint16_t);   // elements per vector
-    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= total) return;
-    const int DV = D / EPV;
-    const int v = (int)(idx % DV);
-    const long long rest = idx / DV;
-    const int r = (int)(rest % (gamma + 1));
-    const long long head = rest / (gamma + 1);             // ((l * B + b) * 2 + kv) * H + h
-    const int b = (int)((head / (2LL * H)) % B);
+    const unsigned idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (unsigned)total) return;
+    const unsigned DV = D / EPV;
+    const unsigned v = idx % DV;
+    const unsigned rest = idx / DV;
+    const int r = (int)(rest % (unsigned)(gamma + 1));
+    const unsigned head = rest / (unsigned)(gamma + 1);   // ((l * B + b) * 2 + kv) * H + h
+    const int b = (int)((head / (2u * H)) % (unsigned)B);
     int A = accept[b];
     A = A < 0 ? 0 : (A > gamma ? gamma : A);
     if (r > A) return;

@@ -149,7 +149,7 @@ QSPEC_EXPORT int qspec_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv,
     if (!cache || !verify_kv || !start_pos || !accept_count) return QSPEC_ERR_NULL;
     if (L < 1 || B < 1 || H < 1 || T < 1 || D < 1 || gamma < 0 || gamma + 1 > T)
         return QSPEC_ERR_SHAPE;
-    if ((long long)L * B * 2 * H * (gamma + 1) * D > kMaxElems) return QSPEC_ERR_SHAPE;
+    if ((long long)L * B * 2 * H * (gamma + 1) * D >= (1LL << 32)) return QSPEC_ERR_SHAPE;   // 32-bit indices
     if (!aligned(cache, 2) || !aligned(verify_kv, 2) || !aligned(start_pos, 4) || !aligned(accept_count, 4))
         return QSPEC_ERR_ALIGN;
     return status_of(qspec::launch_kv_overwrite(cache, verify_kv, start_pos, accept_count, L, B, H, T,

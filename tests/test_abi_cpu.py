@@ -111,7 +111,9 @@ def test_kv_overwrite_validation():
     L = q.lib()
     assert L.qspec_kv_overwrite(None, FAKE, FAKE, FAKE, 1, 1, 1, 8, 8, 2, None) == ERR_NULL
     assert L.qspec_kv_overwrite(FAKE, FAKE, FAKE, None, 1, 1, 1, 8, 8, 2, None) == ERR_NULL
-    for (Lx, B, H, T, D, g) in [(0, 1, 1, 8, 8, 2), (1, 1, 1, 8, 0, 2), (1, 1, 1, 2, 8, 2), (1, 1, 1, 8, 8, -1)]:
+    # the last case: 64 x 1024 x 2 x 64 x 5 x 128 = 5.4e9 staging elements, past the 32-bit indices
+    for (Lx, B, H, T, D, g) in [(0, 1, 1, 8, 8, 2), (1, 1, 1, 8, 0, 2), (1, 1, 1, 2, 8, 2), (1, 1, 1, 8, 8, -1),
+                                (64, 1024, 64, 4096, 128, 4)]:
         assert L.qspec_kv_overwrite(FAKE, FAKE, FAKE, FAKE, Lx, B, H, T, D, g, None) == ERR_SHAPE
 
 
