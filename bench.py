@@ -192,6 +192,9 @@ def parse():
                     help="after the timed region, run one plain device copy of this size (for counter scaling)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output and exit (no GPU needed)")
+    ap.add_argument("--shape-table", metavar="OUT_MD",
+                    help="time every GEMM shape of the workloads (W4A4 and W4A16, graph-replayed, weight copies "
+                         "rotated beyond the last-level cache), write a markdown table to OUT_MD and exit")
     ap.add_argument("--summary-command", default=PROFILE_COMMAND,
                     help="the command that produced the profiles (recorded in the summaries)")
     return ap.parse_args()
@@ -636,10 +639,89 @@ def cpu_leg(args):
     }
 
 
+SHAPE_TABLE_COMMAND = "python3 bench.py --shape-table OUT.md"
+
+
+def shape_table(args):
+    """Per-shape GEMM times: Llama-3-8B projections and the Qwen2.5-7B vocabulary projection at the
+    decode / verify batch sizes, and the Llama-70B-shaped FFN at its large batches.  Each (shape, M)
+    is one graph of launches over rotating weight copies (at least 600 MB, beyond the 256 MB
+    last-level cache), replayed 5 x 5 times; the median per launch is reported with the HBM rate
+    of its algorithmic bytes and, for the large batches, its MFMA rate."""
+    import torch
+
+    import quantized_speculative_decoding_amd as q
+    import synthetic_inputs as si
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shapes = [(f"Llama-3-8B {n}", K, N, (1, 4, 16), (1, 5, 16, 20, 80)) for n, (K, N) in si.LLAMA3_8B_PROJ.items()]
+    shapes.append(("Qwen2.5-7B lm_head (fp32 out)", 3584, 152064, (1, 16), (1, 5, 17, 80)))
+    shapes += [(f"Llama-70B FFN {n}", K, N, (256,), (1280,)) for n, (K, N) in si.LLAMA3_70B_FFN.items()]
+
+    def timed(fn, reps):
+        graph = capture(fn, torch)
+        graph.replay()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(5):
+                graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3 / (5 * reps))
+        return sorted(ts)[2]
+
+    rows = []
+    for name, K, N, m4, m16 in shapes:
+        wc, wm = si.weights_device(K, N, seed=1, device=dev)
+        wbytes = w4_bytes(K, N)
+        R = max(2, int(600e6 // wbytes) + 1)
+        copies = [(wc, wm)] + [(wc.clone(), wm.clone()) for _ in range(R - 1)]
+        out = torch.float32 if "lm_head" in name else torch.bfloat16
+        for kind, Ms in (("W4A4", m4), ("W4A16", m16)):
+            for M in Ms:
+                x = si.activations_device(M, K, seed=3, device=dev)
+                y = torch.empty((M, N), dtype=out, device=dev)
+                if kind == "W4A4":
+                    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+                    sc = torch.empty((M, K // GROUP), dtype=torch.float32, device=dev)
+                    q.qspec_quantize_act(x, codes, sc)
+                    us = timed(lambda: [q.qspec_gemm_w4a4(codes, sc, c, m, y) for c, m in copies], R)
+                    alg = w4a4_alg_bytes(M, K, N) + (2 * M * N if out == torch.float32 else 0)
+                    peak_ops = 5.0e15
+                else:
+                    ws = q.gemm_w4a16_workspace(M, K, N, dev)
+                    us = timed(lambda: [q.qspec_gemm_w4a16(x, c, m, y, ws) for c, m in copies], R)
+                    alg = w4a16_alg_bytes(M, K, N) + (2 * M * N if out == torch.float32 else 0)
+                    peak_ops = 2.5e15
+                tbs = alg / (us * 1e-6) / 1e12
+                ops = 2.0 * M * K * N / (us * 1e-6)
+                rows.append((name, f"{K} -> {N}", kind, M, us, tbs, tbs * 1e3 / HBM_PEAK_GBS, ops / 1e12, ops / peak_ops))
+                print(rows[-1], flush=True)
+        del copies, wc, wm
+        torch.cuda.empty_cache()
+    lines = ["# Per-shape GEMM times on one MI355X (graph-replayed, weight copies rotated beyond the LLC)", "",
+             "Command (from the repository root):", "", "```", SHAPE_TABLE_COMMAND, "```", "",
+             "HBM rate = algorithmic bytes (4-bit codes + per-group fp16 scale and zero, activations in, outputs "
+             "out) / time; its fraction is of 8 TB/s.  Op rate = 2 M K N / time, as a fraction of the dense "
+             "int8 (W4A4, 5.0 POP/s) or bf16 (W4A16, 2.5 PFLOP/s) MFMA peak.", "",
+             "| shape | K -> N | layer | M | us per launch | HBM TB/s | of 8 TB/s | T(FL)OP/s | of MFMA peak |",
+             "|---|---|---|---:|---:|---:|---:|---:|---:|"]
+    for name, kn, kind, M, us, tbs, hf, top, mf in rows:
+        lines.append(f"| {name} | {kn} | {kind} | {M} | {us:.2f} | {tbs:.2f} | {hf:.0%} | {top:.0f} | {mf:.1%} |")
+    open(args.shape_table, "w").write("\n".join(lines) + "\n")
+    print("wrote", args.shape_table)
+
+
 def main():
     args = parse()
     if args.summarize:
         summarize(args)
+        return
+    if args.shape_table:
+        shape_table(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: every box here has one MI355X and this build has no "
