@@ -408,8 +408,12 @@ k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
 constexpr int Q_NT = 2, Q_CW = 4, Q_MT = 4;
 constexpr int Q_TILES = Q_NT * Q_CW;
 
+// Two waves per SIMD (two workgroups per CU) with a 3-deep ring fit 256 registers per lane; the
+// 4-deep ring took 337 (VGPRs and AGPRs) and one wave per SIMD, which measured 28-34% slower on
+// the shapes with enough workgroups to fill the chip twice.  The variant that also stores the
+// exact group dots keeps one wave per SIMD and the 4-deep ring (its extra stores do not fit).
 template <int U, bool DOTS>
-__global__ void __launch_bounds__(Q_CW * 64)
+__global__ void __launch_bounds__(Q_CW * 64) __attribute__((amdgpu_waves_per_eu(DOTS ? 1 : 2)))
 k_w4a4_lds(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, int M,
            const uint8_t *__restrict__ codes, const uint32_t *__restrict__ meta, int K, int N,
            void *__restrict__ y, int y_f32, int32_t *__restrict__ dots, int row_blocks) {
@@ -664,7 +668,7 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M
         hipLaunchKernelGGL((k_w4a4_lds<4, true>), dim3(cbs * rbs), dim3(Q_CW * 64), 0, st, a_codes, a_scales, M, codes,
                            meta, K, N, y, y_f32, group_dots, rbs);
     else
-        hipLaunchKernelGGL((k_w4a4_lds<4, false>), dim3(cbs * rbs), dim3(Q_CW * 64), 0, st, a_codes, a_scales, M, codes,
+        hipLaunchKernelGGL((k_w4a4_lds<3, false>), dim3(cbs * rbs), dim3(Q_CW * 64), 0, st, a_codes, a_scales, M, codes,
                            meta, K, N, y, y_f32, group_dots, rbs);
     return hipGetLastError();
 }
