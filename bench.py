@@ -655,8 +655,10 @@ def shape_table(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    shapes = [(f"Llama-3-8B {n}", K, N, (1, 4, 16), (1, 5, 16, 20, 80)) for n, (K, N) in si.LLAMA3_8B_PROJ.items()]
-    shapes.append(("Qwen2.5-7B lm_head (fp32 out)", 3584, 152064, (1, 16), (1, 5, 17, 80)))
+    shapes = [("512 x 512 layer", 512, 512, (1,), (5,))]
+    shapes += [(f"Llama-3-8B {n}", K, N, (1, 4, 16), (1, 5, 16, 20, 80)) for n, (K, N) in si.LLAMA3_8B_PROJ.items()]
+    shapes += [(f"Qwen2.5-7B {n}", K, N, (1,), (3, 5, 9, 17)) for n, (K, N) in QWEN25_7B.items() if n != "lm_head"]
+    shapes.append(("Qwen2.5-7B lm_head (fp32 out)", 3584, 152064, (1, 16), (1, 3, 5, 9, 17, 80)))
     shapes += [(f"Llama-70B FFN {n}", K, N, (256,), (1280,)) for n, (K, N) in si.LLAMA3_70B_FFN.items()]
 
     def timed(fn, reps):
@@ -673,6 +675,23 @@ def shape_table(args):
             ts.append(a.elapsed_time(b) * 1e3 / (5 * reps))
         return sorted(ts)[2]
 
+    # a read-only streaming reference on this machine: torch's sum over 2 GiB of fp32, timed eagerly
+    # (a multi-block reduction is kept out of graph capture); median of 5 x 5 calls
+    big = torch.ones((1 << 29,), dtype=torch.float32, device=dev)
+    torch.sum(big)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            torch.sum(big)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / 5)
+    read_tbs = big.numel() * 4 / (sorted(ts)[2] * 1e-6) / 1e12
+    del big
+    torch.cuda.empty_cache()
     rows = []
     for name, K, N, m4, m16 in shapes:
         wc, wm = si.weights_device(K, N, seed=1, device=dev)
@@ -707,6 +726,8 @@ def shape_table(args):
              "HBM rate = algorithmic bytes (4-bit codes + per-group fp16 scale and zero, activations in, outputs "
              "out) / time; its fraction is of 8 TB/s.  Op rate = 2 M K N / time, as a fraction of the dense "
              "int8 (W4A4, 5.0 POP/s) or bf16 (W4A16, 2.5 PFLOP/s) MFMA peak.", "",
+             f"Read-only reference on the same box: torch.sum over 2 GiB of fp32 streams at {read_tbs:.2f} TB/s "
+             f"({read_tbs * 1e3 / HBM_PEAK_GBS:.0%} of 8 TB/s).", "",
              "| shape | K -> N | layer | M | us per launch | HBM TB/s | of 8 TB/s | T(FL)OP/s | of MFMA peak |",
              "|---|---|---|---:|---:|---:|---:|---:|---:|"]
     for name, kn, kind, M, us, tbs, hf, top, mf in rows:

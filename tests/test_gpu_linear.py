@@ -226,8 +226,9 @@ def test_w4a4_small_exact_dots_and_outputs(M, K, N):
 # 4096 on, with a ragged last workgroup (odd tile counts), and 1 tile with several K-splitting
 # waves (2 at K = 512, 4 from K = 1024 on); every output element is compared.  K = 3840 gives the
 # 4 waves 7 or 8 groups: a full ring pass, and a last pass that refills only 3 of its 4 slots.
+# 2101 tiles: 2 tiles per workgroup over 2 K-splitting waves (more workgroups than SIMDs).
 DECODE_TILINGS = [(16, 256, 16 * 1025), (3, 128, 16 * 4097), (9, 1024, 16 * 385), (1, 512, 16 * 257),
-                  (5, 1024, 16 * 257), (7, 3840, 16 * 257)]
+                  (5, 1024, 16 * 257), (7, 3840, 16 * 257), (5, 512, 16 * 2101)]
 
 
 @pytest.mark.parametrize("M,K,N", DECODE_TILINGS)
