@@ -35,6 +35,7 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct VerifyLayout {
     int C;            // chunks per row
+    int GCH;          // logits per greedy argmax chunk
     int CR;           // residual chunks per row
     size_t gval, gidx;                                   // greedy partials
     size_t pmax, psum, rowM, rowS, accA, resid, pmass;   // sampling partials
@@ -48,6 +49,9 @@ static VerifyLayout verify_layout(int mode, int B, int gamma, int V) {
     const size_t Rt = (size_t)B * (gamma + 1);
     size_t off = 0;
     if (mode == 0) {
+        const size_t wide = ((size_t)V + 2 * VCHUNK - 1) / (2 * VCHUNK);
+        L.GCH = Rt * wide >= 1024 ? 2 * VCHUNK : VCHUNK;
+        L.C = (V + L.GCH - 1) / L.GCH;
         L.gval = off; off = align256(off + Rt * L.C * sizeof(float));
         L.gidx = off; off = align256(off + Rt * L.C * sizeof(int));
     } else {
@@ -135,16 +139,17 @@ __device__ __forceinline__ void for_chunk(const float *row, int lo, int hi, bool
     }
 }
 
-// The 32 logits of a full, 16-byte-aligned chunk held by this thread: slot 4 k + e is logit
-// lo + 4 VT k + 4 threadIdx.x + e, the order for_chunk visits them in.  All eight loads are issued
-// before the first is used, so a wave waits on one memory latency instead of eight.
+// The N logits of a full, 16-byte-aligned chunk of N VT logits held by this thread: slot 4 k + e
+// is logit lo + 4 VT k + 4 threadIdx.x + e, the order for_chunk visits them in.  All N / 4 loads
+// are issued before the first is used, so a wave waits on one memory latency instead of N / 4.
 constexpr int VPT = VCHUNK / VT;
-__device__ __forceinline__ void load_full_chunk(const float *row, int lo, float (&v)[VPT]) {
-    uint4 q[VPT / 4];
+template <int N>
+__device__ __forceinline__ void load_full_chunk(const float *row, int lo, float (&v)[N]) {
+    uint4 q[N / 4];
 #pragma unroll
-    for (int k = 0; k < VPT / 4; ++k) q[k] = load_stream16(row + lo + 4 * VT * k + 4 * (int)threadIdx.x);
+    for (int k = 0; k < N / 4; ++k) q[k] = load_stream16(row + lo + 4 * VT * k + 4 * (int)threadIdx.x);
 #pragma unroll
-    for (int k = 0; k < VPT / 4; ++k) {
+    for (int k = 0; k < N / 4; ++k) {
         v[4 * k] = __uint_as_float(q[k].x);
         v[4 * k + 1] = __uint_as_float(q[k].y);
         v[4 * k + 2] = __uint_as_float(q[k].z);
@@ -155,22 +160,26 @@ __device__ __forceinline__ void load_full_chunk(const float *row, int lo, float 
 // ---------------------------------------------------------------------------------------------
 // Greedy.
 
+// CH logits per workgroup: 2 VCHUNK when the rows give at least 1024 such workgroups (one
+// generation on the chip, twice the bytes in flight per wave), else VCHUNK.
+template <int CH>
 __global__ void __launch_bounds__(VT)
 k_argmax_partial(const float *__restrict__ target, size_t ldt, int V, int C, bool vec, float *__restrict__ gval,
                  int *__restrict__ gidx) {
+    constexpr int PT = CH / VT;
     const int row = blockIdx.x / C, c = blockIdx.x % C;
     const float *p = target + (size_t)row * ldt;
-    const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
+    const int lo = c * CH, hi = min(V, lo + CH);
     ArgMax a = {-INFINITY, INT_MAX};
     // each thread visits increasing x, so keeping strict improvements keeps the lowest index
     auto visit = [&](int x, float v) {
         if (a.i == INT_MAX || v > a.v) { a.v = v; a.i = x; }
     };
-    if (vec && hi - lo == VCHUNK) {
-        float v[VPT];
+    if (vec && hi - lo == CH) {
+        float v[PT];
         load_full_chunk(p, lo, v);
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) visit(lo + 4 * VT * (k / 4) + 4 * (int)threadIdx.x + k % 4, v[k]);
+        for (int k = 0; k < PT; ++k) visit(lo + 4 * VT * (k / 4) + 4 * (int)threadIdx.x + k % 4, v[k]);
     } else {
         for_chunk(p, lo, hi, vec, visit);
     }
@@ -622,8 +631,12 @@ static hipError_t launch_verify(int mode, const float *target, size_t ldt, const
     if (mode == 0) {
         float *gval = (float *)(w + L.gval);
         int *gidx = (int *)(w + L.gidx);
-        hipLaunchKernelGGL(k_argmax_partial, dim3((unsigned)(Rt * C)), dim3(VT), 0, st, target, ldt, V, C,
-                           vec_t, gval, gidx);
+        if (L.GCH == 2 * VCHUNK)
+            hipLaunchKernelGGL(k_argmax_partial<2 * VCHUNK>, dim3((unsigned)(Rt * C)), dim3(VT), 0, st, target, ldt, V,
+                               C, vec_t, gval, gidx);
+        else
+            hipLaunchKernelGGL(k_argmax_partial<VCHUNK>, dim3((unsigned)(Rt * C)), dim3(VT), 0, st, target, ldt, V, C,
+                               vec_t, gval, gidx);
         hipLaunchKernelGGL(k_greedy_accept, dim3((B + 63) / 64), dim3(64), 0, st, gval, gidx, C, tokens,
                            B, gamma, V, accept, out, ldo);
         return hipGetLastError();

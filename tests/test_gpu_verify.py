@@ -61,6 +61,29 @@ def test_greedy_ties_across_chunks_and_invalid_tokens():
     assert acc.tolist() == [3, 3, 0, 0]          # row 0 matches at 9000, 5 (lowest tie), 9000
 
 
+def test_greedy_wide_chunks_ties():
+    """1024 target rows of 16400 logits take the 16384-logit argmax chunks: ties across that
+    boundary resolve to the lowest index, and the 16-logit ragged chunk is searched too."""
+    B, gamma, V = 256, 3, 16400
+    note(f"verify_accept greedy wide chunks B={B} gamma={gamma} V={V}")
+    t, d = si.logits(B, gamma, V, seed=77)
+    top = np.float32(100.0)
+    t[0, :, 100] = top
+    t[0, :, 16390] = top                          # tie across the chunk boundary: 100 wins
+    t[1, :, 16399] = top                          # maximum in the ragged chunk
+    t[2, :, 16383] = top
+    t[2, :, 16384] = top                          # adjacent tie on the boundary: 16383 wins
+    toks = si.draft_tokens_greedy(d)
+    toks[0, :] = 100
+    toks[1, :] = 16399
+    toks[2, :] = 16383
+    acc, out = run_verify(q.QSPEC_GREEDY, t, d, toks, None, None)
+    oa, oo = oracle.verify_greedy(t, toks)
+    assert np.array_equal(acc, oa) and np.array_equal(out, oo)
+    assert acc[:3].tolist() == [gamma, gamma, gamma]
+    assert out[0, gamma] == 100 and out[1, gamma] == 16399 and out[2, gamma] == 16383
+
+
 def _compare_sampling(t, d, toks, u, v):
     acc, out = run_verify(q.QSPEC_SAMPLE, t, d, toks, u, v)
     oa, oo, diag = oracle.verify_sample(t, d, toks, u, v)
