@@ -412,12 +412,13 @@ constexpr int Q_TILES = Q_NT * Q_CW;
 // 4-deep ring took 337 (VGPRs and AGPRs) and one wave per SIMD, which measured 28-34% slower on
 // the shapes with enough workgroups to fill the chip twice.  The variant that also stores the
 // exact group dots keeps one wave per SIMD and the 4-deep ring (its extra stores do not fit).
-template <int U, bool DOTS>
+template <int U, bool DOTS, int NT>
 __global__ void __launch_bounds__(Q_CW * 64) __attribute__((amdgpu_waves_per_eu(DOTS ? 1 : 2)))
 k_w4a4_lds(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scales, int M,
            const uint8_t *__restrict__ codes, const uint32_t *__restrict__ meta, int K, int N,
            void *__restrict__ y, int y_f32, int32_t *__restrict__ dots, int row_blocks) {
-    constexpr int NT = Q_NT, MT = Q_MT, CW = Q_CW;
+    constexpr int MT = Q_MT, CW = Q_CW;
+    constexpr int TILES = NT * CW;          // column tiles per workgroup
     constexpr int THREADS = CW * 64;
     constexpr int NFW = MT / CW;            // activation row tiles staged per wave
     static_assert(MT % CW == 0, "row tiles per wave");
@@ -436,7 +437,7 @@ k_w4a4_lds(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scal
     const int rblk = t_log % row_blocks, cblk = t_log / row_blocks;
     const int m0 = rblk * MT * 16;
     const int Mb = min(MT * 16, M - m0);
-    const int tile0 = cblk * Q_TILES + cw * NT;
+    const int tile0 = cblk * TILES + cw * NT;
     const i32x4_t izero = {0, 0, 0, 0};
 
     rsrc_t wr[NT], mr[NT];
@@ -583,7 +584,7 @@ k_w4a4_lds(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_scal
                             acc[mt][nt][r];
         }
         __syncthreads();
-        const int n0 = cblk * Q_TILES * 16 + rnd * CHUNK;
+        const int n0 = cblk * TILES * 16 + rnd * CHUNK;
         const int ncols = min(CHUNK, N - n0);
         if (y_f32) {
             float *dst = (float *)y + (size_t)m0 * N;
@@ -661,15 +662,31 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M
         return launch_skinny4<2, 1, 3, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, st);
     if (M <= 64)
         return launch_skinny4<4, 1, 2, 4>(a_codes, a_scales, M, codes, meta, K, N, y, y_f32, group_dots, st);
-    // M > 64: 64-row blocks x 128 columns, one XCD-remapped 1-D grid
+    // M > 64: 64-row blocks x 128 columns, one XCD-remapped 1-D grid; 64-column blocks (one tile
+    // per wave) when 128-column blocks would give at most one workgroup per CU, so that more than
+    // one wave per SIMD is resident (measured: 70B down at M = 256 183 -> 168 us, Llama-3-8B down
+    // at M = 128 88 -> 64 us; with 448 wide blocks, gate+up at M = 80, narrow ones were slower).
+    // Every output's reduction order is the same in both widths.
     const int rbs = (M + Q_MT * 16 - 1) / (Q_MT * 16);
-    const int cbs = (N / 16 + Q_TILES - 1) / Q_TILES;
-    if (group_dots)
-        hipLaunchKernelGGL((k_w4a4_lds<4, true>), dim3(cbs * rbs), dim3(Q_CW * 64), 0, st, a_codes, a_scales, M, codes,
-                           meta, K, N, y, y_f32, group_dots, rbs);
-    else
-        hipLaunchKernelGGL((k_w4a4_lds<3, false>), dim3(cbs * rbs), dim3(Q_CW * 64), 0, st, a_codes, a_scales, M, codes,
-                           meta, K, N, y, y_f32, group_dots, rbs);
+    const int wide_cbs = (N / 16 + Q_TILES - 1) / Q_TILES;
+    const bool narrow = (long long)wide_cbs * rbs <= 256;
+    const int cbs = narrow ? (N / 16 + Q_CW - 1) / Q_CW : wide_cbs;
+    const dim3 grid(cbs * rbs), block(Q_CW * 64);
+    if (group_dots) {
+        if (narrow)
+            hipLaunchKernelGGL((k_w4a4_lds<4, true, 1>), grid, block, 0, st, a_codes, a_scales, M, codes, meta, K, N,
+                               y, y_f32, group_dots, rbs);
+        else
+            hipLaunchKernelGGL((k_w4a4_lds<4, true, Q_NT>), grid, block, 0, st, a_codes, a_scales, M, codes, meta, K,
+                               N, y, y_f32, group_dots, rbs);
+    } else {
+        if (narrow)
+            hipLaunchKernelGGL((k_w4a4_lds<3, false, 1>), grid, block, 0, st, a_codes, a_scales, M, codes, meta, K, N,
+                               y, y_f32, group_dots, rbs);
+        else
+            hipLaunchKernelGGL((k_w4a4_lds<3, false, Q_NT>), grid, block, 0, st, a_codes, a_scales, M, codes, meta, K,
+                               N, y, y_f32, group_dots, rbs);
+    }
     return hipGetLastError();
 }
 

@@ -194,10 +194,11 @@ def test_w4a16_full_shapes_sampled_columns(name, K, N, M):
 # ---------------------------------------------------------------- W4A4
 
 # (24, 5120, 64) and (40, 2944, 48): 10 and 5 - 6 groups per wave in the 16 < M <= 64 kernel, so its
-# ring runs steady passes and a last pass with only some slots refilled.
+# ring runs steady passes and a last pass with only some slots refilled.  M > 64 takes 64-column
+# blocks up to 256 blocks of 128 columns and 128-column blocks past that: (65, 256, 16512) has 258.
 SMALL_W4A4 = [(1, 128, 16), (1, 512, 512), (4, 384, 48), (16, 640, 112), (5, 256, 16),
               (17, 384, 48), (33, 256, 32), (64, 128, 48), (65, 256, 144), (256, 512, 272), (100, 384, 16),
-              (24, 5120, 64), (40, 2944, 48)]
+              (24, 5120, 64), (40, 2944, 48), (65, 256, 16512)]
 
 
 @pytest.mark.parametrize("M,K,N", SMALL_W4A4)
