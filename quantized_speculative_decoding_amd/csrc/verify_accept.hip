@@ -329,6 +329,14 @@ struct ResidRow {
         return dv > 0.0 ? dv : 0.0;
     }
     __device__ __forceinline__ double r(int x) const { return r_of(x, p(x)); }
+    // the same residual from already loaded logits (tv = t[x], dv = d[x] when d is set)
+    __device__ __forceinline__ double r_val(float tv, float dv) const {
+#pragma clang fp contract(off)
+        const double pv = exp((double)tv - Mt) * iSt;
+        if (!d) return pv;
+        const double rv = pv - exp((double)dv - Md) * iSd;
+        return rv > 0.0 ? rv : 0.0;
+    }
 };
 
 __device__ __forceinline__ ResidRow resid_row(const float *target, size_t ldt, const float *draft, int B,
@@ -374,6 +382,55 @@ k_residual_partial(const float *__restrict__ target, size_t ldt, const float *__
     }
 }
 
+// Block-wide helpers for k_residual_pick (VT threads = 4 waves); every result is the same in all
+// threads and comes from one fixed order of operations.
+// Inclusive prefix sum in thread order: a shuffle scan per wave, then the wave totals in order.
+__device__ double block_scan(double v) {
+    __shared__ double wsum[VT / kWave];
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const double o = __shfl_up(v, off, kWave);
+        if (lane >= off) v += o;
+    }
+    if (lane == kWave - 1) wsum[w] = v;
+    __syncthreads();
+    double base = 0.0;
+    for (int k = 0; k < w; ++k) base += wsum[k];
+    __syncthreads();
+    return base + v;
+}
+
+// The smallest (first = true) or largest thread index whose flag is set, or -1.
+__device__ int block_find(bool f, bool first) {
+    __shared__ int wpick[VT / kWave];
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const unsigned long long m = __ballot(f);
+    if (lane == 0)
+        wpick[w] = m == 0ull ? -1 : w * kWave + (first ? __ffsll((long long)m) - 1 : 63 - __clzll((long long)m));
+    __syncthreads();
+    int r = -1;
+    for (int k = 0; k < VT / kWave; ++k) {
+        const int c = first ? wpick[k] : wpick[VT / kWave - 1 - k];
+        if (r < 0) r = c;
+    }
+    __syncthreads();
+    return r;
+}
+
+// The value of v held by thread t (t uniform).
+__device__ double block_bcast(double v, int t) {
+    __shared__ double s;
+    if ((int)threadIdx.x == t) s = v;
+    __syncthreads();
+    const double r = s;
+    __syncthreads();
+    return r;
+}
+
+// One workgroup per sequence: the chunk holding the threshold v * (total residual mass), the
+// segment inside it and the token.  The chunk and segment searches are block-wide prefix sums
+// (fixed order) and ballots; the token's own segment is walked in logit order.
 __global__ void __launch_bounds__(VT)
 k_residual_pick(const float *__restrict__ target, size_t ldt, const float *__restrict__ draft,
                 const float *__restrict__ v, int B, int gamma, int V, int C,
@@ -381,12 +438,39 @@ k_residual_pick(const float *__restrict__ target, size_t ldt, const float *__res
                 const int *__restrict__ accA, const double *__restrict__ resid,
                 const double *__restrict__ pmass, int32_t *__restrict__ out, int ldo) {
     __shared__ double seg[VT];
-    __shared__ int s_chunk, s_fallback, s_usep, s_seg;
-    __shared__ double s_thr, s_run;
+    __shared__ int s_chunk, s_fallback, s_usep;
+    __shared__ double s_thr;
     const int b = blockIdx.x;
+    const int tid = threadIdx.x;
     const int A = accA[b];
     ResidRow R = resid_row(target, ldt, draft, B, gamma, V, b, A, rowM, rowS);
-    if (threadIdx.x == 0) {
+    if (C <= VT) {   // one chunk mass per thread
+        double part = tid < C ? resid[(size_t)b * C + tid] : 0.0;
+        double pre = block_scan(part);
+        double tot = block_bcast(pre, C - 1);
+        const bool usep = !(tot > 0.0);
+        if (usep) {
+            part = tid < C ? pmass[(size_t)b * C + tid] : 0.0;
+            pre = block_scan(part);
+            tot = block_bcast(pre, C - 1);
+        }
+        const double thr = (double)v[b] * tot;
+        int chunk = block_find(tid < C && pre > thr, true);
+        const bool fallback = chunk < 0;
+        double before = 0.0;
+        if (fallback) {
+            chunk = block_find(tid < C && part > 0.0, false);
+            if (chunk < 0) chunk = C - 1;
+        } else {
+            before = block_bcast(pre - part, chunk);
+        }
+        if (tid == 0) {
+            s_chunk = chunk;
+            s_fallback = fallback;
+            s_usep = usep;
+            s_thr = thr - before;
+        }
+    } else if (tid == 0) {   // more chunks than threads: one thread walks them in order
         const double *part = resid + (size_t)b * C;
         double tot = 0.0;
         for (int c = 0; c < C; ++c) tot += part[c];
@@ -398,9 +482,8 @@ k_residual_pick(const float *__restrict__ target, size_t ldt, const float *__res
             for (int c = 0; c < C; ++c) tot += part[c];
         }
         const double thr = (double)v[b] * tot;
-        double run = 0.0;
+        double run = 0.0, before = 0.0;
         int chunk = -1;
-        double before = 0.0;
         for (int c = 0; c < C; ++c) {
             before = run;
             run += part[c];
@@ -421,45 +504,35 @@ k_residual_pick(const float *__restrict__ target, size_t ldt, const float *__res
     __syncthreads();
     if (s_usep) R.d = nullptr;
     const int lo = s_chunk * RCHUNK, hi = min(V, lo + RCHUNK);
-    const int x0 = lo + (int)threadIdx.x * RSEG, x1 = min(hi, x0 + RSEG);
-    double mine = 0.0;
-    for (int x = x0; x < x1; ++x) mine += R.r(x);
-    seg[threadIdx.x] = mine;
-    __syncthreads();
-    // The segment holding the threshold: a sequential running sum over the segment masses in
-    // order (read 8 at a time).
-    if (threadIdx.x == 0) {
-        int tsel = -1;
-        double run = 0.0;
-        if (!s_fallback) {
-            for (int t0 = 0; t0 < VT && tsel < 0; t0 += 8) {
-                double sv[8];
+    const int x0 = lo + tid * RSEG, x1 = min(hi, x0 + RSEG);
+    // the segment's logits first (all loads in flight), then its residual mass in logit order
+    float tv[RSEG], dv[RSEG];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) sv[k] = seg[t0 + k];
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (tsel < 0) {
-                        if (run + sv[k] > s_thr) tsel = t0 + k;
-                        else run += sv[k];
-                    }
-            }
-        }
-        s_seg = tsel;
-        s_run = run;
+    for (int k = 0; k < RSEG; ++k) {
+        const int x = x0 + k;
+        tv[k] = x < x1 ? R.t[x] : 0.f;
+        dv[k] = (R.d && x < x1) ? R.d[x] : 0.f;
     }
-    __syncthreads();
-    const int tsel = s_seg;
+    double mine = 0.0;
+#pragma unroll
+    for (int k = 0; k < RSEG; ++k)
+        if (x0 + k < x1) mine += R.r_val(tv[k], dv[k]);
+    // The segment holding the threshold: the first whose inclusive prefix exceeds it.
+    const double thr = s_thr;
+    const double pre = block_scan(mine);
+    const int tsel = s_fallback ? -1 : block_find(pre > thr, true);
     if (tsel >= 0) {
-        // the segment's masses in parallel, then the running sum through them in order
+        const double run = block_bcast(pre - mine, tsel);   // mass before the segment
+        // the segment's residuals in parallel, then the running sum through them in order
         const int a = lo + tsel * RSEG, e = min(hi, a + RSEG);
-        if ((int)threadIdx.x < e - a) seg[threadIdx.x] = R.r(a + (int)threadIdx.x);
+        if (tid < e - a) seg[tid] = R.r(a + tid);
         __syncthreads();
-        if (threadIdx.x == 0) {
+        if (tid == 0) {
             int tok = -1;
-            double rr = s_run;
+            double rr = run;
             for (int x = a; x < e; ++x) {
                 rr += seg[x - a];
-                if (rr > s_thr) { tok = x; break; }
+                if (rr > thr) { tok = x; break; }
             }
             if (tok < 0)   // rounding left the threshold at the segment's end
                 for (int x = e - 1; x >= a; --x)
@@ -474,15 +547,9 @@ k_residual_pick(const float *__restrict__ target, size_t ldt, const float *__res
     int last = -1;
     for (int x = x1 - 1; x >= x0; --x)
         if (R.r(x) > 0.0) { last = x; break; }
-    __shared__ int s_last[VT];
-    s_last[threadIdx.x] = last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int tok = -1;
-        for (int t = VT - 1; t >= 0 && tok < 0; --t) tok = s_last[t];
-        if (tok < 0) tok = hi - 1;
-        out[(size_t)b * ldo + A] = tok;
-    }
+    const int owner = block_find(last >= 0, false);
+    if (tid == 0 && owner < 0) out[(size_t)b * ldo + A] = hi - 1;
+    if (owner >= 0 && tid == owner) out[(size_t)b * ldo + A] = last;
 }
 
 // ---------------------------------------------------------------------------------------------
