@@ -606,15 +606,18 @@ static hipError_t launch_decode(const uint16_t *x, int M, const uint8_t *codes, 
 
 // K splits of the verify-tier kernel: a function of (K, N) only.  Column blocks alone fill the
 // chip when there are at least 192 of them; otherwise split K as far as the grid still fits one
-// workgroup per CU (256), keeping at least 8 groups (4 per K part) per split, and at most
-// kMaxSplits splits.  Shorter splits measured slower: their fp32 partials cost more traffic than
-// the extra workgroups gain (4096 x 4096 at M = 80: 8 splits 16.3 us, 4 splits 15.7 us).
+// workgroup per CU (256), keeping at least 5 groups per split, and at most kMaxSplits splits.
+// From sweeps of S = 1 .. 9 over the Llama-3-8B and Qwen2.5-7B projections at M = 20 and 80: a
+// grid past 256 workgroups runs a second generation (Llama qkv: 4 splits 11.9 us, 6 splits
+// 16.5 us at M = 20); with fewer than about 5 groups per split the fp32 partials cost more than
+// the extra workgroups gain; in between, Qwen2.5-7B qkv and o (28 groups) ran 10 - 16% faster
+// with 5 splits than with the 3 a floor of 8 groups allowed.
 static int mid_splits(int K, int N) {
     const int G = K / kGroup;
     const int cbs = (N / 16 + MID_TILES - 1) / MID_TILES;
     if (cbs >= 192) return 1;
     const int fit = 256 / cbs;
-    return max(1, min(min(fit, kMaxSplits), G / 8));
+    return max(1, min(min(fit, kMaxSplits), G / 5));
 }
 
 // K splits of the large tier: a function of (K, N) only.  Its 128-row x 256-column blocks run one
