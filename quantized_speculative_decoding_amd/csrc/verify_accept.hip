@@ -5,7 +5,8 @@
 //  acceptance.  QSPEC structure: the verifier produces gamma+1 distributions.)
 //
 // Logit rows are far larger than one workgroup's LDS (a 128256-wide fp32 row is 501 KB), so every
-// row is cut into chunks of VCHUNK logits and reduced in two deterministic stages:
+// row is cut into chunks of VCHUNK logits (2 VCHUNK for a plentiful greedy argmax) and reduced in
+// two deterministic stages:
 //   greedy:   k_argmax_partial (one workgroup per row chunk: max and its lowest index)
 //             -> k_greedy_accept (one thread per sequence: combine chunks in order, prefix match)
 //   sampling: k_softmax_partial (per row chunk: chunk max and sum of exp(l - max) in fp64)
@@ -13,8 +14,8 @@
 //                and test the candidates u < p(d)/q(d) in fp64; a ballot finds the first rejection)
 //             -> k_residual_partial (per RCHUNK-logit chunk of the last row: mass of max(0, p - q),
 //                or of p)
-//             -> k_residual_pick (per sequence: locate the chunk, its segment and the token; the
-//                residual masses are evaluated in parallel, the running sums stay sequential)
+//             -> k_residual_pick (per sequence: locate the chunk and its 8-logit segment with
+//                block-wide prefix sums in one fixed order, then walk that segment in logit order)
 // Softmax normalizers, ratios and running sums are fp64; the exponentials are fp64 as well.  The
 // residual stages use shorter chunks than the softmax statistics: they touch two rows per
 // sequence instead of 2 gamma + 1, so 8192-logit chunks left most of the chip idle.
