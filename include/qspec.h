@@ -132,8 +132,9 @@ int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int32_t M,
 
 /*
  * qspec_gemm_w4a16_workspace_bytes -- device workspace qspec_gemm_w4a16 needs for (M, K, N); 0
- * when the shape needs none (M <= 16, or a shape whose K is not split) or on invalid sizes.  K is
- * split for verify shapes (16 < M <= 80) with few column tiles and for large-batch shapes (M > 80)
+ * when the shape needs none (M <= 16, M <= 32 for small projections and M <= 24 for vocabulary-
+ * sized heads, or a shape whose K is not split) or on invalid sizes.  K is split for verify shapes
+ * (up to M = 80) with few column tiles and for large-batch shapes (M > 80)
  * with fewer than 64 blocks of 256 columns and at least 64 groups; the split count depends on
  * (K, N) and the batch tier only, and the size is S * M * N * 4 bytes.
  */

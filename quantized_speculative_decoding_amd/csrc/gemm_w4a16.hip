@@ -10,9 +10,10 @@
 // load is one contiguous kilobyte.
 //
 // Two kernels share the dequantization routine:
-//  * k_w4a16_decode (M <= 16): HBM-bound decode / short-verify shapes; NT column tiles per
+//  * k_w4a16_decode (M <= 16, and M <= 24 or 32 for the (K, N) where that measured faster):
+//    HBM-bound decode / short-verify shapes; NT column tiles and one or two row tiles per
 //    workgroup, K groups split between its waves, activations in registers.
-//  * k_w4a16_lds (16 < M <= 80 and M > 80): the activation tile of each group is staged once in
+//  * k_w4a16_lds (up to M = 80, and M > 80): the activation tile of each group is staged once in
 //    LDS and shared by the workgroup's waves; the verify tier splits K between two wave groups
 //    (and across workgroups with an ordered reduction), the large tier covers 128-row blocks.
 #include "common.hpp"
@@ -78,30 +79,32 @@ __device__ __forceinline__ void store_out(void *y, int y_f32, size_t idx, float 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode kernel (M <= 16): HBM-bound decode / short-verify shapes.  Lane l: col = l % 16 (B
-// column / A row), kq = l / 16 (k quarter of a group).  In MFMA j (0..3) of a group, k slot
+// Decode kernel (MT 16-row tiles, MT = 1 or 2): HBM-bound decode / short-verify shapes.  Lane l:
+// col = l % 16 (B column / A row within a row tile), kq = l / 16 (k quarter of a group).  In MFMA j (0..3) of a group, k slot
 // (kq, i) holds k = 128 g + 32 kq + 8 j + i for both operands.  Output of
 // v_mfma_f32_16x16x32_bf16: lane l, element r holds D[4 (l / 16) + r][l % 16].
 //
 // A workgroup owns NT column tiles and KW waves split the K groups; every wave loads the group's
-// activations once (64 bytes per lane) and feeds them to the 4 NT MFMAs of its tiles.  Loads are
+// activations once (64 bytes per lane and row tile) and dequantizes each weight block once, for
+// the 4 MT MFMAs of that tile.  A row's MFMAs see the same operands in the same order whatever MT
+// is, so rows do not depend on the batch inside the tier.  Loads are
 // buffer loads from wave-uniform bases through a U-deep register ring: each stage is consumed in
 // place and refilled with group i + U, and a scheduling barrier keeps the stages' loads in group
 // order, so the in-order vmcnt wait for a stage never covers a younger one.  Rows past M read row
 // M - 1 (their MFMA rows are discarded).  Wave partials are summed through LDS in wave order, so
 // the reduction order depends on (K, N) only.
-template <int NT>
+template <int NT, int MT>
 struct W16DStage {
     uint4 w[NT];
     uint32_t meta[NT];
-    uint4 a[4];
+    uint4 a[4 * MT];
 };
 
-template <int NT, int U>
+template <int NT, int U, int MT>
 __global__ void __launch_bounds__(64 * kMaxDecodeWaves)
 k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
                const uint32_t *__restrict__ meta, int K, int N, void *__restrict__ y, int y_f32, int kw) {
-    extern __shared__ __attribute__((aligned(16))) float red[];   // [kw][NT][4][64], sized at launch
+    extern __shared__ __attribute__((aligned(16))) float red[];   // [kw][MT][NT][4][64], sized at launch
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;
@@ -120,10 +123,12 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
         mr[nt] = make_rsrc(meta + ((size_t)t * G + g0) * 16, (uint32_t)ng * 64);
     }
     const rsrc_t xr = make_rsrc(x + (size_t)g0 * kGroup, (uint32_t)(((size_t)M * K - (size_t)g0 * kGroup) * 2));
-    const uint32_t xoff = (uint32_t)(min(col, M - 1) * K + kq * 32) * 2;
+    uint32_t xoff[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xoff[mt] = (uint32_t)(min(col + 16 * mt, M - 1) * K + kq * 32) * 2;
 
     // Group i of this wave; prologue loads past a range shorter than the ring re-read its first group.
-    auto load = [&](W16DStage<NT> &st, int i) {
+    auto load = [&](W16DStage<NT, MT> &st, int i) {
         const uint32_t g = (uint32_t)(i < ng ? i : 0);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -131,14 +136,18 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
             st.meta[nt] = buf_load4(mr[nt], col * 4, g * 64);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st.a[j] = buf_load16(xr, xoff + 16 * j, g * 256);
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st.a[4 * mt + j] = buf_load16(xr, xoff[mt] + 16 * j, g * 256);
     };
 
-    f32x4_t acc[NT];
+    f32x4_t acc[MT][NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const W16DStage<NT> &cur) {
+    auto compute = [&](const W16DStage<NT, MT> &cur) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const DqConst dq = make_dq(cur.meta[nt]);
@@ -147,13 +156,16 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
             for (int j = 0; j < 4; ++j) {
                 uint32_t b[4];
                 dequant8(words[j], dq, b);
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.a[j]),
-                                                                  as_bf16x8(b[0], b[1], b[2], b[3]), acc[nt], 0, 0, 0);
+                const bf16x8_t bw = as_bf16x8(b[0], b[1], b[2], b[3]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, cur.a[4 * mt + j]), bw, acc[mt][nt], 0, 0, 0);
             }
         }
     };
 
-    W16DStage<NT> st[U];
+    W16DStage<NT, MT> st[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         load(st[u], u);
@@ -185,23 +197,25 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
     // row over the waves in wave order and writes them with one 16-byte (bf16) or two 16-byte
     // (f32) stores.
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[((wave * NT + nt) * 4 + r) * 64 + lane] = acc[nt][r];
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[(((wave * MT + mt) * NT + nt) * 4 + r) * 64 + lane] = acc[mt][nt][r];
     __syncthreads();
-    for (int e = threadIdx.x; e < NT * 32; e += blockDim.x) {
-        const int nt = e >> 5, m = (e >> 1) & 15, c0 = (e & 1) * 8;
-        const int t = tbase + nt;
-        if (m >= M || t >= T) continue;
-        const int base = (nt * 4 + (m & 3)) * 64 + 16 * (m >> 2) + c0;
+    for (int e = threadIdx.x; e < MT * NT * 32; e += blockDim.x) {
+        const int mnt = e >> 5, nt = mnt % NT, mt = mnt / NT, m = (e >> 1) & 15, c0 = (e & 1) * 8;
+        const int t = tbase + nt, row = 16 * mt + m;
+        if (row >= M || t >= T) continue;
+        const int base = (mnt * 4 + (m & 3)) * 64 + 16 * (m >> 2) + c0;
         float4 lo = *(const float4 *)&red[base], hi = *(const float4 *)&red[base + 4];
         for (int w = 1; w < kw; ++w) {
-            const float4 a = *(const float4 *)&red[w * NT * 256 + base];
-            const float4 b = *(const float4 *)&red[w * NT * 256 + base + 4];
+            const float4 a = *(const float4 *)&red[w * MT * NT * 256 + base];
+            const float4 b = *(const float4 *)&red[w * MT * NT * 256 + base + 4];
             lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
             hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
         }
-        const size_t idx = (size_t)m * N + 16 * t + c0;
+        const size_t idx = (size_t)row * N + 16 * t + c0;
         if (y_f32) {
             *(float4 *)((float *)y + idx) = lo;
             *(float4 *)((float *)y + idx + 4) = hi;
@@ -217,8 +231,8 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
-// Shared-activation kernel k_w4a16_lds: the verify tier (16 < M <= 80) and the large-batch tier
-// (M > 80).  At these M a group's activation tile (M x 128 bf16: 20 KB at M = 80, 32 KB for a
+// Shared-activation kernel k_w4a16_lds: the verify tier (above the decode tier, up to M = 80) and
+// the large-batch tier (M > 80).  At these M a group's activation tile (M x 128 bf16: 20 KB at M = 80, 32 KB for a
 // 128-row block) is as large as 20 - 32 weight blocks, so it is staged once in LDS and shared by
 // the workgroup's waves, while every weight block is dequantized exactly once, in registers, by
 // the wave whose MFMA B operand it is.
@@ -594,14 +608,32 @@ k_w4a16_splitk_reduce(const float *__restrict__ partials, int S, size_t MN, void
 // ---------------------------------------------------------------------------------------------
 // Host launchers.
 
-template <int NT, int U>
+template <int NT, int U, int MT>
 static hipError_t launch_decode(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K, int N,
                                 void *y, int y_f32, hipStream_t st) {
     const int kw = decode_shape(K, N).kw;
-    const size_t lds = (size_t)kw * NT * 256 * sizeof(float);
-    hipLaunchKernelGGL((k_w4a16_decode<NT, U>), dim3((N / 16 + NT - 1) / NT), dim3(64 * kw), lds, st, x, M, codes,
-                       meta, K, N, y, y_f32, kw);
+    const size_t lds = (size_t)kw * MT * NT * 256 * sizeof(float);
+    hipLaunchKernelGGL((k_w4a16_decode<NT, U, MT>), dim3((N / 16 + NT - 1) / NT), dim3(64 * kw), lds, st, x, M,
+                       codes, meta, K, N, y, y_f32, kw);
     return hipGetLastError();
+}
+
+// Largest batch of the decode tier for (K, N); above 16 rows a wave carries two row tiles
+// (MT = 2).  Every workgroup of the decode kernel reads all M rows of the activations for its
+// column tiles, about 4 M / NT times the bytes of its weights, where the verify tier stages them
+// once per 128 columns; the second row tile pays only where the weights are small (latency-bound
+// launches in one generation of workgroups) or the workgroups are wide (NT = 4).  From an A/B run
+// at M = 17, 24, 32 on the Llama-3-8B and Qwen2.5-7B projections and vocabulary head (µs, verify
+// tier -> decode tier): Llama qkv 11.3 -> 9.0 (M = 17) and 12.5 -> 11.2 (M = 32), Qwen o 10.0 ->
+// 7.5 and 11.0 -> 9.8, Qwen head 99 -> 88 (M = 17) and 100 -> 94 (M = 24), 103 both at M = 32;
+// losses where the activation re-reads dominate: Llama down 16.2 -> 20.4 (M = 17), 18.0 -> 34.7
+// (M = 32), gate+up 23 -> 25 .. 34, and Qwen qkv (288 workgroups, some CUs run two) 10.2 -> 11.4.
+static int decode_max_m(int K, int N) {
+    const DecodeShape d = decode_shape(K, N);
+    const int wgs = (N / 16 + d.nt - 1) / d.nt;
+    if (d.nt == 4) return 24;
+    if (wgs <= 256 && (long long)K * N <= 4096LL * 6144) return 32;
+    return 16;
 }
 
 // K splits of the verify-tier kernel: a function of (K, N) only.  Column blocks alone fill the
@@ -634,7 +666,7 @@ static int big_splits(int K, int N) {
 }
 
 size_t gemm_w4a16_workspace_bytes(int M, int K, int N) {
-    if (M <= 16) return 0;
+    if (M <= decode_max_m(K, N)) return 0;
     const int S = M <= 80 ? mid_splits(K, N) : big_splits(K, N);
     return S == 1 ? 0 : (size_t)S * M * N * sizeof(float);
 }
@@ -659,13 +691,20 @@ static hipError_t launch_mid(const uint16_t *x, int M, const uint8_t *codes, con
 
 hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K,
                              int N, void *y, int y_f32, void *ws, hipStream_t st) {
-    // Batch tiers, each with one reduction order for all its M: M <= 16 (decode), 16 < M <= 80
-    // (shared activations, K parts, optional split-K), M > 80 (shared activations, row blocks).
+    // Batch tiers, each with one reduction order for all its M: M <= decode_max_m(K, N) (decode,
+    // one or two row tiles), up to M = 80 (shared activations, K parts, optional split-K), M > 80
+    // (shared activations, row blocks).
     if (M <= 16) {
         const int nt = decode_shape(K, N).nt;
-        if (nt == 4) return launch_decode<4, 4>(x, M, codes, meta, K, N, y, y_f32, st);
-        if (nt == 2) return launch_decode<2, 4>(x, M, codes, meta, K, N, y, y_f32, st);
-        return launch_decode<1, 4>(x, M, codes, meta, K, N, y, y_f32, st);
+        if (nt == 4) return launch_decode<4, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
+        if (nt == 2) return launch_decode<2, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
+        return launch_decode<1, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
+    }
+    if (M <= decode_max_m(K, N)) {
+        const int nt = decode_shape(K, N).nt;
+        if (nt == 4) return launch_decode<4, 3, 2>(x, M, codes, meta, K, N, y, y_f32, st);
+        if (nt == 2) return launch_decode<2, 4, 2>(x, M, codes, meta, K, N, y, y_f32, st);
+        return launch_decode<1, 3, 2>(x, M, codes, meta, K, N, y, y_f32, st);
     }
     if (M <= 32) return launch_mid<2, 6>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     if (M <= 48) return launch_mid<3, 5>(x, M, codes, meta, K, N, y, y_f32, ws, st);

@@ -74,6 +74,10 @@ def test_gemm_validation():
     assert L.qspec_gemm_w4a16(FAKE, 4, FAKE, FAKE, 256, 64, FAKE, 2, None, 0, None) == ERR_UNSUPPORTED
     # split-K verify shapes need a workspace; decode shapes need none
     assert L.qspec_gemm_w4a16_workspace_bytes(4, 4096, 4096) == 0
+    # decode tier up to M = 32 for a 4096 x 4096 projection, verify tier (split K) above it
+    assert L.qspec_gemm_w4a16_workspace_bytes(32, 4096, 4096) == 0
+    assert L.qspec_gemm_w4a16_workspace_bytes(33, 4096, 4096) == 6 * 33 * 4096 * 4
+    assert L.qspec_gemm_w4a16_workspace_bytes(20, 14336, 4096) == 8 * 20 * 4096 * 4
     need = L.qspec_gemm_w4a16_workspace_bytes(80, 4096, 4096)
     assert need >= 80 * 4096 * 4 * 2
     assert L.qspec_gemm_w4a16(FAKE, 80, FAKE, FAKE, 4096, 4096, FAKE, 0, None, 0, None) == ERR_WS

@@ -111,14 +111,14 @@ def test_w4a16_rows_do_not_depend_on_batch():
     w = si.weights(K, N, seed=4)
     wdev = weights_dev(w)
     x = si.activations(80, K, seed=4)
-    full = {M: run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy() for M in (1, 5, 16, 17, 20, 33, 80)}
-    for M in (1, 5):                     # tier M <= 16
-        assert np.array_equal(full[M], full[16][:M]), M
-    for M in (17, 20, 33):               # tier 16 < M <= 80
+    full = {M: run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy() for M in (1, 5, 16, 17, 20, 32, 33, 48, 80)}
+    for M in (1, 5, 16, 17, 20):         # decode tier (M <= 32 for this small shape): 1 or 2 row tiles
+        assert np.array_equal(full[M], full[32][:M]), M
+    for M in (33, 48):                   # verify tier up to M = 80
         assert np.array_equal(full[M], full[80][:M]), M
 
 
-@pytest.mark.parametrize("M,K,N", [(80, 4096, 4096), (20, 14336, 512), (33, 2048, 784)])
+@pytest.mark.parametrize("M,K,N", [(80, 4096, 4096), (40, 14336, 512), (33, 2048, 784)])
 def test_w4a16_split_k_workspace_reuse(M, K, N):
     """Split-K verify shapes: the workspace needs no initialization (it starts as NaN bytes here)
     and repeated calls on it give identical results."""
@@ -248,6 +248,26 @@ def test_decode_tilings_w4a4_and_w4a16(M, K, N):
     ref, D = oracle.gemm_w4a4(oc, osc, w["codes"], w["meta"])
     assert np.array_equal(dots.cpu().numpy().astype(np.int64), D)
     assert_close(host_f64(y4), ref, False, f"w4a4 {M}x{K}x{N}")
+
+
+# Two row tiles per wave in the W4A16 decode kernel (17 <= M <= 32 where (K, N) selects it):
+# 4 column tiles per workgroup with a ragged tile tail (up to M = 24), 2 tiles over 4 K-splitting
+# waves, 1 tile over 4 waves with 7 or 8 groups each (a ragged ring tail), 1 tile over 2 waves.
+# Rows 0 .. 15 must equal the M = 16 (one row tile) result bit for bit.
+DECODE_TWO_ROW_TILES = [(24, 128, 16 * 4097), (20, 1024, 16 * 385), (32, 3840, 16 * 255), (17, 512, 16 * 200)]
+
+
+@pytest.mark.parametrize("M,K,N", DECODE_TWO_ROW_TILES)
+def test_w4a16_decode_two_row_tiles(M, K, N):
+    note(f"gemm_w4a16 decode two row tiles M={M} K={K} N={N}")
+    w = si.weights(K, N, seed=N % 991)
+    x = si.activations(M, K, seed=M + 3100)
+    wdev = weights_dev(w)
+    assert q.qspec_gemm_w4a16_workspace_bytes(M, K, N) == 0          # decode tier: no K split
+    y = run_w4a16(x, w, torch.float32, wdev)
+    assert_close(host_f64(y), oracle.gemm_w4a16(x, w["codes"], w["meta"]), False, f"w4a16 {M}x{K}x{N}")
+    y16 = run_w4a16(x[:16], w, torch.float32, wdev)
+    assert torch.equal(y[:16], y16)
 
 
 # The decode kernel parks activation scales per wave in chunks of 64 groups: K split over 4 waves
