@@ -170,6 +170,8 @@ FULL_W4A16 = [
     # Qwen2.5-7B-shaped layer at gamma + 1 in 3, 5, 9, 17; fp32 logits for the head
     ("qwen7b.qkv", 3584, 4608, 3), ("qwen7b.gate_up", 3584, 37888, 9), ("qwen7b.down", 18944, 3584, 17),
     ("qwen7b.lm_head", 3584, 152064, 5),
+    # decode kernel with two row tiles: the head at gamma + 1 = 17, Llama qkv at B = 4
+    ("qwen7b.lm_head", 3584, 152064, 17), ("llama8b.qkv", 4096, 6144, 20),
     # 70B-shaped FFN, compute-bound verify at 256 x 5 tokens
     ("llama70b.gate_up", 8192, 57344, 1280), ("llama70b.down", 28672, 8192, 1280),
 ]
