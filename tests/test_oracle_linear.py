@@ -57,6 +57,56 @@ def test_quantizer_golden_ties():
     assert scales[0, 1] == 0.0 and np.all(q[128:] == 0)
 
 
+def _round_binary32(q):
+    """Nearest binary32 value to a positive rational q (normal range), ties to even:
+    the IEEE 754 definition of a correctly rounded binary32 result, in exact arithmetic."""
+    from fractions import Fraction
+    e = 0
+    while Fraction(2) ** e > q:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= q:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    m = q / ulp
+    lo = m.numerator // m.denominator
+    rem = m - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return lo * ulp
+
+
+def _nearest_even_int(q):
+    from fractions import Fraction
+    lo = q.numerator // q.denominator
+    rem = q - lo
+    return lo + 1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1) else lo
+
+
+@pytest.mark.parametrize("case", GOLDEN["quantizer_division"]["cases"], ids=lambda c: "a" + c["absmax"])
+def test_quantizer_golden_division(case):
+    """The quotient x / s_a is one correctly rounded binary32 division (not x * (1 / s_a), not an
+    exact or binary64 quotient), rounded to the nearest integer with ties to even."""
+    from fractions import Fraction
+    a, xv = Fraction(case["absmax"]), Fraction(case["x"])
+    # the stated codes follow from the IEEE definitions, in exact rational arithmetic
+    s_a = _round_binary32(a / 7)
+    assert _nearest_even_int(_round_binary32(xv / s_a)) == case["code"]
+    assert _nearest_even_int(_round_binary32(xv * _round_binary32(1 / s_a))) == case["reciprocal_multiply_code"]
+    assert case["code"] != case["reciprocal_multiply_code"]
+    if "exact_quotient_code" in case:
+        assert _nearest_even_int(xv / s_a) == case["exact_quotient_code"] != case["code"]
+    # the oracle on a group holding a, x, -x and zeros
+    vals = np.zeros((1, 128), np.float32)
+    vals[0, :3] = [float(a), float(xv), -float(xv)]
+    xb = si.f32_to_bf16_bits(vals)
+    assert np.array_equal(bf16_to_f64(xb)[0, :3], vals[0, :3])   # exactly representable
+    codes, scales = oracle.quantize_act(xb)
+    q = unpack_signed(codes)[0]
+    assert Fraction(float(scales[0, 0])) == s_a
+    assert q[:3].tolist() == [7, case["code"], case["code_of_neg_x"]]
+    assert np.all(q[3:] == 0)
+
+
 @pytest.fixture(scope="module")
 def act():
     return si.activations(7, 1024, seed=11)

@@ -169,6 +169,34 @@ def test_sampling_disjoint_supports_reject_first_and_draw_from_target():
     assert stats.chisquare(c[:4], p0[:4] * B).pvalue > 1e-4
 
 
+def test_sampling_zero_mass_residual_falls_back_to_target_row():
+    """After a rejection the correction token is drawn from the target's distribution (the
+    residual max(0, p - q) normalised; p itself when that residual has no mass).  With q == p at
+    every position the residual is exactly zero wherever a rejection happens, and a rejection is
+    forced at position j by an out-of-range draft token, so the token at j must follow p_j.
+    The target rows differ from one another, so a draw from another row, a uniform draw, or no
+    draw at all fails; drawing from q_j instead of p_j is the same distribution here, since a zero
+    residual means q_j = p_j up to rounding."""
+    B, gamma, V, j = 30000, 4, 8, 2
+    rows = np.array([[0.30, 0.05, 0.05, 0.20, 0.10, 0.10, 0.15, 0.05],
+                     [0.02, 0.40, 0.08, 0.10, 0.10, 0.05, 0.05, 0.20],
+                     [0.05, 0.05, 0.50, 0.02, 0.03, 0.15, 0.10, 0.10],
+                     [0.25, 0.25, 0.02, 0.03, 0.15, 0.10, 0.10, 0.10],
+                     [0.10, 0.10, 0.10, 0.40, 0.05, 0.05, 0.10, 0.10]])
+    t = np.broadcast_to(np.log(rows).astype(np.float32), (B, gamma + 1, V)).copy()
+    d = t[:, :gamma, :].copy()                       # q_i == p_i bit for bit
+    toks = si.draft_tokens_sampled(d, 21)
+    toks[:, j] = V                                   # out of range: rejected
+    acc, out, diag = oracle.verify_sample(t, d, toks, si.uniforms((B, gamma), 21), si.uniforms((B,), 22))
+    assert np.all(acc == j)                          # p/q == 1 > u before j
+    assert np.array_equal(out[:, :j], toks[:, :j]) and np.all(out[:, j + 1:] == -1)
+    counts = np.bincount(out[:, j], minlength=V)
+    assert counts.sum() == B
+    assert stats.chisquare(counts, rows[j] * B).pvalue > 1e-4
+    for other in [rows[j - 1], rows[j + 1], np.full(V, 1.0 / V)]:
+        assert stats.chisquare(counts, other * B).pvalue < 1e-12
+
+
 def test_sampling_with_one_hot_distributions_equals_greedy():
     B, gamma, V = 50, 4, 64
     r = si.rng(12)
