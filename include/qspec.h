@@ -122,21 +122,46 @@ int qspec_quantize_act(const uint16_t *x, int32_t M, int32_t K, uint8_t *codes, 
  * group_dots  [out, optional] i32 [K/128][M][N] -- the exact D; NULL to skip
  *             (diagnostic: slower).
  * Batch invariance: the reduction order of an output depends only on (K, N) and on the batch
- * tier of M -- [1, 16], (16, 64] or above 64 -- so row m of y is bit-identical for every M in
- * the same tier.
- * Errors: NULL pointer; M < 1; N < 1 or N % 16 != 0; K < 128 or K % 128 != 0; bad y_dtype.
+ * tier of M -- [1, 16], [17, 64] or 65 and above (qspec_gemm_w4a4_tier reports it) -- so row m
+ * of y is bit-identical for every M in the same tier.  D is exact, hence independent of M.
+ * Errors: NULL pointer; M < 1; N < 1 or N % 16 != 0; K < 128 or K % 128 != 0; min(M, 64) * K / 2
+ * or K * 8 of 2^32 or more (32-bit buffer ranges); bad y_dtype.
  */
 int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int32_t M,
                     const uint8_t *w_codes, const uint32_t *w_meta, int32_t K, int32_t N, void *y,
                     int32_t y_dtype, int32_t *group_dots, qspec_stream_t stream);
 
 /*
+ * qspec_gemm_w4a4_tier -- the batch tier of M for (K, N): returns its index (0, 1 or 2) and sets
+ * [*m_first, *m_last] to the batch sizes that share it (*m_last = INT32_MAX for the last tier).
+ * Every M of one tier reduces each output of qspec_gemm_w4a4 in the same order; different tiers
+ * may round differently.  The tiers are [1, 16], [17, 64] and [65, INT32_MAX] for every (K, N).
+ * Host-only: launches nothing.
+ * Errors (negative status): NULL pointer; the size errors of qspec_gemm_w4a4.
+ */
+int qspec_gemm_w4a4_tier(int32_t M, int32_t K, int32_t N, int32_t *m_first, int32_t *m_last);
+
+/*
+ * qspec_gemm_w4a16_tier -- the batch tier of M for (K, N) in qspec_gemm_w4a16, as
+ * qspec_gemm_w4a4_tier reports it for the W4A4 layer.  The tiers are
+ *   0: [1, D]       the decode kernel (one 16-row tile up to 16 rows, two above);
+ *   1: [D + 1, 80]  the shared-activation kernel with two K parts (and K splits);
+ *   2: [81, INT32_MAX] the shared-activation kernel over 128-row blocks;
+ * with D = 24 when N >= 65536 (vocabulary-sized heads: four column tiles per workgroup),
+ * D = 32 when the decode grid has at most 256 workgroups and K * N <= 4096 * 6144 (small
+ * projections), and D = 16 otherwise.  The decode grid has N / 16 workgroups for N < 6144,
+ * ceil(N / 32) for 6144 <= N < 65536.  Host-only: launches nothing.
+ * Errors (negative status): NULL pointer; the size errors of qspec_gemm_w4a16.
+ */
+int qspec_gemm_w4a16_tier(int32_t M, int32_t K, int32_t N, int32_t *m_first, int32_t *m_last);
+
+/*
  * qspec_gemm_w4a16_workspace_bytes -- device workspace qspec_gemm_w4a16 needs for (M, K, N); 0
- * when the shape needs none (M <= 16, M <= 32 for small projections and M <= 24 for vocabulary-
- * sized heads, or a shape whose K is not split) or on invalid sizes.  K is split for verify shapes
- * (up to M = 80) with few column tiles and for large-batch shapes (M > 80)
- * with fewer than 64 blocks of 256 columns and at least 64 groups; the split count depends on
- * (K, N) and the batch tier only, and the size is S * M * N * 4 bytes.
+ * when the shape needs none (M in tier 0 of qspec_gemm_w4a16_tier, or a shape whose K is not
+ * split) or on invalid sizes.  K is split for tier-1 shapes (up to M = 80) with fewer than 192
+ * blocks of 128 columns and for tier-2 shapes (M > 80) with fewer than 64 blocks of 256 columns
+ * and at least 64 groups; the split count S depends on (K, N) and the tier only, and the size is
+ * S * M * N * 4 bytes.
  */
 size_t qspec_gemm_w4a16_workspace_bytes(int32_t M, int32_t K, int32_t N);
 
@@ -155,11 +180,12 @@ size_t qspec_gemm_w4a16_workspace_bytes(int32_t M, int32_t K, int32_t N);
  *           [S][M][N], which a second kernel on the same stream adds in split order; its contents
  *           need no initialization.  Calls sharing a workspace must be ordered on one stream.
  * Batch invariance: the reduction order of an output depends only on (K, N) and on the
- * batch tier of M -- [1, 16], (16, 80] or above 80 -- so row m of y is bit-identical for every
- * M in the same tier; verifying gamma+1 <= 16 positions therefore reproduces one-position
- * decoding bit for bit.
- * Errors: NULL pointer; M < 1; N < 1 or N % 16 != 0; K < 128 or K % 128 != 0; bad y_dtype;
- * workspace missing or too small.
+ * batch tier of M (qspec_gemm_w4a16_tier), so row m of y is bit-identical for every M in the
+ * same tier; verifying gamma + 1 <= 16 positions of one sequence therefore reproduces
+ * one-position decoding bit for bit.  Across tiers (say plain decoding at M = B = 16 and
+ * verification at M = 5B = 80) rows agree to fp32 rounding, not bit for bit.
+ * Errors: NULL pointer; M < 1; N < 1 or N % 16 != 0; K < 128 or K % 128 != 0; min(M, 128) * K * 2
+ * or K * 8 of 2^32 or more (32-bit buffer ranges); bad y_dtype; workspace missing or too small.
  */
 int qspec_gemm_w4a16(const uint16_t *x, int32_t M, const uint8_t *w_codes, const uint32_t *w_meta,
                      int32_t K, int32_t N, void *y, int32_t y_dtype, void *workspace,

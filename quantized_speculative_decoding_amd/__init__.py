@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.qspec_gemm_w4a16.argtypes = [P, I, P, P, I, I, P, I, P, S, P]
         L.qspec_gemm_w4a16_workspace_bytes.argtypes = [I, I, I]
         L.qspec_gemm_w4a16_workspace_bytes.restype = S
+        L.qspec_gemm_w4a16_tier.argtypes = [I, I, I, P, P]
+        L.qspec_gemm_w4a4_tier.argtypes = [I, I, I, P, P]
         L.qspec_verify_workspace_bytes.argtypes = [I, I, I, I]
         L.qspec_verify_workspace_bytes.restype = S
         L.qspec_verify_accept.argtypes = [I, P, P, P, P, P, I, I, I, P, P, P, S, P]
@@ -76,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.qspec_draft_sample.argtypes = [I, P, I, I, ctypes.c_int64, P, P, I, P, S, P]
         for fn in ("qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_verify_accept",
                    "qspec_kv_overwrite", "qspec_speckv_gamma", "qspec_attention", "qspec_quantize_act_fp8",
-                   "qspec_gemm_w8a8", "qspec_draft_sample"):
+                   "qspec_gemm_w8a8", "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -157,6 +159,24 @@ def qspec_gemm_w4a4(a_codes, a_scales, w_codes, w_meta, y, group_dots=None, stre
 
 def qspec_gemm_w4a16_workspace_bytes(M: int, K: int, N: int) -> int:
     return int(lib().qspec_gemm_w4a16_workspace_bytes(M, K, N))
+
+
+def _tier(fn: str, M: int, K: int, N: int):
+    lo, hi = ctypes.c_int32(0), ctypes.c_int32(0)
+    t = getattr(lib(), fn)(M, K, N, ctypes.byref(lo), ctypes.byref(hi))
+    _check(fn, t if t < 0 else 0)
+    return t, lo.value, hi.value
+
+
+def qspec_gemm_w4a16_tier(M: int, K: int, N: int):
+    """(tier index, first M, last M) of the batch tier of M for a K x N layer: rows of
+    qspec_gemm_w4a16 are bit-identical for every M in [first, last]."""
+    return _tier("qspec_gemm_w4a16_tier", M, K, N)
+
+
+def qspec_gemm_w4a4_tier(M: int, K: int, N: int):
+    """(tier index, first M, last M) of the batch tier of M in qspec_gemm_w4a4."""
+    return _tier("qspec_gemm_w4a4_tier", M, K, N)
 
 
 def gemm_w4a16_workspace(M: int, K: int, N: int, device) -> torch.Tensor:

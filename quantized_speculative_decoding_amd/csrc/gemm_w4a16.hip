@@ -665,6 +665,26 @@ static int big_splits(int K, int N) {
     return S;
 }
 
+// Batch tiers: [1, decode_max_m] (decode kernel, one or two row tiles), (decode_max_m, 80]
+// (shared-activation kernel with K parts), above 80 (shared-activation kernel, 128-row blocks).
+// Inside a tier the per-output reduction order depends on (K, N) only.
+int gemm_w4a16_tier(int M, int K, int N, int *m_first, int *m_last) {
+    const int dm = decode_max_m(K, N);
+    if (M <= dm) {
+        *m_first = 1;
+        *m_last = dm;
+        return 0;
+    }
+    if (M <= 80) {
+        *m_first = dm + 1;
+        *m_last = 80;
+        return 1;
+    }
+    *m_first = 81;
+    *m_last = 0x7FFFFFFF;
+    return 2;
+}
+
 size_t gemm_w4a16_workspace_bytes(int M, int K, int N) {
     if (M <= decode_max_m(K, N)) return 0;
     const int S = M <= 80 ? mid_splits(K, N) : big_splits(K, N);

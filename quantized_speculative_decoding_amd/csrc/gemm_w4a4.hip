@@ -646,6 +646,27 @@ static hipError_t launch_decode4(const uint8_t *a_codes, const float *a_scales, 
     return hipGetLastError();
 }
 
+// Batch tiers: [1, 16] (decode kernel), [17, 64] (skinny kernel, 2 or 4 row tiles per wave),
+// above 64 (shared-activation kernel, 64-row blocks of 64 or 128 columns).  Inside a tier the
+// per-output reduction order depends on (K, N) only.
+int gemm_w4a4_tier(int M, int K, int N, int *m_first, int *m_last) {
+    (void)K;
+    (void)N;
+    if (M <= 16) {
+        *m_first = 1;
+        *m_last = 16;
+        return 0;
+    }
+    if (M <= 64) {
+        *m_first = 17;
+        *m_last = 64;
+        return 1;
+    }
+    *m_first = 65;
+    *m_last = 0x7FFFFFFF;
+    return 2;
+}
+
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M, const uint8_t *codes,
                             const uint32_t *meta, int K, int N, void *y, int y_f32, int32_t *group_dots,
                             hipStream_t st) {

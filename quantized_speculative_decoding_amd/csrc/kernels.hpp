@@ -16,6 +16,10 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, con
 
 size_t gemm_w4a16_workspace_bytes(int M, int K, int N);
 
+// Batch tier of M for (K, N): its index, and the range of M sharing its reduction order.
+int gemm_w4a16_tier(int M, int K, int N, int *m_first, int *m_last);
+int gemm_w4a4_tier(int M, int K, int N, int *m_first, int *m_last);
+
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M, const uint8_t *codes,
                             const uint32_t *meta, int K, int N, void *y, int y_f32, int32_t *group_dots,
                             hipStream_t st);

@@ -24,6 +24,18 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 // grids fit the launch limits; sizes are int32 on the interface.
 constexpr long long kMaxElems = 1LL << 40;
 
+// The shared-INT4 kernels address the activation rows one workgroup reads (at most 128 rows for
+// W4A16, 64 codes rows for W4A4; all M rows below those) and one column tile's weight blocks
+// (K / 128 kilobytes) through 32-bit buffer ranges and offsets.
+inline bool w4a16_range_ok(int32_t M, int32_t K) {
+    const long long rows = M < 128 ? M : 128;
+    return rows * K * 2 < (1LL << 32) && (long long)K * 8 < (1LL << 32);
+}
+inline bool w4a4_range_ok(int32_t M, int32_t K) {
+    const long long rows = M < 64 ? M : 64;
+    return rows * (K / 2) < (1LL << 32) && (long long)K * 8 < (1LL << 32);
+}
+
 }  // namespace
 
 QSPEC_EXPORT const char *qspec_status_string(int status) {
@@ -52,7 +64,7 @@ QSPEC_EXPORT int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, 
                                  void *y, int32_t y_dtype, int32_t *group_dots, qspec_stream_t stream) {
     if (!a_codes || !a_scales || !w_codes || !w_meta || !y) return QSPEC_ERR_NULL;
     if (M < 1 || bad_n(N) || bad_k(K)) return QSPEC_ERR_SHAPE;
-    if ((long long)M * N > kMaxElems) return QSPEC_ERR_SHAPE;
+    if ((long long)M * N > kMaxElems || !w4a4_range_ok(M, K)) return QSPEC_ERR_SHAPE;
     if (y_dtype != QSPEC_OUT_BF16 && y_dtype != QSPEC_OUT_F32) return QSPEC_ERR_UNSUPPORTED;
     if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 4) || !aligned(w_meta, 4) ||
         !aligned(y, 16) || !aligned(group_dots, 4))
@@ -61,17 +73,41 @@ QSPEC_EXPORT int qspec_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, 
                                              y_dtype == QSPEC_OUT_F32, group_dots, as_stream(stream)));
 }
 
+static bool w4a16_sizes_ok(int32_t M, int32_t K, int32_t N) {
+    return M >= 1 && !bad_n(N) && !bad_k(K) && (long long)M * N <= kMaxElems && w4a16_range_ok(M, K);
+}
+
 QSPEC_EXPORT size_t qspec_gemm_w4a16_workspace_bytes(int32_t M, int32_t K, int32_t N) {
-    if (M < 1 || bad_n(N) || bad_k(K) || (long long)M * N > kMaxElems) return 0;
+    if (!w4a16_sizes_ok(M, K, N)) return 0;
     return qspec::gemm_w4a16_workspace_bytes(M, K, N);
+}
+
+QSPEC_EXPORT int qspec_gemm_w4a16_tier(int32_t M, int32_t K, int32_t N, int32_t *m_first, int32_t *m_last) {
+    if (!m_first || !m_last) return QSPEC_ERR_NULL;
+    if (!w4a16_sizes_ok(M, K, N)) return QSPEC_ERR_SHAPE;
+    int lo = 0, hi = 0;
+    const int tier = qspec::gemm_w4a16_tier(M, K, N, &lo, &hi);
+    *m_first = lo;
+    *m_last = hi;
+    return tier;
+}
+
+QSPEC_EXPORT int qspec_gemm_w4a4_tier(int32_t M, int32_t K, int32_t N, int32_t *m_first, int32_t *m_last) {
+    if (!m_first || !m_last) return QSPEC_ERR_NULL;
+    if (M < 1 || bad_n(N) || bad_k(K) || (long long)M * N > kMaxElems || !w4a4_range_ok(M, K))
+        return QSPEC_ERR_SHAPE;
+    int lo = 0, hi = 0;
+    const int tier = qspec::gemm_w4a4_tier(M, K, N, &lo, &hi);
+    *m_first = lo;
+    *m_last = hi;
+    return tier;
 }
 
 QSPEC_EXPORT int qspec_gemm_w4a16(const uint16_t *x, int32_t M, const uint8_t *w_codes,
                                   const uint32_t *w_meta, int32_t K, int32_t N, void *y, int32_t y_dtype,
                                   void *workspace, size_t workspace_bytes, qspec_stream_t stream) {
     if (!x || !w_codes || !w_meta || !y) return QSPEC_ERR_NULL;
-    if (M < 1 || bad_n(N) || bad_k(K)) return QSPEC_ERR_SHAPE;
-    if ((long long)M * N > kMaxElems) return QSPEC_ERR_SHAPE;
+    if (!w4a16_sizes_ok(M, K, N)) return QSPEC_ERR_SHAPE;
     if (y_dtype != QSPEC_OUT_BF16 && y_dtype != QSPEC_OUT_F32) return QSPEC_ERR_UNSUPPORTED;
     const size_t need = qspec::gemm_w4a16_workspace_bytes(M, K, N);
     if (need > 0 && (!workspace || workspace_bytes < need)) return QSPEC_ERR_WORKSPACE;
