@@ -18,7 +18,7 @@ import torch
 import oracle
 import quantized_speculative_decoding_amd as q
 import synthetic_inputs as si
-from gpu_helpers import DEV, assert_close, bf16_dev, cu, note
+from gpu_helpers import DEV, Guarded, assert_close, bf16_dev, cu, note, sample_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -50,21 +50,26 @@ def ptq_store(K, N, seed):
 
 def gpu_quantize(x):
     M, K = x.shape
-    codes = torch.empty((M, K), dtype=torch.uint8, device=DEV)
-    scales = torch.empty((M,), dtype=torch.float32, device=DEV)
-    q.qspec_quantize_act_fp8(bf16_dev(x), codes, scales)
-    return codes, scales
+    codes = Guarded((M, K), torch.uint8)
+    scales = Guarded((M,), torch.float32)
+    q.qspec_quantize_act_fp8(bf16_dev(x), codes.t, scales.t)
+    codes.check("quantize_act_fp8 codes")
+    scales.check("quantize_act_fp8 scales")
+    return codes.t, scales.t
 
 
 def gpu_gemm(a, sa, store, sw, M, out=torch.bfloat16):
     T, G, _ = store.shape
     K, N = G * 128, 16 * T
-    y = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+    y = Guarded((M, N), out, fill=float("nan"))
     nbytes = q.qspec_gemm_w8a8_workspace_bytes(M, K, N)
-    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=DEV) if nbytes else None
+    ws = Guarded((max(nbytes, 1),), torch.uint8) if nbytes else None
     q.qspec_gemm_w8a8(a, sa, cu(store) if isinstance(store, np.ndarray) else store,
-                      cu(sw) if isinstance(sw, np.ndarray) else sw, y, ws)
-    return y
+                      cu(sw) if isinstance(sw, np.ndarray) else sw, y.t, ws.t if ws is not None else None)
+    y.check("gemm_w8a8 y")
+    if ws is not None:
+        ws.check("gemm_w8a8 workspace")
+    return y.t
 
 
 @pytest.mark.parametrize("M,K", [(1, 128), (5, 3584), (17, 18944), (80, 4096), (3, 1024)])
@@ -107,7 +112,8 @@ def test_gemm_w8a8_matches_oracle(M, K, N):
     store, sw = ptq_store(K, N, seed=K + N)
     x = si.activations(M, K, seed=M)
     a, sa = gpu_quantize(x)
-    an, san = a.cpu().numpy(), sa.cpu().numpy()
+    an, san = oracle.quantize_act_fp8(x)                 # the oracle's own codes feed the oracle
+    assert np.array_equal(a.cpu().numpy(), an) and np.array_equal(sa.cpu().numpy(), san)
     ref = oracle.gemm_w8a8(an, san, store, sw)
     w_nk = si.unpack_fp8_weights(store)
     y16 = gpu_gemm(a, sa, store, sw, M).float().cpu().numpy().astype(np.float64)
@@ -155,10 +161,12 @@ def test_gemm_w8a8_qwen25_7b_sampled_tiles(name):
     wst, wsc = si.fp8_weights_device(K, N, seed=1, device=DEV)
     x = si.activations(M, K, seed=11)
     a, sa = gpu_quantize(x)
+    an, san = oracle.quantize_act_fp8(x)
+    assert np.array_equal(a.cpu().numpy(), an) and np.array_equal(sa.cpu().numpy(), san)
     y = gpu_gemm(a, sa, wst, wsc, M, torch.float32).cpu().numpy().astype(np.float64)
-    tiles = np.sort(si.rng(N).choice(N // 16, size=8, replace=False))
+    tiles = sample_tiles(N // 16, 32, seed=N)
     sub = wst[torch.from_numpy(tiles).to(DEV)].cpu().numpy()
     cols = (tiles[:, None] * 16 + np.arange(16)[None, :]).reshape(-1)
-    ref = oracle.gemm_w8a8(a.cpu().numpy(), sa.cpu().numpy(), sub, wsc.cpu().numpy()[cols])
-    check_w8a8(y[:, cols], ref, a.cpu().numpy(), sa.cpu().numpy(), si.unpack_fp8_weights(sub),
-               wsc.cpu().numpy()[cols], False, f"w8a8 {name}")
+    ref = oracle.gemm_w8a8(an, san, sub, wsc.cpu().numpy()[cols])
+    check_w8a8(y[:, cols], ref, an, san, si.unpack_fp8_weights(sub), wsc.cpu().numpy()[cols], False,
+               f"w8a8 {name}")

@@ -19,6 +19,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import quantized_speculative_decoding_amd as q
 import synthetic_inputs as si
 from gpu_helpers import DEV, bf16_dev, cu, note, weights_dev
@@ -223,3 +224,134 @@ def test_qspec_greedy_with_attention_over_the_shared_cache_equals_plain_greedy(s
     assert len(accepts) > 1
     if not unrelated:
         assert sum(accepts) > 0
+
+
+# ---- the identity with a batch of sequences, across W4A16 batch tiers ------------------------
+# Plain decoding of B sequences runs the W4A16 layers at M = B; QSPEC verification at
+# M = B (gamma + 1).  With the vocabulary head at V2 = 16384 columns (its decode tier ends at
+# M = 16) and the KV projection at 256 x 256 (decode tier up to M = 32), B = 4 with gamma = 4
+# verifies the head at M = 20 and B = 16 verifies both layers at M = 80 -- in a different tier
+# from plain decoding -- and B = 1 with gamma = 16 verifies the head at M = 17.  Rows then agree
+# to fp32 rounding instead of bit for bit, so the committed tokens may differ from plain decoding
+# only where plain decoding's own choice is a near tie: a token may differ only where the
+# oracle's top-2 logit gap of the plain run's hidden state is below 1e-4 of the top logit.
+
+V2 = 16384
+
+
+class BatchToy(Toy):
+    def __init__(self, seed: int):
+        self.E = si.activations(V2, H, seed=seed)
+        self.Ef = (self.E.astype(np.uint32) << 16).view(np.float32)
+        self.w_kv = weights_dev(si.weights(H, H, seed=seed + 1))
+        self.w_lm_host = si.weights(H, V2, seed=seed + 2)
+        self.w_lm = weights_dev(self.w_lm_host)
+        self.w_lm_draft = self.w_lm
+
+    def logits16_rows(self, hs: np.ndarray) -> np.ndarray:
+        y = torch.empty((hs.shape[0], V2), dtype=torch.float32, device=DEV)
+        q.qspec_gemm_w4a16(bf16_dev(hs), *self.w_lm, y)
+        return y
+
+    def kv4_rows(self, toks) -> np.ndarray:
+        y = self._w4a4(self.E[np.asarray(toks)], self.w_kv, H, torch.bfloat16)
+        return y.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def logits4_rows(self, hs: np.ndarray) -> np.ndarray:
+        return self._w4a4(hs, self.w_lm_draft, V2, torch.float32).cpu().numpy()
+
+
+def plain_greedy_batch(m: BatchToy, firsts, n: int):
+    B = len(firsts)
+    toks = [[f] for f in firsts]
+    rows = [[] for _ in range(B)]
+    hidden = [[] for _ in range(B)]           # hidden state behind each emitted token
+    for t in range(n):
+        kv = m.kv16([toks[b][t] for b in range(B)])              # M = B
+        hs = []
+        for b in range(B):
+            rows[b].append(kv[b])
+            hs.append(m.hidden(toks[b][t], np.stack(rows[b])))
+        hs = np.stack(hs)
+        nxt = np.argmax(m.logits16_rows(hs).cpu().numpy(), axis=1)   # M = B
+        for b in range(B):
+            toks[b].append(int(nxt[b]))
+            hidden[b].append(hs[b])
+    return toks, hidden
+
+
+def qspec_greedy_batch(m: BatchToy, firsts, n: int, gamma: int):
+    B = len(firsts)
+    ctx = (n + 1) * (gamma + 1) + gamma + 1      # a sequence ahead of the slowest keeps drafting
+    cache = torch.zeros((1, B, 2, HEADS, ctx, D), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty((q.qspec_verify_workspace_bytes(q.QSPEC_GREEDY, B, gamma, V2),), dtype=torch.uint8, device=DEV)
+    acc = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    out = torch.zeros((B, gamma + 1), dtype=torch.int32, device=DEV)
+
+    def rows(b, lo, hi):
+        r = cache[0, b, 0, :, lo:hi, :].permute(1, 0, 2).reshape(hi - lo, H)
+        return r.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    toks = [[f] for f in firsts]
+    p = [0] * B
+    accepts = []
+    while min(len(t) for t in toks) < n + 1:
+        cur = [toks[b][p[b]] for b in range(B)]
+        d = [[] for _ in range(B)]
+        for j in range(gamma):                                   # draft steps at M = B
+            kvd = m.kv4_rows(cur)
+            hs = []
+            for b in range(B):
+                cache[0, b, 0, :, p[b] + j, :] = torch.from_numpy(kvd[b].view(np.int16)).view(
+                    torch.bfloat16).to(DEV).view(HEADS, D)
+                hs.append(m.hidden(cur[b], rows(b, 0, p[b] + j + 1)))
+            nxt = np.argmax(m.logits4_rows(np.stack(hs)), axis=1)
+            for b in range(B):
+                d[b].append(int(nxt[b]))
+                cur[b] = int(nxt[b])
+        vt = [[toks[b][p[b]]] + d[b] for b in range(B)]
+        vkv = m.kv16([t for b in range(B) for t in vt[b]]).reshape(B, gamma + 1, H)   # M = B (gamma + 1)
+        hs = np.stack([m.hidden(vt[b][j], np.concatenate([rows(b, 0, p[b]), vkv[b, : j + 1]]))
+                       for b in range(B) for j in range(gamma + 1)])
+        target = m.logits16_rows(hs).view(B, gamma + 1, V2)                            # M = B (gamma + 1)
+        q.qspec_verify_accept(q.QSPEC_GREEDY, target, None, cu(np.array(d, np.int32)), None, None, acc, out, ws)
+        stage = torch.zeros((1, B, 2, HEADS, gamma + 1, D), dtype=torch.bfloat16, device=DEV)
+        stage[0, :, 0] = torch.from_numpy(vkv.view(np.int16)).view(torch.bfloat16).to(DEV).view(
+            B, gamma + 1, HEADS, D).permute(0, 2, 1, 3)
+        q.qspec_kv_overwrite(cache, stage, cu(np.array(p, np.int32)), acc)
+        A = acc.cpu().numpy()
+        o = out.cpu().numpy()
+        for b in range(B):
+            committed = o[b, : A[b] + 1].tolist()
+            assert committed[: A[b]] == d[b][: A[b]]
+            toks[b].extend(committed)
+            p[b] += int(A[b]) + 1
+        accepts.append(A.tolist())
+    return [t[: n + 1] for t in toks], accepts
+
+
+@pytest.mark.parametrize("B,gamma", [(4, 4), (16, 4), (1, 16)])
+def test_qspec_greedy_batch_equals_plain_w4a16_greedy_across_tiers(B, gamma):
+    note(f"toy decoder identity across W4A16 tiers B={B} gamma={gamma}")
+    m = BatchToy(seed=41 + B)
+    plain_tier = q.qspec_gemm_w4a16_tier(B, H, V2)
+    verify_tier = q.qspec_gemm_w4a16_tier(B * (gamma + 1), H, V2)
+    assert plain_tier[0] != verify_tier[0]                 # the head is verified in another tier
+    n = 24 if B == 16 else 32
+    firsts = [(97 * b + 5) % V2 for b in range(B)]
+    ref, hid = plain_greedy_batch(m, firsts, n)
+    got, accepts = qspec_greedy_batch(m, firsts, n, gamma)
+    note(f"accept counts per round: {accepts}")
+    assert sum(sum(a) for a in accepts) > 0
+    flips = 0
+    for b in range(B):
+        if got[b] == ref[b]:
+            continue
+        i = next(k for k in range(n + 1) if got[b][k] != ref[b][k])
+        h = hid[b][i - 1]                                   # plain run's hidden state before token i
+        logits = oracle.gemm_w4a16(h[None], m.w_lm_host["codes"], m.w_lm_host["meta"])[0]
+        top2 = np.sort(logits)[-2:]
+        gap = top2[1] - top2[0]
+        assert gap < 1e-4 * abs(top2[1]), (b, i, gap, top2)
+        flips += 1
+    note(f"sequences with a near-tie flip: {flips} of {B}")

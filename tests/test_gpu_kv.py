@@ -7,7 +7,7 @@ import torch
 import oracle
 import quantized_speculative_decoding_amd as q
 import synthetic_inputs as si
-from gpu_helpers import DEV, bf16_dev, cu, host_bits16, note
+from gpu_helpers import DEV, Guarded, bf16_dev, cu, host_bits16, note
 
 pytestmark = pytest.mark.gpu
 
@@ -21,10 +21,12 @@ def test_kv_overwrite_exact(L, B, H, T, D, gamma):
     start = si.start_positions(B, T, gamma, seed=B)
     start[0] = T - 2                                  # rows falling off the end are skipped
     acc = si.rng(B).integers(-1, gamma + 3, size=B).astype(np.int32)   # includes clamped values
-    gc = bf16_dev(cache)
-    q.qspec_kv_overwrite(gc, bf16_dev(stage), cu(start), cu(acc))
+    gc = Guarded(cache.shape, torch.bfloat16)
+    gc.t.copy_(bf16_dev(cache))
+    q.qspec_kv_overwrite(gc.t, bf16_dev(stage), cu(start), cu(acc))
+    gc.check("kv_overwrite cache")
     ref = oracle.kv_overwrite(cache.copy(), stage, start, acc)
-    assert np.array_equal(host_bits16(gc), ref)
+    assert np.array_equal(host_bits16(gc.t), ref)
 
 
 def test_kv_overwrite_full_cache_from_verify_accept():
@@ -50,6 +52,15 @@ def test_kv_overwrite_full_cache_from_verify_accept():
     torch.cuda.synchronize()
     a = acc.cpu().numpy()
     assert a.min() >= 0 and a.max() <= gamma
+    # the oracle on sampled (layer, sequence) slices: each slice is a [1][1][2][H][T][D] cache
+    stage_h = si.kv_staging(L, B, H, gamma, D, seed=5)
+    r = si.rng(17)
+    picks = [(0, 0), (L - 1, B - 1)] + [(int(r.integers(L)), int(r.integers(B))) for _ in range(6)]
+    for (l, b) in picks:
+        before = host_bits16(expect[l, b])[None, None]
+        ref = oracle.kv_overwrite(before, stage_h[l, b][None, None], start[b:b + 1], a[b:b + 1])
+        assert np.array_equal(host_bits16(cache[l, b])[None, None], ref), (l, b)
+    # everything else: the whole cache against the expected copy
     for b in range(B):
         rows = slice(int(start[b]), int(start[b]) + int(a[b]) + 1)
         expect[:, b, :, :, rows, :] = stage[:, b, :, :, : int(a[b]) + 1, :]

@@ -14,27 +14,66 @@ import torch
 import oracle
 import quantized_speculative_decoding_amd as q
 import synthetic_inputs as si
-from gpu_helpers import DEV, assert_close, bf16_dev, cu, host_bits16, host_f64, note, weights_dev
+from gpu_helpers import DEV, Guarded, assert_close, bf16_dev, cu, host_bits16, host_f64, note, sample_tiles, weights_dev
 
 pytestmark = pytest.mark.gpu
 
 
 def run_quant(x_bits):
     M, K = x_bits.shape
-    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
-    scales = torch.empty((M, K // 128), dtype=torch.float32, device=DEV)
-    q.qspec_quantize_act(bf16_dev(x_bits), codes, scales)
-    return codes, scales
+    codes = Guarded((M, K // 2), torch.uint8)
+    scales = Guarded((M, K // 128), torch.float32)
+    q.qspec_quantize_act(bf16_dev(x_bits), codes.t, scales.t)
+    codes.check("quantize_act codes")
+    scales.check("quantize_act scales")
+    return codes.t, scales.t
 
 
 def run_w4a16(x_bits, w, out=torch.bfloat16, wdev=None, ws=None):
+    """The W4A16 layer through the C ABI; the output sits between guard regions, checked after
+    the call (and the split-K workspace, when the call allocates it)."""
     M = x_bits.shape[0]
     wc, wm = wdev if wdev is not None else weights_dev(w)
-    y = torch.empty((M, w["N"]), dtype=out, device=DEV)
+    y = Guarded((M, w["N"]), out)
+    wsg = None
     if ws is None:
-        ws = q.gemm_w4a16_workspace(M, w["K"], w["N"], DEV)
-    q.qspec_gemm_w4a16(bf16_dev(x_bits), wc, wm, y, ws)
-    return y
+        wsg = Guarded((max(1, q.qspec_gemm_w4a16_workspace_bytes(M, w["K"], w["N"])),), torch.uint8)
+        ws = wsg.t
+    q.qspec_gemm_w4a16(bf16_dev(x_bits), wc, wm, y.t, ws)
+    y.check(f"gemm_w4a16 y M={M}")
+    if wsg is not None:
+        wsg.check(f"gemm_w4a16 workspace M={M}")
+    return y.t
+
+
+def run_w4a4(codes, scales, wdev, N, out, dots=None):
+    """The W4A4 layer through the C ABI with guarded outputs (y and, if asked, the group dots)."""
+    M = codes.shape[0]
+    y = Guarded((M, N), out)
+    dg = None
+    if dots:
+        K = codes.shape[1] * 2
+        dg = Guarded((K // 128, M, N), torch.int32, fill=-(2 ** 31))
+    q.qspec_gemm_w4a4(codes, scales, *wdev, y.t, group_dots=dg.t if dg is not None else None)
+    y.check(f"gemm_w4a4 y M={M}")
+    if dg is not None:
+        dg.check(f"gemm_w4a4 group dots M={M}")
+    return y.t, (dg.t if dg is not None else None)
+
+
+def full_rows(M: int) -> np.ndarray:
+    """Rows checked at full size: all of them up to 80; beyond, both sides of every 64- and
+    128-row block boundary plus seeded random rows, 64 or more in all."""
+    if M <= 80:
+        return np.arange(M)
+    s = {0, M - 1}
+    for b in (64, 128):
+        for r in range(b, M, b):
+            s.update((r - 1, r))
+    r = si.rng(M)
+    while len(s) < 64:
+        s.add(int(r.integers(0, M)))
+    return np.array(sorted(s))
 
 
 def tile_columns(tiles):
@@ -104,18 +143,27 @@ def test_w4a16_one_hot_rows_reproduce_dequantized_weights_exactly(M):
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
-def test_w4a16_rows_do_not_depend_on_batch():
-    """Every M in one batch tier reduces a row in the same order: bitwise-equal rows."""
-    K, N = 1024, 208
-    note("gemm_w4a16 batch invariance")
+@pytest.mark.parametrize("K,N", [(1024, 208), (1024, 16 * 300), (256, 16 * 4100)])
+def test_w4a16_rows_do_not_depend_on_batch(K, N):
+    """Every M in one batch tier (as qspec_gemm_w4a16_tier reports it: decode up to 32, 16 or 24
+    rows for these three shapes) reduces a row in the same order: bitwise-equal rows.  Across
+    tiers the rows agree to fp32 rounding."""
+    note(f"gemm_w4a16 batch invariance K={K} N={N}")
     w = si.weights(K, N, seed=4)
     wdev = weights_dev(w)
-    x = si.activations(80, K, seed=4)
-    full = {M: run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy() for M in (1, 5, 16, 17, 20, 32, 33, 48, 80)}
-    for M in (1, 5, 16, 17, 20):         # decode tier (M <= 32 for this small shape): 1 or 2 row tiles
-        assert np.array_equal(full[M], full[32][:M]), M
-    for M in (33, 48):                   # verify tier up to M = 80
-        assert np.array_equal(full[M], full[80][:M]), M
+    x = si.activations(96, K, seed=4)
+    Ms = (1, 5, 16, 17, 20, 24, 25, 32, 33, 48, 80, 81, 96)
+    full = {M: run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy() for M in Ms}
+    tiers = {}
+    for M in Ms:
+        t, lo, hi = q.qspec_gemm_w4a16_tier(M, K, N)
+        tiers.setdefault((t, lo, hi), []).append(M)
+    assert len(tiers) == 3
+    for (t, lo, hi), group in tiers.items():
+        top = max(group)
+        for M in group:
+            assert np.array_equal(full[M], full[top][:M]), (t, M, top)
+    assert_close(full[16].astype(np.float64), full[96][:16].astype(np.float64), False, "across tiers")
 
 
 @pytest.mark.parametrize("M,K,N", [(80, 4096, 4096), (40, 14336, 512), (33, 2048, 784)])
@@ -166,10 +214,10 @@ def test_w4a16_large_tier_split_k(M, K, N):
 FULL_W4A16 = [
     # Llama-3-8B-shaped projections, verify at M = 5B for B in 1, 4, 16
     ("llama8b.qkv", 4096, 6144, 80), ("llama8b.o", 4096, 4096, 20), ("llama8b.gate_up", 4096, 28672, 5),
-    ("llama8b.down", 14336, 4096, 80),
+    ("llama8b.down", 14336, 4096, 80), ("llama8b.gate_up", 4096, 28672, 80), ("llama8b.down", 14336, 4096, 16),
     # Qwen2.5-7B-shaped layer at gamma + 1 in 3, 5, 9, 17; fp32 logits for the head
-    ("qwen7b.qkv", 3584, 4608, 3), ("qwen7b.gate_up", 3584, 37888, 9), ("qwen7b.down", 18944, 3584, 17),
-    ("qwen7b.lm_head", 3584, 152064, 5),
+    ("qwen7b.qkv", 3584, 4608, 3), ("qwen7b.o", 3584, 3584, 5), ("qwen7b.gate_up", 3584, 37888, 9),
+    ("qwen7b.down", 18944, 3584, 17), ("qwen7b.lm_head", 3584, 152064, 5),
     # decode kernel with two row tiles: the head at gamma + 1 = 17, Llama qkv at B = 4
     ("qwen7b.lm_head", 3584, 152064, 17), ("llama8b.qkv", 4096, 6144, 20),
     # 70B-shaped FFN, compute-bound verify at 256 x 5 tokens
@@ -184,9 +232,9 @@ def test_w4a16_full_shapes_sampled_columns(name, K, N, M):
     x = si.activations(M, K, seed=M)
     out = torch.float32 if name.endswith("lm_head") else torch.bfloat16
     y = run_w4a16(x, w, out)
-    tiles = np.sort(si.rng(N).choice(N // 16, size=2, replace=False))
+    tiles = sample_tiles(N // 16, 32, seed=N)
     cols = tile_columns(tiles)
-    rows = np.arange(M) if M <= 80 else np.sort(si.rng(M).choice(M, size=64, replace=False))
+    rows = full_rows(M)
     sub = si.slice_tiles(w, tiles)
     ref = oracle.gemm_w4a16(x[rows], sub["codes"], sub["meta"])
     got = host_f64(y)[np.ix_(rows, cols)]
@@ -211,17 +259,14 @@ def test_w4a4_small_exact_dots_and_outputs(M, K, N):
     codes, scales = run_quant(x)
     oc, osc = oracle.quantize_act(x)
     assert np.array_equal(codes.cpu().numpy(), oc)
-    wc, wm = weights_dev(w)
-    dots = torch.full((K // 128, M, N), -(2 ** 31), dtype=torch.int32, device=DEV)
+    wdev = weights_dev(w)
     for out in (torch.bfloat16, torch.float32):
-        y = torch.empty((M, N), dtype=out, device=DEV)
-        q.qspec_gemm_w4a4(codes, scales, wc, wm, y, group_dots=dots)
+        y, dots = run_w4a4(codes, scales, wdev, N, out, dots=True)
         ref, D = oracle.gemm_w4a4(oc, osc, w["codes"], w["meta"])
         assert np.array_equal(dots.cpu().numpy().astype(np.int64), D)
         assert_close(host_f64(y), ref, out == torch.bfloat16, f"w4a4 {M}x{K}x{N}")
         # the diagnostic output does not change y
-        y2 = torch.empty_like(y)
-        q.qspec_gemm_w4a4(codes, scales, wc, wm, y2)
+        y2, _ = run_w4a4(codes, scales, wdev, N, out)
         assert torch.equal(y, y2)
 
 
@@ -244,9 +289,7 @@ def test_decode_tilings_w4a4_and_w4a16(M, K, N):
     assert_close(host_f64(y16), oracle.gemm_w4a16(x, w["codes"], w["meta"]), True, f"w4a16 {M}x{K}x{N}")
     codes, scales = run_quant(x)
     oc, osc = oracle.quantize_act(x)
-    dots = torch.full((K // 128, M, N), -(2 ** 31), dtype=torch.int32, device=DEV)
-    y4 = torch.empty((M, N), dtype=torch.float32, device=DEV)
-    q.qspec_gemm_w4a4(codes, scales, wc, wm, y4, group_dots=dots)
+    y4, dots = run_w4a4(codes, scales, (wc, wm), N, torch.float32, dots=True)
     ref, D = oracle.gemm_w4a4(oc, osc, w["codes"], w["meta"])
     assert np.array_equal(dots.cpu().numpy().astype(np.int64), D)
     assert_close(host_f64(y4), ref, False, f"w4a4 {M}x{K}x{N}")
@@ -285,9 +328,7 @@ def test_w4a4_decode_scale_chunks(M, K, N):
     wc, wm = weights_dev(w)
     codes, scales = run_quant(x)
     oc, osc = oracle.quantize_act(x)
-    dots = torch.full((K // 128, M, N), -(2 ** 31), dtype=torch.int32, device=DEV)
-    y4 = torch.empty((M, N), dtype=torch.float32, device=DEV)
-    q.qspec_gemm_w4a4(codes, scales, wc, wm, y4, group_dots=dots)
+    y4, dots = run_w4a4(codes, scales, (wc, wm), N, torch.float32, dots=True)
     ref, D = oracle.gemm_w4a4(oc, osc, w["codes"], w["meta"])
     assert np.array_equal(dots.cpu().numpy().astype(np.int64), D)
     assert_close(host_f64(y4), ref, False, f"w4a4 {M}x{K}x{N}")
@@ -312,7 +353,9 @@ def test_w4a4_rows_do_not_depend_on_batch():
 
 FULL_W4A4 = [
     ("llama8b.qkv", 4096, 6144, 16), ("llama8b.o", 4096, 4096, 4), ("llama8b.gate_up", 4096, 28672, 1),
-    ("llama8b.down", 14336, 4096, 16), ("qwen7b.gate_up", 3584, 37888, 1), ("qwen7b.lm_head", 3584, 152064, 1),
+    ("llama8b.down", 14336, 4096, 16), ("llama8b.gate_up", 4096, 28672, 16), ("llama8b.o", 4096, 4096, 16),
+    ("qwen7b.qkv", 3584, 4608, 1), ("qwen7b.o", 3584, 3584, 1), ("qwen7b.gate_up", 3584, 37888, 1),
+    ("qwen7b.down", 18944, 3584, 1), ("qwen7b.lm_head", 3584, 152064, 1),
     ("llama70b.gate_up", 8192, 57344, 256), ("llama70b.down", 28672, 8192, 256),
 ]
 
@@ -326,10 +369,9 @@ def test_w4a4_full_shapes_sampled_columns(name, K, N, M):
     oc, osc = oracle.quantize_act(x)
     assert np.array_equal(codes.cpu().numpy(), oc)
     out = torch.float32 if name.endswith("lm_head") else torch.bfloat16
-    wc, wm = weights_dev(w)
-    y = torch.empty((M, N), dtype=out, device=DEV)
-    q.qspec_gemm_w4a4(codes, scales, wc, wm, y)
-    tiles = np.sort(si.rng(N + 1).choice(N // 16, size=2, replace=False))
+    y, _ = run_w4a4(codes, scales, weights_dev(w), N, out)
+    tiles = sample_tiles(N // 16, 32, seed=N + 1)
+    rows = full_rows(M)
     sub = si.slice_tiles(w, tiles)
-    ref, _ = oracle.gemm_w4a4(oc, osc, sub["codes"], sub["meta"], want_dots=False)
-    assert_close(host_f64(y)[:, tile_columns(tiles)], ref, out == torch.bfloat16, name)
+    ref, _ = oracle.gemm_w4a4(oc[rows], osc[rows], sub["codes"], sub["meta"], want_dots=False)
+    assert_close(host_f64(y)[np.ix_(rows, tile_columns(tiles))], ref, out == torch.bfloat16, name)

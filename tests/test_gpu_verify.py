@@ -13,7 +13,7 @@ from scipy import stats
 import oracle
 import quantized_speculative_decoding_amd as q
 import synthetic_inputs as si
-from gpu_helpers import DEV, cu, note
+from gpu_helpers import DEV, Guarded, cu, note
 
 pytestmark = pytest.mark.gpu
 
@@ -23,14 +23,17 @@ NEAR_TIE = 1e-9
 def run_verify(mode, t, d, toks, u, v):
     B, g1, V = t.shape
     gamma = g1 - 1
-    acc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
-    out = torch.full((B, g1), -7, dtype=torch.int32, device=DEV)
-    ws = torch.empty((q.qspec_verify_workspace_bytes(mode, B, gamma, V),), dtype=torch.uint8, device=DEV)
+    acc = Guarded((B,), torch.int32, fill=-7)
+    out = Guarded((B, g1), torch.int32, fill=-7)
+    ws = Guarded((q.qspec_verify_workspace_bytes(mode, B, gamma, V),), torch.uint8)
     q.qspec_verify_accept(mode, cu(t), cu(d) if mode == q.QSPEC_SAMPLE else None,
                           cu(toks) if gamma > 0 else None,
                           cu(u) if mode == q.QSPEC_SAMPLE else None,
-                          cu(v) if mode == q.QSPEC_SAMPLE else None, acc, out, ws)
-    return acc.cpu().numpy(), out.cpu().numpy()
+                          cu(v) if mode == q.QSPEC_SAMPLE else None, acc.t, out.t, ws.t)
+    acc.check("verify_accept accept_count")
+    out.check("verify_accept out_tokens")
+    ws.check("verify_accept workspace")
+    return acc.t.cpu().numpy(), out.t.cpu().numpy()
 
 
 # gamma = 0 is the draft-side sampling head: one token per row from softmax(row) (or its argmax).
