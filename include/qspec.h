@@ -78,7 +78,8 @@ enum qspec_status {
     QSPEC_ERR_UNSUPPORTED = -3, /* unknown dtype or mode */
     QSPEC_ERR_HIP = -4,         /* a kernel launch failed */
     QSPEC_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than qspec_verify_workspace_bytes() */
-    QSPEC_ERR_ALIGN = -6        /* a pointer is not aligned as its call requires */
+    QSPEC_ERR_ALIGN = -6,       /* a pointer is not aligned as its call requires */
+    QSPEC_ERR_TOO_LARGE = -7    /* the problem needs more than a fixed scratch buffer holds */
 };
 
 enum qspec_out_dtype { QSPEC_OUT_BF16 = 0, QSPEC_OUT_F32 = 1 };
@@ -233,6 +234,27 @@ int qspec_verify_accept(int32_t mode, const float *target_logits, const float *d
                         const float *u_resample, int32_t B, int32_t gamma, int32_t V,
                         int32_t *accept_count, int32_t *out_tokens, void *workspace,
                         size_t workspace_bytes, qspec_stream_t stream);
+
+/*
+ * qspec_verify_accept_noalloc -- qspec_verify_accept without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, arithmetic and results as
+ * qspec_verify_accept; the chunk partials go to a fixed device scratch buffer of
+ * QSPEC_VERIFY_SCRATCH_BYTES inside the library (one per GPU, held until the process ends; its
+ * device address is looked up on the first call on each device).  The call allocates and frees
+ * nothing.  The scratch needs no initialization and keeps the last call's contents.  Every call
+ * on one GPU shares that GPU's buffer: calls that may overlap on one GPU (different streams, or
+ * host threads without ordering) race and must not be issued.
+ * Errors: those of qspec_verify_accept (no workspace errors); QSPEC_ERR_TOO_LARGE when
+ * qspec_verify_workspace_bytes(mode, B, gamma, V) exceeds QSPEC_VERIFY_SCRATCH_BYTES (1 MiB:
+ * e.g. B = 32, gamma = 4, V = 128256 in sampling mode needs about 90 KB); QSPEC_ERR_HIP when the
+ * scratch address cannot be obtained or a launch fails.
+ */
+#define QSPEC_VERIFY_SCRATCH_BYTES (1u << 20)
+int qspec_verify_accept_noalloc(int32_t mode, const float *target_logits, const float *draft_logits,
+                                const int32_t *draft_tokens, const float *u_accept,
+                                const float *u_resample, int32_t B, int32_t gamma, int32_t V,
+                                int32_t *accept_count, int32_t *out_tokens, qspec_stream_t stream);
 
 /*
  * qspec_draft_sample_workspace_bytes -- device workspace qspec_draft_sample needs; 0 on invalid

@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.qspec_verify_workspace_bytes.argtypes = [I, I, I, I]
         L.qspec_verify_workspace_bytes.restype = S
         L.qspec_verify_accept.argtypes = [I, P, P, P, P, P, I, I, I, P, P, P, S, P]
+        L.qspec_verify_accept_noalloc.argtypes = [I, P, P, P, P, P, I, I, I, P, P, P]
         L.qspec_kv_overwrite.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         L.qspec_speckv_workspace_bytes.argtypes = [I, I]
         L.qspec_speckv_workspace_bytes.restype = S
@@ -78,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.qspec_draft_sample.argtypes = [I, P, I, I, ctypes.c_int64, P, P, I, P, S, P]
         for fn in ("qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_verify_accept",
                    "qspec_kv_overwrite", "qspec_speckv_gamma", "qspec_attention", "qspec_quantize_act_fp8",
-                   "qspec_gemm_w8a8", "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier"):
+                   "qspec_gemm_w8a8", "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier", "qspec_verify_accept_noalloc"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -229,6 +230,31 @@ def qspec_verify_accept(mode, target_logits, draft_logits, draft_tokens, u_accep
                                      _ptr(u_resample) if mode == QSPEC_SAMPLE else None, B, gamma, V,
                                      _ptr(accept_count), _ptr(out_tokens), _ptr(workspace),
                                      workspace.numel(), _stream(stream, target_logits)))
+
+
+def qspec_verify_accept_noalloc(mode, target_logits, draft_logits, draft_tokens, u_accept, u_resample,
+                                accept_count, out_tokens, stream=None) -> None:
+    """qspec_verify_accept with the library's fixed device scratch instead of a workspace (for
+    callers that cannot allocate); calls that overlap on one GPU race."""
+    _req(target_logits, "target_logits", torch.float32)
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    if gamma > 0 or draft_tokens is not None:
+        _req(draft_tokens, "draft_tokens", torch.int32, (B, gamma))
+    if mode == QSPEC_SAMPLE:
+        if gamma > 0 or draft_logits is not None:
+            _req(draft_logits, "draft_logits", torch.float32, (B, gamma, V))
+        if gamma > 0 or u_accept is not None:
+            _req(u_accept, "u_accept", torch.float32, (B, gamma))
+        _req(u_resample, "u_resample", torch.float32, (B,))
+    _req(accept_count, "accept_count", torch.int32, (B,))
+    _req(out_tokens, "out_tokens", torch.int32, (B, g1))
+    _check("qspec_verify_accept_noalloc",
+           lib().qspec_verify_accept_noalloc(mode, _ptr(target_logits),
+                                             _ptr(draft_logits) if mode == QSPEC_SAMPLE else None,
+                                             _ptr(draft_tokens), _ptr(u_accept) if mode == QSPEC_SAMPLE else None,
+                                             _ptr(u_resample) if mode == QSPEC_SAMPLE else None, B, gamma, V,
+                                             _ptr(accept_count), _ptr(out_tokens), _stream(stream, target_logits)))
 
 
 def qspec_draft_sample_workspace_bytes(mode: int, B: int, V: int) -> int:

@@ -26,6 +26,11 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const float *a_scales, int M
 
 size_t verify_workspace_bytes(int mode, int B, int gamma, int V);
 
+// The fixed device scratch of the verification entry point that allocates nothing: its size, and
+// its address on the current device (looked up once per device).
+constexpr size_t kVerifyScratchBytes = (size_t)1 << 20;
+hipError_t verify_scratch(void **ptr);
+
 hipError_t launch_verify_accept(int mode, const float *target, const float *draft,
                                 const int32_t *draft_tokens, const float *u_accept,
                                 const float *u_resample, int B, int gamma, int V,

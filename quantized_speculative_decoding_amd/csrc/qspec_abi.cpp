@@ -47,6 +47,7 @@ QSPEC_EXPORT const char *qspec_status_string(int status) {
     case QSPEC_ERR_HIP: return "HIP launch failure";
     case QSPEC_ERR_WORKSPACE: return "workspace missing or too small";
     case QSPEC_ERR_ALIGN: return "misaligned pointer";
+    case QSPEC_ERR_TOO_LARGE: return "problem needs more scratch than the fixed buffer holds";
     default: return "unknown status";
     }
 }
@@ -153,6 +154,30 @@ QSPEC_EXPORT int qspec_verify_accept(int32_t mode, const float *target_logits,
                                                  u_accept, u_resample, B, gamma, V, accept_count,
                                                  out_tokens, workspace, as_stream(stream)));
 }
+
+QSPEC_EXPORT int qspec_verify_accept_noalloc(int32_t mode, const float *target_logits,
+                                             const float *draft_logits, const int32_t *draft_tokens,
+                                             const float *u_accept, const float *u_resample, int32_t B,
+                                             int32_t gamma, int32_t V, int32_t *accept_count,
+                                             int32_t *out_tokens, qspec_stream_t stream) {
+    if (mode != QSPEC_GREEDY && mode != QSPEC_SAMPLE) return QSPEC_ERR_UNSUPPORTED;
+    if (!target_logits || !accept_count || !out_tokens) return QSPEC_ERR_NULL;
+    if (gamma > 0 && !draft_tokens) return QSPEC_ERR_NULL;
+    if (mode == QSPEC_SAMPLE && (!u_resample || (gamma > 0 && (!draft_logits || !u_accept))))
+        return QSPEC_ERR_NULL;
+    if (!verify_sizes_ok(B, gamma, V)) return QSPEC_ERR_SHAPE;
+    if (qspec::verify_workspace_bytes(mode, B, gamma, V) > QSPEC_VERIFY_SCRATCH_BYTES) return QSPEC_ERR_TOO_LARGE;
+    if (!aligned(target_logits, 4) || !aligned(draft_logits, 4) || !aligned(draft_tokens, 4) ||
+        !aligned(u_accept, 4) || !aligned(u_resample, 4) || !aligned(accept_count, 4) || !aligned(out_tokens, 4))
+        return QSPEC_ERR_ALIGN;
+    void *ws = nullptr;
+    if (qspec::verify_scratch(&ws) != hipSuccess) return QSPEC_ERR_HIP;
+    return status_of(qspec::launch_verify_accept(mode, target_logits, draft_logits, draft_tokens, u_accept,
+                                                 u_resample, B, gamma, V, accept_count, out_tokens, ws,
+                                                 as_stream(stream)));
+}
+
+static_assert(qspec::kVerifyScratchBytes == QSPEC_VERIFY_SCRATCH_BYTES, "scratch size");
 
 static bool speckv_sizes_ok(int32_t R, int32_t V, int32_t max_gamma) {
     if (R < 1 || V < 1 || max_gamma < 0 || max_gamma > QSPEC_SPECKV_MAX_GAMMA) return false;

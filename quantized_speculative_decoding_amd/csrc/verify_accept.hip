@@ -22,6 +22,8 @@
 #include <float.h>
 #include <limits.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -735,6 +737,33 @@ hipError_t launch_verify_accept(int mode, const float *target, const float *draf
                                 hipStream_t st) {
     return launch_verify(mode, target, (size_t)V, draft, tokens, u_accept, u_resample, B, gamma, V, accept, out,
                          gamma + 1, ws, st);
+}
+
+// The verification's scratch for callers that cannot allocate: a fixed device array, one copy per
+// GPU, alive until the process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a registration handle); the device address comes from hipGetSymbolAddress, once
+// per device, on that device's first call.
+static __device__ __align__(256) unsigned char scratch[kVerifyScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+static void *scratch_ptr[kMaxScratchDevices];
+static std::mutex scratch_mutex;
+
+hipError_t verify_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return hipSuccess;
 }
 
 // The draft-side head: one token per row of a draft step's logits (row b at logits + b * ldt),

@@ -13,7 +13,7 @@ import quantized_speculative_decoding_amd as q
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qspec.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP, ERR_WS, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP, ERR_WS, ERR_ALIGN, ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5, -6, -7
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
 
 
@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
         "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma",
         "qspec_attention_workspace_bytes", "qspec_attention", "qspec_quantize_act_fp8",
         "qspec_gemm_w8a8_workspace_bytes", "qspec_gemm_w8a8", "qspec_draft_sample_workspace_bytes",
-        "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier"])
+        "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier", "qspec_verify_accept_noalloc"])
 
 
 def test_library_exports_every_declared_symbol_and_nothing_else():
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol_and_nothing_else():
 
 def test_status_strings():
     L = q.lib()
-    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP, ERR_WS, ERR_ALIGN):
+    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP, ERR_WS, ERR_ALIGN, ERR_TOO_LARGE):
         assert L.qspec_status_string(s)
     assert L.qspec_status_string(-99) == b"unknown status"
 
@@ -316,3 +316,30 @@ def test_gemm_32bit_range_limits():
     assert L.qspec_gemm_w4a4(FAKE, FAKE, 256, FAKE, FAKE, 2 ** 27, 16, FAKE, 0, None, None) == ERR_SHAPE
     assert L.qspec_gemm_w4a4(FAKE, FAKE, 1, FAKE, FAKE, 2 ** 29, 16, FAKE, 0, None, None) == ERR_SHAPE
     assert L.qspec_gemm_w4a4(FAKE, FAKE, 63, FAKE, FAKE, 2 ** 27, 16, odd, 0, None, None) == ERR_ALIGN
+
+
+def test_verify_accept_noalloc_validation():
+    """The scratch-buffer verification rejects what qspec_verify_accept rejects, and problems whose
+    workspace would exceed its fixed 1 MiB scratch, before touching the GPU."""
+    L = q.lib()
+    g = [0, FAKE, None, FAKE, None, None, 4, 4, 1000, FAKE, FAKE, None]
+    assert L.qspec_verify_accept_noalloc(5, *g[1:]) == ERR_UNSUPPORTED
+    bad = list(g); bad[1] = None
+    assert L.qspec_verify_accept_noalloc(*bad) == ERR_NULL
+    bad = list(g); bad[3] = None
+    assert L.qspec_verify_accept_noalloc(*bad) == ERR_NULL
+    s = [1, FAKE, FAKE, FAKE, FAKE, None, 4, 4, 1000, FAKE, FAKE, None]
+    assert L.qspec_verify_accept_noalloc(*s) == ERR_NULL            # sampling needs u_resample
+    bad = list(g); bad[6] = 0
+    assert L.qspec_verify_accept_noalloc(*bad) == ERR_SHAPE
+    cap = 1 << 20
+    # largest B that fits the scratch at gamma = 4, V = 128256, sampling; one more does not
+    fits = [B for B in (32, 64, 128, 256, 512, 1024)
+            if L.qspec_verify_workspace_bytes(1, B, 4, 128256) <= cap]
+    assert 32 in fits
+    too_big = next(B for B in (64, 128, 256, 512, 1024, 4096) if L.qspec_verify_workspace_bytes(1, B, 4, 128256) > cap)
+    s = [1, FAKE, FAKE, FAKE, FAKE, FAKE, too_big, 4, 128256, FAKE, FAKE, None]
+    assert L.qspec_verify_accept_noalloc(*s) == ERR_TOO_LARGE
+    odd = ctypes.c_void_p(0x1002)
+    s = [1, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 4, 128256, odd, FAKE, None]
+    assert L.qspec_verify_accept_noalloc(*s) == ERR_ALIGN
