@@ -1,23 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the shared-INT4 speculative-decoding hot path on one MI355X.
 
-One step = one QSPEC round over the projections of a Llama-3-8B-shaped model (32 layers of
-qkv 4096->6144, o 4096->4096, gate+up 4096->2x14336, down 14336->4096, each layer with its
-own shared INT4 group-128 weights: 3.65 GB, far beyond the 256 MB last-level cache), batch B
-(default 16) and gamma = 4:
+One step = one QSPEC round over a Llama-3-8B-shaped model's projections and vocabulary head (32
+layers of qkv 4096->6144, o 4096->4096, gate+up 4096->2x14336, down 14336->4096, each layer with
+its own shared INT4 group-128 weights: 3.65 GB, far beyond the 256 MB last-level cache; the head
+4096->128256, 275 MB), batch B (default 16) and gamma = 4:
   draft   gamma x (per layer and projection: qspec_quantize_act + qspec_gemm_w4a4 at M = B; then
-          qspec_draft_sample drawing each sequence's draft token from that step's rows of the
-          [B][gamma][V] draft logits, into the draft-token buffer the verification reads)
-  verify  per layer and projection: qspec_gemm_w4a16 at M = B (gamma + 1)
-  accept  qspec_verify_accept (speculative sampling) over a 128256-word vocabulary
+          the head: qspec_quantize_act + qspec_gemm_w4a4 at M = B writing that step's fp32 draft
+          logits, and qspec_draft_sample drawing each sequence's draft token from them into the
+          draft-token buffer the verification reads; the rows are kept as q_j)
+  verify  per layer and projection qspec_gemm_w4a16 at M = B (gamma + 1), then the head at
+          M = B (gamma + 1) writing the [B][gamma + 1][V] fp32 target logits
+  accept  qspec_verify_accept (speculative sampling) on those target and draft logits
   commit  qspec_kv_overwrite of the accepted rows in a 32-layer x 8-head x 4096 x 128 bf16 cache
-Attention, norms, activations and the vocabulary projection are not on this path; every
-projection reads fixed synthetic activations, so the launches of one phase are independent.
+Attention, norms and activation functions are not on this path: every projection reads fixed
+synthetic activations, and the head reads fixed hidden rows (draft step j and verify position j
+read the same row, so draft and target logits differ only by the W4A4 / W4A16 arithmetic on the
+shared weights).
 
-Each phase is captured once as a HIP graph and replayed; HIP events between phase replays
-time each phase.  The value is verify tokens/s: B (gamma + 1) positions per round over the
-measured round time.  The dominant GEMM phase's graph holds only that GEMM's launches, so its
-event time divided by the launch count is the kernel's average launch duration; with the
+Each phase of each draft step is captured once as a HIP graph and replayed; HIP events between
+phase replays time each phase.  The value is verify tokens/s: B (gamma + 1) positions per round
+over the measured round time.  The dominant GEMM phase's graphs hold only that GEMM's launches,
+so its event time divided by the launch count is the kernel's average launch duration; with the
 algorithmic bytes per launch it gives the roofline figure.
 """
 from __future__ import annotations
@@ -40,8 +44,10 @@ KV_HEADS, HEAD_DIM, CONTEXT = 8, 128, 4096
 
 
 def w4_bytes(K, N):
-    """Shared weight store: 4-bit codes + one 4-byte meta word (fp16 scale, zero) per 128-group."""
-    return K * N // 2 + 4 * N * (K // GROUP)
+    """Algorithmic bytes of the shared weights: 4-bit codes plus a binary16 scale and an 8-bit zero
+    point per (column, 128-group), 0.5234375 B per weight.  (The store's meta word pads the pair to
+    4 bytes, 0.53125 B per weight; the padding is the store's, not the method's.)"""
+    return K * N // 2 + 3 * N * (K // GROUP)
 
 
 def w4a4_alg_bytes(M, K, N):
@@ -195,6 +201,10 @@ def parse():
     ap.add_argument("--shape-table", metavar="OUT_MD",
                     help="time every GEMM shape of the workloads (W4A4 and W4A16, graph-replayed, weight copies "
                          "rotated beyond the last-level cache), write a markdown table to OUT_MD and exit")
+    ap.add_argument("--probe", metavar="LAYER:K:N:M",
+                    help="run one GEMM shape (LAYER w4a4 or w4a16) --probe-reps times on fresh weight copies "
+                         "and exit: a short program for rocprofv3 counter passes")
+    ap.add_argument("--probe-reps", type=int, default=4)
     ap.add_argument("--summary-command", default=PROFILE_COMMAND,
                     help="the command that produced the profiles (recorded in the summaries)")
     return ap.parse_args()
@@ -226,72 +236,100 @@ class Round:
         self.y_draft = [torch.empty((B, N), dtype=torch.bfloat16, device=dev) for _, (K, N) in self.projs]
         self.y_verify = [torch.empty((B * (g + 1), N), dtype=torch.bfloat16, device=dev) for _, (K, N) in self.projs]
         self.ws_verify = [q.gemm_w4a16_workspace(B * (g + 1), K, N, dev) for _, (K, N) in self.projs]
-        # verification: 4 rotating logit sets (4 x 74 MB at B = 16) so no replay reads a cached set
-        self.n_logit_sets = 4
-        self.logits = []
-        for s in range(self.n_logit_sets):
-            t, d = si.logits_device(B, g, VOCAB, seed=s, device=dev)
-            toks = si.draft_tokens_sampled_device(d, seed=s)
-            self.logits.append((t, d, toks, si.uniforms_device((B, g), seed=s, device=dev),
-                                si.uniforms_device((B,), seed=100 + s, device=dev)))
-        # the draft-side head's uniforms, [gamma][B] per logit set (one contiguous row per step)
-        self.head_u = [si.uniforms_device((g, B), seed=200 + s, device=dev) for s in range(self.n_logit_sets)]
-        self.ws_head = torch.empty((q.qspec_draft_sample_workspace_bytes(q.QSPEC_SAMPLE, B, VOCAB),),
+        # the vocabulary projection, shared by the draft (W4A4, fp32 logits per step) and the
+        # verifier (W4A16, fp32 logits of the gamma + 1 positions).  Draft step j reads hidden rows
+        # h_j [B][H]; the verifier reads the same rows at positions j < gamma (row b (gamma + 1) + j)
+        # and one more row at position gamma, so target and draft logits differ only by the W4A4 vs
+        # W4A16 arithmetic on the shared weights.
+        Kh, V = si.LLAMA3_8B_HEAD
+        self.V = V
+        self.w_head = si.weights_device(Kh, V, seed=7777, device=dev)
+        hid = si.activations_device(B * (g + 1), Kh, seed=30, device=dev).view(B, g + 1, Kh)
+        self.x_head_verify = hid.reshape(B * (g + 1), Kh).contiguous()
+        self.x_head_draft = [hid[:, j, :].contiguous() for j in range(g)]
+        self.head_codes = torch.empty((B, Kh // 2), dtype=torch.uint8, device=dev)
+        self.head_scales = torch.empty((B, Kh // GROUP), dtype=torch.float32, device=dev)
+        self.q_step = torch.empty((B, V), dtype=torch.float32, device=dev)          # one step's draft logits
+        self.draft_logits = torch.empty((B, g, V), dtype=torch.float32, device=dev)
+        self.target_logits = torch.empty((B, g + 1, V), dtype=torch.float32, device=dev)
+        self.ws_head_verify = q.gemm_w4a16_workspace(B * (g + 1), Kh, V, dev)
+        self.draft_tokens = torch.zeros((B, g), dtype=torch.int32, device=dev)
+        self.head_u = si.uniforms_device((g, B), seed=200, device=dev)               # draft-side draws
+        self.u_accept = si.uniforms_device((B, g), seed=201, device=dev)
+        self.u_resample = si.uniforms_device((B,), seed=202, device=dev)
+        self.ws_head = torch.empty((q.qspec_draft_sample_workspace_bytes(q.QSPEC_SAMPLE, B, V),),
                                    dtype=torch.uint8, device=dev)
         self.accept = torch.zeros((B,), dtype=torch.int32, device=dev)
         self.out_tokens = torch.zeros((B, g + 1), dtype=torch.int32, device=dev)
-        self.ws = torch.empty((q.qspec_verify_workspace_bytes(q.QSPEC_SAMPLE, B, g, VOCAB),), dtype=torch.uint8,
+        self.ws = torch.empty((q.qspec_verify_workspace_bytes(q.QSPEC_SAMPLE, B, g, V),), dtype=torch.uint8,
                               device=dev)
         # KV cache and the verifier's staging rows
         self.cache = torch.zeros((L, B, 2, KV_HEADS, CONTEXT, HEAD_DIM), dtype=torch.bfloat16, device=dev)
         self.stage = torch.randn((L, B, 2, KV_HEADS, g + 1, HEAD_DIM), device=dev).to(torch.bfloat16)
         self.start = torch.from_numpy(si.start_positions(B, CONTEXT, g, seed=0)).to(dev)
 
-    # ---- phases
-    def quant(self):
+    # ---- phases (draft step j: quantize, W4A4 layers and head, draft-side sampling head)
+    def quant(self, j):
         for l in range(self.L):
             for i in range(len(self.projs)):
                 self.q.qspec_quantize_act(self.x_draft[i], self.codes[l][i], self.ascales[l][i])
+        self.q.qspec_quantize_act(self.x_head_draft[j], self.head_codes, self.head_scales)
 
-    def draft_gemm(self):
+    def draft_gemm(self, j):
         for l in range(self.L):
             for i in range(len(self.projs)):
                 wc, wm = self.weights[l][i]
                 self.q.qspec_gemm_w4a4(self.codes[l][i], self.ascales[l][i], wc, wm, self.y_draft[i])
+        self.q.qspec_gemm_w4a4(self.head_codes, self.head_scales, *self.w_head, self.q_step)
+
+    def draft_head(self, j):
+        self.q.qspec_draft_sample(self.q.QSPEC_SAMPLE, self.q_step, self.draft_tokens[:, j], self.head_u[j],
+                                  self.ws_head)
+        self.draft_logits[:, j, :].copy_(self.q_step)        # q_j for the verification
 
     def verify_gemm(self):
         for l in range(self.L):
             for i in range(len(self.projs)):
                 wc, wm = self.weights[l][i]
                 self.q.qspec_gemm_w4a16(self.x_verify[i], wc, wm, self.y_verify[i], self.ws_verify[i])
+        self.q.qspec_gemm_w4a16(self.x_head_verify, *self.w_head, self.target_logits.view(-1, self.V),
+                                self.ws_head_verify)
 
     def plain_gemm(self):
-        """One plain W4A16 decoding step (M = B) over the same layers: the round model's T_target."""
+        """One plain W4A16 decoding step (M = B) over the same layers and the head: T_target."""
         for l in range(self.L):
             for i in range(len(self.projs)):
                 wc, wm = self.weights[l][i]
                 self.q.qspec_gemm_w4a16(self.x_draft[i], wc, wm, self.y_draft[i])
+        self.q.qspec_gemm_w4a16(self.x_head_draft[0], *self.w_head, self.q_step)
 
-    def draft_head(self, s, j):
-        t, d, toks, u, v = self.logits[s]
-        self.q.qspec_draft_sample(self.q.QSPEC_SAMPLE, d[:, j, :], toks[:, j], self.head_u[s][j], self.ws_head)
-
-    def accept_phase(self, s):
-        t, d, toks, u, v = self.logits[s]
-        self.q.qspec_verify_accept(self.q.QSPEC_SAMPLE, t, d, toks, u, v, self.accept, self.out_tokens, self.ws)
+    def accept_phase(self):
+        self.q.qspec_verify_accept(self.q.QSPEC_SAMPLE, self.target_logits, self.draft_logits, self.draft_tokens,
+                                   self.u_accept, self.u_resample, self.accept, self.out_tokens, self.ws)
 
     def commit(self):
         self.q.qspec_kv_overwrite(self.cache, self.stage, self.start, self.accept)
 
     # ---- algorithmic work per phase
     def draft_gemm_bytes(self):
-        return self.L * sum(w4a4_alg_bytes(self.B, K, N) for _, (K, N) in self.projs)
+        """One draft step's W4A4 launches: the layers' projections and the head (fp32 logits)."""
+        Kh, V = self.w_head_shape()
+        return (self.L * sum(w4a4_alg_bytes(self.B, K, N) for _, (K, N) in self.projs)
+                + w4a4_alg_bytes(self.B, Kh, V) + 2 * self.B * V)
 
     def verify_gemm_bytes(self):
-        return self.L * sum(w4a16_alg_bytes(self.B * (self.gamma + 1), K, N) for _, (K, N) in self.projs)
+        Kh, V = self.w_head_shape()
+        M = self.B * (self.gamma + 1)
+        return (self.L * sum(w4a16_alg_bytes(M, K, N) for _, (K, N) in self.projs)
+                + w4a16_alg_bytes(M, Kh, V) + 2 * M * V)
+
+    def w_head_shape(self):
+        import synthetic_inputs as si
+
+        return si.LLAMA3_8B_HEAD
 
     def launches_per_gemm_phase(self):
-        return self.L * len(self.projs)
+        return self.L * len(self.projs) + 1
 
 
 def capture(fn, torch):
@@ -315,62 +353,66 @@ def gpu_leg(args):
     R = Round(args, dev)
     torch.cuda.synchronize()
 
+    def eager_round():
+        for j in range(R.gamma):
+            R.quant(j); R.draft_gemm(j); R.draft_head(j)
+        R.verify_gemm(); R.accept_phase(); R.commit()
+
     # eager reference outputs, then the captured phases
-    R.quant(); R.draft_gemm()
-    for j in range(R.gamma):
-        R.draft_head(0, j)
-    R.verify_gemm(); R.accept_phase(0); R.commit()
+    eager_round()
     torch.cuda.synchronize()
-    ref = (R.y_draft[2].clone(), R.y_verify[3].clone(), R.accept.clone(), R.out_tokens.clone())
-    g_quant = capture(R.quant, torch)
-    g_draft = capture(R.draft_gemm, torch)
+    ref = (R.y_draft[2].clone(), R.y_verify[3].clone(), R.draft_tokens.clone(), R.accept.clone(),
+           R.out_tokens.clone(), R.target_logits[:, :, :64].clone())
+    g_quant = [capture(lambda j=j: R.quant(j), torch) for j in range(R.gamma)]
+    g_draft = [capture(lambda j=j: R.draft_gemm(j), torch) for j in range(R.gamma)]
+    g_head = [capture(lambda j=j: R.draft_head(j), torch) for j in range(R.gamma)]
     g_verify = capture(R.verify_gemm, torch)
-    g_head = [[capture(lambda s=s, j=j: R.draft_head(s, j), torch) for j in range(R.gamma)]
-              for s in range(R.n_logit_sets)]
-    g_accept = [capture(lambda s=s: R.accept_phase(s), torch) for s in range(R.n_logit_sets)]
+    g_accept = capture(R.accept_phase, torch)
     g_commit = capture(R.commit, torch)
 
     phases = ["quantize_act", "gemm_w4a4", "draft_head", "gemm_w4a16", "verify_accept", "kv_overwrite"]
     n_ev = R.gamma * 3 + 4
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
 
-    def step(i, ev):
+    def step(ev):
         k = 0
         if ev: ev[k].record(); k += 1
         for j in range(R.gamma):
-            g_quant.replay()
+            g_quant[j].replay()
             if ev: ev[k].record(); k += 1
-            g_draft.replay()
+            g_draft[j].replay()
             if ev: ev[k].record(); k += 1
-            g_head[i % R.n_logit_sets][j].replay()
+            g_head[j].replay()
             if ev: ev[k].record(); k += 1
         g_verify.replay()
         if ev: ev[k].record(); k += 1
-        g_accept[i % R.n_logit_sets].replay()
+        g_accept.replay()
         if ev: ev[k].record(); k += 1
         g_commit.replay()
         if ev: ev[k].record(); k += 1
 
-    for i in range(args.warmup):
-        step(i, None)
+    # one untimed round of replays (the captures above ran each phase once, out of round order),
+    # then the warm-up rounds
+    for i in range(1 + args.warmup):
+        step(None)
     torch.cuda.synchronize()
-    # replays reproduce the eager outputs (logit set 0 is replayed at i = 0 below)
-    g_accept[0].replay()
-    torch.cuda.synchronize()
+    # replays reproduce the eager outputs (every round recomputes the same inputs)
     same = (torch.equal(R.y_draft[2], ref[0]) and torch.equal(R.y_verify[3], ref[1])
-            and torch.equal(R.accept, ref[2]) and torch.equal(R.out_tokens, ref[3]))
+            and torch.equal(R.draft_tokens, ref[2]) and torch.equal(R.accept, ref[3])
+            and torch.equal(R.out_tokens, ref[4]) and torch.equal(R.target_logits[:, :, :64], ref[5]))
     if not same:
         raise SystemExit("graph replay differs from the eager run")
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-phase times from the events (ms)
+    # per-phase times from the events (ms), and each round's own time
     ph = {p: 0.0 for p in phases}
+    per_round = []
     for ev in evs:
         k = 0
         for _ in range(R.gamma):
@@ -380,6 +422,7 @@ def gpu_leg(args):
         ph["gemm_w4a16"] += ev[k].elapsed_time(ev[k + 1]); k += 1
         ph["verify_accept"] += ev[k].elapsed_time(ev[k + 1]); k += 1
         ph["kv_overwrite"] += ev[k].elapsed_time(ev[k + 1]); k += 1
+        per_round.append(ev[0].elapsed_time(ev[n_ev - 1]))
     ph = {p: v / args.steps for p, v in ph.items()}
     event_ms = sum(ph.values())
 
@@ -389,7 +432,9 @@ def gpu_leg(args):
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
+    R.per_round_ms = per_round
     R.model = round_model(R, ph, torch)
+    R.verify_tps = verify_tokens_per_s(R, torch)
     R.speckv_us = speckv_controller_us(R, torch)
     R.attention = attention_us(R, torch)
     R.fp8 = fp8_parent_us(R, torch)
@@ -400,8 +445,9 @@ def gpu_leg(args):
 def round_model(R, ph, torch):
     """Outside the timed round: the speedup model S = E[L] T_target / (T_draft + T_verify +
     T_overhead) with every time measured here (T_target = one plain W4A16 decoding step at M = B
-    over the same layers, graph-replayed) and E[L] both as the round's accept counts give it (mean
-    A + 1 over the 4 logit sets) and as (1 - a^(gamma+1)) / (1 - a) at a few acceptance rates a."""
+    over the same layers and the head, graph-replayed), E[L] as the round's accept counts give it
+    (mean A + 1 over the B sequences), and S at a few acceptance rates a through
+    E[L] = (1 - a^(gamma+1)) / (1 - a)."""
     graph = capture(R.plain_gemm, torch)
     graph.replay()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -412,11 +458,8 @@ def round_model(R, ph, torch):
     b.record()
     torch.cuda.synchronize()
     t_target = a.elapsed_time(b) / 5
-    counts = []
-    for s_ in range(R.n_logit_sets):
-        R.accept_phase(s_)
-        counts.append(R.accept.cpu().clone())
-    e_l = float(torch.cat(counts).double().mean()) + 1.0
+    acc = R.accept.cpu().double()
+    e_l = float(acc.mean()) + 1.0
     t_draft = ph["quantize_act"] + ph["gemm_w4a4"] + ph["draft_head"]
     t_verify = ph["gemm_w4a16"]
     t_over = ph["verify_accept"] + ph["kv_overwrite"]
@@ -424,18 +467,62 @@ def round_model(R, ph, torch):
     g = R.gamma
     at = {al: (1 - al ** (g + 1)) / (1 - al) * t_target / t_round for al in (0.6, 0.8, 0.9)}
     return {"T_target_ms": round(t_target, 4), "T_draft_ms": round(t_draft, 4), "T_verify_ms": round(t_verify, 4),
-            "T_overhead_ms": round(t_over, 4), "E_L_measured": round(e_l, 4),
-            "S_measured_E_L": round(e_l * t_target / t_round, 3),
+            "T_overhead_ms": round(t_over, 4), "accept_counts": [int(v) for v in R.accept.cpu().tolist()],
+            "E_L_measured": round(e_l, 4), "S_measured_E_L": round(e_l * t_target / t_round, 3),
             "S_at_alpha": {str(k): round(v, 3) for k, v in at.items()}}
+
+
+def verify_tokens_per_s(R, torch, batches=(1, 4, 16)):
+    """Outside the timed round: verify tokens/s at this gamma as the verify GEMMs alone bound it,
+    B (gamma + 1) / (sum of the four projections' W4A16 times at M = B (gamma + 1)), per layer and
+    for the whole stack, with the HBM roofline bound from the algorithmic bytes at 8 TB/s.  One
+    graph over all layers' projections (each layer its own weights, beyond the last-level cache),
+    replayed 5 x 3 times; median."""
+    import synthetic_inputs as si
+
+    q, dev, g = R.q, R.accept.device, R.gamma
+    out = {}
+    for B in batches:
+        M = B * (g + 1)
+        xs = [si.activations_device(M, K, seed=40 + i, device=dev) for i, (_, (K, N)) in enumerate(R.projs)]
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, (K, N) in R.projs]
+        wss = [q.gemm_w4a16_workspace(M, K, N, dev) for _, (K, N) in R.projs]
+
+        def fn():
+            for l in range(R.L):
+                for i in range(len(R.projs)):
+                    wc, wm = R.weights[l][i]
+                    q.qspec_gemm_w4a16(xs[i], wc, wm, ys[i], wss[i])
+
+        graph = capture(fn, torch)
+        graph.replay()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(3):
+                graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 3)
+        t_layer_us = sorted(ts)[2] * 1e3 / R.L
+        roof_us = sum(w4a16_alg_bytes(M, K, N) for _, (K, N) in R.projs) / (HBM_PEAK_GBS * 1e9) * 1e6
+        out[f"B{B}"] = {"M": M, "layer_us": round(t_layer_us, 2), "tokens_per_s_per_layer": round(M / (t_layer_us * 1e-6), 1),
+                        "tokens_per_s_32_layers": round(M / (t_layer_us * 1e-6) / 32, 1),
+                        "roofline_tokens_per_s_per_layer": round(M / (roof_us * 1e-6), 1),
+                        "fraction_of_roofline": round(roof_us / t_layer_us, 4)}
+        del graph, xs, ys, wss
+    return out
 
 
 def speckv_controller_us(R, torch):
     """Outside the timed round: the adaptive-gamma controller (draft confidence and entropy over
-    one draft row per sequence, then its MLP) on the round's draft logits, graph-replayed over the
-    4 logit sets; random controller weights (the trained ones are not published)."""
-    q, B, V = R.q, R.B, VOCAB
+    one draft row per sequence, then its MLP) on the round's draft logits (the W4A4 head's rows of
+    each draft step), graph-replayed; random controller weights (the trained ones are not
+    published)."""
+    q, B, V = R.q, R.B, R.V
     dev = R.accept.device
-    rows = [d[:, -1, :].contiguous() for (_, d, _, _, _) in R.logits]       # the last draft step
+    rows = [R.draft_logits[:, j, :].contiguous() for j in range(R.gamma)]   # one row set per draft step
     gen = torch.Generator(device=dev).manual_seed(900)
     w1, b1 = torch.randn((64, 3), device=dev, generator=gen), torch.randn((64,), device=dev, generator=gen)
     w2, b2 = torch.randn((9, 64), device=dev, generator=gen), torch.randn((9,), device=dev, generator=gen)
@@ -580,62 +667,118 @@ def fp8_parent_us(R, torch, gamma=4):
     return res
 
 
-def cpu_leg(args):
-    """The oracle, as written, on a bounded sample of one round, scaled to a whole round."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def cpu_leg(args, repeats: int = 5):
+    """The oracle, as written, on a bounded sample of one round, scaled to a whole round: timed on
+    one host thread, and with the sample's GEMM columns split over the host's threads (the oracle's
+    calls release the GIL, so a thread pool runs them in parallel on disjoint column tiles); the
+    median of `repeats` passes of each."""
+    import concurrent.futures
+
     import numpy as np
 
     import oracle
     import synthetic_inputs as si
 
     B, g, L = args.batch, args.gamma, args.layers
-    frac = 16           # every projection is sampled on 1/frac of its output columns
-    est = 0.0
-    t_start = time.perf_counter()
-    parts = {}
+    frac, frac_head = 64, 256      # projections on 1/64 of their columns, the head on 1/256
+    Kh, V = si.LLAMA3_8B_HEAD
+    threads = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()))
+    def cols(N, fr):                # whole 16-column tiles, about N / fr columns
+        return 16 * max(1, N // 16 // fr)
+
+    items = []        # (layers, draft steps, column scale, weights, draft rows, verify rows)
     for i, (name, (K, N)) in enumerate(si.LLAMA3_8B_PROJ.items()):
-        Ns = N // frac
-        w = si.weights(K, Ns, seed=i)
-        xd = si.activations(B, K, seed=10 + i)
-        xv = si.activations(B * (g + 1), K, seed=20 + i)
-        t0 = time.perf_counter()
-        c, s = oracle.quantize_act(xd)
-        t1 = time.perf_counter()
-        oracle.gemm_w4a4(c, s, w["codes"], w["meta"], want_dots=False)
-        t2 = time.perf_counter()
-        oracle.gemm_w4a16(xv, w["codes"], w["meta"])
-        t3 = time.perf_counter()
-        parts[name] = (t1 - t0, t2 - t1, t3 - t2)
-        est += L * (g * ((t1 - t0) + frac * (t2 - t1)) + frac * (t3 - t2))
-    t, d = si.logits(B, g, VOCAB, seed=0)
+        n = cols(N, frac)
+        items.append((L, g, N / n, si.weights(K, n, seed=i), si.activations(B, K, seed=10 + i),
+                      si.activations(B * (g + 1), K, seed=20 + i)))
+    n = cols(V, frac_head)
+    items.append((1, g, V / n, si.weights(Kh, n, seed=99), si.activations(B, Kh, seed=30),
+                  si.activations(B * (g + 1), Kh, seed=31)))
+    t_logits, d_logits = si.logits(B, g, V, seed=0)
     hu = si.uniforms((g, B), 2)
-    toks = np.empty((B, g), np.int32)
-    t0 = time.perf_counter()
-    for j in range(g):              # the draft-side head: verification with gamma = 0 on step j's rows
-        _, o, _ = oracle.verify_sample(d[:, j:j + 1, :], np.zeros((B, 0, VOCAB), np.float32),
-                                       np.zeros((B, 0), np.int32), np.zeros((B, 0), np.float32), hu[j],
-                                       with_diag=False)
-        toks[:, j] = o[:, 0]
     u, v = si.uniforms((B, g), 0), si.uniforms((B,), 1)
-    acc, _, _ = oracle.verify_sample(t, d, toks, u, v, with_diag=False)
-    est += time.perf_counter() - t0
-    # KV: one layer of the cache at a short context (the copy cost does not depend on T)
-    cache = si.kv_canary(1, B, KV_HEADS, 64, HEAD_DIM).reshape(1, B, 2, KV_HEADS, 64, HEAD_DIM)
-    stage = si.kv_staging(1, B, KV_HEADS, g, HEAD_DIM, seed=0)
-    start = si.start_positions(B, 64, g, seed=0)
-    t0 = time.perf_counter()
-    oracle.kv_overwrite(cache, stage, start, acc)
-    est += L * (time.perf_counter() - t0)
+    kv_cache = si.kv_canary(1, B, KV_HEADS, 64, HEAD_DIM).reshape(1, B, 2, KV_HEADS, 64, HEAD_DIM)
+    kv_stage = si.kv_staging(1, B, KV_HEADS, g, HEAD_DIM, seed=0)
+    kv_start = si.start_positions(B, 64, g, seed=0)
+
+    def gemms(w, c, s, xv, pool):
+        """W4A4 at M = B and W4A16 at M = B (gamma + 1) on the slice's column tiles; with a pool, the
+        tiles are split into one contiguous range per thread."""
+        T = w["codes"].shape[0]
+        if pool is None:
+            parts = [np.arange(T)]
+        else:
+            parts = [p for p in np.array_split(np.arange(T), threads) if len(p)]
+        subs = [si.slice_tiles(w, p) for p in parts]
+        f4 = lambda sub: oracle.gemm_w4a4(c, s, sub["codes"], sub["meta"], want_dots=False)
+        f16 = lambda sub: oracle.gemm_w4a16(xv, sub["codes"], sub["meta"])
+        t0 = time.perf_counter()
+        if pool is None:
+            f4(subs[0])
+        else:
+            list(pool.map(f4, subs))
+        t1 = time.perf_counter()
+        if pool is None:
+            f16(subs[0])
+        else:
+            list(pool.map(f16, subs))
+        return t1 - t0, time.perf_counter() - t1
+
+    def one_pass(pool):
+        est = 0.0
+        for (layers, steps, fr, w, xd, xv) in items:
+            t0 = time.perf_counter()
+            c, s = oracle.quantize_act(xd)
+            tq = time.perf_counter() - t0
+            t4, t16 = gemms(w, c, s, xv, pool)
+            est += layers * (steps * (tq + fr * t4) + fr * t16)
+        t0 = time.perf_counter()
+        toks = np.empty((B, g), np.int32)
+        for j in range(g):          # the draft-side head: verification with gamma = 0 on step j's rows
+            _, o, _ = oracle.verify_sample(d_logits[:, j:j + 1, :], np.zeros((B, 0, V), np.float32),
+                                           np.zeros((B, 0), np.int32), np.zeros((B, 0), np.float32), hu[j],
+                                           with_diag=False)
+            toks[:, j] = o[:, 0]
+        acc, _, _ = oracle.verify_sample(t_logits, d_logits, toks, u, v, with_diag=False)
+        est += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.kv_overwrite(kv_cache.copy(), kv_stage, kv_start, acc)
+        est += L * (time.perf_counter() - t0)
+        return est
+
+    t_start = time.perf_counter()
+    single = sorted(one_pass(None) for _ in range(repeats))[repeats // 2]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as pool:
+        multi = sorted(one_pass(pool) for _ in range(repeats))[repeats // 2]
     spent = time.perf_counter() - t_start
+    tok = B * (g + 1)
     return {
-        "value": B * (g + 1) / est,
+        "value": round(tok / multi, 4),
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"one layer of each projection on 1/{frac} of its columns (draft quantize + W4A4 at M={B}, "
-                   f"verify W4A16 at M={B * (g + 1)}), {g} full draft heads and the full verify_accept (sampling, "
-                   f"B={B}, V={VOCAB}), "
-                   f"one KV layer; scaled x{L} layers, x{g} draft steps, x{frac} columns; "
-                   f"estimated round {est:.1f} s from {spent:.1f} s of single-threaded CPU work"),
+        "cpu_model": cpu_model(),
+        "single_thread_tokens_per_s": round(tok / single, 5),
+        "round_s_single_thread": round(single, 1),
+        "round_s_threads": round(multi, 1),
+        "sample": (f"one layer of each projection on 1/{frac} of its columns and the vocabulary head on "
+                   f"1/{frac_head} (quantize + W4A4 at M={B}, W4A16 at M={B * (g + 1)}), {g} full draft-side "
+                   f"heads and the full verify_accept (sampling, B={B}, V={V}), one KV layer; scaled x{L} layers, "
+                   f"x{g} draft steps and by the column fractions; median of {repeats} passes on 1 thread and on "
+                   f"{threads} threads (GEMM column tiles split over a thread pool); {spent:.1f} s of CPU work "
+                   f"in all"),
     }
 
 
@@ -736,8 +879,41 @@ def shape_table(args):
     print("wrote", args.shape_table)
 
 
+def probe(args):
+    """One GEMM shape, launched eagerly --probe-reps times over distinct weight copies (each read
+    from HBM), for counter collection; prints the shape and exits."""
+    import torch
+
+    import quantized_speculative_decoding_amd as q
+    import synthetic_inputs as si
+
+    layer, K, N, M = args.probe.split(":")
+    K, N, M = int(K), int(N), int(M)
+    dev = torch.device("cuda:0")
+    W = [si.weights_device(K, N, seed=c, device=dev) for c in range(args.probe_reps)]
+    x = si.activations_device(M, K, seed=3, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if layer == "w4a4":
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((M, K // GROUP), dtype=torch.float32, device=dev)
+        q.qspec_quantize_act(x, codes, sc)
+        for wc, wm in W:
+            q.qspec_gemm_w4a4(codes, sc, wc, wm, y)
+    elif layer == "w4a16":
+        ws = q.gemm_w4a16_workspace(M, K, N, dev)
+        for wc, wm in W:
+            q.qspec_gemm_w4a16(x, wc, wm, y, ws)
+    else:
+        raise SystemExit(f"unknown layer {layer!r}")
+    torch.cuda.synchronize()
+    print(f"probe {layer} K={K} N={N} M={M} x{args.probe_reps}", flush=True)
+
+
 def main():
     args = parse()
+    if args.probe:
+        probe(args)
+        return
     if args.summarize:
         summarize(args)
         return
@@ -752,6 +928,8 @@ def main():
     B, g = args.batch, args.gamma
     ms_per_step = wall * 1e3 / args.steps
     value = B * (g + 1) / (ms_per_step / 1e3)
+    rounds = sorted(R.per_round_ms)
+    pct = lambda p: rounds[min(len(rounds) - 1, int(round(p * (len(rounds) - 1))))]
     nl = R.launches_per_gemm_phase()
     draft_ms = ph["gemm_w4a4"]                     # gamma draft passes per round
     verify_ms = ph["gemm_w4a16"]
@@ -785,10 +963,12 @@ def main():
         "vs_baseline": None,
         "dtype": "i8+bf16",
         "data": "synthetic",
-        "config": {"workload": f"llama3-8b-projections-{args.layers}L-qspec-round-B{B}-gamma{g}",
+        "config": {"workload": f"llama3-8b-projections-{args.layers}L-and-head-qspec-round-B{B}-gamma{g}",
                    "batch": B, "gamma": g, "layers": args.layers, "draft_M": B, "verify_M": B * (g + 1),
-                   "vocab": VOCAB, "kv_cache": f"{args.layers}x{B}x2x{KV_HEADS}x{CONTEXT}x{HEAD_DIM} bf16",
+                   "vocab": R.V, "head": "4096x128256 shared INT4: W4A4 draft logits per step, W4A16 target logits",
+                   "kv_cache": f"{args.layers}x{B}x2x{KV_HEADS}x{CONTEXT}x{HEAD_DIM} bf16",
                    "verify_mode": "sample"},
+        "round_ms": {"median": round(pct(0.5), 4), "p10": round(pct(0.1), 4), "p90": round(pct(0.9), 4)},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": int(bytes_per_launch), "us_per_launch": round(avg_launch_ms * 1e3, 3),
@@ -798,7 +978,7 @@ def main():
         "gemm_hbm_tbs": {"gemm_w4a4_M%d" % B: round(R.draft_gemm_bytes() * g / (draft_ms / 1e3) / 1e12, 3),
                          "gemm_w4a16_M%d" % (B * (g + 1)): round(R.verify_gemm_bytes() / (verify_ms / 1e3) / 1e12, 3)},
         # outside the timed round: the round-time and speedup model from these measurements
-        # (projections only: attention, norms and the vocabulary projection are not in T_target)
+        # (projections and head only: attention and norms are not in T_target)
         "round_model": R.model,
         # outside the timed round: the adaptive-gamma controller on one draft row per sequence
         "speckv_controller_us": round(R.speckv_us, 1),
@@ -827,10 +1007,9 @@ def main():
                    "kv_hbm_frac": round(2 * rows * 32 * args.layers * 2 * KV_HEADS * HEAD_DIM * 2 / (tk * 1e-6) / 1e9
                                         / HBM_PEAK_GBS, 4)}
             for name, (ta, tk, rows) in R.verify_commit.items()},
-        # verify tokens/s at this gamma as the verify GEMMs alone bound it: B (gamma + 1) tokens per
-        # pass over the layers' four projections (W4A16 at M = B (gamma + 1)), whole stack and per layer
-        "verify_gemm_tokens_per_s": {"layers_%d" % args.layers: round(B * (g + 1) / (verify_ms / 1e3), 1),
-                                     "per_layer": round(B * (g + 1) / (verify_ms / 1e3 / args.layers), 1)},
+        # verify tokens/s at gamma = 4: B (gamma + 1) / (sum of one layer's four W4A16 projections at
+        # M = B (gamma + 1)), measured over all layers at B = 1, 4, 16, with the HBM roofline bound
+        "verify_tokens_per_s": R.verify_tps,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_leg(args)

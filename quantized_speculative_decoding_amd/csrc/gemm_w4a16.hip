@@ -283,15 +283,22 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     const int col = lane & 15, kq = lane >> 4;
     const int G = K / kGroup;
     const int T = N / 16;
-    // Workgroup -> (column block, split, row block).  A 1-D grid (gridDim.y == 1, the large tier)
-    // walks row blocks fastest, then splits, inside each XCD's contiguous range of tiles, so the
-    // workgroups that share a column block's weights run together on one XCD and its L2.
+    // Workgroup -> (column block, split, row block).  A 1-D grid is remapped so that each XCD owns
+    // a contiguous range of logical tiles.  Large tier (row_blocks > 1): row blocks fastest, then
+    // splits, so the workgroups that share a column block's weights run together on one XCD and its
+    // L2.  Verify tier (one row block): column blocks fastest, then splits, so the workgroups of one
+    // split, which read the same activation slice, share one or two XCDs.
     int cblk = blockIdx.x, split = blockIdx.y, rblk = 0;
     if (gridDim.y == 1 && row_blocks > 1) {
         const int t = xcd_remap((int)blockIdx.x, (int)gridDim.x);
         rblk = t % row_blocks;
         split = (t / row_blocks) % S;
         cblk = t / row_blocks / S;
+    } else if (gridDim.y == 1 && S > 1) {
+        const int t = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+        const int cbs = (int)gridDim.x / S;
+        cblk = t % cbs;
+        split = t / cbs;
     }
     const int m0 = rblk * MT * 16;           // this workgroup's row block
     const int Mb = min(MT * 16, M - m0);
@@ -703,7 +710,8 @@ static hipError_t launch_mid(const uint16_t *x, int M, const uint8_t *codes, con
     const int S = mid_splits(K, N);
     const int cbs = (N / 16 + MID_TILES - 1) / MID_TILES;
     float *partials = S > 1 ? (float *)ws : nullptr;
-    hipLaunchKernelGGL((k_w4a16_lds<MT, U, MID_KP, MID_CW>), dim3(cbs, S), dim3(MID_KP * MID_CW * 64), 0, st, x,
+    // one 1-D grid of cbs x S workgroups, remapped split-major inside the kernel (S > 1)
+    hipLaunchKernelGGL((k_w4a16_lds<MT, U, MID_KP, MID_CW>), dim3(cbs * S), dim3(MID_KP * MID_CW * 64), 0, st, x,
                        M, codes, meta, K, N, y, y_f32, S, partials, 1);
     if (S > 1) launch_splitk_reduce(partials, S, M, N, y, y_f32, st);
     return hipGetLastError();

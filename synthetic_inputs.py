@@ -188,6 +188,7 @@ def attention_inputs(B: int, Q: int, Hq: int, Hkv: int, T: int, D: int, seed: in
 
 LLAMA3_8B_PROJ = {"qkv": (4096, 6144), "o": (4096, 4096), "gate_up": (4096, 2 * 14336),
                   "down": (14336, 4096)}
+LLAMA3_8B_HEAD = (4096, 128256)          # the vocabulary projection (hidden -> vocabulary)
 QWEN25_7B_PROJ = {"qkv": (3584, 4608), "o": (3584, 3584), "gate_up": (3584, 2 * 18944),
                   "down": (18944, 3584), "lm_head": (3584, 152064)}
 LLAMA3_70B_FFN = {"gate_up": (8192, 2 * 28672), "down": (28672, 8192)}
