@@ -64,7 +64,7 @@ COPY_MIB = 256
 
 
 # How the summaries under profiles/ are made (OUT = an output folder, REPO = this repository).
-PROFILE_COMMAND = ('cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o bench -- python3 REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline ; rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/prof_fetch -o bench -- python3 REPO/bench.py --steps 1 --warmup 0 --layers 8 --no-cpu-baseline --copy-calibration-mib 256 ; (the same with --pmc WRITE_SIZE -d OUT/prof_write) ; python3 REPO/bench.py --summarize OUT/prof_trace OUT/prof_fetch OUT/prof_write')
+PROFILE_COMMAND = ('cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o bench -- python3 REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline ; rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/prof_fetch -o bench -- python3 REPO/bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration-mib 256 ; (the same with --pmc WRITE_SIZE -d OUT/prof_write) ; python3 REPO/bench.py --summarize OUT/prof_trace OUT/prof_fetch OUT/prof_write')
 
 
 def kernel_source_hash() -> str:
@@ -95,7 +95,8 @@ def summarize(args):
     trace_dir, fetch_dir, write_dir = args.summarize
     stats = list(csv.DictReader(open(find(trace_dir, "kernel_stats.csv"))))
     os.makedirs(PROFILES, exist_ok=True)
-    lines = ["# rocprofv3 kernel statistics: one QSPEC round, Llama-3-8B-shaped projections (32 layers, B=16, gamma=4)",
+    lines = ["# rocprofv3 kernel statistics: one QSPEC round, Llama-3-8B-shaped projections (32 layers) and "
+             "vocabulary head, B=16, gamma=4",
              "", "Command (run from /tmp with TMPDIR=/tmp):", "", "```", args.summary_command or "(not recorded)", "```",
              "", "| kernel | calls | avg us | total % |", "|---|---:|---:|---:|"]
     for r in stats[:16]:
@@ -126,7 +127,7 @@ def summarize(args):
         if "w8a8" in r["Name"] or "fp8" in r["Name"]:
             lines.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    open(os.path.join(PROFILES, "kernel_trace_llama3_8b_round_B16_g4.md"), "w").write("\n".join(lines) + "\n")
+    open(os.path.join(PROFILES, "kernel_trace_llama3_8b_round_with_head_B16_g4.md"), "w").write("\n".join(lines) + "\n")
 
     def per_dispatch(d):
         rows = list(csv.DictReader(open(find(d, "counter_collection.csv"))))
@@ -165,7 +166,7 @@ def summarize(args):
         ent["dispatches"] += len(v)
     for k, e in out["kernels"].items():
         e["bytes_per_dispatch"] = (e["fetch_bytes"] + e["write_bytes"]) / e["dispatches"]
-    open(os.path.join(PROFILES, "pmc_traffic_llama3_8b_round.md"), "w").write("\n".join(md) + "\n")
+    open(os.path.join(PROFILES, "pmc_traffic_llama3_8b_round_with_head.md"), "w").write("\n".join(md) + "\n")
     json.dump(out, open(TRAFFIC_JSON, "w"), indent=1)
     print(f"wrote profiles/ (src_hash {out['src_hash']})")
 
@@ -205,6 +206,9 @@ def parse():
                     help="run one GEMM shape (LAYER w4a4 or w4a16) --probe-reps times on fresh weight copies "
                          "and exit: a short program for rocprofv3 counter passes")
     ap.add_argument("--probe-reps", type=int, default=4)
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
+                    help="OUT_MD LABEL=DIR [LABEL=DIR ...]: summarize rocprofv3 --pmc runs of --probe (one "
+                         "directory per probe and counter pass) into a markdown table and exit")
     ap.add_argument("--summary-command", default=PROFILE_COMMAND,
                     help="the command that produced the profiles (recorded in the summaries)")
     return ap.parse_args()
@@ -236,6 +240,7 @@ class Round:
         self.y_draft = [torch.empty((B, N), dtype=torch.bfloat16, device=dev) for _, (K, N) in self.projs]
         self.y_verify = [torch.empty((B * (g + 1), N), dtype=torch.bfloat16, device=dev) for _, (K, N) in self.projs]
         self.ws_verify = [q.gemm_w4a16_workspace(B * (g + 1), K, N, dev) for _, (K, N) in self.projs]
+        self.ws_plain = [q.gemm_w4a16_workspace(B, K, N, dev) for _, (K, N) in self.projs]
         # the vocabulary projection, shared by the draft (W4A4, fp32 logits per step) and the
         # verifier (W4A16, fp32 logits of the gamma + 1 positions).  Draft step j reads hidden rows
         # h_j [B][H]; the verifier reads the same rows at positions j < gamma (row b (gamma + 1) + j)
@@ -253,6 +258,7 @@ class Round:
         self.draft_logits = torch.empty((B, g, V), dtype=torch.float32, device=dev)
         self.target_logits = torch.empty((B, g + 1, V), dtype=torch.float32, device=dev)
         self.ws_head_verify = q.gemm_w4a16_workspace(B * (g + 1), Kh, V, dev)
+        self.ws_head_plain = q.gemm_w4a16_workspace(B, Kh, V, dev)
         self.draft_tokens = torch.zeros((B, g), dtype=torch.int32, device=dev)
         self.head_u = si.uniforms_device((g, B), seed=200, device=dev)               # draft-side draws
         self.u_accept = si.uniforms_device((B, g), seed=201, device=dev)
@@ -300,8 +306,8 @@ class Round:
         for l in range(self.L):
             for i in range(len(self.projs)):
                 wc, wm = self.weights[l][i]
-                self.q.qspec_gemm_w4a16(self.x_draft[i], wc, wm, self.y_draft[i])
-        self.q.qspec_gemm_w4a16(self.x_head_draft[0], *self.w_head, self.q_step)
+                self.q.qspec_gemm_w4a16(self.x_draft[i], wc, wm, self.y_draft[i], self.ws_plain[i])
+        self.q.qspec_gemm_w4a16(self.x_head_draft[0], *self.w_head, self.q_step, self.ws_head_plain)
 
     def accept_phase(self):
         self.q.qspec_verify_accept(self.q.QSPEC_SAMPLE, self.target_logits, self.draft_logits, self.draft_tokens,
@@ -879,6 +885,87 @@ def shape_table(args):
     print("wrote", args.shape_table)
 
 
+PMC_COMMAND = ("cd /tmp && export TMPDIR=/tmp && for each probe P in the table and each pass C: "
+               "timeout -s KILL 120 rocprofv3 --pmc C --output-format csv -d OUT/P_pass -o probe -- "
+               "python3 REPO/bench.py --probe P --probe-reps 4 ; then python3 REPO/bench.py --summarize-pmc "
+               "OUT.md LABEL=OUT/P_pass ...")
+PMC_PASSES = {
+    "pass1": "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_MFMA "
+             "SQ_BUSY_CYCLES SQ_WAVES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE",
+    "pass2": "SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_INSTS_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT "
+             "SQ_ACTIVE_INST_VMEM SQ_INST_CYCLES_VMEM_RD SQ_CYCLES GRBM_GUI_ACTIVE",
+}
+
+
+def summarize_pmc(args):
+    """Per-dispatch averages of the counters of --probe runs (the qspec kernels only; the passes of
+    one probe merged), with the derived ratios named in the table."""
+    import collections
+    import csv
+    import glob
+
+    out_md, specs = args.summarize_pmc[0], args.summarize_pmc[1:]
+    per = collections.OrderedDict()      # probe -> kernel -> counter -> [values]
+    dur = collections.defaultdict(list)  # (probe, kernel) -> dispatch durations (ns)
+    for spec in specs:
+        label, d = spec.split("=", 1)
+        probe_name = label.rsplit("_pass", 1)[0]
+        hits = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not hits:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        seen = set()
+        for r in csv.DictReader(open(hits[0])):
+            k = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            if "qspec::" not in k:
+                continue
+            per.setdefault(probe_name, collections.OrderedDict()).setdefault(k, collections.defaultdict(list))[
+                r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if (k, r["Dispatch_Id"]) not in seen:
+                seen.add((k, r["Dispatch_Id"]))
+                dur[(probe_name, k)].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    lines = ["# rocprofv3 counters of single GEMM launches (--probe), per dispatch", "",
+             "Command:", "", "```", PMC_COMMAND, "```", "",
+             "Passes (one rocprofv3 run each; a probe's passes are merged per kernel): "
+             + "; ".join(f"{k}: {v}" for k, v in PMC_PASSES.items()), "",
+             "Calibration: SQ_VALU_MFMA_BUSY_CYCLES equals 16 x SQ_INSTS_MFMA for the bf16 16x16x32 MFMA kernels "
+             "(16 cycles of a SIMD's matrix core per instruction); SQ_BUSY_CYCLES sums the 32 shader engines "
+             "(8 XCDs x 4), so C = SQ_BUSY_CYCLES / 32 is the dispatch's cycle count (C / duration gives the "
+             "clock; GRBM_GUI_ACTIVE / 8 agrees on long dispatches but also counts the profiler's window around "
+             "short ones); SQ_WAVE_CYCLES and SQ_WAIT_* count in units of 4 cycles.  "
+             "Derived over 1024 SIMDs: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 C); VALU busy = "
+             "4 (SQ_INSTS_VALU - SQ_INSTS_MFMA) / (1024 C) (SQ_INSTS_VALU counts MFMA instructions too; a wave64 "
+             "VALU instruction occupies a 16-lane SIMD for 4 cycles); co-execution = SQ_VALU_MFMA_COEXEC_CYCLES / "
+             "SQ_VALU_MFMA_BUSY_CYCLES; wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; LDS wait share = "
+             "SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES.", ""]
+    lines += ["| probe | kernel | us | clock GHz | MFMA busy | VALU busy | co-exec | wait share | LDS wait share | "
+              "VALU per MFMA | waves |", "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    raw = ["", "Raw counters per dispatch:", "", "| probe | kernel | counter | per dispatch |", "|---|---|---|---:|"]
+    for probe_name, kernels in per.items():
+        for k, cs in kernels.items():
+            avg = {c: sum(v) / len(v) for c, v in cs.items()}
+            for c in sorted(avg):
+                raw.append(f"| {probe_name} | `{k[:60]}` | {c} | {avg[c]:.4g} |")
+            ds = dur[(probe_name, k)]
+            us = sum(ds) / len(ds) / 1e3 if ds else float("nan")
+            C = avg.get("SQ_BUSY_CYCLES", 0) / 32
+            f = lambda v: f"{v:.3f}" if v == v else "-"
+            nan = float("nan")
+            mb = avg.get("SQ_VALU_MFMA_BUSY_CYCLES", nan) / (1024 * C) if C else nan
+            vb = 4 * (avg.get("SQ_INSTS_VALU", nan) - avg.get("SQ_INSTS_MFMA", nan)) / (1024 * C) if C else nan
+            co = (avg.get("SQ_VALU_MFMA_COEXEC_CYCLES", nan) / avg["SQ_VALU_MFMA_BUSY_CYCLES"]
+                  if avg.get("SQ_VALU_MFMA_BUSY_CYCLES") else nan)
+            wc = avg.get("SQ_WAVE_CYCLES")
+            ws = avg.get("SQ_WAIT_INST_ANY", nan) / wc if wc else nan
+            wl = avg.get("SQ_WAIT_INST_LDS", nan) / wc if wc else nan
+            vpm = ((avg.get("SQ_INSTS_VALU", nan) - avg["SQ_INSTS_MFMA"]) / avg["SQ_INSTS_MFMA"]
+                   if avg.get("SQ_INSTS_MFMA") else nan)
+            clock = C / (us * 1e3) if us == us and us > 0 else nan
+            lines.append(f"| {probe_name} | `{k[:60]}` | {us:.1f} | {f(clock)} | {f(mb)} | {f(vb)} | {f(co)} | {f(ws)} | "
+                         f"{f(wl)} | {f(vpm)} | {avg.get('SQ_WAVES', 0):.0f} |")
+    open(out_md, "w").write("\n".join(lines + raw) + "\n")
+    print("wrote", out_md)
+
+
 def probe(args):
     """One GEMM shape, launched eagerly --probe-reps times over distinct weight copies (each read
     from HBM), for counter collection; prints the shape and exits."""
@@ -911,6 +998,9 @@ def probe(args):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     if args.probe:
         probe(args)
         return

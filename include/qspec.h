@@ -150,8 +150,9 @@ int qspec_gemm_w4a4_tier(int32_t M, int32_t K, int32_t N, int32_t *m_first, int3
  *   2: [81, INT32_MAX] the shared-activation kernel over 128-row blocks;
  * with D = 24 when N >= 65536 (vocabulary-sized heads: four column tiles per workgroup),
  * D = 32 when the decode grid has at most 256 workgroups and K * N <= 4096 * 6144 (small
- * projections), and D = 16 otherwise.  The decode grid has N / 16 workgroups for N < 6144,
- * ceil(N / 32) for 6144 <= N < 65536.  Host-only: launches nothing.
+ * projections), D = 8 when N < 6144 and K >= 12288 (long K over one-tile workgroups), and
+ * D = 16 otherwise.  The decode grid has N / 16 workgroups for N < 6144, ceil(N / 32) for
+ * 6144 <= N < 65536.  Host-only: launches nothing.
  * Errors (negative status): NULL pointer; the size errors of qspec_gemm_w4a16.
  */
 int qspec_gemm_w4a16_tier(int32_t M, int32_t K, int32_t N, int32_t *m_first, int32_t *m_last);

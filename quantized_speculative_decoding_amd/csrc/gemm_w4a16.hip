@@ -640,6 +640,10 @@ static int decode_max_m(int K, int N) {
     const int wgs = (N / 16 + d.nt - 1) / d.nt;
     if (d.nt == 4) return 24;
     if (wgs <= 256 && (long long)K * N <= 4096LL * 6144) return 32;
+    // long K over one-tile workgroups (Llama-3-8B and Qwen2.5-7B down): every decode wave re-reads
+    // all M activation rows of its 28 - 37 groups, and above 8 rows the shared-activation kernel
+    // is faster
+    if (d.nt == 1 && K / kGroup >= 96) return 8;
     return 16;
 }
 
@@ -722,18 +726,20 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, con
     // Batch tiers, each with one reduction order for all its M: M <= decode_max_m(K, N) (decode,
     // one or two row tiles), up to M = 80 (shared activations, K parts, optional split-K), M > 80
     // (shared activations, row blocks).
-    if (M <= 16) {
+    const int dm = decode_max_m(K, N);
+    if (M <= 16 && M <= dm) {
         const int nt = decode_shape(K, N).nt;
         if (nt == 4) return launch_decode<4, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
         if (nt == 2) return launch_decode<2, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
         return launch_decode<1, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
     }
-    if (M <= decode_max_m(K, N)) {
+    if (M <= dm) {
         const int nt = decode_shape(K, N).nt;
         if (nt == 4) return launch_decode<4, 3, 2>(x, M, codes, meta, K, N, y, y_f32, st);
         if (nt == 2) return launch_decode<2, 4, 2>(x, M, codes, meta, K, N, y, y_f32, st);
         return launch_decode<1, 3, 2>(x, M, codes, meta, K, N, y, y_f32, st);
     }
+    if (M <= 16) return launch_mid<1, 6>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     if (M <= 32) return launch_mid<2, 6>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     if (M <= 48) return launch_mid<3, 5>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     if (M <= 64) return launch_mid<4, 4>(x, M, codes, meta, K, N, y, y_f32, ws, st);

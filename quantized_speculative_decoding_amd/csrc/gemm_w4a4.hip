@@ -145,7 +145,7 @@ k_w4a4_skinny(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
                 ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1[mt], B1, ia, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int Dv = ia[r] - zw * sa[mt][r];
+                    const int Dv = ia[r] - __mul24(zw, sa[mt][r]);   // |z sa| <= 15 * 896: 24-bit product
                     acc[mt][nt][r] = __builtin_fmaf(cur.as[mt][r] * sw, (float)Dv, acc[mt][nt][r]);
                     if (DOTS) {
                         const int mo = 16 * mt + 4 * kq + r;
@@ -305,7 +305,7 @@ k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
                 ia = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, ia, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int Dv = ia[r] - zw * sa[r];
+                    const int Dv = ia[r] - __mul24(zw, sa[r]);   // |z sa| <= 15 * 896: 24-bit product
                     acc[nt][r] = __builtin_fmaf(as[r] * sw, (float)Dv, acc[nt][r]);
                     if (DOTS) {
                         const int mo = 4 * kq + r;
@@ -317,25 +317,35 @@ k_w4a4_decode(const uint8_t *__restrict__ a_codes, const float *__restrict__ a_s
         };
 
         W4DStage<NT> st[U];
-        // The chunk's scales first (they come from L2; the ring's first group waits on HBM): lane
-        // l reads row l % 16, groups c0 + c + 4 (l / 16) .. + 3, and parks those inside the chunk
-        // at [group][row].  Reads past the array return 0.
+        // The chunk's scales (from L2) are loaded first, the ring's first U groups (from HBM) right
+        // behind them, and only then are the scales parked in LDS, so the two latencies overlap
+        // (the in-order vmcnt wait for the scales leaves the ring's loads in flight).  Lane l reads
+        // row l % 16, groups c0 + c + 4 (l / 16) .. + 3 for c = 0, 16, 32, 48, and parks those
+        // inside the chunk at [group][row].  Reads past the array return 0.
+        static_assert(kScaleChunk == 64, "four 16-group scale loads per chunk");
+        uint4 sv[4];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // previous chunk's reads first
-        for (int c = 0; c < cn; c += 16) {
-            const int gl = c + 4 * kq;
-            const uint4 v = buf_load16(sr, (srow + (uint32_t)(c0 + gl)) * 4, 0);
-            const float vv[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                                 __uint_as_float(v.w)};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (gl + e < cn) sl[(gl + e) * 16 + col] = vv[e];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int q4 = 0; q4 < 4; ++q4)
+            if (16 * q4 < cn) sv[q4] = buf_load16(sr, (srow + (uint32_t)(c0 + 16 * q4 + 4 * kq)) * 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             load(st[u], u);
             __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            if (16 * q4 < cn) {
+                const int gl = 16 * q4 + 4 * kq;
+                const float vv[4] = {__uint_as_float(sv[q4].x), __uint_as_float(sv[q4].y),
+                                     __uint_as_float(sv[q4].z), __uint_as_float(sv[q4].w)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (gl + e < cn) sl[(gl + e) * 16 + col] = vv[e];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // Steady passes refill every slot with a group of the chunk (no branch around a load); the
         // last pass refills only the slots whose group exists, and the drain consumes them, so no
         // wave waits at its end on loads of groups it never uses.

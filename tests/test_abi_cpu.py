@@ -243,7 +243,10 @@ W4A16_DECODE_LAST = [
     (4096, 4096, 32),      # 256 workgroups, K * N = 4096 * 4096: small projection
     (4096, 6144, 32),      # 192 workgroups (two tiles each), K * N = 4096 * 6144
     (3584, 4608, 16),      # Qwen qkv: 288 one-tile workgroups, more than 256
-    (14336, 4096, 16),     # K * N above 4096 * 6144
+    (14336, 4096, 8),      # Llama down: long K over one-tile workgroups
+    (18944, 3584, 8),      # Qwen down
+    (12160, 4096, 16),     # K just below 12288
+    (28672, 8192, 16),     # 70B down: two-tile workgroups
     (4096, 28672, 16),     # 896 workgroups
     (3584, 152064, 24),    # vocabulary head: four tiles per workgroup
     (4096, 128256, 24),
@@ -257,7 +260,9 @@ def _decode_last(K, N):
     wgs = -(-T // nt)
     if nt == 4:
         return 24
-    return 32 if wgs <= 256 and K * N <= 4096 * 6144 else 16
+    if wgs <= 256 and K * N <= 4096 * 6144:
+        return 32
+    return 8 if nt == 1 and K // 128 >= 96 else 16
 
 
 @pytest.mark.parametrize("K,N,last", W4A16_DECODE_LAST)
@@ -275,7 +280,7 @@ def test_w4a16_tier_rule_on_the_workload_shapes():
     """The header's rule, on the Llama-3-8B and Qwen2.5-7B projections and heads."""
     assert _decode_last(4096, 4096) == 32 and _decode_last(4096, 6144) == 32
     assert _decode_last(3584, 4608) == 16 and _decode_last(3584, 3584) == 32
-    assert _decode_last(14336, 4096) == 16 and _decode_last(18944, 3584) == 16
+    assert _decode_last(14336, 4096) == 8 and _decode_last(18944, 3584) == 8
     assert _decode_last(4096, 28672) == 16 and _decode_last(3584, 37888) == 16
     assert _decode_last(3584, 152064) == 24
 

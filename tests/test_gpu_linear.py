@@ -143,16 +143,16 @@ def test_w4a16_one_hot_rows_reproduce_dequantized_weights_exactly(M):
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("K,N", [(1024, 208), (1024, 16 * 300), (256, 16 * 4100)])
+@pytest.mark.parametrize("K,N", [(1024, 208), (1024, 16 * 300), (256, 16 * 4100), (12288, 256)])
 def test_w4a16_rows_do_not_depend_on_batch(K, N):
-    """Every M in one batch tier (as qspec_gemm_w4a16_tier reports it: decode up to 32, 16 or 24
-    rows for these three shapes) reduces a row in the same order: bitwise-equal rows.  Across
+    """Every M in one batch tier (as qspec_gemm_w4a16_tier reports it: decode up to 32, 16, 24 or 8
+    rows for these four shapes) reduces a row in the same order: bitwise-equal rows.  Across
     tiers the rows agree to fp32 rounding."""
     note(f"gemm_w4a16 batch invariance K={K} N={N}")
     w = si.weights(K, N, seed=4)
     wdev = weights_dev(w)
     x = si.activations(96, K, seed=4)
-    Ms = (1, 5, 16, 17, 20, 24, 25, 32, 33, 48, 80, 81, 96)
+    Ms = (1, 5, 8, 9, 12, 16, 17, 20, 24, 25, 32, 33, 48, 80, 81, 96)
     full = {M: run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy() for M in Ms}
     tiers = {}
     for M in Ms:
@@ -166,7 +166,7 @@ def test_w4a16_rows_do_not_depend_on_batch(K, N):
     assert_close(full[16].astype(np.float64), full[96][:16].astype(np.float64), False, "across tiers")
 
 
-@pytest.mark.parametrize("M,K,N", [(80, 4096, 4096), (40, 14336, 512), (33, 2048, 784)])
+@pytest.mark.parametrize("M,K,N", [(80, 4096, 4096), (40, 14336, 512), (33, 2048, 784), (12, 14336, 2048)])
 def test_w4a16_split_k_workspace_reuse(M, K, N):
     """Split-K verify shapes: the workspace needs no initialization (it starts as NaN bytes here)
     and repeated calls on it give identical results."""
@@ -217,7 +217,7 @@ FULL_W4A16 = [
     ("llama8b.down", 14336, 4096, 80), ("llama8b.gate_up", 4096, 28672, 80), ("llama8b.down", 14336, 4096, 16),
     # Qwen2.5-7B-shaped layer at gamma + 1 in 3, 5, 9, 17; fp32 logits for the head
     ("qwen7b.qkv", 3584, 4608, 3), ("qwen7b.o", 3584, 3584, 5), ("qwen7b.gate_up", 3584, 37888, 9),
-    ("qwen7b.down", 18944, 3584, 17), ("qwen7b.lm_head", 3584, 152064, 5),
+    ("qwen7b.down", 18944, 3584, 17), ("qwen7b.down", 18944, 3584, 12), ("qwen7b.lm_head", 3584, 152064, 5),
     # decode kernel with two row tiles: the head at gamma + 1 = 17, Llama qkv at B = 4
     ("qwen7b.lm_head", 3584, 152064, 17), ("llama8b.qkv", 4096, 6144, 20),
     # 70B-shaped FFN, compute-bound verify at 256 x 5 tokens
