@@ -525,25 +525,42 @@ def speckv_controller_us(R, torch):
     """Outside the timed round: the adaptive-gamma controller (draft confidence and entropy over
     one draft row per sequence, then its MLP) on the round's draft logits (the W4A4 head's rows of
     each draft step), graph-replayed; random controller weights (the trained ones are not
-    published)."""
+    published).  Returns microseconds per draft step for: the controller alone
+    (qspec_speckv_gamma), the draft-side sampling head alone (qspec_draft_sample), and both on
+    the same rows with the head's softmax statistics shared (qspec_draft_sample_speckv)."""
     q, B, V = R.q, R.B, R.V
     dev = R.accept.device
-    rows = [R.draft_logits[:, j, :].contiguous() for j in range(R.gamma)]   # one row set per draft step
+    rows = [R.draft_logits[:, j, :] for j in range(R.gamma)]            # one row set per draft step
+    crows = [r.contiguous() for r in rows]
     gen = torch.Generator(device=dev).manual_seed(900)
     w1, b1 = torch.randn((64, 3), device=dev, generator=gen), torch.randn((64,), device=dev, generator=gen)
     w2, b2 = torch.randn((9, 64), device=dev, generator=gen), torch.randn((9,), device=dev, generator=gen)
     g = torch.empty((B,), dtype=torch.int32, device=dev)
+    toks = torch.empty((B, R.gamma), dtype=torch.int32, device=dev)
     ws = torch.empty((q.qspec_speckv_workspace_bytes(B, V),), dtype=torch.uint8, device=dev)
-    graph = capture(lambda: [q.qspec_speckv_gamma(r, 0.0, w1, b1, w2, b2, g, None, ws) for r in rows], torch)
-    graph.replay()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(5):
+    ws_h = torch.empty((q.qspec_draft_sample_workspace_bytes(q.QSPEC_SAMPLE, B, V),), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty((q.qspec_draft_sample_speckv_workspace_bytes(q.QSPEC_SAMPLE, B, V),), dtype=torch.uint8,
+                       device=dev)
+
+    def per_step(fn):
+        graph = capture(fn, torch)
         graph.replay()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / (5 * len(rows))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(5):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (5 * len(rows))
+
+    ctrl = per_step(lambda: [q.qspec_speckv_gamma(r, 0.0, w1, b1, w2, b2, g, None, ws) for r in crows])
+    head = per_step(lambda: [q.qspec_draft_sample(q.QSPEC_SAMPLE, r, toks[:, j], R.head_u[j], ws_h)
+                             for j, r in enumerate(rows)])
+    both = per_step(lambda: [q.qspec_draft_sample_speckv(q.QSPEC_SAMPLE, r, toks[:, j], R.head_u[j], 0.0, w1, b1, w2,
+                                                         b2, g, None, ws_b) for j, r in enumerate(rows)])
+    return {"controller_alone": round(ctrl, 1), "draft_head_alone": round(head, 1),
+            "draft_head_and_controller_shared_stats": round(both, 1)}
 
 
 def attention_us(R, torch):
@@ -1071,7 +1088,7 @@ def main():
         # (projections and head only: attention and norms are not in T_target)
         "round_model": R.model,
         # outside the timed round: the adaptive-gamma controller on one draft row per sequence
-        "speckv_controller_us": round(R.speckv_us, 1),
+        "speckv_us_per_draft_step": R.speckv_us,
         # outside the timed round: one layer's attention over the full cache; every key and value
         # (B x 8 heads x 4096 positions x 2 x 256 bytes) is read once per call
         "attention": {"workload": f"B{B}-Hq32-Hkv{KV_HEADS}-d{HEAD_DIM}-T{CONTEXT}-one-layer",

@@ -343,6 +343,33 @@ int qspec_speckv_gamma(const float *draft_logits, int32_t R, int32_t V, float qu
                        size_t workspace_bytes, qspec_stream_t stream);
 
 /*
+ * qspec_draft_sample_speckv_workspace_bytes -- device workspace qspec_draft_sample_speckv needs;
+ * 0 on invalid arguments.
+ */
+size_t qspec_draft_sample_speckv_workspace_bytes(int32_t mode, int32_t B, int32_t V);
+
+/*
+ * qspec_draft_sample_speckv -- the draft-side head and the adaptive-gamma controller of one draft
+ * step, on the same draft rows.
+ * [QSPEC notes, QSPEC structure: the draft proposes one token per step from its distribution;
+ * SpecKV notes, architecture and mechanism: the draft's statistics at that step (its largest
+ * probability and its entropy) pick gamma.]  tokens are exactly qspec_draft_sample's, and
+ * gamma_out / features exactly qspec_speckv_gamma's on the rows (R = B): the same kernels.  With
+ * SAMPLE the head's softmax statistics (per-chunk max and sum of exponentials) are the
+ * controller's too, so one statistics pass over the rows serves both; GREEDY takes argmaxes and
+ * runs the controller's statistics pass after them.
+ * Arguments as qspec_draft_sample (mode, logits, B, V, row_stride, u, tokens, token_stride) and
+ * qspec_speckv_gamma (quant_feature, w1, b1, w2, b2, max_gamma, features, gamma_out).
+ * workspace  [in/out] at least qspec_draft_sample_speckv_workspace_bytes(mode, B, V) bytes
+ * Errors: those of both calls.
+ */
+int qspec_draft_sample_speckv(int32_t mode, const float *logits, int32_t B, int32_t V, int64_t row_stride,
+                              const float *u, int32_t *tokens, int32_t token_stride, float quant_feature,
+                              const float *w1, const float *b1, const float *w2, const float *b2,
+                              int32_t max_gamma, double *features, int32_t *gamma_out, void *workspace,
+                              size_t workspace_bytes, qspec_stream_t stream);
+
+/*
  * qspec_attention_workspace_bytes -- device workspace qspec_attention needs; 0 on invalid sizes
  * (the head dimension is QSPEC_ATTN_HEAD_DIM).
  */

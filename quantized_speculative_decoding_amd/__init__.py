@@ -77,9 +77,14 @@ def lib() -> ctypes.CDLL:
         L.qspec_draft_sample_workspace_bytes.argtypes = [I, I, I]
         L.qspec_draft_sample_workspace_bytes.restype = S
         L.qspec_draft_sample.argtypes = [I, P, I, I, ctypes.c_int64, P, P, I, P, S, P]
+        L.qspec_draft_sample_speckv_workspace_bytes.argtypes = [I, I, I]
+        L.qspec_draft_sample_speckv_workspace_bytes.restype = S
+        L.qspec_draft_sample_speckv.argtypes = [I, P, I, I, ctypes.c_int64, P, P, I, ctypes.c_float, P, P, P, P, I, P,
+                                                P, P, S, P]
         for fn in ("qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_verify_accept",
                    "qspec_kv_overwrite", "qspec_speckv_gamma", "qspec_attention", "qspec_quantize_act_fp8",
-                   "qspec_gemm_w8a8", "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier", "qspec_verify_accept_noalloc"):
+                   "qspec_gemm_w8a8", "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier", "qspec_verify_accept_noalloc",
+                   "qspec_draft_sample_speckv"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -281,6 +286,44 @@ def qspec_draft_sample(mode, logits, tokens, u, workspace, stream=None) -> None:
     _check("qspec_draft_sample",
            lib().qspec_draft_sample(mode, _ptr(logits), B, V, logits.stride(0), _ptr(u), _ptr(tokens),
                                     tokens.stride(0), _ptr(workspace), workspace.numel(), _stream(stream, logits)))
+
+
+def qspec_draft_sample_speckv_workspace_bytes(mode: int, B: int, V: int) -> int:
+    return int(lib().qspec_draft_sample_speckv_workspace_bytes(mode, B, V))
+
+
+def qspec_draft_sample_speckv(mode, logits, tokens, u, quant_feature, w1, b1, w2, b2, gamma_out, features,
+                              workspace, stream=None) -> None:
+    """The draft-side head and the adaptive-gamma controller of one step (see include/qspec.h):
+    logits / tokens / u as qspec_draft_sample; w1..b2, gamma_out i32 [B] and features f64 [B][2]
+    (or None) as qspec_speckv_gamma; workspace u8 (qspec_draft_sample_speckv_workspace_bytes)."""
+    for t, name, dt in ((logits, "logits", torch.float32), (tokens, "tokens", torch.int32)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA (HIP) device tensor")
+        if t.dtype != dt:
+            raise TypeError(f"{name} must have dtype {dt}")
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [B][V] with unit stride along V")
+    B, V = logits.shape
+    if tokens.dim() != 1 or tokens.shape[0] != B:
+        raise ValueError("tokens must be [B]")
+    if u is not None:
+        _req(u, "u", torch.float32, (B,))
+    _req(w1, "w1", torch.float32, (64, 3))
+    _req(b1, "b1", torch.float32, (64,))
+    _req(w2, "w2", torch.float32)
+    G1 = w2.shape[0]
+    _req(w2, "w2", torch.float32, (G1, 64))
+    _req(b2, "b2", torch.float32, (G1,))
+    _req(gamma_out, "gamma_out", torch.int32, (B,))
+    if features is not None:
+        _req(features, "features", torch.float64, (B, 2))
+    _req(workspace, "workspace", torch.uint8)
+    _check("qspec_draft_sample_speckv",
+           lib().qspec_draft_sample_speckv(mode, _ptr(logits), B, V, logits.stride(0), _ptr(u), _ptr(tokens),
+                                           tokens.stride(0), float(quant_feature), _ptr(w1), _ptr(b1), _ptr(w2),
+                                           _ptr(b2), G1 - 1, _ptr(features), _ptr(gamma_out), _ptr(workspace),
+                                           workspace.numel(), _stream(stream, logits)))
 
 
 def qspec_kv_overwrite(cache, verify_kv, start_pos, accept_count, stream=None) -> None:

@@ -44,6 +44,14 @@ hipError_t launch_draft_sample(int mode, const float *logits, size_t ldt, const 
 
 size_t speckv_workspace_bytes(int R, int V);
 
+// The draft-side head and the adaptive-gamma controller on one draft step's rows (SAMPLE shares
+// the softmax statistics pass between them).
+size_t draft_speckv_workspace_bytes(int mode, int B, int V);
+hipError_t launch_draft_speckv(int mode, const float *logits, size_t ldt, const float *u, int B, int V,
+                               int32_t *tokens, int ldo, float quant_feature, const float *w1, const float *b1,
+                               const float *w2, const float *b2, int max_gamma, double *features,
+                               int32_t *gamma_out, void *ws, hipStream_t st);
+
 hipError_t launch_speckv_gamma(const float *logits, int R, int V, float quant_feature, const float *w1,
                                const float *b1, const float *w2, const float *b2, int max_gamma,
                                double *features, int32_t *gamma_out, void *workspace, hipStream_t st);

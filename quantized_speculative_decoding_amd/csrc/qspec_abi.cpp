@@ -294,3 +294,30 @@ QSPEC_EXPORT int qspec_draft_sample(int32_t mode, const float *logits, int32_t B
     return status_of(qspec::launch_draft_sample(mode, logits, (size_t)row_stride, u, B, V, tokens, token_stride,
                                                 workspace, as_stream(stream)));
 }
+
+QSPEC_EXPORT size_t qspec_draft_sample_speckv_workspace_bytes(int32_t mode, int32_t B, int32_t V) {
+    if ((mode != QSPEC_GREEDY && mode != QSPEC_SAMPLE) || !verify_sizes_ok(B, 0, V) || !speckv_sizes_ok(B, V, 0))
+        return 0;
+    return qspec::draft_speckv_workspace_bytes(mode, B, V);
+}
+
+QSPEC_EXPORT int qspec_draft_sample_speckv(int32_t mode, const float *logits, int32_t B, int32_t V,
+                                           int64_t row_stride, const float *u, int32_t *tokens, int32_t token_stride,
+                                           float quant_feature, const float *w1, const float *b1, const float *w2,
+                                           const float *b2, int32_t max_gamma, double *features, int32_t *gamma_out,
+                                           void *workspace, size_t workspace_bytes, qspec_stream_t stream) {
+    if (mode != QSPEC_GREEDY && mode != QSPEC_SAMPLE) return QSPEC_ERR_UNSUPPORTED;
+    if (!logits || !tokens || (mode == QSPEC_SAMPLE && !u)) return QSPEC_ERR_NULL;
+    if (!w1 || !b1 || !w2 || !b2 || !gamma_out) return QSPEC_ERR_NULL;
+    if (!verify_sizes_ok(B, 0, V) || !speckv_sizes_ok(B, V, max_gamma) || row_stride < V || token_stride < 1)
+        return QSPEC_ERR_SHAPE;
+    if ((long long)(B - 1) * row_stride + V > kMaxElems) return QSPEC_ERR_SHAPE;
+    if (!workspace || workspace_bytes < qspec::draft_speckv_workspace_bytes(mode, B, V)) return QSPEC_ERR_WORKSPACE;
+    if (!aligned(logits, 4) || !aligned(u, 4) || !aligned(tokens, 4) || !aligned(w1, 4) || !aligned(b1, 4) ||
+        !aligned(w2, 4) || !aligned(b2, 4) || !aligned(features, 8) || !aligned(gamma_out, 4) ||
+        !aligned(workspace, 16))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_draft_speckv(mode, logits, (size_t)row_stride, u, B, V, tokens, token_stride,
+                                                quant_feature, w1, b1, w2, b2, max_gamma, features, gamma_out,
+                                                workspace, as_stream(stream)));
+}

@@ -563,19 +563,23 @@ k_residual_pick(const float *__restrict__ target, size_t ldt, const float *__res
 // sum of exp), k_entropy_partial (per chunk: sum of p log(p + 1e-9) with the row's max and
 // normalizer), k_speckv_head (one wave per row: combine in chunk order, run the MLP).
 constexpr int kSpeckvHidden = 64;
+// The entropy pass spends two fp64 transcendentals per logit; its chunks are a quarter of the
+// statistics chunks, so a few draft rows still give about four workgroups per CU.
+constexpr int ECHUNK = VCHUNK / 4;
 
 struct SpeckvLayout {
-    int C;
+    int C, CE;   // statistics chunks and entropy chunks per row
     size_t pmax, psum, pent, total;
 };
 
 static SpeckvLayout speckv_layout(int R, int V) {
     SpeckvLayout L = {};
     L.C = (V + VCHUNK - 1) / VCHUNK;
+    L.CE = (V + ECHUNK - 1) / ECHUNK;
     size_t off = 0;
     L.pmax = off; off = align256(off + (size_t)R * L.C * sizeof(float));
     L.psum = off; off = align256(off + (size_t)R * L.C * sizeof(double));
-    L.pent = off; off = align256(off + (size_t)R * L.C * sizeof(double));
+    L.pent = off; off = align256(off + (size_t)R * L.CE * sizeof(double));
     L.total = off;
     return L;
 }
@@ -591,11 +595,11 @@ __device__ __forceinline__ void row_stats(const float *pmax, const double *psum,
 }
 
 __global__ void __launch_bounds__(VT)
-k_entropy_partial(const float *__restrict__ logits, int V, int C, const float *__restrict__ pmax,
+k_entropy_partial(const float *__restrict__ logits, size_t ldt, int V, int C, int CE, const float *__restrict__ pmax,
                   const double *__restrict__ psum, double *__restrict__ pent) {
     __shared__ float sM;
     __shared__ double sS;
-    const int row = blockIdx.x / C, c = blockIdx.x % C;
+    const int row = blockIdx.x / CE, c = blockIdx.x % CE;
     if (threadIdx.x == 0) {
         float M;
         double S;
@@ -605,8 +609,8 @@ k_entropy_partial(const float *__restrict__ logits, int V, int C, const float *_
     }
     __syncthreads();
     const double M = (double)sM, S = sS;
-    const float *p = logits + (size_t)row * V;
-    const int lo = c * VCHUNK, hi = min(V, lo + VCHUNK);
+    const float *p = logits + (size_t)row * ldt;
+    const int lo = c * ECHUNK, hi = min(V, lo + ECHUNK);
     double t = 0.0;
     for (int x = lo + (int)threadIdx.x; x < hi; x += VT) {
         const double pv = exp((double)p[x] - M) / S;
@@ -617,7 +621,7 @@ k_entropy_partial(const float *__restrict__ logits, int V, int C, const float *_
 }
 
 __global__ void __launch_bounds__(kWave)
-k_speckv_head(int C, const float *__restrict__ pmax, const double *__restrict__ psum,
+k_speckv_head(int C, int CE, const float *__restrict__ pmax, const double *__restrict__ psum,
               const double *__restrict__ pent, float quant_feature, const float *__restrict__ w1,
               const float *__restrict__ b1, const float *__restrict__ w2, const float *__restrict__ b2, int G1,
               double *__restrict__ features, int32_t *__restrict__ gamma_out) {
@@ -629,7 +633,7 @@ k_speckv_head(int C, const float *__restrict__ pmax, const double *__restrict__ 
     double S;
     row_stats(pmax + (size_t)row * C, psum + (size_t)row * C, C, M, S);
     double ent = 0.0;
-    for (int c = 0; c < C; ++c) ent += pent[(size_t)row * C + c];
+    for (int c = 0; c < CE; ++c) ent += pent[(size_t)row * CE + c];
     ent = -ent;
     const double conf = 1.0 / S;       // the largest probability: exp(M - M) / S
     const double in[3] = {conf, ent, (double)quant_feature};
@@ -678,9 +682,9 @@ hipError_t launch_speckv_gamma(const float *logits, int R, int V, float quant_fe
     // R rows of "target" logits and no draft rows: the verification's chunk pass with gamma = 0
     hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)((long long)R * C)), dim3(VT), 0, st, logits, (size_t)V,
                        (const float *)nullptr, R, 0, V, C, vec, pmax, psum);
-    hipLaunchKernelGGL(k_entropy_partial, dim3((unsigned)((long long)R * C)), dim3(VT), 0, st, logits, V, C, pmax,
-                       psum, pent);
-    hipLaunchKernelGGL(k_speckv_head, dim3(R), dim3(kWave), 0, st, C, pmax, psum, pent, quant_feature, w1, b1, w2, b2,
+    hipLaunchKernelGGL(k_entropy_partial, dim3((unsigned)((long long)R * L.CE)), dim3(VT), 0, st, logits, (size_t)V, V,
+                       C, L.CE, pmax, psum, pent);
+    hipLaunchKernelGGL(k_speckv_head, dim3(R), dim3(kWave), 0, st, C, L.CE, pmax, psum, pent, quant_feature, w1, b1, w2, b2,
                        max_gamma + 1, features, gamma_out);
     return hipGetLastError();
 }
@@ -778,6 +782,55 @@ hipError_t launch_draft_sample(int mode, const float *logits, size_t ldt, const 
                                int32_t *tokens, int ldo, void *ws, hipStream_t st) {
     int32_t *acc = (int32_t *)((char *)ws + align256(verify_layout(mode, B, 0, V).total));
     return launch_verify(mode, logits, ldt, nullptr, nullptr, nullptr, u, B, 0, V, acc, tokens, ldo, ws, st);
+}
+
+// The draft-side head and the adaptive-gamma controller on the same draft rows.  SAMPLE: the
+// head's chunk statistics (max and sum of exp per chunk, k_softmax_partial) are the ones the
+// controller needs, so one statistics pass over the rows feeds both and the controller adds only
+// its entropy pass and its MLP.  GREEDY: the head takes argmaxes, so the controller's statistics
+// pass runs after it.  Workspace: the head's, then the controller's per-chunk entropies (SAMPLE)
+// or its whole layout (GREEDY).
+size_t draft_speckv_workspace_bytes(int mode, int B, int V) {
+    const size_t head = align256(draft_sample_workspace_bytes(mode, B, V));
+    if (mode == 0) return head + speckv_layout(B, V).total;
+    const int CE = (V + ECHUNK - 1) / ECHUNK;
+    return head + align256((size_t)B * CE * sizeof(double));
+}
+
+hipError_t launch_draft_speckv(int mode, const float *logits, size_t ldt, const float *u, int B, int V,
+                               int32_t *tokens, int ldo, float quant_feature, const float *w1, const float *b1,
+                               const float *w2, const float *b2, int max_gamma, double *features,
+                               int32_t *gamma_out, void *ws, hipStream_t st) {
+    hipError_t e = launch_draft_sample(mode, logits, ldt, u, B, V, tokens, ldo, ws, st);
+    if (e != hipSuccess) return e;
+    char *w = (char *)ws;
+    const size_t head = align256(draft_sample_workspace_bytes(mode, B, V));
+    const int C = (V + VCHUNK - 1) / VCHUNK;
+    const float *pmax;
+    const double *psum;
+    double *pent;
+    if (mode == 0) {
+        const SpeckvLayout S = speckv_layout(B, V);
+        float *m = (float *)(w + head + S.pmax);
+        double *sum = (double *)(w + head + S.psum);
+        pent = (double *)(w + head + S.pent);
+        const bool vec = (V % 4 == 0) && (ldt % 4 == 0) && ((uintptr_t)logits % 16 == 0);
+        hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)((long long)B * C)), dim3(VT), 0, st, logits, ldt,
+                           (const float *)nullptr, B, 0, V, C, vec, m, sum);
+        pmax = m;
+        psum = sum;
+    } else {
+        const VerifyLayout L = verify_layout(mode, B, 0, V);
+        pmax = (const float *)(w + L.pmax);
+        psum = (const double *)(w + L.psum);
+        pent = (double *)(w + head);
+    }
+    const int CE = (V + ECHUNK - 1) / ECHUNK;
+    hipLaunchKernelGGL(k_entropy_partial, dim3((unsigned)((long long)B * CE)), dim3(VT), 0, st, logits, ldt, V, C, CE,
+                       pmax, psum, pent);
+    hipLaunchKernelGGL(k_speckv_head, dim3(B), dim3(kWave), 0, st, C, CE, pmax, psum, pent, quant_feature, w1, b1, w2,
+                       b2, max_gamma + 1, features, gamma_out);
+    return hipGetLastError();
 }
 
 }  // namespace qspec

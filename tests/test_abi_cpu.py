@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
         "qspec_kv_overwrite", "qspec_speckv_workspace_bytes", "qspec_speckv_gamma",
         "qspec_attention_workspace_bytes", "qspec_attention", "qspec_quantize_act_fp8",
         "qspec_gemm_w8a8_workspace_bytes", "qspec_gemm_w8a8", "qspec_draft_sample_workspace_bytes",
-        "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier", "qspec_verify_accept_noalloc"])
+        "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier", "qspec_verify_accept_noalloc",
+        "qspec_draft_sample_speckv", "qspec_draft_sample_speckv_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol_and_nothing_else():
@@ -348,3 +349,33 @@ def test_verify_accept_noalloc_validation():
     odd = ctypes.c_void_p(0x1002)
     s = [1, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 4, 128256, odd, FAKE, None]
     assert L.qspec_verify_accept_noalloc(*s) == ERR_ALIGN
+
+
+def test_draft_sample_speckv_validation():
+    """The shared-statistics head + controller checks the arguments of both calls it combines and
+    needs the head's workspace plus the controller's entropies (sampling) or its whole layout."""
+    L = q.lib()
+    f = ctypes.c_float(0.0)
+    for mode in (0, 1):
+        ws = L.qspec_draft_sample_speckv_workspace_bytes(mode, 16, 128256)
+        assert ws >= L.qspec_draft_sample_workspace_bytes(mode, 16, 128256)
+    assert (L.qspec_draft_sample_speckv_workspace_bytes(0, 16, 128256) - L.qspec_draft_sample_workspace_bytes(0, 16, 128256)
+            >= L.qspec_speckv_workspace_bytes(16, 128256))
+    assert L.qspec_draft_sample_speckv_workspace_bytes(2, 16, 1000) == 0
+    assert L.qspec_draft_sample_speckv_workspace_bytes(1, 0, 1000) == 0
+    need = L.qspec_draft_sample_speckv_workspace_bytes(1, 4, 1000)
+    args = [1, FAKE, 4, 1000, 1000, FAKE, FAKE, 1, f, FAKE, FAKE, FAKE, FAKE, 4, None, FAKE, FAKE, need, None]
+    bad = list(args); bad[0] = 3
+    assert L.qspec_draft_sample_speckv(*bad) == ERR_UNSUPPORTED
+    for i in (1, 5, 6, 9, 10, 11, 12, 15):
+        bad = list(args); bad[i] = None
+        assert L.qspec_draft_sample_speckv(*bad) == ERR_NULL, i
+    g = list(args); g[0] = 0; g[5] = None; g[17] = L.qspec_draft_sample_speckv_workspace_bytes(0, 4, 1000) - 1
+    assert L.qspec_draft_sample_speckv(*g) == ERR_WS                  # greedy: u may be NULL
+    for i, v in ((2, 0), (3, 0), (4, 999), (7, 0), (13, -1), (13, 64)):
+        bad = list(args); bad[i] = v
+        assert L.qspec_draft_sample_speckv(*bad) == ERR_SHAPE, (i, v)
+    bad = list(args); bad[17] = need - 1
+    assert L.qspec_draft_sample_speckv(*bad) == ERR_WS
+    bad = list(args); bad[14] = ctypes.c_void_p(0x1004)              # features are f64
+    assert L.qspec_draft_sample_speckv(*bad) == ERR_ALIGN

@@ -78,3 +78,51 @@ def test_speckv_gamma_follows_the_controller_weights():
     logits[0, 5] = 40.0
     g, _ = run_speckv(logits, 0.0, w1, b1, w2, b2)
     assert g.tolist() == [0, G1 - 1]
+
+
+@pytest.mark.parametrize("mode", [q.QSPEC_GREEDY, q.QSPEC_SAMPLE], ids=["greedy", "sample"])
+@pytest.mark.parametrize("B,V,gamma_buf", [(16, 128256, 4), (3, 1000, 1), (5, 8193, 2)])
+def test_draft_sample_speckv_equals_the_two_calls(mode, B, V, gamma_buf):
+    """One draft step of a [B][gamma][V] draft-logit buffer read in place (strided rows) and its
+    tokens written into column j of the [B][gamma] token buffer: the shared-statistics call gives
+    exactly qspec_draft_sample's tokens and qspec_speckv_gamma's gamma and features, and those
+    match the oracle (tokens through the verification oracle with gamma = 0)."""
+    note(f"draft_sample_speckv mode={mode} B={B} V={V}")
+    t, _ = si.logits(B, gamma_buf - 1, V, seed=V + 7 * B)
+    buf = cu(np.ascontiguousarray(t))                     # [B][gamma_buf][V]
+    j = gamma_buf - 1
+    rows = buf[:, j, :]
+    u = cu(si.uniforms((B,), seed=B + 3))
+    w = _weights(V + 1, 9)
+    wd = [cu(a) for a in w]
+    tok_buf = torch.full((B, gamma_buf), -5, dtype=torch.int32, device=DEV)
+    gam = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    feats = torch.full((B, 2), np.nan, dtype=torch.float64, device=DEV)
+    ws = torch.full((q.qspec_draft_sample_speckv_workspace_bytes(mode, B, V),), 0xFF, dtype=torch.uint8, device=DEV)
+    uu = u if mode == q.QSPEC_SAMPLE else None
+    q.qspec_draft_sample_speckv(mode, rows, tok_buf[:, j], uu, 0.5, *wd, gam, feats, ws)
+    # the two separate calls
+    tok2 = torch.full((B, gamma_buf), -5, dtype=torch.int32, device=DEV)
+    ws1 = torch.empty((q.qspec_draft_sample_workspace_bytes(mode, B, V),), dtype=torch.uint8, device=DEV)
+    q.qspec_draft_sample(mode, rows, tok2[:, j], uu, ws1)
+    gam2 = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    feats2 = torch.full((B, 2), np.nan, dtype=torch.float64, device=DEV)
+    ws2 = torch.empty((q.qspec_speckv_workspace_bytes(B, V),), dtype=torch.uint8, device=DEV)
+    q.qspec_speckv_gamma(rows.contiguous(), 0.5, *wd, gam2, feats2, ws2)
+    assert torch.equal(tok_buf, tok2)
+    assert torch.equal(gam, gam2)
+    assert torch.equal(feats, feats2)
+    assert bool((tok_buf[:, :j] == -5).all())               # other columns untouched
+    # the oracle: the controller on the rows, the head as the verification with gamma = 0
+    logits = np.ascontiguousarray(t[:, j, :])
+    compare(logits, 0.5, w)
+    if mode == q.QSPEC_GREEDY:
+        ref = np.argmax(logits, axis=1)
+        assert np.array_equal(tok_buf[:, j].cpu().numpy(), ref)
+    else:
+        A, out, diag = oracle.verify_sample(logits.reshape(B, 1, V), np.zeros((B, 0, V), np.float32),
+                                            np.zeros((B, 0), np.int32), np.zeros((B, 0), np.float32),
+                                            si.uniforms((B,), seed=B + 3))
+        got = tok_buf[:, j].cpu().numpy()
+        for b in range(B):          # a draw may differ only where the oracle flags a CDF near tie
+            assert got[b] == out[b, 0] or diag[b, 0] < 1e-9, (b, got[b], out[b, 0], diag[b, 0])
