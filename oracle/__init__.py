@@ -70,6 +70,8 @@ def _lib():
         lib.orc_double_to_e4m3.argtypes = [ctypes.c_double]
         lib.orc_double_to_e4m3.restype = ctypes.c_uint8
         lib.orc_quantize_act_fp8.argtypes = [P, I, I, P, P]
+        lib.orc_kv_overwrite_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
+        lib.orc_attention_fp8.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, P]
         lib.orc_quantize_weights_fp8.argtypes = [P, I, I, P, P]
         lib.orc_gemm_w8a8.argtypes = [P, P, I, P, P, I, I, P]
         for name in ("orc_dequant", "orc_gemm_w4a16", "orc_quantize_act", "orc_gemm_w4a4",
@@ -281,3 +283,37 @@ def kv_overwrite(cache, verify_kv, start_pos, accept):
     _lib().orc_kv_overwrite(_p(cache), _p(verify_kv), _p(start_pos), _p(accept), L, B, H, T, D,
                             gamma)
     return cache
+
+
+def kv_overwrite_fp8(codes, scales, verify_kv, start_pos, accept):
+    """In place on the FP8 cache (codes u8 [L][B][2][H][T][D], scales f32 [L][B][2][H][T]): rows
+    0..A_b of verify_kv (u16 bf16 [L][B][2][H][g+1][D]) quantized per row at start_pos[b] + r."""
+    assert codes.dtype == np.uint8 and codes.flags["C_CONTIGUOUS"]
+    assert scales.dtype == np.float32 and scales.flags["C_CONTIGUOUS"]
+    L, B, two, H, T, D = codes.shape
+    assert two == 2 and scales.shape == (L, B, 2, H, T)
+    verify_kv = _c(verify_kv, np.uint16)
+    gamma = verify_kv.shape[4] - 1
+    assert verify_kv.shape == (L, B, 2, H, gamma + 1, D)
+    start_pos = _c(start_pos, np.int32).reshape(B)
+    accept = _c(accept, np.int32).reshape(B)
+    _lib().orc_kv_overwrite_fp8(_p(codes), _p(scales), _p(verify_kv), _p(start_pos), _p(accept), L, B, H, T, D,
+                                gamma)
+    return codes, scales
+
+
+def attention_fp8(q, codes, scales, pos, scale):
+    """Causal attention over one layer of the FP8 cache: q u16 [B][Q][Hq][D]; codes u8
+    [B][2][Hkv][T][D]; scales f32 [B][2][Hkv][T]; returns u16 bf16 [B][Q][Hq][D]."""
+    q = _c(q, np.uint16)
+    B, Q, Hq, D = q.shape
+    codes = _c(codes, np.uint8)
+    assert codes.shape[:2] == (B, 2) and codes.shape[4] == D
+    Hkv, T = codes.shape[2], codes.shape[3]
+    scales = _c(scales, np.float32)
+    assert scales.shape == (B, 2, Hkv, T) and Hq % Hkv == 0
+    pos = _c(pos, np.int32).reshape(B)
+    out = np.empty_like(q)
+    _lib().orc_attention_fp8(_p(q), _p(codes), _p(scales), _p(pos), B, Q, Hq, Hkv, T, D, float(scale), _p(out))
+    return out
+

@@ -530,6 +530,84 @@ void orc_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const int32_t 
         }
 }
 
+/* ---- O11: the quantized KV cache -------------------------------------------
+ * [QSPEC notes: the opening summary speaks of quantized KV; QSPEC structure: the
+ * draft's low-precision KV is replaced by the verifier's for accepted tokens.]
+ * Reading used here (the page fixes no format): the cache holds FP8 (OCP E4M3)
+ * codes with one binary32 scale per (position, KV head) row of D values, made by
+ * the per-row quantizer of the FP8 variant (O10): s = max |v| / 448, code =
+ * nearest E4M3 value to v / s (ties to even, binary32 quotient), 0 and s = 0 for an
+ * all-zero row; a value reads back as s * dec(code).
+ * Layout: codes u8 [L][B][2][H][T][D], scales f32 [L][B][2][H][T] (2 = key, value).
+ * orc_kv_overwrite_fp8 writes rows r = 0..A_b of the verifier's bfloat16 rows
+ * there, quantized, at positions start_pos[b] + r (as O7, positions outside [0, T)
+ * skipped, A clamped to [0, gamma]); orc_attention_fp8 is O9 (causal attention)
+ * with each key and value read back from the codes and scales. */
+void orc_quantize_act_fp8(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, float *scales);
+double orc_e4m3_to_double(uint8_t c);
+
+void orc_kv_overwrite_fp8(uint8_t *codes, float *scales, const uint16_t *verify_kv, const int32_t *start_pos,
+                          const int32_t *accept, int64_t L, int64_t B, int64_t H, int64_t T, int64_t D,
+                          int64_t gamma)
+{
+    for (int64_t l = 0; l < L; ++l)
+        for (int64_t b = 0; b < B; ++b) {
+            int64_t A = accept[b];
+            if (A < 0) A = 0;
+            if (A > gamma) A = gamma;
+            for (int64_t kv = 0; kv < 2; ++kv)
+                for (int64_t h = 0; h < H; ++h)
+                    for (int64_t r = 0; r <= A; ++r) {
+                        int64_t t = (int64_t)start_pos[b] + r;
+                        if (t < 0 || t >= T) continue;
+                        int64_t head = ((l * B + b) * 2 + kv) * H + h;
+                        const uint16_t *src = verify_kv + (head * (gamma + 1) + r) * D;
+                        orc_quantize_act_fp8(src, 1, D, codes + (head * T + t) * D, scales + head * T + t);
+                    }
+        }
+}
+
+void orc_attention_fp8(const uint16_t *q, const uint8_t *codes, const float *scales, const int32_t *pos, int64_t B,
+                       int64_t Q, int64_t Hq, int64_t Hkv, int64_t T, int64_t D, float scale, uint16_t *out)
+{
+    double *s = (double *)malloc(sizeof(double) * (size_t)T);
+    double *o = (double *)malloc(sizeof(double) * (size_t)D);
+    const int64_t G = Hq / Hkv;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < Q; ++j)
+            for (int64_t h = 0; h < Hq; ++h) {
+                const int64_t hk = h / G;
+                const uint16_t *qv = q + ((b * Q + j) * Hq + h) * D;
+                const int64_t kh = (b * 2 + 0) * Hkv + hk, vh = (b * 2 + 1) * Hkv + hk;
+                int64_t last = (int64_t)pos[b] + j;
+                if (last > T - 1) last = T - 1;
+                double mx = -INFINITY;
+                for (int64_t t = 0; t <= last; ++t) {
+                    const double sk = (double)scales[kh * T + t];
+                    double d = 0.0;
+                    for (int64_t e = 0; e < D; ++e)
+                        d += (double)bf16_to_float(qv[e]) * (sk * orc_e4m3_to_double(codes[(kh * T + t) * D + e]));
+                    s[t] = (double)scale * d;
+                    if (s[t] > mx) mx = s[t];
+                }
+                double sum = 0.0;
+                for (int64_t t = 0; t <= last; ++t) {
+                    s[t] = exp(s[t] - mx);
+                    sum += s[t];
+                }
+                for (int64_t e = 0; e < D; ++e) o[e] = 0.0;
+                for (int64_t t = 0; t <= last; ++t) {
+                    const double sv = (double)scales[vh * T + t];
+                    for (int64_t e = 0; e < D; ++e)
+                        o[e] += s[t] / sum * (sv * orc_e4m3_to_double(codes[(vh * T + t) * D + e]));
+                }
+                uint16_t *ov = out + ((b * Q + j) * Hq + h) * D;
+                for (int64_t e = 0; e < D; ++e) ov[e] = orc_double_to_bf16(o[e]);
+            }
+    free(s);
+    free(o);
+}
+
 /* ---- O10: the FP8 parent variant ---------------------------------------------
  * [SpecQuant notes, one-line summary, key contributions and approach: INT4, FP8
  * and FP16 variants of one FP16 model are made by post-training quantization

@@ -39,6 +39,11 @@ void orc_quantize_act_fp8(const uint16_t *x, int64_t M, int64_t K, uint8_t *code
 void orc_quantize_weights_fp8(const uint16_t *w, int64_t K, int64_t N, uint8_t *codes_nk, float *scales);
 void orc_gemm_w8a8(const uint8_t *a_codes, const float *a_scales, int64_t M, const uint8_t *w_store,
                    const float *w_scales, int64_t K, int64_t N, double *y);
+void orc_kv_overwrite_fp8(uint8_t *codes, float *scales, const uint16_t *verify_kv, const int32_t *start_pos,
+                          const int32_t *accept, int64_t L, int64_t B, int64_t H, int64_t T, int64_t D,
+                          int64_t gamma);
+void orc_attention_fp8(const uint16_t *q, const uint8_t *codes, const float *scales, const int32_t *pos, int64_t B,
+                       int64_t Q, int64_t Hq, int64_t Hkv, int64_t T, int64_t D, float scale, uint16_t *out);
 
 static uint64_t state = 0x9E3779B97F4A7C15ull;
 
@@ -219,6 +224,47 @@ static void kv(int64_t L, int64_t B, int64_t H, int64_t T, int64_t D, int64_t ga
     free(cache);
 }
 
+/* the quantized cache: rows written by the FP8 overwrite (edge starts and accept counts as in kv),
+ * then attention over one layer of it with the same causal edge positions as attention() */
+static void kv_fp8(int64_t L, int64_t B, int64_t H, int64_t T, int64_t gamma, int64_t Q)
+{
+    const int64_t D = 128;
+    uint8_t *codes = (uint8_t *)alloc((size_t)(L * B * 2 * H * T * D));
+    float *scales = (float *)alloc((size_t)(L * B * 2 * H * T) * sizeof(float));
+    uint16_t *stage = (uint16_t *)alloc((size_t)(L * B * 2 * H * (gamma + 1) * D) * 2);
+    int32_t *start = (int32_t *)alloc((size_t)B * sizeof(int32_t));
+    int32_t *acc = (int32_t *)alloc((size_t)B * sizeof(int32_t));
+    fill_bytes(codes, (size_t)(L * B * 2 * H * T * D));
+    for (int64_t i = 0; i < L * B * 2 * H * T * D; ++i)
+        if ((codes[i] & 0x7F) == 0x7F) codes[i] ^= 1;   /* no NaN codes */
+    for (int64_t i = 0; i < L * B * 2 * H * T; ++i) scales[i] = 0.01f * (float)(1 + i % 7);
+    fill_bf16(stage, (size_t)(L * B * 2 * H * (gamma + 1) * D));
+    for (int64_t i = 0; i < D; ++i) stage[i] = 0;          /* one all-zero row: s = 0, codes 0 */
+    for (int64_t b = 0; b < B; ++b) {
+        start[b] = b == 0 ? -2 : b == 1 ? (int32_t)(T - 1) : (int32_t)(next_u32() % (uint32_t)T);
+        acc[b] = b == 2 ? -4 : (int32_t)(next_u32() % (uint32_t)(gamma + 1));
+    }
+    start[B - 1] = 0;
+    acc[B - 1] = (int32_t)(gamma + 9);
+    orc_kv_overwrite_fp8(codes, scales, stage, start, acc, L, B, H, T, D, gamma);
+    /* attention over layer 0: its B sequences' codes and scales are contiguous */
+    const int64_t Hq = 2 * H;
+    uint16_t *q = (uint16_t *)alloc((size_t)(B * Q * Hq * D) * 2);
+    uint16_t *out = (uint16_t *)alloc((size_t)(B * Q * Hq * D) * 2);
+    int32_t *pos = (int32_t *)alloc((size_t)B * sizeof(int32_t));
+    fill_bf16(q, (size_t)(B * Q * Hq * D));
+    for (int64_t b = 0; b < B; ++b) pos[b] = b == 0 ? -3 : b == 1 ? (int32_t)(T + 5) : (int32_t)(next_u32() % (uint32_t)T);
+    orc_attention_fp8(q, codes, scales, pos, B, Q, Hq, H, T, D, 0.0883883f, out);
+    free(pos);
+    free(out);
+    free(q);
+    free(acc);
+    free(start);
+    free(stage);
+    free(scales);
+    free(codes);
+}
+
 static void fp8(int64_t M, int64_t K, int64_t N)
 {
     for (int c = 0; c < 256; ++c) {
@@ -278,6 +324,8 @@ int main(void)
     kv(2, 5, 2, 9, 8, 3);
     kv(1, 4, 1, 1, 4, 0);
     fp8(3, 256, 32);
+    kv_fp8(2, 4, 2, 9, 3, 2);
+    kv_fp8(1, 3, 1, 1, 0, 1);
     printf("oracle sanitizer driver: done\n");
     return 0;
 }
