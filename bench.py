@@ -566,7 +566,9 @@ def speckv_controller_us(R, torch):
 def attention_us(R, torch):
     """Outside the timed round: one layer's attention over a full 4096-position cache (B
     sequences, 32 query heads, 8 KV heads, d 128) for a draft step (Q = 1) and a verify pass
-    (Q = gamma + 1), graph-replayed; returns {Q: microseconds per call}."""
+    (Q = gamma + 1), graph-replayed; the bfloat16 cache (qspec_attention) and the quantized FP8
+    cache (qspec_attention_fp8: E4M3 codes, one scale per row), each rotated over enough copies to
+    exceed the 256 MB last-level cache.  Returns {(kind, Q): microseconds per call}."""
     import math
 
     import synthetic_inputs as si
@@ -580,18 +582,29 @@ def attention_us(R, torch):
         out = torch.empty((B, Q, Hq, HEAD_DIM), dtype=torch.bfloat16, device=dev)
         ws = torch.empty((q.qspec_attention_workspace_bytes(B, Q, Hq, KV_HEADS, CONTEXT),), dtype=torch.uint8,
                          device=dev)
-        graph = capture(lambda: [q.qspec_attention(qd, cache, pos, 1.0 / math.sqrt(HEAD_DIM), out, ws)
-                                 for _ in range(10)], torch)
-        graph.replay()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(3):
+        codes = torch.empty((B, 2, KV_HEADS, CONTEXT, HEAD_DIM), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, 2, KV_HEADS, CONTEXT), dtype=torch.float32, device=dev)
+        q.qspec_quantize_act_fp8(cache.view(-1, HEAD_DIM), codes.view(-1, HEAD_DIM), scales.view(-1))
+        bf_copies = [cache, cache.clone()]                                  # 2 x 268 MB
+        f8_copies = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(3)]   # 4 x 136 MB
+        for kind, fn, n in (
+                ("bf16", lambda: [q.qspec_attention(qd, bf_copies[i % 2], pos, 1.0 / math.sqrt(HEAD_DIM), out, ws)
+                                  for i in range(8)], 8),
+                ("fp8", lambda: [q.qspec_attention_fp8(qd, *f8_copies[i % 4], pos, 1.0 / math.sqrt(HEAD_DIM), out, ws)
+                                 for i in range(8)], 8)):
+            graph = capture(fn, torch)
             graph.replay()
-        b.record()
-        torch.cuda.synchronize()
-        res[Q] = a.elapsed_time(b) * 1e3 / 30
-        del qd, cache
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(3):
+                graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            res[(kind, Q)] = a.elapsed_time(b) * 1e3 / (3 * n)
+            del graph
+        del qd, cache, codes, scales, bf_copies, f8_copies
+        torch.cuda.empty_cache()
     return res
 
 
@@ -1090,11 +1103,17 @@ def main():
         # outside the timed round: the adaptive-gamma controller on one draft row per sequence
         "speckv_us_per_draft_step": R.speckv_us,
         # outside the timed round: one layer's attention over the full cache; every key and value
-        # (B x 8 heads x 4096 positions x 2 x 256 bytes) is read once per call
+        # (B x 8 heads x 4096 positions x 2 rows of 256 bytes in bfloat16, of 128 code bytes and a
+        # 4-byte scale in the quantized FP8 cache) is read once per call
         "attention": {"workload": f"B{B}-Hq32-Hkv{KV_HEADS}-d{HEAD_DIM}-T{CONTEXT}-one-layer",
-                      **{f"us_Q{Qa}": round(u, 1) for Qa, u in R.attention.items()},
+                      **{f"us_Q{Qa}": round(u, 1) for (k, Qa), u in R.attention.items() if k == "bf16"},
                       **{f"hbm_frac_Q{Qa}": round(B * KV_HEADS * CONTEXT * 2 * HEAD_DIM * 2 / (u * 1e-6) / 1e9
-                                                  / HBM_PEAK_GBS, 4) for Qa, u in R.attention.items()}},
+                                                  / HBM_PEAK_GBS, 4) for (k, Qa), u in R.attention.items() if k == "bf16"},
+                      "fp8_cache": {
+                          **{f"us_Q{Qa}": round(u, 1) for (k, Qa), u in R.attention.items() if k == "fp8"},
+                          **{f"hbm_frac_Q{Qa}": round(B * KV_HEADS * CONTEXT * 2 * (HEAD_DIM + 4) / (u * 1e-6) / 1e9
+                                                      / HBM_PEAK_GBS, 4) for (k, Qa), u in R.attention.items()
+                             if k == "fp8"}}},
         # outside the timed round: the FP8 parent (W8A8, E4M3) verifying gamma = 4 drafts of one
         # sequence (M = 5) on Qwen2.5-7B's projections; HBM fraction of the weight bytes alone
         "fp8_parent_qwen25_7b_M5": {

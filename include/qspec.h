@@ -306,6 +306,46 @@ int qspec_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const int32_t
                        int32_t D, int32_t gamma, qspec_stream_t stream);
 
 /*
+ * qspec_kv_overwrite_fp8 -- replace draft KV with verify KV in a quantized (FP8) cache.
+ * [QSPEC notes: the opening summary speaks of quantized KV; QSPEC structure: for accepted tokens
+ * the draft's low-precision KV is replaced with the verifier's.]  The page fixes no KV format;
+ * this cache holds OCP FP8 E4M3 codes with one binary32 scale per (position, head) row of D = 128
+ * values, the per-row quantizer of qspec_quantize_act_fp8: s = max |v| / 448 (binary32 division),
+ * code = the nearest E4M3 value to v / s (ties to even, binary32 quotient, saturating), s = 0 and
+ * codes 0 for an all-zero row; a value reads back as s * decoded code.  Rows r = 0..A_b of
+ * verify_kv are quantized and written at positions start_pos[b] + r (as qspec_kv_overwrite:
+ * A_b clamped to [0, gamma], positions outside [0, T) skipped); nothing else changes.
+ * cache_codes  [in/out] u8  [L][B][2][H][T][D]
+ * cache_scales [in/out] f32 [L][B][2][H][T]
+ * verify_kv    [in]     u16 [L][B][2][H][gamma+1][D] bfloat16 (finite)
+ * start_pos, accept_count [in] i32 [B] (device)
+ * Errors: NULL pointer; any size < 1 (gamma < 0); gamma + 1 > T; D != QSPEC_ATTN_HEAD_DIM;
+ * misaligned cache_codes (2 bytes), cache_scales / verify_kv / start_pos / accept_count (4).
+ */
+int qspec_kv_overwrite_fp8(uint8_t *cache_codes, float *cache_scales, const uint16_t *verify_kv,
+                           const int32_t *start_pos, const int32_t *accept_count, int32_t L, int32_t B, int32_t H,
+                           int32_t T, int32_t D, int32_t gamma, qspec_stream_t stream);
+
+/*
+ * qspec_attention_fp8 -- qspec_attention over one layer of the quantized (FP8) cache.
+ * [QSPEC notes: quantized KV, read by the draft and the verifier alike.]  The arithmetic of
+ * qspec_attention, with key and value t of a head read back as s_t * decoded code: the MFMAs take
+ * the codes widened exactly to bfloat16, each score is multiplied by its key's scale and each
+ * probability by its value's scale (the softmax normalizer keeps the unscaled probabilities).
+ * Half the bytes of the bfloat16 cache are read.
+ * q            [in]  u16 [B][Q][Hq][D] bfloat16
+ * cache_codes  [in]  u8  [B][2][Hkv][T][D]: one layer of the [L][B][2][H][T][D] codes
+ * cache_scales [in]  f32 [B][2][Hkv][T]:    the same layer's scales (finite)
+ * pos, D, scale, out, workspace: as qspec_attention (workspace of
+ *              qspec_attention_workspace_bytes bytes)
+ * Errors: those of qspec_attention; cache_codes needs 16-byte and cache_scales 4-byte alignment.
+ */
+int qspec_attention_fp8(const uint16_t *q, const uint8_t *cache_codes, const float *cache_scales,
+                        const int32_t *pos, int32_t B, int32_t Q, int32_t Hq, int32_t Hkv, int32_t T, int32_t D,
+                        float scale, uint16_t *out, void *workspace, size_t workspace_bytes,
+                        qspec_stream_t stream);
+
+/*
  * qspec_speckv_workspace_bytes -- device workspace qspec_speckv_gamma needs for R rows of V
  * logits; 0 on invalid sizes.
  */

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.qspec_attention_workspace_bytes.argtypes = [I, I, I, I, I]
         L.qspec_attention_workspace_bytes.restype = S
         L.qspec_attention.argtypes = [P, P, P, I, I, I, I, I, I, ctypes.c_float, P, P, S, P]
+        L.qspec_attention_fp8.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float, P, P, S, P]
+        L.qspec_kv_overwrite_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
         L.qspec_quantize_act_fp8.argtypes = [P, I, I, P, P, P]
         L.qspec_gemm_w8a8_workspace_bytes.argtypes = [I, I, I]
         L.qspec_gemm_w8a8_workspace_bytes.restype = S
@@ -84,7 +86,7 @@ def lib() -> ctypes.CDLL:
         for fn in ("qspec_quantize_act", "qspec_gemm_w4a4", "qspec_gemm_w4a16", "qspec_verify_accept",
                    "qspec_kv_overwrite", "qspec_speckv_gamma", "qspec_attention", "qspec_quantize_act_fp8",
                    "qspec_gemm_w8a8", "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier", "qspec_verify_accept_noalloc",
-                   "qspec_draft_sample_speckv"):
+                   "qspec_draft_sample_speckv", "qspec_attention_fp8", "qspec_kv_overwrite_fp8"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -369,6 +371,47 @@ def qspec_speckv_gamma(draft_logits, quant_feature, w1, b1, w2, b2, gamma_out, f
            lib().qspec_speckv_gamma(_ptr(draft_logits), R, V, float(quant_feature), _ptr(w1), _ptr(b1), _ptr(w2),
                                     _ptr(b2), G1 - 1, _ptr(features), _ptr(gamma_out), _ptr(workspace),
                                     workspace.numel(), _stream(stream, draft_logits)))
+
+
+def qspec_kv_overwrite_fp8(cache_codes, cache_scales, verify_kv, start_pos, accept_count, stream=None) -> None:
+    """Quantized cache: codes u8 [L][B][2][H][T][D], scales f32 [L][B][2][H][T] <- rows 0..A_b of
+    verify_kv bf16 [L][B][2][H][gamma+1][D], quantized per row (FP8 E4M3, absmax / 448)."""
+    _req(cache_codes, "cache_codes", torch.uint8)
+    if cache_codes.dim() != 6 or cache_codes.shape[2] != 2:
+        raise ValueError("cache_codes must be [L][B][2][H][T][D]")
+    L, B, _, H, T, D = cache_codes.shape
+    _req(cache_scales, "cache_scales", torch.float32, (L, B, 2, H, T))
+    _req(verify_kv, "verify_kv", torch.bfloat16)
+    if verify_kv.dim() != 6:
+        raise ValueError("verify_kv must be [L][B][2][H][gamma+1][D]")
+    gamma = verify_kv.shape[4] - 1
+    _req(verify_kv, "verify_kv", torch.bfloat16, (L, B, 2, H, gamma + 1, D))
+    _req(start_pos, "start_pos", torch.int32, (B,))
+    _req(accept_count, "accept_count", torch.int32, (B,))
+    _check("qspec_kv_overwrite_fp8",
+           lib().qspec_kv_overwrite_fp8(_ptr(cache_codes), _ptr(cache_scales), _ptr(verify_kv), _ptr(start_pos),
+                                        _ptr(accept_count), L, B, H, T, D, gamma, _stream(stream, cache_codes)))
+
+
+def qspec_attention_fp8(q, cache_codes, cache_scales, pos, scale, out, workspace, stream=None) -> None:
+    """Causal attention over one layer of the quantized cache; see include/qspec.h.
+    q bf16 [B][Q][Hq][D]; cache_codes u8 [B][2][Hkv][T][D]; cache_scales f32 [B][2][Hkv][T];
+    pos i32 [B]; out bf16 [B][Q][Hq][D]; workspace u8 (qspec_attention_workspace_bytes)."""
+    _req(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B][Q][Hq][D]")
+    B, Q, Hq, D = q.shape
+    _req(cache_codes, "cache_codes", torch.uint8)
+    if cache_codes.dim() != 5 or cache_codes.shape[0] != B or cache_codes.shape[1] != 2 or cache_codes.shape[4] != D:
+        raise ValueError("cache_codes must be [B][2][Hkv][T][D]")
+    Hkv, T = cache_codes.shape[2], cache_codes.shape[3]
+    _req(cache_scales, "cache_scales", torch.float32, (B, 2, Hkv, T))
+    _req(pos, "pos", torch.int32, (B,))
+    _req(out, "out", torch.bfloat16, (B, Q, Hq, D))
+    _req(workspace, "workspace", torch.uint8)
+    _check("qspec_attention_fp8",
+           lib().qspec_attention_fp8(_ptr(q), _ptr(cache_codes), _ptr(cache_scales), _ptr(pos), B, Q, Hq, Hkv, T, D,
+                                     float(scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream, q)))
 
 
 def qspec_attention_workspace_bytes(B: int, Q: int, Hq: int, Hkv: int, T: int) -> int:

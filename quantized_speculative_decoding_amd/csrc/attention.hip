@@ -67,11 +67,25 @@ __device__ __forceinline__ attn_bf16x8_t attn_as_bf16x8(uint32_t a, uint32_t b, 
     return __builtin_bit_cast(attn_bf16x8_t, u);
 }
 
-template <int RT>
+// Eight E4M3 codes (two dwords, code i in byte i) as eight bfloat16 values in the same order (every
+// E4M3 value is a bfloat16 value: the conversion is exact).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false), e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+    return make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(d[0], d[1]), pack_bf16x2(e[0], e[1]));
+}
+
+// FP8: the cache is E4M3 codes [B][2][Hkv][T][D] (kv) with one scale per (position, head) row,
+// [B][2][Hkv][T] (kvs).  Keys and values are read as codes (half the bytes), widened exactly to
+// bfloat16 in registers for the same MFMAs, and the scales enter where they factor out: a score
+// is multiplied by its key's scale, and a probability by its value's scale before the PV product
+// (the row sum keeps the unscaled probability).
+template <int RT, bool FP8>
 __global__ void __launch_bounds__(kAttnWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
-k_attn_partial(const uint16_t *__restrict__ q, const uint16_t *__restrict__ cache, const int32_t *__restrict__ pos,
-               int Q, int Hq, int Hkv, int T, float scale, int NC, float *__restrict__ wm, float *__restrict__ wl,
-               float *__restrict__ wo) {
+k_attn_partial(const uint16_t *__restrict__ q, const void *__restrict__ kv, const float *__restrict__ kvs,
+               const int32_t *__restrict__ pos, int Q, int Hq, int Hkv, int T, float scale, int NC,
+               float *__restrict__ wm, float *__restrict__ wl, float *__restrict__ wo) {
     constexpr int ROWS = 16 * RT;
     __shared__ float sm[kAttnWaves][ROWS], sl[kAttnWaves][ROWS];
     __shared__ __attribute__((aligned(16))) float so[kAttnWaves][ROWS][kAttnOPitch];
@@ -92,23 +106,62 @@ k_attn_partial(const uint16_t *__restrict__ q, const uint16_t *__restrict__ cach
     // Wave-uniform buffer resources over the group's key and value planes, ending after the last
     // visible position: rows past it read as zero (their probabilities are zero).
     const size_t plane = (size_t)T * kAttnD;
-    const rsrc_t kr = make_rsrc(cache + ((size_t)(b * 2 + 0) * Hkv + hk) * plane, (uint32_t)(lastmax + 1) * 256u);
-    const rsrc_t vr = make_rsrc(cache + ((size_t)(b * 2 + 1) * Hkv + hk) * plane, (uint32_t)(lastmax + 1) * 256u);
-    const uint32_t kvo = (uint32_t)c * 256u + 16u * kq;          // key row c of a tile, d = 8 kq ..
-    const uint32_t vvo = (uint32_t)kq * 1024u + 16u * c;         // value rows 4 kq + i, d = 8 c ..
+    constexpr uint32_t ROWB = FP8 ? kAttnD : 2 * kAttnD;         // bytes per cached row
+    const uint8_t *kvb = (const uint8_t *)kv;
+    const rsrc_t kr = make_rsrc(kvb + ((size_t)(b * 2 + 0) * Hkv + hk) * plane * (ROWB / kAttnD),
+                                (uint32_t)(lastmax + 1) * ROWB);
+    const rsrc_t vr = make_rsrc(kvb + ((size_t)(b * 2 + 1) * Hkv + hk) * plane * (ROWB / kAttnD),
+                                (uint32_t)(lastmax + 1) * ROWB);
+    // per-row scales (FP8): the same positions' key and value scales; rows past the last visible
+    // position read as zero (their probabilities are zero)
+    const rsrc_t ksr = make_rsrc(FP8 ? kvs + ((size_t)(b * 2 + 0) * Hkv + hk) * T : kvs, FP8 ? (uint32_t)(lastmax + 1) * 4u : 0u);
+    const rsrc_t vsr = make_rsrc(FP8 ? kvs + ((size_t)(b * 2 + 1) * Hkv + hk) * T : kvs, FP8 ? (uint32_t)(lastmax + 1) * 4u : 0u);
+    constexpr uint32_t EB = FP8 ? 1u : 2u;                        // bytes per element
+    const uint32_t kvo = (uint32_t)c * ROWB + 8u * EB * kq;      // key row c of a tile, d = 8 kq ..
+    const uint32_t vvo = (uint32_t)kq * 4u * ROWB + 8u * EB * c; // value rows 4 kq + i, d = 8 c ..
 
     // K of step s: [position tile tt][d step j]; V of step s: [position slot i]
+    // FP8 keys: lane (c, kq) holds the 32 contiguous codes d = 32 kq .. 32 kq + 31 of its row (two
+    // 16-byte loads per tile) and MFMA j takes d = 32 kq + 8 j + i, the queries in the same slots;
+    // the contraction over d is the same sum, and a quarter of the bfloat16 layout's loads.
     auto load_k = [&](int s, uint4 (&kb)[2][4]) {
-        const uint32_t so = (uint32_t)(wbase + s * kAttnStep) * 256u;
+        const uint32_t so = (uint32_t)(wbase + s * kAttnStep) * ROWB;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            if constexpr (FP8) {
+                const uint32_t off = (uint32_t)c * ROWB + 32u * kq + tt * 16u * ROWB;
+                kb[tt][0] = buf_load16(kr, off, so);
+                kb[tt][1] = buf_load16(kr, off + 16u, so);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kb[tt][j] = buf_load16(kr, kvo + tt * 16u * ROWB + 32u * EB * j, so);
+            }
+        }
+    };
+    auto load_v = [&](int s, uint4 (&vb)[8]) {
+        const uint32_t so = (uint32_t)(wbase + s * kAttnStep) * ROWB;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t off = vvo + (i < 4 ? i : 12 + i) * ROWB;
+            if constexpr (FP8) {
+                typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+                const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(vr, off, so, 0));
+                vb[i].x = v[0];
+                vb[i].y = v[1];
+            } else {
+                vb[i] = buf_load16(vr, off, so);
+            }
+        }
+    };
+    // scales of the lane's 8 position slots of step s: tile tt, positions 16 tt + 4 kq + e; one
+    // dword load each, so that every position up to the last visible one reads its own scale and
+    // every later one reads zero (a 16-byte load straddling the range end is not split)
+    auto load_scales = [&](const rsrc_t &r, int s, float (&sc8)[8]) {
+        const uint32_t so = (uint32_t)(wbase + s * kAttnStep) * 4u;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) kb[tt][j] = buf_load16(kr, kvo + tt * 4096u + 64u * j, so);
-    };
-    auto load_v = [&](int s, uint4 (&vb)[8]) {
-        const uint32_t so = (uint32_t)(wbase + s * kAttnStep) * 256u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vb[i] = buf_load16(vr, vvo + (i < 4 ? i : 12 + i) * 256u, so);
+            for (int e = 0; e < 4; ++e) sc8[4 * tt + e] = __uint_as_float(buf_load4(r, (16u * tt + 4u * kq + e) * 4u, so));
     };
 
     for (int rp = 0; rp < R; rp += ROWS) {
@@ -145,9 +198,26 @@ k_attn_partial(const uint16_t *__restrict__ q, const uint16_t *__restrict__ cach
         for (int s = 0; s < kAttnSteps; ++s) {
             if (s < ns) {
                 const int cb = s & 1;
+                float ks[8], vs[8];
+                if constexpr (FP8) {
+                    load_scales(ksr, s, ks);
+                    load_scales(vsr, s, vs);
+                }
                 if (s + 1 < ns) load_k(s + 1, kb[cb ^ 1]);
                 if (!VRING) load_v(s, vb[0]);
                 const int tb = wbase + s * kAttnStep;
+                uint4 kw[2][4];                                   // this step's keys as bfloat16
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (FP8) {
+                            const uint4 raw = kb[cb][tt][j >> 1];
+                            kw[tt][j] = e4m3x8_to_bf16x8(j & 1 ? make_uint2(raw.z, raw.w) : make_uint2(raw.x, raw.y));
+                        } else {
+                            kw[tt][j] = kb[cb][tt][j];
+                        }
+                    }
                 attn_bf16x8_t phi[RT], plo[RT];
                 float alpha[RT];
 #pragma unroll
@@ -159,13 +229,14 @@ k_attn_partial(const uint16_t *__restrict__ q, const uint16_t *__restrict__ cach
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(attn_bf16x8_t, kb[cb][tt][j]),
-                                __builtin_bit_cast(attn_bf16x8_t, *(const uint4 *)&qs[rt * 16 + c][32 * j + 8 * kq]),
+                                __builtin_bit_cast(attn_bf16x8_t, kw[tt][j]),
+                                __builtin_bit_cast(attn_bf16x8_t, *(const uint4 *)&qs[rt * 16 + c][FP8 ? 32 * kq + 8 * j : 32 * j + 8 * kq]),
                                 acc, 0, 0, 0);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int t = tb + 16 * tt + 4 * kq + e;
-                            sc[tt * 4 + e] = t <= last[rt] ? acc[e] * scale : -INFINITY;
+                            const float a = FP8 ? acc[e] * ks[tt * 4 + e] : acc[e];
+                            sc[tt * 4 + e] = t <= last[rt] ? a * scale : -INFINITY;
                         }
                     }
                     float mk = sc[0];
@@ -189,6 +260,10 @@ k_attn_partial(const uint16_t *__restrict__ q, const uint16_t *__restrict__ cach
 #pragma unroll
                     for (int i = 0; i < 8; ++i) ps += p[i];
                     l[rt] = __builtin_fmaf(l[rt], alpha[rt], ps);
+                    if constexpr (FP8) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) p[i] *= vs[i];
+                    }
                     uint32_t ph[4], pl[4];
 #pragma unroll
                     for (int k2 = 0; k2 < 4; ++k2) {
@@ -201,14 +276,17 @@ k_attn_partial(const uint16_t *__restrict__ q, const uint16_t *__restrict__ cach
                 }
                 if (VRING && s + 1 < ns) load_v(s + 1, vb[(cb ^ 1) % (VRING ? 2 : 1)]);
                 const int vc = VRING ? cb : 0;
+                uint4 vw[8];                                      // this step's values as bfloat16
+#pragma unroll
+                for (int i = 0; i < 8; ++i) vw[i] = FP8 ? e4m3x8_to_bf16x8(make_uint2(vb[vc][i].x, vb[vc][i].y)) : vb[vc][i];
 #pragma unroll
                 for (int mm = 0; mm < 8; ++mm) {
                     // V[slot i][8 c + mm] for the 8 position slots, transposed in registers
                     uint32_t d4[4];
 #pragma unroll
                     for (int k2 = 0; k2 < 4; ++k2) {
-                        const uint32_t x = ((const uint32_t *)&vb[vc][2 * k2])[mm >> 1];
-                        const uint32_t y = ((const uint32_t *)&vb[vc][2 * k2 + 1])[mm >> 1];
+                        const uint32_t x = ((const uint32_t *)&vw[2 * k2])[mm >> 1];
+                        const uint32_t y = ((const uint32_t *)&vw[2 * k2 + 1])[mm >> 1];
                         d4[k2] = (mm & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
                     }
                     const attn_bf16x8_t vt = attn_as_bf16x8(d4[0], d4[1], d4[2], d4[3]);
@@ -315,20 +393,32 @@ k_attn_combine(const int32_t *__restrict__ pos, int Q, int Hq, int T, int NC, co
     out[(size_t)row * kAttnD + d] = to_bf16_bits(acc / L);
 }
 
-hipError_t launch_attention(const uint16_t *q, const uint16_t *cache, const int32_t *pos, int B, int Q, int Hq,
-                            int Hkv, int T, float scale, uint16_t *out, void *ws, hipStream_t st) {
+template <bool FP8>
+static hipError_t launch_attn(const uint16_t *q, const void *kv, const float *kvs, const int32_t *pos, int B, int Q,
+                              int Hq, int Hkv, int T, float scale, uint16_t *out, void *ws, hipStream_t st) {
     const AttnLayout L = attn_layout(B, Q, Hq, T);
     char *w = (char *)ws;
     float *wm = (float *)(w + L.m), *wl = (float *)(w + L.l), *wo = (float *)(w + L.o);
     const dim3 grid(L.NC, B * Hkv);
     if (Q * (Hq / Hkv) <= 16)
-        hipLaunchKernelGGL(k_attn_partial<1>, grid, dim3(kAttnWaves * kWave), 0, st, q, cache, pos, Q, Hq, Hkv, T,
-                           scale, L.NC, wm, wl, wo);
+        hipLaunchKernelGGL((k_attn_partial<1, FP8>), grid, dim3(kAttnWaves * kWave), 0, st, q, kv, kvs, pos, Q, Hq,
+                           Hkv, T, scale, L.NC, wm, wl, wo);
     else
-        hipLaunchKernelGGL(k_attn_partial<2>, grid, dim3(kAttnWaves * kWave), 0, st, q, cache, pos, Q, Hq, Hkv, T,
-                           scale, L.NC, wm, wl, wo);
+        hipLaunchKernelGGL((k_attn_partial<2, FP8>), grid, dim3(kAttnWaves * kWave), 0, st, q, kv, kvs, pos, Q, Hq,
+                           Hkv, T, scale, L.NC, wm, wl, wo);
     hipLaunchKernelGGL(k_attn_combine, dim3(B * Q * Hq), dim3(kAttnD), 0, st, pos, Q, Hq, T, L.NC, wm, wl, wo, out);
     return hipGetLastError();
+}
+
+hipError_t launch_attention(const uint16_t *q, const uint16_t *cache, const int32_t *pos, int B, int Q, int Hq,
+                            int Hkv, int T, float scale, uint16_t *out, void *ws, hipStream_t st) {
+    return launch_attn<false>(q, cache, nullptr, pos, B, Q, Hq, Hkv, T, scale, out, ws, st);
+}
+
+hipError_t launch_attention_fp8(const uint16_t *q, const uint8_t *codes, const float *scales, const int32_t *pos,
+                                int B, int Q, int Hq, int Hkv, int T, float scale, uint16_t *out, void *ws,
+                                hipStream_t st) {
+    return launch_attn<true>(q, codes, scales, pos, B, Q, Hq, Hkv, T, scale, out, ws, st);
 }
 
 }  // namespace qspec

@@ -39,6 +39,26 @@ __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t 
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
+// Nearest E4M3 code to a finite binary32 value, ties to even, saturating at +-448; the sign bit
+// is the value's.  Normal range: a * 2^(3 - e) lies in [8, 16) and rounds (exactly, nearest
+// even) to the 4-bit significand, a carry to 16 moving into the exponent field; below 2^-6 the
+// subnormal step is 2^-9.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    uint32_t code;
+    if (!(a < 448.0f)) {
+        code = 0x7Eu;
+    } else if (a < 0x1p-6f) {
+        code = (uint32_t)__builtin_rintf(a * 0x1p9f);
+    } else {
+        const int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;        // -6 .. 8
+        const float sig = a * __uint_as_float((uint32_t)(127 + 3 - e) << 23);  // [8, 16), exact
+        code = (uint32_t)((e + 7) << 3) + (uint32_t)__builtin_rintf(sig) - 8u;
+    }
+    return sign | code;
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
     return __uint_as_float(b << 16);
 }

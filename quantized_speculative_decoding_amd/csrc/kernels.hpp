@@ -76,5 +76,14 @@ hipError_t launch_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const
                                const int32_t *accept_count, int L, int B, int H, int T, int D,
                                int gamma, hipStream_t st);
 
+// The quantized (FP8 E4M3, one scale per row of 128) cache: committed rows quantized as written,
+// and attention over it.
+hipError_t launch_kv_overwrite_fp8(uint8_t *codes, float *scales, const uint16_t *verify_kv,
+                                   const int32_t *start_pos, const int32_t *accept_count, int L, int B, int H,
+                                   int T, int gamma, hipStream_t st);
+hipError_t launch_attention_fp8(const uint16_t *q, const uint8_t *codes, const float *scales, const int32_t *pos,
+                                int B, int Q, int Hq, int Hkv, int T, float scale, uint16_t *out, void *workspace,
+                                hipStream_t st);
+
 
 }  // namespace qspec

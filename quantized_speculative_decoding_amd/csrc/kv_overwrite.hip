@@ -51,4 +51,48 @@ hipError_t launch_kv_overwrite(uint16_t *cache, const uint16_t *verify_kv, const
     return hipGetLastError();
 }
 
+// The quantized cache (FP8 E4M3 codes [L][B][2][H][T][128] with one binary32 scale per
+// (position, head) row, [L][B][2][H][T]): a committed row is quantized as it is written, with the
+// per-row quantizer of the FP8 variant (s = max |v| / 448, code = E4M3(v / s), nearest even,
+// binary32 division; an all-zero row gets s = 0 and zero codes).  One wave per candidate row
+// (head, r): lane l holds elements 2 l and 2 l + 1; the row's absmax is a wave max.  Rows past
+// the accept count or outside [0, T) are skipped by the whole wave.
+constexpr int kKvD = 128;
+
+__global__ void __launch_bounds__(256)
+k_kv_overwrite_fp8(uint8_t *__restrict__ codes, float *__restrict__ scales, const uint16_t *__restrict__ vkv,
+                   const int32_t *__restrict__ start_pos, const int32_t *__restrict__ accept, int B, int H, int T,
+                   int gamma, long long rows) {
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;                                   // uniform per wave
+    const int lane = threadIdx.x & 63;
+    const int r = (int)(row % (gamma + 1));
+    const long long head = row / (gamma + 1);                  // ((l * B + b) * 2 + kv) * H + h
+    const int b = (int)((head / (2LL * H)) % B);
+    int A = accept[b];
+    A = A < 0 ? 0 : (A > gamma ? gamma : A);
+    if (r > A) return;
+    const long long t = (long long)start_pos[b] + r;
+    if (t < 0 || t >= T) return;
+    const uint32_t pair = *(const uint32_t *)(vkv + (size_t)row * kKvD + 2 * lane);
+    const float x0 = bf16_bits_to_float(pair & 0xFFFFu), x1 = bf16_bits_to_float(pair >> 16);
+    const float a = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    const float s = a / 448.0f;
+    uint32_t c = 0;
+    if (a != 0.0f) c = f32_to_e4m3(x0 / s) | (f32_to_e4m3(x1 / s) << 8);
+    *(uint16_t *)(codes + ((size_t)head * T + (size_t)t) * kKvD + 2 * lane) = (uint16_t)c;
+    if (lane == 0) scales[(size_t)head * T + (size_t)t] = s;
+}
+
+hipError_t launch_kv_overwrite_fp8(uint8_t *codes, float *scales, const uint16_t *verify_kv,
+                                   const int32_t *start_pos, const int32_t *accept_count, int L, int B, int H,
+                                   int T, int gamma, hipStream_t st) {
+    const long long rows = (long long)L * B * 2 * H * (gamma + 1);
+    const unsigned blocks = (unsigned)((rows + 3) / 4);
+    hipLaunchKernelGGL(k_kv_overwrite_fp8, dim3(blocks), dim3(256), 0, st, codes, scales, verify_kv, start_pos,
+                       accept_count, B, H, T, gamma, rows);
+    return hipGetLastError();
+}
+
 }  // namespace qspec
+

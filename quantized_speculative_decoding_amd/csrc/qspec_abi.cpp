@@ -241,6 +241,35 @@ QSPEC_EXPORT int qspec_attention(const uint16_t *q, const uint16_t *cache, const
                                              as_stream(stream)));
 }
 
+QSPEC_EXPORT int qspec_kv_overwrite_fp8(uint8_t *cache_codes, float *cache_scales, const uint16_t *verify_kv,
+                                        const int32_t *start_pos, const int32_t *accept_count, int32_t L, int32_t B,
+                                        int32_t H, int32_t T, int32_t D, int32_t gamma, qspec_stream_t stream) {
+    if (!cache_codes || !cache_scales || !verify_kv || !start_pos || !accept_count) return QSPEC_ERR_NULL;
+    if (L < 1 || B < 1 || H < 1 || T < 1 || gamma < 0 || gamma + 1 > T || D != QSPEC_ATTN_HEAD_DIM)
+        return QSPEC_ERR_SHAPE;
+    if ((long long)L * B * 2 * H * T * D > kMaxElems || (long long)L * B * 2 * H * (gamma + 1) >= (1LL << 31) * 4)
+        return QSPEC_ERR_SHAPE;
+    if (!aligned(cache_codes, 2) || !aligned(cache_scales, 4) || !aligned(verify_kv, 4) || !aligned(start_pos, 4) ||
+        !aligned(accept_count, 4))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_kv_overwrite_fp8(cache_codes, cache_scales, verify_kv, start_pos, accept_count, L,
+                                                    B, H, T, gamma, as_stream(stream)));
+}
+
+QSPEC_EXPORT int qspec_attention_fp8(const uint16_t *q, const uint8_t *cache_codes, const float *cache_scales,
+                                     const int32_t *pos, int32_t B, int32_t Q, int32_t Hq, int32_t Hkv, int32_t T,
+                                     int32_t D, float scale, uint16_t *out, void *workspace, size_t workspace_bytes,
+                                     qspec_stream_t stream) {
+    if (!q || !cache_codes || !cache_scales || !pos || !out) return QSPEC_ERR_NULL;
+    if (!attention_sizes_ok(B, Q, Hq, Hkv, T, D)) return QSPEC_ERR_SHAPE;
+    if (!workspace || workspace_bytes < qspec::attention_workspace_bytes(B, Q, Hq, T)) return QSPEC_ERR_WORKSPACE;
+    if (!aligned(q, 16) || !aligned(cache_codes, 16) || !aligned(cache_scales, 4) || !aligned(pos, 4) ||
+        !aligned(out, 2) || !aligned(workspace, 16))
+        return QSPEC_ERR_ALIGN;
+    return status_of(qspec::launch_attention_fp8(q, cache_codes, cache_scales, pos, B, Q, Hq, Hkv, T, scale, out,
+                                                 workspace, as_stream(stream)));
+}
+
 // The W8A8 kernels address a_codes (M * K bytes) and the FP8 store (K * N bytes) through 32-bit
 // buffer offsets.
 static bool w8a8_sizes_ok(int32_t M, int32_t K, int32_t N) {

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
         "qspec_attention_workspace_bytes", "qspec_attention", "qspec_quantize_act_fp8",
         "qspec_gemm_w8a8_workspace_bytes", "qspec_gemm_w8a8", "qspec_draft_sample_workspace_bytes",
         "qspec_draft_sample", "qspec_gemm_w4a16_tier", "qspec_gemm_w4a4_tier", "qspec_verify_accept_noalloc",
-        "qspec_draft_sample_speckv", "qspec_draft_sample_speckv_workspace_bytes"])
+        "qspec_draft_sample_speckv", "qspec_draft_sample_speckv_workspace_bytes", "qspec_kv_overwrite_fp8",
+        "qspec_attention_fp8"])
 
 
 def test_library_exports_every_declared_symbol_and_nothing_else():
@@ -379,3 +380,35 @@ def test_draft_sample_speckv_validation():
     assert L.qspec_draft_sample_speckv(*bad) == ERR_WS
     bad = list(args); bad[14] = ctypes.c_void_p(0x1004)              # features are f64
     assert L.qspec_draft_sample_speckv(*bad) == ERR_ALIGN
+
+
+def test_quantized_kv_validation():
+    """The FP8 cache calls check what their bfloat16 counterparts check, plus the head dimension
+    (128) of the overwrite and the alignment of codes and scales."""
+    L = q.lib()
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 3, 2, 16, 128, 4, None]
+    for i in range(5):
+        bad = list(ok); bad[i] = None
+        assert L.qspec_kv_overwrite_fp8(*bad) == ERR_NULL, i
+    for i, v in ((5, 0), (6, 0), (7, 0), (8, 0), (9, 64), (10, -1), (10, 16)):
+        bad = list(ok); bad[i] = v
+        assert L.qspec_kv_overwrite_fp8(*bad) == ERR_SHAPE, (i, v)
+    bad = list(ok); bad[1] = ctypes.c_void_p(0x1002)
+    assert L.qspec_kv_overwrite_fp8(*bad) == ERR_ALIGN
+    bad = list(ok); bad[0] = ctypes.c_void_p(0x1001)
+    assert L.qspec_kv_overwrite_fp8(*bad) == ERR_ALIGN
+    need = L.qspec_attention_workspace_bytes(2, 1, 8, 2, 100)
+    f = ctypes.c_float(0.088)
+    ok = [FAKE, FAKE, FAKE, FAKE, 2, 1, 8, 2, 100, 128, f, FAKE, FAKE, need, None]
+    for i in (0, 1, 2, 3, 11):
+        bad = list(ok); bad[i] = None
+        assert L.qspec_attention_fp8(*bad) == ERR_NULL, i
+    for i, v in ((4, 0), (9, 64), (6, 7), (5, 65)):
+        bad = list(ok); bad[i] = v
+        assert L.qspec_attention_fp8(*bad) == ERR_SHAPE, (i, v)
+    bad = list(ok); bad[13] = need - 1
+    assert L.qspec_attention_fp8(*bad) == ERR_WS
+    bad = list(ok); bad[1] = ctypes.c_void_p(0x1008)
+    assert L.qspec_attention_fp8(*bad) == ERR_ALIGN
+    bad = list(ok); bad[2] = ctypes.c_void_p(0x1002)
+    assert L.qspec_attention_fp8(*bad) == ERR_ALIGN
