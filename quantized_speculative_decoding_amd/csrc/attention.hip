@@ -16,8 +16,8 @@
 // the online softmax needs only two cross-lane steps per reduction.  Probabilities enter the MFMA
 // as a bf16 pair hi + lo (p - hi is exact in fp32), which keeps them to about 2^-17 relative.
 //
-// A wave streams 128 positions (4 steps of 32) through a 2-deep register ring; the 4 waves of a
-// workgroup cover a chunk of 512 positions and merge their (max, sum, outputs) through LDS in
+// A wave streams 256 positions (8 steps of 32) through a 2-deep register ring; the 4 waves of a
+// workgroup cover a chunk of 1024 positions and merge their (max, sum, outputs) through LDS in
 // wave order; k_attn_combine merges the chunks of each query row in chunk order.  Keys and values
 // are buffer loads whose range ends after the group's last visible position, so later rows of
 // the cache are never read.
@@ -29,8 +29,8 @@ namespace qspec {
 constexpr int kAttnD = 128;                      // head dimension
 constexpr int kAttnWaves = 4;
 constexpr int kAttnStep = 32;                    // positions per MFMA step
-constexpr int kAttnSteps = 4;                    // steps per wave
-constexpr int kAttnChunk = kAttnWaves * kAttnSteps * kAttnStep;   // 512 positions per workgroup
+constexpr int kAttnSteps = 8;                    // steps per wave
+constexpr int kAttnChunk = kAttnWaves * kAttnSteps * kAttnStep;   // 1024 positions per workgroup
 constexpr int kAttnOPitch = kAttnD + 4;          // floats per LDS output row
 constexpr int kAttnQPitch = kAttnD + 8;          // bf16 per LDS query row
 
