@@ -170,8 +170,8 @@ def test_speckv_validation():
 def test_attention_validation():
     L = q.lib()
     need = q.qspec_attention_workspace_bytes(16, 5, 32, 8, 4096)
-    # chunk partials of 512 positions: (max, sum, 128 outputs) fp32 per (query row, chunk)
-    assert need >= 16 * 5 * 32 * 8 * (2 + 128) * 4
+    # chunk partials of 1024 positions: (max, sum, 128 outputs) fp32 per (query row, chunk)
+    assert need >= 16 * 5 * 32 * 4 * (2 + 128) * 4
     assert q.qspec_attention_workspace_bytes(0, 1, 1, 1, 8) == 0
     assert q.qspec_attention_workspace_bytes(1, 65, 1, 1, 8) == 0          # Q above the limit
     assert q.qspec_attention_workspace_bytes(1, 1, 6, 4, 8) == 0           # Hq not a multiple of Hkv
