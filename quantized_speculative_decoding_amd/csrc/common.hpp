@@ -38,6 +38,12 @@ __device__ __forceinline__ uint4 buf_load16_stream(rsrc_t r, uint32_t voff, uint
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+// 16 bytes per lane from a buffer straight into LDS (no registers): lane l's bytes land at
+// dst + 16 l, dst being wave-uniform.  Kept out of kernel bodies: a kernel whose own body casts to
+// the LDS address space gets no host-side launch stub.
+__device__ __forceinline__ void buf_load16_to_lds(rsrc_t r, unsigned char *dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
 
 // Nearest E4M3 code to a finite binary32 value, ties to even, saturating at +-448; the sign bit
 // is the value's.  Normal range: a * 2^(3 - e) lies in [8, 16) and rounds (exactly, nearest

@@ -579,6 +579,279 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Verify-tier kernel with direct-to-LDS activation staging, k_w4a16_mid<MT, U>, for the 64- and
+// 80-row tiers (4 and 5 row tiles).  The workgroup shape and the reduction order are the verify tier's (2 K parts x 4 column waves, 2 column tiles
+// per wave, the parts added in part order, K splits added by k_w4a16_splitk_reduce), but each
+// part's activation tile travels from memory straight into a U-deep LDS ring
+// (buffer_load ... lds: no registers, no LDS write instructions), and only the weights and their
+// meta words go through a U-deep register ring.  Step i waits for its own group (vmcnt counts the
+// loads of the U - 2 younger groups still in flight), crosses one barrier, refills the ring slot
+// freed by step i - 1 with group i + U - 1, then computes group i.
+// LDS activation layout, per (part, buffer): row-major, 256 bytes per row (128 k), the row's 16
+// chunks of 8 k stored at chunk position c ^ (row % 16).  A direct load writes 4 consecutive rows
+// (lane l: row 4 q + l / 16, position l % 16, so it loads chunk (l % 16) ^ (row % 16)).  The
+// weight packing gives lane group kq the 32 consecutive k of chunks 4 kq .. 4 kq + 3, one chunk
+// per 32-k step j, so the MFMA A fragment (row tile t, step j) of lane l = r + 16 kq reads row
+// 16 t + r, chunk 4 kq + j at position (4 kq + j) ^ r: each 16-lane phase of a ds_read_b128
+// covers the 64 banks once.
+// Each ring slot is an LDS variable of its own, holding both parts' tiles: the compiler tracks
+// direct loads per LDS variable, so a read of slot b waits only for the loads into slot b, where
+// a single array would make every LDS read wait for all direct loads in flight.  For the same
+// reason the step barrier carries no memory fence (a workgroup release fence waits for every
+// direct load in flight): each wave waits for its own loads into the slot, then the barrier.
+// The epilogue keeps part p's sums in slot p: 128 floats per row, column c of row r at
+// c ^ 16 ((r / 4) % 4), so the four row quads of an accumulator store hit distinct banks.
+template <int MT, int U, int B>
+__device__ __forceinline__ unsigned char *mid_slot_var() {
+    static_assert(MID_TILES * 16 * 4 <= 256 * MID_KP, "a part's sums fit one slot");
+    __shared__ __attribute__((aligned(16))) unsigned char slot[MID_KP * MT * 16 * 256];
+    return slot;
+}
+template <int MT, int U, int B = 0>
+__device__ __forceinline__ unsigned char *mid_slot(int b) {   // b: a compile-time value after unrolling
+    if constexpr (B + 1 >= U) return mid_slot_var<MT, U, B>();
+    else return b == B ? mid_slot_var<MT, U, B>() : mid_slot<MT, U, B + 1>(b);
+}
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int MT, int U>
+__global__ void __launch_bounds__(MID_KP * MID_CW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
+            const uint32_t *__restrict__ meta, int K, int N, void *__restrict__ y, int y_f32, int S,
+            float *__restrict__ partials) {
+    constexpr int NT = LDS_NT, CW = MID_CW, KP = MID_KP;
+    constexpr int THREADS = KP * CW * 64;
+    constexpr int TILES = CW * NT;
+    constexpr int ROWS = MT * 16;
+    constexpr int NLD = ROWS / 4 / CW;                     // direct loads per wave per group (4 rows each)
+    static_assert(ROWS % (4 * CW) == 0, "rows per staging wave");
+    constexpr int PBYTES = ROWS * 256;                     // one part's tile in a slot
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kh = wave / CW, cw = wave % CW;
+    const int col = lane & 15, kq = lane >> 4;
+    const int G = K / kGroup;
+    const int T = N / 16;
+    int cblk = blockIdx.x, split = 0;
+    if (S > 1) {
+        const int t = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+        const int cbs = (int)gridDim.x / S;
+        cblk = t % cbs;
+        split = t / cbs;
+    }
+    const int gs0 = (split * G) / S;
+    const int n = ((split + 1) * G) / S - gs0;
+    const int hstart = gs0 + (kh * n) / KP;
+    const int nh = ((kh + 1) * n) / KP - (kh * n) / KP;    // groups of this part
+    const int nsteps = (n + KP - 1) / KP;                  // all parts step together
+    const int hlast = max(nh, 1) - 1;
+    const int tile0 = cblk * TILES + cw * NT;
+
+    rsrc_t wr[NT], mr[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int t = min(tile0 + nt, T - 1);
+        wr[nt] = make_rsrc(codes + (size_t)t * G * 1024, (uint32_t)G * 1024);
+        mr[nt] = make_rsrc(meta + (size_t)t * G * 16, (uint32_t)G * 64);
+    }
+    const rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
+    // direct-load lane offsets: load u of this wave covers rows 4 (cw NLD + u) .. + 3 of the part's
+    // tile; rows past M read row M - 1 (their MFMA rows are discarded)
+    uint32_t xoff[NLD];
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+        const int row = 4 * (cw * NLD + u) + (lane >> 4);
+        const int chunk = (lane & 15) ^ (row & 15);
+        xoff[u] = (uint32_t)(min(row, M - 1) * K + chunk * 8) * 2;
+    }
+
+    struct Stage {
+        uint4 w[NT];
+        uint32_t m[NT];
+    };
+    // Group i of the part into ring slot b = i % U: the weights into registers, the activation
+    // tile into LDS slot b.  Past the end the first group is re-read (long since arrived).
+    auto load = [&](Stage &st, int i, int b) {
+        const uint32_t g = (uint32_t)(hstart + (i <= hlast ? i : 0));
+        unsigned char *dst = mid_slot<MT, U>(b) + kh * PBYTES;
+#pragma unroll
+        for (int u = 0; u < NLD; ++u)
+            buf_load16_to_lds(xr, dst + (cw * NLD + u) * 1024, xoff[u], g * 256);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            st.w[nt] = buf_load16_stream(wr[nt], lane * 16, g * 1024);
+            st.m[nt] = buf_load4(mr[nt], col * 4, g * 64);
+        }
+    };
+
+    f32x4_t acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // dequantization one 32-k step ahead of the MFMAs (as the verify tier of k_w4a16_lds)
+    auto dq_step = [&](const Stage &st, const DqConst (&dq)[NT], int j, bf16x8_t (&bq)[NT]) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const uint32_t word = j == 0 ? st.w[nt].x : j == 1 ? st.w[nt].y : j == 2 ? st.w[nt].z : st.w[nt].w;
+            uint32_t b[4];
+            dequant8(word, dq[nt], b);
+            bq[nt] = as_bf16x8(b[0], b[1], b[2], b[3]);
+        }
+    };
+    auto make_dqs = [&](const Stage &st, DqConst (&dq)[NT]) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) dq[nt] = make_dq(st.m[nt]);
+    };
+    bf16x8_t bq[NT];
+    DqConst dc[NT];
+    auto compute = [&](const Stage &st, const Stage &next, int b) {
+        const unsigned char *a = mid_slot<MT, U>(b) + kh * PBYTES;
+        DqConst dq[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) dq[nt] = dc[nt];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x8_t av[MT], bv[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) bv[nt] = bq[nt];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                av[mt] = *(const bf16x8_t *)(a + (16 * mt + col) * 256 + (((4 * kq + j) ^ col) * 16));
+            if (j < 3) {
+                dq_step(st, dq, j + 1, bq);
+            } else {
+                make_dqs(next, dc);
+                dq_step(next, dc, 0, bq);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+        }
+    };
+
+    // One load per group and wave: NLD direct loads + NT weight and NT meta loads, all counted by
+    // vmcnt in issue order.  At step i the U - 2 younger groups' loads may stay in flight.
+    constexpr int PER = NLD + 2 * NT;
+    Stage st[U];
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u) {
+        load(st[u], u, u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Wait until group i's loads (its activation tile in particular, whose arrival the barrier
+    // must cover for every wave) have landed, leaving `younger` groups' loads in flight.  The
+    // prologue issues groups 0 .. U - 2 and every step of the steady loop one more group, past the
+    // end too (re-reading the first group: a fixed count of loads in flight, and no predicated
+    // load for the compiler's own wait counting to merge); the tail issues only groups that exist.
+    static_assert(PER * (U - 2) < 64, "vmcnt range");
+    auto wait_younger = [&](int younger) {
+        switch (younger) {
+#define QSPEC_WAIT_CASE(k) \
+    case k: if constexpr (k <= U - 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER * k) : "memory"); break;
+            QSPEC_WAIT_CASE(0) QSPEC_WAIT_CASE(1) QSPEC_WAIT_CASE(2) QSPEC_WAIT_CASE(3)
+            QSPEC_WAIT_CASE(4) QSPEC_WAIT_CASE(5) QSPEC_WAIT_CASE(6)
+#undef QSPEC_WAIT_CASE
+            default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        }
+    };
+    static_assert(U - 2 <= 6, "wait cases");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER * (U - 2)) : "memory");
+    make_dqs(st[0], dc);
+    dq_step(st[0], dc, 0, bq);
+    barrier_no_fence();
+    // Step i uses ring slot i % U, a compile-time index once the loops below are unrolled by U.
+    // Slot (i + U - 1) % U held group i - 1; its LDS buffer was last read at step i - 1, which
+    // every wave finished before this step's barrier.  The steady loop never runs the last step,
+    // so every part computes in it.
+    const int nfull = ((nsteps - 1) / U) * U;
+    for (int base = 0; base < nfull; base += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u;
+            if (u > 0 || base > 0) {
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER * (U - 2)) : "memory");
+                barrier_no_fence();
+            }
+            load(st[(u + U - 1) % U], i + U - 1, (u + U - 1) % U);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st[u], st[(u + 1) % U], u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = nfull + u;
+        if (i < nsteps) {                                  // uniform over the workgroup
+            if (i > 0) {
+                wait_younger(max(nfull + U - 2, min(i + U - 2, nsteps - 1)) - i);
+                barrier_no_fence();
+            }
+            if (i + U - 1 < nsteps) load(st[(u + U - 1) % U], i + U - 1, (u + U - 1) % U);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < nh) compute(st[u], st[(u + 1) % U], u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");         // no direct load may land on the epilogue
+    __syncthreads();
+
+    // Epilogue (the sums of K part p in slot p): every wave writes its sums, one barrier, and all
+    // waves add the parts in part order and store 16-byte pieces.
+    constexpr int WCOLS = TILES * 16;
+    static_assert(WCOLS == 128, "epilogue row pitch");
+    auto red_at = [](int m, int c) { return m * WCOLS + (c ^ (16 * ((m >> 2) & 3))); };
+    {
+        float *red = (float *)mid_slot<MT, U>(kh);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    red[red_at(16 * mt + 4 * kq + r, cw * NT * 16 + 16 * nt + col)] = acc[mt][nt][r];
+    }
+    __syncthreads();
+    const int n0 = cblk * TILES * 16;
+    const int ncols = min(WCOLS, N - n0);
+    const int Mb = min(ROWS, M);
+    auto part_sum4 = [&](int m, int c) {             // c: a multiple of 4 (the swizzle keeps the 4)
+        float4 v = *(const float4 *)((const float *)mid_slot<MT, U>(0) + red_at(m, c));
+#pragma unroll
+        for (int p = 1; p < KP; ++p) {
+            const float4 w = *(const float4 *)((const float *)mid_slot<MT, U>(p) + red_at(m, c));
+            v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+        }
+        return v;
+    };
+    float *dstf = S > 1 ? partials + (size_t)split * M * N : (float *)y;
+    uint16_t *dsth = (uint16_t *)y;
+    if (S > 1 || y_f32) {
+        for (int e = tid; e < Mb * (WCOLS / 4); e += THREADS) {
+            const int m = e / (WCOLS / 4), c = (e % (WCOLS / 4)) * 4;
+            if (c < ncols) *(float4 *)(dstf + (size_t)m * N + n0 + c) = part_sum4(m, c);
+        }
+    } else {
+        for (int e = tid; e < Mb * (WCOLS / 8); e += THREADS) {
+            const int m = e / (WCOLS / 8), c = (e % (WCOLS / 8)) * 8;
+            if (c < ncols) {
+                const float4 lo = part_sum4(m, c), hi = part_sum4(m, c + 4);
+                uint4 o;
+                o.x = pack_bf16x2(lo.x, lo.y);
+                o.y = pack_bf16x2(lo.z, lo.w);
+                o.z = pack_bf16x2(hi.x, hi.y);
+                o.w = pack_bf16x2(hi.z, hi.w);
+                *(uint4 *)(dsth + (size_t)m * N + n0 + c) = o;
+            }
+        }
+    }
+}
+
 // y = sum of the S <= kMaxSplits fp32 partials in split order (4 outputs per thread; M * N is a
 // multiple of 16).  All S loads are issued before the first add.  A second kernel rather than a
 // last-arriving workgroup: the device-scope fence that hand-off needs writes back the XCD's L2,
@@ -708,15 +981,22 @@ void launch_splitk_reduce(const float *partials, int S, int M, int N, void *y, i
     hipLaunchKernelGGL(k_w4a16_splitk_reduce, dim3(blocks), dim3(256), 0, st, partials, S, MN, y, y_f32);
 }
 
-template <int MT, int U>
+// DIRECT: k_w4a16_mid (activations straight into an LDS ring) instead of k_w4a16_lds (through
+// registers).  Both reduce every output in the same order, so the rows of the verify tier are
+// bitwise the same whichever kernel a batch size takes.
+template <int MT, int U, bool DIRECT>
 static hipError_t launch_mid(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K, int N,
                              void *y, int y_f32, void *ws, hipStream_t st) {
     const int S = mid_splits(K, N);
     const int cbs = (N / 16 + MID_TILES - 1) / MID_TILES;
     float *partials = S > 1 ? (float *)ws : nullptr;
     // one 1-D grid of cbs x S workgroups, remapped split-major inside the kernel (S > 1)
-    hipLaunchKernelGGL((k_w4a16_lds<MT, U, MID_KP, MID_CW>), dim3(cbs * S), dim3(MID_KP * MID_CW * 64), 0, st, x,
-                       M, codes, meta, K, N, y, y_f32, S, partials, 1);
+    if constexpr (DIRECT)
+        hipLaunchKernelGGL((k_w4a16_mid<MT, U>), dim3(cbs * S), dim3(MID_KP * MID_CW * 64), 0, st, x, M, codes,
+                           meta, K, N, y, y_f32, S, partials);
+    else
+        hipLaunchKernelGGL((k_w4a16_lds<MT, U, MID_KP, MID_CW>), dim3(cbs * S), dim3(MID_KP * MID_CW * 64), 0, st,
+                           x, M, codes, meta, K, N, y, y_f32, S, partials, 1);
     if (S > 1) launch_splitk_reduce(partials, S, M, N, y, y_f32, st);
     return hipGetLastError();
 }
@@ -739,11 +1019,13 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, con
         if (nt == 2) return launch_decode<2, 4, 2>(x, M, codes, meta, K, N, y, y_f32, st);
         return launch_decode<1, 3, 2>(x, M, codes, meta, K, N, y, y_f32, st);
     }
-    if (M <= 16) return launch_mid<1, 6>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    if (M <= 32) return launch_mid<2, 6>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    if (M <= 48) return launch_mid<3, 5>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    if (M <= 64) return launch_mid<4, 4>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    if (M <= 80) return launch_mid<5, 4>(x, M, codes, meta, K, N, y, y_f32, ws, st);
+    // the direct-to-LDS kernel from 49 rows: 2 - 8% faster at 64 and 80 rows on the Llama-3-8B
+    // projections, even or slower below (down at 20 rows: 17.7 against 16.6 us)
+    if (M <= 16) return launch_mid<1, 6, false>(x, M, codes, meta, K, N, y, y_f32, ws, st);
+    if (M <= 32) return launch_mid<2, 6, false>(x, M, codes, meta, K, N, y, y_f32, ws, st);
+    if (M <= 48) return launch_mid<3, 5, false>(x, M, codes, meta, K, N, y, y_f32, ws, st);
+    if (M <= 64) return launch_mid<4, 4, true>(x, M, codes, meta, K, N, y, y_f32, ws, st);
+    if (M <= 80) return launch_mid<5, 4, true>(x, M, codes, meta, K, N, y, y_f32, ws, st);
     // M > 80: 128-row blocks x 256 columns, K splits for shapes with few column blocks, one
     // XCD-remapped 1-D grid (a 2-D (column block, split) grid for a single row block)
     const int rbs = (M + BIG_MT * 16 - 1) / (BIG_MT * 16);

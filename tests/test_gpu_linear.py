@@ -146,13 +146,14 @@ def test_w4a16_one_hot_rows_reproduce_dequantized_weights_exactly(M):
 @pytest.mark.parametrize("K,N", [(1024, 208), (1024, 16 * 300), (256, 16 * 4100), (12288, 256)])
 def test_w4a16_rows_do_not_depend_on_batch(K, N):
     """Every M in one batch tier (as qspec_gemm_w4a16_tier reports it: decode up to 32, 16, 24 or 8
-    rows for these four shapes) reduces a row in the same order: bitwise-equal rows.  Across
-    tiers the rows agree to fp32 rounding."""
+    rows for these four shapes) reduces a row in the same order: bitwise-equal rows, also where
+    the verify tier switches from register to direct-to-LDS activation staging (48 -> 49 rows).
+    Across tiers the rows agree to fp32 rounding."""
     note(f"gemm_w4a16 batch invariance K={K} N={N}")
     w = si.weights(K, N, seed=4)
     wdev = weights_dev(w)
     x = si.activations(96, K, seed=4)
-    Ms = (1, 5, 8, 9, 12, 16, 17, 20, 24, 25, 32, 33, 48, 80, 81, 96)
+    Ms = (1, 5, 8, 9, 12, 16, 17, 20, 24, 25, 32, 33, 48, 49, 64, 65, 80, 81, 96)
     full = {M: run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy() for M in Ms}
     tiers = {}
     for M in Ms:
