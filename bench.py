@@ -1066,7 +1066,7 @@ def main():
         bytes_per_launch = R.verify_gemm_bytes() / nl
         n_launch = nl
         avg_launch_ms = verify_ms / n_launch
-        kernel = "k_w4a16_lds"           # plus k_w4a16_splitk_reduce on split-K shapes
+        kernel = "k_w4a16_mid"           # plus k_w4a16_splitk_reduce on split-K shapes
     achieved = bytes_per_launch / (avg_launch_ms / 1e3) / 1e9
     tb = traffic_for(kernel)
     traffic = None if tb is None else round(tb)

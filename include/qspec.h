@@ -146,13 +146,15 @@ int qspec_gemm_w4a4_tier(int32_t M, int32_t K, int32_t N, int32_t *m_first, int3
  * qspec_gemm_w4a16_tier -- the batch tier of M for (K, N) in qspec_gemm_w4a16, as
  * qspec_gemm_w4a4_tier reports it for the W4A4 layer.  The tiers are
  *   0: [1, D]       the decode kernel (one 16-row tile up to 16 rows, two above);
- *   1: [D + 1, 80]  the shared-activation kernel with two K parts (and K splits);
- *   2: [81, INT32_MAX] the shared-activation kernel over 128-row blocks;
+ *   1: [D + 1, V]   the verify kernel: two K parts (and K splits), ceil(M / 80) row blocks;
+ *   2: [V + 1, INT32_MAX] the shared-activation kernel over 128-row blocks;
  * with D = 24 when N >= 65536 (vocabulary-sized heads: four column tiles per workgroup),
  * D = 32 when the decode grid has at most 256 workgroups and K * N <= 4096 * 6144 (small
  * projections), D = 8 when N < 6144 and K >= 12288 (long K over one-tile workgroups), and
  * D = 16 otherwise.  The decode grid has N / 16 workgroups for N < 6144, ceil(N / 32) for
- * 6144 <= N < 65536.  Host-only: launches nothing.
+ * 6144 <= N < 65536.  With P = ceil(N / 256) * S2, the tier-2 workgroups per 128-row block (S2:
+ * its K split count below), V = 384 for P <= 32, 256 for P <= 64, 160 for P <= 128 and 80
+ * above.  Host-only: launches nothing.
  * Errors (negative status): NULL pointer; the size errors of qspec_gemm_w4a16.
  */
 int qspec_gemm_w4a16_tier(int32_t M, int32_t K, int32_t N, int32_t *m_first, int32_t *m_last);
@@ -160,10 +162,12 @@ int qspec_gemm_w4a16_tier(int32_t M, int32_t K, int32_t N, int32_t *m_first, int
 /*
  * qspec_gemm_w4a16_workspace_bytes -- device workspace qspec_gemm_w4a16 needs for (M, K, N); 0
  * when the shape needs none (M in tier 0 of qspec_gemm_w4a16_tier, or a shape whose K is not
- * split) or on invalid sizes.  K is split for tier-1 shapes (up to M = 80) with fewer than 192
- * blocks of 128 columns and for tier-2 shapes (M > 80) with fewer than 64 blocks of 256 columns
- * and at least 64 groups; the split count S depends on (K, N) and the tier only, and the size is
- * S * M * N * 4 bytes.
+ * split) or on invalid sizes.  K is split for tier-1 shapes with fewer than 192 blocks of 128
+ * columns (S1 = max(1, min(256 / blocks, 16, K / 640)) splits, integer quotients) and for
+ * tier-2 shapes with fewer than 64
+ * blocks of 256 columns and at least 64 groups (S2, the largest power of two up to 8 with
+ * S2 * blocks <= 128 and at least 32 groups per split); the split count depends on (K, N) and
+ * the tier only, and the size is S * M * N * 4 bytes.
  */
 size_t qspec_gemm_w4a16_workspace_bytes(int32_t M, int32_t K, int32_t N);
 

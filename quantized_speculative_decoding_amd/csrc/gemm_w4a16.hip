@@ -9,13 +9,15 @@
 // exactly the 32 codes its v_mfma_f32_16x16x32_bf16 B fragments need.  Every wave-wide weight
 // load is one contiguous kilobyte.
 //
-// Two kernels share the dequantization routine:
+// Three kernels share the dequantization routine:
 //  * k_w4a16_decode (M <= 16, and M <= 24 or 32 for the (K, N) where that measured faster):
 //    HBM-bound decode / short-verify shapes; NT column tiles and one or two row tiles per
 //    workgroup, K groups split between its waves, activations in registers.
-//  * k_w4a16_lds (up to M = 80, and M > 80): the activation tile of each group is staged once in
-//    LDS and shared by the workgroup's waves; the verify tier splits K between two wave groups
-//    (and across workgroups with an ordered reduction), the large tier covers 128-row blocks.
+//  * k_w4a16_mid (the verify tier, from there up to 80 rows and, where the large tier would not
+//    fill the chip, up to 384 in row blocks of at most 80): each group's activation tile goes
+//    straight from memory into LDS and is shared by the workgroup's waves; K is split between two
+//    wave groups (and across workgroups with an ordered reduction).
+//  * k_w4a16_lds (the large tier): 128-row blocks, activations staged through registers into LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -231,83 +233,66 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
-// Shared-activation kernel k_w4a16_lds: the verify tier (above the decode tier, up to M = 80) and
-// the large-batch tier (M > 80).  At these M a group's activation tile (M x 128 bf16: 20 KB at M = 80, 32 KB for a
-// 128-row block) is as large as 20 - 32 weight blocks, so it is staged once in LDS and shared by
-// the workgroup's waves, while every weight block is dequantized exactly once, in registers, by
-// the wave whose MFMA B operand it is.
-//
-// A workgroup = KP K parts x CW column waves; each wave owns LDS_NT = 2 column tiles, so the
-// workgroup covers 16 * 2 * CW columns of one K split and one block of up to 16 MT rows.
-//  * verify tier: KP = 2, CW = 4 (8 waves, 128 columns, all M rows), two waves per SIMD (a single
-//    wave per SIMD issues MFMA and VALU work at about half the rate two waves reach);
-//  * large tier: KP = 1, CW = 8 (8 waves, 256 columns, 128-row blocks).
-// Per group, the CW waves of a K part stage the part's activation tile into LDS in fragment-major
-// order (fragment f = (row tile, 32-k step), lane l's 16 bytes in f's 1 KB block, XOR-swizzled:
+// Shared-activation kernels: the verify tier (k_w4a16_mid, further below) and the large tier
+// (k_w4a16_lds).  At these M a group's activation tile (M x 128 bf16: 20 KB for 80 rows, 32 KB
+// for a 128-row block) is as large as 20 - 32 weight blocks, so it is staged once in LDS and
+// shared by the workgroup's waves, while every weight block is dequantized exactly once, in
+// registers, by the wave whose MFMA B operand it is.  Each wave owns LDS_NT = 2 column tiles.
+//  * verify tier: 2 K parts x 4 column waves (8 waves, 128 columns, up to 80 rows), two waves per
+//    SIMD (a single wave per SIMD issues MFMA and VALU work at about half the rate two reach);
+//  * large tier: 8 column waves (256 columns, 128-row blocks).
+// k_w4a16_lds: per group, the waves stage the activation tile into LDS in fragment-major order
+// (fragment f = (row tile, 32-k step), lane l's 16 bytes in f's 1 KB block, XOR-swizzled:
 // conflict-free 128-bit writes and reads) and every wave reads all fragments from there, each
 // feeding LDS_NT MFMAs.  Activations and weights travel through one U-deep register ring in group
 // order (the in-order vmcnt wait for a stage never covers a younger one); a stage's activations
 // are written to LDS one step before they are consumed, its weights are dequantized in registers
-// when consumed.  One barrier per step.  The K parts are added in LDS in part order.  With S > 1 K
-// splits (a function of (K, N) only), each workgroup writes an fp32 partial tile and
-// k_w4a16_splitk_reduce adds the S partials in split order, so every output has one fixed
-// reduction order per (K, N) in each tier.
+// when consumed.  One barrier per step.  With S > 1 K splits (a function of (K, N) only), each
+// workgroup writes an fp32 partial tile and k_w4a16_splitk_reduce adds the S partials in split
+// order, so every output has one fixed reduction order per (K, N) in each tier.
 constexpr int LDS_NT = 2;                    // column tiles per wave
 constexpr int MID_KP = 2, MID_CW = 4;        // verify tier
 constexpr int MID_TILES = MID_CW * LDS_NT;   // column tiles per verify-tier workgroup
 constexpr int BIG_MT = 8, BIG_CW = 8;        // large tier: 128-row blocks, 256 columns
 constexpr int BIG_TILES = BIG_CW * LDS_NT;
 
-template <int MT, int U, int KP, int CW>
-__global__ void __launch_bounds__(KP * CW * 64)
+template <int MT, int U, int CW>
+__global__ void __launch_bounds__(CW * 64)
 k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
             const uint32_t *__restrict__ meta, int K, int N, void *__restrict__ y, int y_f32, int S,
             float *__restrict__ partials, int row_blocks) {
     constexpr int NT = LDS_NT;
-    constexpr int THREADS = KP * CW * 64;
+    constexpr int THREADS = CW * 64;
     constexpr int TILES = CW * NT;          // column tiles per workgroup
     constexpr int NF = MT * 4;              // activation fragments per group
-    constexpr int NFW = NF / CW;            // staged by each wave of a K part
+    constexpr int NFW = NF / CW;            // staged by each wave
     static_assert(NF % CW == 0, "activation fragments per wave");
-    // LDS: the staging buffers [K part][buffer][fragment][lane]; the epilogue reuses them (and,
-    // with K parts, needs a little more: every part's sums, row-major with a padded pitch).
-    constexpr int STAGE_U4 = KP * 2 * NF * 64;
-    constexpr int EPITCH = TILES * 16 + 4;          // floats per output row, K-part epilogue
-    constexpr int EPI_U4 = KP > 1 ? (KP * MT * 16 * EPITCH + 3) / 4 : 0;
-    __shared__ uint4 lds[STAGE_U4 > EPI_U4 ? STAGE_U4 : EPI_U4];
-    auto abuf = [&](int part, int buf) -> uint4 * { return lds + (part * 2 + buf) * NF * 64; };
+    // LDS: two staging buffers [buffer][fragment][lane]; the epilogue reuses them
+    constexpr int STAGE_U4 = 2 * NF * 64;
+    __shared__ uint4 lds[STAGE_U4];
+    auto abuf = [&](int buf) -> uint4 * { return lds + buf * NF * 64; };
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-    const int kh = wave / CW, cw = wave % CW;
+    const int cw = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform (SGPR)
     const int col = lane & 15, kq = lane >> 4;
     const int G = K / kGroup;
     const int T = N / 16;
-    // Workgroup -> (column block, split, row block).  A 1-D grid is remapped so that each XCD owns
-    // a contiguous range of logical tiles.  Large tier (row_blocks > 1): row blocks fastest, then
-    // splits, so the workgroups that share a column block's weights run together on one XCD and its
-    // L2.  Verify tier (one row block): column blocks fastest, then splits, so the workgroups of one
-    // split, which read the same activation slice, share one or two XCDs.
+    // Workgroup -> (column block, split, row block).  Several row blocks: a 1-D grid remapped so
+    // that each XCD owns a contiguous range of logical tiles, row blocks fastest, then splits, so
+    // the workgroups that share a column block's weights run together on one XCD and its L2.  One
+    // row block: a 2-D (column block, split) grid.
     int cblk = blockIdx.x, split = blockIdx.y, rblk = 0;
     if (gridDim.y == 1 && row_blocks > 1) {
         const int t = xcd_remap((int)blockIdx.x, (int)gridDim.x);
         rblk = t % row_blocks;
         split = (t / row_blocks) % S;
         cblk = t / row_blocks / S;
-    } else if (gridDim.y == 1 && S > 1) {
-        const int t = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-        const int cbs = (int)gridDim.x / S;
-        cblk = t % cbs;
-        split = t / cbs;
     }
     const int m0 = rblk * MT * 16;           // this workgroup's row block
     const int Mb = min(MT * 16, M - m0);
-    const int gs0 = (split * G) / S;
-    const int n = ((split + 1) * G) / S - gs0;
-    const int hstart = gs0 + (kh * n) / KP;
-    const int nh = ((kh + 1) * n) / KP - (kh * n) / KP;   // groups of this part
-    const int nsteps = (n + KP - 1) / KP;                 // all parts step together
-    const int hlast = max(nh, 1) - 1;
+    const int hstart = (split * G) / S;
+    const int nsteps = ((split + 1) * G) / S - hstart;    // groups of this split
+    const int hlast = nsteps - 1;
     const int tile0 = cblk * TILES + cw * NT;
 
     // Buffer resources per column tile (SGPRs) plus one 32-bit lane offset per stream; the
@@ -320,7 +305,7 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         mr[nt] = make_rsrc(meta + (size_t)t * G * 16, (uint32_t)G * 64);
     }
     const rsrc_t xr = make_rsrc(x + (size_t)m0 * K, (uint32_t)Mb * K * 2);
-    // Activation staging: load q = cw * NFW + u of a K part reads rows 4 q .. 4 q + 3 of the
+    // Activation staging: load q = cw * NFW + u reads rows 4 q .. 4 q + 3 of the
     // group, 16 lanes per row (row-contiguous: 8 cache lines per load).  The 16 bytes of (row, 8-k
     // chunk c) are element (row % 16, k = 8 c) of fragment f = 4 (row / 16) + c % 4, i.e. lane
     // l = row % 16 + 16 (c / 4) of it; they are stored at slot l ^ (c / 4) ^ 4 (c % 4) of the
@@ -347,7 +332,7 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         uint32_t m[NT];
         uint4 a[NFW];
     };
-    // Group i of the part; a refill past the end re-reads the first group (long since arrived)
+    // Group i of the split; a refill past the end re-reads the first group (long since arrived)
     // rather than a group whose load may still be in flight.
     auto load = [&](Stage &st, int i) {
         const uint32_t g = (uint32_t)(hstart + (i <= hlast ? i : 0));
@@ -361,7 +346,7 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     };
     auto stage_act = [&](const Stage &st, int buf) {
 #pragma unroll
-        for (int u = 0; u < NFW; ++u) abuf(kh, buf)[xslot[u]] = st.a[u];
+        for (int u = 0; u < NFW; ++u) abuf(buf)[xslot[u]] = st.a[u];
     };
 
     f32x4_t acc[MT][NT];
@@ -370,74 +355,28 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Verify tier (PIPE): dequantization runs one 32-k step ahead of the MFMAs that consume it, so
-    // a wave's VALU and MFMA work are independent and overlap: while the MFMAs of step j run, the
-    // VALU dequantizes step j + 1, and during the group's last step it dequantizes step 0 of the
-    // next group (whose weights have arrived by then: that stage's activations are staged at the
-    // end of this step).  bq / dc carry the next step's operand and the next group's constants
-    // between calls.  The large tier, with 8 row tiles of accumulators, has no registers for the
-    // carried operands and dequantizes each step right before its MFMAs.
-    constexpr bool PIPE = KP > 1;
-    auto dq_step = [&](const Stage &st, const DqConst (&dq)[NT], int j, bf16x8_t (&bq)[NT]) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const uint32_t word = j == 0 ? st.w[nt].x : j == 1 ? st.w[nt].y : j == 2 ? st.w[nt].z : st.w[nt].w;
-            uint32_t b[4];
-            dequant8(word, dq[nt], b);
-            bq[nt] = as_bf16x8(b[0], b[1], b[2], b[3]);
-        }
-    };
-    auto make_dqs = [&](const Stage &st, DqConst (&dq)[NT]) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) dq[nt] = make_dq(st.m[nt]);
-    };
-    bf16x8_t bq[NT];
-    DqConst dc[NT];
-    auto compute = [&](const Stage &st, const Stage &next, int buf) {
-        if constexpr (!PIPE) {
-            DqConst dq[NT];
-            make_dqs(st, dq);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bf16x8_t av[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    av[mt] = __builtin_bit_cast(bf16x8_t, abuf(kh, buf)[(mt * 4 + j) * 64 + (rslot ^ (4 * j))]);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const uint32_t word = j == 0 ? st.w[nt].x : j == 1 ? st.w[nt].y : j == 2 ? st.w[nt].z : st.w[nt].w;
-                    uint32_t b[4];
-                    dequant8(word, dq[nt], b);
-                    const bf16x8_t bv = as_bf16x8(b[0], b[1], b[2], b[3]);
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, acc[mt][nt], 0, 0, 0);
-                }
-            }
-            return;
-        }
+    // Each 32-k step is dequantized right before its MFMAs (8 row tiles of accumulators leave no
+    // registers for carrying the next step's operand).
+    auto compute = [&](const Stage &st, int buf) {
         DqConst dq[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) dq[nt] = dc[nt];
+        for (int nt = 0; nt < NT; ++nt) dq[nt] = make_dq(st.m[nt]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            bf16x8_t av[MT], bv[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) bv[nt] = bq[nt];
+            bf16x8_t av[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                av[mt] = __builtin_bit_cast(bf16x8_t, abuf(kh, buf)[(mt * 4 + j) * 64 + (rslot ^ (4 * j))]);
-            if (j < 3) {
-                dq_step(st, dq, j + 1, bq);
-            } else {
-                make_dqs(next, dc);
-                dq_step(next, dc, 0, bq);
-            }
+                av[mt] = __builtin_bit_cast(bf16x8_t, abuf(buf)[(mt * 4 + j) * 64 + (rslot ^ (4 * j))]);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt) {
+                const uint32_t word = j == 0 ? st.w[nt].x : j == 1 ? st.w[nt].y : j == 2 ? st.w[nt].z : st.w[nt].w;
+                uint32_t b[4];
+                dequant8(word, dq[nt], b);
+                const bf16x8_t bv = as_bf16x8(b[0], b[1], b[2], b[3]);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, acc[mt][nt], 0, 0, 0);
+            }
         }
     };
 
@@ -454,10 +393,6 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         __builtin_amdgcn_sched_barrier(0);
     }
     stage_act(st[0], 0);
-    if constexpr (PIPE) {
-        make_dqs(st[0], dc);
-        dq_step(st[0], dc, 0, bq);
-    }
     __syncthreads();
     const int nfull = ((nsteps - 1) / U) * U;
     for (int base = 0; base < nfull; base += U) {
@@ -465,7 +400,7 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         for (int u = 0; u < U; ++u) {
             const int i = base + u;
             load(st[(u + U - 1) % U], i + U - 1);
-            compute(st[u], st[(u + 1) % U], i & 1);
+            compute(st[u], i & 1);
             __builtin_amdgcn_sched_barrier(0);
             stage_act(st[(u + 1) % U], (i + 1) & 1);
             __syncthreads();
@@ -476,7 +411,7 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         const int i = nfull + u;
         if (i < nsteps) {                        // uniform over the workgroup
             if (i + U - 1 < nsteps) load(st[(u + U - 1) % U], i + U - 1);
-            if (i < nh) compute(st[u], st[(u + 1) % U], i & 1);   // a part may have one group less
+            compute(st[u], i & 1);
             if (i + 1 < nsteps) {
                 stage_act(st[(u + 1) % U], (i + 1) & 1);
                 __syncthreads();
@@ -485,57 +420,12 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     }
     __syncthreads();   // every wave is done reading the staging buffers
 
-    // Epilogue.  With K parts, every wave writes its sums row-major into its part's LDS region,
-    // one barrier, and all waves add the parts in part order and store 16-byte pieces: bfloat16 /
-    // f32 output, or the fp32 partial of this split.  Without K parts (the large tier, whose 128 x
-    // 256 block of sums exceeds the staging buffers), part 0 writes rounds of 64 columns (two
-    // column waves) and all waves store them.
+    // Epilogue: the 128 x 256 block of sums exceeds the staging buffers, so the waves write rounds
+    // of 64 columns (two column waves) to LDS and all waves store them: bfloat16 / f32 output, or
+    // the fp32 partial of this split.
     float *dstf = S > 1 ? partials + (size_t)split * M * N + (size_t)m0 * N : (float *)y + (size_t)m0 * N;
     uint16_t *dsth = (uint16_t *)y + (size_t)m0 * N;
     float *red = (float *)lds;
-    if constexpr (KP > 1) {
-        constexpr int WCOLS = TILES * 16;            // columns of this workgroup
-        constexpr int PART = MT * 16 * EPITCH;       // floats per part region
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    red[kh * PART + (16 * mt + 4 * kq + r) * EPITCH + cw * NT * 16 + 16 * nt + col] = acc[mt][nt][r];
-        __syncthreads();
-        const int n0 = cblk * TILES * 16;
-        const int ncols = min(WCOLS, N - n0);       // a multiple of 16
-        auto part_sum4 = [&](int m, int c) {
-            float4 v = *(const float4 *)(red + m * EPITCH + c);
-#pragma unroll
-            for (int p = 1; p < KP; ++p) {
-                const float4 w = *(const float4 *)(red + p * PART + m * EPITCH + c);
-                v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
-            }
-            return v;
-        };
-        if (S > 1 || y_f32) {
-            for (int e = tid; e < Mb * (WCOLS / 4); e += THREADS) {     // 4 floats per thread
-                const int m = e / (WCOLS / 4), c = (e % (WCOLS / 4)) * 4;
-                if (c < ncols) *(float4 *)(dstf + (size_t)m * N + n0 + c) = part_sum4(m, c);
-            }
-        } else {
-            for (int e = tid; e < Mb * (WCOLS / 8); e += THREADS) {     // 8 outputs per thread
-                const int m = e / (WCOLS / 8), c = (e % (WCOLS / 8)) * 8;
-                if (c < ncols) {
-                    const float4 lo = part_sum4(m, c), hi = part_sum4(m, c + 4);
-                    uint4 o;
-                    o.x = pack_bf16x2(lo.x, lo.y);
-                    o.y = pack_bf16x2(lo.z, lo.w);
-                    o.z = pack_bf16x2(hi.x, hi.y);
-                    o.w = pack_bf16x2(hi.z, hi.w);
-                    *(uint4 *)(dsth + (size_t)m * N + n0 + c) = o;
-                }
-            }
-        }
-        return;
-    }
     constexpr int CHUNK = 64;                       // output columns per round
     constexpr int CHUNK_WAVES = CHUNK / (NT * 16);
     constexpr int OPITCH = CHUNK + 4;               // floats per output row in LDS
@@ -580,10 +470,11 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
 }
 
 // ---------------------------------------------------------------------------------------------
-// Verify-tier kernel with direct-to-LDS activation staging, k_w4a16_mid<MT, U>, for the 64- and
-// 80-row tiers (4 and 5 row tiles).  The workgroup shape and the reduction order are the verify tier's (2 K parts x 4 column waves, 2 column tiles
-// per wave, the parts added in part order, K splits added by k_w4a16_splitk_reduce), but each
-// part's activation tile travels from memory straight into a U-deep LDS ring
+// Verify-tier kernel k_w4a16_mid<MT, U>: a workgroup of 2 K parts x 4 column waves covers 128
+// columns of one K split and one block of up to 16 MT rows (row blocks of equal height in whole
+// row tiles, at most 80 rows each).  The parts are added in part order and the K splits by
+// k_w4a16_splitk_reduce, so a row's reduction order depends on (K, N) only, whatever the block.
+// Each part's activation tile travels from memory straight into a U-deep LDS ring
 // (buffer_load ... lds: no registers, no LDS write instructions), and only the weights and their
 // meta words go through a U-deep register ring.  Step i waits for its own group (vmcnt counts the
 // loads of the U - 2 younger groups still in flight), crosses one barrier, refills the ring slot
@@ -619,7 +510,7 @@ template <int MT, int U>
 __global__ void __launch_bounds__(MID_KP * MID_CW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
             const uint32_t *__restrict__ meta, int K, int N, void *__restrict__ y, int y_f32, int S,
-            float *__restrict__ partials) {
+            float *__restrict__ partials, int row_blocks) {
     constexpr int NT = LDS_NT, CW = MID_CW, KP = MID_KP;
     constexpr int THREADS = KP * CW * 64;
     constexpr int TILES = CW * NT;
@@ -634,13 +525,20 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     const int col = lane & 15, kq = lane >> 4;
     const int G = K / kGroup;
     const int T = N / 16;
-    int cblk = blockIdx.x, split = 0;
-    if (S > 1) {
-        const int t = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-        const int cbs = (int)gridDim.x / S;
+    // Workgroup -> (row block, column block, split), row blocks fastest, then column blocks: the
+    // workgroups that read one column block's weights share an XCD (and its L2), and those of one
+    // split, which read the same activation slice, share one or two.
+    int cblk = blockIdx.x, split = 0, rblk = 0;
+    if (S > 1 || row_blocks > 1) {
+        int t = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+        const int cbs = (int)gridDim.x / (S * row_blocks);
+        rblk = t % row_blocks;
+        t /= row_blocks;
         cblk = t % cbs;
         split = t / cbs;
     }
+    const int m0 = rblk * ROWS;                            // this workgroup's row block
+    const int Mb = min(ROWS, M - m0);
     const int gs0 = (split * G) / S;
     const int n = ((split + 1) * G) / S - gs0;
     const int hstart = gs0 + (kh * n) / KP;
@@ -656,15 +554,15 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         wr[nt] = make_rsrc(codes + (size_t)t * G * 1024, (uint32_t)G * 1024);
         mr[nt] = make_rsrc(meta + (size_t)t * G * 16, (uint32_t)G * 64);
     }
-    const rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
+    const rsrc_t xr = make_rsrc(x + (size_t)m0 * K, (uint32_t)((size_t)Mb * K * 2));
     // direct-load lane offsets: load u of this wave covers rows 4 (cw NLD + u) .. + 3 of the part's
-    // tile; rows past M read row M - 1 (their MFMA rows are discarded)
+    // tile; rows past the block read its last row (their MFMA rows are discarded)
     uint32_t xoff[NLD];
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
         const int row = 4 * (cw * NLD + u) + (lane >> 4);
         const int chunk = (lane & 15) ^ (row & 15);
-        xoff[u] = (uint32_t)(min(row, M - 1) * K + chunk * 8) * 2;
+        xoff[u] = (uint32_t)(min(row, Mb - 1) * K + chunk * 8) * 2;
     }
 
     struct Stage {
@@ -819,7 +717,6 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     __syncthreads();
     const int n0 = cblk * TILES * 16;
     const int ncols = min(WCOLS, N - n0);
-    const int Mb = min(ROWS, M);
     auto part_sum4 = [&](int m, int c) {             // c: a multiple of 4 (the swizzle keeps the 4)
         float4 v = *(const float4 *)((const float *)mid_slot<MT, U>(0) + red_at(m, c));
 #pragma unroll
@@ -829,8 +726,8 @@ k_w4a16_mid(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
         }
         return v;
     };
-    float *dstf = S > 1 ? partials + (size_t)split * M * N : (float *)y;
-    uint16_t *dsth = (uint16_t *)y;
+    float *dstf = S > 1 ? partials + (size_t)split * M * N + (size_t)m0 * N : (float *)y + (size_t)m0 * N;
+    uint16_t *dsth = (uint16_t *)y + (size_t)m0 * N;
     if (S > 1 || y_f32) {
         for (int e = tid; e < Mb * (WCOLS / 4); e += THREADS) {
             const int m = e / (WCOLS / 4), c = (e % (WCOLS / 4)) * 4;
@@ -949,9 +846,24 @@ static int big_splits(int K, int N) {
     return S;
 }
 
-// Batch tiers: [1, decode_max_m] (decode kernel, one or two row tiles), (decode_max_m, 80]
-// (shared-activation kernel with K parts), above 80 (shared-activation kernel, 128-row blocks).
-// Inside a tier the per-output reduction order depends on (K, N) only.
+// Largest batch of the verify tier for (K, N), a step function of P, the large tier's workgroups
+// per 128-row block: 384 rows for P <= 32, 256 for P <= 64, 160 for P <= 128, 80 above.  Past 80
+// rows the verify tier runs row blocks of at most 80 rows, each re-reading the weights, but fills
+// the chip where the large tier's few workgroups leave CUs idle.  From graph-timed sweeps of both
+// tiers at M = 96 - 512 (us, verify / large): Llama-3-8B down (P = 32) 40 / 100 at 128 and 87 / 107
+// at 384, o (16) 47 / 62 at 384, qkv (24) 62 / 62 at 384 and 79 / 64 at 512; Qwen2.5-7B down (56)
+// 71 / 77 at 256 and 95 / 82 at 384; Llama-3-8B gate+up (112) 58 / 68 at 160 and 75 / 69 at 192;
+// Llama-70B down (128) 102 / 117 at 160 and 132 / 120 at 192; Llama-70B gate+up (224) 154 / 126
+// at 96.
+static int mid_max_m(int K, int N) {
+    const int P = ((N / 16 + BIG_TILES - 1) / BIG_TILES) * big_splits(K, N);
+    return P <= 32 ? 384 : P <= 64 ? 256 : P <= 128 ? 160 : 80;
+}
+
+// Batch tiers: [1, decode_max_m] (decode kernel, one or two row tiles), (decode_max_m,
+// mid_max_m] (verify tier: direct-to-LDS kernel with K parts, row blocks of at most 80 rows),
+// above (large tier: shared-activation kernel, 128-row blocks).  Inside a tier the per-output
+// reduction order depends on (K, N) only.
 int gemm_w4a16_tier(int M, int K, int N, int *m_first, int *m_last) {
     const int dm = decode_max_m(K, N);
     if (M <= dm) {
@@ -959,19 +871,20 @@ int gemm_w4a16_tier(int M, int K, int N, int *m_first, int *m_last) {
         *m_last = dm;
         return 0;
     }
-    if (M <= 80) {
+    const int mm = mid_max_m(K, N);
+    if (M <= mm) {
         *m_first = dm + 1;
-        *m_last = 80;
+        *m_last = mm;
         return 1;
     }
-    *m_first = 81;
+    *m_first = mm + 1;
     *m_last = 0x7FFFFFFF;
     return 2;
 }
 
 size_t gemm_w4a16_workspace_bytes(int M, int K, int N) {
     if (M <= decode_max_m(K, N)) return 0;
-    const int S = M <= 80 ? mid_splits(K, N) : big_splits(K, N);
+    const int S = M <= mid_max_m(K, N) ? mid_splits(K, N) : big_splits(K, N);
     return S == 1 ? 0 : (size_t)S * M * N * sizeof(float);
 }
 
@@ -981,22 +894,16 @@ void launch_splitk_reduce(const float *partials, int S, int M, int N, void *y, i
     hipLaunchKernelGGL(k_w4a16_splitk_reduce, dim3(blocks), dim3(256), 0, st, partials, S, MN, y, y_f32);
 }
 
-// DIRECT: k_w4a16_mid (activations straight into an LDS ring) instead of k_w4a16_lds (through
-// registers).  Both reduce every output in the same order, so the rows of the verify tier are
-// bitwise the same whichever kernel a batch size takes.
-template <int MT, int U, bool DIRECT>
+// Verify tier: row_blocks blocks of up to 16 MT rows, cbs column blocks, S K splits, one 1-D grid
+// remapped inside the kernel.
+template <int MT, int U>
 static hipError_t launch_mid(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K, int N,
-                             void *y, int y_f32, void *ws, hipStream_t st) {
+                             void *y, int y_f32, void *ws, int row_blocks, hipStream_t st) {
     const int S = mid_splits(K, N);
     const int cbs = (N / 16 + MID_TILES - 1) / MID_TILES;
     float *partials = S > 1 ? (float *)ws : nullptr;
-    // one 1-D grid of cbs x S workgroups, remapped split-major inside the kernel (S > 1)
-    if constexpr (DIRECT)
-        hipLaunchKernelGGL((k_w4a16_mid<MT, U>), dim3(cbs * S), dim3(MID_KP * MID_CW * 64), 0, st, x, M, codes,
-                           meta, K, N, y, y_f32, S, partials);
-    else
-        hipLaunchKernelGGL((k_w4a16_lds<MT, U, MID_KP, MID_CW>), dim3(cbs * S), dim3(MID_KP * MID_CW * 64), 0, st,
-                           x, M, codes, meta, K, N, y, y_f32, S, partials, 1);
+    hipLaunchKernelGGL((k_w4a16_mid<MT, U>), dim3(cbs * S * row_blocks), dim3(MID_KP * MID_CW * 64), 0, st, x, M,
+                       codes, meta, K, N, y, y_f32, S, partials, row_blocks);
     if (S > 1) launch_splitk_reduce(partials, S, M, N, y, y_f32, st);
     return hipGetLastError();
 }
@@ -1004,8 +911,8 @@ static hipError_t launch_mid(const uint16_t *x, int M, const uint8_t *codes, con
 hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, const uint32_t *meta, int K,
                              int N, void *y, int y_f32, void *ws, hipStream_t st) {
     // Batch tiers, each with one reduction order for all its M: M <= decode_max_m(K, N) (decode,
-    // one or two row tiles), up to M = 80 (shared activations, K parts, optional split-K), M > 80
-    // (shared activations, row blocks).
+    // one or two row tiles), up to mid_max_m(K, N) (verify tier: direct-to-LDS activations, K
+    // parts, optional split-K, row blocks of at most 80), above (large tier, 128-row blocks).
     const int dm = decode_max_m(K, N);
     if (M <= 16 && M <= dm) {
         const int nt = decode_shape(K, N).nt;
@@ -1019,21 +926,28 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, con
         if (nt == 2) return launch_decode<2, 4, 2>(x, M, codes, meta, K, N, y, y_f32, st);
         return launch_decode<1, 3, 2>(x, M, codes, meta, K, N, y, y_f32, st);
     }
-    // the direct-to-LDS kernel from 49 rows: 2 - 8% faster at 64 and 80 rows on the Llama-3-8B
-    // projections, even or slower below (down at 20 rows: 17.7 against 16.6 us)
-    if (M <= 16) return launch_mid<1, 6, false>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    if (M <= 32) return launch_mid<2, 6, false>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    if (M <= 48) return launch_mid<3, 5, false>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    if (M <= 64) return launch_mid<4, 4, true>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    if (M <= 80) return launch_mid<5, 4, true>(x, M, codes, meta, K, N, y, y_f32, ws, st);
-    // M > 80: 128-row blocks x 256 columns, K splits for shapes with few column blocks, one
+    if (M <= mid_max_m(K, N)) {
+        // ceil(M / 80) row blocks of equal height in whole row tiles; ring depth 3 up to 3 row
+        // tiles, 2 above (a sweep over depths 2 - 8 at M = 20 - 80 on the Llama-3-8B projections:
+        // the shallow rings were 1 - 14% faster than 4 - 8 deep ones)
+        const int rbs = (M + 79) / 80;
+        const int mt = ((M + rbs - 1) / rbs + 15) / 16;
+        switch (mt) {
+        case 1: return launch_mid<1, 3>(x, M, codes, meta, K, N, y, y_f32, ws, rbs, st);
+        case 2: return launch_mid<2, 3>(x, M, codes, meta, K, N, y, y_f32, ws, rbs, st);
+        case 3: return launch_mid<3, 3>(x, M, codes, meta, K, N, y, y_f32, ws, rbs, st);
+        case 4: return launch_mid<4, 2>(x, M, codes, meta, K, N, y, y_f32, ws, rbs, st);
+        default: return launch_mid<5, 2>(x, M, codes, meta, K, N, y, y_f32, ws, rbs, st);
+        }
+    }
+    // Large tier: 128-row blocks x 256 columns, K splits for shapes with few column blocks, one
     // XCD-remapped 1-D grid (a 2-D (column block, split) grid for a single row block)
     const int rbs = (M + BIG_MT * 16 - 1) / (BIG_MT * 16);
     const int cbs = (N / 16 + BIG_TILES - 1) / BIG_TILES;
     const int S = big_splits(K, N);
     float *partials = S > 1 ? (float *)ws : nullptr;
     const dim3 grid = rbs > 1 ? dim3(cbs * S * rbs) : dim3(cbs, S);
-    hipLaunchKernelGGL((k_w4a16_lds<BIG_MT, 4, 1, BIG_CW>), grid, dim3(BIG_CW * 64), 0, st, x, M, codes, meta,
+    hipLaunchKernelGGL((k_w4a16_lds<BIG_MT, 4, BIG_CW>), grid, dim3(BIG_CW * 64), 0, st, x, M, codes, meta,
                        K, N, y, y_f32, S, partials, rbs);
     if (S > 1) launch_splitk_reduce(partials, S, M, N, y, y_f32, st);
     return hipGetLastError();

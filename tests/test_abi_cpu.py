@@ -85,10 +85,13 @@ def test_gemm_validation():
     assert L.qspec_gemm_w4a16(FAKE, 80, FAKE, FAKE, 4096, 4096, FAKE, 0, None, 0, None) == ERR_WS
     assert L.qspec_gemm_w4a16(FAKE, 80, FAKE, FAKE, 4096, 4096, FAKE, 0, FAKE, need - 1, None) == ERR_WS
     assert L.qspec_gemm_w4a16_workspace_bytes(80, 4096, 70) == 0
+    # verify tier past 80 rows (row blocks): its own split count
+    assert L.qspec_gemm_w4a16_workspace_bytes(96, 32768, 512) == 16 * 96 * 512 * 4
+    assert L.qspec_gemm_w4a16_workspace_bytes(128, 14336, 4096) == 8 * 128 * 4096 * 4
     # large tier: K is split only for few 256-column blocks and long K
     assert L.qspec_gemm_w4a16_workspace_bytes(1280, 8192, 57344) == 0
     assert L.qspec_gemm_w4a16_workspace_bytes(1280, 28672, 8192) == 4 * 1280 * 8192 * 4
-    assert L.qspec_gemm_w4a16_workspace_bytes(96, 32768, 512) == 8 * 96 * 512 * 4
+    assert L.qspec_gemm_w4a16_workspace_bytes(600, 32768, 512) == 8 * 600 * 512 * 4
     assert L.qspec_gemm_w4a16(FAKE, 1280, FAKE, FAKE, 28672, 8192, FAKE, 0, None, 0, None) == ERR_WS
 
 
@@ -240,20 +243,34 @@ def test_draft_sample_validation():
     assert call(tok=ctypes.c_void_p(0x1002)) == ERR_ALIGN
 
 
-# Batch tiers: (K, N) -> the last M of the W4A16 decode tier, from the rule the header states.
+# Batch tiers: (K, N) -> the last M of the W4A16 decode tier and of the verify tier, from the
+# rules the header states.
 W4A16_DECODE_LAST = [
-    (4096, 4096, 32),      # 256 workgroups, K * N = 4096 * 4096: small projection
-    (4096, 6144, 32),      # 192 workgroups (two tiles each), K * N = 4096 * 6144
-    (3584, 4608, 16),      # Qwen qkv: 288 one-tile workgroups, more than 256
-    (14336, 4096, 8),      # Llama down: long K over one-tile workgroups
-    (18944, 3584, 8),      # Qwen down
-    (12160, 4096, 16),     # K just below 12288
-    (28672, 8192, 16),     # 70B down: two-tile workgroups
-    (4096, 28672, 16),     # 896 workgroups
-    (3584, 152064, 24),    # vocabulary head: four tiles per workgroup
-    (4096, 128256, 24),
-    (512, 512, 32),
+    (4096, 4096, 32, 384),      # 256 workgroups, K * N = 4096 * 4096: small projection
+    (4096, 6144, 32, 384),      # 192 workgroups (two tiles each), K * N = 4096 * 6144
+    (3584, 4608, 16, 384),      # Qwen qkv: 288 one-tile workgroups, more than 256
+    (14336, 4096, 8, 384),      # Llama down: long K over one-tile workgroups
+    (18944, 3584, 8, 256),      # Qwen down
+    (12160, 4096, 16, 384),     # K just below 12288
+    (28672, 8192, 16, 160),     # 70B down: two-tile workgroups; 32 blocks x 4 splits per row block
+    (4096, 28672, 16, 160),     # 896 workgroups; 112 large-tier blocks per row block
+    (3584, 152064, 24, 80),     # vocabulary head: four tiles per workgroup
+    (4096, 128256, 24, 80),
+    (512, 512, 32, 384),
+    (8192, 57344, 16, 80),     # 70B gate+up: 224 blocks per row block
 ]
+
+
+def _large_splits(K, N):
+    blocks, G, S = -(-N // 256), K // 128, 1
+    while S < 8 and 2 * S * blocks <= 128 and G // (2 * S) >= 32:
+        S *= 2
+    return S
+
+
+def _verify_last(K, N):
+    P = -(-N // 256) * _large_splits(K, N)
+    return 384 if P <= 32 else 256 if P <= 64 else 160 if P <= 128 else 80
 
 
 def _decode_last(K, N):
@@ -267,12 +284,12 @@ def _decode_last(K, N):
     return 8 if nt == 1 and K // 128 >= 96 else 16
 
 
-@pytest.mark.parametrize("K,N,last", W4A16_DECODE_LAST)
-def test_w4a16_tier_boundaries(K, N, last):
-    D = _decode_last(K, N)
-    assert D == last
-    for M, tier, lo, hi in [(1, 0, 1, D), (D, 0, 1, D), (D + 1, 1, D + 1, 80), (80, 1, D + 1, 80),
-                            (81, 2, 81, 2 ** 31 - 1), (1280, 2, 81, 2 ** 31 - 1)]:
+@pytest.mark.parametrize("K,N,last,vlast", W4A16_DECODE_LAST)
+def test_w4a16_tier_boundaries(K, N, last, vlast):
+    D, V = _decode_last(K, N), _verify_last(K, N)
+    assert D == last and V == vlast
+    for M, tier, lo, hi in [(1, 0, 1, D), (D, 0, 1, D), (D + 1, 1, D + 1, V), (80, 1, D + 1, V), (V, 1, D + 1, V),
+                            (V + 1, 2, V + 1, 2 ** 31 - 1), (1280, 2, V + 1, 2 ** 31 - 1)]:
         assert q.qspec_gemm_w4a16_tier(M, K, N) == (tier, lo, hi), (M, K, N)
     # the workspace follows the tiers: none in the decode tier
     assert q.qspec_gemm_w4a16_workspace_bytes(D, K, N) == 0

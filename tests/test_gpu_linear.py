@@ -146,25 +146,28 @@ def test_w4a16_one_hot_rows_reproduce_dequantized_weights_exactly(M):
 @pytest.mark.parametrize("K,N", [(1024, 208), (1024, 16 * 300), (256, 16 * 4100), (12288, 256)])
 def test_w4a16_rows_do_not_depend_on_batch(K, N):
     """Every M in one batch tier (as qspec_gemm_w4a16_tier reports it: decode up to 32, 16, 24 or 8
-    rows for these four shapes) reduces a row in the same order: bitwise-equal rows, also where
-    the verify tier switches from register to direct-to-LDS activation staging (48 -> 49 rows).
-    Across tiers the rows agree to fp32 rounding."""
+    rows for these four shapes, verify up to 384, 384, 80 and 384) reduces a row in the same order:
+    bitwise-equal rows, also across the verify tier's row-tile counts and row blocks.  Across
+    tiers the rows agree to fp32 rounding."""
     note(f"gemm_w4a16 batch invariance K={K} N={N}")
     w = si.weights(K, N, seed=4)
     wdev = weights_dev(w)
-    x = si.activations(96, K, seed=4)
-    Ms = (1, 5, 8, 9, 12, 16, 17, 20, 24, 25, 32, 33, 48, 49, 64, 65, 80, 81, 96)
-    full = {M: run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy() for M in Ms}
+    Ms = (1, 5, 8, 9, 12, 16, 17, 20, 24, 25, 32, 33, 48, 49, 64, 65, 80, 81, 96, 161, 240, 512, 513, 600)
+    x = si.activations(max(Ms), K, seed=4)
     tiers = {}
     for M in Ms:
         t, lo, hi = q.qspec_gemm_w4a16_tier(M, K, N)
         tiers.setdefault((t, lo, hi), []).append(M)
     assert len(tiers) == 3
+    tops = {}
     for (t, lo, hi), group in tiers.items():
         top = max(group)
+        tops[t] = run_w4a16(x[:top], w, torch.float32, wdev).cpu().numpy()
         for M in group:
-            assert np.array_equal(full[M], full[top][:M]), (t, M, top)
-    assert_close(full[16].astype(np.float64), full[96][:16].astype(np.float64), False, "across tiers")
+            if M != top:
+                assert np.array_equal(run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy(), tops[t][:M]), (t, M, top)
+    assert_close(tops[0][:16].astype(np.float64), tops[2][:16].astype(np.float64), False, "across tiers")
+    assert_close(tops[1][:16].astype(np.float64), tops[2][:16].astype(np.float64), False, "across tiers")
 
 
 @pytest.mark.parametrize("M,K,N", [(80, 4096, 4096), (40, 14336, 512), (33, 2048, 784), (12, 14336, 2048)])
@@ -189,15 +192,20 @@ def test_w4a16_split_k_workspace_reuse(M, K, N):
                  "split-K")
 
 
-# Large tier (M > 80) with K splits: few 256-column blocks and long K.  8192 x 256 splits K in two
-# (one row block: a 2-D grid; two row blocks, the second ragged: the 1-D remapped grid),
-# 32768 x 512 in eight.
-LARGE_SPLIT = [(100, 8192, 256), (200, 8192, 256), (96, 32768, 512)]
+# Row blocks with K splits.  Verify tier past 80 rows: Llama down at 128 rows (two 64-row blocks,
+# 8 splits), 8192 x 256 at 200 rows (three 80-row blocks, the last ragged; 12 splits), Llama qkv
+# at 161 rows (three 64-row blocks, the last with 33 rows; 5 splits).  Large tier (128-row blocks
+# past the verify tier's last M): 32768 x 256 at 600 rows (five blocks, 8 splits) and 32768 x 2048
+# at 400 rows (four blocks, the last with 16 rows; 8 splits).
+ROW_BLOCKS_SPLIT = [(128, 14336, 4096, 1), (200, 8192, 256, 1), (161, 4096, 6144, 1), (600, 32768, 256, 2),
+                    (400, 32768, 2048, 2)]
 
 
-@pytest.mark.parametrize("M,K,N", LARGE_SPLIT)
-def test_w4a16_large_tier_split_k(M, K, N):
-    note(f"gemm_w4a16 large-tier split-K M={M} K={K} N={N}")
+@pytest.mark.parametrize("M,K,N,tier", ROW_BLOCKS_SPLIT)
+def test_w4a16_row_blocks_split_k(M, K, N, tier):
+    note(f"gemm_w4a16 row blocks split-K M={M} K={K} N={N}")
+    t, lo, _ = q.qspec_gemm_w4a16_tier(M, K, N)
+    assert t == tier
     assert q.qspec_gemm_w4a16_workspace_bytes(M, K, N) >= 2 * 4 * M * N
     w = si.weights(K, N, seed=K // 128 + N)
     wdev = weights_dev(w)
@@ -206,10 +214,10 @@ def test_w4a16_large_tier_split_k(M, K, N):
     tiles = np.array([0, N // 16 - 1])
     sub = si.slice_tiles(w, tiles)
     assert_close(y[:, tile_columns(tiles)].astype(np.float64), oracle.gemm_w4a16(x, sub["codes"], sub["meta"]),
-                 False, "large split-K")
-    if M > 100:                          # same tier, same (K, N): bitwise-equal rows
-        y100 = run_w4a16(x[:100], w, torch.float32, wdev).cpu().numpy()
-        assert np.array_equal(y100, y[:100])
+                 False, "row blocks split-K")
+    # the tier's first M (fewer row blocks, another block height): bitwise-equal rows
+    y_lo = run_w4a16(x[:lo], w, torch.float32, wdev).cpu().numpy()
+    assert np.array_equal(y_lo, y[:lo])
 
 
 FULL_W4A16 = [
