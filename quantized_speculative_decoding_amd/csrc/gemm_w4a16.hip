@@ -914,16 +914,25 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, con
     // one or two row tiles), up to mid_max_m(K, N) (verify tier: direct-to-LDS activations, K
     // parts, optional split-K, row blocks of at most 80), above (large tier, 128-row blocks).
     const int dm = decode_max_m(K, N);
+    // Decode tier.  The ring depth does not change the reduction order, so it follows M: a 2-deep
+    // ring for the wide workgroups where their registers are full (graph-timed, 4 -> 2 deep: Qwen
+    // head at M = 3 - 9 68 -> 63 us, at 17 - 24 81 - 89 -> 77 - 85 us; Llama qkv at M = 16 7.8 -> 7.4
+    // us, at 17 - 32 8.8 - 11.2 -> 8.2 - 10.7 us; Llama gate+up at M = 9 - 12 16.5 - 17.5 -> 17.7 -
+    // 18.0 us, so only above 12 rows there).
     if (M <= 16 && M <= dm) {
         const int nt = decode_shape(K, N).nt;
-        if (nt == 4) return launch_decode<4, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
-        if (nt == 2) return launch_decode<2, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
+        if (nt == 4)
+            return M >= 2 ? launch_decode<4, 2, 1>(x, M, codes, meta, K, N, y, y_f32, st)
+                          : launch_decode<4, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
+        if (nt == 2)
+            return M > 12 ? launch_decode<2, 2, 1>(x, M, codes, meta, K, N, y, y_f32, st)
+                          : launch_decode<2, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
         return launch_decode<1, 4, 1>(x, M, codes, meta, K, N, y, y_f32, st);
     }
     if (M <= dm) {
         const int nt = decode_shape(K, N).nt;
-        if (nt == 4) return launch_decode<4, 3, 2>(x, M, codes, meta, K, N, y, y_f32, st);
-        if (nt == 2) return launch_decode<2, 4, 2>(x, M, codes, meta, K, N, y, y_f32, st);
+        if (nt == 4) return launch_decode<4, 2, 2>(x, M, codes, meta, K, N, y, y_f32, st);
+        if (nt == 2) return launch_decode<2, 2, 2>(x, M, codes, meta, K, N, y, y_f32, st);
         return launch_decode<1, 3, 2>(x, M, codes, meta, K, N, y, y_f32, st);
     }
     if (M <= mid_max_m(K, N)) {
