@@ -924,6 +924,8 @@ PMC_PASSES = {
              "SQ_BUSY_CYCLES SQ_WAVES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE",
     "pass2": "SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_INSTS_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT "
              "SQ_ACTIVE_INST_VMEM SQ_INST_CYCLES_VMEM_RD SQ_CYCLES GRBM_GUI_ACTIVE",
+    "pass3": "FETCH_SIZE",
+    "pass4": "WRITE_SIZE",
 }
 
 

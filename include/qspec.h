@@ -150,8 +150,11 @@ int qspec_gemm_w4a4_tier(int32_t M, int32_t K, int32_t N, int32_t *m_first, int3
  *   2: [V + 1, INT32_MAX] the shared-activation kernel over 128-row blocks;
  * with D = 24 when N >= 65536 (vocabulary-sized heads: four column tiles per workgroup),
  * D = 32 when the decode grid has at most 256 workgroups and K * N <= 4096 * 6144 (small
- * projections), D = 8 when N < 6144 and K >= 12288 (long K over one-tile workgroups), and
- * D = 16 otherwise.  The decode grid has N / 16 workgroups for N < 6144, ceil(N / 32) for
+ * projections), and otherwise: for N < 6144 (one-tile workgroups) D = 8 when K >= 8192 and 12
+ * below; for 6144 <= N < 65536 (two-tile workgroups) D = 8 when K >= 12288, else D = 20 when
+ * tier 1's workgroups W1 = ceil(N / 128) * S1 (S1: its K split count below) leave the last of
+ * ceil(W1 / 256) generations of 256 under three quarters full (4 W1 < 3 * 256 * ceil(W1 / 256)),
+ * and D = 12 otherwise.  The decode grid has N / 16 workgroups for N < 6144, ceil(N / 32) for
  * 6144 <= N < 65536.  With P = ceil(N / 256) * S2, the tier-2 workgroups per 128-row block (S2:
  * its K split count below), V = 384 for P <= 32, 256 for P <= 64, 160 for P <= 128 and 80
  * above.  Host-only: launches nothing.

@@ -805,16 +805,26 @@ static hipError_t launch_decode(const uint16_t *x, int M, const uint8_t *codes, 
 // 7.5 and 11.0 -> 9.8, Qwen head 99 -> 88 (M = 17) and 100 -> 94 (M = 24), 103 both at M = 32;
 // losses where the activation re-reads dominate: Llama down 16.2 -> 20.4 (M = 17), 18.0 -> 34.7
 // (M = 32), gate+up 23 -> 25 .. 34, and Qwen qkv (288 workgroups, some CUs run two) 10.2 -> 11.4.
+static int mid_splits(int K, int N);
+
 static int decode_max_m(int K, int N) {
     const DecodeShape d = decode_shape(K, N);
     const int wgs = (N / 16 + d.nt - 1) / d.nt;
+    const int G = K / kGroup;
     if (d.nt == 4) return 24;
     if (wgs <= 256 && (long long)K * N <= 4096LL * 6144) return 32;
-    // long K over one-tile workgroups (Llama-3-8B and Qwen2.5-7B down): every decode wave re-reads
-    // all M activation rows of its 28 - 37 groups, and above 8 rows the shared-activation kernel
-    // is faster
-    if (d.nt == 1 && K / kGroup >= 96) return 8;
-    return 16;
+    // Every decode wave re-reads all M activation rows of its groups, so past a few rows the verify
+    // tier, which stages them once per 128 columns, wins: from 9 rows on long K (graph-timed,
+    // decode / verify at M = 9 - 16: Llama-3-8B and Qwen2.5-7B down, K = 12160 x 4096 12 - 15 /
+    // 12 us, Llama-70B down 33 - 38 / 30 - 32 us), from 13 rows otherwise (Llama-3-8B gate+up at 16
+    // rows 20.6 / 17.3 us, Llama-70B gate+up 71.5 / 64, Qwen2.5-7B qkv 9.9 / 8.8) -- unless the
+    // verify tier's workgroups leave its last generation mostly idle (Qwen2.5-7B gate+up, 296
+    // workgroups on 256 CUs: decode 22 - 27 / verify 27 - 30 us up to 17 rows, 29.6 / 30.2 at 20).
+    if (d.nt == 1) return G >= 64 ? 8 : 12;
+    if (G >= 96) return 8;
+    const int vw = ((N / 16 + MID_TILES - 1) / MID_TILES) * mid_splits(K, N);   // verify workgroups
+    const int gens = (vw + 255) / 256;
+    return 4 * vw < 3 * 256 * gens ? 20 : 12;
 }
 
 // K splits of the verify-tier kernel: a function of (K, N) only.  Column blocks alone fill the

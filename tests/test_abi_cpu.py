@@ -248,16 +248,17 @@ def test_draft_sample_validation():
 W4A16_DECODE_LAST = [
     (4096, 4096, 32, 384),      # 256 workgroups, K * N = 4096 * 4096: small projection
     (4096, 6144, 32, 384),      # 192 workgroups (two tiles each), K * N = 4096 * 6144
-    (3584, 4608, 16, 384),      # Qwen qkv: 288 one-tile workgroups, more than 256
+    (3584, 4608, 12, 384),      # Qwen qkv: 288 one-tile workgroups, more than 256
     (14336, 4096, 8, 384),      # Llama down: long K over one-tile workgroups
     (18944, 3584, 8, 256),      # Qwen down
-    (12160, 4096, 16, 384),     # K just below 12288
-    (28672, 8192, 16, 160),     # 70B down: two-tile workgroups; 32 blocks x 4 splits per row block
-    (4096, 28672, 16, 160),     # 896 workgroups; 112 large-tier blocks per row block
+    (12160, 4096, 8, 384),     # K just below 12288
+    (28672, 8192, 8, 160),     # 70B down: two-tile workgroups; 32 blocks x 4 splits per row block
+    (4096, 28672, 12, 160),     # 896 workgroups; 112 large-tier blocks per row block
     (3584, 152064, 24, 80),     # vocabulary head: four tiles per workgroup
     (4096, 128256, 24, 80),
     (512, 512, 32, 384),
-    (8192, 57344, 16, 80),     # 70B gate+up: 224 blocks per row block
+    (8192, 57344, 12, 80),     # 70B gate+up: 224 blocks per row block
+    (3584, 37888, 20, 80),     # Qwen gate+up: 296 verify workgroups, the second generation nearly idle
 ]
 
 
@@ -273,6 +274,11 @@ def _verify_last(K, N):
     return 384 if P <= 32 else 256 if P <= 64 else 160 if P <= 128 else 80
 
 
+def _verify_splits(K, N):
+    blocks, G = -(-N // 128), K // 128
+    return 1 if blocks >= 192 else max(1, min(256 // blocks, 16, G // 5))
+
+
 def _decode_last(K, N):
     T = N // 16
     nt = 4 if T >= 4096 else 2 if T >= 384 else 1
@@ -281,7 +287,12 @@ def _decode_last(K, N):
         return 24
     if wgs <= 256 and K * N <= 4096 * 6144:
         return 32
-    return 8 if nt == 1 and K // 128 >= 96 else 16
+    if nt == 1:
+        return 8 if K >= 8192 else 12
+    if K >= 12288:
+        return 8
+    w1 = -(-N // 128) * _verify_splits(K, N)
+    return 20 if 4 * w1 < 3 * 256 * -(-w1 // 256) else 12
 
 
 @pytest.mark.parametrize("K,N,last,vlast", W4A16_DECODE_LAST)
@@ -298,9 +309,9 @@ def test_w4a16_tier_boundaries(K, N, last, vlast):
 def test_w4a16_tier_rule_on_the_workload_shapes():
     """The header's rule, on the Llama-3-8B and Qwen2.5-7B projections and heads."""
     assert _decode_last(4096, 4096) == 32 and _decode_last(4096, 6144) == 32
-    assert _decode_last(3584, 4608) == 16 and _decode_last(3584, 3584) == 32
+    assert _decode_last(3584, 4608) == 12 and _decode_last(3584, 3584) == 32
     assert _decode_last(14336, 4096) == 8 and _decode_last(18944, 3584) == 8
-    assert _decode_last(4096, 28672) == 16 and _decode_last(3584, 37888) == 16
+    assert _decode_last(4096, 28672) == 12 and _decode_last(3584, 37888) == 20
     assert _decode_last(3584, 152064) == 24
 
 

@@ -229,12 +229,13 @@ def test_qspec_greedy_with_attention_over_the_shared_cache_equals_plain_greedy(s
 # ---- the identity with a batch of sequences, across W4A16 batch tiers ------------------------
 # Plain decoding of B sequences runs the W4A16 layers at M = B; QSPEC verification at
 # M = B (gamma + 1).  With the vocabulary head at V2 = 16384 columns (its decode tier ends at
-# M = 16) and the KV projection at 256 x 256 (decode tier up to M = 32), B = 4 with gamma = 4
-# verifies the head at M = 20 and B = 16 verifies both layers at M = 80 -- in a different tier
-# from plain decoding -- and B = 1 with gamma = 16 verifies the head at M = 17.  Rows then agree
-# to fp32 rounding instead of bit for bit, so the committed tokens may differ from plain decoding
-# only where plain decoding's own choice is a near tie: a token may differ only where the
-# oracle's top-2 logit gap of the plain run's hidden state is below 1e-4 of the top logit.
+# M = 20) and the KV projection at 256 x 256 (decode tier up to M = 32), B = 4 with gamma = 5
+# verifies the head at M = 24 and B = 16 verifies both layers at M = 80 -- in a different tier
+# from plain decoding.  Rows then agree to fp32 rounding instead of bit for bit, so the committed
+# tokens may differ from plain decoding only where plain decoding's own choice is a near tie: a
+# token may differ only where the oracle's top-2 logit gap of the plain run's hidden state is
+# below 1e-4 of the top logit.  B = 1 with gamma = 16 verifies at M = 17, inside the decode tier
+# of both layers: the same reduction order as plain decoding, so the tokens are equal outright.
 
 V2 = 16384
 
@@ -330,13 +331,14 @@ def qspec_greedy_batch(m: BatchToy, firsts, n: int, gamma: int):
     return [t[: n + 1] for t in toks], accepts
 
 
-@pytest.mark.parametrize("B,gamma", [(4, 4), (16, 4), (1, 16)])
+@pytest.mark.parametrize("B,gamma", [(4, 5), (16, 4), (1, 16)])
 def test_qspec_greedy_batch_equals_plain_w4a16_greedy_across_tiers(B, gamma):
     note(f"toy decoder identity across W4A16 tiers B={B} gamma={gamma}")
     m = BatchToy(seed=41 + B)
     plain_tier = q.qspec_gemm_w4a16_tier(B, H, V2)
     verify_tier = q.qspec_gemm_w4a16_tier(B * (gamma + 1), H, V2)
-    assert plain_tier[0] != verify_tier[0]                 # the head is verified in another tier
+    cross = plain_tier[0] != verify_tier[0]
+    assert cross == (B > 1)                                # B > 1: the head is verified in another tier
     n = 24 if B == 16 else 32
     firsts = [(97 * b + 5) % V2 for b in range(B)]
     ref, hid = plain_greedy_batch(m, firsts, n)
@@ -347,6 +349,7 @@ def test_qspec_greedy_batch_equals_plain_w4a16_greedy_across_tiers(B, gamma):
     for b in range(B):
         if got[b] == ref[b]:
             continue
+        assert cross, (b, got[b], ref[b])                  # one tier: one reduction order, no flips
         i = next(k for k in range(n + 1) if got[b][k] != ref[b][k])
         h = hid[b][i - 1]                                   # plain run's hidden state before token i
         logits = oracle.gemm_w4a16(h[None], m.w_lm_host["codes"], m.w_lm_host["meta"])[0]

@@ -145,7 +145,7 @@ def test_w4a16_one_hot_rows_reproduce_dequantized_weights_exactly(M):
 
 @pytest.mark.parametrize("K,N", [(1024, 208), (1024, 16 * 300), (256, 16 * 4100), (12288, 256)])
 def test_w4a16_rows_do_not_depend_on_batch(K, N):
-    """Every M in one batch tier (as qspec_gemm_w4a16_tier reports it: decode up to 32, 16, 24 or 8
+    """Every M in one batch tier (as qspec_gemm_w4a16_tier reports it: decode up to 32, 12, 24 and 32
     rows for these four shapes, verify up to 384, 384, 80 and 384) reduces a row in the same order:
     bitwise-equal rows, also across the verify tier's row-tile counts and row blocks.  Across
     tiers the rows agree to fp32 rounding."""
@@ -166,7 +166,8 @@ def test_w4a16_rows_do_not_depend_on_batch(K, N):
         for M in group:
             if M != top:
                 assert np.array_equal(run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy(), tops[t][:M]), (t, M, top)
-    assert_close(tops[0][:16].astype(np.float64), tops[2][:16].astype(np.float64), False, "across tiers")
+    n = min(16, tops[0].shape[0])
+    assert_close(tops[0][:n].astype(np.float64), tops[2][:n].astype(np.float64), False, "across tiers")
     assert_close(tops[1][:16].astype(np.float64), tops[2][:16].astype(np.float64), False, "across tiers")
 
 
