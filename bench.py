@@ -452,8 +452,9 @@ def round_model(R, ph, torch):
     """Outside the timed round: the speedup model S = E[L] T_target / (T_draft + T_verify +
     T_overhead) with every time measured here (T_target = one plain W4A16 decoding step at M = B
     over the same layers and the head, graph-replayed), E[L] as the round's accept counts give it
-    (mean A + 1 over the B sequences), and S at a few acceptance rates a through
-    E[L] = (1 - a^(gamma+1)) / (1 - a)."""
+    (mean A + 1 over the B sequences) and as the round's logits imply it (the per-position
+    acceptance probabilities, free of the sampling noise of B = 16 draws), and S at a few
+    acceptance rates a through E[L] = (1 - a^(gamma+1)) / (1 - a)."""
     graph = capture(R.plain_gemm, torch)
     graph.replay()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -466,6 +467,15 @@ def round_model(R, ph, torch):
     t_target = a.elapsed_time(b) / 5
     acc = R.accept.cpu().double()
     e_l = float(acc.mean()) + 1.0
+    # the acceptance probability of each drafted position, sum_v min(p, q) with p and q the
+    # softmaxes of that position's target and draft logits (the rule's expected acceptance for a
+    # token drawn from q), and the expected committed length it implies for each sequence:
+    # E[L_b] = 1 + sum_k prod_{j<k} alpha_{b,j}.  Computed once in float64 on the round's logits.
+    p = torch.softmax(R.target_logits[:, :R.gamma, :].double(), dim=-1)
+    q = torch.softmax(R.draft_logits.double(), dim=-1)
+    alpha = torch.minimum(p, q).sum(-1)                                     # [B][gamma]
+    e_l_exp = float((1.0 + torch.cumprod(alpha, dim=1).sum(1)).mean())
+    del p, q
     t_draft = ph["quantize_act"] + ph["gemm_w4a4"] + ph["draft_head"]
     t_verify = ph["gemm_w4a16"]
     t_over = ph["verify_accept"] + ph["kv_overwrite"]
@@ -475,6 +485,8 @@ def round_model(R, ph, torch):
     return {"T_target_ms": round(t_target, 4), "T_draft_ms": round(t_draft, 4), "T_verify_ms": round(t_verify, 4),
             "T_overhead_ms": round(t_over, 4), "accept_counts": [int(v) for v in R.accept.cpu().tolist()],
             "E_L_measured": round(e_l, 4), "S_measured_E_L": round(e_l * t_target / t_round, 3),
+            "alpha_per_position_mean": round(float(alpha.mean()), 4),
+            "E_L_expected_from_logits": round(e_l_exp, 4), "S_expected_E_L": round(e_l_exp * t_target / t_round, 3),
             "S_at_alpha": {str(k): round(v, 3) for k, v in at.items()}}
 
 
