@@ -232,6 +232,9 @@ FULL_W4A16 = [
     ("qwen7b.lm_head", 3584, 152064, 17), ("llama8b.qkv", 4096, 6144, 20),
     # 70B-shaped FFN, compute-bound verify at 256 x 5 tokens
     ("llama70b.gate_up", 8192, 57344, 1280), ("llama70b.down", 28672, 8192, 1280),
+    # the Llama-3-8B-shaped vocabulary head as the QSPEC round runs it: verified at B (gamma + 1) = 80
+    # rows, and one plain decoding step at B = 16 rows
+    ("llama8b.lm_head", 4096, 128256, 80), ("llama8b.lm_head", 4096, 128256, 16),
 ]
 
 
@@ -367,6 +370,7 @@ FULL_W4A4 = [
     ("qwen7b.qkv", 3584, 4608, 1), ("qwen7b.o", 3584, 3584, 1), ("qwen7b.gate_up", 3584, 37888, 1),
     ("qwen7b.down", 18944, 3584, 1), ("qwen7b.lm_head", 3584, 152064, 1),
     ("llama70b.gate_up", 8192, 57344, 256), ("llama70b.down", 28672, 8192, 256),
+    ("llama8b.lm_head", 4096, 128256, 16),     # the round's draft head, one draft step at B = 16
 ]
 
 
