@@ -16,6 +16,9 @@
 //                or of p)
 //             -> k_residual_pick (per sequence: locate the chunk and its 8-logit segment with
 //                block-wide prefix sums in one fixed order, then walk that segment in logit order)
+//   sampling with gamma = 0 (the draft-side head): k_softmax_partial -> k_head_pick (per row: the
+//             chunk statistics are the chunk masses, so the chunk, a 32-logit segment inside it
+//             and the token follow without a residual pass)
 // Softmax normalizers, ratios and running sums are fp64; the exponentials are fp64 as well.  The
 // residual stages use shorter chunks than the softmax statistics: they touch two rows per
 // sequence instead of 2 gamma + 1, so 8192-logit chunks left most of the chip idle.
@@ -555,6 +558,115 @@ k_residual_pick(const float *__restrict__ target, size_t ldt, const float *__res
     if (owner >= 0 && tid == owner) out[(size_t)b * ldo + A] = last;
 }
 
+// Sampling with gamma = 0 (the draft-side head; a verification with no draft tokens): the draw
+// from softmax(row) needs no residual pass, because the row's own chunk statistics are its chunk
+// masses.  One workgroup per row: the row's maximum M and total S from the chunk statistics in
+// chunk order, chunk c's mass W_c = psum_c exp(pmax_c - M), the chunk holding u S by a block-wide
+// prefix sum over the chunks, then inside that chunk a prefix sum over 32-logit segments of
+// exp(x - M) and a walk through the crossing segment in logit order (by the thread that holds
+// it).  Rounding can put u S past a chunk's recomputed mass; then, as in k_residual_pick, the
+// last logit of positive mass in the chunk is drawn (a near tie of the inverse CDF).
+constexpr int HSEG = VCHUNK / VT;   // logits per thread in the chunk walk
+static_assert(VCHUNK % VT == 0, "whole segments per chunk");
+
+__global__ void __launch_bounds__(VT)
+k_head_pick(const float *__restrict__ logits, size_t ldt, const float *__restrict__ u, int V, int C,
+            const float *__restrict__ pmax, const double *__restrict__ psum, int32_t *__restrict__ accept,
+            int32_t *__restrict__ out, int ldo) {
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float *row = logits + (size_t)b * ldt;
+    const float *pm = pmax + (size_t)b * C;
+    const double *ps = psum + (size_t)b * C;
+    // the row's statistics in chunk order (every thread the same loop, the same result)
+    float Mf = pm[0];
+    for (int c = 1; c < C; ++c) Mf = fmaxf(Mf, pm[c]);
+    const double M = (double)Mf;
+    __shared__ int s_chunk, s_fallback;
+    __shared__ double s_thr;
+    if (C <= VT) {
+        const double part = tid < C ? ps[tid] * exp((double)pm[tid] - M) : 0.0;
+        const double pre = block_scan(part);
+        const double tot = block_bcast(pre, C - 1);
+        const double thr = (double)u[b] * tot;
+        int chunk = block_find(tid < C && pre > thr, true);
+        const bool fallback = chunk < 0;
+        double before = 0.0;
+        if (fallback) {
+            chunk = block_find(tid < C && part > 0.0, false);
+            if (chunk < 0) chunk = C - 1;
+        } else {
+            before = block_bcast(pre - part, chunk);
+        }
+        if (tid == 0) {
+            s_chunk = chunk;
+            s_fallback = fallback;
+            s_thr = thr - before;
+        }
+    } else if (tid == 0) {   // more chunks than threads: one thread walks them in order
+        double tot = 0.0;
+        for (int c = 0; c < C; ++c) tot += ps[c] * exp((double)pm[c] - M);
+        const double thr = (double)u[b] * tot;
+        double run = 0.0, before = 0.0;
+        int chunk = -1;
+        for (int c = 0; c < C; ++c) {
+            before = run;
+            run += ps[c] * exp((double)pm[c] - M);
+            if (run > thr) { chunk = c; break; }
+        }
+        int fallback = 0;
+        if (chunk < 0) {
+            fallback = 1;
+            for (int c = C - 1; c >= 0; --c)
+                if (ps[c] > 0.0) { chunk = c; break; }
+            if (chunk < 0) chunk = C - 1;
+        }
+        s_chunk = chunk;
+        s_fallback = fallback;
+        s_thr = thr - before;
+    }
+    __syncthreads();
+    const int lo = s_chunk * VCHUNK, hi = min(V, lo + VCHUNK);
+    const int x0 = lo + tid * HSEG, x1 = min(hi, x0 + HSEG);
+    float lv[HSEG];
+#pragma unroll
+    for (int k = 0; k < HSEG; ++k) lv[k] = x0 + k < x1 ? row[x0 + k] : 0.f;
+    double wv[HSEG];   // exp(x - M) of the segment's logits (0 past the chunk), kept for the walk
+#pragma unroll
+    for (int k = 0; k < HSEG; ++k) wv[k] = x0 + k < x1 ? exp((double)lv[k] - M) : 0.0;
+    double mine = 0.0;
+#pragma unroll
+    for (int k = 0; k < HSEG; ++k) mine += wv[k];
+    const double thr = s_thr;
+    const double pre = block_scan(mine);
+    const int tsel = s_fallback ? -1 : block_find(pre > thr, true);
+    if (tid == 0) accept[b] = 0;
+    if (tsel >= 0) {
+        if (tid == tsel) {
+            double run = pre - mine;
+            int tok = -1, lastpos = -1;
+#pragma unroll
+            for (int k = 0; k < HSEG; ++k) {
+                if (tok < 0 && x0 + k < x1) {
+                    if (wv[k] > 0.0) lastpos = x0 + k;
+                    run += wv[k];
+                    if (run > thr) tok = x0 + k;
+                }
+            }
+            if (tok < 0) tok = lastpos >= 0 ? lastpos : min(x0, hi - 1);   // rounding at the segment's end
+            out[(size_t)b * ldo] = tok;
+        }
+        return;
+    }
+    // No crossing: the last logit of positive mass in the chunk, else the chunk's last logit.
+    int last = -1;
+    for (int k = HSEG - 1; k >= 0; --k)
+        if (x0 + k < x1 && wv[k] > 0.0) { last = x0 + k; break; }
+    const int owner = block_find(last >= 0, false);
+    if (tid == 0 && owner < 0) out[(size_t)b * ldo] = hi - 1;
+    if (owner >= 0 && tid == owner) out[(size_t)b * ldo] = last;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Draft statistics and the adaptive-gamma controller (SpecKV notes, architecture and mechanism;
 // the implementation guide's controller): per draft row, confidence = max p and entropy =
@@ -726,6 +838,11 @@ static hipError_t launch_verify(int mode, const float *target, size_t ldt, const
     double *pmass = (double *)(w + L.pmass);
     hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)(R * C)), dim3(VT), 0, st, target, ldt, draft, B,
                        gamma, V, C, vec, pmax, psum);
+    if (gamma == 0) {   // no candidates: the draw from each row's softmax, straight from its statistics
+        hipLaunchKernelGGL(k_head_pick, dim3(B), dim3(VT), 0, st, target, ldt, u_resample, V, C, pmax, psum, accept,
+                           out, ldo);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_sample_accept, dim3(B), dim3(kWave), 0, st, target, ldt, draft, tokens,
                        u_accept, B, gamma, V, C, pmax, psum, rowM, rowS, accA, accept, out, ldo);
     hipLaunchKernelGGL(k_residual_partial, dim3((unsigned)((long long)B * L.CR)), dim3(VT), 0, st, target, ldt,
