@@ -37,8 +37,10 @@ def run_verify(mode, t, d, toks, u, v):
 
 
 # gamma = 0 is the draft-side sampling head: one token per row from softmax(row) (or its argmax).
+# (2, 2, 600000): more residual chunks than a workgroup has threads (one thread walks them);
+# (2, 0, 2200000): the same for the gamma = 0 draw's chunk statistics
 SHAPES = [(1, 4, 1024), (3, 2, 100), (5, 0, 77), (4, 8, 50001), (2, 16, 8191), (7, 3, 8193),
-          (32, 4, 128256), (16, 0, 128256)]
+          (32, 4, 128256), (16, 0, 128256), (2, 2, 600000), (2, 0, 2200000)]
 
 
 @pytest.mark.parametrize("B,gamma,V", SHAPES)
