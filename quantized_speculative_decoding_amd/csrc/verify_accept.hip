@@ -570,7 +570,7 @@ constexpr int HSEG = VCHUNK / VT;   // logits per thread in the chunk walk
 static_assert(VCHUNK % VT == 0, "whole segments per chunk");
 
 __global__ void __launch_bounds__(VT)
-k_head_pick(const float *__restrict__ logits, size_t ldt, const float *__restrict__ u, int V, int C,
+k_head_pick(const float *__restrict__ logits, size_t ldt, const float *__restrict__ u, int V, int C, bool vec,
             const float *__restrict__ pmax, const double *__restrict__ psum, int32_t *__restrict__ accept,
             int32_t *__restrict__ out, int ldo) {
     const int b = blockIdx.x;
@@ -628,9 +628,38 @@ k_head_pick(const float *__restrict__ logits, size_t ldt, const float *__restric
     __syncthreads();
     const int lo = s_chunk * VCHUNK, hi = min(V, lo + VCHUNK);
     const int x0 = lo + tid * HSEG, x1 = min(hi, x0 + HSEG);
+    // The chunk is read with coalesced loads into LDS (4-logit piece q at slot (q / 8) * 8 +
+    // (q % 8) ^ (q / 8 % 8), so that the segment reads below hit distinct bank groups), then each
+    // thread takes its HSEG contiguous logits from there.  Logits past the row read as 0 and are
+    // never used.
+    __shared__ float4 stage[VCHUNK / 4];
+    static_assert(HSEG == 32, "eight 4-logit pieces per thread");
+#pragma unroll
+    for (int k = 0; k < VCHUNK / 4 / VT; ++k) {
+        const int q = tid + VT * k;
+        const int x = lo + 4 * q;
+        float4 v;
+        if (vec && x + 3 < hi) {
+            v = *(const float4 *)(row + x);
+        } else {
+            v.x = x < hi ? row[x] : 0.f;
+            v.y = x + 1 < hi ? row[x + 1] : 0.f;
+            v.z = x + 2 < hi ? row[x + 2] : 0.f;
+            v.w = x + 3 < hi ? row[x + 3] : 0.f;
+        }
+        const int t = q >> 3, i = q & 7;
+        stage[t * 8 + (i ^ (t & 7))] = v;
+    }
+    __syncthreads();
     float lv[HSEG];
 #pragma unroll
-    for (int k = 0; k < HSEG; ++k) lv[k] = x0 + k < x1 ? row[x0 + k] : 0.f;
+    for (int i = 0; i < 8; ++i) {
+        const float4 v = stage[tid * 8 + (i ^ (tid & 7))];
+        lv[4 * i] = v.x;
+        lv[4 * i + 1] = v.y;
+        lv[4 * i + 2] = v.z;
+        lv[4 * i + 3] = v.w;
+    }
     double wv[HSEG];   // exp(x - M) of the segment's logits (0 past the chunk), kept for the walk
 #pragma unroll
     for (int k = 0; k < HSEG; ++k) wv[k] = x0 + k < x1 ? exp((double)lv[k] - M) : 0.0;
@@ -839,8 +868,8 @@ static hipError_t launch_verify(int mode, const float *target, size_t ldt, const
     hipLaunchKernelGGL(k_softmax_partial, dim3((unsigned)(R * C)), dim3(VT), 0, st, target, ldt, draft, B,
                        gamma, V, C, vec, pmax, psum);
     if (gamma == 0) {   // no candidates: the draw from each row's softmax, straight from its statistics
-        hipLaunchKernelGGL(k_head_pick, dim3(B), dim3(VT), 0, st, target, ldt, u_resample, V, C, pmax, psum, accept,
-                           out, ldo);
+        hipLaunchKernelGGL(k_head_pick, dim3(B), dim3(VT), 0, st, target, ldt, u_resample, V, C, vec_t, pmax, psum,
+                           accept, out, ldo);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(k_sample_accept, dim3(B), dim3(kWave), 0, st, target, ldt, draft, tokens,
