@@ -190,9 +190,10 @@ size_t qspec_gemm_w4a16_workspace_bytes(int32_t M, int32_t K, int32_t N);
  *           need no initialization.  Calls sharing a workspace must be ordered on one stream.
  * Batch invariance: the reduction order of an output depends only on (K, N) and on the
  * batch tier of M (qspec_gemm_w4a16_tier), so row m of y is bit-identical for every M in the
- * same tier; verifying gamma + 1 <= 16 positions of one sequence therefore reproduces
- * one-position decoding bit for bit.  Across tiers (say plain decoding at M = B = 16 and
- * verification at M = 5B = 80) rows agree to fp32 rounding, not bit for bit.
+ * same tier; verifying gamma + 1 <= D positions of one sequence (D >= 8 for every shape, 24 or
+ * 32 for some) therefore reproduces one-position decoding bit for bit.  Across tiers (say plain
+ * decoding at M = B = 16 and verification at M = 5B = 80) rows agree to fp32 rounding, not bit
+ * for bit.
  * Errors: NULL pointer; M < 1; N < 1 or N % 16 != 0; K < 128 or K % 128 != 0; min(M, 128) * K * 2
  * or K * 8 of 2^32 or more (32-bit buffer ranges); bad y_dtype; workspace missing or too small.
  */
