@@ -204,7 +204,8 @@ def parse():
                          "rotated beyond the last-level cache), write a markdown table to OUT_MD and exit")
     ap.add_argument("--probe", metavar="LAYER:K:N:M",
                     help="run one GEMM shape (LAYER w4a4 or w4a16) --probe-reps times on fresh weight copies "
-                         "and exit: a short program for rocprofv3 counter passes")
+                         "and exit: a short program for rocprofv3 counter passes; attention:Q runs one "
+                         "layer's attention (B = 16, 4096 positions) for Q query tokens instead")
     ap.add_argument("--probe-reps", type=int, default=4)
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
                     help="OUT_MD LABEL=DIR [LABEL=DIR ...]: summarize rocprofv3 --pmc runs of --probe (one "
@@ -967,7 +968,7 @@ def summarize_pmc(args):
             if (k, r["Dispatch_Id"]) not in seen:
                 seen.add((k, r["Dispatch_Id"]))
                 dur[(probe_name, k)].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
-    lines = ["# rocprofv3 counters of single GEMM launches (--probe), per dispatch", "",
+    lines = ["# rocprofv3 counters of single probed launches (--probe: one GEMM shape, or one layer's attention), per dispatch", "",
              "Command:", "", "```", PMC_COMMAND, "```", "",
              "Passes (one rocprofv3 run each; a probe's passes are merged per kernel): "
              + "; ".join(f"{k}: {v}" for k, v in PMC_PASSES.items()), "",
@@ -1010,14 +1011,42 @@ def summarize_pmc(args):
     print("wrote", out_md)
 
 
-def probe(args):
-    """One GEMM shape, launched eagerly --probe-reps times over distinct weight copies (each read
-    from HBM), for counter collection; prints the shape and exits."""
+def probe_attention(args, Q):
+    """One layer's attention over the bfloat16 cache (the shape of the benchmark's attention
+    figure: B = 16, 32 query heads, 8 KV heads, d 128, a full 4096-position cache) for Q query
+    tokens, launched eagerly --probe-reps times over two cache copies; prints and exits."""
+    import math
+
     import torch
 
     import quantized_speculative_decoding_amd as q
     import synthetic_inputs as si
 
+    dev = torch.device("cuda:0")
+    B, Hq = 16, 32
+    qd, cache = si.attention_inputs_device(B, Q, Hq, KV_HEADS, CONTEXT, HEAD_DIM, 1, dev)
+    pos = torch.full((B,), CONTEXT - Q, dtype=torch.int32, device=dev)
+    out = torch.empty((B, Q, Hq, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((q.qspec_attention_workspace_bytes(B, Q, Hq, KV_HEADS, CONTEXT),), dtype=torch.uint8, device=dev)
+    copies = [cache, cache.clone()]
+    for i in range(args.probe_reps):
+        q.qspec_attention(qd, copies[i % 2], pos, 1.0 / math.sqrt(HEAD_DIM), out, ws)
+    torch.cuda.synchronize()
+    print(f"probe attention B={B} Q={Q} T={CONTEXT} x{args.probe_reps}", flush=True)
+
+
+def probe(args):
+    """One GEMM shape, launched eagerly --probe-reps times over distinct weight copies (each read
+    from HBM), for counter collection; prints the shape and exits.  attention:Q probes the
+    attention kernel instead (probe_attention)."""
+    import torch
+
+    import quantized_speculative_decoding_amd as q
+    import synthetic_inputs as si
+
+    if args.probe.startswith("attention:"):
+        probe_attention(args, int(args.probe.split(":")[1]))
+        return
     layer, K, N, M = args.probe.split(":")
     K, N, M = int(K), int(N), int(M)
     dev = torch.device("cuda:0")
