@@ -17,7 +17,8 @@
 //    fill the chip, up to 384 in row blocks of at most 80): each group's activation tile goes
 //    straight from memory into LDS and is shared by the workgroup's waves; K is split between two
 //    wave groups (and across workgroups with an ordered reduction).
-//  * k_w4a16_lds (the large tier): 128-row blocks, activations staged through registers into LDS.
+//  * k_w4a16_lds (the large tier): 128-row blocks, activations staged through registers into LDS,
+//    2 or 3 column tiles per wave.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -237,14 +238,15 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
 // (k_w4a16_lds).  At these M a group's activation tile (M x 128 bf16: 20 KB for 80 rows, 32 KB
 // for a 128-row block) is as large as 20 - 32 weight blocks, so it is staged once in LDS and
 // shared by the workgroup's waves, while every weight block is dequantized exactly once, in
-// registers, by the wave whose MFMA B operand it is.  Each wave owns LDS_NT = 2 column tiles.
+// registers, by the wave whose MFMA B operand it is.  In the verify tier each wave owns LDS_NT = 2
+// column tiles; in the large tier NT = 2 or 3.
 //  * verify tier: 2 K parts x 4 column waves (8 waves, 128 columns, up to 80 rows), two waves per
 //    SIMD (a single wave per SIMD issues MFMA and VALU work at about half the rate two reach);
-//  * large tier: 8 column waves (256 columns, 128-row blocks).
+//  * large tier: 8 column waves (256 or 384 columns, 128-row blocks).
 // k_w4a16_lds: per group, the waves stage the activation tile into LDS in fragment-major order
 // (fragment f = (row tile, 32-k step), lane l's 16 bytes in f's 1 KB block, XOR-swizzled:
 // conflict-free 128-bit writes and reads) and every wave reads all fragments from there, each
-// feeding LDS_NT MFMAs.  Activations and weights travel through one U-deep register ring in group
+// feeding NT MFMAs.  Activations and weights travel through one U-deep register ring in group
 // order (the in-order vmcnt wait for a stage never covers a younger one); a stage's activations
 // are written to LDS one step before they are consumed, its weights are dequantized in registers
 // when consumed.  One barrier per step.  With S > 1 K splits (a function of (K, N) only), each
@@ -253,15 +255,14 @@ k_w4a16_decode(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict_
 constexpr int LDS_NT = 2;                    // column tiles per wave
 constexpr int MID_KP = 2, MID_CW = 4;        // verify tier
 constexpr int MID_TILES = MID_CW * LDS_NT;   // column tiles per verify-tier workgroup
-constexpr int BIG_MT = 8, BIG_CW = 8;        // large tier: 128-row blocks, 256 columns
-constexpr int BIG_TILES = BIG_CW * LDS_NT;
+constexpr int BIG_MT = 8, BIG_CW = 8;        // large tier: 128-row blocks, 8 column waves
+constexpr int BIG_TILES = BIG_CW * LDS_NT;   // with 2 tiles per wave (the tier and split rules)
 
-template <int MT, int U, int CW>
+template <int MT, int U, int CW, int NT>
 __global__ void __launch_bounds__(CW * 64)
 k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
             const uint32_t *__restrict__ meta, int K, int N, void *__restrict__ y, int y_f32, int S,
             float *__restrict__ partials, int row_blocks) {
-    constexpr int NT = LDS_NT;
     constexpr int THREADS = CW * 64;
     constexpr int TILES = CW * NT;          // column tiles per workgroup
     constexpr int NF = MT * 4;              // activation fragments per group
@@ -426,8 +427,8 @@ k_w4a16_lds(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ c
     float *dstf = S > 1 ? partials + (size_t)split * M * N + (size_t)m0 * N : (float *)y + (size_t)m0 * N;
     uint16_t *dsth = (uint16_t *)y + (size_t)m0 * N;
     float *red = (float *)lds;
-    constexpr int CHUNK = 64;                       // output columns per round
-    constexpr int CHUNK_WAVES = CHUNK / (NT * 16);
+    constexpr int CHUNK_WAVES = NT * 16 >= 64 ? 1 : 64 / (NT * 16);   // column waves per round
+    constexpr int CHUNK = CHUNK_WAVES * NT * 16;    // output columns per round
     constexpr int OPITCH = CHUNK + 4;               // floats per output row in LDS
     static_assert(MT * 16 * OPITCH <= STAGE_U4 * 4, "output buffer");
     static_assert(CW % CHUNK_WAVES == 0, "column rounds");
@@ -960,14 +961,24 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int M, const uint8_t *codes, con
         }
     }
     // Large tier: 128-row blocks x 256 columns, K splits for shapes with few column blocks, one
-    // XCD-remapped 1-D grid (a 2-D (column block, split) grid for a single row block)
+    // XCD-remapped 1-D grid (a 2-D (column block, split) grid for a single row block).  Where even
+    // 384-column blocks give at least four workgroups per CU, the waves take 3 column tiles each
+    // (fewer activation fragment reads from LDS per MFMA) with a 3-deep ring.  A row's reduction
+    // order does not depend on the tiles per wave, so this choice may follow M.
     const int rbs = (M + BIG_MT * 16 - 1) / (BIG_MT * 16);
-    const int cbs = (N / 16 + BIG_TILES - 1) / BIG_TILES;
     const int S = big_splits(K, N);
     float *partials = S > 1 ? (float *)ws : nullptr;
-    const dim3 grid = rbs > 1 ? dim3(cbs * S * rbs) : dim3(cbs, S);
-    hipLaunchKernelGGL((k_w4a16_lds<BIG_MT, 4, BIG_CW>), grid, dim3(BIG_CW * 64), 0, st, x, M, codes, meta,
-                       K, N, y, y_f32, S, partials, rbs);
+    const int cbs3 = (N / 16 + BIG_CW * 3 - 1) / (BIG_CW * 3);
+    if ((long long)cbs3 * S * rbs >= 4 * 256) {
+        const dim3 grid = rbs > 1 ? dim3(cbs3 * S * rbs) : dim3(cbs3, S);
+        hipLaunchKernelGGL((k_w4a16_lds<BIG_MT, 3, BIG_CW, 3>), grid, dim3(BIG_CW * 64), 0, st, x, M, codes, meta,
+                           K, N, y, y_f32, S, partials, rbs);
+    } else {
+        const int cbs = (N / 16 + BIG_TILES - 1) / BIG_TILES;
+        const dim3 grid = rbs > 1 ? dim3(cbs * S * rbs) : dim3(cbs, S);
+        hipLaunchKernelGGL((k_w4a16_lds<BIG_MT, 4, BIG_CW, LDS_NT>), grid, dim3(BIG_CW * 64), 0, st, x, M, codes,
+                           meta, K, N, y, y_f32, S, partials, rbs);
+    }
     if (S > 1) launch_splitk_reduce(partials, S, M, N, y, y_f32, st);
     return hipGetLastError();
 }

@@ -221,6 +221,27 @@ def test_w4a16_row_blocks_split_k(M, K, N, tier):
     assert np.array_equal(y_lo, y[:lo])
 
 
+def test_w4a16_large_tier_tiles_per_wave():
+    """The large tier gives each wave 3 column tiles once 384-column blocks make at least four
+    workgroups per CU, else 2.  1024 x 76928 (4808 tiles: a ragged last block for both widths) in
+    its large tier: 768 rows (6 row blocks of 201 three-tile blocks), 200 and 96 rows (two-tile
+    blocks).  Every row is bitwise the same in all three; sampled tiles match the oracle."""
+    K, N = 1024, 16 * 4808
+    note(f"gemm_w4a16 large-tier tiles per wave K={K} N={N}")
+    t, lo, _ = q.qspec_gemm_w4a16_tier(96, K, N)
+    assert t == 2 and lo <= 96
+    w = si.weights(K, N, seed=31)
+    wdev = weights_dev(w)
+    x = si.activations(768, K, seed=32)
+    y = run_w4a16(x, w, torch.float32, wdev).cpu().numpy()
+    for M in (200, 96):
+        assert np.array_equal(run_w4a16(x[:M], w, torch.float32, wdev).cpu().numpy(), y[:M]), M
+    tiles = np.array([0, 23, 24, 4799, 4800, N // 16 - 1])
+    sub = si.slice_tiles(w, tiles)
+    assert_close(y[:, tile_columns(tiles)].astype(np.float64), oracle.gemm_w4a16(x, sub["codes"], sub["meta"]),
+                 False, "large tier, 3 tiles per wave")
+
+
 FULL_W4A16 = [
     # Llama-3-8B-shaped projections, verify at M = 5B for B in 1, 4, 16
     ("llama8b.qkv", 4096, 6144, 80), ("llama8b.o", 4096, 4096, 20), ("llama8b.gate_up", 4096, 28672, 5),
